@@ -1,0 +1,223 @@
+"""CPU oracle (test infrastructure only).
+
+Plain, slow, obviously correct definitions of what the signal-gated tiled path
+computes, in double precision, written in C (``oracle.c``) and wrapped here with
+ctypes and numpy.  Only the tests, the smoke check and the benchmark's CPU
+baseline may import this package; the product path never does, and this
+package imports nothing from the product.
+
+Functions and the passage each follows (page titles as on the pages):
+
+* ``allgather``      -- Triton-distributed semantics page, "AllGather + GEMM overlap":
+                        the producer gathers every PE's tiles into one buffer.
+* ``ag_gemm``        -- same section: C = AllGather(A) * B_local.
+* ``gemm_rs``        -- Triton-distributed semantics page, "GEMM + ReduceScatter overlap";
+                        Triton-distributed paper summary, "Method" (intra-node
+                        ReduceScatter in push mode): each rank reduces its own row block.
+* ``moe_route`` / ``moe_ag_gemm`` -- paper summary, "Experiments" (MoE routing
+                        operations) and the DITRON article, "three-level tiling"
+                        (dynamic per-expert sizes): top-k routing, expert-grouped rows.
+* ``ag_gemm_protocol`` -- semantics page, "Producer-consumer model", "Signal-based
+                        synchronization", "Threadblock swizzle", "Token-based data
+                        dependency"; paper summary, "Method" (AMD full-mesh swizzle):
+                        the same C computed through host threads that copy tiles,
+                        release flags, and wait on flags before reading.
+
+bf16 arrays are numpy ``uint16`` bit patterns; fp32 arrays are ``float32``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+F32, BF16 = 0, 1
+KN, NK = 0, 1
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (OpenMP over output rows)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+                               "-Wall", "-Wno-unused-function", _SRC, "-o", tmp, "-lpthread"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        P, I64, I32, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        lib.orc_allgather.argtypes = [P, I32, I64, I64, P]
+        lib.orc_gemm_rows.argtypes = [P, I32, P, I32, I32, I64, I64, I64, P, I64, P, I32]
+        lib.orc_gemm_rs.argtypes = [P, I32, P, I32, I32, I64, I64, I64, P, I32, I32, P, I64, P, I32]
+        lib.orc_moe_route.argtypes = [P, I64, I32, I32, P, P, P]
+        lib.orc_moe_route.restype = I32
+        lib.orc_moe_gemm_rows.argtypes = [P, P, I32, I64, I64, I32, P, P, P, I64, P, I32]
+        lib.orc_ag_gemm_protocol.argtypes = [P, I32, I32, I32, P, I32, I32, I64, I64, I64, I64, I64,
+                                             ctypes.c_uint64, D, I32, I32, I32, I32, P, P]
+        lib.orc_ag_gemm_protocol.restype = I32
+        lib.orc_max_threads.restype = I32
+        lib.orc_panel_order.argtypes = [I32, I32, I64, I64, I32, P]
+        lib.orc_panel_order.restype = I32
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().orc_max_threads())
+
+
+def _dt(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.float32:
+        return F32
+    raise TypeError("oracle inputs are bf16 bits (uint16) or float32, got %s" % a.dtype)
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _ptr_array(arrs):
+    return (ctypes.c_void_p * len(arrs))(*[a.ctypes.data for a in arrs])
+
+
+def _rows(rows):
+    if rows is None:
+        return None, None, 0
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    return r, _ptr(r), len(r)
+
+
+def _lay(layout: str) -> int:
+    return {"kn": KN, "nk": NK}[layout]
+
+
+def allgather(shards) -> np.ndarray:
+    """Stack the row shards in shard order (shard p -> rows [p*R, (p+1)*R))."""
+    shards = [np.ascontiguousarray(s) for s in shards]
+    R, K = shards[0].shape
+    out = np.empty((R * len(shards), K), dtype=shards[0].dtype)
+    _load().orc_allgather(_ptr_array(shards), len(shards), R, K * shards[0].itemsize, _ptr(out))
+    return out
+
+
+def gemm(A: np.ndarray, B: np.ndarray, b_layout: str = "kn", rows=None, threads: int = 0) -> np.ndarray:
+    """C = A * B in float64 (ascending-k sums); only the listed rows of A if given."""
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    M, K = A.shape
+    N = B.shape[1] if b_layout == "kn" else B.shape[0]
+    assert (B.shape[0] if b_layout == "kn" else B.shape[1]) == K
+    r, rp, nr = _rows(rows)
+    C = np.empty((nr if r is not None else M, N), np.float64)
+    _load().orc_gemm_rows(_ptr(A), _dt(A), _ptr(B), _dt(B), _lay(b_layout), M, K, N, rp, nr, _ptr(C), threads)
+    return C
+
+
+def ag_gemm(shards, B, b_layout: str = "kn", rows=None, threads: int = 0):
+    """(A_full, C) for C = AllGather(shards) * B; C holds only `rows` if given."""
+    A_full = allgather(shards)
+    return A_full, gemm(A_full, B, b_layout, rows, threads)
+
+
+def gemm_rs(A_local, B, partials, rank: int, b_layout: str = "kn", rows=None, threads: int = 0) -> np.ndarray:
+    """C_shard for `rank`: block `rank` of A_local*B plus every other rank's partial block."""
+    A = np.ascontiguousarray(A_local)
+    B = np.ascontiguousarray(B)
+    W = len(partials)
+    M, K = A.shape
+    N = B.shape[1] if b_layout == "kn" else B.shape[0]
+    assert M % W == 0
+    parts = [np.ascontiguousarray(p, dtype=np.float32) for p in partials]
+    for p in parts:
+        assert p.shape == (M // W, N)
+    r, rp, nr = _rows(rows)
+    C = np.empty((nr if r is not None else M // W, N), np.float64)
+    _load().orc_gemm_rs(_ptr(A), _dt(A), _ptr(B), _dt(B), _lay(b_layout), M, K, N, _ptr_array(parts), W, rank,
+                        rp, nr, _ptr(C), threads)
+    return C
+
+
+def moe_route(logits: np.ndarray, topk: int):
+    """(topk_ids T x k, expert_off E+1, row_token T*k) by descending logit, ties to the lower id."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, topk), np.int32)
+    off = np.empty(E + 1, np.int32)
+    row_token = np.empty(T * topk, np.int32)
+    rc = _load().orc_moe_route(_ptr(logits), T, E, topk, _ptr(ids), _ptr(off), _ptr(row_token))
+    if rc != 0:
+        raise ValueError("bad top-k")
+    return ids, off, row_token
+
+
+def moe_gemm(X_full, W_experts, expert_off, row_token, w_layout: str = "kn", rows=None, threads: int = 0):
+    """Y[row] = X_full[row_token[row]] * W_e for the expert e owning `row` (float64)."""
+    X = np.ascontiguousarray(X_full, dtype=np.uint16)
+    Wt = np.ascontiguousarray(W_experts, dtype=np.uint16)
+    E = Wt.shape[0]
+    H = X.shape[1]
+    I = Wt.shape[2] if w_layout == "kn" else Wt.shape[1]
+    off = np.ascontiguousarray(expert_off, dtype=np.int32)
+    rt = np.ascontiguousarray(row_token, dtype=np.int32)
+    r, rp, nr = _rows(rows)
+    Y = np.empty((nr if r is not None else int(off[E]), I), np.float64)
+    _load().orc_moe_gemm_rows(_ptr(X), _ptr(Wt), _lay(w_layout), H, I, E, _ptr(off), _ptr(rt), rp, nr, _ptr(Y),
+                              threads)
+    return Y
+
+
+def moe_ag_gemm(shards, W_experts, logits, topk: int, w_layout: str = "kn", rows=None, threads: int = 0):
+    """(X_full, topk_ids, expert_off, row_token, Y) for the MoE AllGather-grouped-GEMM."""
+    X_full = allgather(shards)
+    ids, off, rt = moe_route(logits, topk)
+    return X_full, ids, off, rt, moe_gemm(X_full, W_experts, off, rt, w_layout, rows, threads)
+
+
+def panel_order(W: int, rank: int, rows_per_shard: int, panel_rows: int, order: str = "shard") -> np.ndarray:
+    """Order in which the emulated consumer takes the row panels."""
+    out = np.empty(W * rows_per_shard // panel_rows, np.int64)
+    if _load().orc_panel_order(W, rank, rows_per_shard, panel_rows, {"shard": 0, "mesh": 1}[order], _ptr(out)):
+        raise ValueError("bad panel-order arguments")
+    return out
+
+
+def ag_gemm_protocol(shards, B, rank: int, b_layout: str = "kn", flag_rows: int = 16, panel_rows: int = 16,
+                     seed: int = 0, max_delay_us: float = 0.0, global_perm: bool = False, order: str = "shard",
+                     n_consumers: int = 4, skip_wait: bool = False):
+    """(A_gathered, C) computed through the emulated signal protocol.
+
+    The gathered buffer starts as NaN poison, so a consumer that read a tile
+    before its flag would produce NaN or different bits.  ``skip_wait`` drops
+    the consumer's wait (a deliberately wrong oracle, for tests of the tests).
+    """
+    shards = [np.ascontiguousarray(s) for s in shards]
+    B = np.ascontiguousarray(B)
+    W = len(shards)
+    R, K = shards[0].shape
+    M = R * W
+    N = B.shape[1] if b_layout == "kn" else B.shape[0]
+    dt = _dt(shards[0])
+    A_g = np.empty((M, K), shards[0].dtype)
+    A_g.view(np.uint16 if dt == BF16 else np.uint32)[...] = 0x7FC0 if dt == BF16 else 0x7FC00000
+    C = np.empty((M, N), np.float64)
+    rc = _load().orc_ag_gemm_protocol(_ptr_array(shards), W, rank, dt, _ptr(B), _dt(B), _lay(b_layout), M, K, N,
+                                      flag_rows, panel_rows, seed, max_delay_us, int(global_perm),
+                                      {"shard": 0, "mesh": 1}[order], n_consumers, int(skip_wait), _ptr(A_g), _ptr(C))
+    if rc != 0:
+        raise ValueError("bad protocol arguments")
+    return A_g, C

@@ -1,0 +1,271 @@
+"""Pins for the CPU oracle against facts fixed by mathematics and by the pages.
+
+Nothing here re-types the oracle's formula: each check compares it with an
+independent exact computation (Python rationals, integer matrix products), a
+closed form (identity / permutation matrices), a library routine for a special
+case (numpy concatenate, stable argsort), a hand-derived fixture (panel orders
+from the pages' swizzle formula), or an invariant (arrival-order invariance of
+the protocol emulation, with a planted mistake showing the check has teeth).
+"""
+from fractions import Fraction
+import os
+
+import numpy as np
+import pytest
+
+from signal_gated_tiled_amd import inputs as I
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _vals(a):
+    return I.bf16_bits_to_f32(a) if a.dtype == np.uint16 else a
+
+
+def _exact_gemm(A, B, b_layout):
+    """Exact rational product (independent of the oracle): returns (value, sum|a||b|) as Fractions."""
+    Av = _vals(A).astype(np.float64)
+    Bv = _vals(B).astype(np.float64)
+    if b_layout == "nk":
+        Bv = Bv.T
+    M, K = Av.shape
+    N = Bv.shape[1]
+    out = [[None] * N for _ in range(M)]
+    mag = [[None] * N for _ in range(M)]
+    for i in range(M):
+        for j in range(N):
+            s = Fraction(0)
+            m = Fraction(0)
+            for k in range(K):
+                p = Fraction(float(Av[i, k])) * Fraction(float(Bv[k, j]))
+                s += p
+                m += abs(p)
+            out[i][j] = s
+            mag[i][j] = m
+    return out, mag
+
+
+def _rand(shape, dtype, seed):
+    ss = np.random.SeedSequence(seed)
+    return I.uniform_f32(ss, shape) if dtype == "f32" else I.normal_bf16(ss, shape, 0.5)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("b_layout", ["kn", "nk"])
+@pytest.mark.parametrize("M,K,N", [(3, 5, 4), (7, 13, 6), (5, 33, 9)])
+def test_gemm_against_exact_rationals(orc, dtype, b_layout, M, K, N):
+    A = _rand((M, K), dtype, 11 + M)
+    B = _rand((K, N), dtype, 97 + N)
+    Bs = np.ascontiguousarray(B.T) if b_layout == "nk" else B
+    C = orc.gemm(A, Bs, b_layout)
+    exact, mag = _exact_gemm(A, Bs, b_layout)
+    u = 2.0 ** -53
+    for i in range(M):
+        for j in range(N):
+            err = abs(Fraction(float(C[i, j])) - exact[i][j])
+            assert err <= Fraction(K) * Fraction(u) * mag[i][j] + Fraction(1, 2 ** 1074), (i, j)
+    # a transposed operand or a shifted index gives a large error somewhere
+    Cf = np.array([[float(x) for x in row] for row in exact])
+    assert np.allclose(C, Cf, rtol=1e-12, atol=1e-12)
+
+
+def test_allgather_is_row_concatenation(orc):
+    shards = [_rand((6, 10), "bf16", s) for s in range(5)]
+    A = orc.allgather(shards)
+    assert A.shape == (30, 10)
+    assert np.array_equal(A, np.concatenate(shards, axis=0))
+    for p in range(5):
+        assert np.array_equal(A[6 * p:6 * (p + 1)], shards[p])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_identity_B_returns_gathered_rows(orc, dtype):
+    shards = [_rand((8, 24), dtype, 40 + s) for s in range(3)]
+    eye = np.eye(24, dtype=np.float32)
+    B = eye if dtype == "f32" else I.f32_to_bf16_bits(eye)
+    A_full, C = orc.ag_gemm(shards, B)
+    assert np.array_equal(C, _vals(A_full).astype(np.float64))
+
+
+def test_permutation_B_permutes_columns(orc):
+    shards = [_rand((4, 16), "f32", 60 + s) for s in range(4)]
+    perm = np.random.default_rng(3).permutation(16)
+    Pm = np.zeros((16, 16), np.float32)
+    Pm[perm, np.arange(16)] = 1.0          # column j of A*Pm is column perm[j] of A
+    A_full, C = orc.ag_gemm(shards, Pm)
+    assert np.array_equal(C, A_full[:, perm].astype(np.float64))
+    A_full, C = orc.ag_gemm(shards, np.ascontiguousarray(Pm.T), b_layout="nk")
+    assert np.array_equal(C, A_full[:, perm].astype(np.float64))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_integer_inputs_match_integer_product(orc, dtype):
+    ss = np.random.SeedSequence(5)
+    a, b = ss.spawn(2)
+    A = I.small_int(a, (37, 70), dtype=dtype)
+    B = I.small_int(b, (70, 23), dtype=dtype)
+    C = orc.gemm(A, B)
+    ref = _vals(A).astype(np.int64) @ _vals(B).astype(np.int64)
+    assert np.array_equal(C, ref.astype(np.float64))
+
+
+def test_row_subset_matches_full(orc):
+    A = _rand((40, 31), "bf16", 1)
+    B = _rand((31, 12), "bf16", 2)
+    full = orc.gemm(A, B)
+    rows = [39, 0, 17, 17, 5]
+    assert np.array_equal(orc.gemm(A, B, rows=rows), full[rows])
+    assert np.array_equal(orc.gemm(A, B, threads=1), full)
+
+
+def _read_swizzle_fixture():
+    out = []
+    with open(os.path.join(GOLDEN, "swizzle_orders.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            head, tail = line.split(":")
+            order, W, tpp, rank = head.split()
+            out.append((order, int(W), int(tpp), int(rank), [int(x) for x in tail.split()]))
+    return out
+
+
+@pytest.mark.parametrize("case", _read_swizzle_fixture())
+def test_panel_order_matches_fixture(orc, case):
+    order, W, tpp, rank, expect = case
+    got = orc.panel_order(W, rank, rows_per_shard=tpp * 4, panel_rows=4, order=order)
+    assert list(got) == expect
+    assert sorted(got) == list(range(W * tpp))   # a permutation of the panels
+
+
+@pytest.mark.parametrize("order", ["shard", "mesh"])
+@pytest.mark.parametrize("rank", [0, 2, 3])
+def test_protocol_is_invariant_to_arrival_order_and_delay(orc, order, rank):
+    shards, B = I.make_ag(I.TINY)
+    A_ref, C_ref = orc.ag_gemm(shards, B)
+    for seed, delay, gp in [(0, 0.0, False), (1, 30.0, False), (7, 50.0, True), (123, 200.0, True), (9, 5.0, False)]:
+        A_g, C = orc.ag_gemm_protocol(shards, B, rank=rank, flag_rows=16, panel_rows=16, seed=seed,
+                                      max_delay_us=delay, global_perm=gp, order=order, n_consumers=3)
+        assert np.array_equal(A_g, A_ref)
+        assert np.array_equal(C, C_ref), (seed, delay, gp)
+
+
+def test_protocol_panels_spanning_several_flags(orc):
+    w = I.scaled(I.TINY, dtype="bf16", dist="normal", std=0.5)
+    shards, B = I.make_ag(w)
+    _, C_ref = orc.ag_gemm(shards, B)
+    _, C = orc.ag_gemm_protocol(shards, B, rank=1, flag_rows=8, panel_rows=32, seed=4, max_delay_us=40.0)
+    assert np.array_equal(C, C_ref)
+
+
+def test_planted_mistake_is_caught(orc):
+    """A consumer that skips the wait reads poison: the invariance check must fail."""
+    shards, B = I.make_ag(I.TINY)
+    _, C_ref = orc.ag_gemm(shards, B)
+    _, C = orc.ag_gemm_protocol(shards, B, rank=0, seed=3, max_delay_us=3000.0, global_perm=True,
+                                n_consumers=4, skip_wait=True)
+    assert not np.array_equal(C, C_ref)
+
+
+def _rs_inputs(dist_a="normal", peer="normal", W=4, M=32, K=24, N=20, dtype="bf16", seed=2):
+    w = I.RSWorkload("t", W=W, M=M, K=K, N=N, dtype=dtype, dist=dist_a, std=0.5, peer_dist=peer, seed_index=seed)
+    return I.make_rs(w)
+
+
+def test_gemm_rs_exact_small(orc):
+    A, B, parts = _rs_inputs(W=2, M=6, K=9, N=5)
+    for rank in range(2):
+        C = orc.gemm_rs(A, B, parts, rank)
+        exact, mag = _exact_gemm(A[rank * 3:(rank + 1) * 3], B, "kn")
+        for i in range(3):
+            for j in range(5):
+                v = exact[i][j] + sum(Fraction(float(parts[p][i, j])) for p in range(2) if p != rank)
+                assert abs(Fraction(float(C[i, j])) - v) <= Fraction(2 ** -40) * (mag[i][j] + 8)
+
+
+def test_gemm_rs_zero_A_is_sum_of_peers(orc):
+    A, B, parts = _rs_inputs(dist_a="int", peer="int")
+    A = np.zeros_like(A)
+    for rank in range(4):
+        C = orc.gemm_rs(A, B, parts, rank)
+        ref = sum(parts[p].astype(np.float64) for p in range(4) if p != rank)
+        assert np.array_equal(C, ref)
+
+
+def test_gemm_rs_zero_peers_is_block_product(orc):
+    A, B, parts = _rs_inputs(dist_a="int", peer="zero")
+    full = _vals(A).astype(np.int64) @ _vals(B).astype(np.int64)
+    for rank in range(4):
+        C = orc.gemm_rs(A, B, parts, rank)
+        assert np.array_equal(C, full[rank * 8:(rank + 1) * 8].astype(np.float64))
+
+
+def test_gemm_rs_linear_in_peers(orc):
+    A, B, parts = _rs_inputs(dist_a="int", peer="int")
+    base = orc.gemm_rs(A, B, [np.zeros_like(p) for p in parts], 1)
+    one = orc.gemm_rs(A, B, parts, 1)
+    two = orc.gemm_rs(A, B, [2 * p for p in parts], 1)
+    assert np.array_equal(two - base, 2 * (one - base))
+    # the local rank's own entry is never read
+    poisoned = [p.copy() for p in parts]
+    poisoned[1][...] = np.nan
+    assert np.array_equal(orc.gemm_rs(A, B, poisoned, 1), one)
+
+
+def test_moe_route_matches_stable_sort(orc):
+    w = I.scaled(I.MOE, T=256, W=4)
+    _, _, logits = I.make_moe(w)
+    ids, off, row_token = orc.moe_route(logits, w.topk)
+    ref = np.argsort(-logits, axis=1, kind="stable")[:, :w.topk]
+    assert np.array_equal(ids, ref)
+    assert off[0] == 0 and off[-1] == w.T * w.topk
+    assert np.all(np.diff(off) >= 0)
+    for e in range(w.E):
+        toks = row_token[off[e]:off[e + 1]]
+        assert np.all(np.diff(toks) > 0)                 # ascending, no duplicates
+        assert np.array_equal(np.sort(np.nonzero((ids == e).any(1))[0]), toks)
+    counts = np.bincount(row_token, minlength=w.T)
+    assert np.all(counts == w.topk)
+
+
+def test_moe_route_ties_go_to_lower_id(orc):
+    logits = np.zeros((3, 6), np.float32)
+    logits[1, 4] = 1.0
+    logits[2] = [0.5, 2.0, 0.5, 2.0, 0.5, 0.5]
+    ids, off, rt = orc.moe_route(logits, 3)
+    assert ids.tolist() == [[0, 1, 2], [4, 0, 1], [1, 3, 0]]
+    # expert 0: tokens 0,1,2; expert 1: tokens 0,1,2; expert 2: token 0; 3: token 2; 4: token 1; 5: none
+    assert off.tolist() == [0, 3, 6, 7, 8, 9, 9]
+    assert rt.tolist() == [0, 1, 2, 0, 1, 2, 0, 2, 1]
+
+
+def test_moe_skew_is_zipf_like():
+    _, _, logits = I.make_moe(I.MOE)
+    top = np.argsort(-logits, axis=1, kind="stable")[:, :I.MOE.topk]
+    sizes = np.bincount(top.ravel(), minlength=I.MOE.E)
+    assert sizes.sum() == I.MOE.T * I.MOE.topk
+    assert sizes.max() > 4 * sizes.mean() and sizes.min() < sizes.mean() / 4
+
+
+def test_moe_with_one_expert_is_ag_gemm(orc):
+    w = I.scaled(I.MOE, T=64, H=48, I=40, E=1, topk=1, W=4)
+    shards, We, logits = I.make_moe(w)
+    X, ids, off, rt, Y = orc.moe_ag_gemm(shards, We, logits, 1)
+    _, C = orc.ag_gemm(shards, We[0])
+    assert np.array_equal(Y, C)
+
+
+def test_moe_exact_small(orc):
+    w = I.scaled(I.MOE, T=8, H=7, I=5, E=4, topk=2, W=2, std=0.5)
+    shards, We, logits = I.make_moe(w)
+    X, ids, off, rt, Y = orc.moe_ag_gemm(shards, We, logits, 2)
+    for row in range(16):
+        e = int(np.searchsorted(off, row, side="right") - 1)
+        exact, mag = _exact_gemm(X[rt[row]:rt[row] + 1], We[e], "kn")
+        for j in range(5):
+            assert abs(Fraction(float(Y[row, j])) - exact[0][j]) <= Fraction(7 * 2 ** -53) * mag[0][j]
+    # nk storage of the expert weights gives the same bits
+    _, _, _, _, Y2 = orc.moe_ag_gemm(shards, np.ascontiguousarray(np.transpose(We, (0, 2, 1))), logits, 2,
+                                     w_layout="nk")
+    assert np.array_equal(Y, Y2)
