@@ -1,0 +1,231 @@
+/*
+ * sgt.h -- C ABI of libsgt, the signal-gated tiled AllGather+GEMM and
+ * GEMM+ReduceScatter library for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the Triton-distributed pages:
+ *   - "Triton-distributed semantics" (triton-distributed-ascend docs), sections
+ *     "Producer-consumer model", "Signal-based synchronization", "AllGather + GEMM
+ *     overlap", "GEMM + ReduceScatter overlap", "Threadblock swizzle",
+ *     "Token-based data dependency", "Best practices";
+ *   - the Triton-distributed paper summary (hyper.ai, arXiv 2504.19442), section
+ *     "Method": copy-engine/producer AllGather, push-mode intra-node ReduceScatter,
+ *     the AMD full-mesh swizzle and resource partitioning, AMD persistent kernels.
+ *
+ * One GPU holds one rank's share of a tensor-parallel layer.  The W peers'
+ * shards ("symmetric memory" on the pages) are device buffers on that same GPU;
+ * a producer moves them tile by tile into the gathered buffer at a simulated
+ * per-peer link rate and sets one flag per tile; a persistent HIP consumer
+ * waits on each tile's flag before reading it.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; arrays of
+ *     pointers (A_shards, partials, X_shards) are HOST arrays of W device
+ *     pointers.  Matrices are row-major and densely packed.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream) unless opts->blocking is set.  The library allocates nothing per
+ *     call: it owns only a few streams, events, a device status word and
+ *     small schedule tables created with the context.
+ *   - Arguments are validated before anything is launched; a bad argument
+ *     returns SGT_EINVAL (or SGT_EUNSUPPORTED) and launches nothing.
+ *     sgt_last_error() then describes the problem.
+ *   - Flags: uint32 words zeroed once by the caller before first use.  Each
+ *     call takes the next epoch e of its context (1, 2, ...); a flag is "set"
+ *     for this call when (int32_t)(flag - e) >= 0.  On return every flag the
+ *     call owns equals e, so flags are reused across calls without a reset.
+ *     Buffers shared by two contexts would need distinct epochs: use one
+ *     context per buffer set.
+ *   - Every wait inside a kernel is bounded by opts->timeout_ms; on expiry the
+ *     kernel records {SGT_ETIMEDOUT, flag index, value seen, value expected} in
+ *     the context's device status word and exits.  The error is returned by
+ *     sgt_sync() or by a blocking call.  No call can hang the GPU.
+ *   - Two calls that overlap in time on one context (different streams) are
+ *     not supported; calls on one stream are ordered.
+ */
+#ifndef SGT_H_
+#define SGT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define SGT_API __attribute__((visibility("default")))
+#else
+#define SGT_API
+#endif
+
+typedef enum sgt_status {
+  SGT_OK = 0,
+  SGT_EINVAL = -1,        /* bad argument (shape, pointer, alignment, option) */
+  SGT_EUNSUPPORTED = -2,  /* valid request this build does not implement      */
+  SGT_ETIMEDOUT = -3,     /* a kernel's bounded wait on a flag expired         */
+  SGT_EHIP = -4,          /* a HIP runtime call failed                          */
+  SGT_ENOMEM = -5         /* context creation could not allocate               */
+} sgt_status;
+
+enum sgt_dtype { SGT_F32 = 0, SGT_BF16 = 1 };
+
+/* Storage of the K x N right-hand matrix: row-major K x N, or row-major N x K
+ * (the same matrix transposed, as a Linear layer stores its weight). */
+enum sgt_layout { SGT_KN = 0, SGT_NK = 1 };
+
+/* Who moves the peer data and sets the flags. */
+enum sgt_producer {
+  SGT_PROD_CU = 0,      /* producer kernel on a second stream, paced per peer        */
+  SGT_PROD_PRESET = 1,  /* data already resident: flags are set up front, then the
+                           consumer runs (the "GEMM alone" baseline)                */
+  SGT_PROD_SERIAL = 2   /* producer, then consumer, on one stream (debug: barrier
+                           semantics instead of fine-grained signals)               */
+};
+
+/* Consumer order over the row panels of the gathered matrix. */
+enum sgt_order {
+  SGT_ORDER_MESH = 0,   /* local shard first, then the peers' panels round-robin, as
+                           every peer of a full mesh sends at once                   */
+  SGT_ORDER_SHARD = 1   /* pid_m shifted by rank * tiles_per_pe: local shard first,
+                           then whole shards in rank order                            */
+};
+
+typedef struct sgt_opts {
+  int32_t rank;          /* this GPU's rank, 0 <= rank < W                                     */
+  int32_t in_dtype;      /* SGT_BF16 (MFMA path) or SGT_F32 (FMA path)                         */
+  int32_t out_dtype;     /* SGT_F32 (default) or SGT_BF16 (round to nearest even)              */
+  int32_t b_layout;      /* SGT_KN or SGT_NK                                                    */
+  int32_t producer;      /* enum sgt_producer                                                   */
+  int32_t order;         /* enum sgt_order                                                      */
+  int32_t flag_rows;     /* rows per AllGather signal tile; 0 = library default                 */
+  int32_t producer_cus;  /* workgroups of the producer kernel; 0 = library default              */
+  int32_t consumer_cus;  /* workgroups of the persistent consumer; 0 = one per CU               */
+  int32_t blocking;      /* nonzero: synchronize and return the device status                   */
+  double peer_gbps;      /* simulated link rate per peer in GB/s; 0 = unthrottled               */
+  double jitter_us;      /* each remote tile's release is delayed by U[0, jitter_us]            */
+  double timeout_ms;     /* bound on every wait; 0 = 2000 ms                                    */
+  uint64_t arrival_seed; /* 0: each peer's tiles in order; else a seeded order per peer         */
+  int32_t withhold_peer; /* test hook: this peer's tiles are copied but never signalled (-1 off)*/
+  int32_t rs_tile;       /* GEMM+RS signal tile edge (rows = cols); 0 = 128                     */
+  uint64_t* trace;       /* optional device buffer, see sgt_trace_words(); NULL = off           */
+} sgt_opts;
+
+typedef struct sgt_ctx sgt_ctx;
+
+/* Library version string, e.g. "sgt 0.1 gfx950". */
+SGT_API const char* sgt_version(void);
+
+/* Short name of a status code. */
+SGT_API const char* sgt_status_str(int status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+SGT_API const char* sgt_last_error(void);
+
+/* Fill *o with defaults: rank 0, bf16 in, fp32 out, K x N, CU producer, mesh
+ * order, unthrottled, no jitter, 2000 ms timeout, no trace. */
+SGT_API void sgt_opts_init(sgt_opts* o);
+
+/* Create a context on HIP device `device` (streams, events, status word,
+ * schedule tables).  Returns SGT_EINVAL for a bad device, SGT_EHIP/SGT_ENOMEM on
+ * runtime failure.  The context must be destroyed by sgt_ctx_destroy. */
+SGT_API sgt_status sgt_ctx_create(sgt_ctx** out, int device);
+
+/* Wait for all of the context's work and free it.  NULL is accepted. */
+SGT_API sgt_status sgt_ctx_destroy(sgt_ctx* ctx);
+
+/* Wait for the context's outstanding work and return the device status
+ * (SGT_ETIMEDOUT after an expired wait; the status is then cleared). */
+SGT_API sgt_status sgt_sync(sgt_ctx* ctx);
+
+/* Number of AllGather flags sgt_ag_gemm uses for these arguments (the size of
+ * its `flags` array), or a negative status for invalid arguments. */
+SGT_API int64_t sgt_ag_flag_count(int W, int64_t M, int64_t K, const sgt_opts* opts);
+
+/* Rows per consumer panel (the M tile) sgt_ag_gemm uses for these arguments. */
+SGT_API int32_t sgt_ag_panel_rows(int W, int64_t M, int64_t K, int64_t N, const sgt_opts* opts);
+
+/* The order in which the persistent consumer takes the row panels: writes
+ * ceil(M / panel_rows) panel indices to out (host memory).  Source: the
+ * semantics page's "Threadblock swizzle" and the paper summary's AMD full-mesh
+ * swizzle ("Method").  Returns the count or a negative status. */
+SGT_API int64_t sgt_panel_order(int W, int rank, int64_t M, int32_t panel_rows, int order, int32_t* out, int64_t cap);
+
+/*
+ * AllGather + GEMM (semantics page, "AllGather + GEMM overlap"; paper summary,
+ * "Method"):
+ *     A_gathered = rows of A_shards[0], A_shards[1], ..., A_shards[W-1]
+ *     C          = A_gathered * B          (C is M x N, fp32 or bf16)
+ * A_shards[p]: (M/W) x K device buffer of rank p (in_dtype); A_shards[rank] is
+ *     the local shard.  Shard p lands at rows [p*M/W, (p+1)*M/W) of A_gathered.
+ * B: K x N (SGT_KN) or N x K (SGT_NK), in_dtype.
+ * A_gathered: M x K, written by the producer (read-only for SGT_PROD_PRESET,
+ *     where it must already hold the gathered rows).
+ * flags: sgt_ag_flag_count() uint32 words, one per signal tile of flag_rows
+ *     rows x K; zeroed once by the caller.
+ * Requirements: 1 <= W <= 64, M % W == 0, (M/W) % flag_rows == 0, K, N >= 1;
+ *     bf16: K % 8 == 0 and N % 8 == 0; all pointers 16-byte aligned.
+ * M = 0 or N = 0 is a no-op that still advances the epoch.
+ */
+SGT_API sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B, void* A_gathered, void* C,
+                       uint32_t* flags, int W, int64_t M, int64_t K, int64_t N, const sgt_opts* opts, void* stream);
+
+/*
+ * GEMM + ReduceScatter (semantics page, "GEMM + ReduceScatter overlap"; paper
+ * summary, "Method": intra-node ReduceScatter in push mode, reduction running
+ * alongside and synchronized by signals):
+ *     P           = A_local * B              (M x N, fp32)
+ *     partial_out = P  (row block p is this rank's push to rank p; block rank is kept)
+ *     C_shard     = P[block rank] + sum over p != rank, ascending, of partials[p]
+ * The GEMM releases gflags[t] = e after storing each rs_tile x rs_tile tile t
+ * of P; the reduction of a tile of the local block waits for gflags of that
+ * tile and for pflags[p * tiles_per_block + t] of every peer p, then sums in
+ * fp32 (local block first, then peers by ascending rank).
+ * A_local: M x K (in_dtype); B: K x N or N x K (in_dtype).
+ * partials: host array of W device pointers to (M/W) x N fp32 buffers that peer
+ *     p pushed for this rank; partials[rank] is not read (may be NULL).
+ * partial_out: M x N fp32.  C_shard: (M/W) x N fp32.
+ * gflags: ceil(M/rs_tile) * ceil(N/rs_tile) words; pflags: W * (tiles of one
+ *     block) words.  The peers' flags are set by the library before the
+ *     reduction may read (pre-resident peers) or paced by the producer when
+ *     peer_gbps > 0.
+ * Requirements: as sgt_ag_gemm, and (M/W) % rs_tile == 0.
+ */
+SGT_API sgt_status sgt_gemm_rs(sgt_ctx* ctx, const void* A_local, const void* B, const float* const* partials,
+                       float* partial_out, float* C_shard, uint32_t* gflags, uint32_t* pflags, int W, int64_t M,
+                       int64_t K, int64_t N, const sgt_opts* opts, void* stream);
+
+/* Flag counts for sgt_gemm_rs: *gflags_n and *pflags_n (either may be NULL). */
+SGT_API sgt_status sgt_rs_flag_count(int W, int64_t M, int64_t N, const sgt_opts* opts, int64_t* gflags_n, int64_t* pflags_n);
+
+/*
+ * MoE AllGather + grouped GEMM (paper summary, "Experiments": MoE routing
+ * operations; DITRON article, "three-level tiling": device-level tiles whose
+ * size depends on how many tokens each expert receives):
+ *     X_gathered = rows of X_shards[0..W-1]                  (T x H bf16)
+ *     route      = top-k experts per token by descending logit (ties: lower id)
+ *     rows of Y  = (expert, token) pairs grouped by expert ascending, tokens
+ *                  ascending inside a group; expert_off[e] is the first row of e
+ *     Y[row]     = X_gathered[row_token[row]] * W_e          (fp32 or bf16)
+ * The shards arrive through the producer with one flag per shard; each grouped
+ * tile waits for the flags of the shards its rows come from.
+ * X_shards: host array of W device pointers, (T/W) x H bf16.
+ * W_experts: E x H x I (SGT_KN) or E x I x H (SGT_NK) bf16.  logits: T x E fp32.
+ * Outputs: X_gathered T x H; Y (T*topk) x I; expert_off E+1 int32;
+ *     row_token T*topk int32; topk_ids T x topk int32.
+ * shard_flags: W words.  Requirements: T % W == 0, 1 <= topk <= E <= 256,
+ *     H % 8 == 0, I % 8 == 0.
+ */
+SGT_API sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void* W_experts, const float* logits,
+                           void* X_gathered, void* Y, int32_t* expert_off, int32_t* row_token, int32_t* topk_ids,
+                           uint32_t* shard_flags, int W, int64_t T, int64_t H, int64_t I, int E, int topk,
+                           const sgt_opts* opts, void* stream);
+
+/* Words of the optional trace buffer for an AllGather call: per consumer tile
+ * 4 x uint64 {wait start, flag seen, tile end, workgroup}; then per signal tile
+ * 1 x uint64 release time.  Times are the 100 MHz constant GPU clock. */
+SGT_API int64_t sgt_trace_words(int W, int64_t M, int64_t K, int64_t N, const sgt_opts* opts);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGT_H_ */

@@ -1,0 +1,266 @@
+"""ctypes binding of libsgt (include/sgt.h): argument marshalling only.
+
+Every computation happens in the HIP library; this module checks tensor
+devices, dtypes and contiguity, passes raw device pointers, sizes and options
+through the C ABI, and turns status codes into exceptions.  PyTorch provides
+device memory and streams.  If ``libsgt.so`` is missing the calls raise; there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsgt.so")
+
+SGT_OK, SGT_EINVAL, SGT_EUNSUPPORTED, SGT_ETIMEDOUT, SGT_EHIP, SGT_ENOMEM = 0, -1, -2, -3, -4, -5
+SGT_F32, SGT_BF16 = 0, 1
+SGT_KN, SGT_NK = 0, 1
+PRODUCERS = {"cu": 0, "preset": 1, "serial": 2}
+ORDERS = {"mesh": 0, "shard": 1}
+LAYOUTS = {"kn": SGT_KN, "nk": SGT_NK}
+
+
+class SgtError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s: %s" % (_STATUS.get(status, str(status)), msg))
+        self.status = status
+
+
+_STATUS = {0: "SGT_OK", -1: "SGT_EINVAL", -2: "SGT_EUNSUPPORTED", -3: "SGT_ETIMEDOUT", -4: "SGT_EHIP",
+           -5: "SGT_ENOMEM"}
+
+
+class Opts(ctypes.Structure):
+    """Mirror of ``sgt_opts``."""
+    _fields_ = [
+        ("rank", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("b_layout", ctypes.c_int32), ("producer", ctypes.c_int32), ("order", ctypes.c_int32),
+        ("flag_rows", ctypes.c_int32), ("producer_cus", ctypes.c_int32), ("consumer_cus", ctypes.c_int32),
+        ("blocking", ctypes.c_int32), ("peer_gbps", ctypes.c_double), ("jitter_us", ctypes.c_double),
+        ("timeout_ms", ctypes.c_double), ("arrival_seed", ctypes.c_uint64), ("withhold_peer", ctypes.c_int32),
+        ("rs_tile", ctypes.c_int32), ("trace", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsgt.so (built in-tree by ``python -m signal_gated_tiled_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libsgt.so is not built (%s); run `python -m signal_gated_tiled_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        L.sgt_version.restype = ctypes.c_char_p
+        L.sgt_status_str.restype = ctypes.c_char_p
+        L.sgt_status_str.argtypes = [ctypes.c_int]
+        L.sgt_last_error.restype = ctypes.c_char_p
+        L.sgt_opts_init.argtypes = [ctypes.POINTER(Opts)]
+        L.sgt_ctx_create.argtypes = [ctypes.POINTER(P), ctypes.c_int]
+        L.sgt_ctx_destroy.argtypes = [P]
+        L.sgt_sync.argtypes = [P]
+        L.sgt_ag_flag_count.argtypes = [ctypes.c_int, I64, I64, ctypes.POINTER(Opts)]
+        L.sgt_ag_flag_count.restype = I64
+        L.sgt_ag_panel_rows.argtypes = [ctypes.c_int, I64, I64, I64, ctypes.POINTER(Opts)]
+        L.sgt_ag_panel_rows.restype = I32
+        L.sgt_panel_order.argtypes = [ctypes.c_int, ctypes.c_int, I64, I32, ctypes.c_int, P, I64]
+        L.sgt_panel_order.restype = I64
+        L.sgt_trace_words.argtypes = [ctypes.c_int, I64, I64, I64, ctypes.POINTER(Opts)]
+        L.sgt_trace_words.restype = I64
+        L.sgt_ag_gemm.argtypes = [P, P, P, P, P, P, ctypes.c_int, I64, I64, I64, ctypes.POINTER(Opts), P]
+        L.sgt_rs_flag_count.argtypes = [ctypes.c_int, I64, I64, ctypes.POINTER(Opts), ctypes.POINTER(I64),
+                                        ctypes.POINTER(I64)]
+        L.sgt_gemm_rs.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int, I64, I64, I64, ctypes.POINTER(Opts), P]
+        L.sgt_moe_ag_gemm.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_int, I64, I64, I64, ctypes.c_int,
+                                      ctypes.c_int, ctypes.POINTER(Opts), P]
+        for f in ("sgt_ctx_create", "sgt_ctx_destroy", "sgt_sync", "sgt_ag_gemm", "sgt_rs_flag_count", "sgt_gemm_rs",
+                  "sgt_moe_ag_gemm"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def version() -> str:
+    return lib().sgt_version().decode()
+
+
+def _check(status: int):
+    if status != SGT_OK:
+        raise SgtError(status, lib().sgt_last_error().decode())
+
+
+def make_opts(rank: int = 0, in_dtype: int = SGT_BF16, out_dtype: int = SGT_F32, b_layout: str = "kn",
+              producer: str = "cu", order: str = "mesh", flag_rows: int = 0, producer_cus: int = 0,
+              consumer_cus: int = 0, blocking: bool = False, peer_gbps: float = 0.0, jitter_us: float = 0.0,
+              timeout_ms: float = 2000.0, arrival_seed: int = 0, withhold_peer: int = -1, rs_tile: int = 0,
+              trace: int = 0) -> Opts:
+    o = Opts()
+    lib().sgt_opts_init(ctypes.byref(o))
+    o.rank, o.in_dtype, o.out_dtype = rank, in_dtype, out_dtype
+    o.b_layout = LAYOUTS[b_layout]
+    o.producer = PRODUCERS[producer]
+    o.order = ORDERS[order]
+    o.flag_rows, o.producer_cus, o.consumer_cus = flag_rows, producer_cus, consumer_cus
+    o.blocking = 1 if blocking else 0
+    o.peer_gbps, o.jitter_us, o.timeout_ms = float(peer_gbps), float(jitter_us), float(timeout_ms)
+    o.arrival_seed = int(arrival_seed)
+    o.withhold_peer = withhold_peer
+    o.rs_tile = rs_tile
+    o.trace = trace or None
+    return o
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SGT_BF16
+    if t.dtype == torch.float32:
+        return SGT_F32
+    raise TypeError("tensors must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _dev_ptr(t, name: str, device=None) -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    return t.data_ptr()
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def ag_flag_count(W: int, M: int, K: int, **kw) -> int:
+    o = make_opts(**kw)
+    n = lib().sgt_ag_flag_count(W, M, K, ctypes.byref(o))
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def ag_panel_rows(W: int, M: int, K: int, N: int, **kw) -> int:
+    o = make_opts(**kw)
+    return int(lib().sgt_ag_panel_rows(W, M, K, N, ctypes.byref(o)))
+
+
+def panel_order(W: int, rank: int, M: int, panel_rows: int, order: str = "mesh"):
+    n = -(-M // panel_rows)
+    buf = (ctypes.c_int32 * max(n, 1))()
+    r = lib().sgt_panel_order(W, rank, M, panel_rows, ORDERS[order], ctypes.cast(buf, P), n)
+    if r < 0:
+        _check(int(r))
+    return [int(buf[i]) for i in range(int(r))]
+
+
+def trace_words(W: int, M: int, K: int, N: int, **kw) -> int:
+    o = make_opts(**kw)
+    n = lib().sgt_trace_words(W, M, K, N, ctypes.byref(o))
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def rs_flag_count(W: int, M: int, N: int, rs_tile: int = 0):
+    o = make_opts(rs_tile=rs_tile)
+    g, p = I64(), I64()
+    _check(lib().sgt_rs_flag_count(W, M, N, ctypes.byref(o), ctypes.byref(g), ctypes.byref(p)))
+    return int(g.value), int(p.value)
+
+
+class Context:
+    """An sgt context on one device (its epoch counter, producer stream, status word)."""
+
+    def __init__(self, device: int = 0):
+        self._h = P()
+        self.device = device
+        _check(lib().sgt_ctx_create(ctypes.byref(self._h), device))
+
+    def close(self):
+        if self._h:
+            _check(lib().sgt_ctx_destroy(self._h))
+            self._h = P()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def sync(self):
+        """Wait for the context's work; raises SgtError(SGT_ETIMEDOUT) after an expired wait."""
+        _check(lib().sgt_sync(self._h))
+
+    def ag_gemm(self, A_shards: Sequence, B, A_gathered, C, flags, *, stream=None, **kw):
+        """AllGather + GEMM: A_gathered = stack(A_shards); C = A_gathered @ B (B is K x N, or N x K
+        with b_layout='nk').  Options as in sgt_opts (rank, producer, order, peer_gbps, ...)."""
+        dev = B.device
+        W = len(A_shards)
+        M = A_gathered.shape[0]
+        K = A_gathered.shape[1]
+        lay = kw.get("b_layout", "kn")
+        N = B.shape[1] if lay == "kn" else B.shape[0]
+        kw.setdefault("in_dtype", _dtype_code(B))
+        if "out_dtype" not in kw:
+            kw["out_dtype"] = _dtype_code(C) if C is not None else SGT_F32
+        o = make_opts(**kw)
+        ptrs = (P * W)(*[_dev_ptr(a, "A_shards[%d]" % i, dev) for i, a in enumerate(A_shards)])
+        _check(lib().sgt_ag_gemm(self._h, ctypes.cast(ptrs, P), _dev_ptr(B, "B", dev),
+                                 _dev_ptr(A_gathered, "A_gathered", dev), _dev_ptr(C, "C", dev),
+                                 _dev_ptr(flags, "flags", dev), W, M, K, N, ctypes.byref(o), _stream_handle(stream)))
+
+    def gemm_rs(self, A_local, B, partials: Sequence, partial_out, C_shard, gflags, pflags, *, stream=None, **kw):
+        """GEMM + ReduceScatter: partial_out = A_local @ B (fp32); C_shard = partial_out[block rank] +
+        sum of the other ranks' partials."""
+        dev = B.device
+        W = len(partials)
+        M, K = A_local.shape
+        lay = kw.get("b_layout", "kn")
+        N = B.shape[1] if lay == "kn" else B.shape[0]
+        kw.setdefault("in_dtype", _dtype_code(B))
+        o = make_opts(**kw)
+        ptrs = (P * W)(*[_dev_ptr(p, "partials[%d]" % i, dev) if p is not None else 0
+                         for i, p in enumerate(partials)])
+        _check(lib().sgt_gemm_rs(self._h, _dev_ptr(A_local, "A_local", dev), _dev_ptr(B, "B", dev),
+                                 ctypes.cast(ptrs, P), _dev_ptr(partial_out, "partial_out", dev),
+                                 _dev_ptr(C_shard, "C_shard", dev), _dev_ptr(gflags, "gflags", dev),
+                                 _dev_ptr(pflags, "pflags", dev), W, M, K, N, ctypes.byref(o),
+                                 _stream_handle(stream)))
+
+    def moe_ag_gemm(self, X_shards: Sequence, W_experts, logits, X_gathered, Y, expert_off, row_token, topk_ids,
+                    shard_flags, *, topk: int, stream=None, **kw):
+        """MoE AllGather + grouped GEMM (routing by top-k of logits, rows grouped by expert)."""
+        dev = W_experts.device
+        W = len(X_shards)
+        T, H = X_gathered.shape
+        E = W_experts.shape[0]
+        lay = kw.get("b_layout", "kn")
+        I = W_experts.shape[2] if lay == "kn" else W_experts.shape[1]
+        kw.setdefault("in_dtype", SGT_BF16)
+        if "out_dtype" not in kw:
+            kw["out_dtype"] = _dtype_code(Y)
+        o = make_opts(**kw)
+        ptrs = (P * W)(*[_dev_ptr(x, "X_shards[%d]" % i, dev) for i, x in enumerate(X_shards)])
+        _check(lib().sgt_moe_ag_gemm(self._h, ctypes.cast(ptrs, P), _dev_ptr(W_experts, "W_experts", dev),
+                                     _dev_ptr(logits, "logits", dev), _dev_ptr(X_gathered, "X_gathered", dev),
+                                     _dev_ptr(Y, "Y", dev), _dev_ptr(expert_off, "expert_off", dev),
+                                     _dev_ptr(row_token, "row_token", dev), _dev_ptr(topk_ids, "topk_ids", dev),
+                                     _dev_ptr(shard_flags, "shard_flags", dev), W, T, H, I, E, topk,
+                                     ctypes.byref(o), _stream_handle(stream)))

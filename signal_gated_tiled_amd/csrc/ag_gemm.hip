@@ -1,0 +1,168 @@
+// AllGather + GEMM consumer: a persistent GEMM that waits on each row panel's
+// flags before reading it (Triton-distributed semantics page, "AllGather + GEMM
+// overlap": the consumer waits for each tile, then computes it at once;
+// "Threadblock swizzle": start on local data; paper summary, "Method": the GEMM
+// gains wait + consume_token before its loads, and AMD persistent kernels).
+//
+// Two kernels share the schedule and the wait:
+//  * ag_consumer_bf16: bf16 inputs on the matrix cores (mfma_tile.hpp), 256 x 256
+//    tiles, one workgroup per CU.
+//  * ag_consumer_f32: fp32 inputs with fp32 FMAs (64 x 64 tiles), for fp32
+//    workloads where a bf16 downcast would lose the required accuracy.
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+#include "mfma_tile.hpp"
+#include "sched.hpp"
+#include "signal.hpp"
+
+namespace sgt {
+
+namespace {
+
+// Wait for the flags covering rows [m0, m1) and record trace stamps.
+__device__ __forceinline__ bool gate_rows(const AgArgs& a, int64_t m0, int64_t m1, int* ok, int64_t tile_id,
+                                          uint64_t* t_wait) {
+  if (threadIdx.x == 0) *t_wait = clock_ticks();
+  const int64_t f0 = m0 / a.flag_rows, f1 = (m1 - 1) / a.flag_rows + 1;
+  const bool good = wait_flags_block(a.flags, f0, f1, a.epoch, a.timeout_ticks, a.status, ok);
+  if (a.trace && threadIdx.x == 0) {
+    a.trace[tile_id * 4 + 0] = *t_wait;
+    a.trace[tile_id * 4 + 1] = clock_ticks();
+    a.trace[tile_id * 4 + 3] = blockIdx.x;
+  }
+  return good;
+}
+
+template <bool kBNK, bool kOutBf16>
+__global__ void __launch_bounds__(kThreads, 1) ag_consumer_bf16(AgArgs a) {
+  __shared__ int ok;
+  __shared__ uint64_t t_wait;
+  const int total = a.tiles_m * a.tiles_n;
+  const int G = gridDim.x;
+  const uint16_t* A = static_cast<const uint16_t*>(a.A);
+  const uint16_t* B = static_cast<const uint16_t*>(a.B);
+  for (int t = xcd_remap(blockIdx.x, G); t < total; t += G) {
+    const int pn = t % a.tiles_n;
+    const int pm = (int)panel_at(t / a.tiles_n, a.tiles_m, a.rows_per_shard, kBM, a.W, a.rank, a.order);
+    const int64_t m0 = (int64_t)pm * kBM, n0 = (int64_t)pn * kBN;
+    const int64_t m1 = m0 + kBM < a.M ? m0 + kBM : a.M;
+    const int64_t tile_id = (int64_t)pm * a.tiles_n + pn;
+    if (!gate_rows(a, m0, m1, &ok, tile_id, &t_wait)) return;
+
+    const KRows ka = krows_strided(A + m0 * a.K, a.M - m0, a.K);
+    KRows kb;
+    if constexpr (kBNK) kb = krows_strided(B + n0 * a.K, a.N - n0, a.K);
+    MfmaAcc acc;
+    gemm_tile<kBNK>(ka, kb, B, a.N, n0, a.K, acc);
+    store_tile<kOutBf16>(a.C, a.M, a.N, m0, n0, acc);
+    if (a.trace && threadIdx.x == 0) a.trace[tile_id * 4 + 2] = clock_ticks();
+  }
+}
+
+// fp32 path: 64 x 64 tiles, BK = 16, each thread a 4 x 4 block of outputs.
+constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 16;
+
+__global__ void __launch_bounds__(256) ag_consumer_f32(AgArgs a) {
+  __shared__ float As[kF32BK][kF32BM + 4];
+  __shared__ float Bs[kF32BK][kF32BN + 4];
+  __shared__ int ok;
+  __shared__ uint64_t t_wait;
+  const float* A = static_cast<const float*>(a.A);
+  const float* B = static_cast<const float*>(a.B);
+  const int total = a.tiles_m * a.tiles_n;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int G = gridDim.x;
+  for (int t = xcd_remap(blockIdx.x, G); t < total; t += G) {
+    const int64_t pn = t % a.tiles_n;
+    const int64_t pm = panel_at(t / a.tiles_n, a.tiles_m, a.rows_per_shard, kF32BM, a.W, a.rank, a.order);
+    const int64_t m0 = pm * kF32BM, n0 = pn * kF32BN;
+    const int64_t m1 = m0 + kF32BM < a.M ? m0 + kF32BM : a.M;
+    const int64_t tile_id = pm * a.tiles_n + pn;
+    if (!gate_rows(a, m0, m1, &ok, tile_id, &t_wait)) return;
+
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+
+    for (int64_t k0 = 0; k0 < a.K; k0 += kF32BK) {
+      {  // A tile: row tid / 4, k (tid % 4) * 4 + u
+        const int r = tid >> 2, kq = (tid & 3) * 4;
+        const int64_t m = m0 + r;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t k = k0 + kq + u;
+          As[kq + u][r] = (m < a.M && k < a.K) ? A[m * a.K + k] : 0.f;
+        }
+      }
+      if (a.b_layout == 0) {  // K x N: k tid / 16, n (tid % 16) * 4 + u
+        const int kk = tid >> 4, nq = (tid & 15) * 4;
+        const int64_t k = k0 + kk;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t n = n0 + nq + u;
+          Bs[kk][nq + u] = (k < a.K && n < a.N) ? B[k * a.N + n] : 0.f;
+        }
+      } else {  // N x K: n tid / 4, k (tid % 4) * 4 + u
+        const int nn = tid >> 2, kq = (tid & 3) * 4;
+        const int64_t n = n0 + nn;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t k = k0 + kq + u;
+          Bs[kq + u][nn] = (k < a.K && n < a.N) ? B[n * a.K + k] : 0.f;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < kF32BK; ++kk) {
+        float av[4], bv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + ty * 4 + i;
+      if (m >= a.M) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t n = n0 + tx * 4 + j;
+        if (n >= a.N) continue;
+        if (a.out_dtype == 0)
+          static_cast<float*>(a.C)[m * a.N + n] = acc[i][j];
+        else
+          static_cast<uint16_t*>(a.C)[m * a.N + n] = f32_to_bf16_rne(acc[i][j]);
+      }
+    }
+    if (a.trace && threadIdx.x == 0) a.trace[tile_id * 4 + 2] = clock_ticks();
+  }
+}
+
+}  // namespace
+
+int ag_panel_rows(int in_dtype) { return in_dtype == 1 ? kBM : kF32BM; }
+int ag_panel_cols(int in_dtype) { return in_dtype == 1 ? kBN : kF32BN; }
+
+hipError_t launch_ag_consumer(const AgArgs& a, int in_dtype, int grid, hipStream_t stream) {
+  if (in_dtype == 1) {
+    const bool nk = a.b_layout == 1, ob = a.out_dtype == 1;
+    if (nk && ob) hipLaunchKernelGGL((ag_consumer_bf16<true, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    if (nk && !ob) hipLaunchKernelGGL((ag_consumer_bf16<true, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+    if (!nk && ob) hipLaunchKernelGGL((ag_consumer_bf16<false, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    if (!nk && !ob) hipLaunchKernelGGL((ag_consumer_bf16<false, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(ag_consumer_f32, dim3(grid), dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sgt

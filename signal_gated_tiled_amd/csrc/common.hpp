@@ -1,0 +1,69 @@
+// Internal types shared by the host runtime and the kernels of libsgt.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgt {
+
+constexpr int kMaxW = 64;
+
+// Device status word written by a kernel whose bounded wait expired.
+// status[0] = code (0 ok, 3 timeout), [1] = flag index, [2] = value seen, [3] = value expected.
+constexpr uint32_t kStatusTimeout = 3;
+
+struct PtrTable {
+  const void* p[kMaxW];
+};
+
+// One AllGather producer work item: copy signal tile `tile` of the gathered
+// matrix, then release its flag no earlier than `release` clock ticks after the
+// producer workgroup started.
+struct ProdItem {
+  uint32_t tile;
+  uint32_t peer;
+  uint64_t release;
+};
+
+// Arguments of the AllGather consumer (both the bf16 MFMA and fp32 kernels).
+struct AgArgs {
+  const void* A;          // gathered M x K
+  const void* B;          // K x N or N x K
+  void* C;                // M x N
+  const uint32_t* flags;  // one per signal tile
+  uint32_t* status;
+  uint64_t* trace;        // optional: 4 words per consumer tile
+  int64_t M, N, K;
+  int64_t rows_per_shard;
+  int32_t flag_rows;
+  int32_t W, rank, order;
+  int32_t tiles_m, tiles_n;
+  int32_t b_layout, out_dtype;
+  uint32_t epoch;
+  uint32_t pad;
+  uint64_t timeout_ticks;
+};
+
+// Arguments of the GEMM+ReduceScatter kernel.
+struct RsArgs {
+  const void* A;            // A_local M x K
+  const void* B;            // K x N or N x K
+  float* P;                 // partial_out M x N fp32
+  float* C_shard;           // (M/W) x N
+  PtrTable partials;        // W pointers, (M/W) x N fp32
+  uint32_t* gflags;         // per rs_tile^2 tile of P
+  const uint32_t* pflags;   // W x tiles of one block
+  uint32_t* status;
+  int64_t M, N, K;
+  int64_t block_rows;       // M / W
+  int32_t W, rank;
+  int32_t tiles_m, tiles_n; // GEMM tiles
+  int32_t rs_tile;          // signal tile edge
+  int32_t rs_tm, rs_tn;     // signal tiles of one block (rows, cols)
+  int32_t b_layout;
+  int32_t n_gemm_tiles, n_red_items;
+  uint32_t epoch;
+  uint64_t timeout_ticks;
+};
+
+}  // namespace sgt

@@ -1,0 +1,133 @@
+// GEMM + ReduceScatter (Triton-distributed semantics page, "GEMM +
+// ReduceScatter overlap": the GEMM produces output tiles and signals each one;
+// the ReduceScatter consumer waits for a tile and reduces it; paper summary,
+// "Method": intra-node ReduceScatter in push mode, the reduction running in
+// parallel and synchronized by signals).
+//
+// One persistent kernel holds both roles.  Its work list is
+//   [0, n_gemm)            GEMM tiles of P = A_local * B, row block `rank`
+//                          first, then rank+1, rank+2, ... (start from local
+//                          data); each stores its fp32 tile and releases the
+//                          flags of the rs_tile x rs_tile signal tiles it covers;
+//   [n_gemm, n_gemm+n_red) reduction items, one per signal tile of the local
+//                          block: wait for the GEMM flag and the W-1 peer flags,
+//                          then C_shard = P[local] + sum of peer partials
+//                          (fixed order: local, then peers by ascending rank).
+// The reduction items land in the workgroups left idle by the last, partial
+// round of GEMM tiles.  Dependencies only point from reduction to GEMM, and a
+// workgroup never waits on a later item of its own, so the kernel cannot
+// deadlock; every wait is still bounded.
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+#include "mfma_tile.hpp"
+#include "sched.hpp"
+#include "signal.hpp"
+
+namespace sgt {
+
+namespace {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// GEMM m-tiles never straddle row blocks: block b holds tm_b = ceil(block_rows / 256)
+// m-tiles, the last one possibly short.
+__device__ __forceinline__ void gemm_tile_coords(const RsArgs& a, int t, int64_t* m0, int64_t* m_end, int64_t* n0) {
+  const int tm_b = (int)((a.block_rows + kBM - 1) / kBM);
+  const int per_block = tm_b * a.tiles_n;
+  const int bi = t / per_block, rem = t % per_block;
+  const int blk = (a.rank + bi) % a.W;
+  const int mi = rem / a.tiles_n, ni = rem % a.tiles_n;
+  *m0 = (int64_t)blk * a.block_rows + (int64_t)mi * kBM;
+  const int64_t blk_end = (int64_t)(blk + 1) * a.block_rows;
+  *m_end = *m0 + kBM < blk_end ? *m0 + kBM : blk_end;
+  *n0 = (int64_t)ni * kBN;
+}
+
+template <bool kBNK>
+__device__ void do_gemm_item(const RsArgs& a, int t) {
+  int64_t m0, m_end, n0;
+  gemm_tile_coords(a, t, &m0, &m_end, &n0);
+  const uint16_t* A = static_cast<const uint16_t*>(a.A);
+  const uint16_t* B = static_cast<const uint16_t*>(a.B);
+  const KRows ka = krows_strided(A + m0 * a.K, m_end - m0, a.K);
+  KRows kb;
+  if constexpr (kBNK) kb = krows_strided(B + n0 * a.K, a.N - n0, a.K);
+  MfmaAcc acc;
+  gemm_tile<kBNK>(ka, kb, B, a.N, n0, a.K, acc);
+  // rows past m_end belong to the next block's tile: clip to m_end
+  store_tile<false>(a.P, m_end, a.N, m0, n0, acc);
+  // release the covered signal tiles (rs_tile divides 256 and the block rows)
+  const int64_t n_end = n0 + kBN < a.N ? n0 + kBN : a.N;
+  const int64_t gtn = (a.N + a.rs_tile - 1) / a.rs_tile;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    for (int64_t mi = m0 / a.rs_tile; mi <= (m_end - 1) / a.rs_tile; ++mi)
+      for (int64_t nj = n0 / a.rs_tile; nj <= (n_end - 1) / a.rs_tile; ++nj)
+        flag_release(a.gflags + mi * gtn + nj, a.epoch);
+}
+
+__device__ void do_reduce_item(const RsArgs& a, int j, int* ok) {
+  const int ti = j / a.rs_tn, tj = j % a.rs_tn;
+  const int64_t gtn = (a.N + a.rs_tile - 1) / a.rs_tile;
+  const int64_t row0 = (int64_t)a.rank * a.block_rows + (int64_t)ti * a.rs_tile;  // row in P
+  if (threadIdx.x == 0) {
+    bool good = wait_flags_one_thread(a.gflags, (row0 / a.rs_tile) * gtn + tj, (row0 / a.rs_tile) * gtn + tj + 1,
+                                      a.epoch, a.timeout_ticks, a.status);
+    const int64_t per = (int64_t)a.rs_tm * a.rs_tn;
+    for (int p = 0; p < a.W && good; ++p)
+      if (p != a.rank)
+        good = wait_flags_one_thread(a.pflags, p * per + j, p * per + j + 1, a.epoch, a.timeout_ticks, a.status);
+    *ok = good ? 1 : 0;
+  }
+  __syncthreads();
+  if (!*ok) return;
+  // float4 columns: rs_tile / 4 per row; 256 threads cover 1024 / rs_tile rows per pass
+  const int cols4 = a.rs_tile / 4;
+  const int rows_per_pass = kThreads / cols4;
+  const int c4 = threadIdx.x % cols4, rr = threadIdx.x / cols4;
+  const int64_t col = (int64_t)tj * a.rs_tile + 4 * c4;
+  if (col >= a.N) return;  // N % 4 == 0: a float4 is either fully in or out
+  for (int r = rr; r < a.rs_tile; r += rows_per_pass) {
+    const int64_t brow = (int64_t)ti * a.rs_tile + r;  // row inside the block
+    f32x4_t s = *reinterpret_cast<const f32x4_t*>(a.P + (row0 + r) * a.N + col);
+#pragma unroll 8
+    for (int p = 0; p < a.W; ++p) {
+      if (p == a.rank) continue;
+      s += __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.partials.p[p]) + brow * a.N + col));
+    }
+    __builtin_nontemporal_store(s, reinterpret_cast<f32x4_t*>(a.C_shard + brow * a.N + col));
+  }
+}
+
+template <bool kBNK>
+__global__ void __launch_bounds__(kThreads, 1) gemm_rs_kernel(RsArgs a) {
+  __shared__ int ok;
+  const int total = a.n_gemm_tiles + a.n_red_items;
+  const int G = gridDim.x;
+  for (int t = xcd_remap(blockIdx.x, G); t < total; t += G) {
+    if (t < a.n_gemm_tiles) {
+      do_gemm_item<kBNK>(a, t);
+    } else {
+      do_reduce_item(a, t - a.n_gemm_tiles, &ok);
+      if (!ok) return;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+int rs_gemm_tile() { return kBM; }
+
+hipError_t launch_gemm_rs(const RsArgs& a, int grid, hipStream_t stream) {
+  if (a.b_layout == 1)
+    hipLaunchKernelGGL(gemm_rs_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(gemm_rs_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace sgt

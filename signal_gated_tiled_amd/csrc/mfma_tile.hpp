@@ -1,0 +1,283 @@
+// bf16 x bf16 -> fp32 tile GEMM on CDNA4 matrix cores, shared by the
+// AllGather, GEMM+ReduceScatter and MoE consumers.
+//
+// One workgroup = 256 threads = 4 wave64s in a 2 x 2 grid; it computes a
+// 256 x 256 fp32 tile C[m0:m0+256, n0:n0+256] = A[rows, :] * B[:, n0:n0+256]
+// with v_mfma_f32_32x32x16_bf16 (each wave: 4 x 4 MFMA blocks of 32 x 32, i.e.
+// 128 x 128 outputs held in 256 accumulator registers per lane).
+//
+// K loop: BK = 64, two LDS stages of 64 KiB, one barrier per K step.  Operands
+// whose k index is contiguous in memory (A, and B stored N x K) go straight
+// from HBM to LDS with buffer_load_dwordx4 ... lds (no register staging); B
+// stored K x N is loaded to registers in 8 x 8 blocks, transposed there and
+// written to LDS, so LDS always holds [row][k].  The next step's loads are in
+// flight while the current step's 64 MFMAs per wave run.
+//
+// LDS layout of a stage, both operands: [256 rows][64 k] bf16 = 128 bytes per
+// row = 8 chunks of 16 bytes; chunk c of row r is stored at chunk
+// c ^ (r & 7) ^ ((r >> 3) & 3).  The MFMA operand reads (8 consecutive rows,
+// one chunk) hit distinct banks, and since the swizzle only uses row bits 0..4
+// the reads of the four 32-row MFMA blocks differ by a constant (an immediate
+// offset).  The DMA writes whole 1 KiB runs; the K x N loader's transposed
+// writes see at most a 2-way conflict.
+//
+// Tails: 32-bit buffer offsets from a per-tile base; rows past the end of the
+// matrix fall outside the buffer's record range and read as zero, and chunks
+// past K (or columns past N) get an out-of-range offset.  The hardware range
+// check covers the VGPR offset only, so every offset is passed there.  K % 8 == 0 and
+// N % 8 == 0 are required (whole 16-byte chunks).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgt {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 256;
+constexpr int kStageBytes = kBM * kBK * 2;          // one operand, one stage: 32 KiB
+constexpr uint32_t kOOB = 0x80000000u;              // buffer offset that reads 0 / drops a store
+constexpr int kRsrcWord3 = 0x00020000;              // raw buffer, 32-bit data format (gfx9)
+
+__device__ __forceinline__ int lds_swz(int row, int chunk) {
+  return row * 128 + ((chunk ^ (row & 7) ^ ((row >> 3) & 3)) << 4);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcWord3);
+}
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+struct MfmaAcc {
+  f32x16_t v[4][4];
+};
+
+__device__ __forceinline__ void acc_zero(MfmaAcc& acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc.v[i][j][r] = 0.f;
+}
+
+// A k-contiguous operand tile (A, or B stored N x K) seen by the DMA loader:
+// a buffer resource whose record range ends after the last valid row (later
+// rows read as zero), and the byte offset of the row this lane fills for each
+// of its 8 loads (rows `ld` elements apart, or gathered rows for MoE).
+struct KRows {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t lane_off[8];   // byte offset of this lane's row for load i (before the chunk)
+};
+
+// Lane l of wave w, load i (0..7) fills LDS row r = 64 w + 8 i + l / 8,
+// physical chunk l % 8, which holds logical chunk (l % 8) ^ swz(r).
+__device__ __forceinline__ int dma_row(int w, int i, int lane) { return 64 * w + 8 * i + (lane >> 3); }
+__device__ __forceinline__ int dma_chunk(int i, int lane) { return (lane & 7) ^ (lane >> 3) ^ (i & 3); }
+
+// Strided rows: row r at element offset r * ld from base; rows >= rows_valid are zero.
+__device__ __forceinline__ KRows krows_strided(const uint16_t* base, int64_t rows_valid, int64_t ld) {
+  KRows kr;
+  const int64_t rows = rows_valid < kBM ? rows_valid : kBM;
+  kr.rsrc = make_rsrc(base, rows > 0 ? (uint64_t)rows * (uint64_t)ld * 2u : 0u);
+  const int w = wave_id(), lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) kr.lane_off[i] = (uint32_t)(dma_row(w, i, lane) * ld * 2);
+  return kr;
+}
+
+// Issue the DMA of K step [k0, k0 + 64) of a k-contiguous operand into `stage`.
+__device__ __forceinline__ void dma_stage(const KRows& kr, uint8_t* stage, int64_t k0, int64_t K) {
+  const int w = wave_id(), lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = dma_chunk(i, lane);
+    const int64_t k = k0 + 8 * c;
+    const uint32_t off = k < K ? kr.lane_off[i] + (uint32_t)(k * 2) : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr.rsrc, (lds_ptr_t)(stage + (w * 8 + i) * 1024), 16, off, 0, 0, 0);
+  }
+}
+
+// B stored K x N: registers, transpose, LDS.
+struct KNLoader {
+  __amdgpu_buffer_rsrc_t rsrc;  // whole of B
+  uint32_t lane_off;            // (8 kg * N + n0 + 8 ng) * 2, or kOOB when the columns are past N
+  int64_t row_bytes;            // N * 2
+  u32x4_t gb[8];
+
+  __device__ __forceinline__ void init(const uint16_t* B, int64_t K, int64_t N, int64_t n0) {
+    rsrc = make_rsrc(B, (uint64_t)K * (uint64_t)N * 2u);
+    const int t = threadIdx.x, ng = t & 31, kg = t >> 5;
+    row_bytes = N * 2;
+    lane_off = (n0 + 8 * ng < N) ? (uint32_t)((8 * kg) * row_bytes + (n0 + 8 * ng) * 2) : kOOB;
+  }
+  __device__ __forceinline__ void load(int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // the range check ignores soffset, so the whole offset goes in voffset
+      const uint32_t off = lane_off == kOOB ? kOOB : lane_off + (uint32_t)((k0 + i) * row_bytes);
+      gb[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+    }
+  }
+  // gb[i] holds B[k0 + 8kg + i][n0 + 8ng + 0..7]; column j of this 8 x 8 block,
+  // k ascending, becomes LDS row 8 ng + j, chunk kg.
+  __device__ __forceinline__ void store(uint8_t* sB) const {
+    const int t = threadIdx.x, ng = t & 31, kg = t >> 5;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x4_t col;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = gb[2 * q][j >> 1], hi = gb[2 * q + 1][j >> 1];
+        col[q] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+      }
+      *reinterpret_cast<u32x4_t*>(sB + lds_swz(8 * ng + j, kg)) = col;
+    }
+  }
+};
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ void read_frags(const uint8_t* sA, const uint8_t* sB, int kk, bf16x8_t (&a)[4],
+                                           bf16x8_t (&b)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, chunk = 2 * kk + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    a[i] = *reinterpret_cast<const bf16x8_t*>(sA + lds_swz(wm * 128 + i * 32 + lr, chunk));
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    b[j] = *reinterpret_cast<const bf16x8_t*>(sB + lds_swz(wn * 128 + j * 32 + lr, chunk));
+}
+
+// 64 MFMAs of one wave on one LDS stage; the fragments of k-substep kk + 1 are
+// read while the 16 MFMAs of substep kk run.
+__device__ __forceinline__ void mfma_stage(const uint8_t* sA, const uint8_t* sB, MfmaAcc& acc) {
+  bf16x8_t a[2][4], b[2][4];
+  read_frags(sA, sB, 0, a[0], b[0]);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    if (kk < 3) read_frags(sA, sB, kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][i], b[kk & 1][j], acc.v[i][j], 0, 0, 0);
+  }
+}
+
+// Full K loop for one 256 x 256 tile.  A is k-contiguous (DMA); B is N x K
+// (kBNK, DMA) or K x N (register transpose).  The two stages are distinct LDS
+// objects and the loop is unrolled by two, so the compiler can see that a DMA
+// into one stage never aliases the MFMA reads of the other and does not wait
+// for it.  The caller must have passed a barrier since the previous use.
+template <bool kBNK>
+__device__ __forceinline__ void gemm_tile(const KRows& ka, const KRows& kb_nk, const uint16_t* B_kn, int64_t N,
+                                          int64_t n0, int64_t K, MfmaAcc& acc) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[kStageBytes];
+  acc_zero(acc);
+  const int64_t nk = (K + kBK - 1) / kBK;
+  KNLoader kn;
+  if constexpr (!kBNK) {
+    kn.init(B_kn, K, N, n0);
+    kn.load(0);
+  }
+  dma_stage(ka, sA0, 0, K);
+  if constexpr (kBNK) dma_stage(kb_nk, sB0, 0, K);
+  else kn.store(sB0);
+  wait_dma();
+  __syncthreads();
+  // Pairs of K steps: stage 0 computes while stage 1 fills, then the reverse.
+  // (A loop exit between the two halves would split the accumulators' live
+  // ranges; the odd last step is peeled instead.)
+  const int64_t nk2 = nk & ~int64_t(1);
+  for (int64_t kt = 0; kt < nk2; kt += 2) {
+    dma_stage(ka, sA1, (kt + 1) * kBK, K);
+    if constexpr (kBNK) dma_stage(kb_nk, sB1, (kt + 1) * kBK, K);
+    else kn.load((kt + 1) * kBK);
+    mfma_stage(sA0, sB0, acc);
+    if constexpr (!kBNK) kn.store(sB1);
+    wait_dma();
+    __syncthreads();
+    const bool more = kt + 2 < nk;
+    if (more) {
+      dma_stage(ka, sA0, (kt + 2) * kBK, K);
+      if constexpr (kBNK) dma_stage(kb_nk, sB0, (kt + 2) * kBK, K);
+      else kn.load((kt + 2) * kBK);
+    }
+    mfma_stage(sA1, sB1, acc);
+    if constexpr (!kBNK)
+      if (more) kn.store(sB0);
+    wait_dma();
+    __syncthreads();
+  }
+  if (nk & 1) {  // the last K step sits in stage 0
+    mfma_stage(sA0, sB0, acc);
+    __syncthreads();
+  }
+}
+
+// Accumulator (i, j, r) of this lane sits at tile row acc_row(i, r), column acc_col(j):
+// the 32 x 32 MFMA result puts column lane % 32 in a lane and rows
+// 8 (r / 4) + 4 (lane / 32) + r % 4 in its 16 registers.
+__device__ __forceinline__ int acc_row(int i, int r) {
+  const int lane = threadIdx.x & 63;
+  return (wave_id() >> 1) * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+__device__ __forceinline__ int acc_col(int j) {
+  const int lane = threadIdx.x & 63;
+  return (wave_id() & 1) * 128 + j * 32 + (lane & 31);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Store the tile to a row-major M x N output (ldc = N) at (m0, n0); elements
+// outside the matrix are dropped.  kOutBf16: round to bf16, else fp32.
+template <bool kOutBf16>
+__device__ __forceinline__ void store_tile(void* C, int64_t M, int64_t N, int64_t m0, int64_t n0, const MfmaAcc& acc) {
+  const int esz = kOutBf16 ? 2 : 4;
+  const uint8_t* base = static_cast<const uint8_t*>(C) + (m0 * N + n0) * esz;
+  // Record range: from the tile origin to the end of its last valid row (at most
+  // 256 rows, < 2^31 bytes), so an offset of kOOB or more is always dropped.
+  const int64_t rows = M - m0 < kBM ? M - m0 : kBM;
+  const int64_t valid = rows * N - n0;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, valid > 0 ? (uint64_t)valid * esz : 0u);
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int lr = lane & 31, lk = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int col = (w & 1) * 128 + j * 32 + lr;
+    const uint32_t voff = (n0 + col < N) ? (uint32_t)((4 * lk * N + col) * esz) : kOOB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = (w >> 1) * 128 + i * 32 + 8 * (r >> 2) + (r & 3);  // + 4 lk in voff
+        // kOOB + (row offset < 2^31) stays out of range: no select needed
+        const uint32_t off = voff + (uint32_t)(row * N * esz);
+        if constexpr (kOutBf16)
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(acc.v[i][j][r]), rs, off, 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b32(acc.v[i][j][r], rs, off, 0, 0);
+      }
+  }
+}
+
+}  // namespace sgt

@@ -1,0 +1,529 @@
+// Host runtime of libsgt: context, validation, epochs, the producer schedule
+// and the stream choreography of each call (declared in include/sgt.h).
+//
+// Streams (paper summary, "Method": communication and computation are
+// launched on different streams so they run concurrently):
+//   caller's stream  -- consumer kernel (and everything in serial mode)
+//   ctx->prod        -- producer kernel; forked from and joined back into the
+//                       caller's stream with events, so calls stay ordered.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/sgt.h"
+#include "common.hpp"
+#include "sched.hpp"
+
+namespace sgt {
+hipError_t launch_ag_producer(const PtrTable& shards, void* gathered, uint32_t* flags, const ProdItem* items,
+                              int n_items, int64_t tile_bytes, int tiles_per_shard, uint32_t epoch,
+                              int withhold_peer, uint64_t* trace_release, int grid, hipStream_t stream);
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
+hipError_t launch_ag_consumer(const AgArgs& a, int in_dtype, int grid, hipStream_t stream);
+int ag_panel_rows(int in_dtype);
+int ag_panel_cols(int in_dtype);
+hipError_t launch_gemm_rs(const RsArgs& a, int grid, hipStream_t stream);
+int rs_gemm_tile();
+inline int kBMrs() { return rs_gemm_tile(); }
+}  // namespace sgt
+
+using namespace sgt;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sgt_status fail(sgt_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+#define HIP_TRY(expr)                                                                            \
+  do {                                                                                           \
+    hipError_t e_ = (expr);                                                                      \
+    if (e_ != hipSuccess) return fail(SGT_EHIP, "%s: %s (%s:%d)", #expr, hipGetErrorString(e_), \
+                                      __FILE__, __LINE__);                                       \
+  } while (0)
+
+constexpr int kSlots = 4;                 // producer schedule tables in flight
+constexpr int64_t kItemsCap = 1 << 18;    // signal tiles per call
+constexpr double kTicksPerUs = 100.0;     // constant GPU clock: 100 MHz
+
+}  // namespace
+
+struct sgt_ctx {
+  int device = 0;
+  int n_cu = 0;
+  hipStream_t prod = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  uint32_t epoch = 0;
+  uint32_t* d_status = nullptr;  // 4 words
+  ProdItem* h_items[kSlots] = {};
+  ProdItem* d_items[kSlots] = {};
+  hipEvent_t slot_ev[kSlots] = {};
+  bool slot_used[kSlots] = {};
+  int slot = 0;
+  std::mutex mu;
+};
+
+namespace {
+
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) (void)hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(int dtype) { return dtype == SGT_BF16 ? 2 : 4; }
+
+uint64_t timeout_ticks(const sgt_opts& o) {
+  const double ms = o.timeout_ms > 0 ? o.timeout_ms : 2000.0;
+  return (uint64_t)(ms * 1000.0 * kTicksPerUs);
+}
+
+// SplitMix64 (Steele, Lea and Flood, 2014): seeded arrival orders and jitter.
+uint64_t splitmix64(uint64_t& s) {
+  uint64_t z = (s += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Default rows per AllGather signal tile: about 512 KiB per tile (so a link
+// delivers one every few microseconds), a divisor of the shard's rows, and no
+// more than the consumer panel.
+int64_t default_flag_rows(int64_t rows_per_shard, int64_t K, int esz, int panel) {
+  int64_t target = std::max<int64_t>(1, (512 * 1024) / std::max<int64_t>(1, K * esz));
+  target = std::min<int64_t>(target, panel);
+  for (int64_t fr = std::min(target, rows_per_shard); fr > 1; --fr)
+    if (rows_per_shard % fr == 0) return fr;
+  return 1;
+}
+
+sgt_status check_opts(const sgt_opts* o, int W) {
+  if (!o) return fail(SGT_EINVAL, "opts is NULL");
+  if (o->rank < 0 || o->rank >= W) return fail(SGT_EINVAL, "rank %d outside [0, %d)", o->rank, W);
+  if (o->in_dtype != SGT_F32 && o->in_dtype != SGT_BF16) return fail(SGT_EINVAL, "in_dtype %d", o->in_dtype);
+  if (o->out_dtype != SGT_F32 && o->out_dtype != SGT_BF16) return fail(SGT_EINVAL, "out_dtype %d", o->out_dtype);
+  if (o->b_layout != SGT_KN && o->b_layout != SGT_NK) return fail(SGT_EINVAL, "b_layout %d", o->b_layout);
+  if (o->producer < SGT_PROD_CU || o->producer > SGT_PROD_SERIAL) return fail(SGT_EINVAL, "producer %d", o->producer);
+  if (o->order != SGT_ORDER_MESH && o->order != SGT_ORDER_SHARD) return fail(SGT_EINVAL, "order %d", o->order);
+  if (o->flag_rows < 0 || o->producer_cus < 0 || o->consumer_cus < 0) return fail(SGT_EINVAL, "negative count");
+  if (!(o->peer_gbps >= 0) || !(o->jitter_us >= 0) || !(o->timeout_ms >= 0))
+    return fail(SGT_EINVAL, "negative or NaN rate/jitter/timeout");
+  if (o->rs_tile < 0) return fail(SGT_EINVAL, "rs_tile %d", o->rs_tile);
+  return SGT_OK;
+}
+
+struct AgPlan {
+  int64_t rows_per_shard, flag_rows, n_flags, tiles_per_shard;
+  int panel_rows, panel_cols, tiles_m, tiles_n;
+};
+
+sgt_status plan_ag(int W, int64_t M, int64_t K, int64_t N, const sgt_opts& o, AgPlan* p) {
+  if (W < 1 || W > kMaxW) return fail(SGT_EINVAL, "W = %d outside [1, %d]", W, kMaxW);
+  if (M < 0 || N < 0 || K < 1) return fail(SGT_EINVAL, "bad shape M=%lld K=%lld N=%lld", (long long)M,
+                                           (long long)K, (long long)N);
+  if (M % W) return fail(SGT_EINVAL, "M = %lld is not a multiple of W = %d", (long long)M, W);
+  if (o.in_dtype == SGT_BF16 && (K % 8 || N % 8))
+    return fail(SGT_EINVAL, "bf16 needs K %% 8 == 0 and N %% 8 == 0 (K=%lld N=%lld)", (long long)K, (long long)N);
+  const int esz = elem_bytes(o.in_dtype);
+  p->rows_per_shard = M / W;
+  p->panel_rows = ag_panel_rows(o.in_dtype);
+  p->panel_cols = ag_panel_cols(o.in_dtype);
+  if (o.flag_rows > 0) {
+    p->flag_rows = o.flag_rows;
+  } else {
+    p->flag_rows = p->rows_per_shard > 0 ? default_flag_rows(p->rows_per_shard, K, esz, p->panel_rows) : 1;
+  }
+  if (p->rows_per_shard % p->flag_rows)
+    return fail(SGT_EINVAL, "rows per shard %lld not a multiple of flag_rows %lld", (long long)p->rows_per_shard,
+                (long long)p->flag_rows);
+  p->n_flags = M / p->flag_rows;
+  if (p->n_flags > kItemsCap) return fail(SGT_EINVAL, "%lld signal tiles exceed %lld", (long long)p->n_flags,
+                                          (long long)kItemsCap);
+  p->tiles_per_shard = p->rows_per_shard / p->flag_rows;
+  const int64_t tm = (M + p->panel_rows - 1) / p->panel_rows, tn = (N + p->panel_cols - 1) / p->panel_cols;
+  if (tm * tn > (int64_t)1 << 30) return fail(SGT_EINVAL, "too many tiles");
+  p->tiles_m = (int)tm;
+  p->tiles_n = (int)tn;
+  // 32-bit buffer offsets inside a tile and across K x N
+  if ((int64_t)p->panel_rows * K * esz >= ((int64_t)1 << 31) || (int64_t)p->panel_rows * N * 4 >= ((int64_t)1 << 31))
+    return fail(SGT_EUNSUPPORTED, "K or N too large for 32-bit tile offsets");
+  // B stored K x N is addressed as one buffer: its size must stay below the
+  // out-of-range offset 2^31 so masked lanes always read zero.
+  if (o.in_dtype == SGT_BF16 && o.b_layout == SGT_KN && K * N * 2 >= ((int64_t)1 << 31))
+    return fail(SGT_EUNSUPPORTED, "K x N too large for 32-bit offsets");
+  return SGT_OK;
+}
+
+// Producer work list: local signal tiles first (released at once), then every
+// remote tile at the time its peer's link would deliver it.
+int build_schedule(const AgPlan& p, int W, int rank, int64_t K, int esz, const sgt_opts& o, ProdItem* items) {
+  const double tile_bytes = (double)p.flag_rows * (double)K * esz;
+  const double ticks_per_tile = o.peer_gbps > 0 ? tile_bytes / (o.peer_gbps * 1e3) * kTicksPerUs : 0.0;
+  int n = 0;
+  for (int64_t t = 0; t < p.tiles_per_shard; ++t)
+    items[n++] = ProdItem{(uint32_t)(rank * p.tiles_per_shard + t), (uint32_t)rank, 0};
+  std::vector<int64_t> order((size_t)p.tiles_per_shard);
+  const int first_remote = n;
+  for (int d = 1; d < W; ++d) {
+    const int peer = (rank + d) % W;
+    for (int64_t t = 0; t < p.tiles_per_shard; ++t) order[(size_t)t] = t;
+    uint64_t s = o.arrival_seed * 0x100000001B3ull + (uint64_t)peer * 0x9E37ull + 7;
+    if (o.arrival_seed)
+      for (int64_t i = p.tiles_per_shard - 1; i > 0; --i) {
+        const int64_t j = (int64_t)(splitmix64(s) % (uint64_t)(i + 1));
+        std::swap(order[(size_t)i], order[(size_t)j]);
+      }
+    for (int64_t k = 0; k < p.tiles_per_shard; ++k) {
+      double rel = (double)(k + 1) * ticks_per_tile;
+      if (o.jitter_us > 0) rel += o.jitter_us * kTicksPerUs * (double)(splitmix64(s) >> 11) * (1.0 / 9007199254740992.0);
+      items[n++] = ProdItem{(uint32_t)(peer * p.tiles_per_shard + order[(size_t)k]), (uint32_t)peer, (uint64_t)rel};
+    }
+  }
+  std::stable_sort(items + first_remote, items + n,
+                   [](const ProdItem& a, const ProdItem& b) { return a.release < b.release; });
+  return n;
+}
+
+int default_producer_wgs(const sgt_opts& o, int n_cu) {
+  if (o.producer_cus > 0) return o.producer_cus;
+  return std::max(8, n_cu / 8);
+}
+
+sgt_status next_slot(sgt_ctx* ctx, int* slot) {
+  const int s = ctx->slot;
+  ctx->slot = (ctx->slot + 1) % kSlots;
+  if (ctx->slot_used[s]) HIP_TRY(hipEventSynchronize(ctx->slot_ev[s]));
+  *slot = s;
+  return SGT_OK;
+}
+
+sgt_status finish(sgt_ctx* ctx, const sgt_opts& o, hipStream_t stream) {
+  if (!o.blocking) return SGT_OK;
+  HIP_TRY(hipStreamSynchronize(stream));
+  return sgt_sync(ctx);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sgt_version(void) { return "sgt 0.1 gfx950"; }
+
+const char* sgt_status_str(int st) {
+  switch (st) {
+    case SGT_OK: return "SGT_OK";
+    case SGT_EINVAL: return "SGT_EINVAL";
+    case SGT_EUNSUPPORTED: return "SGT_EUNSUPPORTED";
+    case SGT_ETIMEDOUT: return "SGT_ETIMEDOUT";
+    case SGT_EHIP: return "SGT_EHIP";
+    case SGT_ENOMEM: return "SGT_ENOMEM";
+    default: return "SGT_UNKNOWN";
+  }
+}
+
+const char* sgt_last_error(void) { return g_last_error.c_str(); }
+
+void sgt_opts_init(sgt_opts* o) {
+  if (!o) return;
+  std::memset(o, 0, sizeof *o);
+  o->in_dtype = SGT_BF16;
+  o->out_dtype = SGT_F32;
+  o->b_layout = SGT_KN;
+  o->producer = SGT_PROD_CU;
+  o->order = SGT_ORDER_MESH;
+  o->timeout_ms = 2000.0;
+  o->withhold_peer = -1;
+}
+
+sgt_status sgt_ctx_create(sgt_ctx** out, int device) {
+  if (!out) return fail(SGT_EINVAL, "out is NULL");
+  *out = nullptr;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n)
+    return fail(SGT_EINVAL, "device %d not present (%d devices)", device, n);
+  DeviceGuard g(device);
+  sgt_ctx* c = new (std::nothrow) sgt_ctx();
+  if (!c) return fail(SGT_ENOMEM, "context");
+  c->device = device;
+  hipDeviceProp_t prop;
+  sgt_status st = SGT_OK;
+  auto chk = [&](hipError_t e, const char* what) {
+    if (e != hipSuccess && st == SGT_OK) st = fail(SGT_EHIP, "%s: %s", what, hipGetErrorString(e));
+  };
+  chk(hipGetDeviceProperties(&prop, device), "hipGetDeviceProperties");
+  if (st == SGT_OK) c->n_cu = prop.multiProcessorCount;
+  chk(hipStreamCreateWithFlags(&c->prod, hipStreamNonBlocking), "hipStreamCreate");
+  chk(hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming), "hipEventCreate");
+  chk(hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming), "hipEventCreate");
+  chk(hipMalloc(&c->d_status, 4 * sizeof(uint32_t)), "hipMalloc(status)");
+  if (st == SGT_OK) chk(hipMemset(c->d_status, 0, 4 * sizeof(uint32_t)), "hipMemset");
+  for (int s = 0; s < kSlots && st == SGT_OK; ++s) {
+    chk(hipHostMalloc(&c->h_items[s], kItemsCap * sizeof(ProdItem), hipHostMallocDefault), "hipHostMalloc");
+    chk(hipMalloc(&c->d_items[s], kItemsCap * sizeof(ProdItem)), "hipMalloc(items)");
+    chk(hipEventCreateWithFlags(&c->slot_ev[s], hipEventDisableTiming), "hipEventCreate");
+  }
+  if (st != SGT_OK) {
+    std::string keep = g_last_error;
+    sgt_ctx_destroy(c);
+    g_last_error = keep;
+    return st;
+  }
+  *out = c;
+  return SGT_OK;
+}
+
+sgt_status sgt_ctx_destroy(sgt_ctx* c) {
+  if (!c) return SGT_OK;
+  DeviceGuard g(c->device);
+  if (c->prod) (void)hipStreamSynchronize(c->prod);
+  (void)hipDeviceSynchronize();
+  for (int s = 0; s < kSlots; ++s) {
+    if (c->h_items[s]) (void)hipHostFree(c->h_items[s]);
+    if (c->d_items[s]) (void)hipFree(c->d_items[s]);
+    if (c->slot_ev[s]) (void)hipEventDestroy(c->slot_ev[s]);
+  }
+  if (c->d_status) (void)hipFree(c->d_status);
+  if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
+  if (c->ev_join) (void)hipEventDestroy(c->ev_join);
+  if (c->prod) (void)hipStreamDestroy(c->prod);
+  delete c;
+  return SGT_OK;
+}
+
+sgt_status sgt_sync(sgt_ctx* c) {
+  if (!c) return fail(SGT_EINVAL, "ctx is NULL");
+  DeviceGuard g(c->device);
+  HIP_TRY(hipDeviceSynchronize());
+  uint32_t st[4] = {0, 0, 0, 0};
+  HIP_TRY(hipMemcpy(st, c->d_status, sizeof st, hipMemcpyDeviceToHost));
+  if (st[0] == kStatusTimeout) {
+    HIP_TRY(hipMemset(c->d_status, 0, sizeof st));
+    return fail(SGT_ETIMEDOUT, "wait on flag %u timed out: saw %u, expected %u", st[1], st[2], st[3]);
+  }
+  return SGT_OK;
+}
+
+int64_t sgt_ag_flag_count(int W, int64_t M, int64_t K, const sgt_opts* opts) {
+  sgt_opts o;
+  if (opts) o = *opts; else sgt_opts_init(&o);
+  AgPlan p;
+  sgt_status st = plan_ag(W, M, K, o.in_dtype == SGT_BF16 ? 8 : 1, o, &p);
+  return st == SGT_OK ? p.n_flags : (int64_t)st;
+}
+
+int32_t sgt_ag_panel_rows(int W, int64_t M, int64_t K, int64_t N, const sgt_opts* opts) {
+  (void)W; (void)M; (void)K; (void)N;
+  sgt_opts o;
+  if (opts) o = *opts; else sgt_opts_init(&o);
+  return ag_panel_rows(o.in_dtype);
+}
+
+int64_t sgt_panel_order(int W, int rank, int64_t M, int32_t panel_rows, int order, int32_t* out, int64_t cap) {
+  if (W < 1 || W > kMaxW || rank < 0 || rank >= W || M < 0 || M % W || panel_rows < 1 || !out ||
+      (order != SGT_ORDER_MESH && order != SGT_ORDER_SHARD))
+    return fail(SGT_EINVAL, "bad panel-order arguments");
+  const int64_t tiles_m = (M + panel_rows - 1) / panel_rows;
+  if (tiles_m > cap) return fail(SGT_EINVAL, "cap %lld < %lld panels", (long long)cap, (long long)tiles_m);
+  for (int64_t i = 0; i < tiles_m; ++i) out[i] = (int32_t)panel_at(i, tiles_m, M / W, panel_rows, W, rank, order);
+  return tiles_m;
+}
+
+int64_t sgt_trace_words(int W, int64_t M, int64_t K, int64_t N, const sgt_opts* opts) {
+  sgt_opts o;
+  if (opts) o = *opts; else sgt_opts_init(&o);
+  AgPlan p;
+  sgt_status st = plan_ag(W, M, K, N, o, &p);
+  if (st != SGT_OK) return st;
+  return (int64_t)p.tiles_m * p.tiles_n * 4 + p.n_flags;
+}
+
+sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B, void* A_gathered, void* C,
+                       uint32_t* flags, int W, int64_t M, int64_t K, int64_t N, const sgt_opts* opts, void* stream_) {
+  if (!ctx) return fail(SGT_EINVAL, "ctx is NULL");
+  sgt_status st = check_opts(opts, W < 1 ? 1 : W);
+  if (st != SGT_OK) return st;
+  const sgt_opts& o = *opts;
+  AgPlan p;
+  if ((st = plan_ag(W, M, K, N, o, &p)) != SGT_OK) return st;
+  if (!A_shards && M > 0) return fail(SGT_EINVAL, "A_shards is NULL");
+  if (M > 0) {
+    for (int q = 0; q < W; ++q)
+      if (!A_shards[q] || !aligned16(A_shards[q])) return fail(SGT_EINVAL, "A_shards[%d] NULL or not 16-byte aligned", q);
+    if (!A_gathered || !flags || !aligned16(A_gathered) || !aligned16(flags))
+      return fail(SGT_EINVAL, "A_gathered or flags NULL or not 16-byte aligned");
+    if (N > 0 && (!B || !C || !aligned16(B) || !aligned16(C)))
+      return fail(SGT_EINVAL, "B or C NULL or not 16-byte aligned");
+  }
+  std::lock_guard<std::mutex> lock(ctx->mu);
+  DeviceGuard g(ctx->device);
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const uint32_t e = ++ctx->epoch;
+  if (M == 0) return SGT_OK;
+  const int esz = elem_bytes(o.in_dtype);
+
+  AgArgs a{};
+  a.A = A_gathered; a.B = B; a.C = C; a.flags = flags; a.status = ctx->d_status;
+  a.trace = o.trace;
+  a.M = M; a.N = N; a.K = K; a.rows_per_shard = p.rows_per_shard; a.flag_rows = (int32_t)p.flag_rows;
+  a.W = W; a.rank = o.rank; a.order = o.order; a.tiles_m = p.tiles_m; a.tiles_n = p.tiles_n;
+  a.b_layout = o.b_layout; a.out_dtype = o.out_dtype; a.epoch = e; a.timeout_ticks = timeout_ticks(o);
+  const int total_tiles = p.tiles_m * p.tiles_n;
+
+  if (o.producer == SGT_PROD_PRESET) {
+    HIP_TRY(launch_fill_u32(flags, p.n_flags, e, stream));
+    const int grid = std::min(total_tiles, o.consumer_cus > 0 ? o.consumer_cus
+                                            : (o.in_dtype == SGT_BF16 ? ctx->n_cu : 4 * ctx->n_cu));
+    if (N > 0) HIP_TRY(launch_ag_consumer(a, o.in_dtype, grid, stream));
+    return finish(ctx, o, stream);
+  }
+
+  PtrTable shards{};
+  for (int q = 0; q < W; ++q) shards.p[q] = A_shards[q];
+  int slot;
+  if ((st = next_slot(ctx, &slot)) != SGT_OK) return st;
+  const int n_items = build_schedule(p, W, o.rank, K, esz, o, ctx->h_items[slot]);
+  const int pwg = std::min(default_producer_wgs(o, ctx->n_cu), n_items);
+  uint64_t* trace_rel = o.trace ? o.trace + (int64_t)total_tiles * 4 : nullptr;
+  const int64_t tile_bytes = p.flag_rows * K * esz;
+
+  if (o.producer == SGT_PROD_SERIAL) {
+    HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], ctx->h_items[slot], n_items * sizeof(ProdItem),
+                           hipMemcpyHostToDevice, stream));
+    HIP_TRY(launch_ag_producer(shards, A_gathered, flags, ctx->d_items[slot], n_items, tile_bytes,
+                               (int)p.tiles_per_shard, e, o.withhold_peer, trace_rel, pwg, stream));
+    HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
+    ctx->slot_used[slot] = true;
+    const int grid = std::min(total_tiles, o.consumer_cus > 0 ? o.consumer_cus
+                                            : (o.in_dtype == SGT_BF16 ? ctx->n_cu : 4 * ctx->n_cu));
+    if (N > 0) HIP_TRY(launch_ag_consumer(a, o.in_dtype, grid, stream));
+    return finish(ctx, o, stream);
+  }
+
+  // Overlapped: the producer runs on its own stream.  The consumer keeps one
+  // workgroup per CU (its LDS use allows no more) on all but the producer's
+  // share of CUs, so both kernels are resident at once and no wait can starve.
+  HIP_TRY(hipEventRecord(ctx->ev_fork, stream));
+  HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
+  HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], ctx->h_items[slot], n_items * sizeof(ProdItem), hipMemcpyHostToDevice,
+                         ctx->prod));
+  HIP_TRY(launch_ag_producer(shards, A_gathered, flags, ctx->d_items[slot], n_items, tile_bytes,
+                             (int)p.tiles_per_shard, e, o.withhold_peer, trace_rel, pwg, ctx->prod));
+  HIP_TRY(hipEventRecord(ctx->slot_ev[slot], ctx->prod));
+  ctx->slot_used[slot] = true;
+  int grid;
+  if (o.in_dtype == SGT_BF16)
+    grid = o.consumer_cus > 0 ? o.consumer_cus : std::max(1, ctx->n_cu - pwg);
+  else
+    grid = o.consumer_cus > 0 ? o.consumer_cus : 2 * ctx->n_cu;
+  grid = std::min(grid, total_tiles);
+  if (N > 0) HIP_TRY(launch_ag_consumer(a, o.in_dtype, grid, stream));
+  HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
+  HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
+  return finish(ctx, o, stream);
+}
+
+sgt_status sgt_rs_flag_count(int W, int64_t M, int64_t N, const sgt_opts* opts, int64_t* gflags_n,
+                             int64_t* pflags_n) {
+  if (W < 1 || W > kMaxW || M < 0 || N < 0 || M % W) return fail(SGT_EINVAL, "bad GEMM+RS shape");
+  const int rt = opts && opts->rs_tile > 0 ? opts->rs_tile : 128;
+  if (rt < 16 || (rs_gemm_tile() % rt) || ((M / W) % rt))
+    return fail(SGT_EINVAL, "rs_tile %d must be >= 16 and divide %d and the block rows %lld", rt, rs_gemm_tile(),
+                (long long)(M / W));
+  const int64_t tn = (N + rt - 1) / rt;
+  if (gflags_n) *gflags_n = (M / rt) * tn;
+  if (pflags_n) *pflags_n = (int64_t)W * ((M / W) / rt) * tn;
+  return SGT_OK;
+}
+
+sgt_status sgt_gemm_rs(sgt_ctx* ctx, const void* A_local, const void* B, const float* const* partials,
+                       float* partial_out, float* C_shard, uint32_t* gflags, uint32_t* pflags, int W, int64_t M,
+                       int64_t K, int64_t N, const sgt_opts* opts, void* stream_) {
+  if (!ctx) return fail(SGT_EINVAL, "ctx is NULL");
+  sgt_status st = check_opts(opts, W < 1 ? 1 : W);
+  if (st != SGT_OK) return st;
+  const sgt_opts& o = *opts;
+  if (o.in_dtype != SGT_BF16) return fail(SGT_EUNSUPPORTED, "GEMM+RS takes bf16 inputs");
+  if (o.out_dtype != SGT_F32) return fail(SGT_EUNSUPPORTED, "GEMM+RS partials are fp32");
+  if (o.producer == SGT_PROD_CU && o.peer_gbps > 0)
+    return fail(SGT_EUNSUPPORTED, "paced peer arrival for GEMM+RS is not implemented; peers are pre-resident");
+  if (W < 1 || W > kMaxW) return fail(SGT_EINVAL, "W = %d outside [1, %d]", W, kMaxW);
+  if (M < 0 || N < 0 || K < 1 || M % W) return fail(SGT_EINVAL, "bad shape M=%lld K=%lld N=%lld W=%d",
+                                                    (long long)M, (long long)K, (long long)N, W);
+  if (K % 8 || N % 8) return fail(SGT_EINVAL, "bf16 needs K %% 8 == 0 and N %% 8 == 0");
+  int64_t ng = 0, np = 0;
+  if ((st = sgt_rs_flag_count(W, M, N, opts, &ng, &np)) != SGT_OK) return st;
+  const int rt = o.rs_tile > 0 ? o.rs_tile : 128;
+  const int64_t br = M / W;
+  if ((int64_t)kBMrs() * K * 2 >= ((int64_t)1 << 31) || (int64_t)kBMrs() * N * 4 >= ((int64_t)1 << 31) ||
+      (o.b_layout == SGT_KN && K * N * 2 >= ((int64_t)1 << 31)))
+    return fail(SGT_EUNSUPPORTED, "K or N too large for 32-bit tile offsets");
+  if (M > 0 && N > 0) {
+    if (!A_local || !B || !partial_out || !C_shard || !gflags || !pflags || !partials)
+      return fail(SGT_EINVAL, "NULL pointer argument");
+    if (!aligned16(A_local) || !aligned16(B) || !aligned16(partial_out) || !aligned16(C_shard) ||
+        !aligned16(gflags) || !aligned16(pflags))
+      return fail(SGT_EINVAL, "pointers must be 16-byte aligned");
+    for (int p = 0; p < W; ++p)
+      if (p != o.rank && (!partials[p] || !aligned16(partials[p])))
+        return fail(SGT_EINVAL, "partials[%d] NULL or not 16-byte aligned", p);
+  }
+  std::lock_guard<std::mutex> lock(ctx->mu);
+  DeviceGuard g(ctx->device);
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const uint32_t e = ++ctx->epoch;
+  if (M == 0 || N == 0) return SGT_OK;
+
+  RsArgs a{};
+  a.A = A_local; a.B = B; a.P = partial_out; a.C_shard = C_shard;
+  for (int p = 0; p < W; ++p) a.partials.p[p] = (p == o.rank) ? nullptr : partials[p];
+  a.gflags = gflags; a.pflags = pflags; a.status = ctx->d_status;
+  a.M = M; a.N = N; a.K = K; a.block_rows = br; a.W = W; a.rank = o.rank;
+  const int bm = rs_gemm_tile();
+  a.tiles_n = (int)((N + bm - 1) / bm);
+  a.tiles_m = (int)(W * ((br + bm - 1) / bm));
+  a.rs_tile = rt; a.rs_tm = (int)(br / rt); a.rs_tn = (int)((N + rt - 1) / rt);
+  a.b_layout = o.b_layout;
+  a.n_gemm_tiles = a.tiles_m * a.tiles_n;
+  a.n_red_items = a.rs_tm * a.rs_tn;
+  a.epoch = e; a.timeout_ticks = timeout_ticks(o);
+  // Peers' partials are resident: their flags are set before the kernel starts.
+  HIP_TRY(launch_fill_u32(pflags, np, e, stream));
+  const int total = a.n_gemm_tiles + a.n_red_items;
+  const int grid = std::min(total, o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu);
+  HIP_TRY(launch_gemm_rs(a, grid, stream));
+  return finish(ctx, o, stream);
+}
+
+sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void* W_experts, const float* logits,
+                           void* X_gathered, void* Y, int32_t* expert_off, int32_t* row_token, int32_t* topk_ids,
+                           uint32_t* shard_flags, int W, int64_t T, int64_t H, int64_t I, int E, int topk,
+                           const sgt_opts* opts, void* stream) {
+  (void)ctx; (void)X_shards; (void)W_experts; (void)logits; (void)X_gathered; (void)Y; (void)expert_off;
+  (void)row_token; (void)topk_ids; (void)shard_flags; (void)W; (void)T; (void)H; (void)I; (void)E; (void)topk;
+  (void)opts; (void)stream;
+  return fail(SGT_EUNSUPPORTED, "MoE AllGather-grouped-GEMM is not built yet");
+}
+
+}  // extern "C"

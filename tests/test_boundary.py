@@ -1,0 +1,94 @@
+"""The C-ABI library: it loads, exports every symbol include/sgt.h declares, and
+its host-only queries behave (no GPU call is made here)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgt.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^SGT_API\s+[\w\s\*]+?\b(sgt_\w+)\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from signal_gated_tiled_amd import _sgt
+    if not os.path.exists(_sgt.LIB_PATH):
+        from signal_gated_tiled_amd import build
+        build.build()
+    return _sgt.lib()
+
+
+def test_header_declares_the_api():
+    names = _declared()
+    for n in ["sgt_ag_gemm", "sgt_gemm_rs", "sgt_moe_ag_gemm", "sgt_ctx_create", "sgt_ctx_destroy", "sgt_sync"]:
+        assert n in names
+    assert len(names) >= 15
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in _declared():
+        assert hasattr(L, n), n
+
+
+def test_opts_struct_layout_matches(L):
+    from signal_gated_tiled_amd import _sgt
+    o = _sgt.Opts()
+    L.sgt_opts_init(ctypes.byref(o))
+    assert o.in_dtype == _sgt.SGT_BF16 and o.out_dtype == _sgt.SGT_F32 and o.timeout_ms == 2000.0
+    assert o.withhold_peer == -1 and o.trace is None
+    assert ctypes.sizeof(_sgt.Opts) == 88
+
+
+def test_version_and_status_strings(L):
+    import signal_gated_tiled_amd as sgt
+    assert "gfx950" in sgt.version()
+    assert L.sgt_status_str(-3) == b"SGT_ETIMEDOUT"
+
+
+def test_panel_order_matches_pages_fixture():
+    """The order the persistent consumer uses (computed by the library) against the hand-derived fixture."""
+    import signal_gated_tiled_amd as sgt
+    path = os.path.join(ROOT, "tests", "golden", "swizzle_orders.txt")
+    n = 0
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        head, tail = line.split(":")
+        order, W, tpp, rank = head.split()
+        W, tpp, rank = int(W), int(tpp), int(rank)
+        assert sgt.panel_order(W, rank, W * tpp * 16, 16, order) == [int(x) for x in tail.split()]
+        n += 1
+    assert n >= 8
+
+
+def test_panel_order_is_a_permutation_for_ragged_panels():
+    import signal_gated_tiled_amd as sgt
+    for W, R, bm, order in [(4, 200, 256, "mesh"), (3, 300, 256, "shard"), (8, 96, 256, "mesh")]:
+        got = sgt.panel_order(W, W - 1, W * R, bm, order)
+        assert sorted(got) == list(range(-(-W * R // bm)))
+        assert got[0] == ((W - 1) * R) // bm      # starts on the local shard
+
+
+def test_flag_counts_and_argument_errors():
+    import signal_gated_tiled_amd as sgt
+    assert sgt.ag_flag_count(8, 16384, 8192) == 16384 // 32           # 512 KiB signal tiles
+    assert sgt.ag_flag_count(4, 256, 256, in_dtype=sgt.SGT_F32, flag_rows=16) == 16
+    assert sgt.rs_flag_count(8, 8192, 5120) == (64 * 40, 8 * 8 * 40)
+    with pytest.raises(sgt.SgtError):
+        sgt.ag_flag_count(8, 100, 64)                                   # M % W != 0
+    with pytest.raises(sgt.SgtError):
+        sgt.ag_flag_count(4, 256, 60)                                   # bf16 needs K % 8 == 0
+    with pytest.raises(sgt.SgtError):
+        sgt.ag_flag_count(65, 65 * 8, 64)                               # W > 64
+    with pytest.raises(sgt.SgtError):
+        sgt.rs_flag_count(4, 1024, 256, rs_tile=96)                     # must divide 256
+    assert sgt.ag_panel_rows(8, 16384, 8192, 3584) == 256
