@@ -275,7 +275,8 @@ __device__ __forceinline__ void store_tile(void* C, int64_t M, int64_t N, int64_
         if constexpr (kOutBf16)
           __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(acc.v[i][j][r]), rs, off, 0, 0);
         else
-          __builtin_amdgcn_raw_buffer_store_b32(acc.v[i][j][r], rs, off, 0, 0);
+          // the builtin's data operand is an integer: pass the float's bits, not its value
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc.v[i][j][r]), rs, off, 0, 0);
       }
   }
 }

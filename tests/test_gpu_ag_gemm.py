@@ -207,7 +207,7 @@ def test_bad_arguments_are_rejected_before_launch(ctx):
     with pytest.raises(sgt.SgtError):
         ctx.ag_gemm(dA, dev(B), Ag, C, flags, rank=4)               # rank outside [0, W)
     with pytest.raises(sgt.SgtError):
-        ctx.ag_gemm(dA[:3], dev(B), Ag[:255], C[:255], flags)       # M % W != 0
+        ctx.ag_gemm(dA[:3], dev(B), Ag[:254], C[:254], flags)       # M = 254 is not a multiple of W = 3
 
 
 # ---------------------------------------------------------------- full-size workloads
