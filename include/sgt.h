@@ -103,10 +103,15 @@ typedef struct sgt_opts {
   double peer_gbps;      /* simulated link rate per peer in GB/s; 0 = unthrottled               */
   double jitter_us;      /* each remote tile's release is delayed by U[0, jitter_us]            */
   double timeout_ms;     /* bound on every wait; 0 = 2000 ms                                    */
-  uint64_t arrival_seed; /* 0: each peer's tiles in order; else a seeded order per peer         */
+  uint64_t arrival_seed; /* seed of the arrival order (if shuffled) and of the jitter           */
   int32_t withhold_peer; /* test hook: this peer's tiles are copied but never signalled (-1 off)*/
   int32_t rs_tile;       /* GEMM+RS signal tile edge (rows = cols); 0 = 128                     */
+  int32_t arrival_order; /* 0: each peer sends its tiles in order; 1: a seeded order per peer;
+                            2: one seeded order over all remote tiles                             */
+  int32_t reserved;      /* zero                                                                */
   uint64_t* trace;       /* optional device buffer, see sgt_trace_words(); NULL = off           */
+  void* consumer_events[2]; /* optional hipEvent_t pair recorded on the consumer's stream right
+                               before and after the consumer kernel launch (NULL = off)            */
 } sgt_opts;
 
 typedef struct sgt_ctx sgt_ctx;

@@ -21,6 +21,7 @@ SGT_KN, SGT_NK = 0, 1
 PRODUCERS = {"cu": 0, "preset": 1, "serial": 2}
 ORDERS = {"mesh": 0, "shard": 1}
 LAYOUTS = {"kn": SGT_KN, "nk": SGT_NK}
+ARRIVALS = {"inorder": 0, "per_peer": 1, "global": 2}
 
 
 class SgtError(RuntimeError):
@@ -41,7 +42,8 @@ class Opts(ctypes.Structure):
         ("flag_rows", ctypes.c_int32), ("producer_cus", ctypes.c_int32), ("consumer_cus", ctypes.c_int32),
         ("blocking", ctypes.c_int32), ("peer_gbps", ctypes.c_double), ("jitter_us", ctypes.c_double),
         ("timeout_ms", ctypes.c_double), ("arrival_seed", ctypes.c_uint64), ("withhold_peer", ctypes.c_int32),
-        ("rs_tile", ctypes.c_int32), ("trace", ctypes.c_void_p),
+        ("rs_tile", ctypes.c_int32), ("arrival_order", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("trace", ctypes.c_void_p), ("consumer_events", ctypes.c_void_p * 2),
     ]
 
 
@@ -98,7 +100,7 @@ def make_opts(rank: int = 0, in_dtype: int = SGT_BF16, out_dtype: int = SGT_F32,
               producer: str = "cu", order: str = "mesh", flag_rows: int = 0, producer_cus: int = 0,
               consumer_cus: int = 0, blocking: bool = False, peer_gbps: float = 0.0, jitter_us: float = 0.0,
               timeout_ms: float = 2000.0, arrival_seed: int = 0, withhold_peer: int = -1, rs_tile: int = 0,
-              trace: int = 0) -> Opts:
+              trace: int = 0, consumer_events=None, arrival_order: str = "inorder") -> Opts:
     o = Opts()
     lib().sgt_opts_init(ctypes.byref(o))
     o.rank, o.in_dtype, o.out_dtype = rank, in_dtype, out_dtype
@@ -111,8 +113,24 @@ def make_opts(rank: int = 0, in_dtype: int = SGT_BF16, out_dtype: int = SGT_F32,
     o.arrival_seed = int(arrival_seed)
     o.withhold_peer = withhold_peer
     o.rs_tile = rs_tile
+    o.arrival_order = ARRIVALS[arrival_order]
     o.trace = trace or None
+    if consumer_events is not None:
+        o.consumer_events[0] = _event_handle(consumer_events[0])
+        o.consumer_events[1] = _event_handle(consumer_events[1])
     return o
+
+
+def _event_handle(ev) -> int:
+    """Raw hipEvent_t of a torch.cuda.Event, or an int handle.
+
+    A torch event is recorded once here (so torch creates it and accepts it in
+    elapsed_time); the library records it again at the consumer launch.
+    """
+    if isinstance(ev, int):
+        return ev
+    ev.record()
+    return int(ev.cuda_event)
 
 
 def _dtype_code(t) -> int:

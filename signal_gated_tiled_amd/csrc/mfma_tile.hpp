@@ -69,17 +69,16 @@ __device__ __forceinline__ void acc_zero(MfmaAcc& acc) {
 
 // A k-contiguous operand tile (A, or B stored N x K) seen by the DMA loader:
 // a buffer resource whose record range ends after the last valid row (later
-// rows read as zero), and the byte offset of the row this lane fills for each
-// of its 8 loads (rows `ld` elements apart, or gathered rows for MoE).
+// rows read as zero); lane l of wave w fills, with its load i (0..7), LDS row
+// r = 64 w + 8 i + l / 8 at physical chunk l % 8, i.e. logical chunk
+// (l % 8) ^ swz(r) = (l % 8) ^ (l / 8) ^ (i % 4).  The row of load i starts at
+// byte row_base + i * row_step (rows `ld` elements apart; all offsets 32-bit).
 struct KRows {
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t lane_off[8];   // byte offset of this lane's row for load i (before the chunk)
+  uint32_t row_base;   // this lane's row for load 0, in bytes
+  uint32_t row_step;   // bytes between the rows of load i and i + 1 (wave-uniform)
+  uint32_t chunk[4];   // this lane's logical chunk byte offset for i % 4
 };
-
-// Lane l of wave w, load i (0..7) fills LDS row r = 64 w + 8 i + l / 8,
-// physical chunk l % 8, which holds logical chunk (l % 8) ^ swz(r).
-__device__ __forceinline__ int dma_row(int w, int i, int lane) { return 64 * w + 8 * i + (lane >> 3); }
-__device__ __forceinline__ int dma_chunk(int i, int lane) { return (lane & 7) ^ (lane >> 3) ^ (i & 3); }
 
 // Strided rows: row r at element offset r * ld from base; rows >= rows_valid are zero.
 __device__ __forceinline__ KRows krows_strided(const uint16_t* base, int64_t rows_valid, int64_t ld) {
@@ -87,19 +86,24 @@ __device__ __forceinline__ KRows krows_strided(const uint16_t* base, int64_t row
   const int64_t rows = rows_valid < kBM ? rows_valid : kBM;
   kr.rsrc = make_rsrc(base, rows > 0 ? (uint64_t)rows * (uint64_t)ld * 2u : 0u);
   const int w = wave_id(), lane = threadIdx.x & 63;
+  kr.row_base = (uint32_t)((64 * w + (lane >> 3)) * ld * 2);
+  kr.row_step = (uint32_t)(8 * ld * 2);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) kr.lane_off[i] = (uint32_t)(dma_row(w, i, lane) * ld * 2);
+  for (int q = 0; q < 4; ++q) kr.chunk[q] = (uint32_t)((((lane & 7) ^ (lane >> 3) ^ q) & 7) * 16);
   return kr;
 }
 
 // Issue the DMA of K step [k0, k0 + 64) of a k-contiguous operand into `stage`.
+// Chunks at or past K (including whole steps past the end) read as zero.
 __device__ __forceinline__ void dma_stage(const KRows& kr, uint8_t* stage, int64_t k0, int64_t K) {
-  const int w = wave_id(), lane = threadIdx.x & 63;
+  const int w = wave_id();
+  const uint32_t kbyte = (uint32_t)(k0 * 2);
+  const int64_t rem = (K - k0) * 2;                  // valid bytes of this step's rows
+  const uint32_t lim = rem <= 0 ? 0u : (rem >= 128 ? 128u : (uint32_t)rem);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int c = dma_chunk(i, lane);
-    const int64_t k = k0 + 8 * c;
-    const uint32_t off = k < K ? kr.lane_off[i] + (uint32_t)(k * 2) : kOOB;
+    const uint32_t c = kr.chunk[i & 3];
+    const uint32_t off = c < lim ? kr.row_base + (uint32_t)i * kr.row_step + kbyte + c : kOOB;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(kr.rsrc, (lds_ptr_t)(stage + (w * 8 + i) * 1024), 16, off, 0, 0, 0);
   }
 }
@@ -158,27 +162,56 @@ __device__ __forceinline__ void read_frags(const uint8_t* sA, const uint8_t* sB,
     b[j] = *reinterpret_cast<const bf16x8_t*>(sB + lds_swz(wn * 128 + j * 32 + lr, chunk));
 }
 
-// 64 MFMAs of one wave on one LDS stage; the fragments of k-substep kk + 1 are
-// read while the 16 MFMAs of substep kk run.
+// 64 MFMAs of one wave on one LDS stage, software-pipelined over the four
+// k-substeps: the 8 fragment reads of substep kk + 1 are interleaved with the
+// first 8 of the 16 MFMAs of substep kk (1 MFMA, 1 LDS read), so LDS latency and
+// transfer hide under matrix-core work and only the first substep's reads are
+// exposed.  The scheduling barriers keep the compiler from undoing that order
+// and from hoisting the caller's DMA wait and barrier above the MFMAs (they
+// touch no memory, so it otherwise would).
+template <int KK>
+__device__ __forceinline__ void mfma_substep(const uint8_t* sA, const uint8_t* sB, bf16x8_t (&a)[2][4],
+                                             bf16x8_t (&b)[2][4], MfmaAcc& acc) {
+  constexpr int cur = KK & 1;
+  if constexpr (KK < 3) read_frags(sA, sB, KK + 1, a[cur ^ 1], b[cur ^ 1]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j], acc.v[i][j], 0, 0, 0);
+  if constexpr (KK < 3) {
+    // front-load the reads: (1 MFMA, 1 LDS read) x 8, then the other 8 MFMAs
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, KK);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, KK);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, KK);
+  }
+  // one scheduling region per substep: its MFMAs and the next substep's reads
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ void mfma_stage(const uint8_t* sA, const uint8_t* sB, MfmaAcc& acc) {
   bf16x8_t a[2][4], b[2][4];
   read_frags(sA, sB, 0, a[0], b[0]);
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    if (kk < 3) read_frags(sA, sB, kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][i], b[kk & 1][j], acc.v[i][j], 0, 0, 0);
-  }
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_substep<0>(sA, sB, a, b, acc);
+  mfma_substep<1>(sA, sB, a, b, acc);
+  mfma_substep<2>(sA, sB, a, b, acc);
+  mfma_substep<3>(sA, sB, a, b, acc);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Full K loop for one 256 x 256 tile.  A is k-contiguous (DMA); B is N x K
 // (kBNK, DMA) or K x N (register transpose).  The two stages are distinct LDS
 // objects and the loop is unrolled by two, so the compiler can see that a DMA
 // into one stage never aliases the MFMA reads of the other and does not wait
-// for it.  The caller must have passed a barrier since the previous use.
+// for it.  The loop body has no branches: the K-step count is rounded up to
+// even and the loads of steps past K use out-of-range offsets, so they fill
+// the stage with zeros (which add nothing) without touching memory; a
+// conditional MFMA block would split the accumulators' live ranges and force
+// copies.  The caller must have passed a barrier since the previous use.
 template <bool kBNK>
 __device__ __forceinline__ void gemm_tile(const KRows& ka, const KRows& kb_nk, const uint16_t* B_kn, int64_t N,
                                           int64_t n0, int64_t K, MfmaAcc& acc) {
@@ -187,7 +220,7 @@ __device__ __forceinline__ void gemm_tile(const KRows& ka, const KRows& kb_nk, c
   __shared__ __attribute__((aligned(1024))) uint8_t sA1[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sB1[kStageBytes];
   acc_zero(acc);
-  const int64_t nk = (K + kBK - 1) / kBK;
+  const int64_t nk2 = ((K + kBK - 1) / kBK + 1) & ~int64_t(1);
   KNLoader kn;
   if constexpr (!kBNK) {
     kn.init(B_kn, K, N, n0);
@@ -198,11 +231,8 @@ __device__ __forceinline__ void gemm_tile(const KRows& ka, const KRows& kb_nk, c
   else kn.store(sB0);
   wait_dma();
   __syncthreads();
-  // Pairs of K steps: stage 0 computes while stage 1 fills, then the reverse.
-  // (A loop exit between the two halves would split the accumulators' live
-  // ranges; the odd last step is peeled instead.)
-  const int64_t nk2 = nk & ~int64_t(1);
   for (int64_t kt = 0; kt < nk2; kt += 2) {
+    // stage 0 computes while stage 1 fills
     dma_stage(ka, sA1, (kt + 1) * kBK, K);
     if constexpr (kBNK) dma_stage(kb_nk, sB1, (kt + 1) * kBK, K);
     else kn.load((kt + 1) * kBK);
@@ -210,20 +240,13 @@ __device__ __forceinline__ void gemm_tile(const KRows& ka, const KRows& kb_nk, c
     if constexpr (!kBNK) kn.store(sB1);
     wait_dma();
     __syncthreads();
-    const bool more = kt + 2 < nk;
-    if (more) {
-      dma_stage(ka, sA0, (kt + 2) * kBK, K);
-      if constexpr (kBNK) dma_stage(kb_nk, sB0, (kt + 2) * kBK, K);
-      else kn.load((kt + 2) * kBK);
-    }
+    // stage 1 computes while stage 0 fills (past the end: zeros, unused)
+    dma_stage(ka, sA0, (kt + 2) * kBK, K);
+    if constexpr (kBNK) dma_stage(kb_nk, sB0, (kt + 2) * kBK, K);
+    else kn.load((kt + 2) * kBK);
     mfma_stage(sA1, sB1, acc);
-    if constexpr (!kBNK)
-      if (more) kn.store(sB0);
+    if constexpr (!kBNK) kn.store(sB0);
     wait_dma();
-    __syncthreads();
-  }
-  if (nk & 1) {  // the last K step sits in stage 0
-    mfma_stage(sA0, sB0, acc);
     __syncthreads();
   }
 }
@@ -278,6 +301,8 @@ __device__ __forceinline__ void store_tile(void* C, int64_t M, int64_t N, int64_
           // the builtin's data operand is an integer: pass the float's bits, not its value
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc.v[i][j][r]), rs, off, 0, 0);
       }
+    // bound live ranges: one 32 x 32 block at a time
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 

@@ -17,7 +17,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/sgt.h"
+#include "sgt.h"
 #include "common.hpp"
 #include "sched.hpp"
 
@@ -131,6 +131,7 @@ sgt_status check_opts(const sgt_opts* o, int W) {
   if (!(o->peer_gbps >= 0) || !(o->jitter_us >= 0) || !(o->timeout_ms >= 0))
     return fail(SGT_EINVAL, "negative or NaN rate/jitter/timeout");
   if (o->rs_tile < 0) return fail(SGT_EINVAL, "rs_tile %d", o->rs_tile);
+  if (o->arrival_order < 0 || o->arrival_order > 2) return fail(SGT_EINVAL, "arrival_order %d", o->arrival_order);
   return SGT_OK;
 }
 
@@ -177,28 +178,51 @@ sgt_status plan_ag(int W, int64_t M, int64_t K, int64_t N, const sgt_opts& o, Ag
 }
 
 // Producer work list: local signal tiles first (released at once), then every
-// remote tile at the time its peer's link would deliver it.
+// remote tile at the time its link would deliver it.  Each peer's link carries
+// one tile every tile_bytes / peer_gbps; the tiles of a peer go in order, or
+// in a seeded order per peer, or (arrival_order 2) all remote tiles follow one
+// seeded order at the aggregate rate of the W - 1 links.  Each release is then
+// delayed by U[0, jitter].
+double jitter_ticks(const sgt_opts& o, uint64_t& s) {
+  if (o.jitter_us <= 0) return 0.0;
+  return o.jitter_us * kTicksPerUs * (double)(splitmix64(s) >> 11) * (1.0 / 9007199254740992.0);
+}
+
+void shuffle(std::vector<int64_t>& v, uint64_t& s) {
+  for (int64_t i = (int64_t)v.size() - 1; i > 0; --i) {
+    const int64_t j = (int64_t)(splitmix64(s) % (uint64_t)(i + 1));
+    std::swap(v[(size_t)i], v[(size_t)j]);
+  }
+}
+
 int build_schedule(const AgPlan& p, int W, int rank, int64_t K, int esz, const sgt_opts& o, ProdItem* items) {
   const double tile_bytes = (double)p.flag_rows * (double)K * esz;
   const double ticks_per_tile = o.peer_gbps > 0 ? tile_bytes / (o.peer_gbps * 1e3) * kTicksPerUs : 0.0;
+  const int64_t tps = p.tiles_per_shard;
   int n = 0;
-  for (int64_t t = 0; t < p.tiles_per_shard; ++t)
-    items[n++] = ProdItem{(uint32_t)(rank * p.tiles_per_shard + t), (uint32_t)rank, 0};
-  std::vector<int64_t> order((size_t)p.tiles_per_shard);
+  for (int64_t t = 0; t < tps; ++t) items[n++] = ProdItem{(uint32_t)(rank * tps + t), (uint32_t)rank, 0};
   const int first_remote = n;
-  for (int d = 1; d < W; ++d) {
-    const int peer = (rank + d) % W;
-    for (int64_t t = 0; t < p.tiles_per_shard; ++t) order[(size_t)t] = t;
-    uint64_t s = o.arrival_seed * 0x100000001B3ull + (uint64_t)peer * 0x9E37ull + 7;
-    if (o.arrival_seed)
-      for (int64_t i = p.tiles_per_shard - 1; i > 0; --i) {
-        const int64_t j = (int64_t)(splitmix64(s) % (uint64_t)(i + 1));
-        std::swap(order[(size_t)i], order[(size_t)j]);
+  uint64_t s = o.arrival_seed * 0x100000001B3ull + 0x5851F42D4C957F2Dull;
+  if (o.arrival_order == 2 && W > 1) {
+    std::vector<int64_t> all;
+    for (int d = 1; d < W; ++d)
+      for (int64_t t = 0; t < tps; ++t) all.push_back(((rank + d) % W) * tps + t);
+    shuffle(all, s);
+    const double per = ticks_per_tile / (double)(W - 1);
+    for (size_t g = 0; g < all.size(); ++g) {
+      const double rel = (double)(g + 1) * per + jitter_ticks(o, s);
+      items[n++] = ProdItem{(uint32_t)all[g], (uint32_t)(all[g] / tps), (uint64_t)rel};
+    }
+  } else {
+    std::vector<int64_t> order((size_t)tps);
+    for (int d = 1; d < W; ++d) {
+      const int peer = (rank + d) % W;
+      for (int64_t t = 0; t < tps; ++t) order[(size_t)t] = t;
+      if (o.arrival_order == 1) shuffle(order, s);
+      for (int64_t k = 0; k < tps; ++k) {
+        const double rel = (double)(k + 1) * ticks_per_tile + jitter_ticks(o, s);
+        items[n++] = ProdItem{(uint32_t)(peer * tps + order[(size_t)k]), (uint32_t)peer, (uint64_t)rel};
       }
-    for (int64_t k = 0; k < p.tiles_per_shard; ++k) {
-      double rel = (double)(k + 1) * ticks_per_tile;
-      if (o.jitter_us > 0) rel += o.jitter_us * kTicksPerUs * (double)(splitmix64(s) >> 11) * (1.0 / 9007199254740992.0);
-      items[n++] = ProdItem{(uint32_t)(peer * p.tiles_per_shard + order[(size_t)k]), (uint32_t)peer, (uint64_t)rel};
     }
   }
   std::stable_sort(items + first_remote, items + n,
@@ -216,6 +240,13 @@ sgt_status next_slot(sgt_ctx* ctx, int* slot) {
   ctx->slot = (ctx->slot + 1) % kSlots;
   if (ctx->slot_used[s]) HIP_TRY(hipEventSynchronize(ctx->slot_ev[s]));
   *slot = s;
+  return SGT_OK;
+}
+
+// Record the caller's optional event (before / after the consumer launch).
+sgt_status mark(const sgt_opts& o, int which, hipStream_t stream) {
+  if (o.consumer_events[which])
+    HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(o.consumer_events[which]), stream));
   return SGT_OK;
 }
 
@@ -395,7 +426,11 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
     HIP_TRY(launch_fill_u32(flags, p.n_flags, e, stream));
     const int grid = std::min(total_tiles, o.consumer_cus > 0 ? o.consumer_cus
                                             : (o.in_dtype == SGT_BF16 ? ctx->n_cu : 4 * ctx->n_cu));
-    if (N > 0) HIP_TRY(launch_ag_consumer(a, o.in_dtype, grid, stream));
+    if (N > 0) {
+      if ((st = mark(o, 0, stream)) != SGT_OK) return st;
+      HIP_TRY(launch_ag_consumer(a, o.in_dtype, grid, stream));
+      if ((st = mark(o, 1, stream)) != SGT_OK) return st;
+    }
     return finish(ctx, o, stream);
   }
 
@@ -417,7 +452,11 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
     ctx->slot_used[slot] = true;
     const int grid = std::min(total_tiles, o.consumer_cus > 0 ? o.consumer_cus
                                             : (o.in_dtype == SGT_BF16 ? ctx->n_cu : 4 * ctx->n_cu));
-    if (N > 0) HIP_TRY(launch_ag_consumer(a, o.in_dtype, grid, stream));
+    if (N > 0) {
+      if ((st = mark(o, 0, stream)) != SGT_OK) return st;
+      HIP_TRY(launch_ag_consumer(a, o.in_dtype, grid, stream));
+      if ((st = mark(o, 1, stream)) != SGT_OK) return st;
+    }
     return finish(ctx, o, stream);
   }
 
@@ -438,7 +477,11 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   else
     grid = o.consumer_cus > 0 ? o.consumer_cus : 2 * ctx->n_cu;
   grid = std::min(grid, total_tiles);
-  if (N > 0) HIP_TRY(launch_ag_consumer(a, o.in_dtype, grid, stream));
+  if (N > 0) {
+      if ((st = mark(o, 0, stream)) != SGT_OK) return st;
+      HIP_TRY(launch_ag_consumer(a, o.in_dtype, grid, stream));
+      if ((st = mark(o, 1, stream)) != SGT_OK) return st;
+    }
   HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
   HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
   return finish(ctx, o, stream);
@@ -512,7 +555,9 @@ sgt_status sgt_gemm_rs(sgt_ctx* ctx, const void* A_local, const void* B, const f
   HIP_TRY(launch_fill_u32(pflags, np, e, stream));
   const int total = a.n_gemm_tiles + a.n_red_items;
   const int grid = std::min(total, o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu);
+  if ((st = mark(o, 0, stream)) != SGT_OK) return st;
   HIP_TRY(launch_gemm_rs(a, grid, stream));
+  if ((st = mark(o, 1, stream)) != SGT_OK) return st;
   return finish(ctx, o, stream);
 }
 

@@ -44,7 +44,7 @@ def test_opts_struct_layout_matches(L):
     L.sgt_opts_init(ctypes.byref(o))
     assert o.in_dtype == _sgt.SGT_BF16 and o.out_dtype == _sgt.SGT_F32 and o.timeout_ms == 2000.0
     assert o.withhold_peer == -1 and o.trace is None
-    assert ctypes.sizeof(_sgt.Opts) == 88
+    assert ctypes.sizeof(_sgt.Opts) == 112
 
 
 def test_version_and_status_strings(L):

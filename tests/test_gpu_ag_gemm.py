@@ -55,7 +55,8 @@ def test_tiny_f32_random_arrival(ctx, orc, rank):
     outs = []
     for seed in [0, 1, 2, 3, 4, 5]:
         Ag, C, fl = run_ag(ctx, shards, B, rank=rank, flag_rows=w.flag_rows, arrival_seed=seed,
-                           jitter_us=w.jitter_us, peer_gbps=1.0 if seed % 2 else 0.0)
+                           arrival_order="global" if seed else "inorder", jitter_us=w.jitter_us,
+                           peer_gbps=1.0 if seed % 2 else 0.0)
         assert np.array_equal(Ag, A_ref)
         assert len(fl) == w.M // w.flag_rows and (fl == fl[0]).all() and fl[0] > 0
         assert_close(C, C_ref, what="tiny f32 C", **TOL_F32)
@@ -92,7 +93,7 @@ def test_bf16_ragged_parity(ctx, orc, shape, b_layout):
     A_ref, C_ref = orc.ag_gemm(shards, B, b_layout=b_layout)
     for rank in sorted({0, W - 1}):
         Ag, C, fl = run_ag(ctx, shards, B, b_layout=b_layout, rank=rank, flag_rows=fr, arrival_seed=rank + 3,
-                           jitter_us=20.0)
+                           arrival_order="per_peer", jitter_us=20.0)
         assert np.array_equal(Ag, A_ref)
         assert (fl == fl[0]).all()
         assert_close(C, C_ref, what="bf16 %s %s rank %d" % (shape, b_layout, rank), **TOL_BF16)
@@ -113,7 +114,8 @@ def test_identity_B_is_bit_exact(ctx, b_layout):
     w = I.AGWorkload("t", W=W, M=W * R, K=K, N=K, seed_index=13)
     shards, _ = I.make_ag(w)
     eye = I.f32_to_bf16_bits(np.eye(K, dtype=np.float32))
-    Ag, C, _ = run_ag(ctx, shards, eye, b_layout=b_layout, rank=5, flag_rows=32, arrival_seed=9)
+    Ag, C, _ = run_ag(ctx, shards, eye, b_layout=b_layout, rank=5, flag_rows=32, arrival_seed=9,
+                      arrival_order="global")
     assert np.array_equal(C, values(np.concatenate(shards)).astype(np.float32))
 
 
@@ -123,7 +125,7 @@ def test_integer_inputs_are_bit_exact(ctx, orc):
     shards, B = I.make_ag(w)
     _, C_ref = orc.ag_gemm(shards, B)
     for order in ["mesh", "shard"]:
-        _, C, _ = run_ag(ctx, shards, B, rank=1, flag_rows=24, order=order, arrival_seed=2)
+        _, C, _ = run_ag(ctx, shards, B, rank=1, flag_rows=24, order=order, arrival_seed=2, arrival_order="per_peer")
         assert np.array_equal(C.astype(np.float64), C_ref)
 
 
@@ -132,7 +134,9 @@ def test_bits_invariant_across_modes(ctx):
     w = I.AGWorkload("t", W=8, M=8 * 256, K=768, N=512, seed_index=15)
     shards, B = I.make_ag(w)
     ref = None
-    for kw in [dict(producer="serial"), dict(producer="cu"), dict(producer="cu", arrival_seed=5, jitter_us=30.0),
+    for kw in [dict(producer="serial"), dict(producer="cu"),
+               dict(producer="cu", arrival_seed=5, jitter_us=30.0, arrival_order="per_peer"),
+               dict(producer="cu", arrival_seed=6, jitter_us=5.0, arrival_order="global", peer_gbps=40.0),
                dict(producer="cu", peer_gbps=20.0, order="shard", rank=3),
                dict(producer="cu", rank=7, producer_cus=3, consumer_cus=17), dict(producer="cu", flag_rows=256)]:
         kw.setdefault("flag_rows", 64)
