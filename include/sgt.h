@@ -108,7 +108,7 @@ typedef struct sgt_opts {
   int32_t rs_tile;       /* GEMM+RS signal tile edge (rows = cols); 0 = 128                     */
   int32_t arrival_order; /* 0: each peer sends its tiles in order; 1: a seeded order per peer;
                             2: one seeded order over all remote tiles                             */
-  int32_t reserved;      /* zero                                                                */
+  int32_t tile_waves;    /* bf16 consumer workgroup: 4 or 8 wave64s per 256 x 256 tile; 0 = 8   */
   uint64_t* trace;       /* optional device buffer, see sgt_trace_words(); NULL = off           */
   void* consumer_events[2]; /* optional hipEvent_t pair recorded on the consumer's stream right
                                before and after the consumer kernel launch (NULL = off)            */

@@ -42,7 +42,7 @@ class Opts(ctypes.Structure):
         ("flag_rows", ctypes.c_int32), ("producer_cus", ctypes.c_int32), ("consumer_cus", ctypes.c_int32),
         ("blocking", ctypes.c_int32), ("peer_gbps", ctypes.c_double), ("jitter_us", ctypes.c_double),
         ("timeout_ms", ctypes.c_double), ("arrival_seed", ctypes.c_uint64), ("withhold_peer", ctypes.c_int32),
-        ("rs_tile", ctypes.c_int32), ("arrival_order", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("rs_tile", ctypes.c_int32), ("arrival_order", ctypes.c_int32), ("tile_waves", ctypes.c_int32),
         ("trace", ctypes.c_void_p), ("consumer_events", ctypes.c_void_p * 2),
     ]
 
@@ -100,7 +100,7 @@ def make_opts(rank: int = 0, in_dtype: int = SGT_BF16, out_dtype: int = SGT_F32,
               producer: str = "cu", order: str = "mesh", flag_rows: int = 0, producer_cus: int = 0,
               consumer_cus: int = 0, blocking: bool = False, peer_gbps: float = 0.0, jitter_us: float = 0.0,
               timeout_ms: float = 2000.0, arrival_seed: int = 0, withhold_peer: int = -1, rs_tile: int = 0,
-              trace: int = 0, consumer_events=None, arrival_order: str = "inorder") -> Opts:
+              trace: int = 0, consumer_events=None, arrival_order: str = "inorder", tile_waves: int = 0) -> Opts:
     o = Opts()
     lib().sgt_opts_init(ctypes.byref(o))
     o.rank, o.in_dtype, o.out_dtype = rank, in_dtype, out_dtype
@@ -114,6 +114,7 @@ def make_opts(rank: int = 0, in_dtype: int = SGT_BF16, out_dtype: int = SGT_F32,
     o.withhold_peer = withhold_peer
     o.rs_tile = rs_tile
     o.arrival_order = ARRIVALS[arrival_order]
+    o.tile_waves = tile_waves
     o.trace = trace or None
     if consumer_events is not None:
         o.consumer_events[0] = _event_handle(consumer_events[0])

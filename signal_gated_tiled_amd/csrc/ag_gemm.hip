@@ -6,7 +6,7 @@
 //
 // Two kernels share the schedule and the wait:
 //  * ag_consumer_bf16: bf16 inputs on the matrix cores (mfma_tile.hpp), 256 x 256
-//    tiles, one workgroup per CU.
+//    tiles, one workgroup (4 or 8 wave64s) per CU.
 //  * ag_consumer_f32: fp32 inputs with fp32 FMAs (64 x 64 tiles), for fp32
 //    workloads where a bf16 downcast would lose the required accuracy.
 #include <hip/hip_runtime.h>
@@ -34,8 +34,8 @@ __device__ __forceinline__ bool gate_rows(const AgArgs& a, int64_t m0, int64_t m
   return good;
 }
 
-template <bool kBNK, bool kOutBf16>
-__global__ void __launch_bounds__(kThreads, 1) ag_consumer_bf16(AgArgs a) {
+template <int kW, bool kBNK, bool kOutBf16>
+__global__ void __launch_bounds__(Tile<kW>::kThreads, 1) ag_consumer_bf16(AgArgs a) {
   __shared__ int ok;
   __shared__ uint64_t t_wait;
   const int total = a.tiles_m * a.tiles_n;
@@ -50,12 +50,12 @@ __global__ void __launch_bounds__(kThreads, 1) ag_consumer_bf16(AgArgs a) {
     const int64_t tile_id = (int64_t)pm * a.tiles_n + pn;
     if (!gate_rows(a, m0, m1, &ok, tile_id, &t_wait)) return;
 
-    const KRows ka = krows_strided(A + m0 * a.K, a.M - m0, a.K);
-    KRows kb;
-    if constexpr (kBNK) kb = krows_strided(B + n0 * a.K, a.N - n0, a.K);
-    MfmaAcc acc;
-    gemm_tile<kBNK>(ka, kb, B, a.N, n0, a.K, acc);
-    store_tile<kOutBf16>(a.C, a.M, a.N, m0, n0, acc);
+    const KRows ka = krows_strided<kW>(A + m0 * a.K, a.M - m0, a.K);
+    KRows kb = ka;
+    if constexpr (kBNK) kb = krows_strided<kW>(B + n0 * a.K, a.N - n0, a.K);
+    MfmaAcc<kW> acc;
+    gemm_tile<kW, kBNK>(ka, kb, B, a.N, n0, a.K, acc);
+    store_tile<kW, kOutBf16>(a.C, a.M, a.N, m0, n0, acc);
     if (a.trace && threadIdx.x == 0) a.trace[tile_id * 4 + 2] = clock_ticks();
   }
 }
@@ -152,13 +152,20 @@ __global__ void __launch_bounds__(256) ag_consumer_f32(AgArgs a) {
 int ag_panel_rows(int in_dtype) { return in_dtype == 1 ? kBM : kF32BM; }
 int ag_panel_cols(int in_dtype) { return in_dtype == 1 ? kBN : kF32BN; }
 
+template <int kW>
+static void launch_bf16(const AgArgs& a, int grid, hipStream_t stream) {
+  const bool nk = a.b_layout == 1, ob = a.out_dtype == 1;
+  const dim3 blk(Tile<kW>::kThreads);
+  if (nk && ob) hipLaunchKernelGGL((ag_consumer_bf16<kW, true, true>), dim3(grid), blk, 0, stream, a);
+  if (nk && !ob) hipLaunchKernelGGL((ag_consumer_bf16<kW, true, false>), dim3(grid), blk, 0, stream, a);
+  if (!nk && ob) hipLaunchKernelGGL((ag_consumer_bf16<kW, false, true>), dim3(grid), blk, 0, stream, a);
+  if (!nk && !ob) hipLaunchKernelGGL((ag_consumer_bf16<kW, false, false>), dim3(grid), blk, 0, stream, a);
+}
+
 hipError_t launch_ag_consumer(const AgArgs& a, int in_dtype, int grid, hipStream_t stream) {
   if (in_dtype == 1) {
-    const bool nk = a.b_layout == 1, ob = a.out_dtype == 1;
-    if (nk && ob) hipLaunchKernelGGL((ag_consumer_bf16<true, true>), dim3(grid), dim3(kThreads), 0, stream, a);
-    if (nk && !ob) hipLaunchKernelGGL((ag_consumer_bf16<true, false>), dim3(grid), dim3(kThreads), 0, stream, a);
-    if (!nk && ob) hipLaunchKernelGGL((ag_consumer_bf16<false, true>), dim3(grid), dim3(kThreads), 0, stream, a);
-    if (!nk && !ob) hipLaunchKernelGGL((ag_consumer_bf16<false, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+    if (a.tile_waves == 4) launch_bf16<4>(a, grid, stream);
+    else launch_bf16<8>(a, grid, stream);
   } else {
     hipLaunchKernelGGL(ag_consumer_f32, dim3(grid), dim3(256), 0, stream, a);
   }

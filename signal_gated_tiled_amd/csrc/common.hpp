@@ -40,7 +40,7 @@ struct AgArgs {
   int32_t tiles_m, tiles_n;
   int32_t b_layout, out_dtype;
   uint32_t epoch;
-  uint32_t pad;
+  int32_t tile_waves;     // 4 or 8 wave64s per bf16 workgroup
   uint64_t timeout_ticks;
 };
 
@@ -63,6 +63,7 @@ struct RsArgs {
   int32_t b_layout;
   int32_t n_gemm_tiles, n_red_items;
   uint32_t epoch;
+  int32_t tile_waves;
   uint64_t timeout_ticks;
 };
 

@@ -44,19 +44,19 @@ __device__ __forceinline__ void gemm_tile_coords(const RsArgs& a, int t, int64_t
   *n0 = (int64_t)ni * kBN;
 }
 
-template <bool kBNK>
+template <int kW, bool kBNK>
 __device__ void do_gemm_item(const RsArgs& a, int t) {
   int64_t m0, m_end, n0;
   gemm_tile_coords(a, t, &m0, &m_end, &n0);
   const uint16_t* A = static_cast<const uint16_t*>(a.A);
   const uint16_t* B = static_cast<const uint16_t*>(a.B);
-  const KRows ka = krows_strided(A + m0 * a.K, m_end - m0, a.K);
-  KRows kb;
-  if constexpr (kBNK) kb = krows_strided(B + n0 * a.K, a.N - n0, a.K);
-  MfmaAcc acc;
-  gemm_tile<kBNK>(ka, kb, B, a.N, n0, a.K, acc);
+  const KRows ka = krows_strided<kW>(A + m0 * a.K, m_end - m0, a.K);
+  KRows kb = ka;
+  if constexpr (kBNK) kb = krows_strided<kW>(B + n0 * a.K, a.N - n0, a.K);
+  MfmaAcc<kW> acc;
+  gemm_tile<kW, kBNK>(ka, kb, B, a.N, n0, a.K, acc);
   // rows past m_end belong to the next block's tile: clip to m_end
-  store_tile<false>(a.P, m_end, a.N, m0, n0, acc);
+  store_tile<kW, false>(a.P, m_end, a.N, m0, n0, acc);
   // release the covered signal tiles (rs_tile divides 256 and the block rows)
   const int64_t n_end = n0 + kBN < a.N ? n0 + kBN : a.N;
   const int64_t gtn = (a.N + a.rs_tile - 1) / a.rs_tile;
@@ -85,7 +85,7 @@ __device__ void do_reduce_item(const RsArgs& a, int j, int* ok) {
   if (!*ok) return;
   // float4 columns: rs_tile / 4 per row; 256 threads cover 1024 / rs_tile rows per pass
   const int cols4 = a.rs_tile / 4;
-  const int rows_per_pass = kThreads / cols4;
+  const int rows_per_pass = (int)blockDim.x / cols4;
   const int c4 = threadIdx.x % cols4, rr = threadIdx.x / cols4;
   const int64_t col = (int64_t)tj * a.rs_tile + 4 * c4;
   if (col >= a.N) return;  // N % 4 == 0: a float4 is either fully in or out
@@ -102,14 +102,14 @@ __device__ void do_reduce_item(const RsArgs& a, int j, int* ok) {
   }
 }
 
-template <bool kBNK>
-__global__ void __launch_bounds__(kThreads, 1) gemm_rs_kernel(RsArgs a) {
+template <int kW, bool kBNK>
+__global__ void __launch_bounds__(Tile<kW>::kThreads, 1) gemm_rs_kernel(RsArgs a) {
   __shared__ int ok;
   const int total = a.n_gemm_tiles + a.n_red_items;
   const int G = gridDim.x;
   for (int t = xcd_remap(blockIdx.x, G); t < total; t += G) {
     if (t < a.n_gemm_tiles) {
-      do_gemm_item<kBNK>(a, t);
+      do_gemm_item<kW, kBNK>(a, t);
     } else {
       do_reduce_item(a, t - a.n_gemm_tiles, &ok);
       if (!ok) return;
@@ -123,10 +123,16 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_rs_kernel(RsArgs a) {
 int rs_gemm_tile() { return kBM; }
 
 hipError_t launch_gemm_rs(const RsArgs& a, int grid, hipStream_t stream) {
-  if (a.b_layout == 1)
-    hipLaunchKernelGGL(gemm_rs_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(gemm_rs_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a);
+  const bool nk = a.b_layout == 1;
+  if (a.tile_waves == 4) {
+    const dim3 blk(Tile<4>::kThreads);
+    if (nk) hipLaunchKernelGGL((gemm_rs_kernel<4, true>), dim3(grid), blk, 0, stream, a);
+    else hipLaunchKernelGGL((gemm_rs_kernel<4, false>), dim3(grid), blk, 0, stream, a);
+  } else {
+    const dim3 blk(Tile<8>::kThreads);
+    if (nk) hipLaunchKernelGGL((gemm_rs_kernel<8, true>), dim3(grid), blk, 0, stream, a);
+    else hipLaunchKernelGGL((gemm_rs_kernel<8, false>), dim3(grid), blk, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -1,31 +1,36 @@
 // bf16 x bf16 -> fp32 tile GEMM on CDNA4 matrix cores, shared by the
 // AllGather, GEMM+ReduceScatter and MoE consumers.
 //
-// One workgroup = 256 threads = 4 wave64s in a 2 x 2 grid; it computes a
-// 256 x 256 fp32 tile C[m0:m0+256, n0:n0+256] = A[rows, :] * B[:, n0:n0+256]
-// with v_mfma_f32_32x32x16_bf16 (each wave: 4 x 4 MFMA blocks of 32 x 32, i.e.
-// 128 x 128 outputs held in 256 accumulator registers per lane).
+// One workgroup computes a 256 x 256 fp32 tile C[m0:m0+256, n0:n0+256] =
+// A[rows, :] * B[:, n0:n0+256] with v_mfma_f32_32x32x16_bf16.  Two shapes of
+// workgroup, chosen by the template parameter kW (wave64s per workgroup):
+//   kW = 4: 2 x 2 waves of 128 x 128 (4 x 4 MFMA blocks, 256 accumulators per
+//           lane): one wave per SIMD.
+//   kW = 8: 4 x 2 waves of 64 x 128 (2 x 4 MFMA blocks, 128 accumulators): two
+//           waves per SIMD, so one wave's LDS waits and barrier skew are
+//           covered by the other's matrix-core work (a pure MFMA loop reaches
+//           ~11% more throughput with two waves per SIMD than with one).
 //
 // K loop: BK = 64, two LDS stages of 64 KiB, one barrier per K step.  Operands
 // whose k index is contiguous in memory (A, and B stored N x K) go straight
 // from HBM to LDS with buffer_load_dwordx4 ... lds (no register staging); B
-// stored K x N is loaded to registers in 8 x 8 blocks, transposed there and
-// written to LDS, so LDS always holds [row][k].  The next step's loads are in
-// flight while the current step's 64 MFMAs per wave run.
+// stored K x N is loaded to registers in blocks of 8 n x (8 or 4) k,
+// transposed there and written to LDS, so LDS always holds [row][k].  The
+// next step's loads are in flight while the current step's MFMAs run.
 //
 // LDS layout of a stage, both operands: [256 rows][64 k] bf16 = 128 bytes per
 // row = 8 chunks of 16 bytes; chunk c of row r is stored at chunk
 // c ^ (r & 7) ^ ((r >> 3) & 3).  The MFMA operand reads (8 consecutive rows,
 // one chunk) hit distinct banks, and since the swizzle only uses row bits 0..4
-// the reads of the four 32-row MFMA blocks differ by a constant (an immediate
-// offset).  The DMA writes whole 1 KiB runs; the K x N loader's transposed
-// writes see at most a 2-way conflict.
+// the reads of different 32-row MFMA blocks differ by a constant (an
+// immediate offset).  The DMA writes whole 1 KiB runs; the K x N loader's
+// transposed writes see at most a 2-way conflict.
 //
 // Tails: 32-bit buffer offsets from a per-tile base; rows past the end of the
 // matrix fall outside the buffer's record range and read as zero, and chunks
 // past K (or columns past N) get an out-of-range offset.  The hardware range
-// check covers the VGPR offset only, so every offset is passed there.  K % 8 == 0 and
-// N % 8 == 0 are required (whole 16-byte chunks).
+// check covers the VGPR offset only, so every offset is passed there.
+// K % 8 == 0 and N % 8 == 0 are required (whole 16-byte chunks).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -36,12 +41,22 @@ namespace sgt {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 256;
+constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kStageBytes = kBM * kBK * 2;          // one operand, one stage: 32 KiB
 constexpr uint32_t kOOB = 0x80000000u;              // buffer offset that reads 0 / drops a store
 constexpr int kRsrcWord3 = 0x00020000;              // raw buffer, 32-bit data format (gfx9)
+
+template <int kW>
+struct Tile {
+  static_assert(kW == 4 || kW == 8, "4 or 8 waves");
+  static constexpr int kThreads = 64 * kW;
+  static constexpr int kWaveRows = kBM / (kW / 2);  // 128 or 64 rows per wave
+  static constexpr int kMI = kWaveRows / 32;        // 32-row MFMA blocks per wave
+  static constexpr int kDmaLoads = kBM / kW / 8;    // 1 KiB DMA loads per wave per operand and stage
+};
 
 __device__ __forceinline__ int lds_swz(int row, int chunk) {
   return row * 128 + ((chunk ^ (row & 7) ^ ((row >> 3) & 3)) << 4);
@@ -54,13 +69,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+template <int kW>
 struct MfmaAcc {
-  f32x16_t v[4][4];
+  f32x16_t v[Tile<kW>::kMI][4];
 };
 
-__device__ __forceinline__ void acc_zero(MfmaAcc& acc) {
+template <int kW>
+__device__ __forceinline__ void acc_zero(MfmaAcc<kW>& acc) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < Tile<kW>::kMI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -69,8 +86,8 @@ __device__ __forceinline__ void acc_zero(MfmaAcc& acc) {
 
 // A k-contiguous operand tile (A, or B stored N x K) seen by the DMA loader:
 // a buffer resource whose record range ends after the last valid row (later
-// rows read as zero); lane l of wave w fills, with its load i (0..7), LDS row
-// r = 64 w + 8 i + l / 8 at physical chunk l % 8, i.e. logical chunk
+// rows read as zero).  Lane l of wave w fills, with its load i, LDS row
+// r = (256 / kW) w + 8 i + l / 8 at physical chunk l % 8, i.e. logical chunk
 // (l % 8) ^ swz(r) = (l % 8) ^ (l / 8) ^ (i % 4).  The row of load i starts at
 // byte row_base + i * row_step (rows `ld` elements apart; all offsets 32-bit).
 struct KRows {
@@ -81,12 +98,13 @@ struct KRows {
 };
 
 // Strided rows: row r at element offset r * ld from base; rows >= rows_valid are zero.
+template <int kW>
 __device__ __forceinline__ KRows krows_strided(const uint16_t* base, int64_t rows_valid, int64_t ld) {
   KRows kr;
   const int64_t rows = rows_valid < kBM ? rows_valid : kBM;
   kr.rsrc = make_rsrc(base, rows > 0 ? (uint64_t)rows * (uint64_t)ld * 2u : 0u);
   const int w = wave_id(), lane = threadIdx.x & 63;
-  kr.row_base = (uint32_t)((64 * w + (lane >> 3)) * ld * 2);
+  kr.row_base = (uint32_t)(((kBM / kW) * w + (lane >> 3)) * ld * 2);
   kr.row_step = (uint32_t)(8 * ld * 2);
 #pragma unroll
   for (int q = 0; q < 4; ++q) kr.chunk[q] = (uint32_t)((((lane & 7) ^ (lane >> 3) ^ q) & 7) * 16);
@@ -95,111 +113,126 @@ __device__ __forceinline__ KRows krows_strided(const uint16_t* base, int64_t row
 
 // Issue the DMA of K step [k0, k0 + 64) of a k-contiguous operand into `stage`.
 // Chunks at or past K (including whole steps past the end) read as zero.
+template <int kW>
 __device__ __forceinline__ void dma_stage(const KRows& kr, uint8_t* stage, int64_t k0, int64_t K) {
+  constexpr int L = Tile<kW>::kDmaLoads;
   const int w = wave_id();
   const uint32_t kbyte = (uint32_t)(k0 * 2);
   const int64_t rem = (K - k0) * 2;                  // valid bytes of this step's rows
   const uint32_t lim = rem <= 0 ? 0u : (rem >= 128 ? 128u : (uint32_t)rem);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < L; ++i) {
     const uint32_t c = kr.chunk[i & 3];
     const uint32_t off = c < lim ? kr.row_base + (uint32_t)i * kr.row_step + kbyte + c : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr.rsrc, (lds_ptr_t)(stage + (w * 8 + i) * 1024), 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr.rsrc, (lds_ptr_t)(stage + (w * L + i) * 1024), 16, off, 0, 0, 0);
   }
 }
 
-// B stored K x N: registers, transpose, LDS.
+// B stored K x N: registers, transpose, LDS.  Thread t handles columns
+// n0 + 8 (t % 32) .. + 7 and, of the K step's 8 groups of 8 rows, group
+// (t / 32) % 8; with 512 threads each thread takes half of the group's rows.
+template <int kW>
 struct KNLoader {
+  static constexpr int kRows = kW == 4 ? 8 : 4;   // rows per thread
   __amdgpu_buffer_rsrc_t rsrc;  // whole of B
-  uint32_t lane_off;            // (8 kg * N + n0 + 8 ng) * 2, or kOOB when the columns are past N
+  uint32_t lane_off;            // byte offset of this thread's first row at k0 = 0, or kOOB
   int64_t row_bytes;            // N * 2
-  u32x4_t gb[8];
+  u32x4_t gb[kRows];
 
   __device__ __forceinline__ void init(const uint16_t* B, int64_t K, int64_t N, int64_t n0) {
     rsrc = make_rsrc(B, (uint64_t)K * (uint64_t)N * 2u);
-    const int t = threadIdx.x, ng = t & 31, kg = t >> 5;
+    const int t = threadIdx.x, ng = t & 31, kg = (t >> 5) & 7, h = t >> 8;
     row_bytes = N * 2;
-    lane_off = (n0 + 8 * ng < N) ? (uint32_t)((8 * kg) * row_bytes + (n0 + 8 * ng) * 2) : kOOB;
+    lane_off = (n0 + 8 * ng < N) ? (uint32_t)((8 * kg + kRows * h) * row_bytes + (n0 + 8 * ng) * 2) : kOOB;
   }
   __device__ __forceinline__ void load(int64_t k0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kRows; ++i) {
       // the range check ignores soffset, so the whole offset goes in voffset
       const uint32_t off = lane_off == kOOB ? kOOB : lane_off + (uint32_t)((k0 + i) * row_bytes);
       gb[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
     }
   }
-  // gb[i] holds B[k0 + 8kg + i][n0 + 8ng + 0..7]; column j of this 8 x 8 block,
-  // k ascending, becomes LDS row 8 ng + j, chunk kg.
+  // gb[i] holds B[k0 + 8kg + kRows h + i][n0 + 8ng + 0..7] (two bf16 per dword).
+  // Column j of the block, k ascending, goes to LDS row 8 ng + j, chunk kg
+  // (bytes 8 h .. 8 h + 8 of the chunk when a thread holds 4 rows).
   __device__ __forceinline__ void store(uint8_t* sB) const {
-    const int t = threadIdx.x, ng = t & 31, kg = t >> 5;
+    const int t = threadIdx.x, ng = t & 31, kg = (t >> 5) & 7, h = t >> 8;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      u32x4_t col;
+      uint32_t col[kRows / 2];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < kRows / 2; ++q) {
         const uint32_t lo = gb[2 * q][j >> 1], hi = gb[2 * q + 1][j >> 1];
         col[q] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
       }
-      *reinterpret_cast<u32x4_t*>(sB + lds_swz(8 * ng + j, kg)) = col;
+      uint8_t* dst = sB + lds_swz(8 * ng + j, kg);
+      if constexpr (kRows == 8)
+        *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{col[0], col[1], col[2], col[3]};
+      else
+        *reinterpret_cast<u32x2_t*>(dst + 8 * h) = u32x2_t{col[0], col[1]};
     }
   }
 };
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ void read_frags(const uint8_t* sA, const uint8_t* sB, int kk, bf16x8_t (&a)[4],
-                                           bf16x8_t (&b)[4]) {
+template <int kW>
+__device__ __forceinline__ void read_frags(const uint8_t* sA, const uint8_t* sB, int kk,
+                                           bf16x8_t (&a)[Tile<kW>::kMI], bf16x8_t (&b)[4]) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 31, chunk = 2 * kk + (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    a[i] = *reinterpret_cast<const bf16x8_t*>(sA + lds_swz(wm * 128 + i * 32 + lr, chunk));
+  for (int i = 0; i < Tile<kW>::kMI; ++i)
+    a[i] = *reinterpret_cast<const bf16x8_t*>(sA + lds_swz(wm * Tile<kW>::kWaveRows + i * 32 + lr, chunk));
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     b[j] = *reinterpret_cast<const bf16x8_t*>(sB + lds_swz(wn * 128 + j * 32 + lr, chunk));
 }
 
-// 64 MFMAs of one wave on one LDS stage, software-pipelined over the four
-// k-substeps: the 8 fragment reads of substep kk + 1 are interleaved with the
-// first 8 of the 16 MFMAs of substep kk (1 MFMA, 1 LDS read), so LDS latency and
-// transfer hide under matrix-core work and only the first substep's reads are
+// The MFMAs of one wave on one LDS stage, software-pipelined over the four
+// k-substeps: the fragment reads of substep kk + 1 are interleaved with the
+// first MFMAs of substep kk (1 MFMA, 1 LDS read), so LDS latency and transfer
+// hide under matrix-core work and only the first substep's reads are
 // exposed.  The scheduling barriers keep the compiler from undoing that order
 // and from hoisting the caller's DMA wait and barrier above the MFMAs (they
 // touch no memory, so it otherwise would).
-template <int KK>
-__device__ __forceinline__ void mfma_substep(const uint8_t* sA, const uint8_t* sB, bf16x8_t (&a)[2][4],
-                                             bf16x8_t (&b)[2][4], MfmaAcc& acc) {
+template <int kW, int KK>
+__device__ __forceinline__ void mfma_substep(const uint8_t* sA, const uint8_t* sB,
+                                             bf16x8_t (&a)[2][Tile<kW>::kMI], bf16x8_t (&b)[2][4],
+                                             MfmaAcc<kW>& acc) {
+  constexpr int MI = Tile<kW>::kMI;
   constexpr int cur = KK & 1;
-  if constexpr (KK < 3) read_frags(sA, sB, KK + 1, a[cur ^ 1], b[cur ^ 1]);
+  if constexpr (KK < 3) read_frags<kW>(sA, sB, KK + 1, a[cur ^ 1], b[cur ^ 1]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j], acc.v[i][j], 0, 0, 0);
   if constexpr (KK < 3) {
-    // front-load the reads: (1 MFMA, 1 LDS read) x 8, then the other 8 MFMAs
+    constexpr int R = MI + 4;  // reads of the next substep
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, KK);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, KK);
+    for (int g = 0; g < R; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, KK);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, KK);  // 1 LDS read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, KK);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * MI - R, KK);
   }
   // one scheduling region per substep: its MFMAs and the next substep's reads
   __builtin_amdgcn_sched_barrier(0);
 }
 
-__device__ __forceinline__ void mfma_stage(const uint8_t* sA, const uint8_t* sB, MfmaAcc& acc) {
-  bf16x8_t a[2][4], b[2][4];
-  read_frags(sA, sB, 0, a[0], b[0]);
+template <int kW>
+__device__ __forceinline__ void mfma_stage(const uint8_t* sA, const uint8_t* sB, MfmaAcc<kW>& acc) {
+  bf16x8_t a[2][Tile<kW>::kMI], b[2][4];
+  read_frags<kW>(sA, sB, 0, a[0], b[0]);
   __builtin_amdgcn_sched_barrier(0);
-  mfma_substep<0>(sA, sB, a, b, acc);
-  mfma_substep<1>(sA, sB, a, b, acc);
-  mfma_substep<2>(sA, sB, a, b, acc);
-  mfma_substep<3>(sA, sB, a, b, acc);
+  mfma_substep<kW, 0>(sA, sB, a, b, acc);
+  mfma_substep<kW, 1>(sA, sB, a, b, acc);
+  mfma_substep<kW, 2>(sA, sB, a, b, acc);
+  mfma_substep<kW, 3>(sA, sB, a, b, acc);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -212,55 +245,43 @@ __device__ __forceinline__ void mfma_stage(const uint8_t* sA, const uint8_t* sB,
 // the stage with zeros (which add nothing) without touching memory; a
 // conditional MFMA block would split the accumulators' live ranges and force
 // copies.  The caller must have passed a barrier since the previous use.
-template <bool kBNK>
+template <int kW, bool kBNK>
 __device__ __forceinline__ void gemm_tile(const KRows& ka, const KRows& kb_nk, const uint16_t* B_kn, int64_t N,
-                                          int64_t n0, int64_t K, MfmaAcc& acc) {
+                                          int64_t n0, int64_t K, MfmaAcc<kW>& acc) {
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sA1[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sB1[kStageBytes];
-  acc_zero(acc);
+  acc_zero<kW>(acc);
   const int64_t nk2 = ((K + kBK - 1) / kBK + 1) & ~int64_t(1);
-  KNLoader kn;
+  KNLoader<kW> kn;
   if constexpr (!kBNK) {
     kn.init(B_kn, K, N, n0);
     kn.load(0);
   }
-  dma_stage(ka, sA0, 0, K);
-  if constexpr (kBNK) dma_stage(kb_nk, sB0, 0, K);
+  dma_stage<kW>(ka, sA0, 0, K);
+  if constexpr (kBNK) dma_stage<kW>(kb_nk, sB0, 0, K);
   else kn.store(sB0);
   wait_dma();
   __syncthreads();
   for (int64_t kt = 0; kt < nk2; kt += 2) {
     // stage 0 computes while stage 1 fills
-    dma_stage(ka, sA1, (kt + 1) * kBK, K);
-    if constexpr (kBNK) dma_stage(kb_nk, sB1, (kt + 1) * kBK, K);
+    dma_stage<kW>(ka, sA1, (kt + 1) * kBK, K);
+    if constexpr (kBNK) dma_stage<kW>(kb_nk, sB1, (kt + 1) * kBK, K);
     else kn.load((kt + 1) * kBK);
-    mfma_stage(sA0, sB0, acc);
+    mfma_stage<kW>(sA0, sB0, acc);
     if constexpr (!kBNK) kn.store(sB1);
     wait_dma();
     __syncthreads();
     // stage 1 computes while stage 0 fills (past the end: zeros, unused)
-    dma_stage(ka, sA0, (kt + 2) * kBK, K);
-    if constexpr (kBNK) dma_stage(kb_nk, sB0, (kt + 2) * kBK, K);
+    dma_stage<kW>(ka, sA0, (kt + 2) * kBK, K);
+    if constexpr (kBNK) dma_stage<kW>(kb_nk, sB0, (kt + 2) * kBK, K);
     else kn.load((kt + 2) * kBK);
-    mfma_stage(sA1, sB1, acc);
+    mfma_stage<kW>(sA1, sB1, acc);
     if constexpr (!kBNK) kn.store(sB0);
     wait_dma();
     __syncthreads();
   }
-}
-
-// Accumulator (i, j, r) of this lane sits at tile row acc_row(i, r), column acc_col(j):
-// the 32 x 32 MFMA result puts column lane % 32 in a lane and rows
-// 8 (r / 4) + 4 (lane / 32) + r % 4 in its 16 registers.
-__device__ __forceinline__ int acc_row(int i, int r) {
-  const int lane = threadIdx.x & 63;
-  return (wave_id() >> 1) * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-}
-__device__ __forceinline__ int acc_col(int j) {
-  const int lane = threadIdx.x & 63;
-  return (wave_id() & 1) * 128 + j * 32 + (lane & 31);
 }
 
 // fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
@@ -273,8 +294,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 // Store the tile to a row-major M x N output (ldc = N) at (m0, n0); elements
 // outside the matrix are dropped.  kOutBf16: round to bf16, else fp32.
-template <bool kOutBf16>
-__device__ __forceinline__ void store_tile(void* C, int64_t M, int64_t N, int64_t m0, int64_t n0, const MfmaAcc& acc) {
+// Accumulator (i, j, r) of a lane is tile row wm * rows_per_wave + 32 i +
+// 8 (r / 4) + 4 (lane / 32) + r % 4, column 128 wn + 32 j + lane % 32: the
+// 32 x 32 MFMA result puts column lane % 32 in a lane and those rows in its
+// 16 registers.
+template <int kW, bool kOutBf16>
+__device__ __forceinline__ void store_tile(void* C, int64_t M, int64_t N, int64_t m0, int64_t n0,
+                                           const MfmaAcc<kW>& acc) {
   const int esz = kOutBf16 ? 2 : 4;
   const uint8_t* base = static_cast<const uint8_t*>(C) + (m0 * N + n0) * esz;
   // Record range: from the tile origin to the end of its last valid row (at most
@@ -289,10 +315,10 @@ __device__ __forceinline__ void store_tile(void* C, int64_t M, int64_t N, int64_
     const int col = (w & 1) * 128 + j * 32 + lr;
     const uint32_t voff = (n0 + col < N) ? (uint32_t)((4 * lk * N + col) * esz) : kOOB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < Tile<kW>::kMI; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = (w >> 1) * 128 + i * 32 + 8 * (r >> 2) + (r & 3);  // + 4 lk in voff
+        const int row = (w >> 1) * Tile<kW>::kWaveRows + i * 32 + 8 * (r >> 2) + (r & 3);  // + 4 lk in voff
         // kOOB + (row offset < 2^31) stays out of range: no select needed
         const uint32_t off = voff + (uint32_t)(row * N * esz);
         if constexpr (kOutBf16)
@@ -301,7 +327,7 @@ __device__ __forceinline__ void store_tile(void* C, int64_t M, int64_t N, int64_
           // the builtin's data operand is an integer: pass the float's bits, not its value
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc.v[i][j][r]), rs, off, 0, 0);
       }
-    // bound live ranges: one 32 x 32 block at a time
+    // bound live ranges: one column of MFMA blocks at a time
     __builtin_amdgcn_sched_barrier(0);
   }
 }

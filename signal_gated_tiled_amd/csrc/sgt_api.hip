@@ -132,6 +132,8 @@ sgt_status check_opts(const sgt_opts* o, int W) {
     return fail(SGT_EINVAL, "negative or NaN rate/jitter/timeout");
   if (o->rs_tile < 0) return fail(SGT_EINVAL, "rs_tile %d", o->rs_tile);
   if (o->arrival_order < 0 || o->arrival_order > 2) return fail(SGT_EINVAL, "arrival_order %d", o->arrival_order);
+  if (o->tile_waves != 0 && o->tile_waves != 4 && o->tile_waves != 8)
+    return fail(SGT_EINVAL, "tile_waves %d (0, 4 or 8)", o->tile_waves);
   return SGT_OK;
 }
 
@@ -420,6 +422,7 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   a.M = M; a.N = N; a.K = K; a.rows_per_shard = p.rows_per_shard; a.flag_rows = (int32_t)p.flag_rows;
   a.W = W; a.rank = o.rank; a.order = o.order; a.tiles_m = p.tiles_m; a.tiles_n = p.tiles_n;
   a.b_layout = o.b_layout; a.out_dtype = o.out_dtype; a.epoch = e; a.timeout_ticks = timeout_ticks(o);
+  a.tile_waves = o.tile_waves ? o.tile_waves : 8;
   const int total_tiles = p.tiles_m * p.tiles_n;
 
   if (o.producer == SGT_PROD_PRESET) {
@@ -551,6 +554,7 @@ sgt_status sgt_gemm_rs(sgt_ctx* ctx, const void* A_local, const void* B, const f
   a.n_gemm_tiles = a.tiles_m * a.tiles_n;
   a.n_red_items = a.rs_tm * a.rs_tn;
   a.epoch = e; a.timeout_ticks = timeout_ticks(o);
+  a.tile_waves = o.tile_waves ? o.tile_waves : 8;
   // Peers' partials are resident: their flags are set before the kernel starts.
   HIP_TRY(launch_fill_u32(pflags, np, e, stream));
   const int total = a.n_gemm_tiles + a.n_red_items;
