@@ -143,7 +143,25 @@ def main():
                           "tflops": flops / (over_ms * 1e-3) / 1e12}), flush=True)
         ctx.close()
         return
-    alone_ms, alone_kern_ms, _ = timed(ag("preset"), args.steps, args.warmup, torch, ctx)
+    # the same consumer with data resident and flags preset, on all CUs and on the grid the overlapped
+    # run leaves it (all CUs but the producer's); the better of the two is "the GEMM alone"
+    alone_all = timed(ag("preset"), args.steps, args.warmup, torch, ctx)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    prod_wgs = max(8, n_cu // 8)
+    alone_part = timed(ag("preset", consumer_cus=n_cu - prod_wgs), args.steps, args.warmup, torch, ctx)
+    best = min((alone_all, n_cu), (alone_part, n_cu - prod_wgs), key=lambda x: x[0][0])
+    (alone_ms, alone_kern_ms, _), alone_grid = best
+    # Overlap efficiency from interleaved pairs (overlapped call, then the same consumer alone on the same
+    # grid), so clock and thermal drift between two blocks of runs cannot bias the ratio.
+    pair_ev = _events(2 * args.steps, torch)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        ag("cu", arrival_seed=1000 + i, **link)(i, pair_ev[2 * i])
+        ag("preset", consumer_cus=alone_grid)(i, pair_ev[2 * i + 1])
+    torch.cuda.synchronize()
+    ctx.sync()
+    ov_k = statistics.median(a.elapsed_time(b) for a, b in pair_ev[0::2])
+    al_k = statistics.median(a.elapsed_time(b) for a, b in pair_ev[1::2])
     serial_ms, _, _ = timed(lambda i, ev: ag("serial", arrival_seed=i + 1, **link)(i, ev), max(3, args.steps // 4),
                             2, torch, ctx)
     unthr_ms, _, _ = timed(ag("cu"), max(3, args.steps // 4), 2, torch, ctx)
@@ -160,9 +178,17 @@ def main():
         "gemm_alone_tflops": flops / (alone_ms * 1e-3) / 1e12,
         "gemm_alone_kernel_ms": alone_kern_ms,
         "gemm_alone_pct_peak": 100.0 * flops / (alone_kern_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "gemm_alone_grid": alone_grid,
+        "gemm_alone_all_cus_ms": alone_all[0],
+        "gemm_alone_consumer_grid_ms": alone_part[0],
         "serial_ms": serial_ms,
         "unthrottled_producer_ms": unthr_ms,
-        "overlap_efficiency": alone_ms / over_ms,
+        "overlap_efficiency": al_k / ov_k,
+        "overlap_efficiency_note": "median consumer-kernel time of the GEMM alone over that of the overlapped call, "
+                                   "%d interleaved pairs" % args.steps,
+        "overlap_efficiency_blocks": alone_ms / over_ms,
+        "pairs_overlapped_kernel_ms": ov_k,
+        "pairs_alone_kernel_ms": al_k,
         "speedup_vs_serial": serial_ms / over_ms,
         "link_floor_us": link_floor_us,
         "peer_gbps": w.peer_gbps,
@@ -192,6 +218,17 @@ def main():
         g_ms, _, _ = timed(lambda i, ev: ctx.ag_gemm(A_parts, Brs, A, Cg, fl2, rank=rank, b_layout=lay,
                                                      producer="preset", consumer_events=ev), args.steps,
                            args.warmup, torch, ctx)
+        # interleaved pairs: GEMM+RS call, then the same GEMM alone
+        rs_ev = _events(2 * args.steps, torch)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            ctx.gemm_rs(A, Brs, parts, P, Cs, gf, pf, rank=rank, b_layout=lay, consumer_events=rs_ev[2 * i])
+            ctx.ag_gemm(A_parts, Brs, A, Cg, fl2, rank=rank, b_layout=lay, producer="preset",
+                        consumer_events=rs_ev[2 * i + 1])
+        torch.cuda.synchronize()
+        ctx.sync()
+        rs_pair = statistics.median(a.elapsed_time(b) for a, b in rs_ev[0::2])
+        g_pair = statistics.median(a.elapsed_time(b) for a, b in rs_ev[1::2])
         red_bytes = (r.M // r.W) * r.N * 4 * (r.W + 1)   # read local block + W-1 peers, write C_shard
         detail["gemm_rs"] = {
             "workload": r.name, "M": r.M, "K": r.K, "N": r.N, "W": r.W,
@@ -199,7 +236,9 @@ def main():
             "tflops": r.flops / (rs_ms * 1e-3) / 1e12,
             "pct_peak": 100.0 * r.flops / (rs_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "gemm_alone_ms": g_ms,
-            "overlap_efficiency": g_ms / rs_ms,
+            "overlap_efficiency": g_pair / rs_pair,
+            "overlap_efficiency_note": "median kernel time of the GEMM alone over that of GEMM+RS, interleaved pairs",
+            "overlap_efficiency_blocks": g_ms / rs_ms,
             "reduction_algorithmic_bytes": red_bytes,
         }
         del A, Brs, parts, P, Cs, Cg

@@ -226,7 +226,10 @@ SGT_API sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, co
 
 /* Words of the optional trace buffer for an AllGather call: per consumer tile
  * 4 x uint64 {wait start, flag seen, tile end, workgroup}; then per signal tile
- * 1 x uint64 release time.  Times are the 100 MHz constant GPU clock. */
+ * 1 x uint64 release time.  Times are the 100 MHz constant GPU clock.
+ * A GEMM+ReduceScatter call with opts->trace set writes 3 x uint64 {start, end,
+ * workgroup} per work item: first the GEMM tiles ((W * ceil(M/W/256)) *
+ * ceil(N/256), local block first), then the reduction tiles of the local block. */
 SGT_API int64_t sgt_trace_words(int W, int64_t M, int64_t K, int64_t N, const sgt_opts* opts);
 
 #ifdef __cplusplus

@@ -48,9 +48,27 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) ag_consumer_bf16(AgArgs
     const int64_t m0 = (int64_t)pm * kBM, n0 = (int64_t)pn * kBN;
     const int64_t m1 = m0 + kBM < a.M ? m0 + kBM : a.M;
     const int64_t tile_id = (int64_t)pm * a.tiles_n + pn;
-    if (!gate_rows(a, m0, m1, &ok, tile_id, &t_wait)) return;
+    // A panel that lies inside the local shard is read from the shard itself
+    // and needs no wait; any other panel waits for its flags and is read from
+    // the gathered buffer.
+    const int64_t l0 = (int64_t)a.rank * a.rows_per_shard;
+    const bool local = m0 >= l0 && m1 <= l0 + a.rows_per_shard;
+    const uint16_t* Abase = A + m0 * a.K;
+    int64_t rows_valid = a.M - m0;
+    if (local) {
+      Abase = static_cast<const uint16_t*>(a.A_local) + (m0 - l0) * a.K;
+      rows_valid = l0 + a.rows_per_shard - m0;
+      if (a.trace && threadIdx.x == 0) {
+        const uint64_t now = clock_ticks();
+        a.trace[tile_id * 4 + 0] = now;
+        a.trace[tile_id * 4 + 1] = now;
+        a.trace[tile_id * 4 + 3] = blockIdx.x;
+      }
+    } else if (!gate_rows(a, m0, m1, &ok, tile_id, &t_wait)) {
+      return;
+    }
 
-    const KRows ka = krows_strided<kW>(A + m0 * a.K, a.M - m0, a.K);
+    const KRows ka = krows_strided<kW>(Abase, rows_valid, a.K);
     KRows kb = ka;
     if constexpr (kBNK) kb = krows_strided<kW>(B + n0 * a.K, a.N - n0, a.K);
     MfmaAcc<kW> acc;

@@ -17,17 +17,20 @@ struct PtrTable {
 };
 
 // One AllGather producer work item: copy signal tile `tile` of the gathered
-// matrix, then release its flag no earlier than `release` clock ticks after the
-// producer workgroup started.
+// matrix from `src` (inside peer `peer`'s shard), then release its flag no
+// earlier than `release` clock ticks after the producer workgroup started.
 struct ProdItem {
   uint32_t tile;
   uint32_t peer;
   uint64_t release;
+  const char* src;
+  uint64_t pad;
 };
 
 // Arguments of the AllGather consumer (both the bf16 MFMA and fp32 kernels).
 struct AgArgs {
   const void* A;          // gathered M x K
+  const void* A_local;    // this rank's shard: rows [rank * rows_per_shard, +rows_per_shard) of A
   const void* B;          // K x N or N x K
   void* C;                // M x N
   const uint32_t* flags;  // one per signal tile
@@ -54,6 +57,8 @@ struct RsArgs {
   uint32_t* gflags;         // per rs_tile^2 tile of P
   const uint32_t* pflags;   // W x tiles of one block
   uint32_t* status;
+  uint64_t* trace;          // optional: {start, end, workgroup} per work item
+  uint32_t* red_counter;    // next reduction item to claim; zeroed before the launch
   int64_t M, N, K;
   int64_t block_rows;       // M / W
   int32_t W, rank;

@@ -13,10 +13,11 @@
 //                          block: wait for the GEMM flag and the W-1 peer flags,
 //                          then C_shard = P[local] + sum of peer partials
 //                          (fixed order: local, then peers by ascending rank).
-// The reduction items land in the workgroups left idle by the last, partial
+// GEMM tiles are assigned statically; reduction tiles are claimed from an
+// atomic counter, so they land in the workgroups left idle by the last, partial
 // round of GEMM tiles.  Dependencies only point from reduction to GEMM, and a
-// workgroup never waits on a later item of its own, so the kernel cannot
-// deadlock; every wait is still bounded.
+// workgroup claims reduction tiles only after all of its own GEMM tiles, so the
+// kernel cannot deadlock; every wait is still bounded.
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -56,16 +57,18 @@ __device__ void do_gemm_item(const RsArgs& a, int t) {
   MfmaAcc<kW> acc;
   gemm_tile<kW, kBNK>(ka, kb, B, a.N, n0, a.K, acc);
   // rows past m_end belong to the next block's tile: clip to m_end
-  store_tile<kW, false>(a.P, m_end, a.N, m0, n0, acc);
+  store_tile<kW, false, kCpolSc1>(a.P, m_end, a.N, m0, n0, acc);
   // release the covered signal tiles (rs_tile divides 256 and the block rows)
   const int64_t n_end = n0 + kBN < a.N ? n0 + kBN : a.N;
   const int64_t gtn = (a.N + a.rs_tile - 1) / a.rs_tile;
-  __threadfence();
+  // The tile went out with device-scope stores: once every wave's stores are
+  // acknowledged, one lane publishes the covered flags (no L2 write-back).
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0)
     for (int64_t mi = m0 / a.rs_tile; mi <= (m_end - 1) / a.rs_tile; ++mi)
       for (int64_t nj = n0 / a.rs_tile; nj <= (n_end - 1) / a.rs_tile; ++nj)
-        flag_release(a.gflags + mi * gtn + nj, a.epoch);
+        flag_publish_coherent(a.gflags + mi * gtn + nj, a.epoch);
 }
 
 __device__ void do_reduce_item(const RsArgs& a, int j, int* ok) {
@@ -83,38 +86,79 @@ __device__ void do_reduce_item(const RsArgs& a, int j, int* ok) {
   }
   __syncthreads();
   if (!*ok) return;
-  // float4 columns: rs_tile / 4 per row; 256 threads cover 1024 / rs_tile rows per pass
+  // float4 columns: rs_tile / 4 per row; a pass of the workgroup covers
+  // blockDim / (rs_tile / 4) rows.  Four passes are issued together so each
+  // thread has 4 x W loads in flight (the reduction is bound by HBM latency
+  // times bytes in flight per workgroup).
   const int cols4 = a.rs_tile / 4;
   const int rows_per_pass = (int)blockDim.x / cols4;
   const int c4 = threadIdx.x % cols4, rr = threadIdx.x / cols4;
   const int64_t col = (int64_t)tj * a.rs_tile + 4 * c4;
   if (col >= a.N) return;  // N % 4 == 0: a float4 is either fully in or out
-  for (int r = rr; r < a.rs_tile; r += rows_per_pass) {
-    const int64_t brow = (int64_t)ti * a.rs_tile + r;  // row inside the block
-    f32x4_t s = *reinterpret_cast<const f32x4_t*>(a.P + (row0 + r) * a.N + col);
+  constexpr int R = 4;
+  for (int r0 = rr; r0 < a.rs_tile; r0 += R * rows_per_pass) {
+    f32x4_t s[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int r = r0 + u * rows_per_pass;
+      if (r < a.rs_tile) s[u] = *reinterpret_cast<const f32x4_t*>(a.P + (row0 + r) * a.N + col);
+    }
 #pragma unroll 8
     for (int p = 0; p < a.W; ++p) {
       if (p == a.rank) continue;
-      s += __builtin_nontemporal_load(
-          reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.partials.p[p]) + brow * a.N + col));
+      const float* part = static_cast<const float*>(a.partials.p[p]);
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int r = r0 + u * rows_per_pass;
+        if (r < a.rs_tile)
+          s[u] += __builtin_nontemporal_load(
+              reinterpret_cast<const f32x4_t*>(part + ((int64_t)ti * a.rs_tile + r) * a.N + col));
+      }
     }
-    __builtin_nontemporal_store(s, reinterpret_cast<f32x4_t*>(a.C_shard + brow * a.N + col));
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int r = r0 + u * rows_per_pass;
+      if (r < a.rs_tile)
+        __builtin_nontemporal_store(s[u], reinterpret_cast<f32x4_t*>(a.C_shard + ((int64_t)ti * a.rs_tile + r) * a.N + col));
+    }
   }
 }
 
 template <int kW, bool kBNK>
 __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) gemm_rs_kernel(RsArgs a) {
   __shared__ int ok;
-  const int total = a.n_gemm_tiles + a.n_red_items;
+  __shared__ int claimed;
   const int G = gridDim.x;
-  for (int t = xcd_remap(blockIdx.x, G); t < total; t += G) {
-    if (t < a.n_gemm_tiles) {
-      do_gemm_item<kW, kBNK>(a, t);
-    } else {
-      do_reduce_item(a, t - a.n_gemm_tiles, &ok);
-      if (!ok) return;
-    }
+  // GEMM tiles: static, XCD-grouped round robin (tiles sharing operands run on
+  // one XCD at the same time).
+  for (int t = xcd_remap(blockIdx.x, G); t < a.n_gemm_tiles; t += G) {
+    const uint64_t t_start = clock_ticks();
+    do_gemm_item<kW, kBNK>(a, t);
     __syncthreads();
+    if (a.trace && threadIdx.x == 0) {
+      a.trace[3 * t + 0] = t_start;
+      a.trace[3 * t + 1] = clock_ticks();
+      a.trace[3 * t + 2] = blockIdx.x;
+    }
+  }
+  // Reduction tiles: claimed one at a time by whichever workgroups finish their
+  // GEMM tiles first (the ones with one tile fewer in the last partial round).
+  while (true) {
+    if (threadIdx.x == 0) claimed = (int)atomicAdd(a.red_counter, 1u);
+    __syncthreads();
+    const int j = claimed;
+    __syncthreads();
+    if (j >= a.n_red_items) break;
+    const uint64_t t_start = clock_ticks();
+    do_reduce_item(a, j, &ok);
+    if (!ok) return;
+    __syncthreads();
+    if (a.trace && threadIdx.x == 0) {
+      const int t = a.n_gemm_tiles + j;
+      a.trace[3 * t + 0] = t_start;
+      a.trace[3 * t + 1] = clock_ticks();
+      a.trace[3 * t + 2] = blockIdx.x;
+    }
   }
 }
 

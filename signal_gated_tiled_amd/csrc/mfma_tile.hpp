@@ -293,12 +293,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 // Store the tile to a row-major M x N output (ldc = N) at (m0, n0); elements
-// outside the matrix are dropped.  kOutBf16: round to bf16, else fp32.
+// outside the matrix are dropped.  kOutBf16: round to bf16, else fp32.  kCpol:
+// cache policy of the stores (16 = sc1, device scope, for tiles that other
+// workgroups read back in the same kernel).
 // Accumulator (i, j, r) of a lane is tile row wm * rows_per_wave + 32 i +
 // 8 (r / 4) + 4 (lane / 32) + r % 4, column 128 wn + 32 j + lane % 32: the
 // 32 x 32 MFMA result puts column lane % 32 in a lane and those rows in its
 // 16 registers.
-template <int kW, bool kOutBf16>
+template <int kW, bool kOutBf16, int kCpol = 0>
 __device__ __forceinline__ void store_tile(void* C, int64_t M, int64_t N, int64_t m0, int64_t n0,
                                            const MfmaAcc<kW>& acc) {
   const int esz = kOutBf16 ? 2 : 4;
@@ -322,10 +324,10 @@ __device__ __forceinline__ void store_tile(void* C, int64_t M, int64_t N, int64_
         // kOOB + (row offset < 2^31) stays out of range: no select needed
         const uint32_t off = voff + (uint32_t)(row * N * esz);
         if constexpr (kOutBf16)
-          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(acc.v[i][j][r]), rs, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(acc.v[i][j][r]), rs, off, 0, kCpol);
         else
           // the builtin's data operand is an integer: pass the float's bits, not its value
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc.v[i][j][r]), rs, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc.v[i][j][r]), rs, off, 0, kCpol);
       }
     // bound live ranges: one column of MFMA blocks at a time
     __builtin_amdgcn_sched_barrier(0);

@@ -21,56 +21,71 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ inline void copy_bytes(char* __restrict__ dst, const char* __restrict__ src, int64_t bytes) {
-  const bool v16 = ((bytes | (int64_t)(uintptr_t)dst | (int64_t)(uintptr_t)src) & 15) == 0;
-  if (v16) {
-    constexpr int U = 8;
-    const int64_t n = bytes >> 4;
-    const u32x4* s = reinterpret_cast<const u32x4*>(src);
-    u32x4* d = reinterpret_cast<u32x4*>(dst);
-    const int64_t step = (int64_t)blockDim.x * U;
-    for (int64_t base = threadIdx.x; base < n; base += step) {
-      u32x4 v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t i = base + (int64_t)u * blockDim.x;
-        if (i < n) v[u] = __builtin_nontemporal_load(s + i);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t i = base + (int64_t)u * blockDim.x;
-        if (i < n) d[i] = v[u];
-      }
-    }
-  } else {  // 4-byte elements (fp32 rows of any length)
-    const int64_t n = bytes >> 2;
-    const uint32_t* s = reinterpret_cast<const uint32_t*>(src);
-    uint32_t* d = reinterpret_cast<uint32_t*>(dst);
-    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) d[i] = s[i];
-  }
+__device__ inline __amdgpu_buffer_rsrc_t rsrc_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__global__ void __launch_bounds__(256) ag_producer_kernel(PtrTable shards, char* gathered, uint32_t* flags,
-                                                          const ProdItem* items, int n_items, int64_t tile_bytes,
-                                                          int tiles_per_shard, uint32_t epoch, int withhold_peer,
-                                                          uint64_t* trace_release) {
+// Copy `bytes` (< 2^31) from src to dst with the whole workgroup; returns true
+// when the device-coherent path was used.  16-byte multiples use buffer
+// loads (non-temporal: the source is read once) and device-scope stores (sc1:
+// written through to the coherence point) with 32-bit offsets: past the end,
+// loads read zero and stores are dropped by the hardware range check, so the
+// unrolled body needs no bounds tests.
+template <int U>
+__device__ inline bool copy_bytes(char* __restrict__ dst, const char* __restrict__ src, int64_t bytes) {
+  const bool v16 = ((bytes | (int64_t)(uintptr_t)dst | (int64_t)(uintptr_t)src) & 15) == 0;
+  if (v16) {
+    const __amdgpu_buffer_rsrc_t rs = rsrc_of(src, (uint32_t)bytes), rd = rsrc_of(dst, (uint32_t)bytes);
+    const uint32_t lane = threadIdx.x * 16u, stride = blockDim.x * 16u;
+    for (uint32_t b = 0; b < (uint32_t)bytes; b += stride * U) {
+      u32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, b + lane + (uint32_t)u * stride, 0, kCpolNt);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, b + lane + (uint32_t)u * stride, 0, kCpolSc1);
+    }
+    return true;
+  }
+  // 4-byte elements (fp32 rows of any length): plain stores, published by a release
+  const int64_t n = bytes >> 2;
+  const uint32_t* s = reinterpret_cast<const uint32_t*>(src);
+  uint32_t* d = reinterpret_cast<uint32_t*>(dst);
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) d[i] = s[i];
+  return false;
+}
+
+// 256 threads x 32 loads of 16 bytes = 128 KiB in flight per workgroup: a copy
+// is latency-bound, so bytes in flight set each workgroup's bandwidth.
+constexpr int kProdThreads = 256;
+
+__global__ void __launch_bounds__(kProdThreads) ag_producer_kernel(char* gathered, uint32_t* flags,
+                                                                   const ProdItem* items, int n_items,
+                                                                   int64_t tile_bytes, uint32_t epoch,
+                                                                   int withhold_peer, uint64_t* trace_release) {
   __shared__ uint64_t t0;
   if (threadIdx.x == 0) t0 = clock_ticks();
   __syncthreads();
   for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
     const ProdItem item = items[it];
     const int p = (int)item.peer;
-    const int64_t local_tile = (int64_t)item.tile - (int64_t)p * tiles_per_shard;
-    copy_bytes(gathered + (int64_t)item.tile * tile_bytes,
-               static_cast<const char*>(shards.p[p]) + local_tile * tile_bytes, tile_bytes);
-    __threadfence();
+    const bool coherent = copy_bytes<32>(gathered + (int64_t)item.tile * tile_bytes, item.src, tile_bytes);
+    // Every wave waits until its stores are acknowledged; after the barrier one
+    // lane publishes the flag.  Device-scope stores leave nothing in the XCD's
+    // L2 to write back, so the flag needs no release write-back; the plain
+    // 4-byte path takes the full release.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
       // Pace: the link of this peer delivers the tile at t0 + release.  The
       // schedule is finite, so this wait always ends.
       const uint64_t target = t0 + item.release;
       while (clock_ticks() < target) __builtin_amdgcn_s_sleep(4);
-      if (p != withhold_peer) flag_release(flags + item.tile, epoch);
+      if (p != withhold_peer) {
+        if (coherent) flag_publish_coherent(flags + item.tile, epoch);
+        else flag_release(flags + item.tile, epoch);
+      }
       if (trace_release) trace_release[item.tile] = clock_ticks();
     }
   }
@@ -84,15 +99,31 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
     p[i] = v;
 }
 
+// GEMM+RS set-up in one launch: the resident peers' flags take the epoch and
+// the reduction-claim counter restarts at zero.
+__global__ void rs_prepare_kernel(uint32_t* pflags, int64_t n, uint32_t v, uint32_t* counter) {
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i0 == 0) *counter = 0u;
+  for (int64_t i = i0; i < n; i += (int64_t)gridDim.x * blockDim.x) pflags[i] = v;
+}
+
 }  // namespace
 
-hipError_t launch_ag_producer(const PtrTable& shards, void* gathered, uint32_t* flags, const ProdItem* items,
-                              int n_items, int64_t tile_bytes, int tiles_per_shard, uint32_t epoch,
-                              int withhold_peer, uint64_t* trace_release, int grid, hipStream_t stream) {
+hipError_t launch_rs_prepare(uint32_t* pflags, int64_t n, uint32_t v, uint32_t* counter, hipStream_t stream) {
+  int64_t blocks = (n + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(rs_prepare_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pflags, n, v, counter);
+  return hipGetLastError();
+}
+
+hipError_t launch_ag_producer(void* gathered, uint32_t* flags, const ProdItem* items, int n_items,
+                              int64_t tile_bytes, uint32_t epoch, int withhold_peer, uint64_t* trace_release, int grid,
+                              hipStream_t stream) {
   if (n_items <= 0) return hipSuccess;
   if (grid > n_items) grid = n_items;
-  hipLaunchKernelGGL(ag_producer_kernel, dim3(grid), dim3(256), 0, stream, shards, static_cast<char*>(gathered),
-                     flags, items, n_items, tile_bytes, tiles_per_shard, epoch, withhold_peer, trace_release);
+  hipLaunchKernelGGL(ag_producer_kernel, dim3(grid), dim3(kProdThreads), 0, stream, static_cast<char*>(gathered),
+                     flags, items, n_items, tile_bytes, epoch, withhold_peer, trace_release);
   return hipGetLastError();
 }
 

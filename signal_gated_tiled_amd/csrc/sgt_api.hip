@@ -22,10 +22,11 @@
 #include "sched.hpp"
 
 namespace sgt {
-hipError_t launch_ag_producer(const PtrTable& shards, void* gathered, uint32_t* flags, const ProdItem* items,
-                              int n_items, int64_t tile_bytes, int tiles_per_shard, uint32_t epoch,
-                              int withhold_peer, uint64_t* trace_release, int grid, hipStream_t stream);
+hipError_t launch_ag_producer(void* gathered, uint32_t* flags, const ProdItem* items, int n_items,
+                              int64_t tile_bytes, uint32_t epoch, int withhold_peer, uint64_t* trace_release, int grid,
+                              hipStream_t stream);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
+hipError_t launch_rs_prepare(uint32_t* pflags, int64_t n, uint32_t v, uint32_t* counter, hipStream_t stream);
 hipError_t launch_ag_consumer(const AgArgs& a, int in_dtype, int grid, hipStream_t stream);
 int ag_panel_rows(int in_dtype);
 int ag_panel_cols(int in_dtype);
@@ -70,6 +71,7 @@ struct sgt_ctx {
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   uint32_t epoch = 0;
   uint32_t* d_status = nullptr;  // 4 words
+  uint32_t* d_counters = nullptr;  // work-claim counters, zeroed before each launch that uses them
   ProdItem* h_items[kSlots] = {};
   ProdItem* d_items[kSlots] = {};
   hipEvent_t slot_ev[kSlots] = {};
@@ -165,6 +167,7 @@ sgt_status plan_ag(int W, int64_t M, int64_t K, int64_t N, const sgt_opts& o, Ag
   if (p->n_flags > kItemsCap) return fail(SGT_EINVAL, "%lld signal tiles exceed %lld", (long long)p->n_flags,
                                           (long long)kItemsCap);
   p->tiles_per_shard = p->rows_per_shard / p->flag_rows;
+  if (p->flag_rows * K * esz >= ((int64_t)1 << 31)) return fail(SGT_EUNSUPPORTED, "signal tile of 2 GiB or more");
   const int64_t tm = (M + p->panel_rows - 1) / p->panel_rows, tn = (N + p->panel_cols - 1) / p->panel_cols;
   if (tm * tn > (int64_t)1 << 30) return fail(SGT_EINVAL, "too many tiles");
   p->tiles_m = (int)tm;
@@ -179,8 +182,8 @@ sgt_status plan_ag(int W, int64_t M, int64_t K, int64_t N, const sgt_opts& o, Ag
   return SGT_OK;
 }
 
-// Producer work list: local signal tiles first (released at once), then every
-// remote tile at the time its link would deliver it.  Each peer's link carries
+// Producer work list: every remote tile at the time its link would deliver it,
+// then the local signal tiles (released as soon as copied).  Each peer's link carries
 // one tile every tile_bytes / peer_gbps; the tiles of a peer go in order, or
 // in a seeded order per peer, or (arrival_order 2) all remote tiles follow one
 // seeded order at the aggregate rate of the W - 1 links.  Each release is then
@@ -197,12 +200,12 @@ void shuffle(std::vector<int64_t>& v, uint64_t& s) {
   }
 }
 
-int build_schedule(const AgPlan& p, int W, int rank, int64_t K, int esz, const sgt_opts& o, ProdItem* items) {
+int build_schedule(const AgPlan& p, int W, int rank, int64_t K, int esz, const sgt_opts& o,
+                   const void* const* shards, ProdItem* items) {
   const double tile_bytes = (double)p.flag_rows * (double)K * esz;
   const double ticks_per_tile = o.peer_gbps > 0 ? tile_bytes / (o.peer_gbps * 1e3) * kTicksPerUs : 0.0;
   const int64_t tps = p.tiles_per_shard;
   int n = 0;
-  for (int64_t t = 0; t < tps; ++t) items[n++] = ProdItem{(uint32_t)(rank * tps + t), (uint32_t)rank, 0};
   const int first_remote = n;
   uint64_t s = o.arrival_seed * 0x100000001B3ull + 0x5851F42D4C957F2Dull;
   if (o.arrival_order == 2 && W > 1) {
@@ -213,7 +216,7 @@ int build_schedule(const AgPlan& p, int W, int rank, int64_t K, int esz, const s
     const double per = ticks_per_tile / (double)(W - 1);
     for (size_t g = 0; g < all.size(); ++g) {
       const double rel = (double)(g + 1) * per + jitter_ticks(o, s);
-      items[n++] = ProdItem{(uint32_t)all[g], (uint32_t)(all[g] / tps), (uint64_t)rel};
+      items[n++] = ProdItem{(uint32_t)all[g], (uint32_t)(all[g] / tps), (uint64_t)rel, nullptr, 0};
     }
   } else {
     std::vector<int64_t> order((size_t)tps);
@@ -223,12 +226,19 @@ int build_schedule(const AgPlan& p, int W, int rank, int64_t K, int esz, const s
       if (o.arrival_order == 1) shuffle(order, s);
       for (int64_t k = 0; k < tps; ++k) {
         const double rel = (double)(k + 1) * ticks_per_tile + jitter_ticks(o, s);
-        items[n++] = ProdItem{(uint32_t)(peer * tps + order[(size_t)k]), (uint32_t)peer, (uint64_t)rel};
+        items[n++] = ProdItem{(uint32_t)(peer * tps + order[(size_t)k]), (uint32_t)peer, (uint64_t)rel, nullptr, 0};
       }
     }
   }
   std::stable_sort(items + first_remote, items + n,
                    [](const ProdItem& a, const ProdItem& b) { return a.release < b.release; });
+  // The local shard goes last: the consumer reads it from the shard itself, so
+  // its copy into the gathered buffer is off the critical path.
+  for (int64_t t = 0; t < tps; ++t) items[n++] = ProdItem{(uint32_t)(rank * tps + t), (uint32_t)rank, 0, nullptr, 0};
+  for (int i = 0; i < n; ++i) {
+    const int64_t local_tile = (int64_t)items[i].tile - (int64_t)items[i].peer * tps;
+    items[i].src = static_cast<const char*>(shards[items[i].peer]) + local_tile * (int64_t)tile_bytes;
+  }
   return n;
 }
 
@@ -311,6 +321,7 @@ sgt_status sgt_ctx_create(sgt_ctx** out, int device) {
   chk(hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming), "hipEventCreate");
   chk(hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming), "hipEventCreate");
   chk(hipMalloc(&c->d_status, 4 * sizeof(uint32_t)), "hipMalloc(status)");
+  chk(hipMalloc(&c->d_counters, 64 * sizeof(uint32_t)), "hipMalloc(counters)");
   if (st == SGT_OK) chk(hipMemset(c->d_status, 0, 4 * sizeof(uint32_t)), "hipMemset");
   for (int s = 0; s < kSlots && st == SGT_OK; ++s) {
     chk(hipHostMalloc(&c->h_items[s], kItemsCap * sizeof(ProdItem), hipHostMallocDefault), "hipHostMalloc");
@@ -338,6 +349,7 @@ sgt_status sgt_ctx_destroy(sgt_ctx* c) {
     if (c->slot_ev[s]) (void)hipEventDestroy(c->slot_ev[s]);
   }
   if (c->d_status) (void)hipFree(c->d_status);
+  if (c->d_counters) (void)hipFree(c->d_counters);
   if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
   if (c->ev_join) (void)hipEventDestroy(c->ev_join);
   if (c->prod) (void)hipStreamDestroy(c->prod);
@@ -417,7 +429,7 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   const int esz = elem_bytes(o.in_dtype);
 
   AgArgs a{};
-  a.A = A_gathered; a.B = B; a.C = C; a.flags = flags; a.status = ctx->d_status;
+  a.A = A_gathered; a.A_local = A_shards[o.rank]; a.B = B; a.C = C; a.flags = flags; a.status = ctx->d_status;
   a.trace = o.trace;
   a.M = M; a.N = N; a.K = K; a.rows_per_shard = p.rows_per_shard; a.flag_rows = (int32_t)p.flag_rows;
   a.W = W; a.rank = o.rank; a.order = o.order; a.tiles_m = p.tiles_m; a.tiles_n = p.tiles_n;
@@ -437,11 +449,9 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
     return finish(ctx, o, stream);
   }
 
-  PtrTable shards{};
-  for (int q = 0; q < W; ++q) shards.p[q] = A_shards[q];
   int slot;
   if ((st = next_slot(ctx, &slot)) != SGT_OK) return st;
-  const int n_items = build_schedule(p, W, o.rank, K, esz, o, ctx->h_items[slot]);
+  const int n_items = build_schedule(p, W, o.rank, K, esz, o, A_shards, ctx->h_items[slot]);
   const int pwg = std::min(default_producer_wgs(o, ctx->n_cu), n_items);
   uint64_t* trace_rel = o.trace ? o.trace + (int64_t)total_tiles * 4 : nullptr;
   const int64_t tile_bytes = p.flag_rows * K * esz;
@@ -449,8 +459,8 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   if (o.producer == SGT_PROD_SERIAL) {
     HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], ctx->h_items[slot], n_items * sizeof(ProdItem),
                            hipMemcpyHostToDevice, stream));
-    HIP_TRY(launch_ag_producer(shards, A_gathered, flags, ctx->d_items[slot], n_items, tile_bytes,
-                               (int)p.tiles_per_shard, e, o.withhold_peer, trace_rel, pwg, stream));
+    HIP_TRY(launch_ag_producer(A_gathered, flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
+                               trace_rel, pwg, stream));
     HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
     ctx->slot_used[slot] = true;
     const int grid = std::min(total_tiles, o.consumer_cus > 0 ? o.consumer_cus
@@ -470,8 +480,8 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
   HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], ctx->h_items[slot], n_items * sizeof(ProdItem), hipMemcpyHostToDevice,
                          ctx->prod));
-  HIP_TRY(launch_ag_producer(shards, A_gathered, flags, ctx->d_items[slot], n_items, tile_bytes,
-                             (int)p.tiles_per_shard, e, o.withhold_peer, trace_rel, pwg, ctx->prod));
+  HIP_TRY(launch_ag_producer(A_gathered, flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
+                             trace_rel, pwg, ctx->prod));
   HIP_TRY(hipEventRecord(ctx->slot_ev[slot], ctx->prod));
   ctx->slot_used[slot] = true;
   int grid;
@@ -544,7 +554,7 @@ sgt_status sgt_gemm_rs(sgt_ctx* ctx, const void* A_local, const void* B, const f
   RsArgs a{};
   a.A = A_local; a.B = B; a.P = partial_out; a.C_shard = C_shard;
   for (int p = 0; p < W; ++p) a.partials.p[p] = (p == o.rank) ? nullptr : partials[p];
-  a.gflags = gflags; a.pflags = pflags; a.status = ctx->d_status;
+  a.gflags = gflags; a.pflags = pflags; a.status = ctx->d_status; a.trace = o.trace;
   a.M = M; a.N = N; a.K = K; a.block_rows = br; a.W = W; a.rank = o.rank;
   const int bm = rs_gemm_tile();
   a.tiles_n = (int)((N + bm - 1) / bm);
@@ -556,7 +566,9 @@ sgt_status sgt_gemm_rs(sgt_ctx* ctx, const void* A_local, const void* B, const f
   a.epoch = e; a.timeout_ticks = timeout_ticks(o);
   a.tile_waves = o.tile_waves ? o.tile_waves : 8;
   // Peers' partials are resident: their flags are set before the kernel starts.
-  HIP_TRY(launch_fill_u32(pflags, np, e, stream));
+  // The reduction-claim counter starts at zero (a fill kernel, not a memset).
+  a.red_counter = ctx->d_counters;
+  HIP_TRY(launch_rs_prepare(pflags, np, e, ctx->d_counters, stream));
   const int total = a.n_gemm_tiles + a.n_red_items;
   const int grid = std::min(total, o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu);
   if ((st = mark(o, 0, stream)) != SGT_OK) return st;
