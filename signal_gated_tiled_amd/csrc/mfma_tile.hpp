@@ -88,14 +88,26 @@ __device__ __forceinline__ void acc_zero(MfmaAcc<kW>& acc) {
 // a buffer resource whose record range ends after the last valid row (later
 // rows read as zero).  Lane l of wave w fills, with its load i, LDS row
 // r = (256 / kW) w + 8 i + l / 8 at physical chunk l % 8, i.e. logical chunk
-// (l % 8) ^ swz(r) = (l % 8) ^ (l / 8) ^ (i % 4).  The row of load i starts at
-// byte row_base + i * row_step (rows `ld` elements apart; all offsets 32-bit).
+// (l % 8) ^ swz(r) = (l % 8) ^ (l / 8) ^ (i % 4).  row_off[i] is the byte
+// offset of that row (rows `ld` elements apart, or gathered rows for MoE;
+// kOOB for a row that does not exist); all offsets are 32-bit.
 struct KRows {
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t row_base;   // this lane's row for load 0, in bytes
-  uint32_t row_step;   // bytes between the rows of load i and i + 1 (wave-uniform)
+  uint32_t row_off[8];  // entries [0, Tile<kW>::kDmaLoads) are used
   uint32_t chunk[4];   // this lane's logical chunk byte offset for i % 4
 };
+
+__device__ __forceinline__ void krows_chunks(KRows& kr) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) kr.chunk[q] = (uint32_t)((((lane & 7) ^ (lane >> 3) ^ q) & 7) * 16);
+}
+
+// LDS row filled by this lane's load i.
+template <int kW>
+__device__ __forceinline__ int dma_row(int i) {
+  return (kBM / kW) * wave_id() + 8 * i + ((threadIdx.x & 63) >> 3);
+}
 
 // Strided rows: row r at element offset r * ld from base; rows >= rows_valid are zero.
 template <int kW>
@@ -103,11 +115,9 @@ __device__ __forceinline__ KRows krows_strided(const uint16_t* base, int64_t row
   KRows kr;
   const int64_t rows = rows_valid < kBM ? rows_valid : kBM;
   kr.rsrc = make_rsrc(base, rows > 0 ? (uint64_t)rows * (uint64_t)ld * 2u : 0u);
-  const int w = wave_id(), lane = threadIdx.x & 63;
-  kr.row_base = (uint32_t)(((kBM / kW) * w + (lane >> 3)) * ld * 2);
-  kr.row_step = (uint32_t)(8 * ld * 2);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) kr.chunk[q] = (uint32_t)((((lane & 7) ^ (lane >> 3) ^ q) & 7) * 16);
+  for (int i = 0; i < Tile<kW>::kDmaLoads; ++i) kr.row_off[i] = (uint32_t)(dma_row<kW>(i) * ld * 2);
+  krows_chunks(kr);
   return kr;
 }
 
@@ -123,7 +133,8 @@ __device__ __forceinline__ void dma_stage(const KRows& kr, uint8_t* stage, int64
 #pragma unroll
   for (int i = 0; i < L; ++i) {
     const uint32_t c = kr.chunk[i & 3];
-    const uint32_t off = c < lim ? kr.row_base + (uint32_t)i * kr.row_step + kbyte + c : kOOB;
+    // kOOB + (k0 + c) stays >= 2^31, past every record range
+    const uint32_t off = c < lim ? kr.row_off[i] + kbyte + c : kOOB;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(kr.rsrc, (lds_ptr_t)(stage + (w * L + i) * 1024), 16, off, 0, 0, 0);
   }
 }
