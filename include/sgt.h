@@ -210,19 +210,40 @@ SGT_API sgt_status sgt_rs_flag_count(int W, int64_t M, int64_t N, const sgt_opts
  *     rows of Y  = (expert, token) pairs grouped by expert ascending, tokens
  *                  ascending inside a group; expert_off[e] is the first row of e
  *     Y[row]     = X_gathered[row_token[row]] * W_e          (fp32 or bf16)
- * The shards arrive through the producer with one flag per shard; each grouped
- * tile waits for the flags of the shards its rows come from.
- * X_shards: host array of W device pointers, (T/W) x H bf16.
- * W_experts: E x H x I (SGT_KN) or E x I x H (SGT_NK) bf16.  logits: T x E fp32.
- * Outputs: X_gathered T x H; Y (T*topk) x I; expert_off E+1 int32;
- *     row_token T*topk int32; topk_ids T x topk int32.
- * shard_flags: W words.  Requirements: T % W == 0, 1 <= topk <= E <= 256,
- *     H % 8 == 0, I % 8 == 0.
+ * Routing runs on the GPU; the shards arrive through the producer in signal
+ * tiles of opts->flag_rows tokens (default: about 512 KiB per tile), the local
+ * shard first; each grouped tile (expert, 256 rows of its group, 256 columns)
+ * waits for exactly the signal tiles holding its rows' tokens.  Tiles are
+ * claimed in the order their rows can arrive.
+ * X_shards: host array of W device pointers, (T/W) x H bf16, 16-byte aligned.
+ * W_experts: E x H x I (SGT_KN) or E x I x H (SGT_NK) bf16.  logits: T x E fp32
+ *     (NaN logits are not supported: the selection stays k distinct experts,
+ *     in an unspecified order).
+ * Outputs (caller-owned device memory): X_gathered T x H; Y (T*topk) x I in
+ *     opts->out_dtype; expert_off E+1 int32; row_token T*topk int32;
+ *     topk_ids T x topk int32 (in selection order).
+ * shard_flags: sgt_ag_flag_count(W, T, H, opts) words, zeroed once; later
+ *     calls reuse them through the context's epoch.
+ * Modes (opts->producer): SGT_PROD_CU overlapped; SGT_PROD_SERIAL gather then
+ *     compute; SGT_PROD_PRESET X_gathered already holds every shard.
+ * Requirements: opts->in_dtype SGT_BF16; T % W == 0, T <= 2^20;
+ *     1 <= topk <= E <= 256; H % 8 == 0, I % 8 == 0; T*H*2 < 2^31 and, for
+ *     SGT_KN, H*I*2 < 2^31.  The context keeps the routing work list (grown on
+ *     demand, after draining the device); calls sharing a context must be
+ *     ordered on one stream.  Errors: SGT_EINVAL / SGT_EUNSUPPORTED before any
+ *     launch; a wait past opts->timeout_ms surfaces as SGT_ETIMEDOUT from
+ *     sgt_sync (or this call when opts->blocking).
  */
 SGT_API sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void* W_experts, const float* logits,
                            void* X_gathered, void* Y, int32_t* expert_off, int32_t* row_token, int32_t* topk_ids,
                            uint32_t* shard_flags, int W, int64_t T, int64_t H, int64_t I, int E, int topk,
                            const sgt_opts* opts, void* stream);
+
+/* Words of the optional trace buffer of an sgt_moe_ag_gemm call: 4 x uint64
+ * {wait start, flags seen, tile end, workgroup} per work item in claim order
+ * (room for the largest possible routing), then 1 x uint64 release time per
+ * signal tile. */
+SGT_API int64_t sgt_moe_trace_words(int W, int64_t T, int64_t H, int64_t I, int E, int topk, const sgt_opts* opts);
 
 /* Words of the optional trace buffer for an AllGather call: per consumer tile
  * 4 x uint64 {wait start, flag seen, tile end, workgroup}; then per signal tile

@@ -74,6 +74,9 @@ def lib() -> ctypes.CDLL:
         L.sgt_panel_order.restype = I64
         L.sgt_trace_words.argtypes = [ctypes.c_int, I64, I64, I64, ctypes.POINTER(Opts)]
         L.sgt_trace_words.restype = I64
+        L.sgt_moe_trace_words.argtypes = [ctypes.c_int, I64, I64, I64, ctypes.c_int, ctypes.c_int,
+                                          ctypes.POINTER(Opts)]
+        L.sgt_moe_trace_words.restype = I64
         L.sgt_ag_gemm.argtypes = [P, P, P, P, P, P, ctypes.c_int, I64, I64, I64, ctypes.POINTER(Opts), P]
         L.sgt_rs_flag_count.argtypes = [ctypes.c_int, I64, I64, ctypes.POINTER(Opts), ctypes.POINTER(I64),
                                         ctypes.POINTER(I64)]
@@ -186,6 +189,14 @@ def panel_order(W: int, rank: int, M: int, panel_rows: int, order: str = "mesh")
 def trace_words(W: int, M: int, K: int, N: int, **kw) -> int:
     o = make_opts(**kw)
     n = lib().sgt_trace_words(W, M, K, N, ctypes.byref(o))
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def moe_trace_words(W: int, T: int, H: int, I: int, E: int, topk: int, **kw) -> int:
+    o = make_opts(**kw)
+    n = lib().sgt_moe_trace_words(W, T, H, I, E, topk, ctypes.byref(o))
     if n < 0:
         _check(int(n))
     return int(n)

@@ -72,4 +72,40 @@ struct RsArgs {
   uint64_t timeout_ticks;
 };
 
+// One grouped row tile of the MoE consumer: rows [r0, r0 + 256) of expert e's
+// group (clipped to the group's end), with the readiness key used to order it.
+struct MoeTile {
+  int32_t expert;
+  int32_t r0;       // first row (index into the grouped rows of Y)
+};
+
+// Routing and work-list tables of one MoE call (device memory owned by the context).
+struct MoeTables {
+  uint32_t* counts;       // E: tokens routed to each expert
+  uint32_t* n_tiles;      // 1: number of grouped row tiles
+  uint32_t* claim;        // 1: next consumer work item to claim
+  MoeTile* tiles;         // grouped row tiles, expert-major (written by the placement kernel)
+  uint32_t* keys;         // readiness key per entry of `tiles`
+  MoeTile* order;         // the same tiles sorted by key (the consumer's work order)
+};
+
+// Arguments of the MoE grouped consumer.
+struct MoeArgs {
+  const uint16_t* X;          // gathered tokens, T x H bf16
+  const uint16_t* We;         // experts' weights, E x H x I (KN) or E x I x H (NK)
+  void* Y;                    // grouped rows x I
+  const int32_t* row_token;   // token of each grouped row
+  const int32_t* expert_off;  // E + 1
+  const MoeTile* order;
+  const uint32_t* n_tiles;
+  uint32_t* claim;
+  const uint32_t* flags;      // one per signal tile of X
+  uint32_t* status;
+  uint64_t* trace;            // optional: 4 words per work item in claim order
+  int64_t T, H, I;
+  int32_t E, flag_rows, tiles_n;
+  uint32_t epoch;
+  uint64_t timeout_ticks;
+};
+
 }  // namespace sgt

@@ -1,0 +1,128 @@
+// MoE AllGather + grouped GEMM consumer (paper summary, "Experiments": MoE
+// routing kernels; Triton-distributed semantics page, "AllGather + GEMM
+// overlap": wait for the data a tile reads, then compute it; DITRON article,
+// "three-level tiling": device-level tiles sized by each expert's token count).
+//
+// Work item = (grouped row tile, column tile): rows [r0, r0 + 256) of one
+// expert's group (clipped to the group) times 256 columns of that expert's
+// weight.  Persistent workgroups claim items from the readiness-ordered list
+// with an atomic counter.  Before loading, wave 0 polls, lane by lane, the
+// flag of the signal tile that holds each row's token (a tile waits for
+// exactly the tokens it reads); then the rows are gathered straight into LDS
+// (the DMA takes one row offset per load) and the MFMA tile core computes
+// Y[r0 .., n0 ..] = X[row_token[r0 ..]] * W_e[:, n0 ..].
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+#include "mfma_tile.hpp"
+#include "signal.hpp"
+
+namespace sgt {
+
+namespace {
+
+// Wait until every row of the tile has arrived: lane l of wave 0 watches the
+// signal tiles of rows l, l + 64, l + 128, l + 192.  Returns the workgroup's
+// verdict (false after a timeout, recorded in the status word).
+__device__ __forceinline__ bool wait_tile_rows(const MoeArgs& a, const int32_t* tok, int rows_valid, int* ok) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int64_t f[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = lane + 64 * q;
+      f[q] = r < rows_valid ? (int64_t)(tok[r] / a.flag_rows) : -1;
+    }
+    const uint64_t t0 = clock_ticks();
+    bool good = true;
+    while (true) {
+      bool mine = true;
+      uint32_t seen = 0;
+      int64_t which = -1;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (f[q] >= 0) {
+          const uint32_t v = flag_peek(a.flags + f[q]);
+          if (flag_is_set(v, a.epoch)) {
+            f[q] = -1;
+          } else {
+            mine = false;
+            seen = v;
+            which = f[q];
+          }
+        }
+      }
+      if (__all(mine)) break;
+      if (clock_ticks() - t0 > a.timeout_ticks) {
+        if (!mine) report_timeout(a.status, which, seen, a.epoch);
+        good = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (good) acquire_agent();
+    if (lane == 0) *ok = good ? 1 : 0;
+  }
+  __syncthreads();
+  return *ok != 0;
+}
+
+template <int kW, bool kBNK, bool kOutBf16>
+__global__ void __launch_bounds__(Tile<kW>::kThreads, 1) moe_consumer_bf16(MoeArgs a) {
+  __shared__ int item_s, ok;
+  const int64_t n_items = (int64_t)(*a.n_tiles) * a.tiles_n;
+  while (true) {
+    if (threadIdx.x == 0) item_s = (int)atomicAdd(a.claim, 1u);
+    __syncthreads();
+    const int64_t item = item_s;
+    if (item >= n_items) break;
+    const MoeTile mt = a.order[item / a.tiles_n];
+    const int64_t n0 = (item % a.tiles_n) * kBN;
+    const int e = mt.expert;
+    const int64_t r0 = mt.r0;
+    const int64_t r_end = a.expert_off[e + 1];
+    const int rows_valid = (int)(r_end - r0 < kBM ? r_end - r0 : kBM);
+    const int32_t* tok = a.row_token + r0;
+    uint64_t t_wait = 0;
+    if (a.trace && threadIdx.x == 0) t_wait = clock_ticks();
+    if (!wait_tile_rows(a, tok, rows_valid, &ok)) return;
+    if (a.trace && threadIdx.x == 0) {
+      a.trace[item * 4 + 0] = t_wait;
+      a.trace[item * 4 + 1] = clock_ticks();
+      a.trace[item * 4 + 3] = blockIdx.x;
+    }
+
+    // A: gathered rows of X (row offsets < T * H * 2 < 2^31).
+    KRows ka;
+    ka.rsrc = make_rsrc(a.X, (uint64_t)a.T * (uint64_t)a.H * 2u);
+#pragma unroll
+    for (int i = 0; i < Tile<kW>::kDmaLoads; ++i) {
+      const int r = dma_row<kW>(i);
+      ka.row_off[i] = r < rows_valid ? (uint32_t)((int64_t)tok[r] * a.H * 2) : kOOB;
+    }
+    krows_chunks(ka);
+    // B: expert e's weight, H x I (KN) or I x H (NK).
+    const uint16_t* Be = a.We + (int64_t)e * a.H * a.I;
+    KRows kb = ka;
+    if constexpr (kBNK) kb = krows_strided<kW>(Be + n0 * a.H, a.I - n0, a.H);
+    MfmaAcc<kW> acc;
+    gemm_tile<kW, kBNK>(ka, kb, Be, a.I, n0, a.H, acc);
+    store_tile<kW, kOutBf16>(a.Y, r0 + rows_valid, a.I, r0, n0, acc);
+    if (a.trace && threadIdx.x == 0) a.trace[item * 4 + 2] = clock_ticks();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_moe_consumer(const MoeArgs& a, int b_layout, int out_dtype, int grid, hipStream_t stream) {
+  constexpr int kW = 8;
+  const dim3 blk(Tile<kW>::kThreads);
+  const bool nk = b_layout == 1, ob = out_dtype == 1;
+  if (nk && ob) hipLaunchKernelGGL((moe_consumer_bf16<kW, true, true>), dim3(grid), blk, 0, stream, a);
+  if (nk && !ob) hipLaunchKernelGGL((moe_consumer_bf16<kW, true, false>), dim3(grid), blk, 0, stream, a);
+  if (!nk && ob) hipLaunchKernelGGL((moe_consumer_bf16<kW, false, true>), dim3(grid), blk, 0, stream, a);
+  if (!nk && !ob) hipLaunchKernelGGL((moe_consumer_bf16<kW, false, false>), dim3(grid), blk, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace sgt

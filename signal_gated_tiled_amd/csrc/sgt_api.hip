@@ -32,6 +32,12 @@ int ag_panel_rows(int in_dtype);
 int ag_panel_cols(int in_dtype);
 hipError_t launch_gemm_rs(const RsArgs& a, int grid, hipStream_t stream);
 int rs_gemm_tile();
+int moe_route_rows();
+int moe_max_tiles_per_expert();
+hipError_t launch_moe_route(const float* logits, int64_t T, int E, int k, const uint32_t* rank_of_flag,
+                            int32_t flag_rows, uint32_t n_flags, const MoeTables& tb, int32_t* expert_off,
+                            int32_t* row_token, int32_t* topk_ids, hipStream_t stream);
+hipError_t launch_moe_consumer(const MoeArgs& a, int b_layout, int out_dtype, int grid, hipStream_t stream);
 inline int kBMrs() { return rs_gemm_tile(); }
 }  // namespace sgt
 
@@ -74,6 +80,13 @@ struct sgt_ctx {
   uint32_t* d_counters = nullptr;  // work-claim counters, zeroed before each launch that uses them
   ProdItem* h_items[kSlots] = {};
   ProdItem* d_items[kSlots] = {};
+  uint32_t* h_ranks[kSlots] = {};  // arrival rank of each signal tile (MoE work ordering)
+  uint32_t* d_ranks[kSlots] = {};
+  uint32_t* d_moe = nullptr;       // MoE counts (256), tile count, claim counter
+  MoeTile* d_moe_tiles = nullptr;  // MoE row tiles, expert-major and sorted; grows on demand
+  MoeTile* d_moe_order = nullptr;
+  uint32_t* d_moe_keys = nullptr;
+  int64_t moe_cap = 0;
   hipEvent_t slot_ev[kSlots] = {};
   bool slot_used[kSlots] = {};
   int slot = 0;
@@ -200,12 +213,17 @@ void shuffle(std::vector<int64_t>& v, uint64_t& s) {
   }
 }
 
+// local_first: the local shard's tiles go first (released at once), for a
+// consumer that reads every row from the gathered buffer; otherwise they go
+// last.  ranks (optional): ranks[tile] = the tile's position in the list.
 int build_schedule(const AgPlan& p, int W, int rank, int64_t K, int esz, const sgt_opts& o,
-                   const void* const* shards, ProdItem* items) {
+                   const void* const* shards, ProdItem* items, bool local_first = false, uint32_t* ranks = nullptr) {
   const double tile_bytes = (double)p.flag_rows * (double)K * esz;
   const double ticks_per_tile = o.peer_gbps > 0 ? tile_bytes / (o.peer_gbps * 1e3) * kTicksPerUs : 0.0;
   const int64_t tps = p.tiles_per_shard;
   int n = 0;
+  if (local_first)
+    for (int64_t t = 0; t < tps; ++t) items[n++] = ProdItem{(uint32_t)(rank * tps + t), (uint32_t)rank, 0, nullptr, 0};
   const int first_remote = n;
   uint64_t s = o.arrival_seed * 0x100000001B3ull + 0x5851F42D4C957F2Dull;
   if (o.arrival_order == 2 && W > 1) {
@@ -232,12 +250,14 @@ int build_schedule(const AgPlan& p, int W, int rank, int64_t K, int esz, const s
   }
   std::stable_sort(items + first_remote, items + n,
                    [](const ProdItem& a, const ProdItem& b) { return a.release < b.release; });
-  // The local shard goes last: the consumer reads it from the shard itself, so
-  // its copy into the gathered buffer is off the critical path.
-  for (int64_t t = 0; t < tps; ++t) items[n++] = ProdItem{(uint32_t)(rank * tps + t), (uint32_t)rank, 0, nullptr, 0};
+  // The AllGather consumer reads the local shard from the shard itself, so its
+  // copy into the gathered buffer goes last, off the critical path.
+  if (!local_first)
+    for (int64_t t = 0; t < tps; ++t) items[n++] = ProdItem{(uint32_t)(rank * tps + t), (uint32_t)rank, 0, nullptr, 0};
   for (int i = 0; i < n; ++i) {
     const int64_t local_tile = (int64_t)items[i].tile - (int64_t)items[i].peer * tps;
     items[i].src = static_cast<const char*>(shards[items[i].peer]) + local_tile * (int64_t)tile_bytes;
+    if (ranks) ranks[items[i].tile] = (uint32_t)i;
   }
   return n;
 }
@@ -322,10 +342,13 @@ sgt_status sgt_ctx_create(sgt_ctx** out, int device) {
   chk(hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming), "hipEventCreate");
   chk(hipMalloc(&c->d_status, 4 * sizeof(uint32_t)), "hipMalloc(status)");
   chk(hipMalloc(&c->d_counters, 64 * sizeof(uint32_t)), "hipMalloc(counters)");
+  chk(hipMalloc(&c->d_moe, 512 * sizeof(uint32_t)), "hipMalloc(moe)");
   if (st == SGT_OK) chk(hipMemset(c->d_status, 0, 4 * sizeof(uint32_t)), "hipMemset");
   for (int s = 0; s < kSlots && st == SGT_OK; ++s) {
     chk(hipHostMalloc(&c->h_items[s], kItemsCap * sizeof(ProdItem), hipHostMallocDefault), "hipHostMalloc");
     chk(hipMalloc(&c->d_items[s], kItemsCap * sizeof(ProdItem)), "hipMalloc(items)");
+    chk(hipHostMalloc(&c->h_ranks[s], kItemsCap * sizeof(uint32_t), hipHostMallocDefault), "hipHostMalloc");
+    chk(hipMalloc(&c->d_ranks[s], kItemsCap * sizeof(uint32_t)), "hipMalloc(ranks)");
     chk(hipEventCreateWithFlags(&c->slot_ev[s], hipEventDisableTiming), "hipEventCreate");
   }
   if (st != SGT_OK) {
@@ -346,10 +369,16 @@ sgt_status sgt_ctx_destroy(sgt_ctx* c) {
   for (int s = 0; s < kSlots; ++s) {
     if (c->h_items[s]) (void)hipHostFree(c->h_items[s]);
     if (c->d_items[s]) (void)hipFree(c->d_items[s]);
+    if (c->h_ranks[s]) (void)hipHostFree(c->h_ranks[s]);
+    if (c->d_ranks[s]) (void)hipFree(c->d_ranks[s]);
     if (c->slot_ev[s]) (void)hipEventDestroy(c->slot_ev[s]);
   }
   if (c->d_status) (void)hipFree(c->d_status);
   if (c->d_counters) (void)hipFree(c->d_counters);
+  if (c->d_moe) (void)hipFree(c->d_moe);
+  if (c->d_moe_tiles) (void)hipFree(c->d_moe_tiles);
+  if (c->d_moe_order) (void)hipFree(c->d_moe_order);
+  if (c->d_moe_keys) (void)hipFree(c->d_moe_keys);
   if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
   if (c->ev_join) (void)hipEventDestroy(c->ev_join);
   if (c->prod) (void)hipStreamDestroy(c->prod);
@@ -577,14 +606,159 @@ sgt_status sgt_gemm_rs(sgt_ctx* ctx, const void* A_local, const void* B, const f
   return finish(ctx, o, stream);
 }
 
+// Upper bound of the grouped row tiles of a routing: sum over experts of
+// ceil(n_e / 256) <= T * topk / 256 + E.
+static int64_t moe_max_tiles(int64_t T, int E, int topk) {
+  return T * topk / moe_route_rows() + E;
+}
+
+int64_t sgt_moe_trace_words(int W, int64_t T, int64_t H, int64_t I, int E, int topk, const sgt_opts* opts) {
+  sgt_opts o;
+  if (opts) o = *opts; else sgt_opts_init(&o);
+  AgPlan p;
+  sgt_status st = plan_ag(W, T, H, I, o, &p);
+  if (st != SGT_OK) return st;
+  if (E < 1 || topk < 1 || topk > E) return fail(SGT_EINVAL, "bad E / topk");
+  return moe_max_tiles(T, E, topk) * p.tiles_n * 4 + p.n_flags;
+}
+
 sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void* W_experts, const float* logits,
                            void* X_gathered, void* Y, int32_t* expert_off, int32_t* row_token, int32_t* topk_ids,
                            uint32_t* shard_flags, int W, int64_t T, int64_t H, int64_t I, int E, int topk,
-                           const sgt_opts* opts, void* stream) {
-  (void)ctx; (void)X_shards; (void)W_experts; (void)logits; (void)X_gathered; (void)Y; (void)expert_off;
-  (void)row_token; (void)topk_ids; (void)shard_flags; (void)W; (void)T; (void)H; (void)I; (void)E; (void)topk;
-  (void)opts; (void)stream;
-  return fail(SGT_EUNSUPPORTED, "MoE AllGather-grouped-GEMM is not built yet");
+                           const sgt_opts* opts, void* stream_) {
+  if (!ctx) return fail(SGT_EINVAL, "ctx is NULL");
+  sgt_status st = check_opts(opts, W < 1 ? 1 : W);
+  if (st != SGT_OK) return st;
+  const sgt_opts& o = *opts;
+  if (o.in_dtype != SGT_BF16) return fail(SGT_EUNSUPPORTED, "MoE takes bf16 tokens and weights");
+  if (E < 1 || E > 256 || topk < 1 || topk > E) return fail(SGT_EINVAL, "need 1 <= topk <= E <= 256 (E=%d topk=%d)", E, topk);
+  if (T < 0 || H < 1 || I < 0) return fail(SGT_EINVAL, "bad shape T=%lld H=%lld I=%lld", (long long)T, (long long)H,
+                                           (long long)I);
+  if (T > (int64_t)moe_max_tiles_per_expert() * moe_route_rows())
+    return fail(SGT_EUNSUPPORTED, "T = %lld tokens exceeds %lld", (long long)T,
+                (long long)moe_max_tiles_per_expert() * moe_route_rows());
+  AgPlan p;
+  if ((st = plan_ag(W, T, H, I, o, &p)) != SGT_OK) return st;
+  const int64_t lim = (int64_t)1 << 31;
+  if (T * H * 2 >= lim || (int64_t)moe_route_rows() * H * 2 >= lim || (int64_t)moe_route_rows() * I * 4 >= lim ||
+      (o.b_layout == SGT_KN && H * I * 2 >= lim))
+    return fail(SGT_EUNSUPPORTED, "T x H or one expert's H x I too large for 32-bit offsets");
+  if (moe_max_tiles(T, E, topk) * p.tiles_n >= lim) return fail(SGT_EUNSUPPORTED, "too many grouped tiles");
+  if (T > 0) {
+    // W_experts and Y are read / written only when I > 0
+    if (!X_shards || !logits || !X_gathered || !expert_off || !row_token || !topk_ids || !shard_flags ||
+        (I > 0 && (!Y || !W_experts)))
+      return fail(SGT_EINVAL, "NULL pointer argument");
+    for (int q = 0; q < W; ++q)
+      if (!X_shards[q] || !aligned16(X_shards[q])) return fail(SGT_EINVAL, "X_shards[%d] NULL or not 16-byte aligned", q);
+    if (!aligned16(X_gathered) || !aligned16(shard_flags) || (I > 0 && (!aligned16(Y) || !aligned16(W_experts))) ||
+        (reinterpret_cast<uintptr_t>(logits) & 3u) || (reinterpret_cast<uintptr_t>(expert_off) & 3u) ||
+        (reinterpret_cast<uintptr_t>(row_token) & 3u) || (reinterpret_cast<uintptr_t>(topk_ids) & 3u))
+      return fail(SGT_EINVAL, "pointer not aligned (16 bytes for matrices and flags, 4 for tables)");
+  } else if (!expert_off) {
+    return fail(SGT_EINVAL, "expert_off is NULL");
+  }
+  std::lock_guard<std::mutex> lock(ctx->mu);
+  DeviceGuard g(ctx->device);
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const uint32_t e = ++ctx->epoch;
+  if (T == 0) {  // no tokens: every group is empty
+    HIP_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(expert_off), E + 1, 0u, stream));
+    return finish(ctx, o, stream);
+  }
+
+  // Work-list tables: grow (after draining the device) when a larger routing needs more.
+  const int64_t max_tiles = moe_max_tiles(T, E, topk);
+  if (ctx->moe_cap < max_tiles) {
+    HIP_TRY(hipDeviceSynchronize());
+    if (ctx->d_moe_tiles) (void)hipFree(ctx->d_moe_tiles);
+    if (ctx->d_moe_order) (void)hipFree(ctx->d_moe_order);
+    if (ctx->d_moe_keys) (void)hipFree(ctx->d_moe_keys);
+    ctx->d_moe_tiles = ctx->d_moe_order = nullptr;
+    ctx->d_moe_keys = nullptr;
+    ctx->moe_cap = 0;
+    const int64_t cap = std::max<int64_t>(max_tiles, 1024);
+    HIP_TRY(hipMalloc(&ctx->d_moe_tiles, cap * sizeof(MoeTile)));
+    HIP_TRY(hipMalloc(&ctx->d_moe_order, cap * sizeof(MoeTile)));
+    HIP_TRY(hipMalloc(&ctx->d_moe_keys, cap * sizeof(uint32_t)));
+    ctx->moe_cap = cap;
+  }
+  MoeTables tb{};
+  tb.counts = ctx->d_moe;
+  tb.n_tiles = ctx->d_moe + 256;
+  tb.claim = ctx->d_moe + 260;
+  tb.tiles = ctx->d_moe_tiles;
+  tb.keys = ctx->d_moe_keys;
+  tb.order = ctx->d_moe_order;
+
+  const int esz = 2;
+  MoeArgs a{};
+  a.X = static_cast<const uint16_t*>(X_gathered);
+  a.We = static_cast<const uint16_t*>(W_experts);
+  a.Y = Y; a.row_token = row_token; a.expert_off = expert_off; a.order = tb.order; a.n_tiles = tb.n_tiles;
+  a.claim = tb.claim; a.flags = shard_flags; a.status = ctx->d_status; a.trace = o.trace;
+  a.T = T; a.H = H; a.I = I; a.E = E; a.flag_rows = (int32_t)p.flag_rows; a.tiles_n = p.tiles_n;
+  a.epoch = e; a.timeout_ticks = timeout_ticks(o);
+  const int64_t n_items_max = max_tiles * p.tiles_n;
+  uint64_t* trace_rel = o.trace ? o.trace + n_items_max * 4 : nullptr;
+  const int64_t tile_bytes = p.flag_rows * H * esz;
+
+  // Routing and the grouped consumer, on the caller's stream.
+  auto route_and_compute = [&](const uint32_t* ranks, int grid) -> sgt_status {
+    HIP_TRY(launch_fill_u32(tb.counts, E, 0u, stream));
+    HIP_TRY(launch_moe_route(logits, T, E, topk, ranks, a.flag_rows, (uint32_t)p.n_flags, tb, expert_off, row_token,
+                             topk_ids, stream));
+    if (I > 0) {
+      sgt_status s2;
+      if ((s2 = mark(o, 0, stream)) != SGT_OK) return s2;
+      HIP_TRY(launch_moe_consumer(a, o.b_layout, o.out_dtype, (int)std::min<int64_t>(grid, n_items_max), stream));
+      if ((s2 = mark(o, 1, stream)) != SGT_OK) return s2;
+    }
+    return SGT_OK;
+  };
+
+  if (o.producer == SGT_PROD_PRESET) {
+    // X_gathered already holds every shard: all flags take the epoch.
+    HIP_TRY(launch_fill_u32(shard_flags, p.n_flags, e, stream));
+    if ((st = route_and_compute(nullptr, o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu)) != SGT_OK) return st;
+    return finish(ctx, o, stream);
+  }
+
+  int slot;
+  if ((st = next_slot(ctx, &slot)) != SGT_OK) return st;
+  const int n_items = build_schedule(p, W, o.rank, H, esz, o, X_shards, ctx->h_items[slot], true, ctx->h_ranks[slot]);
+  const int pwg = std::min(default_producer_wgs(o, ctx->n_cu), n_items);
+  // The schedule and the ranks go over on the caller's stream, before the fork,
+  // so both the producer and the routing see them.
+  HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], ctx->h_items[slot], n_items * sizeof(ProdItem), hipMemcpyHostToDevice,
+                         stream));
+  HIP_TRY(hipMemcpyAsync(ctx->d_ranks[slot], ctx->h_ranks[slot], p.n_flags * sizeof(uint32_t), hipMemcpyHostToDevice,
+                         stream));
+
+  if (o.producer == SGT_PROD_SERIAL) {
+    HIP_TRY(launch_ag_producer(X_gathered, shard_flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
+                               trace_rel, pwg, stream));
+    if ((st = route_and_compute(ctx->d_ranks[slot], o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu)) != SGT_OK)
+      return st;
+    HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
+    ctx->slot_used[slot] = true;
+    return finish(ctx, o, stream);
+  }
+
+  // Overlapped: producer on its own stream and CUs; routing, then the grouped
+  // consumer on the remaining CUs (one workgroup per CU).
+  HIP_TRY(hipEventRecord(ctx->ev_fork, stream));
+  HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
+  HIP_TRY(launch_ag_producer(X_gathered, shard_flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
+                             trace_rel, pwg, ctx->prod));
+  HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
+  if ((st = route_and_compute(ctx->d_ranks[slot], o.consumer_cus > 0 ? o.consumer_cus : std::max(1, ctx->n_cu - pwg))) !=
+      SGT_OK)
+    return st;
+  HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
+  HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
+  ctx->slot_used[slot] = true;
+  return finish(ctx, o, stream);
 }
 
 }  // extern "C"
