@@ -108,7 +108,10 @@ typedef struct sgt_opts {
   int32_t rs_tile;       /* GEMM+RS signal tile edge (rows = cols); 0 = 128                     */
   int32_t arrival_order; /* 0: each peer sends its tiles in order; 1: a seeded order per peer;
                             2: one seeded order over all remote tiles                             */
-  int32_t tile_waves;    /* bf16 consumer workgroup: 4 or 8 wave64s per 256 x 256 tile; 0 = 8   */
+  int32_t tile_waves;    /* bf16 consumer workgroup: 4 or 8 wave64s per tile; 0 = 8             */
+  int32_t tile_rows;     /* MoE grouped tile height: 128 or 256 rows; 0 = 256 (AllGather and
+                            GEMM+RS tiles are 256 x 256)                                          */
+  int32_t reserved0;     /* must be 0                                                             */
   uint64_t* trace;       /* optional device buffer, see sgt_trace_words(); NULL = off           */
   void* consumer_events[2]; /* optional hipEvent_t pair recorded on the consumer's stream right
                                before and after the consumer kernel launch (NULL = off)            */
@@ -124,6 +127,9 @@ SGT_API const char* sgt_status_str(int status);
 
 /* Detail of the last error on the calling thread ("" if none). */
 SGT_API const char* sgt_last_error(void);
+
+/* sizeof(sgt_opts) as this library was built (for bindings that mirror the struct). */
+SGT_API size_t sgt_opts_size(void);
 
 /* Fill *o with defaults: rank 0, bf16 in, fp32 out, K x N, CU producer, mesh
  * order, unthrottled, no jitter, 2000 ms timeout, no trace. */
@@ -212,7 +218,8 @@ SGT_API sgt_status sgt_rs_flag_count(int W, int64_t M, int64_t N, const sgt_opts
  *     Y[row]     = X_gathered[row_token[row]] * W_e          (fp32 or bf16)
  * Routing runs on the GPU; the shards arrive through the producer in signal
  * tiles of opts->flag_rows tokens (default: about 512 KiB per tile), the local
- * shard first; each grouped tile (expert, 256 rows of its group, 256 columns)
+ * shard first; each grouped tile (expert, opts->tile_rows rows of its group,
+ * 256 columns)
  * waits for exactly the signal tiles holding its rows' tokens.  Tiles are
  * claimed in the order their rows can arrive.
  * X_shards: host array of W device pointers, (T/W) x H bf16, 16-byte aligned.

@@ -72,8 +72,8 @@ struct RsArgs {
   uint64_t timeout_ticks;
 };
 
-// One grouped row tile of the MoE consumer: rows [r0, r0 + 256) of expert e's
-// group (clipped to the group's end), with the readiness key used to order it.
+// One grouped row tile of the MoE consumer: rows [r0, r0 + tile rows) of
+// expert e's group (clipped to the group's end).
 struct MoeTile {
   int32_t expert;
   int32_t r0;       // first row (index into the grouped rows of Y)
@@ -81,7 +81,10 @@ struct MoeTile {
 
 // Routing and work-list tables of one MoE call (device memory owned by the context).
 struct MoeTables {
-  uint32_t* counts;       // E: tokens routed to each expert
+  uint32_t* masks;        // ceil(E / 32) x T: bit e % 32 of word e / 32 set when token t chose e
+  uint32_t* partials;     // n_groups x E: tokens of each top-k token group routed to each expert
+  int32_t n_groups;       // token groups of the top-k kernel (tokens_per_group each, the last ragged)
+  int32_t tokens_per_group;
   uint32_t* n_tiles;      // 1: number of grouped row tiles
   uint32_t* claim;        // 1: next consumer work item to claim
   MoeTile* tiles;         // grouped row tiles, expert-major (written by the placement kernel)

@@ -49,13 +49,16 @@ constexpr int kStageBytes = kBM * kBK * 2;          // one operand, one stage: 3
 constexpr uint32_t kOOB = 0x80000000u;              // buffer offset that reads 0 / drops a store
 constexpr int kRsrcWord3 = 0x00020000;              // raw buffer, 32-bit data format (gfx9)
 
-template <int kW>
+// kR: rows of the tile (256, or 128 for the short tiles of ragged groups);
+// the tile is always 256 columns wide.
+template <int kW, int kR = kBM>
 struct Tile {
   static_assert(kW == 4 || kW == 8, "4 or 8 waves");
+  static_assert(kR == 256 || kR == 128, "256 or 128 rows");
   static constexpr int kThreads = 64 * kW;
-  static constexpr int kWaveRows = kBM / (kW / 2);  // 128 or 64 rows per wave
+  static constexpr int kWaveRows = kR / (kW / 2);   // 128, 64 or 32 rows per wave
   static constexpr int kMI = kWaveRows / 32;        // 32-row MFMA blocks per wave
-  static constexpr int kDmaLoads = kBM / kW / 8;    // 1 KiB DMA loads per wave per operand and stage
+  static constexpr int kDmaLoads = kBM / kW / 8;    // 1 KiB DMA loads per wave per 256-row operand and stage
 };
 
 __device__ __forceinline__ int lds_swz(int row, int chunk) {
@@ -69,15 +72,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-template <int kW>
+template <int kW, int kR = kBM>
 struct MfmaAcc {
-  f32x16_t v[Tile<kW>::kMI][4];
+  f32x16_t v[Tile<kW, kR>::kMI][4];
 };
 
-template <int kW>
-__device__ __forceinline__ void acc_zero(MfmaAcc<kW>& acc) {
+template <int kW, int kR>
+__device__ __forceinline__ void acc_zero(MfmaAcc<kW, kR>& acc) {
 #pragma unroll
-  for (int i = 0; i < Tile<kW>::kMI; ++i)
+  for (int i = 0; i < Tile<kW, kR>::kMI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -87,45 +90,51 @@ __device__ __forceinline__ void acc_zero(MfmaAcc<kW>& acc) {
 // A k-contiguous operand tile (A, or B stored N x K) seen by the DMA loader:
 // a buffer resource whose record range ends after the last valid row (later
 // rows read as zero).  Lane l of wave w fills, with its load i, LDS row
-// r = (256 / kW) w + 8 i + l / 8 at physical chunk l % 8, i.e. logical chunk
+// r = (kRows / kW) w + 8 i + l / 8 at physical chunk l % 8, i.e. logical chunk
 // (l % 8) ^ swz(r) = (l % 8) ^ (l / 8) ^ (i % 4).  row_off[i] is the byte
 // offset of that row (rows `ld` elements apart, or gathered rows for MoE;
 // kOOB for a row that does not exist); all offsets are 32-bit.
 struct KRows {
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t row_off[8];  // entries [0, Tile<kW>::kDmaLoads) are used
+  uint32_t row_off[8];  // entries [0, kRows / kW / 8) are used
   uint32_t chunk[4];   // this lane's logical chunk byte offset for i % 4
 };
 
+// Logical chunk of this lane's load i: its LDS row r has r % 8 = lane / 8
+// and (r / 8) % 4 = (w L + i) % 4 for L = kRows / kW / 8 loads per wave (just
+// i % 4 when L is a multiple of 4).
+template <int kW, int kRows = kBM>
 __device__ __forceinline__ void krows_chunks(KRows& kr) {
-  const int lane = threadIdx.x & 63;
+  constexpr int L = kRows / kW / 8;
+  const int lane = threadIdx.x & 63, w = wave_id();
 #pragma unroll
-  for (int q = 0; q < 4; ++q) kr.chunk[q] = (uint32_t)((((lane & 7) ^ (lane >> 3) ^ q) & 7) * 16);
+  for (int q = 0; q < 4; ++q) kr.chunk[q] = (uint32_t)((((lane & 7) ^ (lane >> 3) ^ ((w * L + q) & 3)) & 7) * 16);
 }
 
-// LDS row filled by this lane's load i.
-template <int kW>
+// LDS row filled by this lane's load i of an operand of kRows rows.
+template <int kW, int kRows = kBM>
 __device__ __forceinline__ int dma_row(int i) {
-  return (kBM / kW) * wave_id() + 8 * i + ((threadIdx.x & 63) >> 3);
+  return (kRows / kW) * wave_id() + 8 * i + ((threadIdx.x & 63) >> 3);
 }
 
 // Strided rows: row r at element offset r * ld from base; rows >= rows_valid are zero.
-template <int kW>
+template <int kW, int kRows = kBM>
 __device__ __forceinline__ KRows krows_strided(const uint16_t* base, int64_t rows_valid, int64_t ld) {
   KRows kr;
-  const int64_t rows = rows_valid < kBM ? rows_valid : kBM;
+  const int64_t rows = rows_valid < kRows ? rows_valid : kRows;
   kr.rsrc = make_rsrc(base, rows > 0 ? (uint64_t)rows * (uint64_t)ld * 2u : 0u);
 #pragma unroll
-  for (int i = 0; i < Tile<kW>::kDmaLoads; ++i) kr.row_off[i] = (uint32_t)(dma_row<kW>(i) * ld * 2);
-  krows_chunks(kr);
+  for (int i = 0; i < kRows / kW / 8; ++i) kr.row_off[i] = (uint32_t)(dma_row<kW, kRows>(i) * ld * 2);
+  krows_chunks<kW, kRows>(kr);
   return kr;
 }
 
-// Issue the DMA of K step [k0, k0 + 64) of a k-contiguous operand into `stage`.
-// Chunks at or past K (including whole steps past the end) read as zero.
-template <int kW>
+// Issue the DMA of K step [k0, k0 + 64) of a k-contiguous operand of kRows
+// rows into `stage`.  Chunks at or past K (including whole steps past the end)
+// read as zero.
+template <int kW, int kRows = kBM>
 __device__ __forceinline__ void dma_stage(const KRows& kr, uint8_t* stage, int64_t k0, int64_t K) {
-  constexpr int L = Tile<kW>::kDmaLoads;
+  constexpr int L = kRows / kW / 8;
   const int w = wave_id();
   const uint32_t kbyte = (uint32_t)(k0 * 2);
   const int64_t rem = (K - k0) * 2;                  // valid bytes of this step's rows
@@ -188,16 +197,16 @@ struct KNLoader {
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <int kW>
+template <int kW, int kR>
 __device__ __forceinline__ void read_frags(const uint8_t* sA, const uint8_t* sB, int kk,
-                                           bf16x8_t (&a)[Tile<kW>::kMI], bf16x8_t (&b)[4]) {
+                                           bf16x8_t (&a)[Tile<kW, kR>::kMI], bf16x8_t (&b)[4]) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 31, chunk = 2 * kk + (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < Tile<kW>::kMI; ++i)
-    a[i] = *reinterpret_cast<const bf16x8_t*>(sA + lds_swz(wm * Tile<kW>::kWaveRows + i * 32 + lr, chunk));
+  for (int i = 0; i < Tile<kW, kR>::kMI; ++i)
+    a[i] = *reinterpret_cast<const bf16x8_t*>(sA + lds_swz(wm * Tile<kW, kR>::kWaveRows + i * 32 + lr, chunk));
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     b[j] = *reinterpret_cast<const bf16x8_t*>(sB + lds_swz(wn * 128 + j * 32 + lr, chunk));
@@ -210,44 +219,46 @@ __device__ __forceinline__ void read_frags(const uint8_t* sA, const uint8_t* sB,
 // exposed.  The scheduling barriers keep the compiler from undoing that order
 // and from hoisting the caller's DMA wait and barrier above the MFMAs (they
 // touch no memory, so it otherwise would).
-template <int kW, int KK>
+template <int kW, int kR, int KK>
 __device__ __forceinline__ void mfma_substep(const uint8_t* sA, const uint8_t* sB,
-                                             bf16x8_t (&a)[2][Tile<kW>::kMI], bf16x8_t (&b)[2][4],
-                                             MfmaAcc<kW>& acc) {
-  constexpr int MI = Tile<kW>::kMI;
+                                             bf16x8_t (&a)[2][Tile<kW, kR>::kMI], bf16x8_t (&b)[2][4],
+                                             MfmaAcc<kW, kR>& acc) {
+  constexpr int MI = Tile<kW, kR>::kMI;
   constexpr int cur = KK & 1;
-  if constexpr (KK < 3) read_frags<kW>(sA, sB, KK + 1, a[cur ^ 1], b[cur ^ 1]);
+  if constexpr (KK < 3) read_frags<kW, kR>(sA, sB, KK + 1, a[cur ^ 1], b[cur ^ 1]);
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j], acc.v[i][j], 0, 0, 0);
   if constexpr (KK < 3) {
-    constexpr int R = MI + 4;  // reads of the next substep
+    constexpr int R = MI + 4;                // reads of the next substep
+    constexpr int P = R < 4 * MI ? R : 4 * MI;  // (MFMA, read) pairs
 #pragma unroll
-    for (int g = 0; g < R; ++g) {
+    for (int g = 0; g < P; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, KK);  // 1 MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, KK);  // 1 LDS read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * MI - R, KK);
+    if constexpr (4 * MI > P) __builtin_amdgcn_sched_group_barrier(0x008, 4 * MI - P, KK);
+    if constexpr (R > P) __builtin_amdgcn_sched_group_barrier(0x100, R - P, KK);
   }
   // one scheduling region per substep: its MFMAs and the next substep's reads
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int kW>
-__device__ __forceinline__ void mfma_stage(const uint8_t* sA, const uint8_t* sB, MfmaAcc<kW>& acc) {
-  bf16x8_t a[2][Tile<kW>::kMI], b[2][4];
-  read_frags<kW>(sA, sB, 0, a[0], b[0]);
+template <int kW, int kR>
+__device__ __forceinline__ void mfma_stage(const uint8_t* sA, const uint8_t* sB, MfmaAcc<kW, kR>& acc) {
+  bf16x8_t a[2][Tile<kW, kR>::kMI], b[2][4];
+  read_frags<kW, kR>(sA, sB, 0, a[0], b[0]);
   __builtin_amdgcn_sched_barrier(0);
-  mfma_substep<kW, 0>(sA, sB, a, b, acc);
-  mfma_substep<kW, 1>(sA, sB, a, b, acc);
-  mfma_substep<kW, 2>(sA, sB, a, b, acc);
-  mfma_substep<kW, 3>(sA, sB, a, b, acc);
+  mfma_substep<kW, kR, 0>(sA, sB, a, b, acc);
+  mfma_substep<kW, kR, 1>(sA, sB, a, b, acc);
+  mfma_substep<kW, kR, 2>(sA, sB, a, b, acc);
+  mfma_substep<kW, kR, 3>(sA, sB, a, b, acc);
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Full K loop for one 256 x 256 tile.  A is k-contiguous (DMA); B is N x K
+// Full K loop for one kR x 256 tile.  A is k-contiguous (DMA); B is N x K
 // (kBNK, DMA) or K x N (register transpose).  The two stages are distinct LDS
 // objects and the loop is unrolled by two, so the compiler can see that a DMA
 // into one stage never aliases the MFMA reads of the other and does not wait
@@ -256,39 +267,39 @@ __device__ __forceinline__ void mfma_stage(const uint8_t* sA, const uint8_t* sB,
 // the stage with zeros (which add nothing) without touching memory; a
 // conditional MFMA block would split the accumulators' live ranges and force
 // copies.  The caller must have passed a barrier since the previous use.
-template <int kW, bool kBNK>
+template <int kW, bool kBNK, int kR = kBM>
 __device__ __forceinline__ void gemm_tile(const KRows& ka, const KRows& kb_nk, const uint16_t* B_kn, int64_t N,
-                                          int64_t n0, int64_t K, MfmaAcc<kW>& acc) {
-  __shared__ __attribute__((aligned(1024))) uint8_t sA0[kStageBytes];
+                                          int64_t n0, int64_t K, MfmaAcc<kW, kR>& acc) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[kR * kBK * 2];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t sA1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[kR * kBK * 2];
   __shared__ __attribute__((aligned(1024))) uint8_t sB1[kStageBytes];
-  acc_zero<kW>(acc);
+  acc_zero<kW, kR>(acc);
   const int64_t nk2 = ((K + kBK - 1) / kBK + 1) & ~int64_t(1);
   KNLoader<kW> kn;
   if constexpr (!kBNK) {
     kn.init(B_kn, K, N, n0);
     kn.load(0);
   }
-  dma_stage<kW>(ka, sA0, 0, K);
+  dma_stage<kW, kR>(ka, sA0, 0, K);
   if constexpr (kBNK) dma_stage<kW>(kb_nk, sB0, 0, K);
   else kn.store(sB0);
   wait_dma();
   __syncthreads();
   for (int64_t kt = 0; kt < nk2; kt += 2) {
     // stage 0 computes while stage 1 fills
-    dma_stage<kW>(ka, sA1, (kt + 1) * kBK, K);
+    dma_stage<kW, kR>(ka, sA1, (kt + 1) * kBK, K);
     if constexpr (kBNK) dma_stage<kW>(kb_nk, sB1, (kt + 1) * kBK, K);
     else kn.load((kt + 1) * kBK);
-    mfma_stage<kW>(sA0, sB0, acc);
+    mfma_stage<kW, kR>(sA0, sB0, acc);
     if constexpr (!kBNK) kn.store(sB1);
     wait_dma();
     __syncthreads();
     // stage 1 computes while stage 0 fills (past the end: zeros, unused)
-    dma_stage<kW>(ka, sA0, (kt + 2) * kBK, K);
+    dma_stage<kW, kR>(ka, sA0, (kt + 2) * kBK, K);
     if constexpr (kBNK) dma_stage<kW>(kb_nk, sB0, (kt + 2) * kBK, K);
     else kn.load((kt + 2) * kBK);
-    mfma_stage<kW>(sA1, sB1, acc);
+    mfma_stage<kW, kR>(sA1, sB1, acc);
     if constexpr (!kBNK) kn.store(sB0);
     wait_dma();
     __syncthreads();
@@ -311,14 +322,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // 8 (r / 4) + 4 (lane / 32) + r % 4, column 128 wn + 32 j + lane % 32: the
 // 32 x 32 MFMA result puts column lane % 32 in a lane and those rows in its
 // 16 registers.
-template <int kW, bool kOutBf16, int kCpol = 0>
+template <int kW, bool kOutBf16, int kCpol = 0, int kR = kBM>
 __device__ __forceinline__ void store_tile(void* C, int64_t M, int64_t N, int64_t m0, int64_t n0,
-                                           const MfmaAcc<kW>& acc) {
+                                           const MfmaAcc<kW, kR>& acc) {
   const int esz = kOutBf16 ? 2 : 4;
   const uint8_t* base = static_cast<const uint8_t*>(C) + (m0 * N + n0) * esz;
   // Record range: from the tile origin to the end of its last valid row (at most
   // 256 rows, < 2^31 bytes), so an offset of kOOB or more is always dropped.
-  const int64_t rows = M - m0 < kBM ? M - m0 : kBM;
+  const int64_t rows = M - m0 < kR ? M - m0 : kR;
   const int64_t valid = rows * N - n0;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, valid > 0 ? (uint64_t)valid * esz : 0u);
   const int lane = threadIdx.x & 63, w = wave_id();
@@ -328,10 +339,10 @@ __device__ __forceinline__ void store_tile(void* C, int64_t M, int64_t N, int64_
     const int col = (w & 1) * 128 + j * 32 + lr;
     const uint32_t voff = (n0 + col < N) ? (uint32_t)((4 * lk * N + col) * esz) : kOOB;
 #pragma unroll
-    for (int i = 0; i < Tile<kW>::kMI; ++i)
+    for (int i = 0; i < Tile<kW, kR>::kMI; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = (w >> 1) * Tile<kW>::kWaveRows + i * 32 + 8 * (r >> 2) + (r & 3);  // + 4 lk in voff
+        const int row = (w >> 1) * Tile<kW, kR>::kWaveRows + i * 32 + 8 * (r >> 2) + (r & 3);  // + 4 lk in voff
         // kOOB + (row offset < 2^31) stays out of range: no select needed
         const uint32_t off = voff + (uint32_t)(row * N * esz);
         if constexpr (kOutBf16)

@@ -3,8 +3,8 @@
 // overlap": wait for the data a tile reads, then compute it; DITRON article,
 // "three-level tiling": device-level tiles sized by each expert's token count).
 //
-// Work item = (grouped row tile, column tile): rows [r0, r0 + 256) of one
-// expert's group (clipped to the group) times 256 columns of that expert's
+// Work item = (grouped row tile, column tile): rows [r0, r0 + kR) of one
+// expert's group (clipped to the group; kR = 128 or 256) times 256 columns of that expert's
 // weight.  Persistent workgroups claim items from the readiness-ordered list
 // with an atomic counter.  Before loading, wave 0 polls, lane by lane, the
 // flag of the signal tile that holds each row's token (a tile waits for
@@ -22,14 +22,16 @@ namespace sgt {
 namespace {
 
 // Wait until every row of the tile has arrived: lane l of wave 0 watches the
-// signal tiles of rows l, l + 64, l + 128, l + 192.  Returns the workgroup's
+// signal tiles of rows l, l + 64, ... (kR / 64 rows).  Returns the workgroup's
 // verdict (false after a timeout, recorded in the status word).
+template <int kR>
 __device__ __forceinline__ bool wait_tile_rows(const MoeArgs& a, const int32_t* tok, int rows_valid, int* ok) {
+  constexpr int Q = kR / 64;
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    int64_t f[4];
+    int64_t f[Q];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < Q; ++q) {
       const int r = lane + 64 * q;
       f[q] = r < rows_valid ? (int64_t)(tok[r] / a.flag_rows) : -1;
     }
@@ -40,7 +42,7 @@ __device__ __forceinline__ bool wait_tile_rows(const MoeArgs& a, const int32_t* 
       uint32_t seen = 0;
       int64_t which = -1;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < Q; ++q) {
         if (f[q] >= 0) {
           const uint32_t v = flag_peek(a.flags + f[q]);
           if (flag_is_set(v, a.epoch)) {
@@ -67,7 +69,7 @@ __device__ __forceinline__ bool wait_tile_rows(const MoeArgs& a, const int32_t* 
   return *ok != 0;
 }
 
-template <int kW, bool kBNK, bool kOutBf16>
+template <int kW, int kR, bool kBNK, bool kOutBf16>
 __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) moe_consumer_bf16(MoeArgs a) {
   __shared__ int item_s, ok;
   const int64_t n_items = (int64_t)(*a.n_tiles) * a.tiles_n;
@@ -81,11 +83,11 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) moe_consumer_bf16(MoeAr
     const int e = mt.expert;
     const int64_t r0 = mt.r0;
     const int64_t r_end = a.expert_off[e + 1];
-    const int rows_valid = (int)(r_end - r0 < kBM ? r_end - r0 : kBM);
+    const int rows_valid = (int)(r_end - r0 < kR ? r_end - r0 : kR);
     const int32_t* tok = a.row_token + r0;
     uint64_t t_wait = 0;
     if (a.trace && threadIdx.x == 0) t_wait = clock_ticks();
-    if (!wait_tile_rows(a, tok, rows_valid, &ok)) return;
+    if (!wait_tile_rows<kR>(a, tok, rows_valid, &ok)) return;
     if (a.trace && threadIdx.x == 0) {
       a.trace[item * 4 + 0] = t_wait;
       a.trace[item * 4 + 1] = clock_ticks();
@@ -96,32 +98,43 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) moe_consumer_bf16(MoeAr
     KRows ka;
     ka.rsrc = make_rsrc(a.X, (uint64_t)a.T * (uint64_t)a.H * 2u);
 #pragma unroll
-    for (int i = 0; i < Tile<kW>::kDmaLoads; ++i) {
-      const int r = dma_row<kW>(i);
+    for (int i = 0; i < kR / kW / 8; ++i) {
+      const int r = dma_row<kW, kR>(i);
       ka.row_off[i] = r < rows_valid ? (uint32_t)((int64_t)tok[r] * a.H * 2) : kOOB;
     }
-    krows_chunks(ka);
+    krows_chunks<kW, kR>(ka);
     // B: expert e's weight, H x I (KN) or I x H (NK).
     const uint16_t* Be = a.We + (int64_t)e * a.H * a.I;
     KRows kb = ka;
     if constexpr (kBNK) kb = krows_strided<kW>(Be + n0 * a.H, a.I - n0, a.H);
-    MfmaAcc<kW> acc;
-    gemm_tile<kW, kBNK>(ka, kb, Be, a.I, n0, a.H, acc);
-    store_tile<kW, kOutBf16>(a.Y, r0 + rows_valid, a.I, r0, n0, acc);
+    MfmaAcc<kW, kR> acc;
+    gemm_tile<kW, kBNK, kR>(ka, kb, Be, a.I, n0, a.H, acc);
+    store_tile<kW, kOutBf16, 0, kR>(a.Y, r0 + rows_valid, a.I, r0, n0, acc);
     if (a.trace && threadIdx.x == 0) a.trace[item * 4 + 2] = clock_ticks();
   }
 }
 
 }  // namespace
 
-hipError_t launch_moe_consumer(const MoeArgs& a, int b_layout, int out_dtype, int grid, hipStream_t stream) {
-  constexpr int kW = 8;
+template <int kW, int kR>
+static void launch_moe(const MoeArgs& a, bool nk, bool ob, int grid, hipStream_t stream) {
   const dim3 blk(Tile<kW>::kThreads);
+  if (nk && ob) hipLaunchKernelGGL((moe_consumer_bf16<kW, kR, true, true>), dim3(grid), blk, 0, stream, a);
+  if (nk && !ob) hipLaunchKernelGGL((moe_consumer_bf16<kW, kR, true, false>), dim3(grid), blk, 0, stream, a);
+  if (!nk && ob) hipLaunchKernelGGL((moe_consumer_bf16<kW, kR, false, true>), dim3(grid), blk, 0, stream, a);
+  if (!nk && !ob) hipLaunchKernelGGL((moe_consumer_bf16<kW, kR, false, false>), dim3(grid), blk, 0, stream, a);
+}
+
+hipError_t launch_moe_consumer(const MoeArgs& a, int b_layout, int out_dtype, int tile_rows, int tile_waves, int grid,
+                               hipStream_t stream) {
   const bool nk = b_layout == 1, ob = out_dtype == 1;
-  if (nk && ob) hipLaunchKernelGGL((moe_consumer_bf16<kW, true, true>), dim3(grid), blk, 0, stream, a);
-  if (nk && !ob) hipLaunchKernelGGL((moe_consumer_bf16<kW, true, false>), dim3(grid), blk, 0, stream, a);
-  if (!nk && ob) hipLaunchKernelGGL((moe_consumer_bf16<kW, false, true>), dim3(grid), blk, 0, stream, a);
-  if (!nk && !ob) hipLaunchKernelGGL((moe_consumer_bf16<kW, false, false>), dim3(grid), blk, 0, stream, a);
+  if (tile_rows == 256) {
+    if (tile_waves == 4) launch_moe<4, 256>(a, nk, ob, grid, stream);
+    else launch_moe<8, 256>(a, nk, ob, grid, stream);
+  } else {
+    if (tile_waves == 4) launch_moe<4, 128>(a, nk, ob, grid, stream);
+    else launch_moe<8, 128>(a, nk, ob, grid, stream);
+  }
   return hipGetLastError();
 }
 

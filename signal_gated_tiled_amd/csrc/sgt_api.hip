@@ -32,12 +32,13 @@ int ag_panel_rows(int in_dtype);
 int ag_panel_cols(int in_dtype);
 hipError_t launch_gemm_rs(const RsArgs& a, int grid, hipStream_t stream);
 int rs_gemm_tile();
-int moe_route_rows();
 int moe_max_tiles_per_expert();
+int moe_tokens_per_group(int64_t T, int k);
 hipError_t launch_moe_route(const float* logits, int64_t T, int E, int k, const uint32_t* rank_of_flag,
-                            int32_t flag_rows, uint32_t n_flags, const MoeTables& tb, int32_t* expert_off,
-                            int32_t* row_token, int32_t* topk_ids, hipStream_t stream);
-hipError_t launch_moe_consumer(const MoeArgs& a, int b_layout, int out_dtype, int grid, hipStream_t stream);
+                            int32_t flag_rows, uint32_t n_flags, int tile_rows, const MoeTables& tb,
+                            int32_t* expert_off, int32_t* row_token, int32_t* topk_ids, hipStream_t stream);
+hipError_t launch_moe_consumer(const MoeArgs& a, int b_layout, int out_dtype, int tile_rows, int tile_waves, int grid,
+                               hipStream_t stream);
 inline int kBMrs() { return rs_gemm_tile(); }
 }  // namespace sgt
 
@@ -80,13 +81,17 @@ struct sgt_ctx {
   uint32_t* d_counters = nullptr;  // work-claim counters, zeroed before each launch that uses them
   ProdItem* h_items[kSlots] = {};
   ProdItem* d_items[kSlots] = {};
-  uint32_t* h_ranks[kSlots] = {};  // arrival rank of each signal tile (MoE work ordering)
-  uint32_t* d_ranks[kSlots] = {};
-  uint32_t* d_moe = nullptr;       // MoE counts (256), tile count, claim counter
-  MoeTile* d_moe_tiles = nullptr;  // MoE row tiles, expert-major and sorted; grows on demand
+  uint32_t* h_ranks[kSlots] = {};  // arrival rank of each signal tile (MoE work ordering), pinned host
+  uint32_t* d_ranks[kSlots] = {};  // the same memory as the GPU addresses it (read in place, no copy)
+  uint32_t* d_moe = nullptr;       // MoE tile count and claim counter
+  MoeTile* d_moe_tiles = nullptr;  // MoE row tiles, expert-major and sorted; grow on demand
   MoeTile* d_moe_order = nullptr;
   uint32_t* d_moe_keys = nullptr;
   int64_t moe_cap = 0;
+  uint32_t* d_moe_masks = nullptr; // MoE token bitmasks and per-group counts; grow on demand
+  int64_t moe_masks_cap = 0;
+  uint32_t* d_moe_partials = nullptr;
+  int64_t moe_partials_cap = 0;
   hipEvent_t slot_ev[kSlots] = {};
   bool slot_used[kSlots] = {};
   int slot = 0;
@@ -149,6 +154,9 @@ sgt_status check_opts(const sgt_opts* o, int W) {
   if (o->arrival_order < 0 || o->arrival_order > 2) return fail(SGT_EINVAL, "arrival_order %d", o->arrival_order);
   if (o->tile_waves != 0 && o->tile_waves != 4 && o->tile_waves != 8)
     return fail(SGT_EINVAL, "tile_waves %d (0, 4 or 8)", o->tile_waves);
+  if (o->tile_rows != 0 && o->tile_rows != 128 && o->tile_rows != 256)
+    return fail(SGT_EINVAL, "tile_rows %d (0, 128 or 256)", o->tile_rows);
+  if (o->reserved0 != 0) return fail(SGT_EINVAL, "reserved0 must be 0");
   return SGT_OK;
 }
 
@@ -308,6 +316,8 @@ const char* sgt_status_str(int st) {
 
 const char* sgt_last_error(void) { return g_last_error.c_str(); }
 
+size_t sgt_opts_size(void) { return sizeof(sgt_opts); }
+
 void sgt_opts_init(sgt_opts* o) {
   if (!o) return;
   std::memset(o, 0, sizeof *o);
@@ -348,7 +358,7 @@ sgt_status sgt_ctx_create(sgt_ctx** out, int device) {
     chk(hipHostMalloc(&c->h_items[s], kItemsCap * sizeof(ProdItem), hipHostMallocDefault), "hipHostMalloc");
     chk(hipMalloc(&c->d_items[s], kItemsCap * sizeof(ProdItem)), "hipMalloc(items)");
     chk(hipHostMalloc(&c->h_ranks[s], kItemsCap * sizeof(uint32_t), hipHostMallocDefault), "hipHostMalloc");
-    chk(hipMalloc(&c->d_ranks[s], kItemsCap * sizeof(uint32_t)), "hipMalloc(ranks)");
+    if (st == SGT_OK) chk(hipHostGetDevicePointer((void**)&c->d_ranks[s], c->h_ranks[s], 0), "hipHostGetDevicePointer");
     chk(hipEventCreateWithFlags(&c->slot_ev[s], hipEventDisableTiming), "hipEventCreate");
   }
   if (st != SGT_OK) {
@@ -370,7 +380,6 @@ sgt_status sgt_ctx_destroy(sgt_ctx* c) {
     if (c->h_items[s]) (void)hipHostFree(c->h_items[s]);
     if (c->d_items[s]) (void)hipFree(c->d_items[s]);
     if (c->h_ranks[s]) (void)hipHostFree(c->h_ranks[s]);
-    if (c->d_ranks[s]) (void)hipFree(c->d_ranks[s]);
     if (c->slot_ev[s]) (void)hipEventDestroy(c->slot_ev[s]);
   }
   if (c->d_status) (void)hipFree(c->d_status);
@@ -379,6 +388,8 @@ sgt_status sgt_ctx_destroy(sgt_ctx* c) {
   if (c->d_moe_tiles) (void)hipFree(c->d_moe_tiles);
   if (c->d_moe_order) (void)hipFree(c->d_moe_order);
   if (c->d_moe_keys) (void)hipFree(c->d_moe_keys);
+  if (c->d_moe_masks) (void)hipFree(c->d_moe_masks);
+  if (c->d_moe_partials) (void)hipFree(c->d_moe_partials);
   if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
   if (c->ev_join) (void)hipEventDestroy(c->ev_join);
   if (c->prod) (void)hipStreamDestroy(c->prod);
@@ -606,11 +617,11 @@ sgt_status sgt_gemm_rs(sgt_ctx* ctx, const void* A_local, const void* B, const f
   return finish(ctx, o, stream);
 }
 
+static int moe_tile_rows(const sgt_opts& o) { return o.tile_rows > 0 ? o.tile_rows : 256; }
+
 // Upper bound of the grouped row tiles of a routing: sum over experts of
-// ceil(n_e / 256) <= T * topk / 256 + E.
-static int64_t moe_max_tiles(int64_t T, int E, int topk) {
-  return T * topk / moe_route_rows() + E;
-}
+// ceil(n_e / rows) <= T * topk / rows + E.
+static int64_t moe_max_tiles(int64_t T, int E, int topk, int rows) { return T * topk / rows + E; }
 
 int64_t sgt_moe_trace_words(int W, int64_t T, int64_t H, int64_t I, int E, int topk, const sgt_opts* opts) {
   sgt_opts o;
@@ -619,7 +630,8 @@ int64_t sgt_moe_trace_words(int W, int64_t T, int64_t H, int64_t I, int E, int t
   sgt_status st = plan_ag(W, T, H, I, o, &p);
   if (st != SGT_OK) return st;
   if (E < 1 || topk < 1 || topk > E) return fail(SGT_EINVAL, "bad E / topk");
-  return moe_max_tiles(T, E, topk) * p.tiles_n * 4 + p.n_flags;
+  if (o.tile_rows != 0 && o.tile_rows != 128 && o.tile_rows != 256) return fail(SGT_EINVAL, "tile_rows");
+  return moe_max_tiles(T, E, topk, moe_tile_rows(o)) * p.tiles_n * 4 + p.n_flags;
 }
 
 sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void* W_experts, const float* logits,
@@ -634,16 +646,17 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   if (E < 1 || E > 256 || topk < 1 || topk > E) return fail(SGT_EINVAL, "need 1 <= topk <= E <= 256 (E=%d topk=%d)", E, topk);
   if (T < 0 || H < 1 || I < 0) return fail(SGT_EINVAL, "bad shape T=%lld H=%lld I=%lld", (long long)T, (long long)H,
                                            (long long)I);
-  if (T > (int64_t)moe_max_tiles_per_expert() * moe_route_rows())
+  const int rows = moe_tile_rows(o);
+  if (T > (int64_t)moe_max_tiles_per_expert() * rows)
     return fail(SGT_EUNSUPPORTED, "T = %lld tokens exceeds %lld", (long long)T,
-                (long long)moe_max_tiles_per_expert() * moe_route_rows());
+                (long long)moe_max_tiles_per_expert() * rows);
   AgPlan p;
   if ((st = plan_ag(W, T, H, I, o, &p)) != SGT_OK) return st;
   const int64_t lim = (int64_t)1 << 31;
-  if (T * H * 2 >= lim || (int64_t)moe_route_rows() * H * 2 >= lim || (int64_t)moe_route_rows() * I * 4 >= lim ||
+  if (T * H * 2 >= lim || (int64_t)256 * H * 2 >= lim || (int64_t)256 * I * 4 >= lim ||
       (o.b_layout == SGT_KN && H * I * 2 >= lim))
     return fail(SGT_EUNSUPPORTED, "T x H or one expert's H x I too large for 32-bit offsets");
-  if (moe_max_tiles(T, E, topk) * p.tiles_n >= lim) return fail(SGT_EUNSUPPORTED, "too many grouped tiles");
+  if (moe_max_tiles(T, E, topk, rows) * p.tiles_n >= lim) return fail(SGT_EUNSUPPORTED, "too many grouped tiles");
   if (T > 0) {
     // W_experts and Y are read / written only when I > 0
     if (!X_shards || !logits || !X_gathered || !expert_off || !row_token || !topk_ids || !shard_flags ||
@@ -667,26 +680,50 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
     return finish(ctx, o, stream);
   }
 
-  // Work-list tables: grow (after draining the device) when a larger routing needs more.
-  const int64_t max_tiles = moe_max_tiles(T, E, topk);
-  if (ctx->moe_cap < max_tiles) {
+  // Routing tables: grow (after draining the device) when a larger routing needs more.
+  const int64_t max_tiles = moe_max_tiles(T, E, topk, rows);
+  const int tpg = moe_tokens_per_group(T, topk);
+  const int64_t n_groups = (T + tpg - 1) / tpg;
+  const int64_t mask_words = (int64_t)((E + 31) / 32) * T, partial_words = n_groups * E;
+  if (ctx->moe_cap < max_tiles || ctx->moe_masks_cap < mask_words || ctx->moe_partials_cap < partial_words) {
     HIP_TRY(hipDeviceSynchronize());
-    if (ctx->d_moe_tiles) (void)hipFree(ctx->d_moe_tiles);
-    if (ctx->d_moe_order) (void)hipFree(ctx->d_moe_order);
-    if (ctx->d_moe_keys) (void)hipFree(ctx->d_moe_keys);
-    ctx->d_moe_tiles = ctx->d_moe_order = nullptr;
-    ctx->d_moe_keys = nullptr;
-    ctx->moe_cap = 0;
-    const int64_t cap = std::max<int64_t>(max_tiles, 1024);
-    HIP_TRY(hipMalloc(&ctx->d_moe_tiles, cap * sizeof(MoeTile)));
-    HIP_TRY(hipMalloc(&ctx->d_moe_order, cap * sizeof(MoeTile)));
-    HIP_TRY(hipMalloc(&ctx->d_moe_keys, cap * sizeof(uint32_t)));
-    ctx->moe_cap = cap;
+    if (ctx->moe_cap < max_tiles) {
+      if (ctx->d_moe_tiles) (void)hipFree(ctx->d_moe_tiles);
+      if (ctx->d_moe_order) (void)hipFree(ctx->d_moe_order);
+      if (ctx->d_moe_keys) (void)hipFree(ctx->d_moe_keys);
+      ctx->d_moe_tiles = ctx->d_moe_order = nullptr;
+      ctx->d_moe_keys = nullptr;
+      ctx->moe_cap = 0;
+      const int64_t cap = std::max<int64_t>(max_tiles, 1024);
+      HIP_TRY(hipMalloc(&ctx->d_moe_tiles, cap * sizeof(MoeTile)));
+      HIP_TRY(hipMalloc(&ctx->d_moe_order, cap * sizeof(MoeTile)));
+      HIP_TRY(hipMalloc(&ctx->d_moe_keys, cap * sizeof(uint32_t)));
+      ctx->moe_cap = cap;
+    }
+    if (ctx->moe_masks_cap < mask_words) {
+      if (ctx->d_moe_masks) (void)hipFree(ctx->d_moe_masks);
+      ctx->d_moe_masks = nullptr;
+      ctx->moe_masks_cap = 0;
+      const int64_t cap = std::max<int64_t>(mask_words, 1 << 16);
+      HIP_TRY(hipMalloc(&ctx->d_moe_masks, cap * sizeof(uint32_t)));
+      ctx->moe_masks_cap = cap;
+    }
+    if (ctx->moe_partials_cap < partial_words) {
+      if (ctx->d_moe_partials) (void)hipFree(ctx->d_moe_partials);
+      ctx->d_moe_partials = nullptr;
+      ctx->moe_partials_cap = 0;
+      const int64_t cap = std::max<int64_t>(partial_words, 1 << 16);
+      HIP_TRY(hipMalloc(&ctx->d_moe_partials, cap * sizeof(uint32_t)));
+      ctx->moe_partials_cap = cap;
+    }
   }
   MoeTables tb{};
-  tb.counts = ctx->d_moe;
-  tb.n_tiles = ctx->d_moe + 256;
-  tb.claim = ctx->d_moe + 260;
+  tb.masks = ctx->d_moe_masks;
+  tb.partials = ctx->d_moe_partials;
+  tb.n_groups = (int32_t)n_groups;
+  tb.tokens_per_group = tpg;
+  tb.n_tiles = ctx->d_moe;
+  tb.claim = ctx->d_moe + 4;
   tb.tiles = ctx->d_moe_tiles;
   tb.keys = ctx->d_moe_keys;
   tb.order = ctx->d_moe_order;
@@ -705,13 +742,13 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
 
   // Routing and the grouped consumer, on the caller's stream.
   auto route_and_compute = [&](const uint32_t* ranks, int grid) -> sgt_status {
-    HIP_TRY(launch_fill_u32(tb.counts, E, 0u, stream));
-    HIP_TRY(launch_moe_route(logits, T, E, topk, ranks, a.flag_rows, (uint32_t)p.n_flags, tb, expert_off, row_token,
-                             topk_ids, stream));
+    HIP_TRY(launch_moe_route(logits, T, E, topk, ranks, a.flag_rows, (uint32_t)p.n_flags, rows, tb, expert_off,
+                             row_token, topk_ids, stream));
     if (I > 0) {
       sgt_status s2;
       if ((s2 = mark(o, 0, stream)) != SGT_OK) return s2;
-      HIP_TRY(launch_moe_consumer(a, o.b_layout, o.out_dtype, (int)std::min<int64_t>(grid, n_items_max), stream));
+      HIP_TRY(launch_moe_consumer(a, o.b_layout, o.out_dtype, rows, o.tile_waves ? o.tile_waves : 8,
+                                  (int)std::min<int64_t>(grid, n_items_max), stream));
       if ((s2 = mark(o, 1, stream)) != SGT_OK) return s2;
     }
     return SGT_OK;
@@ -728,14 +765,12 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   if ((st = next_slot(ctx, &slot)) != SGT_OK) return st;
   const int n_items = build_schedule(p, W, o.rank, H, esz, o, X_shards, ctx->h_items[slot], true, ctx->h_ranks[slot]);
   const int pwg = std::min(default_producer_wgs(o, ctx->n_cu), n_items);
-  // The schedule and the ranks go over on the caller's stream, before the fork,
-  // so both the producer and the routing see them.
-  HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], ctx->h_items[slot], n_items * sizeof(ProdItem), hipMemcpyHostToDevice,
-                         stream));
-  HIP_TRY(hipMemcpyAsync(ctx->d_ranks[slot], ctx->h_ranks[slot], p.n_flags * sizeof(uint32_t), hipMemcpyHostToDevice,
-                         stream));
-
+  // The placement kernel reads the arrival ranks straight from pinned host
+  // memory (a few words per workgroup); the producer's schedule is copied on
+  // the stream that runs the producer.
   if (o.producer == SGT_PROD_SERIAL) {
+    HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], ctx->h_items[slot], n_items * sizeof(ProdItem), hipMemcpyHostToDevice,
+                           stream));
     HIP_TRY(launch_ag_producer(X_gathered, shard_flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
                                trace_rel, pwg, stream));
     if ((st = route_and_compute(ctx->d_ranks[slot], o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu)) != SGT_OK)
@@ -749,6 +784,8 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   // consumer on the remaining CUs (one workgroup per CU).
   HIP_TRY(hipEventRecord(ctx->ev_fork, stream));
   HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
+  HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], ctx->h_items[slot], n_items * sizeof(ProdItem), hipMemcpyHostToDevice,
+                         ctx->prod));
   HIP_TRY(launch_ag_producer(X_gathered, shard_flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
                              trace_rel, pwg, ctx->prod));
   HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));

@@ -74,18 +74,21 @@ SMALL = [
     (4, 256, 256, 192, 16, 4, 16),      # one row tile per expert, I tail of 192
     (8, 1024, 264, 320, 64, 8, 32),     # Zipf groups beyond 256 rows, H tail of 8, I tail of 64
     (2, 600, 128, 256, 5, 2, 100),      # E not a multiple of 64, shards of 300 tokens
+    (4, 512, 128, 128, 40, 12, 32),     # top-k above 8 (the wave-per-token selection)
 ]
+TILES = [(128, 8), (256, 8), (128, 4)]   # (tile rows, waves per workgroup)
 
 
+@pytest.mark.parametrize("tile", TILES, ids=["r%dw%d" % t for t in TILES])
 @pytest.mark.parametrize("shape", SMALL)
 @pytest.mark.parametrize("w_layout", ["kn", "nk"])
-def test_moe_parity_overlapped(ctx, orc, shape, w_layout):
+def test_moe_parity_overlapped(ctx, orc, shape, w_layout, tile):
     W, T, H, Ic, E, k, fr = shape
     w = I.scaled(I.MOE, W=W, T=T, H=H, I=Ic, E=E, topk=k)
     shards, We, logits = I.make_moe(w, W_layout=w_layout)
     res = run_moe(ctx, shards, We, logits, k, w_layout=w_layout, flag_rows=fr, peer_gbps=20.0, jitter_us=5.0,
-                  arrival_seed=3, rank=W - 1)
-    check_moe(orc, shards, We, logits, k, res, w_layout=w_layout, what="moe %s %s" % (shape, w_layout))
+                  arrival_seed=3, rank=W - 1, tile_rows=tile[0], tile_waves=tile[1])
+    check_moe(orc, shards, We, logits, k, res, w_layout=w_layout, what="moe %s %s %s" % (shape, w_layout, tile))
     assert (res[5] == res[5][0]).all() and res[5][0] > 0
 
 
@@ -197,19 +200,23 @@ def test_moe_bad_args(ctx):
         run_moe(ctx, shards, We, logits, 5)          # topk > E
     with pytest.raises(sgt.SgtError):
         run_moe(ctx, shards, We, logits, 2, flag_rows=48)   # does not divide 64 rows per shard
+    with pytest.raises(sgt.SgtError):
+        run_moe(ctx, shards, We, logits, 2, tile_rows=64)   # 128 or 256 only
     bad = [s[:, :60].copy() for s in shards]         # H % 8 != 0
     with pytest.raises(sgt.SgtError):
         run_moe(ctx, bad, We[:, :60].copy(), logits, 2)
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("tile_rows", [128, 256])
 @pytest.mark.parametrize("w_layout", ["kn", "nk"])
-def test_moe_full_shape(ctx, orc, w_layout):
+def test_moe_full_shape(ctx, orc, w_layout, tile_rows):
     """The full workload (T 4096, H 2048, I 768, 64 experts, top-8), overlapped at 50 GB/s per peer:
     routing tables and the gathered tokens in full, Y on sampled rows."""
     w = I.MOE
     shards, We, logits = I.make_moe(w, W_layout=w_layout)
-    res = run_moe(ctx, shards, We, logits, w.topk, w_layout=w_layout, peer_gbps=w.peer_gbps, arrival_seed=1)
+    res = run_moe(ctx, shards, We, logits, w.topk, w_layout=w_layout, peer_gbps=w.peer_gbps, arrival_seed=1,
+                  tile_rows=tile_rows)
     Xg, Y, ids, off, rt, _ = res
     X_ref = np.concatenate(shards, axis=0)
     ids_ref, off_ref, rt_ref = orc.moe_route(logits, w.topk)
