@@ -58,7 +58,7 @@ def timed(fn, steps, warmup, torch, ctx):
     return step_ms, statistics.mean(kern), kern
 
 
-def cpu_baseline(shards, B, M, N, K, seconds: float):
+def cpu_baseline(shards, B, M, N, K, seconds: float, b_layout: str = "kn"):
     """The oracle (concat + fp64 loops over output rows), timed on a bounded sample of rows."""
     import numpy as np
     import oracle
@@ -66,14 +66,15 @@ def cpu_baseline(shards, B, M, N, K, seconds: float):
     t = time.perf_counter()
     A_full = oracle.allgather(shards)
     t_gather = time.perf_counter() - t
-    rows = np.arange(0, M, max(1, M // 4096), dtype=np.int64)
+    # candidate rows interleaved over the whole matrix (every shard early in the list)
+    rows = np.concatenate([np.arange(r, M, 64, dtype=np.int64) for r in range(64)])
     n = max(threads, 8)
     t = time.perf_counter()
-    oracle.gemm(A_full, B, rows=rows[:n])
+    oracle.gemm(A_full, B, b_layout=b_layout, rows=rows[:n])
     dt = time.perf_counter() - t
     n2 = int(min(len(rows), max(n, n * seconds / max(dt, 1e-3))))
     t = time.perf_counter()
-    oracle.gemm(A_full, B, rows=rows[:n2])
+    oracle.gemm(A_full, B, b_layout=b_layout, rows=rows[:n2])
     dt = time.perf_counter() - t
     flops = 2.0 * n2 * N * K
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
@@ -158,7 +159,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rs", action="store_true", help="skip the GEMM+ReduceScatter workload")
     ap.add_argument("--no-moe", action="store_true", help="skip the MoE AllGather + grouped GEMM workload")
-    ap.add_argument("--b-layout", default="kn", choices=["kn", "nk"])
+    ap.add_argument("--b-layout", default="nk", choices=["kn", "nk"],
+                    help="B as N x K (a Linear layer's weight, default) or K x N")
     ap.add_argument("--headline-only", action="store_true",
                     help="only the overlapped steps (for a profiler run whose kernel list is exactly the timed one)")
     args = ap.parse_args()
@@ -316,7 +318,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(shards_h, B_h, M, N, K, args.cpu_seconds)
+        cpu = cpu_baseline(shards_h, B_h, M, N, K, args.cpu_seconds, b_layout=lay)
         cpu.pop("seconds", None)
 
     line = {

@@ -43,9 +43,10 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) ag_consumer_bf16(AgArgs
   const uint16_t* A = static_cast<const uint16_t*>(a.A);
   const uint16_t* B = static_cast<const uint16_t*>(a.B);
   for (int t = xcd_remap(blockIdx.x, G); t < total; t += G) {
-    const int pn = t % a.tiles_n;
-    const int pm = (int)panel_at(t / a.tiles_n, a.tiles_m, a.rows_per_shard, kBM, a.W, a.rank, a.order);
-    const int64_t m0 = (int64_t)pm * kBM, n0 = (int64_t)pn * kBN;
+    int64_t seq_m, pn;
+    tile_at(t, a.tiles_m, a.tiles_n, &seq_m, &pn);
+    const int64_t pm = panel_at(seq_m, a.tiles_m, a.rows_per_shard, kBM, a.W, a.rank, a.order);
+    const int64_t m0 = pm * kBM, n0 = pn * kBN;
     const int64_t m1 = m0 + kBM < a.M ? m0 + kBM : a.M;
     const int64_t tile_id = (int64_t)pm * a.tiles_n + pn;
     // A panel that lies inside the local shard is read from the shard itself

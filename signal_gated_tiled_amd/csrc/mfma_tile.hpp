@@ -251,10 +251,14 @@ __device__ __forceinline__ void mfma_stage(const uint8_t* sA, const uint8_t* sB,
   bf16x8_t a[2][Tile<kW, kR>::kMI], b[2][4];
   read_frags<kW, kR>(sA, sB, 0, a[0], b[0]);
   __builtin_amdgcn_sched_barrier(0);
+  // A wave in its MFMA phase takes issue priority over the other wave of its
+  // SIMD (which is then typically issuing loads or waiting at the barrier).
+  __builtin_amdgcn_s_setprio(1);
   mfma_substep<kW, kR, 0>(sA, sB, a, b, acc);
   mfma_substep<kW, kR, 1>(sA, sB, a, b, acc);
   mfma_substep<kW, kR, 2>(sA, sB, a, b, acc);
   mfma_substep<kW, kR, 3>(sA, sB, a, b, acc);
+  __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_sched_barrier(0);
 }
 

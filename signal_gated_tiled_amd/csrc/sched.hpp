@@ -30,6 +30,20 @@ __host__ __device__ inline int64_t panel_at(int64_t i, int64_t tiles_m, int64_t 
   return (i + first) % tiles_m;
 }
 
+// Tile t of the consumer's sequence: panels are taken in groups of four (in
+// panel order) and, inside a group, column tile by column tile, so the 32 or
+// so consecutive tiles one XCD runs in a round share 4 A panels and about 8
+// column tiles of B in its L2 (instead of 2 panels and every column tile).
+constexpr int kPanelGroup = 4;
+
+__host__ __device__ inline void tile_at(int64_t t, int64_t tiles_m, int64_t tiles_n, int64_t* seq_m, int64_t* pn) {
+  const int64_t grp = t / (kPanelGroup * tiles_n);
+  const int64_t gm = tiles_m - grp * kPanelGroup < kPanelGroup ? tiles_m - grp * kPanelGroup : kPanelGroup;
+  const int64_t idx = t - grp * kPanelGroup * tiles_n;
+  *pn = idx / gm;
+  *seq_m = grp * kPanelGroup + idx % gm;
+}
+
 // Workgroup b of a persistent grid of G workgroups is dispatched to XCD b % 8.
 // Renumber so that the workgroups sharing an XCD take consecutive tiles of each
 // round (tiles sharing an A panel then hit the same XCD-private L2).
