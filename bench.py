@@ -34,6 +34,54 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 fl
 PEAK_HBM_GBS = 8000.0
 
 
+# HBM traffic of the consumer from the committed counter summary: valid only
+# while the consumer's sources are the ones the counters were taken on.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "ag_consumer_bf16_llama70b_traffic.md")
+CONSUMER_SOURCES = ["ag_gemm.hip", "mfma_tile.hpp", "signal.hpp", "sched.hpp", "common.hpp"]
+
+
+def consumer_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in CONSUMER_SOURCES:
+        with open(os.path.join(ROOT, "signal_gated_tiled_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per consumer dispatch (FETCH + WRITE, copy-calibrated), or None when the
+    summary is missing or was taken on other consumer sources."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("consumer_source_sha256_16") != consumer_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch, steps: int):
+    """A plain copy of known size (fp32, 1 GiB read + 1 GiB written per launch) whose FETCH_SIZE and
+    WRITE_SIZE counters scale the consumer's."""
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": n * 4, "bytes_written": n * 4, "launches": steps,
+                                           "kernel": "torch.neg (vectorized elementwise)"}}), flush=True)
+
+
 def _events(n, torch):
     return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
 
@@ -161,6 +209,12 @@ def main():
     ap.add_argument("--no-moe", action="store_true", help="skip the MoE AllGather + grouped GEMM workload")
     ap.add_argument("--b-layout", default="nk", choices=["kn", "nk"],
                     help="B as N x K (a Linear layer's weight, default) or K x N")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only a plain 1 GiB device copy (counter calibration for the traffic figure)")
+    ap.add_argument("--consumer-alone", action="store_true",
+                    help="only the headline's consumer kernel on resident data with flags preset, on the grid the "
+                         "overlapped call gives it (for counter passes, which serialize kernels and so cannot "
+                         "run the overlapped call)")
     ap.add_argument("--headline-only", action="store_true",
                     help="only the overlapped steps (for a profiler run whose kernel list is exactly the timed one)")
     args = ap.parse_args()
@@ -179,6 +233,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
+    if args.copy_calibration:
+        copy_calibration(torch, max(1, args.steps))
+        return
 
     def up(a):
         a = np.ascontiguousarray(a)
@@ -206,6 +263,15 @@ def main():
         return fn
 
     link = dict(peer_gbps=w.peer_gbps, jitter_us=w.jitter_us)
+    if args.consumer_alone:
+        Ag.copy_(torch.cat(shards))
+        n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+        grid = n_cu - max(8, n_cu // 8)
+        ms, kern_ms, _ = timed(ag("preset", consumer_cus=grid), args.steps, args.warmup, torch, ctx)
+        print(json.dumps({"workload": w.name, "consumer_alone_ms": ms, "consumer_kernel_ms": kern_ms, "grid": grid,
+                          "tflops": flops / (kern_ms * 1e-3) / 1e12}), flush=True)
+        ctx.close()
+        return
     over_ms, over_kern_ms, _ = timed(lambda i, ev: ag("cu", arrival_seed=i + 1, **link)(i, ev), args.steps,
                                      args.warmup, torch, ctx)
     if args.headline_only:
@@ -339,7 +405,8 @@ def main():
                    "inputs": "bf16 ~N(0,0.02), SeedSequence(1003)"},
         "roofline": {"bound": "mfma", "kernel": "ag_consumer_bf16 (overlapped)", "achieved": kern_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": kern_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": None},
+                     "traffic": traffic_from_profile(), "traffic_unit": "bytes per launch (HBM, counters)",
+                     "algorithmic_bytes": (M * K + K * N) * 2 + M * N * 4},
         "cpu_baseline": cpu,
         "detail": detail,
     }
