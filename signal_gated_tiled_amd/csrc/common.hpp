@@ -82,11 +82,15 @@ struct MoeTile {
 // Routing and work-list tables of one MoE call (device memory owned by the context).
 struct MoeTables {
   uint32_t* masks;        // ceil(E / 32) x T: bit e % 32 of word e / 32 set when token t chose e
-  uint32_t* partials;     // n_groups x E: tokens of each top-k token group routed to each expert
-  int32_t n_groups;       // token groups of the top-k kernel (tokens_per_group each, the last ragged)
+  uint32_t* counts;       // E: tokens routed to each expert (zero on entry: cleared by the previous call)
+  uint32_t* counts_next;  // E: the next call's counts, cleared by this call's top-k kernel
+  int32_t n_groups;       // workgroups of the top-k kernel (tokens_per_group tokens each, the last ragged)
   int32_t tokens_per_group;
   uint32_t* n_tiles;      // 1: number of grouped row tiles
+  uint32_t tiles_cap;     // entries of tiles / keys / order
   uint32_t* claim;        // 1: next consumer work item to claim
+  uint32_t* done;         // 1: placement workgroups finished (cleared by the top-k kernel)
+  uint32_t* ranks;        // arrival rank of each signal tile, device copy (written by the top-k kernel)
   MoeTile* tiles;         // grouped row tiles, expert-major (written by the placement kernel)
   uint32_t* keys;         // readiness key per entry of `tiles`
   MoeTile* order;         // the same tiles sorted by key (the consumer's work order)
@@ -101,11 +105,16 @@ struct MoeArgs {
   const int32_t* expert_off;  // E + 1
   const MoeTile* order;
   const uint32_t* n_tiles;
+  uint32_t tiles_cap;         // entries of `order`
   uint32_t* claim;
   const uint32_t* flags;      // one per signal tile of X
   uint32_t* status;
   uint64_t* trace;            // optional: 4 words per work item in claim order
   int64_t T, H, I;
+  int64_t rows;               // T * topk: rows of Y and row_token
+  const uint32_t* started;    // producer workgroups started so far (cumulative over calls), or null
+  uint32_t started_all;       // its value once every producer workgroup of this call runs
+  int32_t late_blocks;        // the last late_blocks workgroups run only when started == started_all
   int32_t E, flag_rows, tiles_n;
   uint32_t epoch;
   uint64_t timeout_ticks;

@@ -72,7 +72,16 @@ __device__ __forceinline__ bool wait_tile_rows(const MoeArgs& a, const int32_t* 
 template <int kW, int kR, bool kBNK, bool kOutBf16>
 __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) moe_consumer_bf16(MoeArgs a) {
   __shared__ int item_s, ok;
-  const int64_t n_items = (int64_t)(*a.n_tiles) * a.tiles_n;
+  if (a.late_blocks > 0 && (int)blockIdx.x >= (int)gridDim.x - a.late_blocks) {
+    // a workgroup that may sit on a CU the producer needs: run only if every
+    // producer workgroup is already running (one check, no wait)
+    if (threadIdx.x == 0)
+      ok = __hip_atomic_load(a.started, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.started_all ? 1 : 0;
+    __syncthreads();
+    if (!ok) return;
+  }
+  const uint32_t nt = *a.n_tiles;
+  const int64_t n_items = (int64_t)(nt < a.tiles_cap ? nt : a.tiles_cap) * a.tiles_n;
   while (true) {
     if (threadIdx.x == 0) item_s = (int)atomicAdd(a.claim, 1u);
     __syncthreads();
@@ -82,7 +91,12 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) moe_consumer_bf16(MoeAr
     const int64_t n0 = (item % a.tiles_n) * kBN;
     const int e = mt.expert;
     const int64_t r0 = mt.r0;
-    const int64_t r_end = a.expert_off[e + 1];
+    int64_t r_end = a.expert_off[e + 1];
+    r_end = r_end < a.rows ? r_end : a.rows;  // the tables are exact; this only bounds every access
+    if (r0 >= r_end) {  // (uniform) the barrier keeps item_s from being overwritten before all read it
+      __syncthreads();
+      continue;
+    }
     const int rows_valid = (int)(r_end - r0 < kR ? r_end - r0 : kR);
     const int32_t* tok = a.row_token + r0;
     uint64_t t_wait = 0;

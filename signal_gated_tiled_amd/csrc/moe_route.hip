@@ -5,25 +5,25 @@
 // device-level tiles of an MoE layer take their sizes from how many tokens each
 // expert receives, known only at run time).
 //
-// Three launches:
-//  1. top-k (largest logit first, equal logits: lower expert id).  For
-//     k <= 8, one thread per token keeps its 8 best (logit, id) pairs sorted
-//     in registers while it scans the logits in expert order; otherwise one
-//     wave per token runs k rounds of a wave-wide argmax.  Each token's picks
-//     also go to a bitmask (one bit per expert), and each workgroup writes how
-//     many of its tokens chose each expert.
-//  2. moe_place_kernel -- one workgroup per expert: the per-group counts give
-//     every expert's size, and prefix sums over experts its first row
+// Two launches:
+//  1. moe_topk_kernel  -- one wave per token, one lane per expert (up to four
+//     experts a lane): k rounds of a wave-wide argmax (largest logit first,
+//     equal logits: lower expert id).  Each token's picks also go to a bitmask
+//     (one bit per expert), and each workgroup adds how many of its tokens
+//     chose each expert to the call's counts.
+//  2. moe_place_kernel -- one workgroup per expert: prefix sums of the counts
+//     over experts give its first row
 //     (expert_off) and first row tile; one pass over the tokens' mask words in
 //     ascending token order (a prefix sum over threads) places each token that
 //     chose the expert at the next row of its group.  Each group is cut into
 //     row tiles of the consumer's tile height; the readiness key of a row tile
 //     is the latest arrival rank among the signal tiles its rows come from.
-//  3. moe_sort_kernel  -- one workgroup: a stable counting sort of the row tiles
-//     by readiness key, so the consumer claims first the tiles whose rows land
-//     first.
-// No table depends on the order of concurrent updates (no global atomics):
-// counts are per-workgroup sums, positions are prefix sums over tokens.
+//  3. the last placement workgroup to finish sorts the row tiles by readiness
+//     key (stable counting sort), so the consumer claims first the tiles whose
+//     rows land first.
+// No table depends on the order of concurrent updates: counts are integer
+// sums, positions are prefix sums over tokens.  The counts are double-buffered
+// by call parity: each call's top-k kernel clears the next call's buffer.
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -44,239 +44,161 @@ __device__ __forceinline__ uint32_t sort_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
-    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+// Branch-free 32-bit loads: a buffer resource over [base, base + bytes) reads
+// 0 for any offset past the end, so guarded loads need no branch (a branch per
+// load would make each one wait for the previous).
+constexpr uint32_t kNoLoad = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t words_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes >= 0x80000000ull ? 0x7FFFFFFFu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
 }
 
-__device__ __forceinline__ uint64_t pack_choice(float logit, int e) {
-  return ((uint64_t)sort_key(logit) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+__device__ __forceinline__ uint32_t load_word(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
 }
 
-// One thread per token, k <= 8.  best[0..7] stays sorted in decreasing packed
-// order: each new (logit, id) is bubbled in with max / min exchanges, so among
-// equal logits the earlier (lower) id stays ahead, as k rounds of argmax with
-// ties to the lower id would pick.  Workgroup g takes tokens [256 g, 256 g + 256).
-__global__ void __launch_bounds__(256) moe_topk8_kernel(const float* __restrict__ logits, int64_t T, int E, int k,
-                                                        int32_t* __restrict__ topk_ids, uint32_t* __restrict__ masks,
-                                                        uint32_t* __restrict__ partials) {
-  __shared__ uint32_t cnt[256];
-  const int tid = threadIdx.x;
-  cnt[tid] = 0u;
-  __syncthreads();
-  const int64_t t = (int64_t)blockIdx.x * 256 + tid;
-  if (t < T) {
-    const float* l = logits + t * E;
-    uint64_t best[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) best[j] = 0ull;
-#pragma unroll 4
-    for (int e = 0; e < E; ++e) {
-      uint64_t x = pack_choice(l[e], e);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint64_t hi = best[j] > x ? best[j] : x;
-        x = best[j] > x ? x : best[j];
-        best[j] = hi;
-      }
-    }
-    uint32_t words[8];
-#pragma unroll
-    for (int w = 0; w < 8; ++w) words[w] = 0u;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      if (s < k) {
-        const int e = (int)(0xFFFFFFFFu - (uint32_t)best[s]);
-        topk_ids[t * k + s] = e;
-        atomicAdd(&cnt[e], 1u);
-#pragma unroll
-        for (int w = 0; w < 8; ++w)
-          if (w == (e >> 5)) words[w] |= 1u << (e & 31);
-      }
-    }
-    const int nw = (E + 31) >> 5;
-#pragma unroll
-    for (int w = 0; w < 8; ++w)
-      if (w < nw) masks[(int64_t)w * T + t] = words[w];
-  }
-  __syncthreads();
-  if (tid < E) partials[(int64_t)blockIdx.x * E + tid] = cnt[tid];
+// Maximum over the 64 lanes of a wave, returned to every lane: DPP exchanges
+// inside each row of 16 lanes (quad swaps, then half-row and row mirrors),
+// then the four row results read out of lanes 15, 31, 47 and 63.
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v, uint32_t ctrl_result) { return v > ctrl_result ? v : ctrl_result; }
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
+  v = dpp_max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1
+  v = dpp_max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, true));  // row_half_mirror
+  v = dpp_max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, true));  // row_mirror
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15), r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47), r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+  const uint32_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+  return a > b ? a : b;
 }
 
-// Workgroup g (4 waves) takes tokens [g * tpg, (g + 1) * tpg); a wave takes
-// every 4th of them.  Lane l holds experts l, l + 64, l + 128, l + 192 as
-// (key << 32) | (0xFFFFFFFF - e): the wave maximum is the largest logit and,
-// among equal logits, the lowest expert id.  A taken expert's entry becomes 0,
-// below every live entry.
-__global__ void __launch_bounds__(256) moe_topk_kernel(const float* __restrict__ logits, int64_t T, int E, int k,
-                                                       int tpg, int32_t* __restrict__ topk_ids,
-                                                       uint32_t* __restrict__ masks, uint32_t* __restrict__ partials) {
+// Workgroup g (8 waves) takes tokens [g * tpg, (g + 1) * tpg); a wave takes
+// every 8th of them, their logits loaded up front.  Lane l holds the keys of
+// experts l, l + 64, ... (kSlots = ceil(E / 64) of them).  Each of the k rounds
+// takes the wave maximum of the live keys and then, with one ballot per slot,
+// the lowest expert id holding it: the largest logit first and, among equal
+// logits, the lowest id.  Round s's pick is kept by lane s % 64 (slot s / 64);
+// the picks are written, counted and turned into mask words once per token.
+// The workgroup's picks per expert are summed in LDS and added to the call's
+// counts (integer sums: the order of the atomic updates does not matter).
+constexpr int kTopkWaves = 8;
+constexpr int kTopkPerWave = 4;
+
+template <int kSlots>
+__global__ void __launch_bounds__(64 * kTopkWaves) moe_topk_kernel(const float* __restrict__ logits, int64_t T, int E,
+                                                                  int k, int tpg, int32_t* __restrict__ topk_ids,
+                                                                  uint32_t* __restrict__ masks, uint32_t* counts,
+                                                                  uint32_t* counts_next, uint32_t* done,
+                                                                  const uint32_t* rank_host, uint32_t* rank_dev,
+                                                                  uint32_t n_flags) {
   __shared__ uint32_t cnt[256];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // The arrival ranks come from pinned host memory: each workgroup copies a
+  // slice to device memory, so the placement reads them from HBM.
+  if (rank_host) {
+    const uint32_t per = (n_flags + gridDim.x - 1) / gridDim.x, f0 = blockIdx.x * per;
+    for (uint32_t f = f0 + tid; f < f0 + per && f < n_flags; f += blockDim.x) rank_dev[f] = rank_host[f];
+  }
+  if (blockIdx.x == 0) {
+    if (tid == 0) *done = 0u;                  // the placement's completion count for this call
+    if (tid < 256) counts_next[tid] = 0u;      // all 256 entries: the next call may have more experts
+  }
   const int nw = (E + 31) >> 5;
-  cnt[tid] = 0u;
+  if (tid < 256) cnt[tid] = 0u;
   __syncthreads();
-  for (int j = wv; j < tpg; j += 4) {
-    const int64_t t = (int64_t)blockIdx.x * tpg + j;
-    if (t >= T) break;
-    const float* l = logits + t * E;
-    uint64_t v[4];
+  // this workgroup's logits (T * E * 4 < 2^31 bytes, checked by the host)
+  const int64_t g0 = (int64_t)blockIdx.x * tpg;
+  const int64_t g1 = g0 + tpg < T ? g0 + tpg : T;
+  const __amdgpu_buffer_rsrc_t lr = words_rsrc(logits + g0 * E, (uint64_t)(g1 > g0 ? g1 - g0 : 0) * E * 4);
+  for (int j0 = wv; j0 < tpg; j0 += kTopkWaves * kTopkPerWave) {
+    // this wave's tokens of the pass, all their logits in flight at once
+    uint32_t raw[kTopkPerWave][kSlots];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      v[q] = e < E ? pack_choice(l[e], e) : 0ull;
-    }
-    uint32_t word = 0u;  // lane l < nw builds mask word l of this token
-    for (int s = 0; s < k; ++s) {
-      uint64_t m = v[0];
+    for (int u = 0; u < kTopkPerWave; ++u) {
+      const int j = j0 + u * kTopkWaves;
 #pragma unroll
-      for (int q = 1; q < 4; ++q) m = v[q] > m ? v[q] : m;
-      m = wave_max_u64(m);
-      const int e = (int)(0xFFFFFFFFu - (uint32_t)m);
-      if ((e & 63) == lane) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (q == (e >> 6)) v[q] = 0ull;
-      }
-      if (lane == (e >> 5)) word |= 1u << (e & 31);
-      if (lane == 0) {
-        topk_ids[t * k + s] = e;
-        atomicAdd(&cnt[e], 1u);
+      for (int q = 0; q < kSlots; ++q) {
+        const int e = lane + 64 * q;
+        raw[u][q] = load_word(lr, (j < tpg && e < E) ? (uint32_t)(j * E + e) * 4u : kNoLoad);
       }
     }
-    if (lane < nw) masks[(int64_t)lane * T + t] = word;
-  }
-  __syncthreads();
-  if (tid < E) partials[(int64_t)blockIdx.x * E + tid] = cnt[tid];
-}
-
-// Exclusive prefix sum over one value per thread of a 256-thread workgroup.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* sh /* 256 */, uint32_t* total) {
-  const int t = threadIdx.x;
-  sh[t] = x;
-  __syncthreads();
-  for (int d = 1; d < 256; d <<= 1) {
-    const uint32_t y = t >= d ? sh[t - d] : 0u;
-    __syncthreads();
-    sh[t] += y;
-    __syncthreads();
-  }
-  const uint32_t incl = sh[t];
-  *total = sh[255];
-  __syncthreads();
-  return incl - x;
-}
-
-// One workgroup (256 threads) per expert.
-__global__ void __launch_bounds__(256) moe_place_kernel(const uint32_t* __restrict__ masks,
-                                                        const uint32_t* __restrict__ partials, int n_groups,
-                                                        int64_t T, int E, const uint32_t* __restrict__ rank_of_flag,
-                                                        int32_t flag_rows, int tile_rows, MoeTables tb,
-                                                        int32_t* __restrict__ expert_off,
-                                                        int32_t* __restrict__ row_token) {
-  __shared__ uint32_t sh[256];
-  __shared__ uint32_t cnt[256];
-  __shared__ uint32_t keys[kMaxTilesPerExpert];
-  __shared__ uint32_t ranks[kRankCache];
-  __shared__ uint32_t my_row0, my_tile0, my_count;
-  const int tid = threadIdx.x;
-  const int e = blockIdx.x;
-  // The arrival ranks may live in host memory: read each once into LDS.
-  const int64_t n_flags = (T + flag_rows - 1) / flag_rows;
-  const bool cached = rank_of_flag && n_flags <= kRankCache;
-  if (cached)
-    for (int64_t f = tid; f < n_flags; f += 256) ranks[f] = rank_of_flag[f];
-
-  // Every expert's token count: the top-k groups' counts summed, 256 / E
-  // threads per expert each taking every (256 / E)-th group.
-  cnt[tid] = 0u;
-  __syncthreads();
-  {
-    const int q = 256 / E;
-    if (tid < q * E) {
-      const int x = tid % E, part = tid / E;
-      uint32_t sum = 0u;
-#pragma unroll 8
-      for (int g = part; g < n_groups; g += q) sum += partials[(int64_t)g * E + x];
-      atomicAdd(&cnt[x], sum);
-    }
-  }
-  __syncthreads();
-
-  // First row and first row tile of every expert: prefix sums over experts.
-  const uint32_t c = tid < E ? cnt[tid] : 0u;
-  uint32_t rows_total, tiles_total;
-  const uint32_t row0 = block_exclusive_scan(c, sh, &rows_total);
-  const uint32_t tiles = (c + tile_rows - 1) / tile_rows;
-  const uint32_t tile0 = block_exclusive_scan(tiles, sh, &tiles_total);
-  if (tid == e) {
-    my_row0 = row0;
-    my_tile0 = tile0;
-    my_count = c;
-  }
-  if (e == 0) {
-    if (tid < E) expert_off[tid] = (int32_t)row0;
-    if (tid == 0) {
-      expert_off[E] = (int32_t)rows_total;
-      *tb.n_tiles = tiles_total;
-      *tb.claim = 0u;
-    }
-  }
-  __syncthreads();
-  const uint32_t n_e = my_count, base_row = my_row0, base_tile = my_tile0;
-  const uint32_t nt_e = (n_e + tile_rows - 1) / tile_rows;
-  for (uint32_t j = tid; j < nt_e; j += 256) keys[j] = 0u;
-  __syncthreads();
-
-  // Place the tokens that chose e, in ascending token order: thread i takes
-  // 16 consecutive tokens of each 4096-token round.
-  const uint32_t* mw = masks + (int64_t)(e >> 5) * T;
-  const int bit = e & 31;
-  uint32_t placed = 0;
-  for (int64_t rb = 0; rb < T; rb += 4096) {
-    const int64_t t0 = rb + 16 * tid;
-    uint32_t sel = 0u;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int64_t t = t0 + u;
-      const uint32_t m = t < T ? mw[t] : 0u;
-      sel |= ((m >> bit) & 1u) << u;
+    for (int u = 0; u < kTopkPerWave; ++u) {
+      const int64_t t = g0 + j0 + u * kTopkWaves;
+      if (!(j0 + u * kTopkWaves < tpg && t < T)) break;
+      uint32_t v[kSlots];   // live keys; a taken or absent expert holds 0 and is not live
+      bool live[kSlots];
+#pragma unroll
+      for (int q = 0; q < kSlots; ++q) {
+        live[q] = lane + 64 * q < E;
+        v[q] = live[q] ? sort_key(__uint_as_float(raw[u][q])) : 0u;
+      }
+      int pick[kSlots];
+#pragma unroll
+      for (int q = 0; q < kSlots; ++q) pick[q] = -1;
+      uint32_t word = 0u;  // lane l < nw builds mask word l of this token
+      for (int s = 0; s < k; ++s) {
+        uint32_t lm = 0u;
+#pragma unroll
+        for (int q = 0; q < kSlots; ++q) lm = (live[q] && v[q] > lm) ? v[q] : lm;
+        const uint32_t m = wave_max_u32(lm);
+        int e = -1;
+#pragma unroll
+        for (int q = 0; q < kSlots; ++q) {
+          const uint64_t b = __ballot(live[q] && v[q] == m);
+          if (e < 0 && b) e = 64 * q + __ffsll((unsigned long long)b) - 1;
+        }
+        // k <= E keeps a live entry, so e >= 0 (all lanes agree on it)
+#pragma unroll
+        for (int q = 0; q < kSlots; ++q) {
+          if (lane + 64 * q == e) live[q] = false;
+          if (s == lane + 64 * q) pick[q] = e;
+        }
+        if (lane == (e >> 5)) word |= 1u << (e & 31);
+      }
+#pragma unroll
+      for (int q = 0; q < kSlots; ++q) {
+        if (pick[q] >= 0) {
+          topk_ids[t * k + lane + 64 * q] = pick[q];
+          atomicAdd(&cnt[pick[q]], 1u);
+        }
+      }
+      if (lane < nw) masks[(int64_t)lane * T + t] = word;
     }
-    uint32_t total;
-    uint32_t pos = placed + block_exclusive_scan((uint32_t)__popc(sel), sh, &total);
-    while (sel) {
-      const int u = __ffs(sel) - 1;
-      sel &= sel - 1u;
-      const int64_t t = t0 + u;
-      row_token[base_row + pos] = (int32_t)t;
-      const int64_t f = t / flag_rows;
-      const uint32_t key = cached ? ranks[f] : (rank_of_flag ? rank_of_flag[f] : 0u);
-      atomicMax(&keys[pos / tile_rows], key);
-      ++pos;
-    }
-    placed += total;
   }
   __syncthreads();
-  for (uint32_t j = tid; j < nt_e; j += 256) {
-    tb.tiles[base_tile + j] = MoeTile{e, (int32_t)(base_row + j * tile_rows)};
-    tb.keys[base_tile + j] = keys[j];
-  }
+  if (tid < E && cnt[tid]) atomicAdd(counts + tid, cnt[tid]);
 }
 
-// One workgroup of 256 threads: stable counting sort of the row tiles by
-// readiness key (keys < n_keys, folded into 256 buckets).
-__global__ void __launch_bounds__(256) moe_sort_kernel(MoeTables tb, uint32_t n_keys) {
-  __shared__ uint32_t base[kSortBuckets];
-  __shared__ uint32_t chunk_b[kSortBuckets];
-  __shared__ uint32_t sh[256];
+// Exclusive prefix sum over one value per thread of a 256-thread workgroup:
+// an inclusive scan inside each wave with cross-lane shifts, then each wave
+// adds the totals of the waves before it.  `sh` holds 4 words.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* sh, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint32_t incl = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = (uint32_t)__shfl_up((int)incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) sh[wv] = incl;
+  __syncthreads();
+  uint32_t before = 0u;
+  for (int w = 0; w < wv; ++w) before += sh[w];
+  *total = sh[0] + sh[1] + sh[2] + sh[3];
+  __syncthreads();
+  return before + incl - x;
+}
+
+// Stable counting sort of the row tiles by readiness key (keys < n_keys,
+// folded into 256 buckets) by one workgroup of 256 threads; base and chunk_b
+// are 256 words of LDS each, sh the scan scratch.
+__device__ void sort_row_tiles(const MoeTables& tb, uint32_t n_keys, uint32_t* base, uint32_t* chunk_b,
+                               uint32_t* sh) {
   const int tid = threadIdx.x;
-  const uint32_t n = *tb.n_tiles;
+  const uint32_t n = *tb.n_tiles < tb.tiles_cap ? *tb.n_tiles : tb.tiles_cap;
   auto bucket = [&](uint32_t key) -> uint32_t {
     if (n_keys <= kSortBuckets) return key < n_keys ? key : n_keys - 1;
     const uint64_t b = (uint64_t)key * kSortBuckets / n_keys;
@@ -308,31 +230,145 @@ __global__ void __launch_bounds__(256) moe_sort_kernel(MoeTables tb, uint32_t n_
   }
 }
 
+// One workgroup (256 threads) per expert.
+__global__ void __launch_bounds__(256) moe_place_kernel(const uint32_t* __restrict__ masks, int64_t T, int E,
+                                                        const uint32_t* __restrict__ rank_of_flag, int32_t flag_rows,
+                                                        int tile_rows, int tile_shift, int64_t rows_cap, MoeTables tb,
+                                                        int32_t* __restrict__ expert_off,
+                                                        int32_t* __restrict__ row_token) {
+  __shared__ uint32_t sh[256];
+  __shared__ uint32_t keys[kMaxTilesPerExpert];
+  __shared__ uint32_t ranks[kRankCache];
+  __shared__ uint32_t my_row0, my_tile0, my_count;
+  const int tid = threadIdx.x;
+  const int e = blockIdx.x;
+  // The arrival ranks may live in host memory: read each once into LDS.
+  const int64_t n_flags = (T + flag_rows - 1) / flag_rows;
+  const bool cached = rank_of_flag && n_flags <= kRankCache;
+  if (cached)
+    for (int64_t f = tid; f < n_flags; f += 256) ranks[f] = rank_of_flag[f];
+
+  // First row and first row tile of every expert: prefix sums over experts.
+  const uint32_t c = tid < E ? tb.counts[tid] : 0u;
+  uint32_t rows_total, tiles_total;
+  const uint32_t row0 = block_exclusive_scan(c, sh, &rows_total);
+  const uint32_t tiles = (c + tile_rows - 1) / tile_rows;
+  const uint32_t tile0 = block_exclusive_scan(tiles, sh, &tiles_total);
+  if (tid == e) {
+    my_row0 = row0;
+    my_tile0 = tile0;
+    my_count = c;
+  }
+  if (e == 0) {
+    if (tid < E) expert_off[tid] = (int32_t)row0;
+    if (tid == 0) {
+      expert_off[E] = (int32_t)rows_total;
+      *tb.n_tiles = tiles_total;
+      *tb.claim = 0u;
+    }
+  }
+  __syncthreads();
+  const uint32_t n_e = my_count, base_row = my_row0, base_tile = my_tile0;
+  // (counts are exact by construction; the clamps only keep every index inside
+  // its buffer whatever the tables hold)
+  uint32_t nt_e = (n_e + tile_rows - 1) / tile_rows;
+  nt_e = nt_e < (uint32_t)kMaxTilesPerExpert ? nt_e : (uint32_t)kMaxTilesPerExpert;
+  for (uint32_t j = tid; j < nt_e; j += 256) keys[j] = 0u;
+  __syncthreads();
+
+  // Place the tokens that chose e, in ascending token order: thread i takes
+  // 16 consecutive tokens of each 4096-token round.
+  const __amdgpu_buffer_rsrc_t mr = words_rsrc(masks + (int64_t)(e >> 5) * T, (uint64_t)T * 4);
+  const int bit = e & 31;
+  uint32_t placed = 0;
+  for (int64_t rb = 0; rb < T; rb += 4096) {
+    const int64_t t0 = rb + 16 * tid;
+    uint32_t m[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) m[u] = load_word(mr, t0 + u < T ? (uint32_t)(t0 + u) * 4u : kNoLoad);
+    uint32_t sel = 0u;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) sel |= ((m[u] >> bit) & 1u) << u;
+    uint32_t total;
+    uint32_t pos = placed + block_exclusive_scan((uint32_t)__popc(sel), sh, &total);
+    // A thread's (at most 16) rows are consecutive, so they touch at most two
+    // row tiles: reduce the keys locally and update each tile once.
+    uint32_t cur_tile = 0xFFFFFFFFu, cur_key = 0u;
+    while (sel) {
+      const int u = __ffs(sel) - 1;
+      sel &= sel - 1u;
+      const uint32_t t = (uint32_t)(t0 + u);  // T <= 2^20
+      if ((int64_t)base_row + pos < rows_cap) row_token[base_row + pos] = (int32_t)t;
+      const uint32_t f = t / (uint32_t)flag_rows;
+      const uint32_t key = cached ? ranks[f] : (rank_of_flag ? rank_of_flag[f] : 0u);
+      uint32_t tile = pos >> tile_shift;
+      tile = tile < nt_e ? tile : nt_e - 1;
+      if (tile != cur_tile) {
+        if (cur_tile != 0xFFFFFFFFu) atomicMax(&keys[cur_tile], cur_key);
+        cur_tile = tile;
+        cur_key = key;
+      } else {
+        cur_key = key > cur_key ? key : cur_key;
+      }
+      ++pos;
+    }
+    if (cur_tile != 0xFFFFFFFFu) atomicMax(&keys[cur_tile], cur_key);
+    placed += total;
+  }
+  __syncthreads();
+  // The tiles and keys the sorting workgroup reads go out with device-scope
+  // stores (written through to the coherence point), so publishing them needs
+  // no L2 write-back: each wave waits for its stores' acknowledgement, then one
+  // relaxed device-scope increment counts the workgroup done.
+  for (uint32_t j = tid; j < nt_e && base_tile + j < tb.tiles_cap; j += 256) {
+    int32_t* tile = reinterpret_cast<int32_t*>(tb.tiles + base_tile + j);
+    __hip_atomic_store(tile, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(tile + 1, (int32_t)(base_row + j * tile_rows), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(tb.keys + base_tile + j, keys[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __shared__ int last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0)
+    last = __hip_atomic_fetch_add(tb.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(E - 1);
+  __syncthreads();
+  if (!last) return;
+  // the last workgroup: drop any stale cached copy before reading the others' tables
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  sort_row_tiles(tb, (uint32_t)n_flags, keys, keys + kSortBuckets, sh);
+}
+
 }  // namespace
 
 int moe_max_tiles_per_expert() { return kMaxTilesPerExpert; }
 
-// Tokens per top-k workgroup: 256 (one per thread) when k <= 8; else 16 (four
-// per wave), or more when that would make over 4096 groups.
+// Tokens per top-k workgroup: 64 (four per wave), or more when that would
+// make over 4096 groups.
 int moe_tokens_per_group(int64_t T, int k) {
-  if (k <= 8) return 256;
-  int64_t tpg = 16;
-  if ((T + tpg - 1) / tpg > 4096) tpg = ((T + 4095) / 4096 + 3) / 4 * 4;
+  (void)k;
+  int64_t tpg = kTopkWaves * kTopkPerWave;
+  if ((T + tpg - 1) / tpg > 4096) tpg = ((T + 4095) / 4096 + tpg - 1) / tpg * tpg;
   return (int)tpg;
 }
 
 hipError_t launch_moe_route(const float* logits, int64_t T, int E, int k, const uint32_t* rank_of_flag,
                             int32_t flag_rows, uint32_t n_flags, int tile_rows, const MoeTables& tb,
                             int32_t* expert_off, int32_t* row_token, int32_t* topk_ids, hipStream_t stream) {
-  if (k <= 8)
-    hipLaunchKernelGGL(moe_topk8_kernel, dim3((unsigned)tb.n_groups), dim3(256), 0, stream, logits, T, E, k, topk_ids,
-                       tb.masks, tb.partials);
+  const dim3 g((unsigned)tb.n_groups), b(64 * kTopkWaves);
+  const int slots = (E + 63) / 64;
+  uint32_t* rank_dev = rank_of_flag ? tb.ranks : nullptr;
+  if (slots == 1)
+    hipLaunchKernelGGL(moe_topk_kernel<1>, g, b, 0, stream, logits, T, E, k, tb.tokens_per_group, topk_ids, tb.masks,
+                       tb.counts, tb.counts_next, tb.done, rank_of_flag, rank_dev, n_flags);
+  else if (slots == 2)
+    hipLaunchKernelGGL(moe_topk_kernel<2>, g, b, 0, stream, logits, T, E, k, tb.tokens_per_group, topk_ids, tb.masks,
+                       tb.counts, tb.counts_next, tb.done, rank_of_flag, rank_dev, n_flags);
   else
-    hipLaunchKernelGGL(moe_topk_kernel, dim3((unsigned)tb.n_groups), dim3(256), 0, stream, logits, T, E, k,
-                       tb.tokens_per_group, topk_ids, tb.masks, tb.partials);
-  hipLaunchKernelGGL(moe_place_kernel, dim3((unsigned)E), dim3(256), 0, stream, tb.masks, tb.partials, tb.n_groups,
-                     T, E, rank_of_flag, flag_rows, tile_rows, tb, expert_off, row_token);
-  hipLaunchKernelGGL(moe_sort_kernel, dim3(1), dim3(256), 0, stream, tb, n_flags);
+    hipLaunchKernelGGL(moe_topk_kernel<4>, g, b, 0, stream, logits, T, E, k, tb.tokens_per_group, topk_ids, tb.masks,
+                       tb.counts, tb.counts_next, tb.done, rank_of_flag, rank_dev, n_flags);
+  const int shift = tile_rows == 128 ? 7 : 8;
+  hipLaunchKernelGGL(moe_place_kernel, dim3((unsigned)E), dim3(256), 0, stream, tb.masks, T, E,
+                     (const uint32_t*)rank_dev, flag_rows, tile_rows, shift, T * k, tb, expert_off, row_token);
   return hipGetLastError();
 }
 

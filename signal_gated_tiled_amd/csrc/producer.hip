@@ -60,16 +60,36 @@ __device__ inline bool copy_bytes(char* __restrict__ dst, const char* __restrict
 // is latency-bound, so bytes in flight set each workgroup's bandwidth.
 constexpr int kProdThreads = 256;
 
+// A simulated link delivers a tile's bytes over the tile's transfer time, not
+// in one burst: a workgroup starts each paced tile's copy only `lead` ticks
+// before its release, `lead` being twice the workgroup's last measured copy
+// time (so the copy is done by the release), which keeps the producer's HBM
+// traffic close to the links' rate instead of front-loading it.
 __global__ void __launch_bounds__(kProdThreads) ag_producer_kernel(char* gathered, uint32_t* flags,
                                                                    const ProdItem* items, int n_items,
                                                                    int64_t tile_bytes, uint32_t epoch,
-                                                                   int withhold_peer, uint64_t* trace_release) {
-  __shared__ uint64_t t0;
-  if (threadIdx.x == 0) t0 = clock_ticks();
+                                                                   int withhold_peer, uint64_t* trace_release,
+                                                                   uint64_t lead0, uint32_t* started) {
+  __shared__ uint64_t t0, lead;
+  if (threadIdx.x == 0) {
+    t0 = clock_ticks();
+    lead = lead0;
+    // counts this workgroup as running, for a consumer launched later that
+    // may only take the producer's CUs once every producer workgroup holds one
+    if (started) __hip_atomic_fetch_add(started, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   __syncthreads();
   for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
     const ProdItem item = items[it];
     const int p = (int)item.peer;
+    uint64_t c0 = 0;
+    if (threadIdx.x == 0) {
+      // the schedule is finite, so this wait always ends
+      if (item.release > lead)
+        while (clock_ticks() < t0 + item.release - lead) __builtin_amdgcn_s_sleep(4);
+      c0 = clock_ticks();
+    }
+    __syncthreads();
     const bool coherent = copy_bytes<32>(gathered + (int64_t)item.tile * tile_bytes, item.src, tile_bytes);
     // Every wave waits until its stores are acknowledged; after the barrier one
     // lane publishes the flag.  Device-scope stores leave nothing in the XCD's
@@ -78,6 +98,8 @@ __global__ void __launch_bounds__(kProdThreads) ag_producer_kernel(char* gathere
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
+      const uint64_t d = clock_ticks() - c0;
+      lead = 2 * d > 100 ? 2 * d : 100;
       // Pace: the link of this peer delivers the tile at t0 + release.  The
       // schedule is finite, so this wait always ends.
       const uint64_t target = t0 + item.release;
@@ -119,11 +141,13 @@ hipError_t launch_rs_prepare(uint32_t* pflags, int64_t n, uint32_t v, uint32_t* 
 
 hipError_t launch_ag_producer(void* gathered, uint32_t* flags, const ProdItem* items, int n_items,
                               int64_t tile_bytes, uint32_t epoch, int withhold_peer, uint64_t* trace_release, int grid,
-                              hipStream_t stream) {
+                              hipStream_t stream, uint32_t* started) {
   if (n_items <= 0) return hipSuccess;
   if (grid > n_items) grid = n_items;
+  // first estimate of a tile's copy time: at 16 GB/s per workgroup (100 MHz ticks)
+  const uint64_t lead0 = (uint64_t)(tile_bytes / 160) + 100;
   hipLaunchKernelGGL(ag_producer_kernel, dim3(grid), dim3(kProdThreads), 0, stream, static_cast<char*>(gathered),
-                     flags, items, n_items, tile_bytes, epoch, withhold_peer, trace_release);
+                     flags, items, n_items, tile_bytes, epoch, withhold_peer, trace_release, lead0, started);
   return hipGetLastError();
 }
 

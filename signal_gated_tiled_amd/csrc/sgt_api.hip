@@ -24,7 +24,7 @@
 namespace sgt {
 hipError_t launch_ag_producer(void* gathered, uint32_t* flags, const ProdItem* items, int n_items,
                               int64_t tile_bytes, uint32_t epoch, int withhold_peer, uint64_t* trace_release, int grid,
-                              hipStream_t stream);
+                              hipStream_t stream, uint32_t* started = nullptr);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
 hipError_t launch_rs_prepare(uint32_t* pflags, int64_t n, uint32_t v, uint32_t* counter, hipStream_t stream);
 hipError_t launch_ag_consumer(const AgArgs& a, int in_dtype, int grid, hipStream_t stream);
@@ -83,15 +83,16 @@ struct sgt_ctx {
   ProdItem* d_items[kSlots] = {};
   uint32_t* h_ranks[kSlots] = {};  // arrival rank of each signal tile (MoE work ordering), pinned host
   uint32_t* d_ranks[kSlots] = {};  // the same memory as the GPU addresses it (read in place, no copy)
-  uint32_t* d_moe = nullptr;       // MoE tile count and claim counter
+  uint32_t* d_moe = nullptr;       // MoE: tile count, claim counter, done count, counts[2][256] by call parity
+  int moe_parity = 0;
+  uint32_t moe_prod_started = 0;   // producer workgroups launched by overlapped MoE calls (cumulative)
   MoeTile* d_moe_tiles = nullptr;  // MoE row tiles, expert-major and sorted; grow on demand
   MoeTile* d_moe_order = nullptr;
   uint32_t* d_moe_keys = nullptr;
   int64_t moe_cap = 0;
-  uint32_t* d_moe_masks = nullptr; // MoE token bitmasks and per-group counts; grow on demand
+  uint32_t* d_moe_ranks = nullptr; // MoE: device copy of a call's arrival ranks (kItemsCap words)
+  uint32_t* d_moe_masks = nullptr; // MoE token bitmasks; grow on demand
   int64_t moe_masks_cap = 0;
-  uint32_t* d_moe_partials = nullptr;
-  int64_t moe_partials_cap = 0;
   hipEvent_t slot_ev[kSlots] = {};
   bool slot_used[kSlots] = {};
   int slot = 0;
@@ -352,7 +353,9 @@ sgt_status sgt_ctx_create(sgt_ctx** out, int device) {
   chk(hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming), "hipEventCreate");
   chk(hipMalloc(&c->d_status, 4 * sizeof(uint32_t)), "hipMalloc(status)");
   chk(hipMalloc(&c->d_counters, 64 * sizeof(uint32_t)), "hipMalloc(counters)");
-  chk(hipMalloc(&c->d_moe, 512 * sizeof(uint32_t)), "hipMalloc(moe)");
+  chk(hipMalloc(&c->d_moe, 1024 * sizeof(uint32_t)), "hipMalloc(moe)");
+  if (st == SGT_OK) chk(hipMemset(c->d_moe, 0, 1024 * sizeof(uint32_t)), "hipMemset(moe)");
+  chk(hipMalloc(&c->d_moe_ranks, kItemsCap * sizeof(uint32_t)), "hipMalloc(moe ranks)");
   if (st == SGT_OK) chk(hipMemset(c->d_status, 0, 4 * sizeof(uint32_t)), "hipMemset");
   for (int s = 0; s < kSlots && st == SGT_OK; ++s) {
     chk(hipHostMalloc(&c->h_items[s], kItemsCap * sizeof(ProdItem), hipHostMallocDefault), "hipHostMalloc");
@@ -389,7 +392,7 @@ sgt_status sgt_ctx_destroy(sgt_ctx* c) {
   if (c->d_moe_order) (void)hipFree(c->d_moe_order);
   if (c->d_moe_keys) (void)hipFree(c->d_moe_keys);
   if (c->d_moe_masks) (void)hipFree(c->d_moe_masks);
-  if (c->d_moe_partials) (void)hipFree(c->d_moe_partials);
+  if (c->d_moe_ranks) (void)hipFree(c->d_moe_ranks);
   if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
   if (c->ev_join) (void)hipEventDestroy(c->ev_join);
   if (c->prod) (void)hipStreamDestroy(c->prod);
@@ -684,8 +687,8 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   const int64_t max_tiles = moe_max_tiles(T, E, topk, rows);
   const int tpg = moe_tokens_per_group(T, topk);
   const int64_t n_groups = (T + tpg - 1) / tpg;
-  const int64_t mask_words = (int64_t)((E + 31) / 32) * T, partial_words = n_groups * E;
-  if (ctx->moe_cap < max_tiles || ctx->moe_masks_cap < mask_words || ctx->moe_partials_cap < partial_words) {
+  const int64_t mask_words = (int64_t)((E + 31) / 32) * T;
+  if (ctx->moe_cap < max_tiles || ctx->moe_masks_cap < mask_words) {
     HIP_TRY(hipDeviceSynchronize());
     if (ctx->moe_cap < max_tiles) {
       if (ctx->d_moe_tiles) (void)hipFree(ctx->d_moe_tiles);
@@ -708,22 +711,18 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
       HIP_TRY(hipMalloc(&ctx->d_moe_masks, cap * sizeof(uint32_t)));
       ctx->moe_masks_cap = cap;
     }
-    if (ctx->moe_partials_cap < partial_words) {
-      if (ctx->d_moe_partials) (void)hipFree(ctx->d_moe_partials);
-      ctx->d_moe_partials = nullptr;
-      ctx->moe_partials_cap = 0;
-      const int64_t cap = std::max<int64_t>(partial_words, 1 << 16);
-      HIP_TRY(hipMalloc(&ctx->d_moe_partials, cap * sizeof(uint32_t)));
-      ctx->moe_partials_cap = cap;
-    }
   }
   MoeTables tb{};
   tb.masks = ctx->d_moe_masks;
-  tb.partials = ctx->d_moe_partials;
+  tb.counts = ctx->d_moe + 256 + 256 * ctx->moe_parity;
+  tb.counts_next = ctx->d_moe + 256 + 256 * (1 - ctx->moe_parity);
   tb.n_groups = (int32_t)n_groups;
   tb.tokens_per_group = tpg;
   tb.n_tiles = ctx->d_moe;
+  tb.tiles_cap = (uint32_t)ctx->moe_cap;
   tb.claim = ctx->d_moe + 4;
+  tb.done = ctx->d_moe + 8;
+  tb.ranks = ctx->d_moe_ranks;
   tb.tiles = ctx->d_moe_tiles;
   tb.keys = ctx->d_moe_keys;
   tb.order = ctx->d_moe_order;
@@ -733,8 +732,9 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   a.X = static_cast<const uint16_t*>(X_gathered);
   a.We = static_cast<const uint16_t*>(W_experts);
   a.Y = Y; a.row_token = row_token; a.expert_off = expert_off; a.order = tb.order; a.n_tiles = tb.n_tiles;
+  a.tiles_cap = tb.tiles_cap;
   a.claim = tb.claim; a.flags = shard_flags; a.status = ctx->d_status; a.trace = o.trace;
-  a.T = T; a.H = H; a.I = I; a.E = E; a.flag_rows = (int32_t)p.flag_rows; a.tiles_n = p.tiles_n;
+  a.T = T; a.H = H; a.I = I; a.rows = T * topk; a.E = E; a.flag_rows = (int32_t)p.flag_rows; a.tiles_n = p.tiles_n;
   a.epoch = e; a.timeout_ticks = timeout_ticks(o);
   const int64_t n_items_max = max_tiles * p.tiles_n;
   uint64_t* trace_rel = o.trace ? o.trace + n_items_max * 4 : nullptr;
@@ -744,6 +744,7 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   auto route_and_compute = [&](const uint32_t* ranks, int grid) -> sgt_status {
     HIP_TRY(launch_moe_route(logits, T, E, topk, ranks, a.flag_rows, (uint32_t)p.n_flags, rows, tb, expert_off,
                              row_token, topk_ids, stream));
+    ctx->moe_parity ^= 1;  // this call's top-k cleared the other counts buffer for the next call
     if (I > 0) {
       sgt_status s2;
       if ((s2 = mark(o, 0, stream)) != SGT_OK) return s2;
@@ -787,10 +788,19 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], ctx->h_items[slot], n_items * sizeof(ProdItem), hipMemcpyHostToDevice,
                          ctx->prod));
   HIP_TRY(launch_ag_producer(X_gathered, shard_flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
-                             trace_rel, pwg, ctx->prod));
+                             trace_rel, pwg, ctx->prod, ctx->d_moe + 12));
   HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
-  if ((st = route_and_compute(ctx->d_ranks[slot], o.consumer_cus > 0 ? o.consumer_cus : std::max(1, ctx->n_cu - pwg))) !=
-      SGT_OK)
+  // The consumer takes the whole chip: its last pwg workgroups land on the
+  // producer's CUs as the producer finishes (they claim work dynamically, so
+  // arriving late only means fewer items).  Each of those checks once, without
+  // waiting, that every producer workgroup is running; if not (the producer is
+  // not fully dispatched), it exits, so it can never keep the producer off the
+  // chip.  A count that never matches (a failed earlier call) only makes them exit.
+  ctx->moe_prod_started += (uint32_t)pwg;
+  a.started = ctx->d_moe + 12;
+  a.started_all = ctx->moe_prod_started;
+  a.late_blocks = o.consumer_cus > 0 ? 0 : std::min(pwg, ctx->n_cu - 1);
+  if ((st = route_and_compute(ctx->d_ranks[slot], o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu)) != SGT_OK)
     return st;
   HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
   HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));

@@ -152,6 +152,16 @@ def test_moe_repeat_reuses_flags(ctx, orc):
         last = fl[0]
 
 
+def test_moe_expert_count_changes_between_calls(ctx, orc):
+    """One context, successive calls with fewer and more experts: every call's routing tables must be
+    exact whatever the previous call routed (the per-expert counts are reused across calls)."""
+    for (E, k) in [(5, 2), (200, 12), (3, 3), (64, 8), (256, 1)]:
+        w = I.scaled(I.MOE, W=2, T=384, H=64, I=64, E=E, topk=k)
+        shards, We, logits = I.make_moe(w, salt=E)
+        res = run_moe(ctx, shards, We, logits, k, flag_rows=32, peer_gbps=10.0, arrival_seed=E)
+        check_moe(orc, shards, We, logits, k, res, what="E=%d k=%d" % (E, k))
+
+
 def test_moe_bits_independent_of_arrival(ctx):
     """The order in which tiles land and are claimed changes no bit of the results."""
     w = I.scaled(I.MOE, W=8, T=1024, H=256, I=256, E=64, topk=8)
