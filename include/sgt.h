@@ -195,14 +195,38 @@ SGT_API sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const 
  *     p pushed for this rank; partials[rank] is not read (may be NULL).
  * partial_out: M x N fp32.  C_shard: (M/W) x N fp32.
  * gflags: ceil(M/rs_tile) * ceil(N/rs_tile) words; pflags: W * (tiles of one
- *     block) words.  The peers' flags are set by the library before the
- *     reduction may read (pre-resident peers) or paced by the producer when
- *     peer_gbps > 0.
+ *     block) words.  The peers' partials are resident: their flags are set by
+ *     the library before the reduction may read (for paced arrival see
+ *     sgt_gemm_rs_paced; here opts->peer_gbps > 0 is SGT_EUNSUPPORTED).
  * Requirements: as sgt_ag_gemm, and (M/W) % rs_tile == 0.
  */
 SGT_API sgt_status sgt_gemm_rs(sgt_ctx* ctx, const void* A_local, const void* B, const float* const* partials,
                        float* partial_out, float* C_shard, uint32_t* gflags, uint32_t* pflags, int W, int64_t M,
                        int64_t K, int64_t N, const sgt_opts* opts, void* stream);
+
+/*
+ * GEMM + ReduceScatter with the peers' blocks arriving over simulated links
+ * (semantics page, "GEMM + ReduceScatter overlap": the reduction of a tile
+ * waits for the signals of every contribution to it; paper summary, "Method":
+ * ReduceScatter in push mode).  Same results as sgt_gemm_rs with
+ * partials = peer_blocks, but the peers' data is not resident: the producer
+ * copies each peer's block peer_blocks[p] (its push for this rank, in its
+ * memory) into this rank's receive buffer inbox[p], in bands of rs_tile rows,
+ * and releases the peer flags of a band's rs_tile x rs_tile tiles no earlier
+ * than the time link p would deliver the band at opts->peer_gbps (0 =
+ * unthrottled), in order or seeded order (opts->arrival_order != 0), plus
+ * U[0, opts->jitter_us].  The reduction sums inbox[p] as tiles arrive.
+ * peer_blocks, inbox: host arrays of W device pointers to (M/W) x N fp32
+ *     (16-byte aligned); entry [rank] is not read.  On return inbox[p] holds
+ *     peer_blocks[p] bit for bit.  Other arguments as sgt_gemm_rs.
+ * Modes: SGT_PROD_CU (overlapped: the producer on its own stream and CUs) or
+ *     SGT_PROD_SERIAL; SGT_PROD_PRESET is SGT_EINVAL (use sgt_gemm_rs).
+ * Requirements: as sgt_gemm_rs, and rs_tile * N * 4 < 2^31.
+ */
+SGT_API sgt_status sgt_gemm_rs_paced(sgt_ctx* ctx, const void* A_local, const void* B, const float* const* peer_blocks,
+                                     float* const* inbox, float* partial_out, float* C_shard, uint32_t* gflags,
+                                     uint32_t* pflags, int W, int64_t M, int64_t K, int64_t N, const sgt_opts* opts,
+                                     void* stream);
 
 /* Flag counts for sgt_gemm_rs: *gflags_n and *pflags_n (either may be NULL). */
 SGT_API sgt_status sgt_rs_flag_count(int W, int64_t M, int64_t N, const sgt_opts* opts, int64_t* gflags_n, int64_t* pflags_n);

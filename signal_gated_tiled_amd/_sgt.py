@@ -82,10 +82,12 @@ def lib() -> ctypes.CDLL:
         L.sgt_rs_flag_count.argtypes = [ctypes.c_int, I64, I64, ctypes.POINTER(Opts), ctypes.POINTER(I64),
                                         ctypes.POINTER(I64)]
         L.sgt_gemm_rs.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int, I64, I64, I64, ctypes.POINTER(Opts), P]
+        L.sgt_gemm_rs_paced.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_int, I64, I64, I64,
+                                        ctypes.POINTER(Opts), P]
         L.sgt_moe_ag_gemm.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_int, I64, I64, I64, ctypes.c_int,
                                       ctypes.c_int, ctypes.POINTER(Opts), P]
         for f in ("sgt_ctx_create", "sgt_ctx_destroy", "sgt_sync", "sgt_ag_gemm", "sgt_rs_flag_count", "sgt_gemm_rs",
-                  "sgt_moe_ag_gemm"):
+                  "sgt_gemm_rs_paced", "sgt_moe_ag_gemm"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -276,6 +278,25 @@ class Context:
                                  _dev_ptr(C_shard, "C_shard", dev), _dev_ptr(gflags, "gflags", dev),
                                  _dev_ptr(pflags, "pflags", dev), W, M, K, N, ctypes.byref(o),
                                  _stream_handle(stream)))
+
+    def gemm_rs_paced(self, A_local, B, peer_blocks: Sequence, inbox: Sequence, partial_out, C_shard, gflags, pflags, *,
+                      stream=None, **kw):
+        """GEMM+ReduceScatter with the peers' blocks copied into `inbox` at the simulated link rate."""
+        dev = A_local.device
+        W = len(peer_blocks)
+        M, K = A_local.shape
+        lay = kw.get("b_layout", "kn")
+        N = B.shape[1] if lay == "kn" else B.shape[0]
+        kw.setdefault("in_dtype", _dtype_code(B))
+        o = make_opts(**kw)
+        src = (P * W)(*[_dev_ptr(p, "peer_blocks[%d]" % i, dev) if p is not None else 0
+                        for i, p in enumerate(peer_blocks)])
+        dst = (P * W)(*[_dev_ptr(p, "inbox[%d]" % i, dev) if p is not None else 0 for i, p in enumerate(inbox)])
+        _check(lib().sgt_gemm_rs_paced(self._h, _dev_ptr(A_local, "A_local", dev), _dev_ptr(B, "B", dev),
+                                       ctypes.cast(src, P), ctypes.cast(dst, P),
+                                       _dev_ptr(partial_out, "partial_out", dev), _dev_ptr(C_shard, "C_shard", dev),
+                                       _dev_ptr(gflags, "gflags", dev), _dev_ptr(pflags, "pflags", dev), W, M, K, N,
+                                       ctypes.byref(o), _stream_handle(stream)))
 
     def moe_ag_gemm(self, X_shards: Sequence, W_experts, logits, X_gathered, Y, expert_off, row_token, topk_ids,
                     shard_flags, *, topk: int, stream=None, **kw):

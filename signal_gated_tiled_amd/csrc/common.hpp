@@ -16,15 +16,18 @@ struct PtrTable {
   const void* p[kMaxW];
 };
 
-// One AllGather producer work item: copy signal tile `tile` of the gathered
-// matrix from `src` (inside peer `peer`'s shard), then release its flag no
-// earlier than `release` clock ticks after the producer workgroup started.
+// One producer work item: copy tile_bytes from `src` (in peer `peer`'s
+// buffer) to `dst`, then release flags [flag0, flag0 + nflags) no earlier than
+// `release` clock ticks after the producer workgroup started.  An AllGather
+// signal tile releases its one flag; a GEMM+ReduceScatter band of a peer's
+// partial block releases the flags of every tile in the band.
 struct ProdItem {
-  uint32_t tile;
-  uint32_t peer;
-  uint64_t release;
   const char* src;
-  uint64_t pad;
+  char* dst;
+  uint64_t release;
+  uint32_t flag0;
+  uint16_t nflags;
+  uint16_t peer;
 };
 
 // Arguments of the AllGather consumer (both the bf16 MFMA and fp32 kernels).

@@ -65,7 +65,7 @@ constexpr int kProdThreads = 256;
 // before its release, `lead` being twice the workgroup's last measured copy
 // time (so the copy is done by the release), which keeps the producer's HBM
 // traffic close to the links' rate instead of front-loading it.
-__global__ void __launch_bounds__(kProdThreads) ag_producer_kernel(char* gathered, uint32_t* flags,
+__global__ void __launch_bounds__(kProdThreads) ag_producer_kernel(uint32_t* flags,
                                                                    const ProdItem* items, int n_items,
                                                                    int64_t tile_bytes, uint32_t epoch,
                                                                    int withhold_peer, uint64_t* trace_release,
@@ -90,7 +90,7 @@ __global__ void __launch_bounds__(kProdThreads) ag_producer_kernel(char* gathere
       c0 = clock_ticks();
     }
     __syncthreads();
-    const bool coherent = copy_bytes<32>(gathered + (int64_t)item.tile * tile_bytes, item.src, tile_bytes);
+    const bool coherent = copy_bytes<32>(item.dst, item.src, tile_bytes);
     // Every wave waits until its stores are acknowledged; after the barrier one
     // lane publishes the flag.  Device-scope stores leave nothing in the XCD's
     // L2 to write back, so the flag needs no release write-back; the plain
@@ -105,10 +105,14 @@ __global__ void __launch_bounds__(kProdThreads) ag_producer_kernel(char* gathere
       const uint64_t target = t0 + item.release;
       while (clock_ticks() < target) __builtin_amdgcn_s_sleep(4);
       if (p != withhold_peer) {
-        if (coherent) flag_publish_coherent(flags + item.tile, epoch);
-        else flag_release(flags + item.tile, epoch);
+        if (coherent) {
+          for (uint32_t f = 0; f < item.nflags; ++f) flag_publish_coherent(flags + item.flag0 + f, epoch);
+        } else {
+          flag_release(flags + item.flag0, epoch);
+          for (uint32_t f = 1; f < item.nflags; ++f) flag_publish_coherent(flags + item.flag0 + f, epoch);
+        }
       }
-      if (trace_release) trace_release[item.tile] = clock_ticks();
+      if (trace_release) trace_release[item.flag0] = clock_ticks();
     }
   }
 }
@@ -139,15 +143,15 @@ hipError_t launch_rs_prepare(uint32_t* pflags, int64_t n, uint32_t v, uint32_t* 
   return hipGetLastError();
 }
 
-hipError_t launch_ag_producer(void* gathered, uint32_t* flags, const ProdItem* items, int n_items,
+hipError_t launch_ag_producer(uint32_t* flags, const ProdItem* items, int n_items,
                               int64_t tile_bytes, uint32_t epoch, int withhold_peer, uint64_t* trace_release, int grid,
                               hipStream_t stream, uint32_t* started) {
   if (n_items <= 0) return hipSuccess;
   if (grid > n_items) grid = n_items;
   // first estimate of a tile's copy time: at 16 GB/s per workgroup (100 MHz ticks)
   const uint64_t lead0 = (uint64_t)(tile_bytes / 160) + 100;
-  hipLaunchKernelGGL(ag_producer_kernel, dim3(grid), dim3(kProdThreads), 0, stream, static_cast<char*>(gathered),
-                     flags, items, n_items, tile_bytes, epoch, withhold_peer, trace_release, lead0, started);
+  hipLaunchKernelGGL(ag_producer_kernel, dim3(grid), dim3(kProdThreads), 0, stream, flags, items, n_items, tile_bytes,
+                     epoch, withhold_peer, trace_release, lead0, started);
   return hipGetLastError();
 }
 

@@ -22,7 +22,7 @@
 #include "sched.hpp"
 
 namespace sgt {
-hipError_t launch_ag_producer(void* gathered, uint32_t* flags, const ProdItem* items, int n_items,
+hipError_t launch_ag_producer(uint32_t* flags, const ProdItem* items, int n_items,
                               int64_t tile_bytes, uint32_t epoch, int withhold_peer, uint64_t* trace_release, int grid,
                               hipStream_t stream, uint32_t* started = nullptr);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
@@ -225,14 +225,24 @@ void shuffle(std::vector<int64_t>& v, uint64_t& s) {
 // local_first: the local shard's tiles go first (released at once), for a
 // consumer that reads every row from the gathered buffer; otherwise they go
 // last.  ranks (optional): ranks[tile] = the tile's position in the list.
+ProdItem sched_item(int64_t tile, int peer, double release) {
+  ProdItem it{};
+  it.flag0 = (uint32_t)tile;
+  it.nflags = 1;
+  it.peer = (uint16_t)peer;
+  it.release = (uint64_t)release;
+  return it;
+}
+
 int build_schedule(const AgPlan& p, int W, int rank, int64_t K, int esz, const sgt_opts& o,
-                   const void* const* shards, ProdItem* items, bool local_first = false, uint32_t* ranks = nullptr) {
+                   const void* const* shards, void* gathered, ProdItem* items, bool local_first = false,
+                   uint32_t* ranks = nullptr) {
   const double tile_bytes = (double)p.flag_rows * (double)K * esz;
   const double ticks_per_tile = o.peer_gbps > 0 ? tile_bytes / (o.peer_gbps * 1e3) * kTicksPerUs : 0.0;
   const int64_t tps = p.tiles_per_shard;
   int n = 0;
   if (local_first)
-    for (int64_t t = 0; t < tps; ++t) items[n++] = ProdItem{(uint32_t)(rank * tps + t), (uint32_t)rank, 0, nullptr, 0};
+    for (int64_t t = 0; t < tps; ++t) items[n++] = sched_item(rank * tps + t, rank, 0.0);
   const int first_remote = n;
   uint64_t s = o.arrival_seed * 0x100000001B3ull + 0x5851F42D4C957F2Dull;
   if (o.arrival_order == 2 && W > 1) {
@@ -243,7 +253,7 @@ int build_schedule(const AgPlan& p, int W, int rank, int64_t K, int esz, const s
     const double per = ticks_per_tile / (double)(W - 1);
     for (size_t g = 0; g < all.size(); ++g) {
       const double rel = (double)(g + 1) * per + jitter_ticks(o, s);
-      items[n++] = ProdItem{(uint32_t)all[g], (uint32_t)(all[g] / tps), (uint64_t)rel, nullptr, 0};
+      items[n++] = sched_item(all[g], (int)(all[g] / tps), rel);
     }
   } else {
     std::vector<int64_t> order((size_t)tps);
@@ -253,7 +263,7 @@ int build_schedule(const AgPlan& p, int W, int rank, int64_t K, int esz, const s
       if (o.arrival_order == 1) shuffle(order, s);
       for (int64_t k = 0; k < tps; ++k) {
         const double rel = (double)(k + 1) * ticks_per_tile + jitter_ticks(o, s);
-        items[n++] = ProdItem{(uint32_t)(peer * tps + order[(size_t)k]), (uint32_t)peer, (uint64_t)rel, nullptr, 0};
+        items[n++] = sched_item(peer * tps + order[(size_t)k], peer, rel);
       }
     }
   }
@@ -262,11 +272,12 @@ int build_schedule(const AgPlan& p, int W, int rank, int64_t K, int esz, const s
   // The AllGather consumer reads the local shard from the shard itself, so its
   // copy into the gathered buffer goes last, off the critical path.
   if (!local_first)
-    for (int64_t t = 0; t < tps; ++t) items[n++] = ProdItem{(uint32_t)(rank * tps + t), (uint32_t)rank, 0, nullptr, 0};
+    for (int64_t t = 0; t < tps; ++t) items[n++] = sched_item(rank * tps + t, rank, 0.0);
   for (int i = 0; i < n; ++i) {
-    const int64_t local_tile = (int64_t)items[i].tile - (int64_t)items[i].peer * tps;
+    const int64_t tile = items[i].flag0, local_tile = tile - (int64_t)items[i].peer * tps;
     items[i].src = static_cast<const char*>(shards[items[i].peer]) + local_tile * (int64_t)tile_bytes;
-    if (ranks) ranks[items[i].tile] = (uint32_t)i;
+    items[i].dst = static_cast<char*>(gathered) + tile * (int64_t)tile_bytes;
+    if (ranks) ranks[tile] = (uint32_t)i;
   }
   return n;
 }
@@ -494,7 +505,7 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
 
   int slot;
   if ((st = next_slot(ctx, &slot)) != SGT_OK) return st;
-  const int n_items = build_schedule(p, W, o.rank, K, esz, o, A_shards, ctx->h_items[slot]);
+  const int n_items = build_schedule(p, W, o.rank, K, esz, o, A_shards, A_gathered, ctx->h_items[slot]);
   const int pwg = std::min(default_producer_wgs(o, ctx->n_cu), n_items);
   uint64_t* trace_rel = o.trace ? o.trace + (int64_t)total_tiles * 4 : nullptr;
   const int64_t tile_bytes = p.flag_rows * K * esz;
@@ -502,7 +513,7 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   if (o.producer == SGT_PROD_SERIAL) {
     HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], ctx->h_items[slot], n_items * sizeof(ProdItem),
                            hipMemcpyHostToDevice, stream));
-    HIP_TRY(launch_ag_producer(A_gathered, flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
+    HIP_TRY(launch_ag_producer(flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
                                trace_rel, pwg, stream));
     HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
     ctx->slot_used[slot] = true;
@@ -523,7 +534,7 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
   HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], ctx->h_items[slot], n_items * sizeof(ProdItem), hipMemcpyHostToDevice,
                          ctx->prod));
-  HIP_TRY(launch_ag_producer(A_gathered, flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
+  HIP_TRY(launch_ag_producer(flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
                              trace_rel, pwg, ctx->prod));
   HIP_TRY(hipEventRecord(ctx->slot_ev[slot], ctx->prod));
   ctx->slot_used[slot] = true;
@@ -556,17 +567,30 @@ sgt_status sgt_rs_flag_count(int W, int64_t M, int64_t N, const sgt_opts* opts, 
   return SGT_OK;
 }
 
-sgt_status sgt_gemm_rs(sgt_ctx* ctx, const void* A_local, const void* B, const float* const* partials,
-                       float* partial_out, float* C_shard, uint32_t* gflags, uint32_t* pflags, int W, int64_t M,
-                       int64_t K, int64_t N, const sgt_opts* opts, void* stream_) {
+}  // extern "C"
+
+namespace {
+
+// GEMM + ReduceScatter, shared by the resident and the paced entry points.
+// reduce_from[p]: what the reduction sums for peer p.  peer_blocks == NULL:
+// the peers' data is resident and their flags are preset.  Otherwise the
+// producer copies peer_blocks[p] into reduce_from[p] in bands of rs_tile rows,
+// each band released (its tiles' peer flags) when peer p's link would deliver it.
+sgt_status gemm_rs_impl(sgt_ctx* ctx, const void* A_local, const void* B, const float* const* reduce_from,
+                        const float* const* peer_blocks, float* partial_out, float* C_shard, uint32_t* gflags,
+                        uint32_t* pflags, int W, int64_t M, int64_t K, int64_t N, const sgt_opts* opts,
+                        void* stream_) {
   if (!ctx) return fail(SGT_EINVAL, "ctx is NULL");
   sgt_status st = check_opts(opts, W < 1 ? 1 : W);
   if (st != SGT_OK) return st;
   const sgt_opts& o = *opts;
+  const bool paced = peer_blocks != nullptr;
   if (o.in_dtype != SGT_BF16) return fail(SGT_EUNSUPPORTED, "GEMM+RS takes bf16 inputs");
   if (o.out_dtype != SGT_F32) return fail(SGT_EUNSUPPORTED, "GEMM+RS partials are fp32");
-  if (o.producer == SGT_PROD_CU && o.peer_gbps > 0)
-    return fail(SGT_EUNSUPPORTED, "paced peer arrival for GEMM+RS is not implemented; peers are pre-resident");
+  if (!paced && o.producer == SGT_PROD_CU && o.peer_gbps > 0)
+    return fail(SGT_EUNSUPPORTED, "sgt_gemm_rs takes resident peers; paced arrival is sgt_gemm_rs_paced");
+  if (paced && o.producer == SGT_PROD_PRESET)
+    return fail(SGT_EINVAL, "sgt_gemm_rs_paced needs a producer mode (CU or serial); resident peers: sgt_gemm_rs");
   if (W < 1 || W > kMaxW) return fail(SGT_EINVAL, "W = %d outside [1, %d]", W, kMaxW);
   if (M < 0 || N < 0 || K < 1 || M % W) return fail(SGT_EINVAL, "bad shape M=%lld K=%lld N=%lld W=%d",
                                                     (long long)M, (long long)K, (long long)N, W);
@@ -578,15 +602,23 @@ sgt_status sgt_gemm_rs(sgt_ctx* ctx, const void* A_local, const void* B, const f
   if ((int64_t)kBMrs() * K * 2 >= ((int64_t)1 << 31) || (int64_t)kBMrs() * N * 4 >= ((int64_t)1 << 31) ||
       (o.b_layout == SGT_KN && K * N * 2 >= ((int64_t)1 << 31)))
     return fail(SGT_EUNSUPPORTED, "K or N too large for 32-bit tile offsets");
+  const int64_t band_bytes = (int64_t)rt * N * 4;
+  const int64_t rs_tn = (N + rt - 1) / rt;
+  if (paced && (band_bytes >= ((int64_t)1 << 31) || rs_tn > 65535 || (int64_t)(W - 1) * (br / rt) > kItemsCap))
+    return fail(SGT_EUNSUPPORTED, "bands too large or too many for the producer");
   if (M > 0 && N > 0) {
-    if (!A_local || !B || !partial_out || !C_shard || !gflags || !pflags || !partials)
+    if (!A_local || !B || !partial_out || !C_shard || !gflags || !pflags || !reduce_from)
       return fail(SGT_EINVAL, "NULL pointer argument");
     if (!aligned16(A_local) || !aligned16(B) || !aligned16(partial_out) || !aligned16(C_shard) ||
         !aligned16(gflags) || !aligned16(pflags))
       return fail(SGT_EINVAL, "pointers must be 16-byte aligned");
-    for (int p = 0; p < W; ++p)
-      if (p != o.rank && (!partials[p] || !aligned16(partials[p])))
-        return fail(SGT_EINVAL, "partials[%d] NULL or not 16-byte aligned", p);
+    for (int p = 0; p < W; ++p) {
+      if (p == o.rank) continue;
+      if (!reduce_from[p] || !aligned16(reduce_from[p]))
+        return fail(SGT_EINVAL, "%s[%d] NULL or not 16-byte aligned", paced ? "inbox" : "partials", p);
+      if (paced && (!peer_blocks[p] || !aligned16(peer_blocks[p])))
+        return fail(SGT_EINVAL, "peer_blocks[%d] NULL or not 16-byte aligned", p);
+    }
   }
   std::lock_guard<std::mutex> lock(ctx->mu);
   DeviceGuard g(ctx->device);
@@ -596,28 +628,105 @@ sgt_status sgt_gemm_rs(sgt_ctx* ctx, const void* A_local, const void* B, const f
 
   RsArgs a{};
   a.A = A_local; a.B = B; a.P = partial_out; a.C_shard = C_shard;
-  for (int p = 0; p < W; ++p) a.partials.p[p] = (p == o.rank) ? nullptr : partials[p];
+  for (int p = 0; p < W; ++p) a.partials.p[p] = (p == o.rank) ? nullptr : reduce_from[p];
   a.gflags = gflags; a.pflags = pflags; a.status = ctx->d_status; a.trace = o.trace;
   a.M = M; a.N = N; a.K = K; a.block_rows = br; a.W = W; a.rank = o.rank;
   const int bm = rs_gemm_tile();
   a.tiles_n = (int)((N + bm - 1) / bm);
   a.tiles_m = (int)(W * ((br + bm - 1) / bm));
-  a.rs_tile = rt; a.rs_tm = (int)(br / rt); a.rs_tn = (int)((N + rt - 1) / rt);
+  a.rs_tile = rt; a.rs_tm = (int)(br / rt); a.rs_tn = (int)rs_tn;
   a.b_layout = o.b_layout;
   a.n_gemm_tiles = a.tiles_m * a.tiles_n;
   a.n_red_items = a.rs_tm * a.rs_tn;
   a.epoch = e; a.timeout_ticks = timeout_ticks(o);
   a.tile_waves = o.tile_waves ? o.tile_waves : 8;
-  // Peers' partials are resident: their flags are set before the kernel starts.
-  // The reduction-claim counter starts at zero (a fill kernel, not a memset).
   a.red_counter = ctx->d_counters;
-  HIP_TRY(launch_rs_prepare(pflags, np, e, ctx->d_counters, stream));
   const int total = a.n_gemm_tiles + a.n_red_items;
-  const int grid = std::min(total, o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu);
+
+  if (!paced) {
+    // Peers' partials are resident: their flags are set before the kernel
+    // starts, and the reduction-claim counter restarts (a fill kernel, not a memset).
+    HIP_TRY(launch_rs_prepare(pflags, np, e, ctx->d_counters, stream));
+    const int grid = std::min(total, o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu);
+    if ((st = mark(o, 0, stream)) != SGT_OK) return st;
+    HIP_TRY(launch_gemm_rs(a, grid, stream));
+    if ((st = mark(o, 1, stream)) != SGT_OK) return st;
+    return finish(ctx, o, stream);
+  }
+
+  // Paced peers: the producer schedule (each peer's bands, in order or shuffled,
+  // one band every band_bytes / peer_gbps on each link, plus jitter).
+  int slot;
+  if ((st = next_slot(ctx, &slot)) != SGT_OK) return st;
+  ProdItem* items = ctx->h_items[slot];
+  const int64_t bands = a.rs_tm, block_tiles = (int64_t)a.rs_tm * a.rs_tn;
+  const double ticks_per_band = o.peer_gbps > 0 ? (double)band_bytes / (o.peer_gbps * 1e3) * kTicksPerUs : 0.0;
+  uint64_t seed = o.arrival_seed * 0x100000001B3ull + 0x5851F42D4C957F2Dull;
+  int n = 0;
+  std::vector<int64_t> order((size_t)bands);
+  for (int d = 1; d < W; ++d) {
+    const int peer = (o.rank + d) % W;
+    for (int64_t j = 0; j < bands; ++j) order[(size_t)j] = j;
+    if (o.arrival_order != 0) shuffle(order, seed);
+    for (int64_t q = 0; q < bands; ++q) {
+      const int64_t j = order[(size_t)q];
+      ProdItem it = sched_item(peer * block_tiles + j * a.rs_tn, peer, (double)(q + 1) * ticks_per_band +
+                                                                        jitter_ticks(o, seed));
+      it.nflags = (uint16_t)a.rs_tn;
+      it.src = reinterpret_cast<const char*>(peer_blocks[peer]) + j * band_bytes;
+      it.dst = reinterpret_cast<char*>(const_cast<float*>(reduce_from[peer])) + j * band_bytes;
+      items[n++] = it;
+    }
+  }
+  std::stable_sort(items, items + n, [](const ProdItem& x, const ProdItem& y) { return x.release < y.release; });
+  const int pwg = std::min(default_producer_wgs(o, ctx->n_cu), std::max(n, 1));
+  HIP_TRY(launch_rs_prepare(pflags, 0, e, ctx->d_counters, stream));  // counter only: peers' flags come on arrival
+  if (o.producer == SGT_PROD_SERIAL) {
+    HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], items, n * sizeof(ProdItem), hipMemcpyHostToDevice, stream));
+    HIP_TRY(launch_ag_producer(pflags, ctx->d_items[slot], n, band_bytes, e, o.withhold_peer, nullptr, pwg, stream));
+    HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
+    ctx->slot_used[slot] = true;
+    const int grid = std::min(total, o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu);
+    if ((st = mark(o, 0, stream)) != SGT_OK) return st;
+    HIP_TRY(launch_gemm_rs(a, grid, stream));
+    if ((st = mark(o, 1, stream)) != SGT_OK) return st;
+    return finish(ctx, o, stream);
+  }
+  // Overlapped: the producer on its own stream and CUs; the GEMM+RS kernel on
+  // the rest (one workgroup per CU), so the reduction's waits cannot starve it.
+  HIP_TRY(hipEventRecord(ctx->ev_fork, stream));
+  HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
+  HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], items, n * sizeof(ProdItem), hipMemcpyHostToDevice, ctx->prod));
+  HIP_TRY(launch_ag_producer(pflags, ctx->d_items[slot], n, band_bytes, e, o.withhold_peer, nullptr, pwg, ctx->prod));
+  HIP_TRY(hipEventRecord(ctx->slot_ev[slot], ctx->prod));
+  ctx->slot_used[slot] = true;
+  const int grid = std::min(total, o.consumer_cus > 0 ? o.consumer_cus : std::max(1, ctx->n_cu - pwg));
   if ((st = mark(o, 0, stream)) != SGT_OK) return st;
   HIP_TRY(launch_gemm_rs(a, grid, stream));
   if ((st = mark(o, 1, stream)) != SGT_OK) return st;
+  HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
+  HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
   return finish(ctx, o, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+sgt_status sgt_gemm_rs(sgt_ctx* ctx, const void* A_local, const void* B, const float* const* partials,
+                       float* partial_out, float* C_shard, uint32_t* gflags, uint32_t* pflags, int W, int64_t M,
+                       int64_t K, int64_t N, const sgt_opts* opts, void* stream) {
+  return gemm_rs_impl(ctx, A_local, B, partials, nullptr, partial_out, C_shard, gflags, pflags, W, M, K, N, opts,
+                      stream);
+}
+
+sgt_status sgt_gemm_rs_paced(sgt_ctx* ctx, const void* A_local, const void* B, const float* const* peer_blocks,
+                             float* const* inbox, float* partial_out, float* C_shard, uint32_t* gflags,
+                             uint32_t* pflags, int W, int64_t M, int64_t K, int64_t N, const sgt_opts* opts,
+                             void* stream) {
+  if (!peer_blocks || !inbox) return fail(SGT_EINVAL, "peer_blocks or inbox is NULL");
+  return gemm_rs_impl(ctx, A_local, B, inbox, peer_blocks, partial_out, C_shard, gflags, pflags, W, M, K, N, opts,
+                      stream);
 }
 
 static int moe_tile_rows(const sgt_opts& o) { return o.tile_rows > 0 ? o.tile_rows : 256; }
@@ -764,7 +873,8 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
 
   int slot;
   if ((st = next_slot(ctx, &slot)) != SGT_OK) return st;
-  const int n_items = build_schedule(p, W, o.rank, H, esz, o, X_shards, ctx->h_items[slot], true, ctx->h_ranks[slot]);
+  const int n_items =
+      build_schedule(p, W, o.rank, H, esz, o, X_shards, X_gathered, ctx->h_items[slot], true, ctx->h_ranks[slot]);
   const int pwg = std::min(default_producer_wgs(o, ctx->n_cu), n_items);
   // The placement kernel reads the arrival ranks straight from pinned host
   // memory (a few words per workgroup); the producer's schedule is copied on
@@ -772,7 +882,7 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   if (o.producer == SGT_PROD_SERIAL) {
     HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], ctx->h_items[slot], n_items * sizeof(ProdItem), hipMemcpyHostToDevice,
                            stream));
-    HIP_TRY(launch_ag_producer(X_gathered, shard_flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
+    HIP_TRY(launch_ag_producer(shard_flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
                                trace_rel, pwg, stream));
     if ((st = route_and_compute(ctx->d_ranks[slot], o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu)) != SGT_OK)
       return st;
@@ -787,7 +897,7 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
   HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], ctx->h_items[slot], n_items * sizeof(ProdItem), hipMemcpyHostToDevice,
                          ctx->prod));
-  HIP_TRY(launch_ag_producer(X_gathered, shard_flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
+  HIP_TRY(launch_ag_producer(shard_flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
                              trace_rel, pwg, ctx->prod, ctx->d_moe + 12));
   HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
   // The consumer takes the whole chip: its last pwg workgroups land on the

@@ -108,3 +108,90 @@ def test_full_gemm_rs_shape(ctx, orc):
     prow = sample_rows(w.M, w.W, per_shard=3, seed=2)
     assert_close(P[prow], orc.gemm(A, B, rows=prow), what="partial_out", **TOL_BF16)
     assert (gf == gf[0]).all() and (pf == gf[0]).all()
+
+
+def run_rs_paced(ctx, A, B, parts, rank, b_layout="kn", rs_tile=0, **kw):
+    """sgt_gemm_rs_paced: the peers' blocks start outside the inbox and arrive through the producer."""
+    W = len(parts)
+    M, K = A.shape
+    N = B.shape[1] if b_layout == "kn" else B.shape[0]
+    ng, npf = sgt.rs_flag_count(W, M, N, rs_tile=rs_tile)
+    P = poison_like(torch.empty((M, N), dtype=torch.float32, device="cuda:0"))
+    Cs = poison_like(torch.empty((M // W, N), dtype=torch.float32, device="cuda:0"))
+    gf = torch.zeros(max(ng, 4), dtype=torch.int32, device="cuda:0")
+    pf = torch.zeros(max(npf, 4), dtype=torch.int32, device="cuda:0")
+    src = [dev(p) if q != rank else None for q, p in enumerate(parts)]
+    inbox = [poison_like(torch.empty_like(s)) if s is not None else None for s in src]
+    ctx.gemm_rs_paced(dev(A), dev(B), src, inbox, P, Cs, gf, pf, rank=rank, b_layout=b_layout, rs_tile=rs_tile,
+                      blocking=True, **kw)
+    torch.cuda.synchronize()
+    return host(P), host(Cs), host(gf)[:ng], host(pf)[:npf], [host(x) if x is not None else None for x in inbox]
+
+
+PACED = [
+    dict(producer="cu"),
+    dict(producer="cu", peer_gbps=40.0, jitter_us=3.0, arrival_seed=5),
+    dict(producer="cu", peer_gbps=20.0, arrival_order="global", arrival_seed=9),
+    dict(producer="serial", peer_gbps=60.0),
+]
+
+
+@pytest.mark.parametrize("opts", PACED, ids=["cu", "cu-40gbps-jitter", "cu-20gbps-shuffled", "serial"])
+@pytest.mark.parametrize("shape", [SHAPES[0], SHAPES[2]])
+def test_gemm_rs_paced_parity(ctx, orc, shape, opts):
+    W, br, K, N, rt = shape
+    w = I.RSWorkload("t", W=W, M=W * br, K=K, N=N, seed_index=26)
+    A, B, parts = I.make_rs(w)
+    rank = 1
+    P, Cs, gf, pf, inbox = run_rs_paced(ctx, A, B, parts, rank, rs_tile=rt, **opts)
+    for q in range(W):
+        if q != rank:
+            assert np.array_equal(inbox[q].view(np.uint32), parts[q].view(np.uint32)), "inbox %d" % q
+    assert_close(P, orc.gemm(A, B), what="partial_out", **TOL_BF16)
+    assert_close(Cs, orc.gemm_rs(A, B, parts, rank), what="C_shard", **TOL_BF16)
+    assert (gf == gf[0]).all() and gf[0] != 0
+    nb = len(pf) // W
+    for q in range(W):
+        if q != rank:
+            assert (pf[q * nb:(q + 1) * nb] == gf[0]).all(), "peer %d flags" % q
+
+
+def test_gemm_rs_paced_matches_resident_bits(ctx):
+    w = I.RSWorkload("t", W=4, M=1024, K=256, N=392, seed_index=27)
+    A, B, parts = I.make_rs(w, B_layout="nk")
+    a = run_rs(ctx, A, B, parts, 2, b_layout="nk")
+    b = run_rs_paced(ctx, A, B, parts, 2, b_layout="nk", peer_gbps=30.0)
+    assert np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32))
+    assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+def test_gemm_rs_paced_zero_A_is_exact_peer_sum(ctx, orc):
+    w = I.RSWorkload("t", W=8, M=1024, K=64, N=256, dist="int", peer_dist="int", seed_index=28)
+    A, B, parts = I.make_rs(w)
+    A = np.zeros_like(A)
+    for rank in [0, 7]:
+        _, Cs, _, _, _ = run_rs_paced(ctx, A, B, parts, rank, peer_gbps=50.0, arrival_order="global",
+                                      arrival_seed=rank + 1)
+        assert np.array_equal(Cs.astype(np.float64), orc.gemm_rs(A, B, parts, rank))
+
+
+def test_gemm_rs_paced_withheld_peer_times_out(ctx):
+    w = I.RSWorkload("t", W=4, M=1024, K=64, N=256, seed_index=29)
+    A, B, parts = I.make_rs(w)
+    with pytest.raises(sgt.SgtError) as ei:
+        run_rs_paced(ctx, A, B, parts, 0, withhold_peer=2, timeout_ms=20.0)
+    assert ei.value.status == sgt.SGT_ETIMEDOUT
+    # the context stays usable
+    _, Cs, _, _, _ = run_rs_paced(ctx, A, B, parts, 0)
+    assert np.isfinite(Cs).all()
+
+
+def test_gemm_rs_paced_rejects_bad_modes(ctx):
+    w = I.RSWorkload("t", W=4, M=1024, K=64, N=256, seed_index=30)
+    A, B, parts = I.make_rs(w)
+    with pytest.raises(sgt.SgtError) as ei:
+        run_rs_paced(ctx, A, B, parts, 0, producer="preset")
+    assert ei.value.status == sgt.SGT_EINVAL
+    with pytest.raises(sgt.SgtError) as ei:
+        run_rs(ctx, A, B, parts, 0, peer_gbps=10.0)
+    assert ei.value.status == sgt.SGT_EUNSUPPORTED
