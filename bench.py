@@ -11,10 +11,14 @@ waits on each panel's flags.  Inputs are resident in HBM before timing.
 Prints one JSON line.  `value` is TFLOP/s of the overlapped step (2 M N K per
 step).  Alongside: the same consumer with the data pre-resident and flags
 preset (the GEMM alone), the serial producer-then-consumer run, the overlap
-efficiency E = T(GEMM alone) / T(overlapped), the consumer kernel's roofline
-(timed with HIP events recorded on its own stream around its launch), the
-GEMM+ReduceScatter workload (M = 8192, K = 3200, N = 5120, 7 resident fp32
-peer partials), and the CPU oracle timed on a bounded sample of rows.
+efficiency E = T(GEMM alone) / T(overlapped) from interleaved pairs and its
+ceiling E_max, median and p10/p90 of the per-call times, an arrival sweep
+(unthrottled, 153.6 and 50 GB/s per peer), MALL-flushed timings, the consumer
+kernel's roofline (timed with HIP events recorded on its own stream around its
+launch), the GEMM+ReduceScatter workload (M = 8192, K = 3200, N = 5120, 7
+fp32 peer partials, resident and paced at 50 GB/s) with its reduction window,
+the MoE AllGather + grouped GEMM workload, measured copy and hipBLASLt
+ceilings, and the CPU oracle timed on a bounded sample of rows.
 """
 from __future__ import annotations
 
@@ -106,6 +110,90 @@ def timed(fn, steps, warmup, torch, ctx):
     return step_ms, statistics.mean(kern), kern
 
 
+def spread(vals):
+    """Median and 10th / 90th percentiles of a list of times."""
+    v = sorted(vals)
+    q = statistics.quantiles(v, n=10, method="inclusive") if len(v) > 1 else [v[0]] * 9
+    return {"median": statistics.median(v), "p10": q[0], "p90": q[8], "n": len(v)}
+
+
+def pairs(fn_a, fn_b, n, torch, ctx):
+    """Interleave n calls of fn_a and fn_b (each given its consumer events); per-call kernel times of each.
+
+    Pairs taken back to back see the same clock and thermal state, so their ratio is not biased by drift
+    between two blocks of runs."""
+    ev = _events(2 * n, torch)
+    torch.cuda.synchronize()
+    for i in range(n):
+        fn_a(i, ev[2 * i])
+        fn_b(i, ev[2 * i + 1])
+    torch.cuda.synchronize()
+    ctx.sync()
+    return [a.elapsed_time(b) for a, b in ev[0::2]], [a.elapsed_time(b) for a, b in ev[1::2]]
+
+
+def flushed(fn, n, torch, ctx, scrub):
+    """Per call: overwrite a 512 MiB buffer (evicts the 256 MB MALL and the L2s), then time the whole call
+    (producer fork to join) with events on the calling stream; returns the per-call times."""
+    out = []
+    for i in range(n):
+        scrub.fill_(i & 0x7F)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(i, None)
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b))
+    ctx.sync()
+    return out
+
+
+def device_clocks():
+    """Engine and memory clocks as rocm-smi reports them right now (None if it is unavailable)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+    except Exception:  # noqa: BLE001 - a missing tool only drops this field
+        return None
+    lines = [ln.strip() for ln in r.stdout.splitlines() if "clock level" in ln.lower()]
+    return lines or None
+
+
+def microbench(torch, A, B_kn, steps):
+    """Measured ceilings on this device: a 1 GiB device copy and hipBLASLt's bf16 GEMM (torch.matmul) at the
+    headline shape, both timed with events; context for the hand-written kernels, not part of the method."""
+    n = 1 << 28
+    x = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    x.fill_(1.0)
+    for _ in range(2):
+        y.copy_(x)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        y.copy_(x)
+    b.record()
+    torch.cuda.synchronize()
+    copy_ms = a.elapsed_time(b) / steps
+    del x, y
+    M, K = A.shape
+    N = B_kn.shape[1]
+    for _ in range(2):
+        C = torch.matmul(A, B_kn)
+    a.record()
+    for _ in range(steps):
+        C = torch.matmul(A, B_kn)
+    b.record()
+    torch.cuda.synchronize()
+    mm_ms = a.elapsed_time(b) / steps
+    del C
+    return {"copy_1gib_gbs": 2 * 4 * n / (copy_ms * 1e-3) / 1e9,
+            "copy_note": "read + write bytes of a 1 GiB fp32 device copy / time",
+            "hipblaslt_bf16_gemm_tflops": 2.0 * M * N * K / (mm_ms * 1e-3) / 1e12,
+            "hipblaslt_note": "torch.matmul of the resident gathered A (bf16) by a row-major K x N bf16 B, bf16 "
+                              "output, same M, K, N"}
+
+
 def cpu_baseline(shards, B, M, N, K, seconds: float, b_layout: str = "kn"):
     """The oracle (concat + fp64 loops over output rows), timed on a bounded sample of rows."""
     import numpy as np
@@ -161,15 +249,9 @@ def bench_moe(ctx, up, args, torch, sgt, I, lay):
                             max(3, args.steps // 4), 2, torch, ctx)
     # the overlapped call's consumer runs on the whole chip (its last workgroups take the producer's CUs as
     # the producer finishes), so the GEMM alone is timed on the whole chip too
-    pair_ev = _events(2 * args.steps, torch)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        call("cu", arrival_seed=2000 + i, **link)(i, pair_ev[2 * i])
-        call("preset")(i, pair_ev[2 * i + 1])
-    torch.cuda.synchronize()
-    ctx.sync()
-    ov_k = statistics.median(a.elapsed_time(b) for a, b in pair_ev[0::2])
-    al_k = statistics.median(a.elapsed_time(b) for a, b in pair_ev[1::2])
+    ov_l, al_l = pairs(lambda i, ev: call("cu", arrival_seed=2000 + i, **link)(i, ev), call("preset"), args.steps,
+                       torch, ctx)
+    ov_k, al_k = statistics.median(ov_l), statistics.median(al_l)
     # spot checks (parity itself is the tests' job): gathered bits, and group offsets that cover T * topk rows
     assert torch.equal(Xg.view(torch.int16), torch.cat(sh).view(torch.int16)), "MoE gathered buffer mismatch"
     off_h = off.cpu().numpy()
@@ -194,6 +276,7 @@ def bench_moe(ctx, up, args, torch, sgt, I, lay):
                                    "chip, as the overlapped consumer) over that of the overlapped call, interleaved "
                                    "pairs; routing excluded",
         "step_overlap_efficiency": alone_ms / over_ms,
+        "pairs_kernel_ms": spread(ov_l), "pairs_preset_kernel_ms": spread(al_l),
         "link_floor_us": (m.T // m.W) * m.H * 2 / (m.peer_gbps * 1e9) * 1e6,
     }
     del sh, We, lg, Xg, Y
@@ -203,7 +286,7 @@ def bench_moe(ctx, up, args, torch, sgt, I, lay):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -274,8 +357,8 @@ def main():
                           "tflops": flops / (kern_ms * 1e-3) / 1e12}), flush=True)
         ctx.close()
         return
-    over_ms, over_kern_ms, _ = timed(lambda i, ev: ag("cu", arrival_seed=i + 1, **link)(i, ev), args.steps,
-                                     args.warmup, torch, ctx)
+    over_ms, over_kern_ms, over_list = timed(lambda i, ev: ag("cu", arrival_seed=i + 1, **link)(i, ev),
+                                             args.steps, args.warmup, torch, ctx)
     if args.headline_only:
         print(json.dumps({"workload": w.name, "overlapped_ms": over_ms, "consumer_kernel_ms": over_kern_ms,
                           "tflops": flops / (over_ms * 1e-3) / 1e12}), flush=True)
@@ -289,17 +372,10 @@ def main():
     alone_part = timed(ag("preset", consumer_cus=n_cu - prod_wgs), args.steps, args.warmup, torch, ctx)
     best = min((alone_all, n_cu), (alone_part, n_cu - prod_wgs), key=lambda x: x[0][0])
     (alone_ms, alone_kern_ms, _), alone_grid = best
-    # Overlap efficiency from interleaved pairs (overlapped call, then the same consumer alone on the same
-    # grid), so clock and thermal drift between two blocks of runs cannot bias the ratio.
-    pair_ev = _events(2 * args.steps, torch)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        ag("cu", arrival_seed=1000 + i, **link)(i, pair_ev[2 * i])
-        ag("preset", consumer_cus=alone_grid)(i, pair_ev[2 * i + 1])
-    torch.cuda.synchronize()
-    ctx.sync()
-    ov_k = statistics.median(a.elapsed_time(b) for a, b in pair_ev[0::2])
-    al_k = statistics.median(a.elapsed_time(b) for a, b in pair_ev[1::2])
+    # Overlap efficiency from interleaved pairs: overlapped call, then the same consumer alone on the same grid.
+    ov_list, al_list = pairs(lambda i, ev: ag("cu", arrival_seed=1000 + i, **link)(i, ev),
+                             ag("preset", consumer_cus=alone_grid), args.steps, torch, ctx)
+    ov_k, al_k = statistics.median(ov_list), statistics.median(al_list)
     serial_ms, _, _ = timed(lambda i, ev: ag("serial", arrival_seed=i + 1, **link)(i, ev), max(3, args.steps // 4),
                             2, torch, ctx)
     unthr_ms, _, _ = timed(ag("cu"), max(3, args.steps // 4), 2, torch, ctx)
@@ -310,8 +386,43 @@ def main():
     link_floor_us = shard_bytes / (w.peer_gbps * 1e9) * 1e6
     tflops = flops / (over_ms * 1e-3) / 1e12
     kern_tflops = flops / (over_kern_ms * 1e-3) / 1e12
+    n_tiles = (M // 256) * (-(-N // 256))
+
+    def e_max(floor_us):
+        # ceiling on E: the last panel cannot start before the link delivers it, and then takes one tile time
+        # (its tiles run side by side); one tile time = T_alone * grid / tiles
+        t_alone = al_k * 1e3
+        t_tile = t_alone * alone_grid / n_tiles
+        return t_alone / max(t_alone, floor_us + t_tile)
+
+    # the arrival sweep: unthrottled, the xGMI link rate and 50 GB/s, jitter up to one signal tile's link time
+    sweep = []
+    sweep_n = max(4, args.steps // 2)
+    for gbps in (0.0, 153.6, 50.0):
+        jit = (256 * K * 2) / (gbps * 1e9) * 1e6 if gbps else 0.0
+        kw = dict(peer_gbps=gbps, jitter_us=jit)
+        o_l, a_l = pairs(lambda i, ev: ag("cu", arrival_seed=3000 + i, **kw)(i, ev),
+                         ag("preset", consumer_cus=alone_grid), sweep_n, torch, ctx)
+        floor = shard_bytes / (gbps * 1e9) * 1e6 + jit if gbps else 0.0
+        sweep.append({"peer_gbps": gbps or None, "jitter_us": jit, "link_floor_us": floor,
+                      "overlapped_kernel_ms": spread(o_l), "alone_kernel_ms": spread(a_l),
+                      "tflops_median": flops / (statistics.median(o_l) * 1e-3) / 1e12,
+                      "overlap_efficiency": statistics.median(a_l) / statistics.median(o_l),
+                      "overlap_efficiency_max": e_max(floor)})
+    # MALL-flushed (a 512 MiB scrub buffer written before each call) against warm back-to-back calls
+    scrub = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+    fl_n = max(4, args.steps // 2)
+    cold = flushed(lambda i, ev: ag("cu", arrival_seed=4000 + i, **link)(i, ev), fl_n, torch, ctx, scrub)
+    cold_alone = flushed(ag("preset", consumer_cus=alone_grid), fl_n, torch, ctx, scrub)
+    del scrub
+    clocks = device_clocks()
+    B_kn = B.t().contiguous() if lay == "nk" else B
+    micro = microbench(torch, Ag, B_kn, max(3, args.steps // 4))
+    del B_kn
+
     detail = {
         "overlapped_ms": over_ms,
+        "overlapped_kernel_ms": spread(over_list),
         "gemm_alone_ms": alone_ms,
         "gemm_alone_tflops": flops / (alone_ms * 1e-3) / 1e12,
         "gemm_alone_kernel_ms": alone_kern_ms,
@@ -320,18 +431,31 @@ def main():
         "gemm_alone_all_cus_ms": alone_all[0],
         "gemm_alone_consumer_grid_ms": alone_part[0],
         "serial_ms": serial_ms,
+        "producer_only_ms_est": serial_ms - alone_all[0],
+        "producer_only_note": "serial call (paced producer, then the consumer on all CUs) minus the GEMM alone on "
+                              "all CUs",
         "unthrottled_producer_ms": unthr_ms,
         "overlap_efficiency": al_k / ov_k,
+        "overlap_efficiency_max": e_max(link_floor_us + w.jitter_us),
         "overlap_efficiency_note": "median consumer-kernel time of the GEMM alone over that of the overlapped call, "
-                                   "%d interleaved pairs" % args.steps,
+                                   "%d interleaved pairs; the maximum assumes the last panel arrives at the link "
+                                   "floor plus the jitter bound and then takes one tile time" % args.steps,
         "overlap_efficiency_blocks": alone_ms / over_ms,
-        "pairs_overlapped_kernel_ms": ov_k,
-        "pairs_alone_kernel_ms": al_k,
+        "pairs_overlapped_kernel_ms": spread(ov_list),
+        "pairs_alone_kernel_ms": spread(al_list),
         "speedup_vs_serial": serial_ms / over_ms,
         "link_floor_us": link_floor_us,
         "peer_gbps": w.peer_gbps,
         "jitter_us": w.jitter_us,
         "pct_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "arrival_sweep": sweep,
+        "mall_flushed_call_ms": spread(cold),
+        "mall_flushed_alone_call_ms": spread(cold_alone),
+        "mall_flushed_tflops_median": flops / (statistics.median(cold) * 1e-3) / 1e12,
+        "mall_flushed_overlap_efficiency": statistics.median(cold_alone) / statistics.median(cold),
+        "mall_flushed_note": "whole call (producer fork to join) timed alone after writing a 512 MiB buffer",
+        "rocm_smi_clocks": clocks,
+        "microbench": micro,
     }
 
     if not args.no_rs:
@@ -357,17 +481,28 @@ def main():
                                                      producer="preset", consumer_events=ev), args.steps,
                            args.warmup, torch, ctx)
         # interleaved pairs: GEMM+RS call, then the same GEMM alone
-        rs_ev = _events(2 * args.steps, torch)
-        torch.cuda.synchronize()
-        for i in range(args.steps):
-            ctx.gemm_rs(A, Brs, parts, P, Cs, gf, pf, rank=rank, b_layout=lay, consumer_events=rs_ev[2 * i])
-            ctx.ag_gemm(A_parts, Brs, A, Cg, fl2, rank=rank, b_layout=lay, producer="preset",
-                        consumer_events=rs_ev[2 * i + 1])
-        torch.cuda.synchronize()
-        ctx.sync()
-        rs_pair = statistics.median(a.elapsed_time(b) for a, b in rs_ev[0::2])
-        g_pair = statistics.median(a.elapsed_time(b) for a, b in rs_ev[1::2])
+        rs_l, g_l = pairs(lambda i, ev: ctx.gemm_rs(A, Brs, parts, P, Cs, gf, pf, rank=rank, b_layout=lay,
+                                                    consumer_events=ev),
+                          lambda i, ev: ctx.ag_gemm(A_parts, Brs, A, Cg, fl2, rank=rank, b_layout=lay,
+                                                    producer="preset", consumer_events=ev), args.steps, torch, ctx)
+        rs_pair, g_pair = statistics.median(rs_l), statistics.median(g_l)
         red_bytes = (r.M // r.W) * r.N * 4 * (r.W + 1)   # read local block + W-1 peers, write C_shard
+        # reduction window from the kernel's own stamps (100 MHz clock): first reduction start to last end
+        nw = sgt.trace_words(r.W, r.M, r.K, r.N)
+        tr = torch.zeros(nw, dtype=torch.int64, device=dev)
+        ctx.gemm_rs(A, Brs, parts, P, Cs, gf, pf, rank=rank, b_layout=lay, trace=tr.data_ptr(), blocking=True)
+        t = tr.cpu().numpy().view(np.uint64).reshape(-1, 3)
+        n_g = (r.W * (-(-(r.M // r.W) // 256))) * (-(-r.N // 256))
+        red_t, gem_t = t[n_g:].astype(np.int64), t[:n_g].astype(np.int64)
+        red_win_us = (red_t[:, 1].max() - red_t[:, 0].min()) / 100.0
+        red_item_us = (red_t[:, 1] - red_t[:, 0]) / 100.0
+        # paced peers at 50 GB/s per link (the comm-bound variant): peers' blocks copied into an inbox
+        gbps_rs = 50.0
+        inbox = [torch.empty_like(p) if p is not None else None for p in parts]
+        pc_ms, pc_k, pc_l = timed(lambda i, ev: ctx.gemm_rs_paced(A, Brs, parts, inbox, P, Cs, gf, pf, rank=rank,
+                                                                  b_layout=lay, peer_gbps=gbps_rs,
+                                                                  consumer_events=ev),
+                                  max(4, args.steps // 2), 2, torch, ctx)
         detail["gemm_rs"] = {
             "workload": r.name, "M": r.M, "K": r.K, "N": r.N, "W": r.W,
             "step_ms": rs_ms, "kernel_ms": rs_kern_ms,
@@ -377,8 +512,21 @@ def main():
             "overlap_efficiency": g_pair / rs_pair,
             "overlap_efficiency_note": "median kernel time of the GEMM alone over that of GEMM+RS, interleaved pairs",
             "overlap_efficiency_blocks": g_ms / rs_ms,
+            "pairs_kernel_ms": spread(rs_l), "pairs_gemm_alone_kernel_ms": spread(g_l),
             "reduction_algorithmic_bytes": red_bytes,
+            "reduction_window_us": float(red_win_us),
+            "reduction_window_gbs": red_bytes / (red_win_us * 1e-6) / 1e9,
+            "reduction_tile_us": spread(red_item_us.tolist()),
+            "reduction_note": "window = first reduction-tile start to last end in one traced call (the tiles run "
+                              "while other workgroups finish GEMM tiles, so the rate is a lower bound); tile time "
+                              "includes its flag wait",
+            "gemm_tiles_end_us": float((gem_t[:, 1].max() - gem_t[:, 0].min()) / 100.0),
+            "paced_50gbps": {"peer_gbps": gbps_rs, "step_ms": pc_ms, "kernel_ms": spread(pc_l),
+                             "tflops": r.flops / (pc_ms * 1e-3) / 1e12,
+                             "link_floor_us": (r.M // r.W) * r.N * 4 / (gbps_rs * 1e9) * 1e6},
         }
+        assert torch.equal(inbox[(rank + 1) % r.W], parts[(rank + 1) % r.W]), "paced inbox mismatch"
+        del inbox, tr
         del A, Brs, parts, P, Cs, Cg
 
     if not args.no_moe:
