@@ -13,10 +13,11 @@
 //
 // K loop: BK = 64, two LDS stages of 64 KiB, one barrier per K step.  Operands
 // whose k index is contiguous in memory (A, and B stored N x K) go straight
-// from HBM to LDS with buffer_load_dwordx4 ... lds (no register staging); B
-// stored K x N is loaded to registers in blocks of 8 n x (8 or 4) k,
-// transposed there and written to LDS, so LDS always holds [row][k].  The
-// next step's loads are in flight while the current step's MFMAs run.
+// from HBM to LDS with buffer_load_dwordx4 ... lds (no register staging),
+// issued between the MFMAs of the current step's first substep; B stored
+// K x N is loaded to registers in blocks of 8 n x (8 or 4) k, transposed
+// there and written to LDS, so LDS always holds [row][k].  The next step's
+// loads are in flight while the current step's MFMAs run.
 //
 // LDS layout of a stage, both operands: [256 rows][64 k] bf16 = 128 bytes per
 // row = 8 chunks of 16 bytes; chunk c of row r is stored at chunk
@@ -212,52 +213,102 @@ __device__ __forceinline__ void read_frags(const uint8_t* sA, const uint8_t* sB,
     b[j] = *reinterpret_cast<const bf16x8_t*>(sB + lds_swz(wn * 128 + j * 32 + lr, chunk));
 }
 
+// The DMA loads of one K step of the k-contiguous operands (A, then B when it
+// is stored N x K), issued one at a time from inside the MFMA stream: load j
+// is A's load j for j < kLA, else B's load j - kLA.
+template <int kW, int kR, bool kBNK>
+struct StepDma {
+  static constexpr int kLA = kR / kW / 8, kLB = kBNK ? kBM / kW / 8 : 0, kN = kLA + kLB;
+  const KRows* ka;
+  const KRows* kb;
+  uint8_t* sA;
+  uint8_t* sB;
+  uint32_t kbyte, lim;
+  __device__ __forceinline__ StepDma(const KRows& a, const KRows& b, uint8_t* stA, uint8_t* stB, int64_t k0,
+                                     int64_t K)
+      : ka(&a), kb(&b), sA(stA), sB(stB), kbyte((uint32_t)(k0 * 2)) {
+    const int64_t rem = (K - k0) * 2;  // valid bytes of this step's rows
+    lim = rem <= 0 ? 0u : (rem >= 128 ? 128u : (uint32_t)rem);
+  }
+  template <int L>
+  __device__ __forceinline__ void one(const KRows& kr, uint8_t* stage, int i) const {
+    const uint32_t c = kr.chunk[i & 3];
+    // kOOB + (k0 + c) stays >= 2^31, past every record range
+    const uint32_t off = c < lim ? kr.row_off[i] + kbyte + c : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr.rsrc, (lds_ptr_t)(stage + (wave_id() * L + i) * 1024), 16, off, 0,
+                                             0, 0);
+  }
+  __device__ __forceinline__ void issue(int j) const {
+    if (j < kLA) one<kLA>(*ka, sA, j);
+    else if constexpr (kLB > 0) one<kLB>(*kb, sB, j - kLA);
+  }
+};
+
+// Substeps over which a K step's DMA loads are spread.  Issued in one burst
+// by all waves right after the barrier, the loads (1 KiB each, 64 KiB per step
+// and CU) back each wave's in-order issue up behind the CU's load path while
+// the matrix cores idle; interleaved with the first substep's MFMAs they drain
+// under matrix-core work and still have three substeps of MFMA time to land
+// before the end-of-step wait.  Spreading them further (2 or 4 substeps)
+// measured slower: the last loads then land after the wait begins.
+constexpr int kDmaSubsteps = 1;
+
 // The MFMAs of one wave on one LDS stage, software-pipelined over the four
 // k-substeps: the fragment reads of substep kk + 1 are interleaved with the
-// first MFMAs of substep kk (1 MFMA, 1 LDS read), so LDS latency and transfer
-// hide under matrix-core work and only the first substep's reads are
-// exposed.  The scheduling barriers keep the compiler from undoing that order
-// and from hoisting the caller's DMA wait and barrier above the MFMAs (they
-// touch no memory, so it otherwise would).
-template <int kW, int kR, int KK>
+// MFMAs of substep kk (1 MFMA, 1 LDS read), so LDS latency and transfer hide
+// under matrix-core work and only the first substep's reads are exposed; the
+// next K step's DMA loads are interleaved with the MFMAs of the first
+// kDmaSubsteps substeps.  The scheduling barriers keep the compiler from
+// undoing that order and from hoisting the caller's DMA wait and barrier above
+// the MFMAs (they touch no memory, so it otherwise would).
+template <int kW, int kR, int KK, class Dma>
 __device__ __forceinline__ void mfma_substep(const uint8_t* sA, const uint8_t* sB,
                                              bf16x8_t (&a)[2][Tile<kW, kR>::kMI], bf16x8_t (&b)[2][4],
-                                             MfmaAcc<kW, kR>& acc) {
+                                             MfmaAcc<kW, kR>& acc, const Dma& dma) {
   constexpr int MI = Tile<kW, kR>::kMI;
+  constexpr int NM = 4 * MI;                                    // MFMAs
   constexpr int cur = KK & 1;
+  constexpr int R = KK < 3 ? MI + 4 : 0;                        // reads of the next substep
+  constexpr int J0 = KK < kDmaSubsteps ? KK * Dma::kN / kDmaSubsteps : 0;
+  constexpr int J1 = KK < kDmaSubsteps ? (KK + 1) * Dma::kN / kDmaSubsteps : 0;
+  constexpr int V = J1 - J0;                                    // DMA loads
   if constexpr (KK < 3) read_frags<kW, kR>(sA, sB, KK + 1, a[cur ^ 1], b[cur ^ 1]);
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j], acc.v[i][j], 0, 0, 0);
-  if constexpr (KK < 3) {
-    constexpr int R = MI + 4;                // reads of the next substep
-    constexpr int P = R < 4 * MI ? R : 4 * MI;  // (MFMA, read) pairs
 #pragma unroll
-    for (int g = 0; g < P; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, KK);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, KK);  // 1 LDS read
-    }
-    if constexpr (4 * MI > P) __builtin_amdgcn_sched_group_barrier(0x008, 4 * MI - P, KK);
-    if constexpr (R > P) __builtin_amdgcn_sched_group_barrier(0x100, R - P, KK);
+  for (int j = J0; j < J1; ++j) dma.issue(j);
+  // order: after MFMA m comes one read (while reads remain) and the DMA
+  // loads whose even share of the NM slots ends there (V may exceed NM)
+  static_assert(NM >= 4 && V >= 0 && R >= 0, "substep shape");
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, KK);        // 1 MFMA
+    if (m < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, KK);  // 1 LDS read
+    const int nv = (m + 1) * V / NM - m * V / NM;
+#pragma unroll
+    for (int q = 0; q < nv; ++q) __builtin_amdgcn_sched_group_barrier(0x060, 1, KK);  // 1 DMA load
   }
-  // one scheduling region per substep: its MFMAs and the next substep's reads
+  if constexpr (R > NM) __builtin_amdgcn_sched_group_barrier(0x100, R - NM, KK);
+  // one scheduling region per substep
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int kW, int kR>
-__device__ __forceinline__ void mfma_stage(const uint8_t* sA, const uint8_t* sB, MfmaAcc<kW, kR>& acc) {
+template <int kW, int kR, class Dma>
+__device__ __forceinline__ void mfma_stage(const uint8_t* sA, const uint8_t* sB, MfmaAcc<kW, kR>& acc,
+                                           const Dma& dma) {
   bf16x8_t a[2][Tile<kW, kR>::kMI], b[2][4];
   read_frags<kW, kR>(sA, sB, 0, a[0], b[0]);
   __builtin_amdgcn_sched_barrier(0);
   // A wave in its MFMA phase takes issue priority over the other wave of its
   // SIMD (which is then typically issuing loads or waiting at the barrier).
   __builtin_amdgcn_s_setprio(1);
-  mfma_substep<kW, kR, 0>(sA, sB, a, b, acc);
-  mfma_substep<kW, kR, 1>(sA, sB, a, b, acc);
-  mfma_substep<kW, kR, 2>(sA, sB, a, b, acc);
-  mfma_substep<kW, kR, 3>(sA, sB, a, b, acc);
+  mfma_substep<kW, kR, 0>(sA, sB, a, b, acc, dma);
+  mfma_substep<kW, kR, 1>(sA, sB, a, b, acc, dma);
+  mfma_substep<kW, kR, 2>(sA, sB, a, b, acc, dma);
+  mfma_substep<kW, kR, 3>(sA, sB, a, b, acc, dma);
   __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -292,18 +343,14 @@ __device__ __forceinline__ void gemm_tile(const KRows& ka, const KRows& kb_nk, c
   __syncthreads();
   for (int64_t kt = 0; kt < nk2; kt += 2) {
     // stage 0 computes while stage 1 fills
-    dma_stage<kW, kR>(ka, sA1, (kt + 1) * kBK, K);
-    if constexpr (kBNK) dma_stage<kW>(kb_nk, sB1, (kt + 1) * kBK, K);
-    else kn.load((kt + 1) * kBK);
-    mfma_stage<kW, kR>(sA0, sB0, acc);
+    if constexpr (!kBNK) kn.load((kt + 1) * kBK);
+    mfma_stage<kW, kR>(sA0, sB0, acc, StepDma<kW, kR, kBNK>(ka, kb_nk, sA1, sB1, (kt + 1) * kBK, K));
     if constexpr (!kBNK) kn.store(sB1);
     wait_dma();
     __syncthreads();
     // stage 1 computes while stage 0 fills (past the end: zeros, unused)
-    dma_stage<kW, kR>(ka, sA0, (kt + 2) * kBK, K);
-    if constexpr (kBNK) dma_stage<kW>(kb_nk, sB0, (kt + 2) * kBK, K);
-    else kn.load((kt + 2) * kBK);
-    mfma_stage<kW, kR>(sA1, sB1, acc);
+    if constexpr (!kBNK) kn.load((kt + 2) * kBK);
+    mfma_stage<kW, kR>(sA1, sB1, acc, StepDma<kW, kR, kBNK>(ka, kb_nk, sA0, sB0, (kt + 2) * kBK, K));
     if constexpr (!kBNK) kn.store(sB0);
     wait_dma();
     __syncthreads();

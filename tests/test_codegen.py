@@ -1,0 +1,81 @@
+"""Checks on the built gfx950 code object (CPU only; reads the AMD assembly of this library's own build).
+
+A tile kernel whose matrix-core loop the compiler has dropped (for instance
+after undefined behaviour in a compile-time schedule) still links and runs,
+but computes nothing; counting the MFMAs of each tile kernel catches that
+without a GPU.  The same pass checks that no kernel writes through the scalar
+data cache.
+"""
+from __future__ import annotations
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+import signal_gated_tiled_amd as sgt
+
+OBJDUMP = shutil.which("llvm-objdump") or "/opt/rocm/llvm/bin/llvm-objdump"
+
+
+@pytest.fixture(scope="module")
+def kernels(tmp_path_factory):
+    if not os.path.exists(sgt.LIB_PATH):
+        pytest.skip("libsgt.so is not built")
+    if not os.path.exists(OBJDUMP):
+        pytest.skip("llvm-objdump not found")
+    d = tmp_path_factory.mktemp("codeobj")
+    lib = str(d / "libsgt.so")
+    shutil.copy(sgt.LIB_PATH, lib)
+    subprocess.run([OBJDUMP, "--offloading", lib], cwd=str(d), check=True, capture_output=True)
+    objs = [str(d / f) for f in os.listdir(d) if f.endswith("gfx950")]
+    assert objs, "no gfx950 code object in libsgt.so"
+    funcs = {}
+    for o in objs:
+        txt = subprocess.run([OBJDUMP, "-d", "--no-show-raw-insn", o], check=True, capture_output=True,
+                             text=True).stdout
+        name = None
+        for line in txt.splitlines():
+            m = re.match(r"^[0-9a-f]+ <(.+)>:$", line)
+            if m:
+                name = m.group(1)
+                funcs.setdefault(name, [])
+            elif name is not None and line.strip():
+                funcs[name].append(line.strip())
+    return funcs
+
+
+def _tile_shape(name):
+    """(waves, rows) of a tile kernel from its mangled template arguments, or None."""
+    m = re.search(r"(ag_consumer_bf16|gemm_rs_kernel)ILi(\d)E", name)
+    if m:
+        return int(m.group(2)), 256
+    m = re.search(r"moe_consumer_bf16ILi(\d)ELi(\d+)E", name)
+    if m:
+        return int(m.group(1)), int(m.group(2))
+    return None
+
+
+def test_every_tile_kernel_keeps_its_mfma_loop(kernels):
+    seen = 0
+    for name, body in kernels.items():
+        shape = _tile_shape(name)
+        if shape is None:
+            continue
+        kw, kr = shape
+        mi = kr // (kw // 2) // 32
+        n = sum(1 for ln in body if ln.startswith("v_mfma_f32_32x32x16_bf16"))
+        # the K loop is unrolled over the two LDS stages: 2 x 4 substeps x (MI x 4) MFMAs
+        assert n == 2 * 4 * mi * 4, "%s: %d MFMAs, expected %d" % (name, n, 32 * mi)
+        seen += 1
+    # 8 AllGather, 16 MoE and 4 GEMM+RS instantiations
+    assert seen == 28, seen
+
+
+def test_no_scalar_cache_writes(kernels):
+    bad = re.compile(r"^s_(store|buffer_store|scratch_store|atomic|buffer_atomic|dcache_wb|dcache_discard)")
+    for name, body in kernels.items():
+        hits = [ln for ln in body if bad.match(ln)]
+        assert not hits, "%s: %s" % (name, hits[:3])
