@@ -255,17 +255,26 @@ int build_schedule(const AgPlan& p, int W, int rank, int64_t K, int esz, const s
       const double rel = (double)(g + 1) * per + jitter_ticks(o, s);
       items[n++] = sched_item(all[g], (int)(all[g] / tps), rel);
     }
-  } else {
-    std::vector<int64_t> order((size_t)tps);
+  } else if (W > 1) {
+    // each link delivers its tiles in order (or a seeded order per link), all
+    // links concurrently; items with equal release times (unthrottled links)
+    // keep the order the consumer takes panels in: round-robin over the peers
+    // for the mesh order, peer by peer for the shard order
+    std::vector<std::vector<int64_t>> order((size_t)W - 1, std::vector<int64_t>((size_t)tps));
     for (int d = 1; d < W; ++d) {
-      const int peer = (rank + d) % W;
-      for (int64_t t = 0; t < tps; ++t) order[(size_t)t] = t;
-      if (o.arrival_order == 1) shuffle(order, s);
-      for (int64_t k = 0; k < tps; ++k) {
-        const double rel = (double)(k + 1) * ticks_per_tile + jitter_ticks(o, s);
-        items[n++] = sched_item(peer * tps + order[(size_t)k], peer, rel);
-      }
+      std::vector<int64_t>& od = order[(size_t)d - 1];
+      for (int64_t t = 0; t < tps; ++t) od[(size_t)t] = t;
+      if (o.arrival_order == 1) shuffle(od, s);
     }
+    const bool mesh = o.order == SGT_ORDER_MESH;
+    for (int64_t outer = 0; outer < (mesh ? tps : (int64_t)W - 1); ++outer)
+      for (int64_t inner = 0; inner < (mesh ? (int64_t)W - 1 : tps); ++inner) {
+        const int d = 1 + (int)(mesh ? inner : outer);
+        const int64_t k = mesh ? outer : inner;
+        const int peer = (rank + d) % W;
+        const double rel = (double)(k + 1) * ticks_per_tile + jitter_ticks(o, s);
+        items[n++] = sched_item(peer * tps + order[(size_t)d - 1][(size_t)k], peer, rel);
+      }
   }
   std::stable_sort(items + first_remote, items + n,
                    [](const ProdItem& a, const ProdItem& b) { return a.release < b.release; });
