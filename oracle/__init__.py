@@ -17,6 +17,11 @@ Functions and the passage each follows (page titles as on the pages):
 * ``moe_route`` / ``moe_ag_gemm`` -- paper summary, "Experiments" (MoE routing
                         operations) and the DITRON article, "three-level tiling"
                         (dynamic per-expert sizes): top-k routing, expert-grouped rows.
+* ``moe_gemm_rs``    -- paper summary, "Experiments" (MoE ReduceScatter) and the semantics
+                        page, "GEMM + ReduceScatter overlap": the combine side of an MoE
+                        layer -- grouped rows times their expert's weight, each token's
+                        rows summed with its gate weights, then the ReduceScatter over
+                        token blocks.
 * ``ag_gemm_protocol`` -- semantics page, "Producer-consumer model", "Signal-based
                         synchronization", "Threadblock swizzle", "Token-based data
                         dependency"; paper summary, "Method" (AMD full-mesh swizzle):
@@ -65,6 +70,9 @@ def _load():
         lib.orc_moe_route.argtypes = [P, I64, I32, I32, P, P, P]
         lib.orc_moe_route.restype = I32
         lib.orc_moe_gemm_rows.argtypes = [P, P, I32, I64, I64, I32, P, P, P, I64, P, I32]
+        lib.orc_moe_gemm_rs.argtypes = [P, P, I32, I64, I32, I64, I64, I32, P, P, P, P, P, I32, I32, P, I64, P, P,
+                                        I32]
+        lib.orc_moe_gemm_rs.restype = I32
         lib.orc_ag_gemm_protocol.argtypes = [P, I32, I32, I32, P, I32, I32, I64, I64, I64, I64, I64,
                                              ctypes.c_uint64, D, I32, I32, I32, I32, P, P]
         lib.orc_ag_gemm_protocol.restype = I32
@@ -186,6 +194,62 @@ def moe_ag_gemm(shards, W_experts, logits, topk: int, w_layout: str = "kn", rows
     X_full = allgather(shards)
     ids, off, rt = moe_route(logits, topk)
     return X_full, ids, off, rt, moe_gemm(X_full, W_experts, off, rt, w_layout, rows, threads)
+
+
+def moe_gemm_rs(Hg, W2, gate, topk_ids, expert_off, row_token, partials, rank: int, w_layout: str = "kn",
+                tokens=None, want_p: bool = False, threads: int = 0):
+    """C for `rank` (its T/W tokens x H, float64), and P (tokens x H) when want_p.
+
+    Hg: grouped rows (rows x I bf16), W2: E x I x H ("kn") or E x H x I ("nk") bf16, gate: T x k float32,
+    topk_ids: T x k, expert_off: E+1, row_token: rows; partials: W arrays of (T/W) x H float32 ([rank] unused).
+    tokens: token indices to compute (default: the rank's block).
+    """
+    Hg = np.ascontiguousarray(Hg, dtype=np.uint16)
+    W2 = np.ascontiguousarray(W2, dtype=np.uint16)
+    gate = np.ascontiguousarray(gate, dtype=np.float32)
+    ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
+    off = np.ascontiguousarray(expert_off, dtype=np.int32)
+    rt = np.ascontiguousarray(row_token, dtype=np.int32)
+    T, k = ids.shape
+    E = W2.shape[0]
+    I = Hg.shape[1]
+    H = W2.shape[2] if w_layout == "kn" else W2.shape[1]
+    W = len(partials)
+    assert T % W == 0
+    parts = [np.ascontiguousarray(p, dtype=np.float32) if p is not None else np.zeros((T // W, H), np.float32)
+             for p in partials]
+    if tokens is None:
+        tokens = np.arange(rank * (T // W), (rank + 1) * (T // W), dtype=np.int64)
+    tk = np.ascontiguousarray(tokens, dtype=np.int64)
+    C = np.empty((len(tk), H), np.float64)
+    P = np.empty((len(tk), H), np.float64) if want_p else None
+    rc = _load().orc_moe_gemm_rs(_ptr(Hg), _ptr(W2), _lay(w_layout), T, k, I, H, E, _ptr(ids), _ptr(gate), _ptr(off),
+                                 _ptr(rt), _ptr_array(parts), W, rank, _ptr(tk), len(tk),
+                                 _ptr(P) if want_p else None, _ptr(C), threads)
+    if rc != 0:
+        raise ValueError("moe_gemm_rs: bad routing tables or tokens (%d)" % rc)
+    return (C, P) if want_p else C
+
+
+def moe_gemm_rs_p(Hg, W2, gate, topk_ids, expert_off, row_token, tokens, w_layout: str = "kn", threads: int = 0):
+    """P rows (the combined partial, float64) for any tokens, without the ReduceScatter."""
+    Hg = np.ascontiguousarray(Hg, dtype=np.uint16)
+    W2 = np.ascontiguousarray(W2, dtype=np.uint16)
+    gate = np.ascontiguousarray(gate, dtype=np.float32)
+    ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
+    off = np.ascontiguousarray(expert_off, dtype=np.int32)
+    rt = np.ascontiguousarray(row_token, dtype=np.int32)
+    T, k = ids.shape
+    E = W2.shape[0]
+    I = Hg.shape[1]
+    H = W2.shape[2] if w_layout == "kn" else W2.shape[1]
+    tk = np.ascontiguousarray(tokens, dtype=np.int64)
+    P = np.empty((len(tk), H), np.float64)
+    rc = _load().orc_moe_gemm_rs(_ptr(Hg), _ptr(W2), _lay(w_layout), T, k, I, H, E, _ptr(ids), _ptr(gate), _ptr(off),
+                                 _ptr(rt), None, 1, 0, _ptr(tk), len(tk), _ptr(P), None, threads)
+    if rc != 0:
+        raise ValueError("moe_gemm_rs: bad routing tables (%d)" % rc)
+    return P
 
 
 def panel_order(W: int, rank: int, rows_per_shard: int, panel_rows: int, order: str = "shard") -> np.ndarray:

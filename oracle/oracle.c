@@ -14,6 +14,9 @@
  *                    other ranks' partial blocks: C_shard = P[r] + sum_p partial[p].
  *   MoE AG-GEMM      each gathered token is routed to its top-k experts and
  *                    multiplied by each expert's weight.
+ *   MoE GEMM+RS      each grouped row times its expert's weight, the rows of a
+ *                    token summed with its gate weights, then the ReduceScatter
+ *                    of GEMM+RS over token blocks.
  *
  * Both results have a plain definition, so the oracle is that definition,
  * written out: loops in double precision, each output element summed in
@@ -199,6 +202,67 @@ void orc_moe_gemm_rows(const uint16_t* X_full, const uint16_t* W_experts, int w_
     gemm_row(x, ORC_BF16, w, ORC_BF16, w_layout, H, I, Y + (size_t)r * I);
   }
   (void)nthreads;
+}
+
+/*
+ * MoE GEMM + ReduceScatter, the combine side of an MoE layer (paper summary,
+ * "Experiments": MoE ReduceScatter; semantics page, "GEMM + ReduceScatter
+ * overlap"), as its plain definition.  Grouped rows Hg (rows x I bf16, in the
+ * expert-grouped order of the routing tables) times the owning expert's W2
+ * (E x I x H "kn" or E x H x I "nk" bf16), combined per token with its gate
+ * weights in pick order:
+ *   P[t][n] = sum_j gate[t][j] * sum_i Hg[row(t, j)][i] * W2[e(t, j)][i][n]
+ * with e(t, j) = topk_ids[t][j] and row(t, j) the row of group e(t, j) that
+ * holds token t; rank r's block then adds the other ranks' partial blocks:
+ *   C[t - r T/W][n] = P[t][n] + sum_{p != r} partial_p[t - r T/W][n].
+ * tokens: the tokens to compute (NULL: all T).  P_out: ntok x H (may be NULL);
+ * C_out: ntok x H for tokens of block `rank` (may be NULL; -3 if a token is
+ * outside the block).  Returns -2 when a pick has no row in its group.
+ */
+int orc_moe_gemm_rs(const uint16_t* Hg, const uint16_t* W2, int w_layout, int64_t T, int k, int64_t I, int64_t H,
+                    int E, const int32_t* topk_ids, const float* gate, const int32_t* expert_off,
+                    const int32_t* row_token, const float* const* partials, int W, int rank, const int64_t* tokens,
+                    int64_t ntok, double* P_out, double* C_out, int nthreads) {
+  if (tokens == NULL) ntok = T;
+  const int64_t blk = T / W, b0 = (int64_t)rank * blk;
+  int bad = 0;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : bad)
+#endif
+  for (int64_t i = 0; i < ntok; ++i) {
+    const int64_t t = tokens ? tokens[i] : i;
+    double* acc = (double*)calloc((size_t)H, sizeof(double));
+    double* y = (double*)malloc((size_t)H * sizeof(double));
+    for (int j = 0; j < k && !bad; ++j) {
+      const int e = topk_ids[t * k + j];
+      int64_t row = -1;
+      for (int64_t r = expert_off[e]; r < expert_off[e + 1]; ++r)
+        if (row_token[r] == t) { row = r; break; }
+      if (row < 0) { bad |= 2; break; }
+      gemm_row(Hg + (size_t)row * I, ORC_BF16, W2 + (size_t)e * I * H, ORC_BF16, w_layout, I, H, y);
+      const double g = (double)gate[t * k + j];
+      for (int64_t n = 0; n < H; ++n) acc[n] += g * y[n];
+    }
+    if (P_out)
+      for (int64_t n = 0; n < H; ++n) P_out[i * H + n] = acc[n];
+    if (C_out) {
+      if (t < b0 || t >= b0 + blk) {
+        bad |= 4;
+      } else {
+        for (int p = 0; p < W; ++p) {
+          if (p == rank) continue;
+          const float* part = partials[p] + (size_t)(t - b0) * H;
+          for (int64_t n = 0; n < H; ++n) acc[n] += (double)part[n];
+        }
+        for (int64_t n = 0; n < H; ++n) C_out[i * H + n] = acc[n];
+      }
+    }
+    free(acc);
+    free(y);
+  }
+  (void)nthreads;
+  return (bad & 2) ? -2 : (bad & 4) ? -3 : 0;
 }
 
 /* ------------------------------------------------------------------------- */

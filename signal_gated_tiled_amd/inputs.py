@@ -143,6 +143,27 @@ class MoEWorkload:
         return 2.0 * self.T * self.topk * self.H * self.I
 
 
+@dataclasses.dataclass(frozen=True)
+class MoERSWorkload:
+    """Combine side of the MoE layer: P[t] = sum_j gate[t, j] * Hg[row(t, j)] @ W2_e, then ReduceScatter."""
+    name: str
+    W: int
+    T: int
+    I: int      # input width of the down projection (the up projection's output)
+    H: int      # output width (hidden)
+    E: int
+    topk: int
+    std: float = 0.02
+    zipf_alpha: float = 1.0
+    dist: str = "normal"
+    peer_dist: str = "normal"
+    seed_index: int = 5
+
+    @property
+    def flops(self) -> float:
+        return 2.0 * self.T * self.topk * self.I * self.H
+
+
 # The five workloads (index = seed offset).  Shapes follow the pages' model
 # shapes: Qwen3-32B MLP (hidden 5120, intermediate 25600), Llama-3-70B MLP
 # (hidden 8192, intermediate 28672), each split 8 ways.
@@ -155,7 +176,10 @@ LLAMA_AG = AGWorkload("ag_llama3_70b_mlp_w8", W=8, M=16384, K=8192, N=3584, peer
 MOE = MoEWorkload("moe_ag_grouped_w8", W=8, T=4096, H=2048, I=768, E=64, topk=8, peer_gbps=50.0,
                   seed_index=4)
 
-WORKLOADS = {w.name: w for w in (TINY, QWEN_AG, GEMM_RS, LLAMA_AG, MOE)}
+# The down projection of the same MoE layer (the next workload on the pages' list).
+MOE_RS = MoERSWorkload("moe_gemm_rs_w8", W=8, T=4096, I=768, H=2048, E=64, topk=8, seed_index=5)
+
+WORKLOADS = {w.name: w for w in (TINY, QWEN_AG, GEMM_RS, LLAMA_AG, MOE, MOE_RS)}
 
 
 def _streams(seed_index: int, n: int, salt: int = 0):
@@ -222,6 +246,36 @@ def make_moe(w: MoEWorkload, salt: int = 0, W_layout: str = "kn"):
     if W_layout == "nk":
         We = np.ascontiguousarray(np.transpose(We, (0, 2, 1)))
     return shards, We, logits
+
+
+def make_moe_rs(w: MoERSWorkload, salt: int = 0, W_layout: str = "kn"):
+    """Return (Hg, W2, gate, logits, partials).
+
+    Hg: (T * topk) x I bf16, the grouped rows (row r belongs to whatever (expert, token) the routing of
+    `logits` puts at r).  W2: E x I x H ("kn") or E x H x I ("nk") bf16.  gate: T x topk float32 in (0, 1),
+    one weight per pick.  logits: as in make_moe.  partials: W arrays of (T/W) x H float32.
+    """
+    assert w.T % w.W == 0
+    ss = _streams(w.seed_index, 5 + w.W, salt)
+    Hg = _draw(w.dist, ss[0], (w.T * w.topk, w.I), "bf16", w.std * 50 if w.dist == "normal" else w.std)
+    W2 = _draw(w.dist, ss[1], (w.E, w.I, w.H), "bf16", w.std)
+    gate = _rng(ss[2]).random(size=(w.T, w.topk), dtype=np.float32)
+    g = _rng(ss[3]).standard_normal(size=(w.T, w.E), dtype=np.float32)
+    perm = _rng(ss[4]).permutation(w.E)
+    beta = (-w.zipf_alpha * np.log1p(perm.astype(np.float64))).astype(np.float32)
+    logits = (g + beta[None, :]).astype(np.float32)
+    mb = w.T // w.W
+    partials = []
+    for p in range(w.W):
+        if w.peer_dist == "zero":
+            partials.append(np.zeros((mb, w.H), np.float32))
+        elif w.peer_dist == "int":
+            partials.append(small_int(ss[5 + p], (mb, w.H), -8, 8, dtype="f32"))
+        else:
+            partials.append(normal_f32(ss[5 + p], (mb, w.H), 1.0))
+    if W_layout == "nk":
+        W2 = np.ascontiguousarray(np.transpose(W2, (0, 2, 1)))
+    return Hg, W2, gate, logits, partials
 
 
 def scaled(w, **kw):

@@ -269,3 +269,107 @@ def test_moe_exact_small(orc):
     _, _, _, _, Y2 = orc.moe_ag_gemm(shards, np.ascontiguousarray(np.transpose(We, (0, 2, 1))), logits, 2,
                                      w_layout="nk")
     assert np.array_equal(Y, Y2)
+
+
+# ---------------------------------------------------------------------------
+# MoE GEMM + ReduceScatter (combine side)
+# ---------------------------------------------------------------------------
+def _group(ids, E):
+    """Routing tables of a given pick matrix: rows grouped by expert ascending, tokens ascending inside."""
+    T, k = ids.shape
+    off = np.zeros(E + 1, np.int32)
+    rows = []
+    for e in range(E):
+        off[e] = len(rows)
+        rows += [t for t in range(T) for j in range(k) if ids[t, j] == e]
+    off[E] = len(rows)
+    return off, np.array(rows, np.int32)
+
+
+def _moe_rs_small(seed=7, T=16, k=2, E=4, n_in=8, H=6, W=4, dist="int"):
+    w = I.scaled(I.MOE_RS, T=T, topk=k, E=E, I=n_in, H=H, W=W, dist=dist, peer_dist="int", seed_index=seed)
+    return w, I.make_moe_rs(w)
+
+
+def test_moe_rs_single_expert_top1_is_dense_gemm_rs(orc):
+    # one expert, one pick per token, gate 1: the grouped rows are the tokens in order, so P = Hg @ W2[0]
+    # (a plain matrix product) and C adds the peers' blocks
+    w, (Hg, W2, gate, logits, parts) = _moe_rs_small(T=16, k=1, E=1, n_in=8, H=6, W=4)
+    ids = np.zeros((16, 1), np.int32)
+    off, rt = _group(ids, 1)
+    gate = np.ones((16, 1), np.float32)
+    A = I.bf16_bits_to_f32(Hg).astype(np.float64)
+    B = I.bf16_bits_to_f32(W2[0]).astype(np.float64)
+    P_ref = A @ B
+    for rank in range(4):
+        C = orc.moe_gemm_rs(Hg, W2, gate, ids, off, rt, parts, rank)
+        blk = slice(rank * 4, rank * 4 + 4)
+        C_ref = P_ref[blk] + sum(parts[p].astype(np.float64) for p in range(4) if p != rank)
+        assert np.array_equal(C, C_ref)
+
+
+def test_moe_rs_one_hot_routing_is_per_expert_products(orc):
+    # token t picks expert t % E alone, with gate 2^-(t % 3): P[t] = gate * Hg[row] @ W2[t % E]
+    w, (Hg, W2, gate, logits, parts) = _moe_rs_small(T=24, k=1, E=3, n_in=10, H=7, W=2)
+    ids = (np.arange(24) % 3).astype(np.int32)[:, None]
+    off, rt = _group(ids, 3)
+    gate = (2.0 ** -(np.arange(24) % 3)).astype(np.float32)[:, None]
+    P = orc.moe_gemm_rs_p(Hg, W2, gate, ids, off, rt, np.arange(24))
+    A = I.bf16_bits_to_f32(Hg).astype(np.float64)
+    for t in range(24):
+        e = t % 3
+        r = int(np.nonzero(rt[off[e]:off[e + 1]] == t)[0][0]) + int(off[e])
+        ref = float(gate[t, 0]) * (A[r] @ I.bf16_bits_to_f32(W2[e]).astype(np.float64))
+        assert np.array_equal(P[t], ref)
+
+
+def test_moe_rs_gates_are_linear(orc):
+    w, (Hg, W2, gate, logits, parts) = _moe_rs_small(T=16, k=3, E=5, n_in=8, H=6, W=4)
+    ids, off, rt = orc.moe_route(logits, 3)
+    g = (2.0 ** -np.random.default_rng(1).integers(0, 3, size=(16, 3))).astype(np.float32)
+    C1 = orc.moe_gemm_rs(Hg, W2, g, ids, off, rt, parts, 1)
+    C2 = orc.moe_gemm_rs(Hg, W2, 2 * g, ids, off, rt, parts, 1)
+    peers = sum(parts[p].astype(np.float64) for p in range(4) if p != 1)
+    assert np.array_equal(C2 - peers, 2 * (C1 - peers))
+
+
+def test_moe_rs_expert_relabelling_is_invisible(orc):
+    # renaming the experts (weights permuted alike, rows regrouped in the new expert order) leaves P unchanged
+    w, (Hg, W2, gate, logits, parts) = _moe_rs_small(T=12, k=2, E=4, n_in=8, H=5, W=2)
+    ids, off, rt = orc.moe_route(logits, 2)
+    P = orc.moe_gemm_rs_p(Hg, W2, gate, ids, off, rt, np.arange(12))
+    pi = np.array([2, 0, 3, 1])                      # expert e is called pi[e] after renaming
+    ids2 = pi[ids].astype(np.int32)
+    W22 = np.empty_like(W2)
+    W22[pi] = W2
+    off2, rt2 = _group(ids2, 4)
+    # row of (t, new expert pi[e]) takes the old row of (t, e)
+    Hg2 = np.empty_like(Hg)
+    for e in range(4):
+        for r in range(off[e], off[e + 1]):
+            t = rt[r]
+            r2 = int(np.nonzero(rt2[off2[pi[e]]:off2[pi[e] + 1]] == t)[0][0]) + int(off2[pi[e]])
+            Hg2[r2] = Hg[r]
+    P2 = orc.moe_gemm_rs_p(Hg2, W22, gate, ids2, off2, rt2, np.arange(12))
+    assert np.array_equal(P, P2)
+
+
+def test_moe_rs_pick_order_only_moves_gates(orc):
+    # reversing each token's picks together with its gates leaves P unchanged (integer data: exact sums)
+    w, (Hg, W2, gate, logits, parts) = _moe_rs_small(T=10, k=3, E=6, n_in=8, H=4, W=2)
+    ids, off, rt = orc.moe_route(logits, 3)
+    g = np.ones((10, 3), np.float32)
+    P = orc.moe_gemm_rs_p(Hg, W2, g, ids, off, rt, np.arange(10))
+    P2 = orc.moe_gemm_rs_p(Hg, W2, g[:, ::-1].copy(), ids[:, ::-1].copy(), off, rt, np.arange(10))
+    assert np.array_equal(P, P2)
+
+
+def test_moe_rs_planted_mistake_is_caught(orc):
+    # a routing table that sends a pick to a group without the token is rejected
+    w, (Hg, W2, gate, logits, parts) = _moe_rs_small(T=8, k=1, E=2, n_in=8, H=4, W=2)
+    ids = np.zeros((8, 1), np.int32)
+    off, rt = _group(ids, 2)
+    bad = ids.copy()
+    bad[3, 0] = 1
+    with pytest.raises(ValueError):
+        orc.moe_gemm_rs_p(Hg, W2, gate, bad, off, rt, np.arange(8))
