@@ -82,6 +82,28 @@ struct MoeTile {
   int32_t r0;       // first row (index into the grouped rows of Y)
 };
 
+// MoE GEMM + ReduceScatter (the combine side).  `rs` carries the
+// ReduceScatter part exactly as the dense GEMM+ReduceScatter uses it (P is
+// the combined partial, M = T tokens, N = H).
+struct MoeRsArgs {
+  const uint16_t* Hg;        // rows x I bf16, grouped rows
+  const uint16_t* W2;        // E x I x H (KN) or E x H x I (NK) bf16
+  float* Y;                  // rows x H fp32: each grouped row times its expert's weight
+  const float* gate;         // T x k
+  const int32_t* topk_ids;   // T x k
+  const int32_t* expert_off; // E + 1
+  const int32_t* row_token;  // rows
+  int32_t* row_of;           // T x k: grouped row of pick (t, j) (prologue)
+  MoeTile* tiles;            // 256-row tiles of the expert groups (prologue)
+  uint32_t* n_row_tiles;     // (prologue)
+  uint32_t* col_done;        // per 256-column GEMM tile: row tiles stored (cleared by the prologue)
+  uint32_t* claim;           // combine / reduction claim counter (cleared by the prologue)
+  int64_t T, I, H, rows;
+  int32_t E, k, tiles_n, tiles_cap;
+  int32_t b_layout;
+  RsArgs rs;
+};
+
 // Routing and work-list tables of one MoE call (device memory owned by the context).
 struct MoeTables {
   uint32_t* masks;        // ceil(E / 32) x T: bit e % 32 of word e / 32 set when token t chose e

@@ -37,9 +37,11 @@ int moe_tokens_per_group(int64_t T, int k);
 hipError_t launch_moe_route(const float* logits, int64_t T, int E, int k, const uint32_t* rank_of_flag,
                             int32_t flag_rows, uint32_t n_flags, int tile_rows, const MoeTables& tb,
                             int32_t* expert_off, int32_t* row_token, int32_t* topk_ids, hipStream_t stream);
+hipError_t launch_moe_rs(const MoeRsArgs& a, int grid, hipStream_t stream);
 hipError_t launch_moe_consumer(const MoeArgs& a, int b_layout, int out_dtype, int tile_rows, int tile_waves, int grid,
                                hipStream_t stream);
 inline int kBMrs() { return rs_gemm_tile(); }
+constexpr int kBNmoe() { return 256; }  // column tile of the tile core
 }  // namespace sgt
 
 using namespace sgt;
@@ -93,6 +95,14 @@ struct sgt_ctx {
   uint32_t* d_moe_ranks = nullptr; // MoE: device copy of a call's arrival ranks (kItemsCap words)
   uint32_t* d_moe_masks = nullptr; // MoE token bitmasks; grow on demand
   int64_t moe_masks_cap = 0;
+  // MoE combine side: inverse routing table, group row tiles, counters (tile
+  // count, claim, per-column done counts); grow on demand
+  int32_t* d_mrs_rowof = nullptr;
+  int64_t mrs_rowof_cap = 0;
+  MoeTile* d_mrs_tiles = nullptr;
+  int64_t mrs_tiles_cap = 0;
+  uint32_t* d_mrs_ctr = nullptr;
+  int64_t mrs_ctr_cap = 0;
   hipEvent_t slot_ev[kSlots] = {};
   bool slot_used[kSlots] = {};
   int slot = 0;
@@ -413,6 +423,9 @@ sgt_status sgt_ctx_destroy(sgt_ctx* c) {
   if (c->d_moe_keys) (void)hipFree(c->d_moe_keys);
   if (c->d_moe_masks) (void)hipFree(c->d_moe_masks);
   if (c->d_moe_ranks) (void)hipFree(c->d_moe_ranks);
+  if (c->d_mrs_rowof) (void)hipFree(c->d_mrs_rowof);
+  if (c->d_mrs_tiles) (void)hipFree(c->d_mrs_tiles);
+  if (c->d_mrs_ctr) (void)hipFree(c->d_mrs_ctr);
   if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
   if (c->ev_join) (void)hipEventDestroy(c->ev_join);
   if (c->prod) (void)hipStreamDestroy(c->prod);
@@ -924,6 +937,112 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
   HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
   ctx->slot_used[slot] = true;
+  return finish(ctx, o, stream);
+}
+
+
+sgt_status sgt_moe_gemm_rs(sgt_ctx* ctx, const void* Hg, const void* W2, const float* gate, const int32_t* topk_ids,
+                           const int32_t* expert_off, const int32_t* row_token, const float* const* partials,
+                           float* Y, float* partial_out, float* C_shard, uint32_t* gflags, uint32_t* pflags, int W,
+                           int64_t T, int topk, int64_t I, int64_t H, int E, const sgt_opts* opts, void* stream_) {
+  if (!ctx) return fail(SGT_EINVAL, "ctx is NULL");
+  sgt_status st = check_opts(opts, W < 1 ? 1 : W);
+  if (st != SGT_OK) return st;
+  const sgt_opts& o = *opts;
+  if (o.in_dtype != SGT_BF16) return fail(SGT_EUNSUPPORTED, "MoE takes bf16 rows and weights");
+  if (o.out_dtype != SGT_F32) return fail(SGT_EUNSUPPORTED, "the combined partials are fp32");
+  if (o.peer_gbps > 0) return fail(SGT_EUNSUPPORTED, "the peers' partials are resident (peer_gbps must be 0)");
+  if (o.rs_tile != 0 && o.rs_tile != 128) return fail(SGT_EINVAL, "rs_tile %d (the combine tile is 128)", o.rs_tile);
+  if (o.tile_waves != 0 && o.tile_waves != 8) return fail(SGT_EUNSUPPORTED, "tile_waves %d (8 only)", o.tile_waves);
+  if (W < 1 || W > kMaxW) return fail(SGT_EINVAL, "W = %d outside [1, %d]", W, kMaxW);
+  if (E < 1 || E > 256 || topk < 1 || topk > E) return fail(SGT_EINVAL, "need 1 <= topk <= E <= 256 (E=%d topk=%d)", E, topk);
+  if (T < 1 || I < 8 || H < 8 || I % 8 || H % 8 || T % W || (T / W) % 128)
+    return fail(SGT_EINVAL, "bad shape T=%lld I=%lld H=%lld W=%d (I, H multiples of 8; T/W a multiple of 128)",
+                (long long)T, (long long)I, (long long)H, W);
+  const int64_t rows = T * topk;
+  const int64_t lim = (int64_t)1 << 31;
+  if (rows * H * 4 >= lim || T * H * 4 >= lim || (int64_t)256 * I * 2 >= lim || (int64_t)256 * H * 4 >= lim ||
+      (o.b_layout == SGT_KN && I * H * 2 >= lim))
+    return fail(SGT_EUNSUPPORTED, "rows x H or one expert's I x H too large for 32-bit offsets");
+  if (!Hg || !W2 || !gate || !topk_ids || !expert_off || !row_token || !Y || !partial_out || !C_shard || !gflags ||
+      !pflags || !partials)
+    return fail(SGT_EINVAL, "NULL pointer argument");
+  if (!aligned16(Hg) || !aligned16(W2) || !aligned16(Y) || !aligned16(partial_out) || !aligned16(C_shard) ||
+      !aligned16(gflags) || !aligned16(pflags) || (reinterpret_cast<uintptr_t>(gate) & 3u) ||
+      (reinterpret_cast<uintptr_t>(topk_ids) & 3u) || (reinterpret_cast<uintptr_t>(expert_off) & 3u) ||
+      (reinterpret_cast<uintptr_t>(row_token) & 3u))
+    return fail(SGT_EINVAL, "pointer not aligned (16 bytes for matrices and flags, 4 for tables)");
+  for (int p = 0; p < W; ++p)
+    if (p != o.rank && (!partials[p] || !aligned16(partials[p])))
+      return fail(SGT_EINVAL, "partials[%d] NULL or not 16-byte aligned", p);
+  int64_t ng = 0, np = 0;
+  sgt_opts o128 = o;
+  o128.rs_tile = 128;
+  if ((st = sgt_rs_flag_count(W, T, H, &o128, &ng, &np)) != SGT_OK) return st;
+
+  std::lock_guard<std::mutex> lock(ctx->mu);
+  DeviceGuard g(ctx->device);
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const int64_t tiles_n = (H + kBNmoe() - 1) / kBNmoe();
+  const int64_t max_tiles = (rows + 255) / 256 + E;
+  if (ctx->mrs_rowof_cap < rows || ctx->mrs_tiles_cap < max_tiles || ctx->mrs_ctr_cap < tiles_n + 4) {
+    // grow the tables after draining the device (no call of this context is in flight then)
+    HIP_TRY(hipDeviceSynchronize());
+    if (ctx->mrs_rowof_cap < rows) {
+      if (ctx->d_mrs_rowof) (void)hipFree(ctx->d_mrs_rowof);
+      ctx->d_mrs_rowof = nullptr;
+      ctx->mrs_rowof_cap = 0;
+      const int64_t cap = std::max<int64_t>(rows, 1 << 16);
+      HIP_TRY(hipMalloc(&ctx->d_mrs_rowof, cap * sizeof(int32_t)));
+      HIP_TRY(hipMemset(ctx->d_mrs_rowof, 0, cap * sizeof(int32_t)));
+      ctx->mrs_rowof_cap = cap;
+    }
+    if (ctx->mrs_tiles_cap < max_tiles) {
+      if (ctx->d_mrs_tiles) (void)hipFree(ctx->d_mrs_tiles);
+      ctx->d_mrs_tiles = nullptr;
+      ctx->mrs_tiles_cap = 0;
+      const int64_t cap = std::max<int64_t>(max_tiles, 1024);
+      HIP_TRY(hipMalloc(&ctx->d_mrs_tiles, cap * sizeof(MoeTile)));
+      ctx->mrs_tiles_cap = cap;
+    }
+    if (ctx->mrs_ctr_cap < tiles_n + 4) {
+      if (ctx->d_mrs_ctr) (void)hipFree(ctx->d_mrs_ctr);
+      ctx->d_mrs_ctr = nullptr;
+      ctx->mrs_ctr_cap = 0;
+      const int64_t cap = std::max<int64_t>(tiles_n + 4, 256);
+      HIP_TRY(hipMalloc(&ctx->d_mrs_ctr, cap * sizeof(uint32_t)));
+      HIP_TRY(hipMemset(ctx->d_mrs_ctr, 0, cap * sizeof(uint32_t)));
+      ctx->mrs_ctr_cap = cap;
+    }
+  }
+  const uint32_t e = ++ctx->epoch;
+
+  RsArgs rs{};
+  rs.P = partial_out; rs.C_shard = C_shard;
+  for (int p = 0; p < W; ++p) rs.partials.p[p] = (p == o.rank) ? nullptr : partials[p];
+  rs.gflags = gflags; rs.pflags = pflags; rs.status = ctx->d_status; rs.trace = nullptr;
+  rs.M = T; rs.N = H; rs.K = I; rs.block_rows = T / W; rs.W = W; rs.rank = o.rank;
+  rs.rs_tile = 128; rs.rs_tm = (int)((T / W) / 128); rs.rs_tn = (int)((H + 127) / 128);
+  rs.n_red_items = rs.rs_tm * rs.rs_tn;
+  rs.epoch = e; rs.timeout_ticks = timeout_ticks(o);
+  rs.red_counter = ctx->d_mrs_ctr + 1;
+
+  MoeRsArgs a{};
+  a.Hg = static_cast<const uint16_t*>(Hg);
+  a.W2 = static_cast<const uint16_t*>(W2);
+  a.Y = Y; a.gate = gate; a.topk_ids = topk_ids; a.expert_off = expert_off; a.row_token = row_token;
+  a.row_of = ctx->d_mrs_rowof; a.tiles = ctx->d_mrs_tiles;
+  a.n_row_tiles = ctx->d_mrs_ctr; a.claim = ctx->d_mrs_ctr + 1; a.col_done = ctx->d_mrs_ctr + 4;
+  a.T = T; a.I = I; a.H = H; a.rows = rows; a.E = E; a.k = topk; a.tiles_n = (int32_t)tiles_n;
+  a.tiles_cap = (int32_t)ctx->mrs_tiles_cap; a.b_layout = o.b_layout;
+  a.rs = rs;
+
+  // the peers' partials are resident: their flags take the epoch before the kernel
+  HIP_TRY(launch_rs_prepare(pflags, np, e, a.claim, stream));
+  const int grid = o.consumer_cus > 0 ? std::min(o.consumer_cus, ctx->n_cu) : ctx->n_cu;
+  if ((st = mark(o, 0, stream)) != SGT_OK) return st;
+  HIP_TRY(launch_moe_rs(a, grid, stream));
+  if ((st = mark(o, 1, stream)) != SGT_OK) return st;
   return finish(ctx, o, stream);
 }
 
