@@ -291,7 +291,49 @@ def bench_moe(ctx, up, args, torch, sgt, I, lay):
         "link_floor_us": (m.T // m.W) * m.H * 2 / (m.peer_gbps * 1e9) * 1e6,
     }
     del sh, We, lg, Xg, Y
-    return out
+    return out, (off, rt, ids)
+
+
+def bench_moe_rs(ctx, up, args, torch, sgt, I, lay, tables):
+    """MoE GEMM + ReduceScatter (combine side) of the same layer: T 4096 tokens, top-8 of 64 experts, I 768 ->
+    H 2048, W 8; routing tables from the AllGather side's GPU routing; peers' partials resident."""
+    import numpy as np
+    m = I.MOE_RS
+    dev = "cuda:0"
+    off, rt, ids = tables
+    Hg_h, W2_h, gate_h, _, parts_h = I.make_moe_rs(m, W_layout=lay)
+    Hg, W2, gate = up(Hg_h), up(W2_h), up(gate_h)
+    rank = 0
+    parts = [up(p) if q != rank else None for q, p in enumerate(parts_h)]
+    rows = m.T * m.topk
+    Y = torch.empty((rows, m.H), dtype=torch.float32, device=dev)
+    P = torch.empty((m.T, m.H), dtype=torch.float32, device=dev)
+    Cs = torch.empty((m.T // m.W, m.H), dtype=torch.float32, device=dev)
+    ng, npf = sgt.rs_flag_count(m.W, m.T, m.H, rs_tile=128)
+    gf = torch.zeros(ng, dtype=torch.int32, device=dev)
+    pf = torch.zeros(npf, dtype=torch.int32, device=dev)
+
+    def fn(i, ev):
+        ctx.moe_gemm_rs(Hg, W2, gate, ids, off, rt, parts, Y, P, Cs, gf, pf, rank=rank, b_layout=lay,
+                        consumer_events=ev)
+    step_ms, kern_ms, kern = timed(fn, args.steps, args.warmup, torch, ctx)
+    flops = m.flops
+    # algorithmic HBM bytes: Hg and W2 read once, Y written and read back once, P written, this rank's block of
+    # P read back with the W-1 peers' blocks, C written
+    blk = (m.T // m.W) * m.H * 4
+    hbm = rows * m.I * 2 + m.E * m.I * m.H * 2 + 2 * rows * m.H * 4 + m.T * m.H * 4 + (m.W + 1) * blk
+    med = statistics.median(kern)
+    return {
+        "workload": m.name, "T": m.T, "I": m.I, "H": m.H, "E": m.E, "topk": m.topk, "W": m.W,
+        "routing": "the AllGather side's GPU routing of the same tokens (group sizes as above)",
+        "gflop": flops / 1e9, "algorithmic_hbm_bytes": hbm,
+        "step_ms": step_ms, "tflops_step": flops / (step_ms * 1e-3) / 1e12,
+        "kernel_ms": spread(kern),
+        "kernel_mfma_frac": flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "kernel_hbm_frac": hbm / (med * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "note": "one persistent kernel: grouped GEMM tiles, gate-weighted combine tiles gated on their GEMM "
+                "column, signal-gated reduction of this rank's block; peers' partials resident",
+    }
 
 
 def main():
@@ -542,7 +584,9 @@ def main():
         del A, Brs, parts, P, Cs, Cg
 
     if not args.no_moe:
-        detail["moe_ag_grouped"] = bench_moe(ctx, up, args, torch, sgt, I, lay)
+        detail["moe_ag_grouped"], tables = bench_moe(ctx, up, args, torch, sgt, I, lay)
+        detail["moe_gemm_rs"] = bench_moe_rs(ctx, up, args, torch, sgt, I, lay, tables)
+        del tables
 
     cpu = None
     if not args.no_cpu_baseline:
