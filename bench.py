@@ -317,6 +317,16 @@ def bench_moe_rs(ctx, up, args, torch, sgt, I, lay, tables):
         ctx.moe_gemm_rs(Hg, W2, gate, ids, off, rt, parts, Y, P, Cs, gf, pf, rank=rank, b_layout=lay,
                         consumer_events=ev)
     step_ms, kern_ms, kern = timed(fn, args.steps, args.warmup, torch, ctx)
+    # the peers' partials arriving at 50 GB/s per link into an inbox
+    gbps = 50.0
+    inbox = [torch.empty_like(p) if p is not None else None for p in parts]
+
+    def fn_paced(i, ev):
+        ctx.moe_gemm_rs(Hg, W2, gate, ids, off, rt, parts, Y, P, Cs, gf, pf, rank=rank, b_layout=lay,
+                        consumer_events=ev, inbox=inbox, peer_gbps=gbps, arrival_seed=i + 1)
+    pc_ms, _, pc_k = timed(fn_paced, max(4, args.steps // 2), 2, torch, ctx)
+    assert torch.equal(inbox[1], parts[1]), "paced inbox mismatch"
+    del inbox
     flops = m.flops
     # algorithmic HBM bytes: Hg and W2 read once, Y written and read back once, P written, this rank's block of
     # P read back with the W-1 peers' blocks, C written
@@ -331,8 +341,11 @@ def bench_moe_rs(ctx, up, args, torch, sgt, I, lay, tables):
         "kernel_ms": spread(kern),
         "kernel_mfma_frac": flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "kernel_hbm_frac": hbm / (med * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "paced_50gbps": {"peer_gbps": gbps, "step_ms": pc_ms, "kernel_ms": spread(pc_k),
+                         "tflops": flops / (pc_ms * 1e-3) / 1e12,
+                         "link_floor_us": (m.T // m.W) * m.H * 4 / (gbps * 1e9) * 1e6},
         "note": "one persistent kernel: grouped GEMM tiles, gate-weighted combine tiles gated on their GEMM "
-                "column, signal-gated reduction of this rank's block; peers' partials resident",
+                "column, signal-gated reduction of this rank's block; peers' partials resident (and paced)",
     }
 
 

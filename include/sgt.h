@@ -290,7 +290,8 @@ SGT_API sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, co
  * gflags / pflags: as sgt_gemm_rs with M = T, N = H and rs_tile 128
  *     (sgt_rs_flag_count); pflags are set by the library (resident peers).
  * Requirements: bf16 in, fp32 out, 1 <= topk <= E <= 256, I and H multiples of
- *     8, T/W a multiple of 128, rows x H x 4 < 2^31, peer_gbps = 0, tile_waves
+ *     8, T/W a multiple of 128, rows x H x 4 < 2^31, peer_gbps = 0 (paced peers:
+ *     sgt_moe_gemm_rs_paced; here it is SGT_EUNSUPPORTED), tile_waves
  *     0 or 8, rs_tile 0 or 128; 16-byte aligned matrices and flags, 4-byte
  *     aligned tables.  Routing tables that disagree with each other are not
  *     detected (the result is then undefined, but every access stays in bounds).
@@ -303,6 +304,25 @@ SGT_API sgt_status sgt_moe_gemm_rs(sgt_ctx* ctx, const void* Hg, const void* W2,
                                    const float* const* partials, float* Y, float* partial_out, float* C_shard,
                                    uint32_t* gflags, uint32_t* pflags, int W, int64_t T, int topk, int64_t I,
                                    int64_t H, int E, const sgt_opts* opts, void* stream);
+
+/*
+ * sgt_moe_gemm_rs with the peers' partials arriving over simulated links (as
+ * sgt_gemm_rs_paced does for the dense ReduceScatter): peer p's block
+ * peer_blocks[p] ((T/W) x H fp32, in its memory) is copied into this rank's
+ * inbox[p] in bands of 128 rows, each band released (its peer flags) no
+ * earlier than link p would deliver it at opts->peer_gbps (0 = unthrottled), in
+ * order or seeded order, plus U[0, opts->jitter_us]; the reduction sums the
+ * inboxes.  On return inbox[p] holds peer_blocks[p] bit for bit.
+ * Modes: SGT_PROD_CU (overlapped; the combine kernel on the CUs the producer
+ * leaves) or SGT_PROD_SERIAL; SGT_PROD_PRESET is SGT_EINVAL.  Other arguments,
+ * requirements and errors as sgt_moe_gemm_rs.
+ */
+SGT_API sgt_status sgt_moe_gemm_rs_paced(sgt_ctx* ctx, const void* Hg, const void* W2, const float* gate,
+                                         const int32_t* topk_ids, const int32_t* expert_off, const int32_t* row_token,
+                                         const float* const* peer_blocks, float* const* inbox, float* Y,
+                                         float* partial_out, float* C_shard, uint32_t* gflags, uint32_t* pflags,
+                                         int W, int64_t T, int topk, int64_t I, int64_t H, int E,
+                                         const sgt_opts* opts, void* stream);
 
 /* Words of the optional trace buffer of an sgt_moe_ag_gemm call: 4 x uint64
  * {wait start, flags seen, tile end, workgroup} per work item in claim order

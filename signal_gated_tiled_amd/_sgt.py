@@ -86,10 +86,13 @@ def lib() -> ctypes.CDLL:
                                         ctypes.POINTER(Opts), P]
         L.sgt_moe_gemm_rs.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int, I64, ctypes.c_int, I64,
                                       I64, ctypes.c_int, ctypes.POINTER(Opts), P]
+        L.sgt_moe_gemm_rs_paced.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int, I64,
+                                            ctypes.c_int, I64, I64, ctypes.c_int, ctypes.POINTER(Opts), P]
         L.sgt_moe_ag_gemm.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_int, I64, I64, I64, ctypes.c_int,
                                       ctypes.c_int, ctypes.POINTER(Opts), P]
         for f in ("sgt_ctx_create", "sgt_ctx_destroy", "sgt_sync", "sgt_ag_gemm", "sgt_rs_flag_count", "sgt_gemm_rs",
-                  "sgt_gemm_rs_paced", "sgt_moe_ag_gemm", "sgt_moe_gemm_rs"):
+                  "sgt_gemm_rs_paced", "sgt_moe_ag_gemm", "sgt_moe_gemm_rs",
+                  "sgt_moe_gemm_rs_paced"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -301,8 +304,9 @@ class Context:
                                        ctypes.byref(o), _stream_handle(stream)))
 
     def moe_gemm_rs(self, Hg, W2, gate, topk_ids, expert_off, row_token, partials: Sequence, Y, partial_out,
-                    C_shard, gflags, pflags, *, stream=None, **kw):
-        """MoE GEMM + ReduceScatter (combine side); see sgt_moe_gemm_rs."""
+                    C_shard, gflags, pflags, *, stream=None, inbox: Optional[Sequence] = None, **kw):
+        """MoE GEMM + ReduceScatter (combine side); see sgt_moe_gemm_rs.  With `inbox`, `partials` are the
+        peers' blocks and arrive into `inbox` at the simulated link rate (sgt_moe_gemm_rs_paced)."""
         dev = Hg.device
         W = len(partials)
         rows, n_in = Hg.shape
@@ -316,6 +320,18 @@ class Context:
         o = make_opts(**kw)
         parts = (P * W)(*[_dev_ptr(p, "partials[%d]" % i, dev) if p is not None else 0
                           for i, p in enumerate(partials)])
+        if inbox is not None:
+            box = (P * W)(*[_dev_ptr(p, "inbox[%d]" % i, dev) if p is not None else 0 for i, p in enumerate(inbox)])
+            _check(lib().sgt_moe_gemm_rs_paced(self._h, _dev_ptr(Hg, "Hg", dev), _dev_ptr(W2, "W2", dev),
+                                               _dev_ptr(gate, "gate", dev), _dev_ptr(topk_ids, "topk_ids", dev),
+                                               _dev_ptr(expert_off, "expert_off", dev),
+                                               _dev_ptr(row_token, "row_token", dev), ctypes.cast(parts, P),
+                                               ctypes.cast(box, P), _dev_ptr(Y, "Y", dev),
+                                               _dev_ptr(partial_out, "partial_out", dev),
+                                               _dev_ptr(C_shard, "C_shard", dev), _dev_ptr(gflags, "gflags", dev),
+                                               _dev_ptr(pflags, "pflags", dev), W, T, topk, n_in, H, E,
+                                               ctypes.byref(o), _stream_handle(stream)))
+            return
         _check(lib().sgt_moe_gemm_rs(self._h, _dev_ptr(Hg, "Hg", dev), _dev_ptr(W2, "W2", dev),
                                      _dev_ptr(gate, "gate", dev), _dev_ptr(topk_ids, "topk_ids", dev),
                                      _dev_ptr(expert_off, "expert_off", dev), _dev_ptr(row_token, "row_token", dev),

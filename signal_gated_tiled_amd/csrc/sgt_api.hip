@@ -593,6 +593,68 @@ sgt_status sgt_rs_flag_count(int W, int64_t M, int64_t N, const sgt_opts* opts, 
 
 namespace {
 
+// Paced peers of a ReduceScatter: peer p's block (bands of rs_tile rows, band_bytes
+// each, rs_tm bands) is copied from peer_blocks[p] into inbox[p] by the producer,
+// each band no earlier than link p would deliver it (in order or shuffled, plus
+// jitter), and the band's rs_tn peer flags are published.  The peers' flags
+// start unset and `counter` (the reduction claim counter) restarts at zero.
+// Serial mode: the producer runs first on the caller's stream.  Otherwise it
+// runs on the context's producer stream, forked from the caller's; the caller
+// launches its consumer and then joins with join_paced_peers.  *pwg_out: the
+// producer's workgroups.
+sgt_status launch_paced_peers(sgt_ctx* ctx, const sgt_opts& o, uint32_t* pflags, const float* const* peer_blocks,
+                              const float* const* inbox, int W, int rs_tm, int rs_tn, int64_t band_bytes, uint32_t e,
+                              uint32_t* counter, hipStream_t stream, int* pwg_out) {
+  int slot;
+  sgt_status st;
+  if ((st = next_slot(ctx, &slot)) != SGT_OK) return st;
+  ProdItem* items = ctx->h_items[slot];
+  const int64_t bands = rs_tm, block_tiles = (int64_t)rs_tm * rs_tn;
+  const double ticks_per_band = o.peer_gbps > 0 ? (double)band_bytes / (o.peer_gbps * 1e3) * kTicksPerUs : 0.0;
+  uint64_t seed = o.arrival_seed * 0x100000001B3ull + 0x5851F42D4C957F2Dull;
+  int n = 0;
+  std::vector<int64_t> order((size_t)bands);
+  for (int d = 1; d < W; ++d) {
+    const int peer = (o.rank + d) % W;
+    for (int64_t j = 0; j < bands; ++j) order[(size_t)j] = j;
+    if (o.arrival_order != 0) shuffle(order, seed);
+    for (int64_t q = 0; q < bands; ++q) {
+      const int64_t j = order[(size_t)q];
+      ProdItem it = sched_item(peer * block_tiles + j * rs_tn, peer, (double)(q + 1) * ticks_per_band +
+                                                                      jitter_ticks(o, seed));
+      it.nflags = (uint16_t)rs_tn;
+      it.src = reinterpret_cast<const char*>(peer_blocks[peer]) + j * band_bytes;
+      it.dst = reinterpret_cast<char*>(const_cast<float*>(inbox[peer])) + j * band_bytes;
+      items[n++] = it;
+    }
+  }
+  std::stable_sort(items, items + n, [](const ProdItem& x, const ProdItem& y) { return x.release < y.release; });
+  const int pwg = std::min(default_producer_wgs(o, ctx->n_cu), std::max(n, 1));
+  *pwg_out = pwg;
+  HIP_TRY(launch_rs_prepare(pflags, 0, e, counter, stream));  // counter only: peers' flags come on arrival
+  if (o.producer == SGT_PROD_SERIAL) {
+    HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], items, n * sizeof(ProdItem), hipMemcpyHostToDevice, stream));
+    HIP_TRY(launch_ag_producer(pflags, ctx->d_items[slot], n, band_bytes, e, o.withhold_peer, nullptr, pwg, stream));
+    HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
+    ctx->slot_used[slot] = true;
+    return SGT_OK;
+  }
+  HIP_TRY(hipEventRecord(ctx->ev_fork, stream));
+  HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
+  HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], items, n * sizeof(ProdItem), hipMemcpyHostToDevice, ctx->prod));
+  HIP_TRY(launch_ag_producer(pflags, ctx->d_items[slot], n, band_bytes, e, o.withhold_peer, nullptr, pwg, ctx->prod));
+  HIP_TRY(hipEventRecord(ctx->slot_ev[slot], ctx->prod));
+  ctx->slot_used[slot] = true;
+  return SGT_OK;
+}
+
+// The caller's stream waits for the producer forked by launch_paced_peers.
+sgt_status join_paced_peers(sgt_ctx* ctx, hipStream_t stream) {
+  HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
+  HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
+  return SGT_OK;
+}
+
 // GEMM + ReduceScatter, shared by the resident and the paced entry points.
 // reduce_from[p]: what the reduction sums for peer p.  peer_blocks == NULL:
 // the peers' data is resident and their flags are preset.  Otherwise the
@@ -676,58 +738,26 @@ sgt_status gemm_rs_impl(sgt_ctx* ctx, const void* A_local, const void* B, const 
     return finish(ctx, o, stream);
   }
 
-  // Paced peers: the producer schedule (each peer's bands, in order or shuffled,
-  // one band every band_bytes / peer_gbps on each link, plus jitter).
-  int slot;
-  if ((st = next_slot(ctx, &slot)) != SGT_OK) return st;
-  ProdItem* items = ctx->h_items[slot];
-  const int64_t bands = a.rs_tm, block_tiles = (int64_t)a.rs_tm * a.rs_tn;
-  const double ticks_per_band = o.peer_gbps > 0 ? (double)band_bytes / (o.peer_gbps * 1e3) * kTicksPerUs : 0.0;
-  uint64_t seed = o.arrival_seed * 0x100000001B3ull + 0x5851F42D4C957F2Dull;
-  int n = 0;
-  std::vector<int64_t> order((size_t)bands);
-  for (int d = 1; d < W; ++d) {
-    const int peer = (o.rank + d) % W;
-    for (int64_t j = 0; j < bands; ++j) order[(size_t)j] = j;
-    if (o.arrival_order != 0) shuffle(order, seed);
-    for (int64_t q = 0; q < bands; ++q) {
-      const int64_t j = order[(size_t)q];
-      ProdItem it = sched_item(peer * block_tiles + j * a.rs_tn, peer, (double)(q + 1) * ticks_per_band +
-                                                                        jitter_ticks(o, seed));
-      it.nflags = (uint16_t)a.rs_tn;
-      it.src = reinterpret_cast<const char*>(peer_blocks[peer]) + j * band_bytes;
-      it.dst = reinterpret_cast<char*>(const_cast<float*>(reduce_from[peer])) + j * band_bytes;
-      items[n++] = it;
-    }
-  }
-  std::stable_sort(items, items + n, [](const ProdItem& x, const ProdItem& y) { return x.release < y.release; });
-  const int pwg = std::min(default_producer_wgs(o, ctx->n_cu), std::max(n, 1));
-  HIP_TRY(launch_rs_prepare(pflags, 0, e, ctx->d_counters, stream));  // counter only: peers' flags come on arrival
+  // Paced peers: the producer, on its own stream (or first on the caller's in
+  // serial mode), copies the peers' bands into the inbox and releases their flags.
+  int pwg = 0;
+  if ((st = launch_paced_peers(ctx, o, pflags, peer_blocks, reduce_from, W, a.rs_tm, a.rs_tn, band_bytes, e,
+                               ctx->d_counters, stream, &pwg)) != SGT_OK)
+    return st;
   if (o.producer == SGT_PROD_SERIAL) {
-    HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], items, n * sizeof(ProdItem), hipMemcpyHostToDevice, stream));
-    HIP_TRY(launch_ag_producer(pflags, ctx->d_items[slot], n, band_bytes, e, o.withhold_peer, nullptr, pwg, stream));
-    HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
-    ctx->slot_used[slot] = true;
     const int grid = std::min(total, o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu);
     if ((st = mark(o, 0, stream)) != SGT_OK) return st;
     HIP_TRY(launch_gemm_rs(a, grid, stream));
     if ((st = mark(o, 1, stream)) != SGT_OK) return st;
     return finish(ctx, o, stream);
   }
-  // Overlapped: the producer on its own stream and CUs; the GEMM+RS kernel on
-  // the rest (one workgroup per CU), so the reduction's waits cannot starve it.
-  HIP_TRY(hipEventRecord(ctx->ev_fork, stream));
-  HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
-  HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], items, n * sizeof(ProdItem), hipMemcpyHostToDevice, ctx->prod));
-  HIP_TRY(launch_ag_producer(pflags, ctx->d_items[slot], n, band_bytes, e, o.withhold_peer, nullptr, pwg, ctx->prod));
-  HIP_TRY(hipEventRecord(ctx->slot_ev[slot], ctx->prod));
-  ctx->slot_used[slot] = true;
+  // Overlapped: the GEMM+RS kernel on the CUs the producer leaves (one
+  // workgroup per CU), so the reduction's waits cannot starve it.
   const int grid = std::min(total, o.consumer_cus > 0 ? o.consumer_cus : std::max(1, ctx->n_cu - pwg));
   if ((st = mark(o, 0, stream)) != SGT_OK) return st;
   HIP_TRY(launch_gemm_rs(a, grid, stream));
   if ((st = mark(o, 1, stream)) != SGT_OK) return st;
-  HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
-  HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
+  if ((st = join_paced_peers(ctx, stream)) != SGT_OK) return st;
   return finish(ctx, o, stream);
 }
 
@@ -941,17 +971,30 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
 }
 
 
-sgt_status sgt_moe_gemm_rs(sgt_ctx* ctx, const void* Hg, const void* W2, const float* gate, const int32_t* topk_ids,
-                           const int32_t* expert_off, const int32_t* row_token, const float* const* partials,
-                           float* Y, float* partial_out, float* C_shard, uint32_t* gflags, uint32_t* pflags, int W,
-                           int64_t T, int topk, int64_t I, int64_t H, int E, const sgt_opts* opts, void* stream_) {
+}  // extern "C"
+
+namespace {
+
+// MoE GEMM + ReduceScatter, shared by the resident and the paced entry points
+// (partials: what the reduction sums for each peer; peer_blocks == NULL: they
+// are resident and their flags preset, else the producer copies peer_blocks[p]
+// into partials[p] band by band at the link rate).
+sgt_status moe_gemm_rs_impl(sgt_ctx* ctx, const void* Hg, const void* W2, const float* gate, const int32_t* topk_ids,
+                            const int32_t* expert_off, const int32_t* row_token, const float* const* partials,
+                            const float* const* peer_blocks, float* Y, float* partial_out, float* C_shard,
+                            uint32_t* gflags, uint32_t* pflags, int W, int64_t T, int topk, int64_t I, int64_t H,
+                            int E, const sgt_opts* opts, void* stream_) {
   if (!ctx) return fail(SGT_EINVAL, "ctx is NULL");
   sgt_status st = check_opts(opts, W < 1 ? 1 : W);
   if (st != SGT_OK) return st;
   const sgt_opts& o = *opts;
   if (o.in_dtype != SGT_BF16) return fail(SGT_EUNSUPPORTED, "MoE takes bf16 rows and weights");
   if (o.out_dtype != SGT_F32) return fail(SGT_EUNSUPPORTED, "the combined partials are fp32");
-  if (o.peer_gbps > 0) return fail(SGT_EUNSUPPORTED, "the peers' partials are resident (peer_gbps must be 0)");
+  const bool paced = peer_blocks != nullptr;
+  if (!paced && o.peer_gbps > 0)
+    return fail(SGT_EUNSUPPORTED, "sgt_moe_gemm_rs takes resident peers; paced arrival is sgt_moe_gemm_rs_paced");
+  if (paced && o.producer == SGT_PROD_PRESET)
+    return fail(SGT_EINVAL, "sgt_moe_gemm_rs_paced needs a producer mode (CU or serial)");
   if (o.rs_tile != 0 && o.rs_tile != 128) return fail(SGT_EINVAL, "rs_tile %d (the combine tile is 128)", o.rs_tile);
   if (o.tile_waves != 0 && o.tile_waves != 8) return fail(SGT_EUNSUPPORTED, "tile_waves %d (8 only)", o.tile_waves);
   if (W < 1 || W > kMaxW) return fail(SGT_EINVAL, "W = %d outside [1, %d]", W, kMaxW);
@@ -972,9 +1015,16 @@ sgt_status sgt_moe_gemm_rs(sgt_ctx* ctx, const void* Hg, const void* W2, const f
       (reinterpret_cast<uintptr_t>(topk_ids) & 3u) || (reinterpret_cast<uintptr_t>(expert_off) & 3u) ||
       (reinterpret_cast<uintptr_t>(row_token) & 3u))
     return fail(SGT_EINVAL, "pointer not aligned (16 bytes for matrices and flags, 4 for tables)");
-  for (int p = 0; p < W; ++p)
-    if (p != o.rank && (!partials[p] || !aligned16(partials[p])))
-      return fail(SGT_EINVAL, "partials[%d] NULL or not 16-byte aligned", p);
+  for (int p = 0; p < W; ++p) {
+    if (p == o.rank) continue;
+    if (!partials[p] || !aligned16(partials[p]))
+      return fail(SGT_EINVAL, "%s[%d] NULL or not 16-byte aligned", paced ? "inbox" : "partials", p);
+    if (paced && (!peer_blocks[p] || !aligned16(peer_blocks[p])))
+      return fail(SGT_EINVAL, "peer_blocks[%d] NULL or not 16-byte aligned", p);
+  }
+  const int64_t band_bytes = (int64_t)128 * H * 4;
+  if (paced && ((int64_t)(W - 1) * ((T / W) / 128) > kItemsCap || (H + 127) / 128 > 65535))
+    return fail(SGT_EUNSUPPORTED, "too many bands for the producer");
   int64_t ng = 0, np = 0;
   sgt_opts o128 = o;
   o128.rs_tile = 128;
@@ -1037,13 +1087,49 @@ sgt_status sgt_moe_gemm_rs(sgt_ctx* ctx, const void* Hg, const void* W2, const f
   a.tiles_cap = (int32_t)ctx->mrs_tiles_cap; a.b_layout = o.b_layout;
   a.rs = rs;
 
-  // the peers' partials are resident: their flags take the epoch before the kernel
-  HIP_TRY(launch_rs_prepare(pflags, np, e, a.claim, stream));
-  const int grid = o.consumer_cus > 0 ? std::min(o.consumer_cus, ctx->n_cu) : ctx->n_cu;
+  if (!paced) {
+    // the peers' partials are resident: their flags take the epoch before the kernel
+    HIP_TRY(launch_rs_prepare(pflags, np, e, a.claim, stream));
+    const int grid = o.consumer_cus > 0 ? std::min(o.consumer_cus, ctx->n_cu) : ctx->n_cu;
+    if ((st = mark(o, 0, stream)) != SGT_OK) return st;
+    HIP_TRY(launch_moe_rs(a, grid, stream));
+    if ((st = mark(o, 1, stream)) != SGT_OK) return st;
+    return finish(ctx, o, stream);
+  }
+  int pwg = 0;
+  if ((st = launch_paced_peers(ctx, o, pflags, peer_blocks, partials, W, rs.rs_tm, rs.rs_tn, band_bytes, e, a.claim,
+                               stream, &pwg)) != SGT_OK)
+    return st;
+  const bool serial = o.producer == SGT_PROD_SERIAL;
+  const int avail = serial ? ctx->n_cu : std::max(1, ctx->n_cu - pwg);
+  const int grid = o.consumer_cus > 0 ? std::min(o.consumer_cus, avail) : avail;
   if ((st = mark(o, 0, stream)) != SGT_OK) return st;
   HIP_TRY(launch_moe_rs(a, grid, stream));
   if ((st = mark(o, 1, stream)) != SGT_OK) return st;
+  if (!serial && (st = join_paced_peers(ctx, stream)) != SGT_OK) return st;
   return finish(ctx, o, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+sgt_status sgt_moe_gemm_rs(sgt_ctx* ctx, const void* Hg, const void* W2, const float* gate, const int32_t* topk_ids,
+                           const int32_t* expert_off, const int32_t* row_token, const float* const* partials,
+                           float* Y, float* partial_out, float* C_shard, uint32_t* gflags, uint32_t* pflags, int W,
+                           int64_t T, int topk, int64_t I, int64_t H, int E, const sgt_opts* opts, void* stream) {
+  return moe_gemm_rs_impl(ctx, Hg, W2, gate, topk_ids, expert_off, row_token, partials, nullptr, Y, partial_out,
+                          C_shard, gflags, pflags, W, T, topk, I, H, E, opts, stream);
+}
+
+sgt_status sgt_moe_gemm_rs_paced(sgt_ctx* ctx, const void* Hg, const void* W2, const float* gate,
+                                 const int32_t* topk_ids, const int32_t* expert_off, const int32_t* row_token,
+                                 const float* const* peer_blocks, float* const* inbox, float* Y, float* partial_out,
+                                 float* C_shard, uint32_t* gflags, uint32_t* pflags, int W, int64_t T, int topk,
+                                 int64_t I, int64_t H, int E, const sgt_opts* opts, void* stream) {
+  if (!peer_blocks || !inbox) return fail(SGT_EINVAL, "NULL peer_blocks or inbox");
+  return moe_gemm_rs_impl(ctx, Hg, W2, gate, topk_ids, expert_off, row_token, inbox, peer_blocks, Y, partial_out,
+                          C_shard, gflags, pflags, W, T, topk, I, H, E, opts, stream);
 }
 
 }  // extern "C"

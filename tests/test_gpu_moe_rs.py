@@ -27,8 +27,9 @@ def ctx():
     c.close()
 
 
-def run_moe_rs(ctx, Hg, W2, gate, ids, off, rt, parts, rank, w_layout="kn", **kw):
-    """Upload, run sgt_moe_gemm_rs (blocking); return host (Y, P, C, gflags, pflags)."""
+def run_moe_rs(ctx, Hg, W2, gate, ids, off, rt, parts, rank, w_layout="kn", paced=False, **kw):
+    """Upload, run sgt_moe_gemm_rs (or the paced variant, whose peers' blocks arrive into an inbox);
+    return host (Y, P, C, gflags, pflags) and, when paced, the inbox."""
     W = len(parts)
     T, k = ids.shape
     H = W2.shape[2] if w_layout == "kn" else W2.shape[1]
@@ -40,10 +41,14 @@ def run_moe_rs(ctx, Hg, W2, gate, ids, off, rt, parts, rank, w_layout="kn", **kw
     gf = torch.zeros(max(ng, 4), dtype=torch.int32, device="cuda:0")
     pf = torch.zeros(max(npf, 4), dtype=torch.int32, device="cuda:0")
     dparts = [dev(p) if q != rank else None for q, p in enumerate(parts)]
+    inbox = [poison_like(torch.empty_like(p)) if p is not None else None for p in dparts] if paced else None
     ctx.moe_gemm_rs(dev(Hg), dev(W2), dev(gate), dev(ids), dev(off), dev(rt), dparts, Y, P, C, gf, pf, rank=rank,
-                    b_layout=w_layout, blocking=True, **kw)
+                    b_layout=w_layout, blocking=True, inbox=inbox, **kw)
     torch.cuda.synchronize()
-    return host(Y), host(P), host(C), host(gf)[:ng], host(pf)[:npf]
+    out = (host(Y), host(P), host(C), host(gf)[:ng], host(pf)[:npf])
+    if paced:
+        return out + ([host(x) if x is not None else None for x in inbox],)
+    return out
 
 
 def make(w, w_layout="kn", pow2_gates=False):
@@ -143,6 +148,39 @@ def test_moe_rs_takes_gpu_routing(ctx, orc):
     assert_close(C, orc.moe_gemm_rs(Hg, W2, gate, ids_o, off_o, rt_o, parts, 3), what="C", **TOL_BF16)
 
 
+@pytest.mark.parametrize("opts", [dict(producer="cu", peer_gbps=40.0, jitter_us=3.0, arrival_seed=2),
+                                  dict(producer="cu", peer_gbps=0.0, arrival_order="global", arrival_seed=5),
+                                  dict(producer="serial", peer_gbps=60.0)], ids=["cu-40gbps", "cu-unthrottled",
+                                                                                 "serial"])
+def test_moe_rs_paced_matches_resident_bits(ctx, orc, opts):
+    w = I.scaled(I.MOE_RS, T=1024, W=4, E=8, topk=2, I=128, H=264, seed_index=38)
+    Hg, W2, gate, logits, parts = make(w, "nk")
+    ids, off, rt = orc.moe_route(logits, 2)
+    a = run_moe_rs(ctx, Hg, W2, gate, ids, off, rt, parts, 2, "nk")
+    b = run_moe_rs(ctx, Hg, W2, gate, ids, off, rt, parts, 2, "nk", paced=True, **opts)
+    for x, y in zip(a[:3], b[:3]):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    for q in range(4):
+        if q != 2:
+            assert np.array_equal(b[5][q].view(np.uint32), parts[q].view(np.uint32)), "inbox %d" % q
+    nb = len(b[4]) // 4   # peer flags, one block per rank; this rank's own block is never sent
+    for q in range(4):
+        if q != 2:
+            assert (b[4][q * nb:(q + 1) * nb] == b[3][0]).all(), "peer %d flags" % q
+
+
+def test_moe_rs_paced_withheld_peer_times_out(ctx, orc):
+    w = I.scaled(I.MOE_RS, T=512, W=4, E=8, topk=2, I=64, H=128, seed_index=39)
+    Hg, W2, gate, logits, parts = make(w)
+    ids, off, rt = orc.moe_route(logits, 2)
+    with pytest.raises(sgt.SgtError) as ei:
+        run_moe_rs(ctx, Hg, W2, gate, ids, off, rt, parts, 0, paced=True, withhold_peer=1, timeout_ms=20.0)
+    assert ei.value.status == sgt.SGT_ETIMEDOUT
+    # the context stays usable
+    _, _, C, _, _ = run_moe_rs(ctx, Hg, W2, gate, ids, off, rt, parts, 0)
+    assert_close(C, orc.moe_gemm_rs(Hg, W2, gate, ids, off, rt, parts, 0), what="C", **TOL_BF16)
+
+
 def test_moe_rs_bad_args(ctx, orc):
     w = I.scaled(I.MOE_RS, T=512, W=4, E=8, topk=2, I=64, H=128, seed_index=37)
     Hg, W2, gate, logits, parts = make(w)
@@ -150,9 +188,12 @@ def test_moe_rs_bad_args(ctx, orc):
     with pytest.raises(sgt.SgtError) as ei:      # T/W not a multiple of 128
         run_moe_rs(ctx, Hg[:2 * 384], W2, gate[:384], ids[:384], off, rt[:768], parts, 0)
     assert ei.value.status == sgt.SGT_EINVAL
-    with pytest.raises(sgt.SgtError) as ei:      # paced peers are not supported here
+    with pytest.raises(sgt.SgtError) as ei:      # paced peers go through the paced entry point
         run_moe_rs(ctx, Hg, W2, gate, ids, off, rt, parts, 0, peer_gbps=10.0)
     assert ei.value.status == sgt.SGT_EUNSUPPORTED
+    with pytest.raises(sgt.SgtError) as ei:      # the paced entry point needs a producer mode
+        run_moe_rs(ctx, Hg, W2, gate, ids, off, rt, parts, 0, paced=True, producer="preset")
+    assert ei.value.status == sgt.SGT_EINVAL
 
 
 @pytest.mark.slow
