@@ -93,31 +93,32 @@ def _events(n, torch):
 def timed(fn, steps, warmup, torch, ctx):
     """Run fn(i, events) warmup times, then two blocks of `steps` calls.
 
-    The first block passes no events: its wall time between two synchronizations is the step time (a timing
-    event recorded around every call costs the stream up to tens of microseconds per call, so it is kept out
-    of the step).  The second block records HIP events around every consumer launch for the kernel times.
+    The first block records HIP events around every consumer launch (the kernel times).  The second passes
+    no events: its wall time between two synchronizations is the step time (a timing event recorded around
+    every call costs the stream up to tens of microseconds per call, so it is kept out of the step; running
+    it second also lets the clocks settle under the load first).
     Returns (ms per step, mean consumer-kernel ms, per-call kernel ms).
     """
     for i in range(warmup):
         fn(i, None)
     torch.cuda.synchronize()
     ctx.sync()
+    evk = _events(steps, torch)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        fn(warmup + i, evk[i])
+    torch.cuda.synchronize()
+    ctx.sync()
+    kern = [a.elapsed_time(b) for a, b in evk]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
     for i in range(steps):
-        fn(warmup + i, None)
+        fn(warmup + steps + i, None)
     t1.record()
     torch.cuda.synchronize()
     ctx.sync()
     step_ms = t0.elapsed_time(t1) / steps
-    evk = _events(steps, torch)
-    torch.cuda.synchronize()
-    for i in range(steps):
-        fn(warmup + steps + i, evk[i])
-    torch.cuda.synchronize()
-    ctx.sync()
-    kern = [a.elapsed_time(b) for a, b in evk]
     return step_ms, statistics.mean(kern), kern
 
 
