@@ -231,6 +231,58 @@ def cpu_baseline(shards, B, M, N, K, seconds: float, b_layout: str = "kn"):
             "seconds": dt}
 
 
+def bench_ag_other(ctx, up, args, torch, sgt, I, lay):
+    """The other AllGather workloads: the Qwen3-32B MLP share at 50 GB/s per peer (the link floor exceeds the
+    GEMM, so E is bounded well below 1) and the tiny fp32 case (launch-bound)."""
+    out = {}
+    for w, kw in ((I.QWEN_AG, dict(b_layout=lay)), (I.TINY, dict(b_layout="kn"))):
+        shards_h, B_h = I.make_ag(w, B_layout=kw["b_layout"])
+        shards = [up(x) for x in shards_h]
+        B = up(B_h)
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        Ag = torch.empty((w.M, w.K), dtype=dt, device="cuda:0")
+        C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda:0")
+        fr = getattr(w, "flag_rows", 0)
+        flags = torch.zeros(sgt.ag_flag_count(w.W, w.M, w.K, flag_rows=fr), dtype=torch.int32, device="cuda:0")
+        link = dict(peer_gbps=w.peer_gbps, jitter_us=w.jitter_us, flag_rows=fr)
+        if w is I.TINY:
+            link["arrival_order"] = "global"
+
+        def ag(producer, **k2):
+            def fn(i, ev):
+                ctx.ag_gemm(shards, B, Ag, C, flags, rank=0, producer=producer, consumer_events=ev, **kw, **k2)
+            return fn
+        over_ms, _, over_l = timed(lambda i, ev: ag("cu", arrival_seed=i + 1, **link)(i, ev), args.steps,
+                                   args.warmup, torch, ctx)
+        n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+        ov_l, al_l = pairs(lambda i, ev: ag("cu", arrival_seed=500 + i, **link)(i, ev),
+                           ag("preset", consumer_cus=n_cu - max(8, n_cu // 8)), args.steps, torch, ctx)
+        assert torch.equal(Ag.view(torch.int16 if w.dtype == "bf16" else torch.int32),
+                           torch.cat(shards).view(torch.int16 if w.dtype == "bf16" else torch.int32)), w.name
+        floor_us = (w.M // w.W) * w.K * (2 if w.dtype == "bf16" else 4) / (w.peer_gbps * 1e9) * 1e6 \
+            if w.peer_gbps else 0.0
+        flops = 2.0 * w.M * w.N * w.K
+        al = statistics.median(al_l)
+        bm = 256 if w.dtype == "bf16" else 64
+        grid = n_cu - max(8, n_cu // 8)
+        tiles = -(-w.M // bm) * -(-w.N // bm)
+        out[w.name] = {
+            "M": w.M, "K": w.K, "N": w.N, "W": w.W, "dtype": w.dtype, "peer_gbps": w.peer_gbps or None,
+            "jitter_us": w.jitter_us, "step_ms": over_ms, "tflops_step": flops / (over_ms * 1e-3) / 1e12,
+            "overlapped_kernel_ms": spread(over_l), "pairs_alone_kernel_ms": spread(al_l),
+            "overlap_efficiency": al / statistics.median(ov_l),
+            "overlap_efficiency_max": (al * 1e3 / max(al * 1e3, floor_us + al * 1e3 * grid / tiles)
+                                       if floor_us else 1.0),
+            "link_floor_us": floor_us,
+        }
+        del shards, B, Ag, C, flags
+    out["note"] = ("overlap_efficiency_max estimates the ceiling: the GEMM alone over the link floor plus one "
+                   "tile time (the last panels cannot land earlier and then take a tile time; tiles that run "
+                   "alone at the end run faster, so a measured value can exceed it slightly); "
+                   "the tiny fp32 case is latency-bound and checked mainly for correctness")
+    return out
+
+
 def bench_moe(ctx, up, args, torch, sgt, I, lay):
     """MoE AllGather + grouped GEMM (T 4096 tokens in 8 shards, H 2048, I 768, 64 experts, top-8, Zipf-skewed
     logits), overlapped at 50 GB/s per simulated peer; the grouped consumer's MFMA and HBM roofline fractions."""
@@ -596,6 +648,8 @@ def main():
         assert torch.equal(inbox[(rank + 1) % r.W], parts[(rank + 1) % r.W]), "paced inbox mismatch"
         del inbox, tr
         del A, Brs, parts, P, Cs, Cg
+
+    detail["ag_other_workloads"] = bench_ag_other(ctx, up, args, torch, sgt, I, lay)
 
     if not args.no_moe:
         detail["moe_ag_grouped"], tables = bench_moe(ctx, up, args, torch, sgt, I, lay)
