@@ -330,6 +330,53 @@ SGT_API sgt_status sgt_moe_gemm_rs_paced(sgt_ctx* ctx, const void* Hg, const voi
  * signal tile. */
 SGT_API int64_t sgt_moe_trace_words(int W, int64_t T, int64_t H, int64_t I, int E, int topk, const sgt_opts* opts);
 
+/*
+ * Stand-alone AllGather, flag-based (Triton-distributed semantics page,
+ * "Producer-consumer model", "Signal-based synchronization"; paper summary,
+ * "Method": intra-node AllGather by a producer, pull mode).
+ *   gathered (M x K) = the W row shards shards[0..W-1] ((M/W) x K each) stacked
+ *   in rank order, moved in chunks of flag_rows rows (the signal tiles of the
+ *   AllGather+GEMM plan, sgt_ag_flag_count with N = 0); after each chunk the
+ *   producer releases its flag (as sgt_ag_gemm, same pacing options: peer_gbps,
+ *   jitter_us, arrival_seed, arrival_order, withhold_peer; the local shard
+ *   first, unpaced).  The receiving side waits for every flag in arrival order
+ *   (producer_cus / consumer_cus workgroups; 0 = max(8, CUs / 8)).
+ * Element size from opts->in_dtype (SGT_BF16: 2 bytes, SGT_F32: 4).  A chunk
+ * (flag_rows x K elements) must be a multiple of 16 bytes.  Modes SGT_PROD_CU
+ * (producer on the context's stream, receiver on `stream`) or SGT_PROD_SERIAL;
+ * SGT_PROD_PRESET is SGT_EINVAL.  opts->trace (optional, 2 words per chunk):
+ * {tick the producer began the chunk, tick the receiver saw its flag}.
+ * Errors as sgt_ag_gemm; a withheld peer gives SGT_ETIMEDOUT with the flag index.
+ */
+SGT_API sgt_status sgt_allgather(sgt_ctx* ctx, const void* const* shards, void* gathered, uint32_t* flags, int W,
+                                 int64_t M, int64_t K, const sgt_opts* opts, void* stream);
+
+/*
+ * Low-latency (LL) AllGather (paper summary, "Method": for short messages the
+ * AllGather stores data and flag together in 8-byte blocks and spins on them,
+ * saving the signal operation of every transfer).
+ *   LL packet: an aligned 8-byte word, payload dword first (bits 0..31), the
+ *   call's epoch second (bits 32..63).  ll_buf (sgt_ll_buffer_bytes() bytes,
+ *   16-byte aligned, zeroed once before first use like flags) receives peer
+ *   p's shard as packets: chunk c (flag_rows rows, c over the gathered rows)
+ *   at byte offset 2 * c * chunk_bytes, payload dword i of the chunk in word i.
+ *   The producer (simulated peers) writes the remote chunks' packets, paced at
+ *   opts->peer_gbps per peer counted on the packets (twice the payload); the
+ *   receiver polls the packets until each holds the epoch and unpacks them
+ *   into gathered, and copies the local shard; no flag is stored or read.
+ *   On return gathered is as for sgt_allgather and every remote chunk's packets
+ *   hold {payload, epoch}; the local shard's slot is untouched.
+ * Options, modes, requirements and trace as sgt_allgather (2 * chunk < 2^31).
+ * A withheld peer gives SGT_ETIMEDOUT; its "flag index" is then the index of
+ * the first missing 8-byte packet in ll_buf.
+ */
+SGT_API sgt_status sgt_ll_allgather(sgt_ctx* ctx, const void* const* shards, void* ll_buf, void* gathered, int W,
+                                    int64_t M, int64_t K, const sgt_opts* opts, void* stream);
+
+/* Bytes of the LL receive buffer of an sgt_ll_allgather call (2 * M * K *
+ * element size), or -1 for an invalid shape or options. */
+SGT_API int64_t sgt_ll_buffer_bytes(int W, int64_t M, int64_t K, const sgt_opts* opts);
+
 /* Words of the optional trace buffer for an AllGather call: per consumer tile
  * 4 x uint64 {wait start, flag seen, tile end, workgroup}; then per signal tile
  * 1 x uint64 release time.  Times are the 100 MHz constant GPU clock.

@@ -11,6 +11,10 @@ Functions and the passage each follows (page titles as on the pages):
 * ``allgather``      -- Triton-distributed semantics page, "AllGather + GEMM overlap":
                         the producer gathers every PE's tiles into one buffer.
 * ``ag_gemm``        -- same section: C = AllGather(A) * B_local.
+* ``ll_pack`` / ``ll_buffer`` -- paper summary, "Method" (low-latency protocol for
+                        short messages): data and flag stored together in 8-byte
+                        blocks; the packets an LL AllGather leaves in the receiver's
+                        buffer.
 * ``gemm_rs``        -- Triton-distributed semantics page, "GEMM + ReduceScatter overlap";
                         Triton-distributed paper summary, "Method" (intra-node
                         ReduceScatter in push mode): each rank reduces its own row block.
@@ -65,6 +69,7 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         P, I64, I32, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
         lib.orc_allgather.argtypes = [P, I32, I64, I64, P]
+        lib.orc_ll_pack.argtypes = [P, I64, ctypes.c_uint32, P]
         lib.orc_gemm_rows.argtypes = [P, I32, P, I32, I32, I64, I64, I64, P, I64, P, I32]
         lib.orc_gemm_rs.argtypes = [P, I32, P, I32, I32, I64, I64, I64, P, I32, I32, P, I64, P, I32]
         lib.orc_moe_route.argtypes = [P, I64, I32, I32, P, P, P]
@@ -120,6 +125,30 @@ def allgather(shards) -> np.ndarray:
     R, K = shards[0].shape
     out = np.empty((R * len(shards), K), dtype=shards[0].dtype)
     _load().orc_allgather(_ptr_array(shards), len(shards), R, K * shards[0].itemsize, _ptr(out))
+    return out
+
+
+def ll_pack(payload: np.ndarray, epoch: int) -> np.ndarray:
+    """Low-latency packets of a payload (any dtype, a whole number of 4-byte words): one uint64
+    per payload word, the word in bits 0..31 and the epoch in bits 32..63."""
+    words = np.ascontiguousarray(payload).reshape(-1).view(np.uint32)
+    out = np.empty(words.size, dtype=np.uint64)
+    _load().orc_ll_pack(_ptr(words), words.size, int(epoch), _ptr(out))
+    return out
+
+
+def ll_buffer(shards, rank: int, epoch: int, chunk_rows: int, before: np.ndarray = None) -> np.ndarray:
+    """Expected LL receive buffer after an LL AllGather (as uint64 words): each remote shard's
+    rows, chunk by chunk (chunk_rows rows, in gathered-row order), as packets of `epoch`; the
+    local shard's slot keeps what it held (`before`, zeros by default)."""
+    R = shards[0].shape[0]
+    assert R % chunk_rows == 0
+    out = np.zeros(sum(s.size * s.itemsize for s in shards) // 4, dtype=np.uint64) if before is None \
+        else np.array(before, dtype=np.uint64).reshape(-1)
+    per = shards[0].size * shards[0].itemsize // 4
+    for p, s in enumerate(shards):
+        if p != rank:
+            out[p * per:(p + 1) * per] = ll_pack(s, epoch)
     return out
 
 

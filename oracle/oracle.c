@@ -80,6 +80,13 @@ void orc_allgather(const void* const* shards, int W, int64_t rows_per_shard, int
     memcpy((char*)out + (size_t)p * rows_per_shard * row_bytes, shards[p], (size_t)(rows_per_shard * row_bytes));
 }
 
+/* Low-latency packets (paper summary, "Method": for short messages data and
+ * flag share one 8-byte block): word i = the payload's 4-byte word i in the
+ * low half and the flag value (the call's epoch) in the high half. */
+void orc_ll_pack(const uint32_t* payload, int64_t n_words, uint32_t epoch, uint64_t* out) {
+  for (int64_t i = 0; i < n_words; ++i) out[i] = ((uint64_t)epoch << 32) | (uint64_t)payload[i];
+}
+
 /* One output row: c[j] = sum_{k ascending} a[k] * B(k, j), all in double. */
 static void gemm_row(const void* a_row, int a_dt, const void* B, int b_dt, int b_layout, int64_t K, int64_t N,
                      double* c) {

@@ -90,9 +90,13 @@ def lib() -> ctypes.CDLL:
                                             ctypes.c_int, I64, I64, ctypes.c_int, ctypes.POINTER(Opts), P]
         L.sgt_moe_ag_gemm.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_int, I64, I64, I64, ctypes.c_int,
                                       ctypes.c_int, ctypes.POINTER(Opts), P]
+        L.sgt_allgather.argtypes = [P, P, P, P, ctypes.c_int, I64, I64, ctypes.POINTER(Opts), P]
+        L.sgt_ll_allgather.argtypes = [P, P, P, P, ctypes.c_int, I64, I64, ctypes.POINTER(Opts), P]
+        L.sgt_ll_buffer_bytes.argtypes = [ctypes.c_int, I64, I64, ctypes.POINTER(Opts)]
+        L.sgt_ll_buffer_bytes.restype = I64
         for f in ("sgt_ctx_create", "sgt_ctx_destroy", "sgt_sync", "sgt_ag_gemm", "sgt_rs_flag_count", "sgt_gemm_rs",
                   "sgt_gemm_rs_paced", "sgt_moe_ag_gemm", "sgt_moe_gemm_rs",
-                  "sgt_moe_gemm_rs_paced"):
+                  "sgt_moe_gemm_rs_paced", "sgt_allgather", "sgt_ll_allgather"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -212,6 +216,15 @@ def moe_trace_words(W: int, T: int, H: int, I: int, E: int, topk: int, **kw) -> 
     return int(n)
 
 
+def ll_buffer_bytes(W: int, M: int, K: int, **kw) -> int:
+    """Bytes of the LL receive buffer of an ll_allgather call (twice the gathered bytes)."""
+    o = make_opts(**kw)
+    n = lib().sgt_ll_buffer_bytes(W, M, K, ctypes.byref(o))
+    if n < 0:
+        raise SgtError(SGT_EINVAL, "invalid LL AllGather shape or options")
+    return int(n)
+
+
 def rs_flag_count(W: int, M: int, N: int, rs_tile: int = 0):
     o = make_opts(rs_tile=rs_tile)
     g, p = I64(), I64()
@@ -265,6 +278,31 @@ class Context:
         _check(lib().sgt_ag_gemm(self._h, ctypes.cast(ptrs, P), _dev_ptr(B, "B", dev),
                                  _dev_ptr(A_gathered, "A_gathered", dev), _dev_ptr(C, "C", dev),
                                  _dev_ptr(flags, "flags", dev), W, M, K, N, ctypes.byref(o), _stream_handle(stream)))
+
+    def allgather(self, shards: Sequence, gathered, flags, *, stream=None, **kw):
+        """Flag-based AllGather: gathered = stack(shards); one flag per chunk of flag_rows rows
+        (ag_flag_count with the same options).  Options as in sgt_opts."""
+        dev = gathered.device
+        W = len(shards)
+        M, K = gathered.shape[0], gathered.shape[1]
+        kw.setdefault("in_dtype", _dtype_code(gathered))
+        o = make_opts(**kw)
+        ptrs = (P * W)(*[_dev_ptr(a, "shards[%d]" % i, dev) for i, a in enumerate(shards)])
+        _check(lib().sgt_allgather(self._h, ctypes.cast(ptrs, P), _dev_ptr(gathered, "gathered", dev),
+                                   _dev_ptr(flags, "flags", dev), W, M, K, ctypes.byref(o), _stream_handle(stream)))
+
+    def ll_allgather(self, shards: Sequence, ll_buf, gathered, *, stream=None, **kw):
+        """Low-latency AllGather: the peers' chunks arrive as 8-byte {payload, epoch} packets in
+        ll_buf (ll_buffer_bytes bytes, zeroed once); gathered = stack(shards)."""
+        dev = gathered.device
+        W = len(shards)
+        M, K = gathered.shape[0], gathered.shape[1]
+        kw.setdefault("in_dtype", _dtype_code(gathered))
+        o = make_opts(**kw)
+        ptrs = (P * W)(*[_dev_ptr(a, "shards[%d]" % i, dev) for i, a in enumerate(shards)])
+        _check(lib().sgt_ll_allgather(self._h, ctypes.cast(ptrs, P), _dev_ptr(ll_buf, "ll_buf", dev),
+                                      _dev_ptr(gathered, "gathered", dev), W, M, K, ctypes.byref(o),
+                                      _stream_handle(stream)))
 
     def gemm_rs(self, A_local, B, partials: Sequence, partial_out, C_shard, gflags, pflags, *, stream=None, **kw):
         """GEMM + ReduceScatter: partial_out = A_local @ B (fp32); C_shard = partial_out[block rank] +

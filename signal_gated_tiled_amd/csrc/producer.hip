@@ -69,7 +69,8 @@ __global__ void __launch_bounds__(kProdThreads) ag_producer_kernel(uint32_t* fla
                                                                    const ProdItem* items, int n_items,
                                                                    int64_t tile_bytes, uint32_t epoch,
                                                                    int withhold_peer, uint64_t* trace_release,
-                                                                   uint64_t lead0, uint32_t* started) {
+                                                                   uint64_t lead0, uint32_t* started,
+                                                                   uint64_t* trace_issue) {
   __shared__ uint64_t t0, lead;
   if (threadIdx.x == 0) {
     t0 = clock_ticks();
@@ -88,6 +89,7 @@ __global__ void __launch_bounds__(kProdThreads) ag_producer_kernel(uint32_t* fla
       if (item.release > lead)
         while (clock_ticks() < t0 + item.release - lead) __builtin_amdgcn_s_sleep(4);
       c0 = clock_ticks();
+      if (trace_issue) trace_issue[2 * (int64_t)item.flag0] = c0;
     }
     __syncthreads();
     const bool coherent = copy_bytes<32>(item.dst, item.src, tile_bytes);
@@ -145,13 +147,13 @@ hipError_t launch_rs_prepare(uint32_t* pflags, int64_t n, uint32_t v, uint32_t* 
 
 hipError_t launch_ag_producer(uint32_t* flags, const ProdItem* items, int n_items,
                               int64_t tile_bytes, uint32_t epoch, int withhold_peer, uint64_t* trace_release, int grid,
-                              hipStream_t stream, uint32_t* started) {
+                              hipStream_t stream, uint32_t* started, uint64_t* trace_issue) {
   if (n_items <= 0) return hipSuccess;
   if (grid > n_items) grid = n_items;
   // first estimate of a tile's copy time: at 16 GB/s per workgroup (100 MHz ticks)
   const uint64_t lead0 = (uint64_t)(tile_bytes / 160) + 100;
   hipLaunchKernelGGL(ag_producer_kernel, dim3(grid), dim3(kProdThreads), 0, stream, flags, items, n_items, tile_bytes,
-                     epoch, withhold_peer, trace_release, lead0, started);
+                     epoch, withhold_peer, trace_release, lead0, started, trace_issue);
   return hipGetLastError();
 }
 

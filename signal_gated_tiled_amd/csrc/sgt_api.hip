@@ -24,7 +24,14 @@
 namespace sgt {
 hipError_t launch_ag_producer(uint32_t* flags, const ProdItem* items, int n_items,
                               int64_t tile_bytes, uint32_t epoch, int withhold_peer, uint64_t* trace_release, int grid,
-                              hipStream_t stream, uint32_t* started = nullptr);
+                              hipStream_t stream, uint32_t* started = nullptr, uint64_t* trace_issue = nullptr);
+hipError_t launch_ll_producer(const ProdItem* items, int n_items, int64_t chunk_bytes, uint32_t epoch,
+                              int withhold_peer, uint64_t lead, uint64_t* trace, int grid, hipStream_t stream);
+hipError_t launch_ll_receive(const ProdItem* items, int n_items, int64_t chunk_bytes, uint32_t epoch, int rank,
+                             uint64_t timeout_ticks, uint32_t* status, uint64_t* trace, int grid, hipStream_t stream);
+hipError_t launch_ag_flag_wait(const ProdItem* items, int n_items, const uint32_t* flags, uint32_t epoch,
+                               uint64_t timeout_ticks, uint32_t* status, uint64_t* trace, int grid,
+                               hipStream_t stream);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
 hipError_t launch_rs_prepare(uint32_t* pflags, int64_t n, uint32_t v, uint32_t* counter, hipStream_t stream);
 hipError_t launch_ag_consumer(const AgArgs& a, int in_dtype, int grid, hipStream_t stream);
@@ -1130,6 +1137,127 @@ sgt_status sgt_moe_gemm_rs_paced(sgt_ctx* ctx, const void* Hg, const void* W2, c
   if (!peer_blocks || !inbox) return fail(SGT_EINVAL, "NULL peer_blocks or inbox");
   return moe_gemm_rs_impl(ctx, Hg, W2, gate, topk_ids, expert_off, row_token, inbox, peer_blocks, Y, partial_out,
                           C_shard, gflags, pflags, W, T, topk, I, H, E, opts, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Stand-alone AllGather, flag-based (ll_buf == NULL) or low-latency (LL).
+// Chunks are the signal tiles of the AllGather+GEMM plan (flag_rows rows).
+// Flag-based: the producer copies each chunk into the gathered buffer and
+// releases its flag; the receiving side waits on the flags in arrival order.
+// LL: the producer writes each remote chunk as packets into ll_buf (chunk c at
+// byte 2 * c * chunk_bytes); the receiver spins on the packets and unpacks
+// them into the gathered buffer, and copies the local shard itself.
+sgt_status allgather_impl(sgt_ctx* ctx, const void* const* shards, void* gathered, uint32_t* flags, void* ll_buf,
+                          bool ll, int W, int64_t M, int64_t K, const sgt_opts* opts, void* stream_) {
+  if (!ctx) return fail(SGT_EINVAL, "ctx is NULL");
+  sgt_status st = check_opts(opts, W < 1 ? 1 : W);
+  if (st != SGT_OK) return st;
+  const sgt_opts& o = *opts;
+  if (o.producer == SGT_PROD_PRESET) return fail(SGT_EINVAL, "an AllGather needs a producer mode (CU or serial)");
+  AgPlan p;
+  if ((st = plan_ag(W, M, K, 0, o, &p)) != SGT_OK) return st;
+  const int esz = elem_bytes(o.in_dtype);
+  const int64_t chunk = p.flag_rows * K * esz;
+  if (chunk % 16) return fail(SGT_EINVAL, "a chunk (flag_rows x K elements = %lld bytes) must be a multiple of 16",
+                              (long long)chunk);
+  if (ll && 2 * chunk >= ((int64_t)1 << 31)) return fail(SGT_EUNSUPPORTED, "LL chunk of 1 GiB or more");
+  if (M > 0) {
+    if (!shards) return fail(SGT_EINVAL, "shards is NULL");
+    for (int q = 0; q < W; ++q)
+      if (!shards[q] || !aligned16(shards[q])) return fail(SGT_EINVAL, "shards[%d] NULL or not 16-byte aligned", q);
+    if (!gathered || !aligned16(gathered)) return fail(SGT_EINVAL, "gathered NULL or not 16-byte aligned");
+    if (!ll && (!flags || !aligned16(flags))) return fail(SGT_EINVAL, "flags NULL or not 16-byte aligned");
+    if (ll && (!ll_buf || !aligned16(ll_buf))) return fail(SGT_EINVAL, "ll_buf NULL or not 16-byte aligned");
+  }
+  std::lock_guard<std::mutex> lock(ctx->mu);
+  DeviceGuard g(ctx->device);
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const uint32_t e = ++ctx->epoch;
+  if (M == 0) return SGT_OK;
+
+  int s_recv, s_prod;
+  if ((st = next_slot(ctx, &s_recv)) != SGT_OK) return st;
+  if ((st = next_slot(ctx, &s_prod)) != SGT_OK) return st;
+  ProdItem* recv = ctx->h_items[s_recv];
+  ProdItem* prod = ctx->h_items[s_prod];
+  const int n = build_schedule(p, W, o.rank, K, esz, o, shards, gathered, recv, /*local_first=*/true);
+  int n_prod = 0;
+  if (ll) {
+    // producer: the remote chunks into their packets; receiver: packets (or
+    // the local shard) into the gathered rows, in the same order
+    for (int i = 0; i < n; ++i) {
+      if ((int)recv[i].peer == o.rank) continue;
+      ProdItem it = recv[i];
+      it.dst = static_cast<char*>(ll_buf) + (int64_t)it.flag0 * 2 * chunk;
+      prod[n_prod++] = it;
+      recv[i].src = it.dst;
+    }
+  } else {
+    std::copy(recv, recv + n, prod);
+    n_prod = n;
+  }
+  const int pwg = std::min(default_producer_wgs(o, ctx->n_cu), std::max(n_prod, 1));
+  const int rgrid = std::min(n, o.consumer_cus > 0 ? o.consumer_cus : default_producer_wgs(o, ctx->n_cu));
+  const bool serial = o.producer == SGT_PROD_SERIAL;
+  hipStream_t ps = serial ? stream : ctx->prod;
+  if (!serial) {
+    HIP_TRY(hipEventRecord(ctx->ev_fork, stream));
+    HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
+  }
+  if (n_prod > 0) {
+    HIP_TRY(hipMemcpyAsync(ctx->d_items[s_prod], prod, n_prod * sizeof(ProdItem), hipMemcpyHostToDevice, ps));
+    if (ll) {
+      // start a chunk's writes about one write time before its release (at
+      // about 24 GB/s per workgroup: 240 bytes per 10 ns tick)
+      const uint64_t lead = (uint64_t)(2 * chunk / 240) + 100;
+      HIP_TRY(launch_ll_producer(ctx->d_items[s_prod], n_prod, chunk, e, o.withhold_peer, lead, o.trace, pwg, ps));
+    } else {
+      HIP_TRY(launch_ag_producer(flags, ctx->d_items[s_prod], n_prod, chunk, e, o.withhold_peer, nullptr, pwg, ps,
+                                 nullptr, o.trace));
+    }
+  }
+  HIP_TRY(hipEventRecord(ctx->slot_ev[s_prod], ps));
+  ctx->slot_used[s_prod] = true;
+  HIP_TRY(hipMemcpyAsync(ctx->d_items[s_recv], recv, n * sizeof(ProdItem), hipMemcpyHostToDevice, stream));
+  if ((st = mark(o, 0, stream)) != SGT_OK) return st;
+  if (ll)
+    HIP_TRY(launch_ll_receive(ctx->d_items[s_recv], n, chunk, e, o.rank, timeout_ticks(o), ctx->d_status, o.trace,
+                              rgrid, stream));
+  else
+    HIP_TRY(launch_ag_flag_wait(ctx->d_items[s_recv], n, flags, e, timeout_ticks(o), ctx->d_status, o.trace, rgrid,
+                                stream));
+  if ((st = mark(o, 1, stream)) != SGT_OK) return st;
+  HIP_TRY(hipEventRecord(ctx->slot_ev[s_recv], stream));
+  ctx->slot_used[s_recv] = true;
+  if (!serial) {
+    HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
+    HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
+  }
+  return finish(ctx, o, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t sgt_ll_buffer_bytes(int W, int64_t M, int64_t K, const sgt_opts* opts) {
+  if (!opts || check_opts(opts, W < 1 ? 1 : W) != SGT_OK) return -1;
+  AgPlan p;
+  if (plan_ag(W, M, K, 0, *opts, &p) != SGT_OK) return -1;
+  return 2 * M * K * elem_bytes(opts->in_dtype);
+}
+
+sgt_status sgt_allgather(sgt_ctx* ctx, const void* const* shards, void* gathered, uint32_t* flags, int W, int64_t M,
+                         int64_t K, const sgt_opts* opts, void* stream) {
+  return allgather_impl(ctx, shards, gathered, flags, nullptr, false, W, M, K, opts, stream);
+}
+
+sgt_status sgt_ll_allgather(sgt_ctx* ctx, const void* const* shards, void* ll_buf, void* gathered, int W, int64_t M,
+                            int64_t K, const sgt_opts* opts, void* stream) {
+  return allgather_impl(ctx, shards, gathered, nullptr, ll_buf, true, W, M, K, opts, stream);
 }
 
 }  // extern "C"

@@ -95,3 +95,7 @@ def test_flag_counts_and_argument_errors():
     with pytest.raises(sgt.SgtError):
         sgt.rs_flag_count(4, 1024, 256, rs_tile=96)                     # must divide 256
     assert sgt.ag_panel_rows(8, 16384, 8192, 3584) == 256
+    assert sgt.ll_buffer_bytes(8, 128, 8192, flag_rows=2) == 2 * 128 * 8192 * 2   # packets: twice the payload
+    assert sgt.ll_buffer_bytes(4, 24, 40, in_dtype=sgt.SGT_F32, flag_rows=3) == 2 * 24 * 40 * 4
+    with pytest.raises(sgt.SgtError):
+        sgt.ll_buffer_bytes(8, 100, 64)                                 # M % W != 0

@@ -373,3 +373,56 @@ def test_moe_rs_planted_mistake_is_caught(orc):
     bad[3, 0] = 1
     with pytest.raises(ValueError):
         orc.moe_gemm_rs_p(Hg, W2, gate, bad, off, rt, np.arange(8))
+
+
+# ---- low-latency packets (paper summary, "Method": data and flag share one 8-byte block) ----
+
+def test_ll_pack_word_is_epoch_high_payload_low(orc):
+    # closed form with Python integers: word = epoch * 2^32 + payload word
+    rng = np.random.default_rng(11)
+    payload = rng.integers(0, 2**32, size=37, dtype=np.uint64).astype(np.uint32)
+    for epoch in (1, 7, 2**32 - 1):
+        got = orc.ll_pack(payload, epoch)
+        assert got.dtype == np.uint64 and got.size == payload.size
+        assert [int(v) for v in got] == [epoch * 2**32 + int(w) for w in payload]
+
+
+def test_ll_pack_bytes_of_a_worked_example(orc):
+    # two payload words, epoch 5: little-endian bytes, payload first, flag second
+    got = orc.ll_pack(np.array([0x11223344, 0xAABBCCDD], np.uint32), 5).tobytes()
+    assert got == bytes([0x44, 0x33, 0x22, 0x11, 5, 0, 0, 0, 0xDD, 0xCC, 0xBB, 0xAA, 5, 0, 0, 0])
+
+
+def test_ll_pack_of_bf16_rows_keeps_element_pairs(orc):
+    # a bf16 payload packs two elements per word: the low half of each packet is
+    # the pair's bytes as laid out in memory, so unpacking the low halves of a
+    # row's packets gives the row back
+    row = np.arange(1, 9, dtype=np.uint16)
+    got = orc.ll_pack(row, 3)
+    assert np.array_equal((got & 0xFFFFFFFF).astype(np.uint32).view(np.uint16), row)
+    assert np.all(got >> 32 == 3)
+
+
+def test_ll_buffer_slots_follow_the_gathered_rows(orc):
+    rng = np.random.default_rng(12)
+    shards = [rng.integers(0, 2**16, size=(4, 6), dtype=np.uint64).astype(np.uint16) for _ in range(3)]
+    before = np.full(3 * 4 * 6 // 2, 99, np.uint64)
+    got = orc.ll_buffer(shards, rank=1, epoch=9, chunk_rows=2, before=before)
+    gathered = np.concatenate(shards)           # library routine for the row order
+    words = gathered.reshape(-1).view(np.uint32)
+    per = 4 * 6 // 2
+    for p in range(3):
+        seg = got[p * per:(p + 1) * per]
+        if p == 1:
+            assert np.all(seg == 99)              # the local slot is left as it was
+        else:
+            assert np.array_equal(seg & 0xFFFFFFFF, words[p * per:(p + 1) * per])
+            assert np.all(seg >> 32 == 9)
+
+
+def test_ll_planted_swap_is_caught(orc):
+    # a packer that put the flag in the low half would fail the closed form above
+    payload = np.array([1, 2, 3], np.uint32)
+    good = orc.ll_pack(payload, 4)
+    swapped = (good << np.uint64(32)) | (good >> np.uint64(32))
+    assert [int(v) for v in swapped] != [4 * 2**32 + int(w) for w in payload]
