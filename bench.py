@@ -283,6 +283,73 @@ def bench_ag_other(ctx, up, args, torch, sgt, I, lay):
     return out
 
 
+def bench_ll(ctx, up, args, torch, sgt, I):
+    """Low-latency (packet) AllGather against the flag-based one at decode sizes: Llama-3-70B hidden size
+    (K = 8192, bf16), W = 8, 1 to 1024 tokens per rank, chunks of 1 row (16 KiB) and of 4 rows (64 KiB),
+    32 or 96 workgroups for the simulated peers and as many for the receiver (96 lets the peers' side
+    deliver LL's doubled bytes at the 153.6 GB/s link rate).
+
+    Per call: the whole call's time (back to back, stream-ordered), the kernel's time, and from an
+    in-kernel trace the time from the producer's first write to the receiver's last chunk seen and the
+    per-chunk latency (remote chunks: producer's first write of the chunk to the receiver seeing all of it).
+    """
+    import numpy as np
+    out = {}
+    W, K = 8, 8192
+    for tokens in (1, 16, 128, 1024):
+        M = W * tokens
+        w = I.AGWorkload("ll", W=W, M=M, K=K, N=0, seed_index=6)
+        shards = [up(s) for s in I.make_ag(w)[0]]
+        ref = torch.cat(shards)
+        G = torch.empty((M, K), dtype=torch.bfloat16, device="cuda:0")
+        ll = torch.zeros(sgt.ll_buffer_bytes(W, M, K) // 8, dtype=torch.int64, device="cuda:0")
+        row = {"M": M, "K": K, "W": W, "tokens_per_rank": tokens, "payload_mib": M * K * 2 / 2**20}
+        best = {}
+        variants = [(fr, cus, link, gbps) for fr in sorted({1, min(tokens, 4)}) for cus in (32, 96)
+                    for link, gbps in (("unthrottled", 0.0), ("153.6GBps", 153.6))
+                    if cus == 96 or gbps == 0.0]
+        for fr, cus, link, gbps in variants:
+            n = M // fr
+            fl = torch.zeros(sgt.ag_flag_count(W, M, K, flag_rows=fr), dtype=torch.int32, device="cuda:0")
+            tr = torch.zeros(2 * n, dtype=torch.int64, device="cuda:0")
+            per_shard = tokens // fr
+            if True:
+                for kind in ("ll", "flag"):
+                    def call(i, ev, trace=0, kind=kind, gbps=gbps, fr=fr, fl=fl, cus=cus):
+                        kw = dict(rank=0, flag_rows=fr, peer_gbps=gbps, consumer_events=ev, trace=trace,
+                                  producer_cus=cus, consumer_cus=cus)
+                        if kind == "ll":
+                            ctx.ll_allgather(shards, ll, G, **kw)
+                        else:
+                            ctx.allgather(shards, G, fl, **kw)
+                    step_ms, _, kern = timed(call, args.steps, 5, torch, ctx)
+                    G.zero_()
+                    call(0, None, trace=tr.data_ptr())
+                    torch.cuda.synchronize()
+                    ctx.sync()
+                    assert torch.equal(G, ref), "gathered rows differ (%s, %d tokens)" % (kind, tokens)
+                    t = tr.cpu().numpy().reshape(n, 2).astype(np.float64)
+                    remote = np.arange(n) >= per_shard          # rank 0: chunks past the first shard
+                    lat = (t[remote, 1] - t[remote, 0]) / 100.0  # 100 MHz ticks -> us
+                    r = {"call_us": step_ms * 1e3,
+                         "kernel_us": {k: v * 1e3 if k != "n" else v for k, v in spread(kern).items()},
+                         "first_write_to_last_seen_us": (t[:, 1].max() - t[:, 0].min()) / 100.0,
+                         "chunk_latency_us": spread(list(lat))}
+                    key = "%s_%s" % (kind, link)
+                    row["%s_chunk%dkib_wg%d" % (key, fr * K * 2 // 1024, cus)] = r
+                    if key not in best or r["first_write_to_last_seen_us"] < best[key][2]:
+                        best[key] = (fr * K * 2 // 1024, cus, r["first_write_to_last_seen_us"],
+                                     r["chunk_latency_us"]["median"], r["call_us"])
+        row["best"] = {k: {"chunk_kib": v[0], "workgroups_each_side": v[1], "first_write_to_last_seen_us": v[2],
+                           "chunk_latency_median_us": v[3], "call_us": v[4]} for k, v in best.items()}
+        out["ll_ag_decode_%dtok" % tokens] = row
+    out["note"] = ("LL packets carry their epoch, so the receiver reads data and arrival in one load; the flag path "
+                   "copies, waits for the stores' acknowledgement, publishes a flag, and the receiver polls it. "
+                   "LL moves twice the bytes on the link and unpacks on the receiver. call_us is host-bound "
+                   "(argument marshalling and one launch) at these sizes; the in-kernel figures compare the methods.")
+    return out
+
+
 def bench_moe(ctx, up, args, torch, sgt, I, lay):
     """MoE AllGather + grouped GEMM (T 4096 tokens in 8 shards, H 2048, I 768, 64 experts, top-8, Zipf-skewed
     logits), overlapped at 50 GB/s per simulated peer; the grouped consumer's MFMA and HBM roofline fractions."""
@@ -411,6 +478,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rs", action="store_true", help="skip the GEMM+ReduceScatter workload")
     ap.add_argument("--no-moe", action="store_true", help="skip the MoE AllGather + grouped GEMM workload")
+    ap.add_argument("--no-ll", action="store_true", help="skip the low-latency AllGather comparison")
+    ap.add_argument("--ll-only", action="store_true", help="only the low-latency AllGather comparison")
     ap.add_argument("--b-layout", default="nk", choices=["kn", "nk"],
                     help="B as N x K (a Linear layer's weight, default) or K x N")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -446,6 +515,11 @@ def main():
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
+
+    if args.ll_only:
+        with sgt.Context(0) as c:
+            print(json.dumps({"ll_allgather": bench_ll(c, up, args, torch, sgt, I)}))
+        return
 
     w = I.LLAMA_AG
     W, M, K, N = w.W, w.M, w.K, w.N
@@ -650,6 +724,8 @@ def main():
         del A, Brs, parts, P, Cs, Cg
 
     detail["ag_other_workloads"] = bench_ag_other(ctx, up, args, torch, sgt, I, lay)
+    if not args.no_ll:
+        detail["ll_allgather"] = bench_ll(ctx, up, args, torch, sgt, I)
 
     if not args.no_moe:
         detail["moe_ag_grouped"], tables = bench_moe(ctx, up, args, torch, sgt, I, lay)

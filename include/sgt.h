@@ -22,9 +22,10 @@
  *     pointers (A_shards, partials, X_shards) are HOST arrays of W device
  *     pointers.  Matrices are row-major and densely packed.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
- *     stream) unless opts->blocking is set.  The library allocates nothing per
- *     call: it owns only a few streams, events, a device status word and
- *     small schedule tables created with the context.
+ *     stream) unless opts->blocking is set.  The library allocates no device
+ *     memory per call: it owns only a few streams, events, a device status
+ *     word and small schedule tables created with the context (the MoE calls'
+ *     tables grow on demand).
  *   - Arguments are validated before anything is launched; a bad argument
  *     returns SGT_EINVAL (or SGT_EUNSUPPORTED) and launches nothing.
  *     sgt_last_error() then describes the problem.
@@ -340,11 +341,12 @@ SGT_API int64_t sgt_moe_trace_words(int W, int64_t T, int64_t H, int64_t I, int 
  *   producer releases its flag (as sgt_ag_gemm, same pacing options: peer_gbps,
  *   jitter_us, arrival_seed, arrival_order, withhold_peer; the local shard
  *   first, unpaced).  The receiving side waits for every flag in arrival order
- *   (producer_cus / consumer_cus workgroups; 0 = max(8, CUs / 8)).
+ *   (producer_cus / consumer_cus workgroups; 0 = max(8, CUs / 8)).  SGT_PROD_CU
+ *   runs both in one launch (the producer's workgroups beside the receiver's);
+ *   SGT_PROD_SERIAL runs the producer's launch, then the receiver's.
  * Element size from opts->in_dtype (SGT_BF16: 2 bytes, SGT_F32: 4).  A chunk
- * (flag_rows x K elements) must be a multiple of 16 bytes.  Modes SGT_PROD_CU
- * (producer on the context's stream, receiver on `stream`) or SGT_PROD_SERIAL;
- * SGT_PROD_PRESET is SGT_EINVAL.  opts->trace (optional, 2 words per chunk):
+ * (flag_rows x K elements) must be a multiple of 16 bytes, and at most 2^17
+ * chunks.  SGT_PROD_PRESET is SGT_EINVAL.  opts->trace (optional, 2 words per chunk):
  * {tick the producer began the chunk, tick the receiver saw its flag}.
  * Errors as sgt_ag_gemm; a withheld peer gives SGT_ETIMEDOUT with the flag index.
  */

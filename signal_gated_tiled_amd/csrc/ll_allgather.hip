@@ -42,16 +42,15 @@ __device__ inline __amdgpu_buffer_rsrc_t ll_rsrc(const void* base, uint32_t byte
 // writes start `lead` ticks before the item's release so that the chunk lands
 // about when the peer's link would have delivered it.  trace_issue (optional):
 // trace_issue[2 * chunk] = the tick the chunk's writes began.
-__global__ void __launch_bounds__(kLlThreads) ll_producer_kernel(const ProdItem* __restrict__ items, int n_items,
-                                                                 int64_t chunk_bytes, uint32_t epoch,
-                                                                 int withhold_peer, uint64_t lead,
-                                                                 uint64_t* trace_issue) {
+__device__ __forceinline__ void ll_produce(int first, int stride, const ProdItem* __restrict__ items, int n_items,
+                                           int64_t chunk_bytes, uint32_t epoch, int withhold_peer, uint64_t lead,
+                                           uint64_t* trace_issue) {
   __shared__ uint64_t t0;
   if (threadIdx.x == 0) t0 = clock_ticks();
   __syncthreads();
   const uint32_t cb = (uint32_t)chunk_bytes;
-  const uint32_t lane = threadIdx.x * 16u, stride = kLlThreads * 16u;
-  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+  const uint32_t lane = threadIdx.x * 16u, step = kLlThreads * 16u;
+  for (int it = first; it < n_items; it += stride) {
     const ProdItem item = items[it];
     if ((int)item.peer == withhold_peer) continue;  // uniform: the item is the workgroup's
     if (threadIdx.x == 0) {
@@ -64,14 +63,14 @@ __global__ void __launch_bounds__(kLlThreads) ll_producer_kernel(const ProdItem*
     const __amdgpu_buffer_rsrc_t rs = ll_rsrc(item.src, cb), rd = ll_rsrc(item.dst, 2u * cb);
     // 16 payload bytes -> two 16-byte lines of two packets each; offsets past
     // the chunk read zero and their stores are dropped by the range check
-    for (uint32_t b = 0; b < cb; b += stride * kLlUnroll) {
+    for (uint32_t b = 0; b < cb; b += step * kLlUnroll) {
       u32x4 v[kLlUnroll];
 #pragma unroll
       for (int u = 0; u < kLlUnroll; ++u)
-        v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, b + lane + (uint32_t)u * stride, 0, kCpolNt);
+        v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, b + lane + (uint32_t)u * step, 0, kCpolNt);
 #pragma unroll
       for (int u = 0; u < kLlUnroll; ++u) {
-        const uint32_t o = 2u * (b + lane + (uint32_t)u * stride);
+        const uint32_t o = 2u * (b + lane + (uint32_t)u * step);
         const u32x4 lo = {v[u].x, epoch, v[u].y, epoch};
         const u32x4 hi = {v[u].z, epoch, v[u].w, epoch};
         __builtin_amdgcn_raw_buffer_store_b128(lo, rd, o, 0, kCpolSc1);
@@ -105,16 +104,15 @@ __device__ inline void ll_copy_local(char* dst, const char* src, uint32_t bytes)
 // A wave whose budget expires records the packet in the status word; the
 // workgroup then stops at the item's end.  trace_seen (optional):
 // trace_seen[2 * chunk + 1] = the tick the whole chunk had been seen.
-__global__ void __launch_bounds__(kLlThreads) ll_receive_kernel(const ProdItem* __restrict__ items, int n_items,
-                                                                int64_t chunk_bytes, uint32_t epoch, int rank,
-                                                                uint64_t timeout_ticks, uint32_t* status,
-                                                                uint64_t* trace) {
+__device__ __forceinline__ void ll_receive(int first, int stride, const ProdItem* __restrict__ items, int n_items,
+                                           int64_t chunk_bytes, uint32_t epoch, int rank, uint64_t timeout_ticks,
+                                           uint32_t* status, uint64_t* trace) {
   __shared__ int failed;
   if (threadIdx.x == 0) failed = 0;
   __syncthreads();
   const uint32_t cb = (uint32_t)chunk_bytes, pb = 2u * cb;
-  const uint32_t lane = threadIdx.x * 16u, stride = kLlThreads * 16u;
-  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+  const uint32_t lane = threadIdx.x * 16u, step = kLlThreads * 16u;
+  for (int it = first; it < n_items; it += stride) {
     const ProdItem item = items[it];
     const int64_t chunk = item.flag0;
     if ((int)item.peer == rank) {
@@ -125,7 +123,7 @@ __global__ void __launch_bounds__(kLlThreads) ll_receive_kernel(const ProdItem* 
     const __amdgpu_buffer_rsrc_t rs = ll_rsrc(item.src, pb), rd = ll_rsrc(item.dst, cb);
     const uint64_t t0 = clock_ticks();
     bool good = true;
-    for (uint32_t b = 0; b < pb; b += stride * kLlUnroll) {
+    for (uint32_t b = 0; b < pb; b += step * kLlUnroll) {
       u32x4 v[kLlUnroll];
       // Two phases keep the polling traffic low while the chunk is still on
       // its way: first each lane polls one line of its pass, then it loads
@@ -136,7 +134,7 @@ __global__ void __launch_bounds__(kLlThreads) ll_receive_kernel(const ProdItem* 
 #pragma unroll
           for (int u = 0; u < kLlUnroll; ++u) {
             if (phase == 0 && u > 0) break;
-            const uint32_t o = b + lane + (uint32_t)u * stride;
+            const uint32_t o = b + lane + (uint32_t)u * step;
             v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, kCpolSc1);
             // past the chunk: nothing to wait for (the load read zero); bitwise
             // operators keep the checks free of branches and per-load waits
@@ -150,7 +148,7 @@ __global__ void __launch_bounds__(kLlThreads) ll_receive_kernel(const ProdItem* 
               int64_t at = -1;
               uint32_t seen = 0;
               for (int u = (phase == 0 ? 0 : kLlUnroll - 1); u >= 0; --u) {
-                const uint32_t o = b + lane + (uint32_t)u * stride;
+                const uint32_t o = b + lane + (uint32_t)u * step;
                 if (o < pb && !flag_is_set(v[u].y, epoch)) {
                   at = o;
                   seen = v[u].y;
@@ -172,7 +170,7 @@ __global__ void __launch_bounds__(kLlThreads) ll_receive_kernel(const ProdItem* 
 #pragma unroll
       for (int u = 0; u < kLlUnroll; ++u) {
         const u32x2 d = {v[u].x, v[u].z};
-        __builtin_amdgcn_raw_buffer_store_b64(d, rd, (b + lane + (uint32_t)u * stride) >> 1, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(d, rd, (b + lane + (uint32_t)u * step) >> 1, 0, 0);
       }
     }
     __syncthreads();
@@ -181,50 +179,30 @@ __global__ void __launch_bounds__(kLlThreads) ll_receive_kernel(const ProdItem* 
   }
 }
 
-// Receiving side of the flag-based AllGather: the producer has copied each
-// chunk into the gathered buffer and released its flag; workgroup g waits for
-// the flags of items g, g + G, ... in arrival order (wave 0 polls, then the
-// acquire).  trace (optional): trace[2 * chunk + 1] = the tick the flag was seen.
-__global__ void __launch_bounds__(64) ag_flag_wait_kernel(const ProdItem* __restrict__ items, int n_items, const uint32_t* flags,
-                                                          uint32_t epoch, uint64_t timeout_ticks, uint32_t* status,
-                                                          uint64_t* trace) {
-  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
-    const int64_t f = items[it].flag0;
-    if (!wait_flags_wave(flags, f, f + 1, epoch, timeout_ticks, status)) return;  // uniform (one wave)
-    if (trace && threadIdx.x == 0) trace[2 * f + 1] = clock_ticks();
-  }
+// Stand-alone LL AllGather in one launch: workgroups [0, n_prod_blocks) are
+// the simulated peers (items[0, n_prod)), the others the receiver
+// (items[n_prod, n_prod + n_recv)).  A launch with n_prod_blocks equal to its
+// grid is the peers alone, one with 0 the receiver alone.
+__global__ void __launch_bounds__(kLlThreads) ll_allgather_kernel(const ProdItem* __restrict__ items, int n_prod,
+                                                                  int n_recv, int n_prod_blocks, int64_t chunk_bytes,
+                                                                  uint32_t epoch, int withhold_peer, uint64_t lead,
+                                                                  int rank, uint64_t timeout_ticks, uint32_t* status,
+                                                                  uint64_t* trace) {
+  if ((int)blockIdx.x < n_prod_blocks)
+    ll_produce(blockIdx.x, n_prod_blocks, items, n_prod, chunk_bytes, epoch, withhold_peer, lead, trace);
+  else
+    ll_receive(blockIdx.x - n_prod_blocks, gridDim.x - n_prod_blocks, items + n_prod, n_recv, chunk_bytes, epoch,
+               rank, timeout_ticks, status, trace);
 }
 
 }  // namespace
 
-int ll_threads() { return kLlThreads; }
-
-hipError_t launch_ll_producer(const ProdItem* items, int n_items, int64_t chunk_bytes, uint32_t epoch,
-                              int withhold_peer, uint64_t lead, uint64_t* trace, int grid, hipStream_t stream) {
-  if (n_items <= 0) return hipSuccess;
-  if (grid > n_items) grid = n_items;
-  hipLaunchKernelGGL(ll_producer_kernel, dim3(grid), dim3(kLlThreads), 0, stream, items, n_items, chunk_bytes, epoch,
-                     withhold_peer, lead, trace);
-  return hipGetLastError();
-}
-
-hipError_t launch_ll_receive(const ProdItem* items, int n_items, int64_t chunk_bytes, uint32_t epoch, int rank,
-                             uint64_t timeout_ticks, uint32_t* status, uint64_t* trace, int grid,
-                             hipStream_t stream) {
-  if (n_items <= 0) return hipSuccess;
-  if (grid > n_items) grid = n_items;
-  hipLaunchKernelGGL(ll_receive_kernel, dim3(grid), dim3(kLlThreads), 0, stream, items, n_items, chunk_bytes, epoch,
-                     rank, timeout_ticks, status, trace);
-  return hipGetLastError();
-}
-
-hipError_t launch_ag_flag_wait(const ProdItem* items, int n_items, const uint32_t* flags, uint32_t epoch,
-                               uint64_t timeout_ticks, uint32_t* status, uint64_t* trace, int grid,
-                               hipStream_t stream) {
-  if (n_items <= 0) return hipSuccess;
-  if (grid > n_items) grid = n_items;
-  hipLaunchKernelGGL(ag_flag_wait_kernel, dim3(grid), dim3(64), 0, stream, items, n_items, flags, epoch,
-                     timeout_ticks, status, trace);
+hipError_t launch_ll_allgather(const ProdItem* items, int n_prod, int n_recv, int n_prod_blocks, int grid,
+                               int64_t chunk_bytes, uint32_t epoch, int withhold_peer, uint64_t lead, int rank,
+                               uint64_t timeout_ticks, uint32_t* status, uint64_t* trace, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ll_allgather_kernel, dim3(grid), dim3(kLlThreads), 0, stream, items, n_prod, n_recv,
+                     n_prod_blocks, chunk_bytes, epoch, withhold_peer, lead, rank, timeout_ticks, status, trace);
   return hipGetLastError();
 }
 

@@ -42,6 +42,10 @@ __device__ inline bool copy_bytes(char* __restrict__ dst, const char* __restrict
 #pragma unroll
       for (int u = 0; u < U; ++u)
         v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, b + lane + (uint32_t)u * stride, 0, kCpolNt);
+      // all U loads in flight before the first store: left to itself the
+      // scheduler pairs each store with its load to save registers, which
+      // leaves one 16-byte load in flight per lane
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < U; ++u)
         __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, b + lane + (uint32_t)u * stride, 0, kCpolSc1);
@@ -65,12 +69,11 @@ constexpr int kProdThreads = 256;
 // before its release, `lead` being twice the workgroup's last measured copy
 // time (so the copy is done by the release), which keeps the producer's HBM
 // traffic close to the links' rate instead of front-loading it.
-__global__ void __launch_bounds__(kProdThreads) ag_producer_kernel(uint32_t* flags,
-                                                                   const ProdItem* items, int n_items,
-                                                                   int64_t tile_bytes, uint32_t epoch,
-                                                                   int withhold_peer, uint64_t* trace_release,
-                                                                   uint64_t lead0, uint32_t* started,
-                                                                   uint64_t* trace_issue) {
+// Producer role: this workgroup takes items first, first + stride, ...
+__device__ __forceinline__ void produce_items(int first, int stride, uint32_t* flags,
+                                              const ProdItem* __restrict__ items, int n_items, int64_t tile_bytes,
+                                              uint32_t epoch, int withhold_peer, uint64_t* trace_release,
+                                              uint64_t lead0, uint32_t* started, uint64_t* trace_issue) {
   __shared__ uint64_t t0, lead;
   if (threadIdx.x == 0) {
     t0 = clock_ticks();
@@ -80,7 +83,7 @@ __global__ void __launch_bounds__(kProdThreads) ag_producer_kernel(uint32_t* fla
     if (started) __hip_atomic_fetch_add(started, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+  for (int it = first; it < n_items; it += stride) {
     const ProdItem item = items[it];
     const int p = (int)item.peer;
     uint64_t c0 = 0;
@@ -119,6 +122,43 @@ __global__ void __launch_bounds__(kProdThreads) ag_producer_kernel(uint32_t* fla
   }
 }
 
+__global__ void __launch_bounds__(kProdThreads) ag_producer_kernel(uint32_t* flags,
+                                                                   const ProdItem* __restrict__ items, int n_items,
+                                                                   int64_t tile_bytes, uint32_t epoch,
+                                                                   int withhold_peer, uint64_t* trace_release,
+                                                                   uint64_t lead0, uint32_t* started,
+                                                                   uint64_t* trace_issue) {
+  produce_items(blockIdx.x, gridDim.x, flags, items, n_items, tile_bytes, epoch, withhold_peer, trace_release, lead0,
+                started, trace_issue);
+}
+
+// Stand-alone flag-based AllGather in one launch: workgroups [0, n_prod_blocks)
+// are the producer (items[0, n_prod)), the others the receiving side, which
+// waits for the flags of items[n_prod, n_prod + n_recv) in arrival order
+// (wave 0 polls, then the acquire).  A launch with n_prod_blocks equal to its
+// grid is the producer alone, one with 0 the receiver alone.  trace
+// (optional, 2 words per chunk): {producer began the chunk, receiver saw its flag}.
+__global__ void __launch_bounds__(kProdThreads) ag_allgather_kernel(uint32_t* flags, const ProdItem* __restrict__ items,
+                                                                    int n_prod, int n_recv, int n_prod_blocks,
+                                                                    int64_t tile_bytes, uint32_t epoch,
+                                                                    int withhold_peer, uint64_t lead0,
+                                                                    uint64_t timeout_ticks, uint32_t* status,
+                                                                    uint64_t* trace) {
+  if ((int)blockIdx.x < n_prod_blocks) {
+    produce_items(blockIdx.x, n_prod_blocks, flags, items, n_prod, tile_bytes, epoch, withhold_peer, nullptr, lead0,
+                  nullptr, trace);
+    return;
+  }
+  __shared__ int ok;
+  const ProdItem* __restrict__ recv = items + n_prod;
+  const int stride = gridDim.x - n_prod_blocks;
+  for (int it = blockIdx.x - n_prod_blocks; it < n_recv; it += stride) {
+    const int64_t f = recv[it].flag0;
+    if (!wait_flags_block(flags, f, f + 1, epoch, timeout_ticks, status, &ok)) return;  // uniform
+    if (trace && threadIdx.x == 0) trace[2 * f + 1] = clock_ticks();
+  }
+}
+
 // Sets n flags to the epoch (pre-resident data, or the peers' flags of a
 // GEMM+RS call whose partials are already in place).  Plain stores: the kernel
 // boundary orders them before the consumer launched after it on the stream.
@@ -154,6 +194,16 @@ hipError_t launch_ag_producer(uint32_t* flags, const ProdItem* items, int n_item
   const uint64_t lead0 = (uint64_t)(tile_bytes / 160) + 100;
   hipLaunchKernelGGL(ag_producer_kernel, dim3(grid), dim3(kProdThreads), 0, stream, flags, items, n_items, tile_bytes,
                      epoch, withhold_peer, trace_release, lead0, started, trace_issue);
+  return hipGetLastError();
+}
+
+hipError_t launch_ag_allgather(uint32_t* flags, const ProdItem* items, int n_prod, int n_recv, int n_prod_blocks,
+                               int grid, int64_t tile_bytes, uint32_t epoch, int withhold_peer,
+                               uint64_t timeout_ticks, uint32_t* status, uint64_t* trace, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  const uint64_t lead0 = (uint64_t)(tile_bytes / 160) + 100;
+  hipLaunchKernelGGL(ag_allgather_kernel, dim3(grid), dim3(kProdThreads), 0, stream, flags, items, n_prod, n_recv,
+                     n_prod_blocks, tile_bytes, epoch, withhold_peer, lead0, timeout_ticks, status, trace);
   return hipGetLastError();
 }
 

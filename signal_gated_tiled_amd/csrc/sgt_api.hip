@@ -25,13 +25,12 @@ namespace sgt {
 hipError_t launch_ag_producer(uint32_t* flags, const ProdItem* items, int n_items,
                               int64_t tile_bytes, uint32_t epoch, int withhold_peer, uint64_t* trace_release, int grid,
                               hipStream_t stream, uint32_t* started = nullptr, uint64_t* trace_issue = nullptr);
-hipError_t launch_ll_producer(const ProdItem* items, int n_items, int64_t chunk_bytes, uint32_t epoch,
-                              int withhold_peer, uint64_t lead, uint64_t* trace, int grid, hipStream_t stream);
-hipError_t launch_ll_receive(const ProdItem* items, int n_items, int64_t chunk_bytes, uint32_t epoch, int rank,
-                             uint64_t timeout_ticks, uint32_t* status, uint64_t* trace, int grid, hipStream_t stream);
-hipError_t launch_ag_flag_wait(const ProdItem* items, int n_items, const uint32_t* flags, uint32_t epoch,
-                               uint64_t timeout_ticks, uint32_t* status, uint64_t* trace, int grid,
-                               hipStream_t stream);
+hipError_t launch_ll_allgather(const ProdItem* items, int n_prod, int n_recv, int n_prod_blocks, int grid,
+                               int64_t chunk_bytes, uint32_t epoch, int withhold_peer, uint64_t lead, int rank,
+                               uint64_t timeout_ticks, uint32_t* status, uint64_t* trace, hipStream_t stream);
+hipError_t launch_ag_allgather(uint32_t* flags, const ProdItem* items, int n_prod, int n_recv, int n_prod_blocks,
+                               int grid, int64_t tile_bytes, uint32_t epoch, int withhold_peer,
+                               uint64_t timeout_ticks, uint32_t* status, uint64_t* trace, hipStream_t stream);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
 hipError_t launch_rs_prepare(uint32_t* pflags, int64_t n, uint32_t v, uint32_t* counter, hipStream_t stream);
 hipError_t launch_ag_consumer(const AgArgs& a, int in_dtype, int grid, hipStream_t stream);
@@ -112,6 +111,8 @@ struct sgt_ctx {
   int64_t mrs_ctr_cap = 0;
   hipEvent_t slot_ev[kSlots] = {};
   bool slot_used[kSlots] = {};
+  std::vector<ProdItem> slot_items[kSlots];  // what d_items[slot] holds since its last upload
+  std::vector<ProdItem> build;               // host scratch for building a schedule (grows only)
   int slot = 0;
   std::mutex mu;
 };
@@ -318,6 +319,53 @@ sgt_status next_slot(sgt_ctx* ctx, int* slot) {
   ctx->slot = (ctx->slot + 1) % kSlots;
   if (ctx->slot_used[s]) HIP_TRY(hipEventSynchronize(ctx->slot_ev[s]));
   *slot = s;
+  return SGT_OK;
+}
+
+// Upload a schedule into a slot's device table, unless the table already
+// holds exactly these items (a repeated call with the same arguments).  The
+// slot's previous upload is complete: next_slot has waited for the event
+// recorded after the last kernel that read the slot, which ran after it.
+sgt_status upload_items(sgt_ctx* ctx, int slot, const ProdItem* items, int n, hipStream_t stream) {
+  std::vector<ProdItem>& held = ctx->slot_items[slot];
+  if (n <= 0) return SGT_OK;
+  if ((int)held.size() == n && std::memcmp(held.data(), items, (size_t)n * sizeof(ProdItem)) == 0) return SGT_OK;
+  HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], items, (size_t)n * sizeof(ProdItem), hipMemcpyHostToDevice, stream));
+  held.assign(items, items + n);
+  return SGT_OK;
+}
+
+// Host scratch of at least n items for building a schedule.
+ProdItem* build_buffer(sgt_ctx* ctx, int64_t n) {
+  if ((int64_t)ctx->build.size() < n) ctx->build.resize((size_t)n);
+  return ctx->build.data();
+}
+
+// Make `items` resident in a slot's device table and return the slot.  A
+// slot that already holds exactly these items (a repeated call with the same
+// arguments) is reused as it is: kernels only read the tables, so no upload
+// and no wait are needed.  Otherwise the next slot is taken (waiting for its
+// last reader), and the items go through its pinned staging buffer on
+// `stream`.  The caller records slot_ev[slot] after the kernel that reads it.
+sgt_status stage_items(sgt_ctx* ctx, const ProdItem* items, int n, hipStream_t stream, int* slot_out) {
+  const size_t bytes = (size_t)std::max(n, 0) * sizeof(ProdItem);
+  for (int s = 0; s < kSlots; ++s) {
+    const std::vector<ProdItem>& held = ctx->slot_items[s];
+    if (n > 0 && (int)held.size() == n && std::memcmp(held.data(), items, bytes) == 0) {
+      *slot_out = s;
+      return SGT_OK;
+    }
+  }
+  int s;
+  sgt_status st = next_slot(ctx, &s);
+  if (st != SGT_OK) return st;
+  ctx->slot_items[s].clear();
+  if (n > 0) {
+    std::memcpy(ctx->h_items[s], items, bytes);
+    HIP_TRY(hipMemcpyAsync(ctx->d_items[s], ctx->h_items[s], bytes, hipMemcpyHostToDevice, stream));
+    ctx->slot_items[s].assign(items, items + n);
+  }
+  *slot_out = s;
   return SGT_OK;
 }
 
@@ -533,15 +581,14 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   }
 
   int slot;
-  if ((st = next_slot(ctx, &slot)) != SGT_OK) return st;
-  const int n_items = build_schedule(p, W, o.rank, K, esz, o, A_shards, A_gathered, ctx->h_items[slot]);
+  ProdItem* items = build_buffer(ctx, p.n_flags);
+  const int n_items = build_schedule(p, W, o.rank, K, esz, o, A_shards, A_gathered, items);
   const int pwg = std::min(default_producer_wgs(o, ctx->n_cu), n_items);
   uint64_t* trace_rel = o.trace ? o.trace + (int64_t)total_tiles * 4 : nullptr;
   const int64_t tile_bytes = p.flag_rows * K * esz;
 
   if (o.producer == SGT_PROD_SERIAL) {
-    HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], ctx->h_items[slot], n_items * sizeof(ProdItem),
-                           hipMemcpyHostToDevice, stream));
+    if ((st = stage_items(ctx, items, n_items, stream, &slot)) != SGT_OK) return st;
     HIP_TRY(launch_ag_producer(flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
                                trace_rel, pwg, stream));
     HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
@@ -561,8 +608,7 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   // share of CUs, so both kernels are resident at once and no wait can starve.
   HIP_TRY(hipEventRecord(ctx->ev_fork, stream));
   HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
-  HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], ctx->h_items[slot], n_items * sizeof(ProdItem), hipMemcpyHostToDevice,
-                         ctx->prod));
+  if ((st = stage_items(ctx, items, n_items, ctx->prod, &slot)) != SGT_OK) return st;
   HIP_TRY(launch_ag_producer(flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
                              trace_rel, pwg, ctx->prod));
   HIP_TRY(hipEventRecord(ctx->slot_ev[slot], ctx->prod));
@@ -614,9 +660,8 @@ sgt_status launch_paced_peers(sgt_ctx* ctx, const sgt_opts& o, uint32_t* pflags,
                               uint32_t* counter, hipStream_t stream, int* pwg_out) {
   int slot;
   sgt_status st;
-  if ((st = next_slot(ctx, &slot)) != SGT_OK) return st;
-  ProdItem* items = ctx->h_items[slot];
   const int64_t bands = rs_tm, block_tiles = (int64_t)rs_tm * rs_tn;
+  ProdItem* items = build_buffer(ctx, (int64_t)(W - 1) * bands);
   const double ticks_per_band = o.peer_gbps > 0 ? (double)band_bytes / (o.peer_gbps * 1e3) * kTicksPerUs : 0.0;
   uint64_t seed = o.arrival_seed * 0x100000001B3ull + 0x5851F42D4C957F2Dull;
   int n = 0;
@@ -640,7 +685,7 @@ sgt_status launch_paced_peers(sgt_ctx* ctx, const sgt_opts& o, uint32_t* pflags,
   *pwg_out = pwg;
   HIP_TRY(launch_rs_prepare(pflags, 0, e, counter, stream));  // counter only: peers' flags come on arrival
   if (o.producer == SGT_PROD_SERIAL) {
-    HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], items, n * sizeof(ProdItem), hipMemcpyHostToDevice, stream));
+    if ((st = stage_items(ctx, items, n, stream, &slot)) != SGT_OK) return st;
     HIP_TRY(launch_ag_producer(pflags, ctx->d_items[slot], n, band_bytes, e, o.withhold_peer, nullptr, pwg, stream));
     HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
     ctx->slot_used[slot] = true;
@@ -648,7 +693,7 @@ sgt_status launch_paced_peers(sgt_ctx* ctx, const sgt_opts& o, uint32_t* pflags,
   }
   HIP_TRY(hipEventRecord(ctx->ev_fork, stream));
   HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
-  HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], items, n * sizeof(ProdItem), hipMemcpyHostToDevice, ctx->prod));
+  if ((st = stage_items(ctx, items, n, ctx->prod, &slot)) != SGT_OK) return st;
   HIP_TRY(launch_ag_producer(pflags, ctx->d_items[slot], n, band_bytes, e, o.withhold_peer, nullptr, pwg, ctx->prod));
   HIP_TRY(hipEventRecord(ctx->slot_ev[slot], ctx->prod));
   ctx->slot_used[slot] = true;
@@ -939,8 +984,7 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   // memory (a few words per workgroup); the producer's schedule is copied on
   // the stream that runs the producer.
   if (o.producer == SGT_PROD_SERIAL) {
-    HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], ctx->h_items[slot], n_items * sizeof(ProdItem), hipMemcpyHostToDevice,
-                           stream));
+    if ((st = upload_items(ctx, slot, ctx->h_items[slot], n_items, stream)) != SGT_OK) return st;
     HIP_TRY(launch_ag_producer(shard_flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
                                trace_rel, pwg, stream));
     if ((st = route_and_compute(ctx->d_ranks[slot], o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu)) != SGT_OK)
@@ -954,8 +998,7 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   // consumer on the remaining CUs (one workgroup per CU).
   HIP_TRY(hipEventRecord(ctx->ev_fork, stream));
   HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
-  HIP_TRY(hipMemcpyAsync(ctx->d_items[slot], ctx->h_items[slot], n_items * sizeof(ProdItem), hipMemcpyHostToDevice,
-                         ctx->prod));
+  if ((st = upload_items(ctx, slot, ctx->h_items[slot], n_items, ctx->prod)) != SGT_OK) return st;
   HIP_TRY(launch_ag_producer(shard_flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
                              trace_rel, pwg, ctx->prod, ctx->d_moe + 12));
   HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
@@ -1164,6 +1207,8 @@ sgt_status allgather_impl(sgt_ctx* ctx, const void* const* shards, void* gathere
   if (chunk % 16) return fail(SGT_EINVAL, "a chunk (flag_rows x K elements = %lld bytes) must be a multiple of 16",
                               (long long)chunk);
   if (ll && 2 * chunk >= ((int64_t)1 << 31)) return fail(SGT_EUNSUPPORTED, "LL chunk of 1 GiB or more");
+  if (2 * p.n_flags > kItemsCap)
+    return fail(SGT_EUNSUPPORTED, "%lld chunks exceed the schedule table", (long long)p.n_flags);
   if (M > 0) {
     if (!shards) return fail(SGT_EINVAL, "shards is NULL");
     for (int q = 0; q < W; ++q)
@@ -1178,64 +1223,58 @@ sgt_status allgather_impl(sgt_ctx* ctx, const void* const* shards, void* gathere
   const uint32_t e = ++ctx->epoch;
   if (M == 0) return SGT_OK;
 
-  int s_recv, s_prod;
-  if ((st = next_slot(ctx, &s_recv)) != SGT_OK) return st;
-  if ((st = next_slot(ctx, &s_prod)) != SGT_OK) return st;
-  ProdItem* recv = ctx->h_items[s_recv];
-  ProdItem* prod = ctx->h_items[s_prod];
+  // One schedule table: the producer's items, then the receiver's.
+  int slot;
+  // The receiver's list is built in the upper half of a host buffer, the
+  // producer's derived from it at the start, and the receiver's then moved
+  // down behind it.
+  ProdItem* tab = build_buffer(ctx, 2 * p.n_flags);
+  ProdItem* recv = tab + p.n_flags;
   const int n = build_schedule(p, W, o.rank, K, esz, o, shards, gathered, recv, /*local_first=*/true);
   int n_prod = 0;
-  if (ll) {
-    // producer: the remote chunks into their packets; receiver: packets (or
-    // the local shard) into the gathered rows, in the same order
-    for (int i = 0; i < n; ++i) {
-      if ((int)recv[i].peer == o.rank) continue;
-      ProdItem it = recv[i];
-      it.dst = static_cast<char*>(ll_buf) + (int64_t)it.flag0 * 2 * chunk;
-      prod[n_prod++] = it;
-      recv[i].src = it.dst;
+  for (int i = 0; i < n; ++i) {
+    // LL: the peers write the remote chunks' packets, and the receiver reads
+    // the packets (the local shard it copies itself); flag-based: the
+    // producer copies every chunk and the receiver waits on each flag
+    if (ll && (int)recv[i].peer == o.rank) continue;
+    tab[n_prod] = recv[i];
+    if (ll) {
+      tab[n_prod].dst = static_cast<char*>(ll_buf) + (int64_t)recv[i].flag0 * 2 * chunk;
+      recv[i].src = tab[n_prod].dst;
     }
-  } else {
-    std::copy(recv, recv + n, prod);
-    n_prod = n;
+    ++n_prod;
   }
+  if (tab + n_prod != recv) std::memmove(tab + n_prod, recv, (size_t)n * sizeof(ProdItem));
   const int pwg = std::min(default_producer_wgs(o, ctx->n_cu), std::max(n_prod, 1));
   const int rgrid = std::min(n, o.consumer_cus > 0 ? o.consumer_cus : default_producer_wgs(o, ctx->n_cu));
-  const bool serial = o.producer == SGT_PROD_SERIAL;
-  hipStream_t ps = serial ? stream : ctx->prod;
-  if (!serial) {
-    HIP_TRY(hipEventRecord(ctx->ev_fork, stream));
-    HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
+  const uint64_t to = timeout_ticks(o);
+  if ((st = stage_items(ctx, tab, n_prod + n, stream, &slot)) != SGT_OK) return st;
+  const ProdItem* d = ctx->d_items[slot];
+  // LL: start a chunk's writes about one write time before its release (at
+  // about 24 GB/s per workgroup: 240 bytes per 10 ns tick)
+  const uint64_t lead = (uint64_t)(2 * chunk / 240) + 100;
+  auto launch = [&](int n_pb, int grid) -> hipError_t {
+    return ll ? launch_ll_allgather(d, n_prod, n, n_pb, grid, chunk, e, o.withhold_peer, lead, o.rank, to,
+                                    ctx->d_status, o.trace, stream)
+              : launch_ag_allgather(flags, d, n_prod, n, n_pb, grid, chunk, e, o.withhold_peer, to, ctx->d_status,
+                                    o.trace, stream);
+  };
+  if (o.producer == SGT_PROD_SERIAL) {
+    // the peers' part first, then the receiver, one launch each
+    if (n_prod > 0) HIP_TRY(launch(pwg, pwg));
+    if ((st = mark(o, 0, stream)) != SGT_OK) return st;
+    HIP_TRY(launch(0, rgrid));
+    if ((st = mark(o, 1, stream)) != SGT_OK) return st;
+  } else {
+    // one launch: the peers' workgroups and the receiver's side by side (a
+    // small grid, so all of it is resident at once and every wait can end)
+    const int n_pb = n_prod > 0 ? pwg : 0;
+    if ((st = mark(o, 0, stream)) != SGT_OK) return st;
+    HIP_TRY(launch(n_pb, n_pb + rgrid));
+    if ((st = mark(o, 1, stream)) != SGT_OK) return st;
   }
-  if (n_prod > 0) {
-    HIP_TRY(hipMemcpyAsync(ctx->d_items[s_prod], prod, n_prod * sizeof(ProdItem), hipMemcpyHostToDevice, ps));
-    if (ll) {
-      // start a chunk's writes about one write time before its release (at
-      // about 24 GB/s per workgroup: 240 bytes per 10 ns tick)
-      const uint64_t lead = (uint64_t)(2 * chunk / 240) + 100;
-      HIP_TRY(launch_ll_producer(ctx->d_items[s_prod], n_prod, chunk, e, o.withhold_peer, lead, o.trace, pwg, ps));
-    } else {
-      HIP_TRY(launch_ag_producer(flags, ctx->d_items[s_prod], n_prod, chunk, e, o.withhold_peer, nullptr, pwg, ps,
-                                 nullptr, o.trace));
-    }
-  }
-  HIP_TRY(hipEventRecord(ctx->slot_ev[s_prod], ps));
-  ctx->slot_used[s_prod] = true;
-  HIP_TRY(hipMemcpyAsync(ctx->d_items[s_recv], recv, n * sizeof(ProdItem), hipMemcpyHostToDevice, stream));
-  if ((st = mark(o, 0, stream)) != SGT_OK) return st;
-  if (ll)
-    HIP_TRY(launch_ll_receive(ctx->d_items[s_recv], n, chunk, e, o.rank, timeout_ticks(o), ctx->d_status, o.trace,
-                              rgrid, stream));
-  else
-    HIP_TRY(launch_ag_flag_wait(ctx->d_items[s_recv], n, flags, e, timeout_ticks(o), ctx->d_status, o.trace, rgrid,
-                                stream));
-  if ((st = mark(o, 1, stream)) != SGT_OK) return st;
-  HIP_TRY(hipEventRecord(ctx->slot_ev[s_recv], stream));
-  ctx->slot_used[s_recv] = true;
-  if (!serial) {
-    HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
-    HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
-  }
+  HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
+  ctx->slot_used[slot] = true;
   return finish(ctx, o, stream);
 }
 

@@ -81,3 +81,25 @@ def test_no_scalar_cache_writes(kernels):
     for name, body in kernels.items():
         hits = [ln for ln in body if bad.match(ln)]
         assert not hits, "%s: %s" % (name, hits[:3])
+
+
+def test_copy_loops_keep_their_loads_in_flight(kernels):
+    # A copy is latency-bound: each pass must issue all of its 16-byte loads
+    # before its first store.  (Left to itself the scheduler pairs every store
+    # with its load, which halves a producer workgroup's bandwidth.)
+    want = {"ag_producer_kernel": 32, "ag_allgather_kernel": 32, "ll_allgather_kernel": 8}
+    found = set()
+    for name, body in kernels.items():
+        key = next((k for k in want if k in name), None)
+        if key is None:
+            continue
+        found.add(key)
+        run = best = 0
+        for ln in body:
+            if ln.startswith("buffer_load_dwordx4"):
+                run += 1
+            elif ln.startswith("buffer_store_dwordx4"):
+                best = max(best, run)
+                run = 0
+        assert best >= want[key], "%s: at most %d loads before a store" % (name, best)
+    assert found == set(want), found
