@@ -379,6 +379,51 @@ SGT_API sgt_status sgt_ll_allgather(sgt_ctx* ctx, const void* const* shards, voi
  * element size), or -1 for an invalid shape or options. */
 SGT_API int64_t sgt_ll_buffer_bytes(int W, int64_t M, int64_t K, const sgt_opts* opts);
 
+/*
+ * One rank's share of a signal-gated ring AllReduce (Triton-distributed
+ * semantics page, "Example: ring AllReduce with overlap": a ReduceScatter
+ * phase and an AllGather phase of W-1 steps each, every tile synchronized on
+ * its own, no barrier between steps).
+ *   out (N fp32) = the elementwise sum over the W ranks' vectors.  This rank
+ *   (opts->rank = r) holds x (N fp32), cut into W chunks of C = N / W
+ *   elements (chunk c = [c*C, (c+1)*C)) and each chunk into T tiles
+ *   (sgt_ring_flag_count).  It receives from rank r-1 and sends to r+1 (mod W).
+ *   ReduceScatter step s = 0 .. W-2: it sends chunk r-s and receives chunk
+ *   r-s-1, to which it adds its own x; after the last step it holds the full
+ *   sum of chunk r+1.  AllGather step s = 0 .. W-2: it sends chunk r+1-s (the
+ *   chunk it just finished, then what it received the step before) and
+ *   receives the full chunk r-s.  Message k (k = s in the ReduceScatter,
+ *   W-1+s in the AllGather) is C floats.
+ *   inbox (2(W-1) x C): message k from the left neighbour lands at inbox + k*C;
+ *   outbox (2(W-1) x C): this rank's message k to its right neighbour (the
+ *   neighbour's inbox on a real ring), written tile by tile with device-scope
+ *   stores.  flags (4(W-1)T uint32, zeroed once): the first 2(W-1)T are the
+ *   arrival flags of the inbox tiles (message k, tile j at k*T + j), the rest
+ *   this rank's notifications for its outbox tiles, same order.
+ *   left_msgs (2(W-1) x C): the left neighbour's messages in its memory.  With
+ *   SGT_PROD_CU (overlapped) or SGT_PROD_SERIAL the library's producer copies
+ *   them into the inbox tile by tile as that link would deliver them (one link,
+ *   messages in order, a tile every tile_bytes / opts->peer_gbps, plus
+ *   U[0, opts->jitter_us]) and sets each arrival flag; with SGT_PROD_PRESET the
+ *   inbox already holds them (left_msgs may be NULL) and the arrival flags are
+ *   set before the kernel.  Every tile of this rank's work waits only on its
+ *   own arrival flag.  W = 1: out = x.
+ * Requirements: fp32 (in_dtype = out_dtype = SGT_F32), N a multiple of W, C a
+ * multiple of 4, C*4 < 2^31; 16-byte aligned buffers.  opts->trace (optional):
+ * 3 x uint64 {wait start, flag seen, end} per item, T*(2W-1) items: the T
+ * tiles of the first send, then message k's tiles, k ascending.
+ * Errors: SGT_EINVAL / SGT_EUNSUPPORTED before any launch; SGT_ETIMEDOUT from a
+ * bounded wait (a withheld left neighbour, opts->withhold_peer = r-1).
+ */
+SGT_API sgt_status sgt_ring_allreduce(sgt_ctx* ctx, const float* x, const float* left_msgs, float* inbox,
+                                      float* outbox, float* out, uint32_t* flags, int W, int64_t N,
+                                      const sgt_opts* opts, void* stream);
+
+/* Flag words of an sgt_ring_allreduce call (4(W-1)T), or -1 for an invalid
+ * shape; *tile_elems (optional) receives the tile: the largest multiple of 4
+ * dividing C that is at most 16384 elements (C itself when C is smaller). */
+SGT_API int64_t sgt_ring_flag_count(int W, int64_t N, int64_t* tile_elems);
+
 /* Words of the optional trace buffer for an AllGather call: per consumer tile
  * 4 x uint64 {wait start, flag seen, tile end, workgroup}; then per signal tile
  * 1 x uint64 release time.  Times are the 100 MHz constant GPU clock.

@@ -26,6 +26,11 @@ Functions and the passage each follows (page titles as on the pages):
                         layer -- grouped rows times their expert's weight, each token's
                         rows summed with its gate weights, then the ReduceScatter over
                         token blocks.
+* ``allreduce`` / ``ring_allreduce`` / ``ring_rank`` -- semantics page, "Example: ring
+                        AllReduce with overlap": the sum over ranks, the ring's two
+                        phases emulated over all ranks (the messages every rank
+                        receives and sends), and one rank's steps given what it
+                        receives.
 * ``ag_gemm_protocol`` -- semantics page, "Producer-consumer model", "Signal-based
                         synchronization", "Threadblock swizzle", "Token-based data
                         dependency"; paper summary, "Method" (AMD full-mesh swizzle):
@@ -314,3 +319,106 @@ def ag_gemm_protocol(shards, B, rank: int, b_layout: str = "kn", flag_rows: int 
     if rc != 0:
         raise ValueError("bad protocol arguments")
     return A_g, C
+
+
+# ---- ring AllReduce (semantics page, "Example: ring AllReduce with overlap") ----
+
+def allreduce(xs) -> np.ndarray:
+    """The plain definition: the elementwise sum of the ranks' vectors, in double precision."""
+    out = np.zeros(np.asarray(xs[0]).size, dtype=np.float64)
+    for x in xs:
+        out += np.asarray(x, dtype=np.float64).reshape(-1)
+    return out
+
+
+def _f32_add(a, b):
+    """One fp32 addition: the sum in double precision rounded once to fp32.  Double has more than
+    2 * 24 + 2 bits of precision, so this equals the correctly rounded fp32 sum."""
+    return (np.asarray(a, np.float64) + np.asarray(b, np.float64)).astype(np.float32)
+
+
+def ring_allreduce(xs, planted: str = ""):
+    """Emulate the ring over all W ranks, step by step in the pages' two phases.
+
+    Chunk c of a vector is [c*C, (c+1)*C), C = N / W.  Rank q receives from q-1 and sends to q+1.
+    ReduceScatter step s = 0..W-2: q sends chunk q-s (its own x at s = 0, else what it reduced at
+    step s-1) and receives chunk q-s-1, adding its own x to it in fp32; after W-1 steps q holds the
+    full chunk q+1.  AllGather step s = 0..W-2: q sends chunk q+1-s (the chunk it finished, then
+    what it received the step before) and receives the full chunk q-s.
+
+    Returns (outs, inboxes, outboxes): per rank the fp32 result, the 2(W-1) messages it received
+    and the 2(W-1) it sent (message k = s in the ReduceScatter, W-1+s in the AllGather).
+    ``planted`` (tests only): "rs_chunk" receives chunk q-s instead of q-s-1.
+    """
+    xs = [np.asarray(x, np.float32).reshape(-1) for x in xs]
+    W = len(xs)
+    N = xs[0].size
+    assert N % W == 0
+    C = N // W
+
+    def ch(v, c):
+        c %= W
+        return v[c * C:(c + 1) * C]
+
+    outs = [np.full(N, np.nan, np.float32) for _ in range(W)]
+    if W == 1:
+        outs[0][:] = xs[0]
+        return outs, [np.zeros((0, C), np.float32)], [np.zeros((0, C), np.float32)]
+    inbox = [np.zeros((2 * (W - 1), C), np.float32) for _ in range(W)]
+    outbox = [np.zeros((2 * (W - 1), C), np.float32) for _ in range(W)]
+    reduced = [None] * W
+    for s in range(W - 1):
+        for q in range(W):
+            outbox[q][s] = ch(xs[q], q) if s == 0 else reduced[q]
+        for q in range(W):
+            got = outbox[(q - 1) % W][s]
+            inbox[q][s] = got
+            c = q - s if planted == "rs_chunk" else q - s - 1
+            reduced[q] = _f32_add(ch(xs[q], c), got)
+    for q in range(W):
+        ch(outs[q], q + 1)[:] = reduced[q]
+    last = list(reduced)
+    for s in range(W - 1):
+        k = W - 1 + s
+        for q in range(W):
+            outbox[q][k] = last[q]
+        for q in range(W):
+            got = outbox[(q - 1) % W][k]
+            inbox[q][k] = got
+            ch(outs[q], q - s)[:] = got
+            last[q] = got
+    return outs, inbox, outbox
+
+
+def ring_rank(x, inbox, rank: int, W: int):
+    """One rank's steps given the messages it receives (inbox: 2(W-1) x C, message k in row k):
+    returns (out, outbox) as that rank computes and sends them."""
+    x = np.asarray(x, np.float32).reshape(-1)
+    N = x.size
+    C = N // W
+    out = np.full(N, np.nan, np.float32)
+    if W == 1:
+        out[:] = x
+        return out, np.zeros((0, C), np.float32)
+    inbox = np.asarray(inbox, np.float32).reshape(2 * (W - 1), C)
+    outbox = np.zeros((2 * (W - 1), C), np.float32)
+
+    def sl(c):
+        c %= W
+        return slice(c * C, (c + 1) * C)
+
+    outbox[0] = x[sl(rank)]
+    for k in range(W - 1):
+        c = rank - k - 1
+        v = _f32_add(x[sl(c)], inbox[k])
+        if k < W - 2:
+            outbox[k + 1] = v
+        else:
+            out[sl(c)] = v
+            outbox[W - 1] = v
+    for s in range(W - 1):
+        k = W - 1 + s
+        out[sl(rank - s)] = inbox[k]
+        if s < W - 2:
+            outbox[k + 1] = inbox[k]
+    return out, outbox

@@ -94,9 +94,12 @@ def lib() -> ctypes.CDLL:
         L.sgt_ll_allgather.argtypes = [P, P, P, P, ctypes.c_int, I64, I64, ctypes.POINTER(Opts), P]
         L.sgt_ll_buffer_bytes.argtypes = [ctypes.c_int, I64, I64, ctypes.POINTER(Opts)]
         L.sgt_ll_buffer_bytes.restype = I64
+        L.sgt_ring_allreduce.argtypes = [P, P, P, P, P, P, P, ctypes.c_int, I64, ctypes.POINTER(Opts), P]
+        L.sgt_ring_flag_count.argtypes = [ctypes.c_int, I64, ctypes.POINTER(I64)]
+        L.sgt_ring_flag_count.restype = I64
         for f in ("sgt_ctx_create", "sgt_ctx_destroy", "sgt_sync", "sgt_ag_gemm", "sgt_rs_flag_count", "sgt_gemm_rs",
                   "sgt_gemm_rs_paced", "sgt_moe_ag_gemm", "sgt_moe_gemm_rs",
-                  "sgt_moe_gemm_rs_paced", "sgt_allgather", "sgt_ll_allgather"):
+                  "sgt_moe_gemm_rs_paced", "sgt_allgather", "sgt_ll_allgather", "sgt_ring_allreduce"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -225,6 +228,15 @@ def ll_buffer_bytes(W: int, M: int, K: int, **kw) -> int:
     return int(n)
 
 
+def ring_flag_count(W: int, N: int):
+    """(flag words, tile elements) of a ring AllReduce of N fp32 elements over W ranks."""
+    t = I64()
+    n = lib().sgt_ring_flag_count(W, N, ctypes.byref(t))
+    if n < 0:
+        raise SgtError(SGT_EINVAL, "invalid ring AllReduce shape (N a multiple of W, N / W a multiple of 4)")
+    return int(n), int(t.value)
+
+
 def rs_flag_count(W: int, M: int, N: int, rs_tile: int = 0):
     o = make_opts(rs_tile=rs_tile)
     g, p = I64(), I64()
@@ -303,6 +315,19 @@ class Context:
         _check(lib().sgt_ll_allgather(self._h, ctypes.cast(ptrs, P), _dev_ptr(ll_buf, "ll_buf", dev),
                                       _dev_ptr(gathered, "gathered", dev), W, M, K, ctypes.byref(o),
                                       _stream_handle(stream)))
+
+    def ring_allreduce(self, x, left_msgs, inbox, outbox, out, flags, W: int, *, stream=None, **kw):
+        """One rank's share of a ring AllReduce: out = sum over ranks (fp32).  left_msgs / inbox /
+        outbox: 2(W-1) messages of N / W floats; flags: ring_flag_count(W, N)[0] words.  left_msgs
+        may be None with producer='preset' (the inbox already holds the messages)."""
+        dev = x.device
+        kw.setdefault("in_dtype", SGT_F32)
+        kw.setdefault("out_dtype", SGT_F32)
+        o = make_opts(**kw)
+        _check(lib().sgt_ring_allreduce(self._h, _dev_ptr(x, "x", dev), _dev_ptr(left_msgs, "left_msgs", dev),
+                                        _dev_ptr(inbox, "inbox", dev), _dev_ptr(outbox, "outbox", dev),
+                                        _dev_ptr(out, "out", dev), _dev_ptr(flags, "flags", dev), W, x.numel(),
+                                        ctypes.byref(o), _stream_handle(stream)))
 
     def gemm_rs(self, A_local, B, partials: Sequence, partial_out, C_shard, gflags, pflags, *, stream=None, **kw):
         """GEMM + ReduceScatter: partial_out = A_local @ B (fp32); C_shard = partial_out[block rank] +

@@ -19,6 +19,7 @@
 
 #include "sgt.h"
 #include "common.hpp"
+#include "ring.hpp"
 #include "sched.hpp"
 
 namespace sgt {
@@ -28,6 +29,7 @@ hipError_t launch_ag_producer(uint32_t* flags, const ProdItem* items, int n_item
 hipError_t launch_ll_allgather(const ProdItem* items, int n_prod, int n_recv, int n_prod_blocks, int grid,
                                int64_t chunk_bytes, uint32_t epoch, int withhold_peer, uint64_t lead, int rank,
                                uint64_t timeout_ticks, uint32_t* status, uint64_t* trace, hipStream_t stream);
+hipError_t launch_ring_allreduce(const RingArgs& a, int grid, hipStream_t stream);
 hipError_t launch_ag_allgather(uint32_t* flags, const ProdItem* items, int n_prod, int n_recv, int n_prod_blocks,
                                int grid, int64_t tile_bytes, uint32_t epoch, int withhold_peer,
                                uint64_t timeout_ticks, uint32_t* status, uint64_t* trace, hipStream_t stream);
@@ -1297,6 +1299,137 @@ sgt_status sgt_allgather(sgt_ctx* ctx, const void* const* shards, void* gathered
 sgt_status sgt_ll_allgather(sgt_ctx* ctx, const void* const* shards, void* ll_buf, void* gathered, int W, int64_t M,
                             int64_t K, const sgt_opts* opts, void* stream) {
   return allgather_impl(ctx, shards, gathered, nullptr, ll_buf, true, W, M, K, opts, stream);
+}
+
+}  // extern "C"
+
+
+namespace {
+
+constexpr int64_t kRingTileMax = 16384;  // elements (64 KiB of fp32)
+
+// Tile of a ring chunk of C elements: the largest multiple of 4 dividing C,
+// at most kRingTileMax (C itself when C is smaller).
+int64_t ring_tile(int64_t C) {
+  if (C <= kRingTileMax) return C;
+  for (int64_t t = kRingTileMax; t >= 4; t -= 4)
+    if (C % t == 0) return t;
+  return 4;
+}
+
+sgt_status ring_plan(int W, int64_t N, int64_t* C, int64_t* tile, int64_t* T) {
+  if (W < 1 || W > kMaxW) return fail(SGT_EINVAL, "W = %d outside [1, %d]", W, kMaxW);
+  if (N < 0 || N % W) return fail(SGT_EINVAL, "N = %lld is not a non-negative multiple of W = %d", (long long)N, W);
+  *C = N / W;
+  if (*C % 4) return fail(SGT_EINVAL, "a chunk (N / W = %lld elements) must be a multiple of 4", (long long)*C);
+  if (*C * 4 >= ((int64_t)1 << 31)) return fail(SGT_EUNSUPPORTED, "chunk of 2 GiB or more");
+  *tile = *C > 0 ? ring_tile(*C) : 4;
+  *T = *C > 0 ? *C / *tile : 0;
+  if (*T * (2 * (int64_t)W - 1) > kItemsCap) return fail(SGT_EUNSUPPORTED, "%lld ring tiles exceed the schedule table",
+                                                          (long long)(*T * (2 * (int64_t)W - 1)));
+  return SGT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t sgt_ring_flag_count(int W, int64_t N, int64_t* tile_elems) {
+  int64_t C, tile, T;
+  if (ring_plan(W, N, &C, &tile, &T) != SGT_OK) return -1;
+  if (tile_elems) *tile_elems = tile;
+  return 4 * (int64_t)(W - 1) * T;
+}
+
+sgt_status sgt_ring_allreduce(sgt_ctx* ctx, const float* x, const float* left_msgs, float* inbox, float* outbox,
+                              float* out, uint32_t* flags, int W, int64_t N, const sgt_opts* opts, void* stream_) {
+  if (!ctx) return fail(SGT_EINVAL, "ctx is NULL");
+  sgt_status st = check_opts(opts, W < 1 ? 1 : W);
+  if (st != SGT_OK) return st;
+  const sgt_opts& o = *opts;
+  if (o.in_dtype != SGT_F32 || o.out_dtype != SGT_F32) return fail(SGT_EUNSUPPORTED, "the ring AllReduce is fp32");
+  int64_t C, tile, T;
+  if ((st = ring_plan(W, N, &C, &tile, &T)) != SGT_OK) return st;
+  const bool resident = o.producer == SGT_PROD_PRESET;
+  if (N > 0) {
+    if (!x || !out || !aligned16(x) || !aligned16(out)) return fail(SGT_EINVAL, "x or out NULL or not 16-byte aligned");
+    if (W > 1) {
+      if (!inbox || !outbox || !flags || !aligned16(inbox) || !aligned16(outbox) || !aligned16(flags))
+        return fail(SGT_EINVAL, "inbox, outbox or flags NULL or not 16-byte aligned");
+      if (!resident && (!left_msgs || !aligned16(left_msgs)))
+        return fail(SGT_EINVAL, "left_msgs NULL or not 16-byte aligned (needed unless the producer is preset)");
+    }
+  }
+  std::lock_guard<std::mutex> lock(ctx->mu);
+  DeviceGuard g(ctx->device);
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const uint32_t e = ++ctx->epoch;
+  if (N == 0) return SGT_OK;
+
+  const int64_t n_msg = 2 * (int64_t)(W - 1);
+  RingArgs a{};
+  a.x = x; a.inbox = inbox; a.outbox = outbox; a.out = out;
+  a.in_flags = flags; a.out_flags = flags ? flags + n_msg * T : nullptr;
+  a.status = ctx->d_status; a.trace = o.trace;
+  a.C = C; a.W = W; a.rank = o.rank; a.T = (int32_t)T; a.tile = (int32_t)tile;
+  a.epoch = e; a.timeout_ticks = timeout_ticks(o);
+  const int64_t n_items = T * (2 * (int64_t)W - 1);
+
+  if (W == 1 || resident) {
+    // the left neighbour's messages are already in the inbox
+    if (W > 1) HIP_TRY(launch_fill_u32(flags, n_msg * T, e, stream));
+    const int grid = (int)std::min<int64_t>(n_items, o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu);
+    if ((st = mark(o, 0, stream)) != SGT_OK) return st;
+    HIP_TRY(launch_ring_allreduce(a, grid, stream));
+    if ((st = mark(o, 1, stream)) != SGT_OK) return st;
+    return finish(ctx, o, stream);
+  }
+
+  // The left neighbour's link delivers its messages in order, one tile every
+  // tile_bytes / peer_gbps (plus jitter), into the inbox, each with its flag.
+  ProdItem* items = build_buffer(ctx, n_msg * T);
+  const double tile_bytes = (double)tile * 4.0;
+  const double ticks_per_tile = o.peer_gbps > 0 ? tile_bytes / (o.peer_gbps * 1e3) * kTicksPerUs : 0.0;
+  uint64_t seed = o.arrival_seed * 0x100000001B3ull + 0x5851F42D4C957F2Dull;
+  const int left = (o.rank + W - 1) % W;
+  const int n = (int)(n_msg * T);
+  for (int i = 0; i < n; ++i) {
+    ProdItem it = sched_item(i, left, (double)(i + 1) * ticks_per_tile + jitter_ticks(o, seed));
+    it.src = reinterpret_cast<const char*>(left_msgs) + (int64_t)i * tile * 4;
+    it.dst = reinterpret_cast<char*>(inbox) + (int64_t)i * tile * 4;
+    items[i] = it;
+  }
+  std::stable_sort(items, items + n, [](const ProdItem& p, const ProdItem& q) { return p.release < q.release; });
+  const int pwg = std::min(default_producer_wgs(o, ctx->n_cu), n);
+  int slot;
+  if (o.producer == SGT_PROD_SERIAL) {
+    if ((st = stage_items(ctx, items, n, stream, &slot)) != SGT_OK) return st;
+    HIP_TRY(launch_ag_producer(flags, ctx->d_items[slot], n, (int64_t)tile * 4, e, o.withhold_peer, nullptr, pwg,
+                               stream));
+    HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
+    ctx->slot_used[slot] = true;
+    const int grid = (int)std::min<int64_t>(n_items, o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu);
+    if ((st = mark(o, 0, stream)) != SGT_OK) return st;
+    HIP_TRY(launch_ring_allreduce(a, grid, stream));
+    if ((st = mark(o, 1, stream)) != SGT_OK) return st;
+    return finish(ctx, o, stream);
+  }
+  HIP_TRY(hipEventRecord(ctx->ev_fork, stream));
+  HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
+  if ((st = stage_items(ctx, items, n, ctx->prod, &slot)) != SGT_OK) return st;
+  HIP_TRY(launch_ag_producer(flags, ctx->d_items[slot], n, (int64_t)tile * 4, e, o.withhold_peer, nullptr, pwg,
+                             ctx->prod));
+  HIP_TRY(hipEventRecord(ctx->slot_ev[slot], ctx->prod));
+  ctx->slot_used[slot] = true;
+  // the ring's workgroups take the CUs the producer leaves, so every wait can end
+  const int grid = (int)std::min<int64_t>(n_items, o.consumer_cus > 0 ? o.consumer_cus
+                                                                       : std::max(1, ctx->n_cu - pwg));
+  if ((st = mark(o, 0, stream)) != SGT_OK) return st;
+  HIP_TRY(launch_ring_allreduce(a, grid, stream));
+  if ((st = mark(o, 1, stream)) != SGT_OK) return st;
+  HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
+  HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
+  return finish(ctx, o, stream);
 }
 
 }  // extern "C"

@@ -164,6 +164,22 @@ class MoERSWorkload:
         return 2.0 * self.T * self.topk * self.I * self.H
 
 
+@dataclasses.dataclass(frozen=True)
+class RingWorkload:
+    """Ring AllReduce of W ranks' fp32 vectors of N elements, one rank's share."""
+    name: str
+    W: int
+    N: int
+    peer_gbps: float = 0.0      # the left neighbour's link; 0 = unthrottled
+    jitter_us: float = 0.0
+    dist: str = "normal"        # "normal" N(0,1) or "int" {-8..8}
+    seed_index: int = 7
+
+    @property
+    def bytes_per_rank(self) -> int:
+        return 4 * self.N
+
+
 # The five workloads (index = seed offset).  Shapes follow the pages' model
 # shapes: Qwen3-32B MLP (hidden 5120, intermediate 25600), Llama-3-70B MLP
 # (hidden 8192, intermediate 28672), each split 8 ways.
@@ -179,7 +195,11 @@ MOE = MoEWorkload("moe_ag_grouped_w8", W=8, T=4096, H=2048, I=768, E=64, topk=8,
 # The down projection of the same MoE layer (the next workload on the pages' list).
 MOE_RS = MoERSWorkload("moe_gemm_rs_w8", W=8, T=4096, I=768, H=2048, E=64, topk=8, seed_index=5)
 
-WORKLOADS = {w.name: w for w in (TINY, QWEN_AG, GEMM_RS, LLAMA_AG, MOE, MOE_RS)}
+# The ring AllReduce of the pages' second example at the Llama-3-70B row-parallel output of 2048 tokens
+# (2048 x 8192 fp32 per rank), over the 153.6 GB/s link from the left neighbour.
+RING = RingWorkload("ring_allreduce_llama3_70b_w8", W=8, N=2048 * 8192, peer_gbps=153.6, seed_index=7)
+
+WORKLOADS = {w.name: w for w in (TINY, QWEN_AG, GEMM_RS, LLAMA_AG, MOE, MOE_RS, RING)}
 
 
 def _streams(seed_index: int, n: int, salt: int = 0):
@@ -276,6 +296,15 @@ def make_moe_rs(w: MoERSWorkload, salt: int = 0, W_layout: str = "kn"):
     if W_layout == "nk":
         W2 = np.ascontiguousarray(np.transpose(W2, (0, 2, 1)))
     return Hg, W2, gate, logits, partials
+
+
+def make_ring(w: RingWorkload, salt: int = 0):
+    """Return the W ranks' vectors (fp32, N each)."""
+    assert w.N % w.W == 0
+    ss = _streams(w.seed_index, w.W, salt)
+    if w.dist == "int":
+        return [small_int(ss[p], (w.N,), -8, 8, dtype="f32") for p in range(w.W)]
+    return [normal_f32(ss[p], (w.N,), 1.0) for p in range(w.W)]
 
 
 def scaled(w, **kw):

@@ -99,3 +99,8 @@ def test_flag_counts_and_argument_errors():
     assert sgt.ll_buffer_bytes(4, 24, 40, in_dtype=sgt.SGT_F32, flag_rows=3) == 2 * 24 * 40 * 4
     with pytest.raises(sgt.SgtError):
         sgt.ll_buffer_bytes(8, 100, 64)                                 # M % W != 0
+    assert sgt.ring_flag_count(8, 2048 * 8192) == (4 * 7 * 128, 16384)   # 2M-element chunks, 64 KiB tiles
+    assert sgt.ring_flag_count(3, 3 * 16396) == (4 * 2 * 4099, 4)       # 16396 = 4 * 4099: 4-element tiles
+    assert sgt.ring_flag_count(1, 16) == (0, 16)
+    with pytest.raises(sgt.SgtError):
+        sgt.ring_flag_count(4, 4 * 6)                                   # chunk not a multiple of 4

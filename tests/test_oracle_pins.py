@@ -426,3 +426,61 @@ def test_ll_planted_swap_is_caught(orc):
     good = orc.ll_pack(payload, 4)
     swapped = (good << np.uint64(32)) | (good >> np.uint64(32))
     assert [int(v) for v in swapped] != [4 * 2**32 + int(w) for w in payload]
+
+
+# ---- ring AllReduce (semantics page, "Example: ring AllReduce with overlap") ----
+
+def _ring_xs(W, N, kind="float", seed=21):
+    rng = np.random.default_rng(seed)
+    if kind == "int":
+        return [rng.integers(-50, 51, size=N).astype(np.float32) for _ in range(W)]
+    return [rng.standard_normal(N).astype(np.float32) for _ in range(W)]
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 5, 8])
+def test_ring_result_is_the_sum_on_every_rank(orc, W):
+    xs = _ring_xs(W, W * 12)
+    outs, _, _ = orc.ring_allreduce(xs)
+    ref = np.sum(np.stack(xs).astype(np.float64), axis=0)           # library routine, fp64
+    mag = np.sum(np.abs(np.stack(xs).astype(np.float64)), axis=0)
+    for q in range(W):
+        assert np.all(np.abs(outs[q] - ref) <= W * 2.0**-24 * mag + 1e-30), q
+
+
+def test_ring_integer_inputs_are_exact(orc):
+    xs = _ring_xs(8, 8 * 20, kind="int")
+    outs, _, _ = orc.ring_allreduce(xs)
+    ref = np.sum(np.stack(xs).astype(np.int64), axis=0)
+    for o in outs:
+        assert np.array_equal(o.astype(np.int64), ref)
+
+
+def test_ring_sums_each_chunk_in_ring_order(orc):
+    # W = 3, one element per chunk.  Chunk 0 starts at rank 0 and gains rank 1's, then rank 2's
+    # value, each sum rounded to fp32: (2^24 + 1) + 1 rounds to 2^24 twice (ties to even), while
+    # 2^24 + (1 + 1) would be 2^24 + 2.  Chunk 1 starts at rank 1: (1 + 2^24) + 1 rounds to 2^24 as
+    # well; chunk 2 starts at rank 2: (1 + 1) + 2^24 = 2^24 + 2 exactly.
+    xs = [np.array([2.0**24, 1.0, 1.0], np.float32), np.array([1.0, 1.0, 2.0**24], np.float32),
+          np.array([1.0, 2.0**24, 1.0], np.float32)]
+    outs, _, _ = orc.ring_allreduce(xs)
+    for o in outs:
+        assert o[0] == 2.0**24 and o[1] == 2.0**24 and o[2] == 2.0**24 + 2
+
+
+def test_ring_closes_and_rank_view_matches(orc):
+    for W in (2, 4, 7):
+        xs = _ring_xs(W, W * 8, seed=22 + W)
+        outs, inbox, outbox = orc.ring_allreduce(xs)
+        for q in range(W):
+            # what q sends is what q+1 receives
+            assert np.array_equal(outbox[q], inbox[(q + 1) % W])
+            # the rank's own recurrence, given what it receives, gives the same result and sends
+            o, ob = orc.ring_rank(xs[q], inbox[q], q, W)
+            assert np.array_equal(o, outs[q]) and np.array_equal(ob, outbox[q])
+
+
+def test_ring_planted_mistake_is_caught(orc):
+    xs = _ring_xs(4, 16, kind="int")
+    outs, _, _ = orc.ring_allreduce(xs, planted="rs_chunk")
+    ref = np.sum(np.stack(xs).astype(np.int64), axis=0)
+    assert not all(np.array_equal(o.astype(np.int64), ref) for o in outs)
