@@ -350,6 +350,63 @@ def bench_ll(ctx, up, args, torch, sgt, I):
     return out
 
 
+def bench_ring(ctx, up, args, torch, sgt, I):
+    """One rank's share of the signal-gated ring AllReduce: 2048 x 8192 fp32 per rank, W = 8, the left
+    neighbour's link at 153.6 GB/s.
+
+    Kernel alone (messages resident, flags preset) against HBM; the overlapped call against the link floor
+    (2(W-1) messages of N/W floats over one link); the serial call (all messages land, then the kernel).
+    """
+    w = I.RING
+    W, N = w.W, w.N
+    C = N // W
+    x = up(I.make_ring(w)[0])
+    msgs = up(I.make_ring_messages(w)).reshape(-1)
+    inbox = torch.empty(2 * (W - 1) * C, dtype=torch.float32, device="cuda:0")
+    outbox = torch.empty_like(inbox)
+    out = torch.empty(N, dtype=torch.float32, device="cuda:0")
+    nf, tile = sgt.ring_flag_count(W, N)
+    flags = torch.zeros(nf, dtype=torch.int32, device="cuda:0")
+
+    def call(producer, **kw):
+        def fn(i, ev):
+            ctx.ring_allreduce(x, msgs, inbox, outbox, out, flags, W, rank=0, producer=producer,
+                               consumer_events=ev, **kw)
+        return fn
+
+    res = {"workload": w.name, "N": N, "W": W, "tile_elems": tile, "peer_gbps": w.peer_gbps}
+    # algorithmic bytes of one rank per chunk element: first send 8, ReduceScatter steps 12 (the last 16),
+    # AllGather steps 12 (the last 8)
+    alg = (32 + 24 * (W - 2)) * C
+    inbox.copy_(msgs)
+    step, mean_k, kern = timed(call("preset"), args.steps, 5, torch, ctx)
+    k = spread(kern)
+    res["resident"] = {"step_ms": step, "kernel_ms": k, "hbm_gbps": alg / (k["median"] * 1e-3) / 1e9,
+                       "hbm_frac": alg / (k["median"] * 1e-3) / 8e12, "algorithmic_mb": alg / 1e6}
+    floor_us = 2 * (W - 1) * C * 4 / (w.peer_gbps * 1e3)
+    for name, kw in (("overlapped_153.6GBps", dict(peer_gbps=w.peer_gbps)),
+                     ("serial_153.6GBps", dict(peer_gbps=w.peer_gbps)),
+                     ("overlapped_unthrottled", dict())):
+        prod = "serial" if name.startswith("serial") else "cu"
+        step, _, kern = timed(call(prod, **kw), max(10, args.steps // 2), 3, torch, ctx)
+        r = {"step_ms": step, "kernel_ms": spread(kern)}
+        if "153.6" in name:
+            r["link_floor_us"] = floor_us
+            r["efficiency_vs_link_floor"] = floor_us / (step * 1e3)
+        res[name] = r
+    # check this rank's result against its own steps (torch on the device, the same fp32 additions)
+    owned = 1 % W
+    exp_owned = x[owned * C:(owned + 1) * C] + msgs[(W - 2) * C:(W - 1) * C]
+    assert torch.equal(out[owned * C:(owned + 1) * C], exp_owned), "owned chunk"
+    for s_ in range(W - 1):
+        c = (0 - s_) % W
+        k_ = W - 1 + s_
+        assert torch.equal(out[c * C:(c + 1) * C], msgs[k_ * C:(k_ + 1) * C]), "gathered chunk %d" % c
+    res["note"] = ("overlapped: every tile waits only on its own arrival flag, so the reduction and forwarding "
+                   "hide under the link; serial: the messages land first, then the same kernel runs")
+    return res
+
+
 def bench_moe(ctx, up, args, torch, sgt, I, lay):
     """MoE AllGather + grouped GEMM (T 4096 tokens in 8 shards, H 2048, I 768, 64 experts, top-8, Zipf-skewed
     logits), overlapped at 50 GB/s per simulated peer; the grouped consumer's MFMA and HBM roofline fractions."""
@@ -480,6 +537,8 @@ def main():
     ap.add_argument("--no-moe", action="store_true", help="skip the MoE AllGather + grouped GEMM workload")
     ap.add_argument("--no-ll", action="store_true", help="skip the low-latency AllGather comparison")
     ap.add_argument("--ll-only", action="store_true", help="only the low-latency AllGather comparison")
+    ap.add_argument("--no-ring", action="store_true", help="skip the ring AllReduce")
+    ap.add_argument("--ring-only", action="store_true", help="only the ring AllReduce")
     ap.add_argument("--b-layout", default="nk", choices=["kn", "nk"],
                     help="B as N x K (a Linear layer's weight, default) or K x N")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -516,9 +575,12 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
-    if args.ll_only:
+    if args.ll_only or args.ring_only:
         with sgt.Context(0) as c:
-            print(json.dumps({"ll_allgather": bench_ll(c, up, args, torch, sgt, I)}))
+            if args.ll_only:
+                print(json.dumps({"ll_allgather": bench_ll(c, up, args, torch, sgt, I)}))
+            else:
+                print(json.dumps({"ring_allreduce": bench_ring(c, up, args, torch, sgt, I)}))
         return
 
     w = I.LLAMA_AG
@@ -726,6 +788,8 @@ def main():
     detail["ag_other_workloads"] = bench_ag_other(ctx, up, args, torch, sgt, I, lay)
     if not args.no_ll:
         detail["ll_allgather"] = bench_ll(ctx, up, args, torch, sgt, I)
+    if not args.no_ring:
+        detail["ring_allreduce"] = bench_ring(ctx, up, args, torch, sgt, I)
 
     if not args.no_moe:
         detail["moe_ag_grouped"], tables = bench_moe(ctx, up, args, torch, sgt, I, lay)

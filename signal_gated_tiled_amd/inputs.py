@@ -307,6 +307,13 @@ def make_ring(w: RingWorkload, salt: int = 0):
     return [normal_f32(ss[p], (w.N,), 1.0) for p in range(w.W)]
 
 
+def make_ring_messages(w: RingWorkload, salt: int = 0):
+    """Stand-ins for the left neighbour's 2(W-1) messages of N / W floats each, N(0,1) (the timed
+    work does not depend on their values; parity tests build consistent ones with the oracle)."""
+    ss = _streams(w.seed_index, 1, salt + 1000)
+    return normal_f32(ss[0], (2 * (w.W - 1), w.N // w.W), 1.0)
+
+
 def scaled(w, **kw):
     """A copy of a workload with some fields replaced (used for reduced test sizes)."""
     return dataclasses.replace(w, **kw)
