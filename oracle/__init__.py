@@ -31,6 +31,11 @@ Functions and the passage each follows (page titles as on the pages):
                         phases emulated over all ranks (the messages every rank
                         receives and sends), and one rank's steps given what it
                         receives.
+* ``a2a_dispatch`` / ``a2a_slots`` / ``a2a_combine_recv`` / ``a2a_combine`` -- paper summary,
+                        "Experiments" (expert-parallel AllToAll dispatch and combine) and the
+                        complete guide, §4.2 (low-latency AllToAll for expert parallelism): each
+                        token's row goes to the owner of every expert it picked, and comes back
+                        as that expert's output, summed with the token's gate weights.
 * ``ag_gemm_protocol`` -- semantics page, "Producer-consumer model", "Signal-based
                         synchronization", "Threadblock swizzle", "Token-based data
                         dependency"; paper summary, "Method" (AMD full-mesh swizzle):
@@ -422,3 +427,102 @@ def ring_rank(x, inbox, rank: int, W: int):
         if s < W - 2:
             outbox[k + 1] = inbox[k]
     return out, outbox
+
+
+# ---- expert-parallel AllToAll (paper summary, "Experiments": AllToAll dispatch and combine measured against
+#      DeepEP; complete guide, §4.2: low-latency AllToAll for expert parallelism) ----
+
+def a2a_owner(e, E: int, W: int):
+    """Rank that holds expert e: the E experts are split into W contiguous blocks of E / W."""
+    return np.asarray(e) // (E // W)
+
+
+def a2a_tokens(topk: np.ndarray, e: int) -> np.ndarray:
+    """Ascending indices of the tokens (rows of topk) that picked expert e (a token counts once)."""
+    topk = np.asarray(topk)
+    return np.nonzero((topk == e).any(axis=1))[0].astype(np.int32)
+
+
+def a2a_dispatch(X, topk, E: int, rank: int, before=None):
+    """The dispatch as rank `rank` receives it.
+
+    X: W arrays T_r x H (any dtype; rows are copied as bits); topk: W arrays T_r x k of expert ids (ids outside
+    [0, E) select nothing).  For local expert l (global e = rank * E/W + l) and source p, slot i of block (l, p)
+    holds X[p][tok_i], tok_0 < tok_1 < ... being the tokens of p that picked e.
+    Returns (recv E_l x W x T_r x H, recv_token E_l x W x T_r, count E_l x W).  Slots past the count keep
+    `before` (default zeros) and their token entries are -1.
+    """
+    W = len(X)
+    E_l = E // W
+    T_r, H = np.asarray(X[0]).shape
+    recv = np.zeros((E_l, W, T_r, H), np.asarray(X[0]).dtype) if before is None else np.array(before, copy=True)
+    tok = np.full((E_l, W, T_r), -1, np.int32)
+    count = np.zeros((E_l, W), np.int64)
+    for l in range(E_l):
+        e = rank * E_l + l
+        for p in range(W):
+            ts = a2a_tokens(topk[p], e)
+            n = len(ts)
+            count[l, p] = n
+            tok[l, p, :n] = ts
+            recv[l, p, :n] = np.asarray(X[p])[ts]
+    return recv, tok, count
+
+
+def a2a_slots(topk: np.ndarray, E: int) -> np.ndarray:
+    """slot[t, j]: the position of token t in expert topk[t, j]'s list of this rank's tokens, i.e. the number of
+    tokens before t that picked that expert; -1 for ids outside [0, E)."""
+    topk = np.asarray(topk)
+    T_r, k = topk.shape
+    slot = np.full((T_r, k), -1, np.int64)
+    seen = np.zeros(E, np.int64)
+    for t in range(T_r):
+        picked = set()
+        for j in range(k):
+            e = int(topk[t, j])
+            if 0 <= e < E:
+                slot[t, j] = seen[e]
+                picked.add(e)
+        for e in picked:
+            seen[e] += 1
+    return slot
+
+
+def a2a_combine_recv(back, topk, E: int, before=None):
+    """What the combine's senders leave in this rank's receive buffer: for expert e (owner q, local index l),
+    rows [0, n_e) of back[q][l] at cbuf[e], n_e = this rank's tokens that picked e.  back: W arrays
+    E_l x T_r x H.  Rows past n_e keep `before` (default zeros)."""
+    W = len(back)
+    E_l = E // W
+    _, T_r, H = np.asarray(back[0]).shape
+    cbuf = np.zeros((E, T_r, H), np.asarray(back[0]).dtype) if before is None else np.array(before, copy=True)
+    for e in range(E):
+        n = len(a2a_tokens(topk, e))
+        cbuf[e, :n] = np.asarray(back[e // E_l])[e % E_l, :n]
+    return cbuf
+
+
+def _bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns to float64 (exact): a bf16 value is the upper half of the fp32 with the same bits."""
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def a2a_combine(back, topk, gate, E: int):
+    """The combine on this rank: out[t] = sum over picks j of gate[t, j] * Y_e[slot(t, j)], e = topk[t, j],
+    Y_e = back[owner(e)][e mod E/W] (bf16 bits), in float64, picks in order; ids outside [0, E) add nothing."""
+    W = len(back)
+    E_l = E // W
+    topk = np.asarray(topk)
+    gate = np.asarray(gate, np.float32)
+    T_r, k = topk.shape
+    H = np.asarray(back[0]).shape[2]
+    slot = a2a_slots(topk, E)
+    out = np.zeros((T_r, H), np.float64)
+    for t in range(T_r):
+        for j in range(k):
+            e = int(topk[t, j])
+            if not 0 <= e < E:
+                continue
+            y = _bf16_to_f64(np.asarray(back[e // E_l])[e % E_l, slot[t, j]])
+            out[t] += np.float64(gate[t, j]) * y
+    return out

@@ -180,6 +180,27 @@ class RingWorkload:
         return 4 * self.N
 
 
+@dataclasses.dataclass(frozen=True)
+class A2AWorkload:
+    """Expert-parallel AllToAll of one MoE layer, one rank's share: the dispatch of every rank's tokens to the
+    owners of the experts they picked, and the combine of the expert outputs back into this rank's tokens."""
+    name: str
+    W: int
+    T: int          # tokens over all ranks (T / W per rank)
+    H: int
+    E: int
+    topk: int
+    std: float = 0.02
+    zipf_alpha: float = 1.0
+    peer_gbps: float = 0.0
+    chunk_rows: int = 32
+    seed_index: int = 8
+
+    @property
+    def tokens_per_rank(self) -> int:
+        return self.T // self.W
+
+
 # The five workloads (index = seed offset).  Shapes follow the pages' model
 # shapes: Qwen3-32B MLP (hidden 5120, intermediate 25600), Llama-3-70B MLP
 # (hidden 8192, intermediate 28672), each split 8 ways.
@@ -199,7 +220,11 @@ MOE_RS = MoERSWorkload("moe_gemm_rs_w8", W=8, T=4096, I=768, H=2048, E=64, topk=
 # (2048 x 8192 fp32 per rank), over the 153.6 GB/s link from the left neighbour.
 RING = RingWorkload("ring_allreduce_llama3_70b_w8", W=8, N=2048 * 8192, peer_gbps=153.6, seed_index=7)
 
-WORKLOADS = {w.name: w for w in (TINY, QWEN_AG, GEMM_RS, LLAMA_AG, MOE, MOE_RS, RING)}
+# The AllToAll dispatch and combine of the same MoE layer with expert parallelism over the 8 ranks (8 experts
+# per rank), links at 50 GB/s per peer.
+A2A = A2AWorkload("a2a_moe_ep8", W=8, T=4096, H=2048, E=64, topk=8, peer_gbps=50.0, seed_index=8)
+
+WORKLOADS = {w.name: w for w in (TINY, QWEN_AG, GEMM_RS, LLAMA_AG, MOE, MOE_RS, RING, A2A)}
 
 
 def _streams(seed_index: int, n: int, salt: int = 0):
@@ -312,6 +337,28 @@ def make_ring_messages(w: RingWorkload, salt: int = 0):
     work does not depend on their values; parity tests build consistent ones with the oracle)."""
     ss = _streams(w.seed_index, 1, salt + 1000)
     return normal_f32(ss[0], (2 * (w.W - 1), w.N // w.W), 1.0)
+
+
+def make_a2a(w: A2AWorkload, salt: int = 0):
+    """Return (X, logits, gate, back).
+
+    X: W arrays of (T/W) x H bf16 ~N(0, std), the ranks' tokens.  logits: T x E float32, as in make_moe (Gaussian
+    plus a seeded Zipf-like popularity skew); rank p's tokens are rows [p*T/W, (p+1)*T/W).  gate: T x topk float32
+    in (0, 1), one weight per pick.  back: W arrays of (E/W) x (T/W) x H bf16 ~N(0, 1), stand-ins for the expert
+    outputs that each expert owner sends back to this rank (slot i of expert l: this rank's i-th token routed to
+    it; only the first count rows are ever read).
+    """
+    assert w.T % w.W == 0 and w.E % w.W == 0
+    ss = _streams(w.seed_index, 2 * w.W + 3, salt)
+    T_r, E_l = w.T // w.W, w.E // w.W
+    X = [normal_bf16(ss[p], (T_r, w.H), w.std) for p in range(w.W)]
+    g = _rng(ss[w.W]).standard_normal(size=(w.T, w.E), dtype=np.float32)
+    perm = _rng(ss[w.W + 1]).permutation(w.E)
+    beta = (-w.zipf_alpha * np.log1p(perm.astype(np.float64))).astype(np.float32)
+    logits = (g + beta[None, :]).astype(np.float32)
+    gate = _rng(ss[w.W + 2]).random(size=(w.T, w.topk), dtype=np.float32)
+    back = [normal_bf16(ss[w.W + 3 + q], (E_l, T_r, w.H), 1.0) for q in range(w.W)]
+    return X, logits, gate, back
 
 
 def scaled(w, **kw):

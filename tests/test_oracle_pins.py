@@ -484,3 +484,130 @@ def test_ring_planted_mistake_is_caught(orc):
     outs, _, _ = orc.ring_allreduce(xs, planted="rs_chunk")
     ref = np.sum(np.stack(xs).astype(np.int64), axis=0)
     assert not all(np.array_equal(o.astype(np.int64), ref) for o in outs)
+
+
+# ---- expert-parallel AllToAll ----
+
+def _a2a_case(seed, W=4, E=8, T_r=13, k=3, H=5, invalid=False):
+    rng = np.random.default_rng(seed)
+    X = [I.f32_to_bf16_bits(rng.standard_normal((T_r, H)).astype(np.float32)) for _ in range(W)]
+    topk = [np.array([rng.permutation(E)[:k] for _ in range(T_r)], np.int32) for _ in range(W)]
+    if invalid:
+        for tk in topk:
+            tk[rng.integers(0, T_r, 3), rng.integers(0, k, 3)] = [-1, E, E + 7]
+    return X, topk
+
+
+@pytest.mark.parametrize("invalid", [False, True])
+def test_a2a_dispatch_delivers_every_pick_once_to_its_owner(orc, invalid):
+    from collections import Counter
+    W, E = 4, 8
+    X, topk = _a2a_case(1, W=W, E=E, invalid=invalid)
+    E_l = E // W
+    got = Counter()
+    for r in range(W):
+        recv, tok, cnt = orc.a2a_dispatch(X, topk, E, r)
+        for l in range(E_l):
+            for p in range(W):
+                n = int(cnt[l, p])
+                ts = tok[l, p, :n]
+                assert (np.diff(ts) > 0).all() and (tok[l, p, n:] == -1).all()
+                assert np.array_equal(recv[l, p, :n], X[p][ts])
+                assert not recv[l, p, n:].any()
+                got.update((p, int(t), r * E_l + l) for t in ts)
+    want = Counter((p, t, int(e)) for p in range(W) for t in range(topk[p].shape[0]) for e in topk[p][t]
+                   if 0 <= e < E)
+    assert got == want
+    assert sum(got.values()) == sum(int(((tk >= 0) & (tk < E)).sum()) for tk in topk)
+
+
+def test_a2a_dispatch_blocks_concatenate_to_moe_groups(orc):
+    # the expert groups of the (separately written, C) MoE routing over all ranks' tokens are the
+    # dispatch blocks of that expert's owner, taken source by source
+    W, E, T, k = 4, 16, 96, 4
+    rng = np.random.default_rng(5)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    ids, off, row_token = orc.moe_route(logits, k)
+    T_r, E_l = T // W, E // W
+    X = [np.arange(T_r * 2, dtype=np.uint16).reshape(T_r, 2) for _ in range(W)]
+    topk = [ids[p * T_r:(p + 1) * T_r] for p in range(W)]
+    for r in range(W):
+        _, tok, cnt = orc.a2a_dispatch(X, topk, E, r)
+        for l in range(E_l):
+            e = r * E_l + l
+            cat = np.concatenate([p * T_r + tok[l, p, :cnt[l, p]] for p in range(W)])
+            assert np.array_equal(cat, row_token[off[e]:off[e + 1]])
+
+
+def _dense_combine(back, topk, gate, E):
+    """Independent matrix form: G[t, e] = sum of the gates of t's picks of e; the slot of t in expert e's list
+    is the running count (cumulative sum) of the tokens up to t that picked e, minus one."""
+    W = len(back)
+    E_l = E // W
+    topk = np.asarray(topk)
+    T_r = topk.shape[0]
+    onehot = np.zeros((T_r, E), np.float64)
+    G = np.zeros((T_r, E), np.float64)
+    for j in range(topk.shape[1]):
+        valid = (topk[:, j] >= 0) & (topk[:, j] < E)
+        rows = np.nonzero(valid)[0]
+        onehot[rows, topk[rows, j]] = 1.0
+        G[rows, topk[rows, j]] += gate[rows, j].astype(np.float64)
+    hit = onehot > 0
+    slots = np.cumsum(hit, axis=0) - 1
+    H = back[0].shape[2]
+    out = np.zeros((T_r, H), np.float64)
+    for e in range(E):
+        Y = I.bf16_bits_to_f32(back[e // E_l][e % E_l]).astype(np.float64)
+        sel = np.where(hit[:, e], slots[:, e], 0)
+        out += (G[:, e] * hit[:, e])[:, None] * Y[sel]
+    return out
+
+
+@pytest.mark.parametrize("invalid", [False, True])
+def test_a2a_combine_matches_dense_selection_form(orc, invalid):
+    W, E, T_r, k, H = 4, 8, 13, 3, 6
+    rng = np.random.default_rng(11)
+    _, topk = _a2a_case(2, W=W, E=E, T_r=T_r, k=k, H=H, invalid=invalid)
+    back = [I.f32_to_bf16_bits(rng.standard_normal((E // W, T_r, H)).astype(np.float32)) for _ in range(W)]
+    gate = rng.random((T_r, k), dtype=np.float32)
+    for r in (0, 3):
+        out = orc.a2a_combine(back, topk[r], gate, E)
+        ref = _dense_combine(back, topk[r], gate, E)
+        assert np.allclose(out, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_a2a_combine_of_identity_experts_returns_the_tokens(orc):
+    # each expert sends back exactly the rows it received; gates that are powers of two summing to one
+    # make every sum exact, so the combine must return each token's own row bit for bit
+    W, E, T_r, k, H = 4, 8, 17, 4, 5
+    X, topk = _a2a_case(3, W=W, E=E, T_r=T_r, k=k, H=H)
+    gate = np.tile(np.array([0.5, 0.25, 0.125, 0.125], np.float32), (T_r, 1))
+    recv = [orc.a2a_dispatch(X, topk, E, q)[0] for q in range(W)]
+    for r in range(W):
+        back = [recv[q][:, r] for q in range(W)]
+        out = orc.a2a_combine(back, topk[r], gate, E)
+        assert np.array_equal(out, I.bf16_bits_to_f32(X[r]).astype(np.float64))
+        cbuf = orc.a2a_combine_recv(back, topk[r], E)
+        for e in range(E):
+            ts = orc.a2a_tokens(topk[r], e)
+            assert np.array_equal(cbuf[e, :len(ts)], X[r][ts])
+
+
+def test_a2a_slots_of_a_worked_example(orc):
+    # three tokens, E = 4: token 0 picks (2, 0), token 1 picks (0, 3), token 2 picks (0, 2)
+    topk = np.array([[2, 0], [0, 3], [0, 2]], np.int32)
+    assert orc.a2a_slots(topk, 4).tolist() == [[0, 0], [1, 0], [2, 1]]
+
+
+def test_a2a_planted_slot_mistake_is_caught(orc, monkeypatch):
+    W, E, T_r, k, H = 4, 8, 13, 3, 6
+    rng = np.random.default_rng(12)
+    _, topk = _a2a_case(4, W=W, E=E, T_r=T_r, k=k, H=H)
+    back = [I.f32_to_bf16_bits(rng.standard_normal((E // W, T_r, H)).astype(np.float32)) for _ in range(W)]
+    gate = rng.random((T_r, k), dtype=np.float32)
+    good = orc.a2a_slots
+    # counting the token itself (a slot off by one) must break the agreement with the dense form
+    monkeypatch.setattr(orc, "a2a_slots", lambda tk, E_: np.minimum(good(tk, E_) + 1, T_r - 1))
+    out = orc.a2a_combine(back, topk[1], gate, E)
+    assert not np.allclose(out, _dense_combine(back, topk[1], gate, E), rtol=1e-6, atol=1e-6)
