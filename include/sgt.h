@@ -424,6 +424,74 @@ SGT_API sgt_status sgt_ring_allreduce(sgt_ctx* ctx, const float* x, const float*
  * dividing C that is at most 16384 elements (C itself when C is smaller). */
 SGT_API int64_t sgt_ring_flag_count(int W, int64_t N, int64_t* tile_elems);
 
+/*
+ * Expert-parallel AllToAll, one rank's share (paper summary, "Experiments":
+ * AllToAll dispatch and combine of expert parallelism, measured against
+ * DeepEP; complete guide, §4.2: low-latency AllToAll for expert parallelism).
+ * E experts in contiguous blocks of E_l = E / W per rank (expert e lives on
+ * rank e / E_l).  Each of the W ranks holds T_r tokens of H elements and its
+ * routing topk (T_r x k int32 expert ids; ids outside [0, E) select nothing).
+ * This rank is opts->rank = r.  Blocks travel in chunks of opts->flag_rows
+ * rows (0 = 32, at most 1024); n_chunks = ceil(T_r / chunk rows).  On one GPU
+ * the other ranks' sending is simulated by sender workgroups in the same
+ * launch, each publishing its chunk's flag no earlier than its link (one per
+ * peer at opts->peer_gbps, all concurrent, blocks in expert order; the local
+ * rank's own blocks unthrottled; 0 = unthrottled) would deliver it.
+ *
+ * sgt_a2a_dispatch: rank r receives, for its local expert l (global e =
+ * r*E_l + l) and each source p, the rows of p's tokens that picked e, in
+ * ascending token order:
+ *   X[p] (T_r x H, bf16 or fp32 per opts->in_dtype; rows copied as bits);
+ *   topk[p] (T_r x k int32);
+ *   recv (E_l x W x T_r x H): block (l, p) at rows (l*W + p)*T_r, slot i =
+ *     X[p][token i]; slots past the count are not written;
+ *   recv_token (E_l x W x T_r int32): token i of block (l, p); entries past the
+ *     count are not written;
+ *   recv_count (E_l x W uint64): packet (epoch << 32) | count, stored with
+ *     device scope before the block's data;
+ *   flags (sgt_a2a_flag_count words, zeroed once): chunk c of block b = l*W + p
+ *     at b*n_chunks + c, set to the call's epoch once its rows have landed
+ *     (chunks past the count are not written).
+ *   opts->producer: SGT_PROD_CU (default) or SGT_PROD_SERIAL (the same launch).
+ *
+ * sgt_a2a_combine: the expert outputs come back to rank r in the same slot
+ * order, and token t's output is out[t] = sum over picks j of gate[t, j] *
+ * (row slot(t, j) of expert topk[t, j]), fp32, picks in order, where
+ * slot(t, j) = the number of r's tokens before t that picked that expert:
+ *   back[q] (E_l x T_r x H bf16): owner q's outputs for r's tokens, expert
+ *     q*E_l + l at rows l*T_r, slot i for r's i-th token routed to it (only
+ *     the first count rows are read);
+ *   topk (T_r x k int32), gate (T_r x k fp32): this rank's routing;
+ *   cbuf (E x T_r x H bf16): the receive slots, expert e at rows e*T_r;
+ *   slot_of (T_r x k int32, written): slot(t, j), -1 for ids outside [0, E);
+ *   out (T_r x H fp32, written);
+ *   flags (sgt_a2a_flag_count words, zeroed once): chunk c of expert e at
+ *     e*n_chunks + c.  Each token waits only on the chunks holding its rows.
+ *   opts->producer: SGT_PROD_CU (senders and receiver in one launch),
+ *   SGT_PROD_SERIAL (senders, then the receiver), SGT_PROD_PRESET (cbuf already
+ *   holds the rows, back may be NULL: flags set, then the receiver alone).
+ *   opts->consumer_cus: receiver workgroups (4 tokens at a time each; 0 =
+ *   min(ceil(T_r / 4), CUs / 2)).  in_dtype must be SGT_BF16, out_dtype SGT_F32.
+ *
+ * Requirements: 1 <= W <= 64, E a multiple of W with E <= 4096, 1 <= k <= 64,
+ * rows of a multiple of 16 bytes, T_r*H*elem < 2^31; X, back, recv, cbuf, out
+ * 16-byte aligned.  Ownership: every buffer is the caller's device memory; the
+ * context keeps a table of E per-block row counts between the two kernels of
+ * a call.  Errors: SGT_EINVAL / SGT_EUNSUPPORTED before any launch;
+ * SGT_ETIMEDOUT when a combine wait expires (a withheld link,
+ * opts->withhold_peer = q, whose chunks are copied but never flagged).
+ */
+SGT_API sgt_status sgt_a2a_dispatch(sgt_ctx* ctx, const void* const* X, const int32_t* const* topk, void* recv,
+                                    int32_t* recv_token, uint64_t* recv_count, uint32_t* flags, int W, int64_t T_r,
+                                    int64_t H, int E, int k, const sgt_opts* opts, void* stream);
+SGT_API sgt_status sgt_a2a_combine(sgt_ctx* ctx, const void* const* back, const int32_t* topk, const float* gate,
+                                   void* cbuf, int32_t* slot_of, float* out, uint32_t* flags, int W, int64_t T_r,
+                                   int64_t H, int E, int k, const sgt_opts* opts, void* stream);
+
+/* Flag words of an AllToAll call (E * ceil(T_r / chunk rows)), or -1 for an
+ * invalid shape. */
+SGT_API int64_t sgt_a2a_flag_count(int W, int64_t T_r, int E, const sgt_opts* opts);
+
 /* Words of the optional trace buffer for an AllGather call: per consumer tile
  * 4 x uint64 {wait start, flag seen, tile end, workgroup}; then per signal tile
  * 1 x uint64 release time.  Times are the 100 MHz constant GPU clock.

@@ -97,9 +97,16 @@ def lib() -> ctypes.CDLL:
         L.sgt_ring_allreduce.argtypes = [P, P, P, P, P, P, P, ctypes.c_int, I64, ctypes.POINTER(Opts), P]
         L.sgt_ring_flag_count.argtypes = [ctypes.c_int, I64, ctypes.POINTER(I64)]
         L.sgt_ring_flag_count.restype = I64
+        L.sgt_a2a_dispatch.argtypes = [P, P, P, P, P, P, P, ctypes.c_int, I64, I64, ctypes.c_int, ctypes.c_int,
+                                       ctypes.POINTER(Opts), P]
+        L.sgt_a2a_combine.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int, I64, I64, ctypes.c_int, ctypes.c_int,
+                                      ctypes.POINTER(Opts), P]
+        L.sgt_a2a_flag_count.argtypes = [ctypes.c_int, I64, ctypes.c_int, ctypes.POINTER(Opts)]
+        L.sgt_a2a_flag_count.restype = I64
         for f in ("sgt_ctx_create", "sgt_ctx_destroy", "sgt_sync", "sgt_ag_gemm", "sgt_rs_flag_count", "sgt_gemm_rs",
                   "sgt_gemm_rs_paced", "sgt_moe_ag_gemm", "sgt_moe_gemm_rs",
-                  "sgt_moe_gemm_rs_paced", "sgt_allgather", "sgt_ll_allgather", "sgt_ring_allreduce"):
+                  "sgt_moe_gemm_rs_paced", "sgt_allgather", "sgt_ll_allgather", "sgt_ring_allreduce",
+                  "sgt_a2a_dispatch", "sgt_a2a_combine"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -235,6 +242,15 @@ def ring_flag_count(W: int, N: int):
     if n < 0:
         raise SgtError(SGT_EINVAL, "invalid ring AllReduce shape (N a multiple of W, N / W a multiple of 4)")
     return int(n), int(t.value)
+
+
+def a2a_flag_count(W: int, T_r: int, E: int, **kw) -> int:
+    """Flag words of an AllToAll dispatch or combine (E x ceil(T_r / chunk rows))."""
+    o = make_opts(**kw)
+    n = lib().sgt_a2a_flag_count(W, T_r, E, ctypes.byref(o))
+    if n < 0:
+        raise SgtError(SGT_EINVAL, "invalid AllToAll shape or options")
+    return int(n)
 
 
 def rs_flag_count(W: int, M: int, N: int, rs_tile: int = 0):
@@ -422,4 +438,45 @@ class Context:
                                      _dev_ptr(Y, "Y", dev), _dev_ptr(expert_off, "expert_off", dev),
                                      _dev_ptr(row_token, "row_token", dev), _dev_ptr(topk_ids, "topk_ids", dev),
                                      _dev_ptr(shard_flags, "shard_flags", dev), W, T, H, I, E, topk,
+                                     ctypes.byref(o), _stream_handle(stream)))
+
+    def a2a_dispatch(self, X: Sequence, topk: Sequence, recv, recv_token, recv_count, flags, E: int, *, stream=None,
+                     **kw):
+        """Expert-parallel AllToAll dispatch as rank `rank` receives it.  X: W tensors T_r x H (bf16 or fp32);
+        topk: W int32 tensors T_r x k; recv: E/W x W x T_r x H; recv_token: E/W x W x T_r int32;
+        recv_count: E/W x W int64 packets (epoch << 32 | count); flags: a2a_flag_count words."""
+        dev = recv.device
+        W = len(X)
+        T_r, H = X[0].shape[0], X[0].shape[1]
+        k = topk[0].shape[1]
+        kw.setdefault("in_dtype", _dtype_code(X[0]))
+        o = make_opts(**kw)
+        xp = (P * W)(*[_dev_ptr(a, "X[%d]" % i, dev) for i, a in enumerate(X)])
+        tp = (P * W)(*[_dev_ptr(t, "topk[%d]" % i, dev) for i, t in enumerate(topk)])
+        _check(lib().sgt_a2a_dispatch(self._h, ctypes.cast(xp, P), ctypes.cast(tp, P), _dev_ptr(recv, "recv", dev),
+                                      _dev_ptr(recv_token, "recv_token", dev), _dev_ptr(recv_count, "recv_count", dev),
+                                      _dev_ptr(flags, "flags", dev), W, T_r, H, E, k, ctypes.byref(o),
+                                      _stream_handle(stream)))
+
+    def a2a_combine(self, back: Optional[Sequence], topk, gate, cbuf, slot_of, out, flags, W: int, *, stream=None,
+                    **kw):
+        """Expert-parallel AllToAll combine on rank `rank`: out[t] = sum_j gate[t, j] * (row slot(t, j) of expert
+        topk[t, j]).  back: W bf16 tensors E/W x T_r x H (None with producer='preset': cbuf already holds the
+        rows); topk, gate: T_r x k (int32, fp32); cbuf: E x T_r x H bf16; slot_of: T_r x k int32 (written);
+        out: T_r x H fp32; flags: a2a_flag_count words."""
+        dev = out.device
+        T_r, H = out.shape[0], out.shape[1]
+        k = topk.shape[1]
+        E = cbuf.shape[0]
+        kw.setdefault("in_dtype", SGT_BF16)
+        kw.setdefault("out_dtype", SGT_F32)
+        o = make_opts(**kw)
+        if back is not None:
+            bp = (P * W)(*[_dev_ptr(b, "back[%d]" % i, dev) for i, b in enumerate(back)])
+            bptr = ctypes.cast(bp, P)
+        else:
+            bptr = None
+        _check(lib().sgt_a2a_combine(self._h, bptr, _dev_ptr(topk, "topk", dev), _dev_ptr(gate, "gate", dev),
+                                     _dev_ptr(cbuf, "cbuf", dev), _dev_ptr(slot_of, "slot_of", dev),
+                                     _dev_ptr(out, "out", dev), _dev_ptr(flags, "flags", dev), W, T_r, H, E, k,
                                      ctypes.byref(o), _stream_handle(stream)))

@@ -21,6 +21,7 @@
 #include "common.hpp"
 #include "ring.hpp"
 #include "sched.hpp"
+#include "alltoall.hpp"
 
 namespace sgt {
 hipError_t launch_ag_producer(uint32_t* flags, const ProdItem* items, int n_items,
@@ -48,6 +49,8 @@ hipError_t launch_moe_route(const float* logits, int64_t T, int E, int k, const 
 hipError_t launch_moe_rs(const MoeRsArgs& a, int grid, hipStream_t stream);
 hipError_t launch_moe_consumer(const MoeArgs& a, int b_layout, int out_dtype, int tile_rows, int tile_waves, int grid,
                                hipStream_t stream);
+hipError_t launch_a2a_scan(const A2aArgs& a, hipStream_t stream);
+hipError_t launch_a2a(const A2aArgs& a, int recv_grid, hipStream_t stream);
 inline int kBMrs() { return rs_gemm_tile(); }
 constexpr int kBNmoe() { return 256; }  // column tile of the tile core
 }  // namespace sgt
@@ -111,6 +114,7 @@ struct sgt_ctx {
   int64_t mrs_tiles_cap = 0;
   uint32_t* d_mrs_ctr = nullptr;
   int64_t mrs_ctr_cap = 0;
+  int32_t* d_a2a_counts = nullptr;  // AllToAll: rows of each (link, expert) block, kA2aMaxE entries
   hipEvent_t slot_ev[kSlots] = {};
   bool slot_used[kSlots] = {};
   std::vector<ProdItem> slot_items[kSlots];  // what d_items[slot] holds since its last upload
@@ -443,6 +447,7 @@ sgt_status sgt_ctx_create(sgt_ctx** out, int device) {
   chk(hipMalloc(&c->d_moe, 1024 * sizeof(uint32_t)), "hipMalloc(moe)");
   if (st == SGT_OK) chk(hipMemset(c->d_moe, 0, 1024 * sizeof(uint32_t)), "hipMemset(moe)");
   chk(hipMalloc(&c->d_moe_ranks, kItemsCap * sizeof(uint32_t)), "hipMalloc(moe ranks)");
+  chk(hipMalloc(&c->d_a2a_counts, kA2aMaxE * sizeof(int32_t)), "hipMalloc(a2a counts)");
   if (st == SGT_OK) chk(hipMemset(c->d_status, 0, 4 * sizeof(uint32_t)), "hipMemset");
   for (int s = 0; s < kSlots && st == SGT_OK; ++s) {
     chk(hipHostMalloc(&c->h_items[s], kItemsCap * sizeof(ProdItem), hipHostMallocDefault), "hipHostMalloc");
@@ -483,6 +488,7 @@ sgt_status sgt_ctx_destroy(sgt_ctx* c) {
   if (c->d_mrs_rowof) (void)hipFree(c->d_mrs_rowof);
   if (c->d_mrs_tiles) (void)hipFree(c->d_mrs_tiles);
   if (c->d_mrs_ctr) (void)hipFree(c->d_mrs_ctr);
+  if (c->d_a2a_counts) (void)hipFree(c->d_a2a_counts);
   if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
   if (c->ev_join) (void)hipEventDestroy(c->ev_join);
   if (c->prod) (void)hipStreamDestroy(c->prod);
@@ -1429,6 +1435,181 @@ sgt_status sgt_ring_allreduce(sgt_ctx* ctx, const float* x, const float* left_ms
   if ((st = mark(o, 1, stream)) != SGT_OK) return st;
   HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
   HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
+  return finish(ctx, o, stream);
+}
+
+}  // extern "C"
+
+
+namespace {
+
+constexpr int kA2aDefaultChunkRows = 32;
+
+bool aligned_to(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shape checks shared by the AllToAll calls; chunk rows and chunks per block.
+sgt_status a2a_plan(int W, int64_t T_r, int E, int k, const sgt_opts& o, int* cr, int64_t* nch) {
+  if (W < 1 || W > kMaxW) return fail(SGT_EINVAL, "W = %d outside [1, %d]", W, kMaxW);
+  if (E < 1 || E > kA2aMaxE || E % W) return fail(SGT_EINVAL, "E = %d: must be a multiple of W = %d in [1, %d]", E, W,
+                                                  kA2aMaxE);
+  if (k < 1 || k > 64) return fail(SGT_EINVAL, "k = %d outside [1, 64]", k);
+  if (T_r < 0) return fail(SGT_EINVAL, "negative token count");
+  *cr = o.flag_rows > 0 ? o.flag_rows : kA2aDefaultChunkRows;
+  if (*cr > kA2aMaxChunkRows) return fail(SGT_EINVAL, "chunk rows %d above %d", *cr, kA2aMaxChunkRows);
+  *nch = (T_r + *cr - 1) / *cr;
+  if ((int64_t)E * *nch > ((int64_t)1 << 30)) return fail(SGT_EUNSUPPORTED, "%lld chunks", (long long)(E * *nch));
+  return SGT_OK;
+}
+
+sgt_status a2a_rows_ok(int64_t T_r, int64_t H, int esz) {
+  if (H < 0) return fail(SGT_EINVAL, "negative H");
+  if ((H * esz) % 16) return fail(SGT_EINVAL, "a row (H = %lld elements) must be a multiple of 16 bytes", (long long)H);
+  if (T_r * H * esz >= ((int64_t)1 << 31)) return fail(SGT_EUNSUPPORTED, "a block of T_r rows is 2 GiB or more");
+  return SGT_OK;
+}
+
+A2aArgs a2a_args(sgt_ctx* ctx, const sgt_opts& o, int W, int64_t T_r, int64_t row_bytes, int E, int k, int cr,
+                 int64_t nch, int mode, uint32_t* flags, uint32_t e) {
+  A2aArgs a{};
+  a.counts = ctx->d_a2a_counts;
+  a.flags = flags;
+  a.status = ctx->d_status;
+  a.T_r = T_r; a.row_bytes = row_bytes;
+  a.W = W; a.E = E; a.E_l = E / W; a.k = k; a.rank = o.rank; a.chunk_rows = cr; a.n_chunks = (int32_t)nch;
+  a.mode = mode;
+  a.n_send = (int32_t)(E * nch);
+  a.withhold = o.withhold_peer;
+  a.epoch = e;
+  // 100 MHz ticks per row on a link of peer_gbps GB/s (= peer_gbps * 1e3 bytes per microsecond)
+  a.ticks_per_row = o.peer_gbps > 0 ? (double)row_bytes / (o.peer_gbps * 1e3) * kTicksPerUs : 0.0;
+  a.timeout_ticks = timeout_ticks(o);
+  return a;
+}
+
+// The slowest link's last release (all of a link's blocks full) must come
+// within the call's time budget, so no sender workgroup waits longer than it.
+sgt_status a2a_pacing_ok(const A2aArgs& a) {
+  const double last = (double)a.E_l * (double)a.T_r * a.ticks_per_row;
+  if (last > (double)a.timeout_ticks)
+    return fail(SGT_EINVAL, "links of %.3g GB/s need up to %.0f us, beyond the %.0f us timeout",
+                a.ticks_per_row > 0 ? (double)a.row_bytes / a.ticks_per_row * kTicksPerUs / 1e3 : 0.0,
+                last / kTicksPerUs, (double)a.timeout_ticks / kTicksPerUs);
+  return SGT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t sgt_a2a_flag_count(int W, int64_t T_r, int E, const sgt_opts* opts) {
+  if (!opts || check_opts(opts, W < 1 ? 1 : W) != SGT_OK) return -1;
+  int cr;
+  int64_t nch;
+  if (a2a_plan(W, T_r, E, 1, *opts, &cr, &nch) != SGT_OK) return -1;
+  return (int64_t)E * nch;
+}
+
+sgt_status sgt_a2a_dispatch(sgt_ctx* ctx, const void* const* X, const int32_t* const* topk, void* recv,
+                            int32_t* recv_token, uint64_t* recv_count, uint32_t* flags, int W, int64_t T_r, int64_t H,
+                            int E, int k, const sgt_opts* opts, void* stream_) {
+  if (!ctx) return fail(SGT_EINVAL, "ctx is NULL");
+  sgt_status st = check_opts(opts, W < 1 ? 1 : W);
+  if (st != SGT_OK) return st;
+  const sgt_opts& o = *opts;
+  if (o.producer == SGT_PROD_PRESET) return fail(SGT_EINVAL, "a dispatch needs a producer mode (CU or serial)");
+  int cr;
+  int64_t nch;
+  if ((st = a2a_plan(W, T_r, E, k, o, &cr, &nch)) != SGT_OK) return st;
+  const int esz = elem_bytes(o.in_dtype);
+  if ((st = a2a_rows_ok(T_r, H, esz)) != SGT_OK) return st;
+  if (!topk || !recv_count || !aligned_to(recv_count, 8)) return fail(SGT_EINVAL, "topk or recv_count NULL or misaligned");
+  for (int p = 0; p < W; ++p)
+    if (!topk[p] || !aligned_to(topk[p], 4)) return fail(SGT_EINVAL, "topk[%d] NULL or misaligned", p);
+  if (T_r > 0) {
+    if (!X) return fail(SGT_EINVAL, "X is NULL");
+    for (int p = 0; p < W; ++p)
+      if (!X[p] || !aligned16(X[p])) return fail(SGT_EINVAL, "X[%d] NULL or not 16-byte aligned", p);
+    if (!recv || !aligned16(recv)) return fail(SGT_EINVAL, "recv NULL or not 16-byte aligned");
+    if (!recv_token || !aligned_to(recv_token, 4)) return fail(SGT_EINVAL, "recv_token NULL or misaligned");
+    if (!flags || !aligned_to(flags, 4)) return fail(SGT_EINVAL, "flags NULL or misaligned");
+  }
+  std::lock_guard<std::mutex> lock(ctx->mu);
+  DeviceGuard g(ctx->device);
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const uint32_t e = ++ctx->epoch;
+  A2aArgs a = a2a_args(ctx, o, W, T_r, H * esz, E, k, cr, nch, 0, flags, e);
+  if ((st = a2a_pacing_ok(a)) != SGT_OK) return st;
+  for (int p = 0; p < W; ++p) {
+    a.src.p[p] = X ? X[p] : nullptr;
+    a.table.p[p] = topk[p];
+  }
+  a.dst = static_cast<char*>(recv);
+  a.lists = recv_token;
+  a.count_sig = recv_count;
+  if ((st = mark(o, 0, stream)) != SGT_OK) return st;
+  HIP_TRY(launch_a2a_scan(a, stream));
+  if (a.n_send > 0) HIP_TRY(launch_a2a(a, 0, stream));
+  if ((st = mark(o, 1, stream)) != SGT_OK) return st;
+  return finish(ctx, o, stream);
+}
+
+sgt_status sgt_a2a_combine(sgt_ctx* ctx, const void* const* back, const int32_t* topk, const float* gate, void* cbuf,
+                           int32_t* slot_of, float* out, uint32_t* flags, int W, int64_t T_r, int64_t H, int E, int k,
+                           const sgt_opts* opts, void* stream_) {
+  if (!ctx) return fail(SGT_EINVAL, "ctx is NULL");
+  sgt_status st = check_opts(opts, W < 1 ? 1 : W);
+  if (st != SGT_OK) return st;
+  const sgt_opts& o = *opts;
+  if (o.in_dtype != SGT_BF16 || o.out_dtype != SGT_F32)
+    return fail(SGT_EUNSUPPORTED, "the combine takes bf16 expert outputs and writes fp32");
+  int cr;
+  int64_t nch;
+  if ((st = a2a_plan(W, T_r, E, k, o, &cr, &nch)) != SGT_OK) return st;
+  if ((st = a2a_rows_ok(T_r, H, 2)) != SGT_OK) return st;
+  const bool preset = o.producer == SGT_PROD_PRESET;
+  if (T_r > 0) {
+    if (!topk || !gate || !slot_of || !aligned_to(topk, 4) || !aligned_to(gate, 4) || !aligned_to(slot_of, 4))
+      return fail(SGT_EINVAL, "topk, gate or slot_of NULL or misaligned");
+    if (!preset) {
+      if (!back) return fail(SGT_EINVAL, "back is NULL");
+      for (int q = 0; q < W; ++q)
+        if (!back[q] || !aligned16(back[q])) return fail(SGT_EINVAL, "back[%d] NULL or not 16-byte aligned", q);
+    }
+    if (!cbuf || !out || !aligned16(cbuf) || !aligned16(out)) return fail(SGT_EINVAL, "cbuf or out NULL or misaligned");
+    if (!flags || !aligned_to(flags, 4)) return fail(SGT_EINVAL, "flags NULL or misaligned");
+  }
+  std::lock_guard<std::mutex> lock(ctx->mu);
+  DeviceGuard g(ctx->device);
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const uint32_t e = ++ctx->epoch;
+  if (T_r == 0) return finish(ctx, o, stream);
+  A2aArgs a = a2a_args(ctx, o, W, T_r, H * 2, E, k, cr, nch, 1, flags, e);
+  if ((st = a2a_pacing_ok(a)) != SGT_OK) return st;
+  for (int q = 0; q < W; ++q) a.src.p[q] = back && !preset ? back[q] : nullptr;
+  a.table.p[0] = topk;
+  a.dst = static_cast<char*>(cbuf);
+  a.lists = slot_of;
+  a.gate = gate;
+  a.out = out;
+  const int rgrid = (int)std::max<int64_t>(1, o.consumer_cus > 0 ? o.consumer_cus
+                                                                 : std::min<int64_t>((T_r + 3) / 4, ctx->n_cu / 2));
+  if ((st = mark(o, 0, stream)) != SGT_OK) return st;
+  HIP_TRY(launch_a2a_scan(a, stream));
+  if (preset) {
+    // the expert outputs are already in cbuf: every chunk flag set, then the receiver alone
+    HIP_TRY(launch_fill_u32(flags, E * nch, e, stream));
+    A2aArgs r = a;
+    r.n_send = 0;
+    HIP_TRY(launch_a2a(r, rgrid, stream));
+  } else if (o.producer == SGT_PROD_SERIAL) {
+    HIP_TRY(launch_a2a(a, 0, stream));
+    A2aArgs r = a;
+    r.n_send = 0;
+    HIP_TRY(launch_a2a(r, rgrid, stream));
+  } else {
+    HIP_TRY(launch_a2a(a, rgrid, stream));
+  }
+  if ((st = mark(o, 1, stream)) != SGT_OK) return st;
   return finish(ctx, o, stream);
 }
 

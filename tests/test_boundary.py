@@ -104,3 +104,15 @@ def test_flag_counts_and_argument_errors():
     assert sgt.ring_flag_count(1, 16) == (0, 16)
     with pytest.raises(sgt.SgtError):
         sgt.ring_flag_count(4, 4 * 6)                                   # chunk not a multiple of 4
+
+
+def test_a2a_flag_counts():
+    import signal_gated_tiled_amd as sgt
+    assert sgt.a2a_flag_count(8, 512, 64) == 64 * 16                     # 32-row chunks by default
+    assert sgt.a2a_flag_count(4, 37, 8, flag_rows=5) == 8 * 8             # ragged last chunk
+    assert sgt.a2a_flag_count(2, 0, 6) == 0
+    for bad in (dict(W=8, T_r=64, E=60), dict(W=8, T_r=64, E=8 * 4097), dict(W=65, T_r=8, E=65)):
+        with pytest.raises(sgt.SgtError):
+            sgt.a2a_flag_count(bad["W"], bad["T_r"], bad["E"])            # E % W, E too large, W > 64
+    with pytest.raises(sgt.SgtError):
+        sgt.a2a_flag_count(8, 64, 64, flag_rows=1025)                    # chunk above 1024 rows
