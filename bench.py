@@ -407,6 +407,129 @@ def bench_ring(ctx, up, args, torch, sgt, I):
     return res
 
 
+def moe_routing(ctx, up, torch, sgt, I):
+    """(expert_off, row_token, topk_ids) of the MoE workload's tokens from one MoE AllGather + grouped GEMM call
+    (the library's GPU routing)."""
+    m = I.MOE
+    dev = "cuda:0"
+    sh_h, We_h, lg_h = I.make_moe(m)
+    Xg = torch.empty((m.T, m.H), dtype=torch.bfloat16, device=dev)
+    Y = torch.empty((m.T * m.topk, m.I), dtype=torch.float32, device=dev)
+    off = torch.empty(m.E + 1, dtype=torch.int32, device=dev)
+    rt = torch.empty(m.T * m.topk, dtype=torch.int32, device=dev)
+    ids = torch.empty((m.T, m.topk), dtype=torch.int32, device=dev)
+    fl = torch.zeros(sgt.ag_flag_count(m.W, m.T, m.H), dtype=torch.int32, device=dev)
+    ctx.moe_ag_gemm([up(s) for s in sh_h], up(We_h), up(lg_h), Xg, Y, off, rt, ids, fl, topk=m.topk, blocking=True)
+    return off, rt, ids
+
+
+def bench_a2a(ctx, up, args, torch, sgt, I, tables):
+    """Expert-parallel AllToAll of the same MoE layer on rank 0 (W 8, 512 tokens per rank, hidden 2048 bf16,
+    top-8 of 64 experts, 8 per rank, 32-row chunks): the dispatch and the combine, each with links at 50 GB/s
+    per peer and unthrottled, against the link floor (the busiest link's bytes over its rate) and HBM."""
+    import numpy as np
+    w = I.A2A
+    W, T_r, H, E, k = w.W, w.tokens_per_rank, w.H, w.E, w.topk
+    E_l = E // W
+    rank = 0
+    dev = "cuda:0"
+    _, _, ids = tables   # the MoE AllGather side's GPU routing of the layer's 4096 tokens (T x k)
+    X_h, _, gate_h, back_h = I.make_a2a(w)
+    X = [up(x) for x in X_h]
+    topk = [ids[p * T_r:(p + 1) * T_r].contiguous() for p in range(W)]
+    gate = up(gate_h[rank * T_r:(rank + 1) * T_r])
+    back = [up(b) for b in back_h]
+    recv = torch.empty((E_l, W, T_r, H), dtype=torch.bfloat16, device=dev)
+    tok = torch.empty((E_l, W, T_r), dtype=torch.int32, device=dev)
+    cnt = torch.zeros((E_l, W), dtype=torch.int64, device=dev)
+    nf = sgt.a2a_flag_count(W, T_r, E, flag_rows=w.chunk_rows)
+    dfl = torch.zeros(nf, dtype=torch.int32, device=dev)
+    cbuf = torch.empty((E, T_r, H), dtype=torch.bfloat16, device=dev)
+    slot = torch.empty((T_r, k), dtype=torch.int32, device=dev)
+    out = torch.empty((T_r, H), dtype=torch.float32, device=dev)
+    cfl = torch.zeros(nf, dtype=torch.int32, device=dev)
+    row = H * 2
+
+    def disp(**kw):
+        def fn(i, ev):
+            ctx.a2a_dispatch(X, topk, recv, tok, cnt, dfl, E, rank=rank, flag_rows=w.chunk_rows,
+                             consumer_events=ev, **kw)
+        return fn
+
+    def comb(**kw):
+        def fn(i, ev):
+            ctx.a2a_combine(back if kw.get("producer") != "preset" else None, topk[rank], gate, cbuf, slot, out,
+                            cfl, W, rank=rank, flag_rows=w.chunk_rows, consumer_events=ev, **kw)
+        return fn
+
+    res = {"workload": w.name, "W": W, "tokens_per_rank": T_r, "H": H, "E": E, "topk": k, "rank": rank,
+           "chunk_rows": w.chunk_rows, "routing": "the MoE AllGather side's GPU routing of the same 4096 tokens"}
+    n_steps = max(10, args.steps // 2)
+    # dispatch
+    d_link = {}
+    for name, kw in (("paced_50GBps", dict(peer_gbps=w.peer_gbps)), ("unthrottled", dict())):
+        step, _, kern = timed(disp(**kw), n_steps, 3, torch, ctx)
+        d_link[name] = {"step_ms": step, "kernel_ms": spread(kern)}
+    counts = (cnt.cpu().numpy() & 0xFFFFFFFF).astype(np.int64)           # E_l x W
+    link_rows = counts.sum(axis=0)                                        # rows per source link
+    remote = [p for p in range(W) if p != rank]
+    floor_us = max(link_rows[p] for p in remote) * row / (w.peer_gbps * 1e3)
+    rows = int(counts.sum())
+    # algorithmic bytes: every received row read once and written once, the W routing tables read, the
+    # token lists and count packets written
+    d_bytes = 2 * rows * row + W * T_r * k * 4 + rows * 4 + E * 8
+    d_link["paced_50GBps"]["link_floor_us"] = floor_us
+    d_link["paced_50GBps"]["efficiency_vs_link_floor"] = floor_us / (d_link["paced_50GBps"]["kernel_ms"]["median"]
+                                                                     * 1e3)
+    u = d_link["unthrottled"]["kernel_ms"]["median"]
+    d_link["unthrottled"]["hbm_gbps"] = d_bytes / (u * 1e-3) / 1e9
+    d_link["unthrottled"]["hbm_frac"] = d_bytes / (u * 1e-3) / 1e9 / PEAK_HBM_GBS
+    d_link["rows_received"] = rows
+    d_link["rows_per_link_min_max"] = [int(link_rows.min()), int(link_rows.max())]
+    d_link["algorithmic_bytes"] = d_bytes
+    # spot check: a few received blocks against the tokens they name (bits)
+    for l, p in ((0, 1), (E_l - 1, W - 1), (3, rank)):
+        n = int(counts[l, p])
+        assert torch.equal(recv[l, p, :n].view(torch.int16), X[p][tok[l, p, :n].long()].view(torch.int16)), \
+            "dispatch block (%d, %d)" % (l, p)
+    res["dispatch"] = d_link
+    # combine
+    c_res = {}
+    for name, kw in (("paced_50GBps", dict(peer_gbps=w.peer_gbps)),
+                     ("serial_50GBps", dict(peer_gbps=w.peer_gbps, producer="serial")),
+                     ("unthrottled", dict()), ("receiver_alone", dict(producer="preset"))):
+        step, _, kern = timed(comb(**kw), n_steps, 3, torch, ctx)
+        c_res[name] = {"step_ms": step, "kernel_ms": spread(kern)}
+    ids_r = topk[rank].cpu().numpy()
+    n_e = np.array([int(((ids_r == e).any(axis=1)).sum()) for e in range(E)])
+    c_link = n_e.reshape(W, E_l).sum(axis=1)                              # rows per owner link
+    c_floor = max(c_link[q] for q in remote) * row / (w.peer_gbps * 1e3)
+    c_res["paced_50GBps"]["link_floor_us"] = c_floor
+    c_res["paced_50GBps"]["efficiency_vs_link_floor"] = c_floor / (c_res["paced_50GBps"]["kernel_ms"]["median"]
+                                                                   * 1e3)
+    c_res["serial_50GBps"]["link_floor_us"] = c_floor
+    # receiver bytes: k bf16 rows read and one fp32 row written per token, the routing, gate and slot tables
+    r_bytes = T_r * k * row + T_r * H * 4 + T_r * k * 12
+    ra = c_res["receiver_alone"]["kernel_ms"]["median"]
+    c_res["receiver_alone"]["hbm_gbps"] = r_bytes / (ra * 1e-3) / 1e9
+    c_res["receiver_alone"]["hbm_frac"] = r_bytes / (ra * 1e-3) / 1e9 / PEAK_HBM_GBS
+    c_res["receiver_algorithmic_bytes"] = r_bytes
+    c_res["rows_per_link_min_max"] = [int(c_link.min()), int(c_link.max())]
+    # spot check: token 0's output from its picks' rows in the receive buffer (fp32 on the device)
+    s0 = slot[0].long()
+    e0 = topk[rank][0].long()
+    ref0 = torch.zeros(H, dtype=torch.float32, device=dev)
+    for j in range(k):
+        ref0 = torch.addcmul(ref0, gate[0, j].expand(H), cbuf[e0[j], s0[j]].float())
+    assert torch.allclose(out[0], ref0, rtol=1e-5, atol=1e-5), "combine token 0"
+    res["combine"] = c_res
+    res["note"] = ("senders simulate the peers: each (link, expert) block travels in 32-row chunks, each flagged "
+                   "when its link would deliver it; the combine receiver waits per token only on the chunks "
+                   "of its picks")
+    del recv, cbuf, back, X
+    return res
+
+
 def bench_moe(ctx, up, args, torch, sgt, I, lay):
     """MoE AllGather + grouped GEMM (T 4096 tokens in 8 shards, H 2048, I 768, 64 experts, top-8, Zipf-skewed
     logits), overlapped at 50 GB/s per simulated peer; the grouped consumer's MFMA and HBM roofline fractions."""
@@ -539,6 +662,8 @@ def main():
     ap.add_argument("--ll-only", action="store_true", help="only the low-latency AllGather comparison")
     ap.add_argument("--no-ring", action="store_true", help="skip the ring AllReduce")
     ap.add_argument("--ring-only", action="store_true", help="only the ring AllReduce")
+    ap.add_argument("--no-a2a", action="store_true", help="skip the expert-parallel AllToAll")
+    ap.add_argument("--a2a-only", action="store_true", help="only the expert-parallel AllToAll")
     ap.add_argument("--b-layout", default="nk", choices=["kn", "nk"],
                     help="B as N x K (a Linear layer's weight, default) or K x N")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -575,6 +700,11 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
+    if args.a2a_only:
+        with sgt.Context(0) as c:
+            print(json.dumps({"a2a": bench_a2a(c, up, args, torch, sgt, I, moe_routing(c, up, torch, sgt, I))}),
+                  flush=True)
+        return
     if args.ll_only or args.ring_only:
         with sgt.Context(0) as c:
             if args.ll_only:
@@ -794,6 +924,8 @@ def main():
     if not args.no_moe:
         detail["moe_ag_grouped"], tables = bench_moe(ctx, up, args, torch, sgt, I, lay)
         detail["moe_gemm_rs"] = bench_moe_rs(ctx, up, args, torch, sgt, I, lay, tables)
+        if not args.no_a2a:
+            detail["a2a"] = bench_a2a(ctx, up, args, torch, sgt, I, tables)
         del tables
 
     cpu = None

@@ -36,7 +36,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kA2aThreads = 256;
 constexpr int kA2aUnroll = 8;    // 16-byte loads in flight per thread in the copy
 constexpr int kRecvUnits = 2;    // 16-byte units (8 bf16) per lane per pass of the combine
-constexpr int kRecvPicks = 4;    // picks whose rows are loaded together
+constexpr int kRecvPicks = 8;    // picks whose rows are loaded together
 constexpr uint32_t kOob = 0x80000000u;  // past every buffer range (ranges are below 2^31 bytes)
 
 __device__ inline __amdgpu_buffer_rsrc_t a2a_rsrc(const void* base, uint32_t bytes) {
@@ -49,44 +49,95 @@ __device__ inline __amdgpu_buffer_rsrc_t a2a_rsrc(const void* base, uint32_t byt
 // count packet; combine writes each such pick's position to slot_of (and
 // workgroup 0 marks picks of ids outside [0, E) with -1).  Both write the
 // block's count to the context's count table.
+//
+// A pass covers kScanSub x 256 tokens: every thread loads the ids of its
+// kScanSub tokens first (16-byte loads when k is 4 or 8), so a pass costs
+// one memory round trip; the positions then come from one ballot per
+// sub-pass and one barrier for all of them.
+constexpr int kScanSub = 4;
+
+__device__ __forceinline__ void scan_mark(const A2aArgs& a, int b, int e, bool combine, int64_t t, int j, int v,
+                                          int pos) {
+  if (!combine) return;
+  if (v == e) a.lists[t * a.k + j] = pos;
+  else if (b == 0 && (v < 0 || v >= a.E)) a.lists[t * a.k + j] = -1;
+}
+
 __global__ void __launch_bounds__(kA2aThreads) a2a_scan_kernel(A2aArgs a) {
-  __shared__ int wsum[kA2aThreads / 64];
+  __shared__ int wsum[kScanSub][kA2aThreads / 64];
   const int b = blockIdx.x;
   const bool combine = a.mode == 1;
   const int e = combine ? b : a.rank * a.E_l + b / a.W;
   const int32_t* tab = static_cast<const int32_t*>(combine ? a.table.p[0] : a.table.p[b % a.W]);
   const int k = a.k;
+  const bool vec = (k == 4 || k == 8) && ((reinterpret_cast<uintptr_t>(tab) & 15u) == 0);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int running = 0;
-  for (int64_t t0 = 0; t0 < a.T_r; t0 += kA2aThreads) {
-    const int64_t t = t0 + threadIdx.x;
-    bool hit = false;
-    if (t < a.T_r) {
-      for (int j = 0; j < k; ++j) {
-        const int v = tab[t * k + j];
-        hit |= v == e;
-        if (combine && b == 0 && (v < 0 || v >= a.E)) a.lists[t * k + j] = -1;
+  for (int64_t t0 = 0; t0 < a.T_r; t0 += kA2aThreads * kScanSub) {
+    bool hit[kScanSub];
+    int4 v[kScanSub][2];
+    if (vec) {
+      // all loads of the pass in flight before any use
+#pragma unroll
+      for (int i = 0; i < kScanSub; ++i) {
+        const int64_t t = t0 + i * kA2aThreads + threadIdx.x;
+        const int4* row = reinterpret_cast<const int4*>(tab + t * k);
+        const int4 none = make_int4(-1, -1, -1, -1);
+        v[i][0] = t < a.T_r ? row[0] : none;
+        v[i][1] = t < a.T_r && k == 8 ? row[1] : none;
+      }
+#pragma unroll
+      for (int i = 0; i < kScanSub; ++i) {
+        hit[i] = false;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          hit[i] |= (v[i][q].x == e) | (v[i][q].y == e) | (v[i][q].z == e) | (v[i][q].w == e);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kScanSub; ++i) {
+        const int64_t t = t0 + i * kA2aThreads + threadIdx.x;
+        hit[i] = false;
+        if (t < a.T_r)
+          for (int j = 0; j < k; ++j) hit[i] |= tab[t * k + j] == e;
       }
     }
-    const uint64_t bal = __ballot(hit);
-    const int pre = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) wsum[wave] = __popcll(bal);
+    int pre[kScanSub];
+#pragma unroll
+    for (int i = 0; i < kScanSub; ++i) {
+      const uint64_t bal = __ballot(hit[i]);
+      pre[i] = __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) wsum[i][wave] = __popcll(bal);
+    }
     __syncthreads();
-    int off = running, tot = 0;
-    for (int w = 0; w < kA2aThreads / 64; ++w) {
-      if (w < wave) off += wsum[w];
-      tot += wsum[w];
-    }
-    if (hit) {
-      const int pos = off + pre;
-      if (combine) {
-        for (int j = 0; j < k; ++j)
-          if (tab[t * k + j] == e) a.lists[t * k + j] = pos;
-      } else {
-        a.lists[(int64_t)b * a.T_r + pos] = (int32_t)t;
+    int base = running;
+#pragma unroll
+    for (int i = 0; i < kScanSub; ++i) {
+      int off = base, tot = 0;
+      for (int w = 0; w < kA2aThreads / 64; ++w) {
+        if (w < wave) off += wsum[i][w];
+        tot += wsum[i][w];
       }
+      const int64_t t = t0 + i * kA2aThreads + threadIdx.x;
+      const int pos = off + pre[i];
+      if (hit[i] && !combine) a.lists[(int64_t)b * a.T_r + pos] = (int32_t)t;
+      if (combine && t < a.T_r) {
+        if (vec) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            if (q * 4 >= k) break;
+            scan_mark(a, b, e, true, t, q * 4 + 0, v[i][q].x, pos);
+            scan_mark(a, b, e, true, t, q * 4 + 1, v[i][q].y, pos);
+            scan_mark(a, b, e, true, t, q * 4 + 2, v[i][q].z, pos);
+            scan_mark(a, b, e, true, t, q * 4 + 3, v[i][q].w, pos);
+          }
+        } else {
+          for (int j = 0; j < k; ++j) scan_mark(a, b, e, true, t, j, tab[t * k + j], pos);
+        }
+      }
+      base += tot;
     }
-    running += tot;
+    running = base;
     __syncthreads();  // wsum is rewritten by the next pass
   }
   if (threadIdx.x == 0) {
