@@ -874,7 +874,7 @@ def main():
         rs_pair, g_pair = statistics.median(rs_l), statistics.median(g_l)
         red_bytes = (r.M // r.W) * r.N * 4 * (r.W + 1)   # read local block + W-1 peers, write C_shard
         # reduction window from the kernel's own stamps (100 MHz clock): first reduction start to last end
-        nw = sgt.trace_words(r.W, r.M, r.K, r.N)
+        nw = sgt.rs_trace_words(r.W, r.M, r.N)
         tr = torch.zeros(nw, dtype=torch.int64, device=dev)
         ctx.gemm_rs(A, Brs, parts, P, Cs, gf, pf, rank=rank, b_layout=lay, trace=tr.data_ptr(), blocking=True)
         t = tr.cpu().numpy().view(np.uint64).reshape(-1, 3)
@@ -902,10 +902,10 @@ def main():
             "reduction_algorithmic_bytes": red_bytes,
             "reduction_window_us": float(red_win_us),
             "reduction_window_gbs": red_bytes / (red_win_us * 1e-6) / 1e9,
-            "reduction_tile_us": spread(red_item_us.tolist()),
-            "reduction_note": "window = first reduction-tile start to last end in one traced call (the tiles run "
-                              "while other workgroups finish GEMM tiles, so the rate is a lower bound); tile time "
-                              "includes its flag wait",
+            "reduction_item_us": spread(red_item_us.tolist()),
+            "reduction_note": "window = first reduction-item start to last end in one traced call (the items run "
+                              "while other workgroups finish GEMM tiles, so the rate is a lower bound); an item is "
+                              "a 32-row band of a 128 x 128 signal tile, its time includes its flag wait",
             "gemm_tiles_end_us": float((gem_t[:, 1].max() - gem_t[:, 0].min()) / 100.0),
             "paced_50gbps": {"peer_gbps": gbps_rs, "step_ms": pc_ms, "kernel_ms": spread(pc_l),
                              "tflops": r.flops / (pc_ms * 1e-3) / 1e12,

@@ -495,10 +495,16 @@ SGT_API int64_t sgt_a2a_flag_count(int W, int64_t T_r, int E, const sgt_opts* op
 /* Words of the optional trace buffer for an AllGather call: per consumer tile
  * 4 x uint64 {wait start, flag seen, tile end, workgroup}; then per signal tile
  * 1 x uint64 release time.  Times are the 100 MHz constant GPU clock.
- * A GEMM+ReduceScatter call with opts->trace set writes 3 x uint64 {start, end,
- * workgroup} per work item: first the GEMM tiles ((W * ceil(M/W/256)) *
- * ceil(N/256), local block first), then the reduction tiles of the local block. */
+ * (A GEMM+ReduceScatter call's trace is sized by sgt_rs_trace_words.) */
 SGT_API int64_t sgt_trace_words(int W, int64_t M, int64_t K, int64_t N, const sgt_opts* opts);
+
+/* Words of the optional trace buffer for a GEMM+ReduceScatter call (M x N
+ * output, W row blocks, opts->rs_tile), or -1 for an invalid shape: 3 x uint64
+ * {start, end, workgroup} per work item, first the GEMM tiles ((W *
+ * ceil(M/W/256)) * ceil(N/256), local block first), then the reduction items:
+ * each signal tile of the local block (tile-row-major) cut into row bands of
+ * 32 rows (the whole tile when rs_tile <= 32), band-minor. */
+SGT_API int64_t sgt_rs_trace_words(int W, int64_t M, int64_t N, const sgt_opts* opts);
 
 #ifdef __cplusplus
 }

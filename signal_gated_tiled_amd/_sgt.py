@@ -103,6 +103,8 @@ def lib() -> ctypes.CDLL:
                                       ctypes.POINTER(Opts), P]
         L.sgt_a2a_flag_count.argtypes = [ctypes.c_int, I64, ctypes.c_int, ctypes.POINTER(Opts)]
         L.sgt_a2a_flag_count.restype = I64
+        L.sgt_rs_trace_words.argtypes = [ctypes.c_int, I64, I64, ctypes.POINTER(Opts)]
+        L.sgt_rs_trace_words.restype = I64
         for f in ("sgt_ctx_create", "sgt_ctx_destroy", "sgt_sync", "sgt_ag_gemm", "sgt_rs_flag_count", "sgt_gemm_rs",
                   "sgt_gemm_rs_paced", "sgt_moe_ag_gemm", "sgt_moe_gemm_rs",
                   "sgt_moe_gemm_rs_paced", "sgt_allgather", "sgt_ll_allgather", "sgt_ring_allreduce",
@@ -250,6 +252,15 @@ def a2a_flag_count(W: int, T_r: int, E: int, **kw) -> int:
     n = lib().sgt_a2a_flag_count(W, T_r, E, ctypes.byref(o))
     if n < 0:
         raise SgtError(SGT_EINVAL, "invalid AllToAll shape or options")
+    return int(n)
+
+
+def rs_trace_words(W: int, M: int, N: int, rs_tile: int = 0) -> int:
+    """Words (uint64) of the optional trace buffer of a GEMM+ReduceScatter call."""
+    o = make_opts(rs_tile=rs_tile)
+    n = lib().sgt_rs_trace_words(W, M, N, ctypes.byref(o))
+    if n < 0:
+        raise SgtError(SGT_EINVAL, "invalid GEMM+ReduceScatter shape")
     return int(n)
 
 

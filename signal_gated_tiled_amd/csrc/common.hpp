@@ -70,6 +70,7 @@ struct RsArgs {
   int32_t rs_tm, rs_tn;     // signal tiles of one block (rows, cols)
   int32_t b_layout;
   int32_t n_gemm_tiles, n_red_items;
+  int32_t red_split;        // reduction items per signal tile: row bands of rs_tile / red_split rows
   uint32_t epoch;
   int32_t tile_waves;
   uint64_t timeout_ticks;

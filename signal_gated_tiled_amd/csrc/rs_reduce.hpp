@@ -4,10 +4,12 @@
 // ReduceScatter with the reduction synchronized by signals), shared by the
 // dense GEMM+ReduceScatter and the MoE combine kernels.
 //
-// Item j is signal tile j of this rank's row block: wait for its flag in
-// gflags (the local partial P) and for the W-1 peer flags, then
-// C_shard = P[local] + sum of the peers' partials, in fixed order (local, then
-// peers by ascending rank).
+// Item j is row band j % red_split of signal tile j / red_split of this
+// rank's row block: wait for the tile's flag in gflags (the local partial P)
+// and for its W-1 peer flags, then C_shard = P[local] + sum of the peers'
+// partials over the band's rows, in fixed order (local, then peers by
+// ascending rank).  Bands of a few tens of rows keep the items small enough
+// to spread evenly over the workgroups (each streams at a bounded rate).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,17 +23,37 @@ namespace sgt {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ inline void do_reduce_item(const RsArgs& a, int j, int* ok) {
-  const int ti = j / a.rs_tn, tj = j % a.rs_tn;
+  // item j: row band `rband` of signal tile jt (red_split bands per tile)
+  const int jt = j / a.red_split, rband = j % a.red_split;
+  const int ti = jt / a.rs_tn, tj = jt % a.rs_tn;
   const int64_t gtn = (a.N + a.rs_tile - 1) / a.rs_tile;
   const int64_t row0 = (int64_t)a.rank * a.block_rows + (int64_t)ti * a.rs_tile;  // row in P
-  if (threadIdx.x == 0) {
-    bool good = wait_flags_one_thread(a.gflags, (row0 / a.rs_tile) * gtn + tj, (row0 / a.rs_tile) * gtn + tj + 1,
-                                      a.epoch, a.timeout_ticks, a.status);
+  if (threadIdx.x < 64) {
+    // One lane per contribution, all polled at once: lane `rank` waits on the
+    // GEMM flag of the local tile, lane p on peer p's flag of the tile.
+    const int lane = threadIdx.x;
     const int64_t per = (int64_t)a.rs_tm * a.rs_tn;
-    for (int p = 0; p < a.W && good; ++p)
-      if (p != a.rank)
-        good = wait_flags_one_thread(a.pflags, p * per + j, p * per + j + 1, a.epoch, a.timeout_ticks, a.status);
-    *ok = good ? 1 : 0;
+    const int64_t gidx = (row0 / a.rs_tile) * gtn + tj, pidx = lane * per + jt;
+    const uint32_t* f = lane < a.W ? (lane == a.rank ? a.gflags + gidx : a.pflags + pidx) : nullptr;
+    bool mine = f == nullptr;
+    uint32_t v = 0;
+    bool good = true;
+    const uint64_t t0 = clock_ticks();
+    while (true) {
+      if (!mine) {
+        v = flag_peek(f);
+        mine = flag_is_set(v, a.epoch);
+      }
+      if (__all(mine)) break;
+      if (clock_ticks() - t0 > a.timeout_ticks) {  // the clock is a scalar read: uniform over the wave
+        if (!mine) report_timeout(a.status, lane == a.rank ? gidx : pidx, v, a.epoch);
+        good = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (good) acquire_agent();
+    if (lane == 0) *ok = good ? 1 : 0;
   }
   __syncthreads();
   if (!*ok) return;
@@ -52,12 +74,13 @@ __device__ inline void do_reduce_item(const RsArgs& a, int j, int* ok) {
   const __amdgpu_buffer_rsrc_t rP = make_rsrc(a.P + row0 * a.N, band);
   const __amdgpu_buffer_rsrc_t rC = make_rsrc(a.C_shard + (int64_t)ti * a.rs_tile * a.N, band);
   constexpr int R = 4;
-  for (int r0 = rr; r0 < a.rs_tile; r0 += R * rows_per_pass) {
+  const int band_rows = a.rs_tile / a.red_split, rb_end = (rband + 1) * band_rows;
+  for (int r0 = rband * band_rows + rr; r0 < rb_end; r0 += R * rows_per_pass) {
     uint32_t off[R];
 #pragma unroll
     for (int u = 0; u < R; ++u) {
       const int r = r0 + u * rows_per_pass;
-      off[u] = (col_ok && r < a.rs_tile) ? (uint32_t)(((int64_t)r * a.N + col) * 4) : kOOB;
+      off[u] = (col_ok && r < rb_end) ? (uint32_t)(((int64_t)r * a.N + col) * 4) : kOOB;
     }
     f32x4_t s[R];
 #pragma unroll

@@ -390,6 +390,11 @@ sgt_status finish(sgt_ctx* ctx, const sgt_opts& o, hipStream_t stream) {
 
 }  // namespace
 
+// Reduction items per ReduceScatter signal tile: row bands of kRedBandRows
+// rows (the whole tile when it is shorter).
+constexpr int kRedBandRows = 32;
+int rs_red_split(int rs_tile) { return rs_tile > kRedBandRows ? rs_tile / kRedBandRows : 1; }
+
 extern "C" {
 
 const char* sgt_version(void) { return "sgt 0.1 gfx950"; }
@@ -637,6 +642,17 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   return finish(ctx, o, stream);
 }
 
+int64_t sgt_rs_trace_words(int W, int64_t M, int64_t N, const sgt_opts* opts) {
+  int64_t ng;
+  if (sgt_rs_flag_count(W, M, N, opts, &ng, nullptr) != SGT_OK) return -1;
+  const int rt = opts && opts->rs_tile > 0 ? opts->rs_tile : 128;
+  const int bm = rs_gemm_tile();
+  const int64_t br = M / W, tn = (N + bm - 1) / bm;
+  const int64_t n_gemm = (int64_t)W * ((br + bm - 1) / bm) * tn;
+  const int64_t n_red = (br / rt) * ((N + rt - 1) / rt) * rs_red_split(rt);
+  return 3 * (n_gemm + n_red);
+}
+
 sgt_status sgt_rs_flag_count(int W, int64_t M, int64_t N, const sgt_opts* opts, int64_t* gflags_n,
                              int64_t* pflags_n) {
   if (W < 1 || W > kMaxW || M < 0 || N < 0 || M % W) return fail(SGT_EINVAL, "bad GEMM+RS shape");
@@ -781,7 +797,8 @@ sgt_status gemm_rs_impl(sgt_ctx* ctx, const void* A_local, const void* B, const 
   a.rs_tile = rt; a.rs_tm = (int)(br / rt); a.rs_tn = (int)rs_tn;
   a.b_layout = o.b_layout;
   a.n_gemm_tiles = a.tiles_m * a.tiles_n;
-  a.n_red_items = a.rs_tm * a.rs_tn;
+  a.red_split = rs_red_split(rt);
+  a.n_red_items = a.rs_tm * a.rs_tn * a.red_split;
   a.epoch = e; a.timeout_ticks = timeout_ticks(o);
   a.tile_waves = o.tile_waves ? o.tile_waves : 8;
   a.red_counter = ctx->d_counters;
@@ -1131,7 +1148,8 @@ sgt_status moe_gemm_rs_impl(sgt_ctx* ctx, const void* Hg, const void* W2, const 
   rs.gflags = gflags; rs.pflags = pflags; rs.status = ctx->d_status; rs.trace = nullptr;
   rs.M = T; rs.N = H; rs.K = I; rs.block_rows = T / W; rs.W = W; rs.rank = o.rank;
   rs.rs_tile = 128; rs.rs_tm = (int)((T / W) / 128); rs.rs_tn = (int)((H + 127) / 128);
-  rs.n_red_items = rs.rs_tm * rs.rs_tn;
+  rs.red_split = rs_red_split(rs.rs_tile);
+  rs.n_red_items = rs.rs_tm * rs.rs_tn * rs.red_split;
   rs.epoch = e; rs.timeout_ticks = timeout_ticks(o);
   rs.red_counter = ctx->d_mrs_ctr + 1;
 
