@@ -116,3 +116,13 @@ def test_a2a_flag_counts():
             sgt.a2a_flag_count(bad["W"], bad["T_r"], bad["E"])            # E % W, E too large, W > 64
     with pytest.raises(sgt.SgtError):
         sgt.a2a_flag_count(8, 64, 64, flag_rows=1025)                    # chunk above 1024 rows
+
+
+def test_rs_trace_words():
+    import signal_gated_tiled_amd as sgt
+    # Qwen shape: 8 blocks x 4 x 20 GEMM tiles of 256 x 256, 8 x 40 signal tiles of 128 x 128 in 32-row bands
+    assert sgt.rs_trace_words(8, 8192, 5120) == 3 * (8 * 4 * 20 + 8 * 40 * 4)
+    assert sgt.rs_trace_words(4, 1024, 392, rs_tile=64) == 3 * (4 * 1 * 2 + 4 * 7 * 2)
+    assert sgt.rs_trace_words(4, 1024, 392, rs_tile=32) == 3 * (4 * 1 * 2 + 8 * 13)
+    with pytest.raises(sgt.SgtError):
+        sgt.rs_trace_words(4, 1000, 392)                               # M % W != 0

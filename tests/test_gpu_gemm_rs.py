@@ -89,6 +89,24 @@ def test_gemm_rs_bits_repeat(ctx):
     assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
 
 
+@pytest.mark.parametrize("rs_tile", [128, 64])
+def test_gemm_rs_trace_fills_exactly_its_words(ctx, rs_tile):
+    """A traced call writes every one of sgt_rs_trace_words' words (one record per GEMM tile and reduction
+    item) and nothing past them; results are the untraced call's bits."""
+    w = I.RSWorkload("t", W=4, M=1024, K=256, N=392, seed_index=26)
+    A, B, parts = I.make_rs(w)
+    nw = sgt.rs_trace_words(w.W, w.M, w.N, rs_tile=rs_tile)
+    canary = 0x5A5A5A5A5A5A5A5A
+    tr = torch.full((nw + 64,), canary, dtype=torch.int64, device="cuda:0")
+    a = run_rs(ctx, A, B, parts, 1, rs_tile=rs_tile, trace=tr.data_ptr())
+    b = run_rs(ctx, A, B, parts, 1, rs_tile=rs_tile)
+    t = tr.cpu().numpy()
+    assert (t[nw:] == canary).all(), "trace written past sgt_rs_trace_words"
+    rec = t[:nw].reshape(-1, 3)
+    assert (rec[:, 0] != canary).all() and (rec[:, 1] >= rec[:, 0]).all(), "a work item left no record"
+    assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
 def test_gemm_rs_rejects_bad_tile(ctx):
     w = I.RSWorkload("t", W=4, M=1024, K=64, N=256, seed_index=25)
     A, B, parts = I.make_rs(w)
