@@ -627,6 +627,15 @@ def bench_moe_rs(ctx, up, args, torch, sgt, I, lay, tables):
     pc_ms, _, pc_k = timed(fn_paced, max(4, args.steps // 2), 2, torch, ctx)
     assert torch.equal(inbox[1], parts[1]), "paced inbox mismatch"
     del inbox
+    # Y stored in bf16 (half the bytes written and read back; P and C stay fp32)
+    Yb = torch.empty((rows, m.H), dtype=torch.bfloat16, device=dev)
+
+    def fn_b(i, ev):
+        ctx.moe_gemm_rs(Hg, W2, gate, ids, off, rt, parts, Yb, P, Cs, gf, pf, rank=rank, b_layout=lay,
+                        consumer_events=ev)
+    yb_ms, _, yb_k = timed(fn_b, args.steps, args.warmup, torch, ctx)
+    hbm_b = rows * m.I * 2 + m.E * m.I * m.H * 2 + 2 * rows * m.H * 2 + m.T * m.H * 4 + (m.W + 1) * (m.T // m.W) * m.H * 4
+    del Yb
     flops = m.flops
     # algorithmic HBM bytes: Hg and W2 read once, Y written and read back once, P written, this rank's block of
     # P read back with the W-1 peers' blocks, C written
@@ -644,6 +653,10 @@ def bench_moe_rs(ctx, up, args, torch, sgt, I, lay, tables):
         "paced_50gbps": {"peer_gbps": gbps, "step_ms": pc_ms, "kernel_ms": spread(pc_k),
                          "tflops": flops / (pc_ms * 1e-3) / 1e12,
                          "link_floor_us": (m.T // m.W) * m.H * 4 / (gbps * 1e9) * 1e6},
+        "y_bf16": {"step_ms": yb_ms, "kernel_ms": spread(yb_k), "tflops": flops / (yb_ms * 1e-3) / 1e12,
+                   "algorithmic_hbm_bytes": hbm_b,
+                   "kernel_hbm_frac": hbm_b / (statistics.median(yb_k) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                   "kernel_mfma_frac": flops / (statistics.median(yb_k) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
         "note": "one persistent kernel: grouped GEMM tiles, gate-weighted combine tiles gated on their GEMM "
                 "column, signal-gated reduction of this rank's block; peers' partials resident (and paced)",
     }

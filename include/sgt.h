@@ -277,7 +277,7 @@ SGT_API sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, co
  * page, "GEMM + ReduceScatter overlap": the GEMM signals output tiles and the
  * reduction waits for exactly the tiles it reads).  One GPU's share: this
  * rank's slice of the intermediate width of every expert.
- *   Y[r]   = Hg[r] * W2[e(r)]                    (fp32; e(r) = the expert of grouped row r)
+ *   Y[r]   = Hg[r] * W2[e(r)]                    (fp32 accumulation; e(r) = the expert of grouped row r)
  *   P[t]   = sum_j gate[t][j] * Y[row(t, j)]     (j ascending; row(t, j) = the row of group
  *                                                 topk_ids[t][j] that holds token t)
  *   C_shard = P[rank block] + sum_{p != rank} partials[p]   (p ascending)
@@ -286,11 +286,14 @@ SGT_API sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, co
  * W2: E x I x H (SGT_KN) or E x H x I (SGT_NK) bf16.  gate: T x topk fp32.
  * partials: host array of W device pointers to (T/W) x H fp32 (entry [rank]
  *     not read): the peers' combined partials for this rank's tokens, resident.
- * Y: (T * topk) x H fp32, out.  partial_out: T x H fp32, out (P; block p is
- *     this rank's push to rank p).  C_shard: (T/W) x H fp32, out.
+ * Y: (T * topk) x H, out: fp32, or bf16 (round to nearest even) when
+ *     opts->out_dtype = SGT_BF16, which halves the bytes Y is written and read
+ *     back with (the combine then sums the rounded rows; P and C_shard stay
+ *     fp32).  partial_out: T x H fp32, out (P; block p is this rank's push to
+ *     rank p).  C_shard: (T/W) x H fp32, out.
  * gflags / pflags: as sgt_gemm_rs with M = T, N = H and rs_tile 128
  *     (sgt_rs_flag_count); pflags are set by the library (resident peers).
- * Requirements: bf16 in, fp32 out, 1 <= topk <= E <= 256, I and H multiples of
+ * Requirements: bf16 in, Y fp32 or bf16, 1 <= topk <= E <= 256, I and H multiples of
  *     8, T/W a multiple of 128, rows x H x 4 < 2^31, peer_gbps = 0 (paced peers:
  *     sgt_moe_gemm_rs_paced; here it is SGT_EUNSUPPORTED), tile_waves
  *     0 or 8, rs_tile 0 or 128; 16-byte aligned matrices and flags, 4-byte
@@ -302,7 +305,7 @@ SGT_API sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, co
  */
 SGT_API sgt_status sgt_moe_gemm_rs(sgt_ctx* ctx, const void* Hg, const void* W2, const float* gate,
                                    const int32_t* topk_ids, const int32_t* expert_off, const int32_t* row_token,
-                                   const float* const* partials, float* Y, float* partial_out, float* C_shard,
+                                   const float* const* partials, void* Y, float* partial_out, float* C_shard,
                                    uint32_t* gflags, uint32_t* pflags, int W, int64_t T, int topk, int64_t I,
                                    int64_t H, int E, const sgt_opts* opts, void* stream);
 
@@ -320,7 +323,7 @@ SGT_API sgt_status sgt_moe_gemm_rs(sgt_ctx* ctx, const void* Hg, const void* W2,
  */
 SGT_API sgt_status sgt_moe_gemm_rs_paced(sgt_ctx* ctx, const void* Hg, const void* W2, const float* gate,
                                          const int32_t* topk_ids, const int32_t* expert_off, const int32_t* row_token,
-                                         const float* const* peer_blocks, float* const* inbox, float* Y,
+                                         const float* const* peer_blocks, float* const* inbox, void* Y,
                                          float* partial_out, float* C_shard, uint32_t* gflags, uint32_t* pflags,
                                          int W, int64_t T, int topk, int64_t I, int64_t H, int E,
                                          const sgt_opts* opts, void* stream);

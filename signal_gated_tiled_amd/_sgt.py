@@ -395,8 +395,9 @@ class Context:
 
     def moe_gemm_rs(self, Hg, W2, gate, topk_ids, expert_off, row_token, partials: Sequence, Y, partial_out,
                     C_shard, gflags, pflags, *, stream=None, inbox: Optional[Sequence] = None, **kw):
-        """MoE GEMM + ReduceScatter (combine side); see sgt_moe_gemm_rs.  With `inbox`, `partials` are the
-        peers' blocks and arrive into `inbox` at the simulated link rate (sgt_moe_gemm_rs_paced)."""
+        """MoE GEMM + ReduceScatter (combine side); see sgt_moe_gemm_rs.  Y may be fp32 or bf16 (its dtype sets
+        out_dtype).  With `inbox`, `partials` are the peers' blocks and arrive into `inbox` at the simulated link
+        rate (sgt_moe_gemm_rs_paced)."""
         dev = Hg.device
         W = len(partials)
         rows, n_in = Hg.shape
@@ -407,6 +408,7 @@ class Context:
         if rows != T * topk:
             raise ValueError("Hg has %d rows, expected T * topk = %d" % (rows, T * topk))
         kw.setdefault("in_dtype", _dtype_code(Hg))
+        kw.setdefault("out_dtype", _dtype_code(Y))   # Y fp32, or bf16 to halve its traffic
         o = make_opts(**kw)
         parts = (P * W)(*[_dev_ptr(p, "partials[%d]" % i, dev) if p is not None else 0
                           for i, p in enumerate(partials)])

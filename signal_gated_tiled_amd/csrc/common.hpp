@@ -89,7 +89,7 @@ struct MoeTile {
 struct MoeRsArgs {
   const uint16_t* Hg;        // rows x I bf16, grouped rows
   const uint16_t* W2;        // E x I x H (KN) or E x H x I (NK) bf16
-  float* Y;                  // rows x H fp32: each grouped row times its expert's weight
+  void* Y;                   // rows x H fp32 (or bf16): each grouped row times its expert's weight
   const float* gate;         // T x k
   const int32_t* topk_ids;   // T x k
   const int32_t* expert_off; // E + 1
@@ -102,6 +102,7 @@ struct MoeRsArgs {
   int64_t T, I, H, rows;
   int32_t E, k, tiles_n, tiles_cap;
   int32_t b_layout;
+  int32_t y_bf16;            // Y stored as bf16 (RNE) instead of fp32
   RsArgs rs;
 };
 

@@ -66,7 +66,26 @@ __global__ void moe_rs_prep_kernel(MoeRsArgs a) {
   }
 }
 
+// Four columns of grouped row `row` of Y as fp32 (an fp32 Y: one 16-byte
+// load; a bf16 Y: one 8-byte load of four bf16, widened exactly).
+template <bool kYbf16>
+__device__ __forceinline__ f32x4_t load_y4(__amdgpu_buffer_rsrc_t rY, int32_t row, int64_t H, int64_t col,
+                                           bool col_ok) {
+  if constexpr (kYbf16) {
+    const uint32_t off = col_ok ? (uint32_t)(((int64_t)row * H + col) * 2) : kOOB;
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t w = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rY, off, 0, 0));
+    const f32x4_t v = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+    return v;
+  } else {
+    const uint32_t off = col_ok ? (uint32_t)(((int64_t)row * H + col) * 4) : kOOB;
+    return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rY, off, 0, 0));
+  }
+}
+
 // Combine tile c of P: 128 tokens x 128 columns, column-major.
+template <bool kYbf16>
 __device__ void do_combine_item(const MoeRsArgs& a, int64_t c, uint32_t n_rt, int* ok) {
   const int64_t ptm = a.T / kCombTile;
   const int64_t cn = c / ptm, cm = c % ptm;
@@ -96,7 +115,7 @@ __device__ void do_combine_item(const MoeRsArgs& a, int64_t c, uint32_t n_rt, in
   const int c4 = threadIdx.x % cols4, rr = threadIdx.x / cols4;
   const int64_t col = cn * kCombTile + 4 * c4;
   const bool col_ok = col < a.H;
-  const __amdgpu_buffer_rsrc_t rY = make_rsrc(a.Y, (uint64_t)a.rows * (uint64_t)a.H * 4u);
+  const __amdgpu_buffer_rsrc_t rY = make_rsrc(a.Y, (uint64_t)a.rows * (uint64_t)a.H * (kYbf16 ? 2u : 4u));
   const __amdgpu_buffer_rsrc_t rP = make_rsrc(a.rs.P, (uint64_t)a.T * (uint64_t)a.H * 4u);
   const __amdgpu_buffer_rsrc_t rG = make_rsrc(a.gate, (uint64_t)a.T * (uint64_t)a.k * 4u);
   const __amdgpu_buffer_rsrc_t rR = make_rsrc(a.row_of, (uint64_t)a.T * (uint64_t)a.k * 4u);
@@ -110,8 +129,7 @@ __device__ void do_combine_item(const MoeRsArgs& a, int64_t c, uint32_t n_rt, in
       const uint32_t pick = (uint32_t)((tok * a.k + j) * 4);
       const float g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rG, pick, 0, 0));
       const int32_t row = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rR, pick, 0, 0);
-      const uint32_t off = col_ok ? (uint32_t)(((int64_t)row * a.H + col) * 4) : kOOB;
-      return g * __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rY, off, 0, 0));
+      return g * load_y4<kYbf16>(rY, row, a.H, col, col_ok);
     };
 #pragma unroll
     for (int u = 0; u < R; ++u) {
@@ -138,7 +156,7 @@ __device__ void do_combine_item(const MoeRsArgs& a, int64_t c, uint32_t n_rt, in
   }
 }
 
-template <bool kBNK>
+template <bool kBNK, bool kYbf16>
 __global__ void __launch_bounds__(Tile<8>::kThreads, 1) moe_rs_kernel(MoeRsArgs a) {
   constexpr int kW = 8;
   __shared__ int ok;
@@ -163,7 +181,7 @@ __global__ void __launch_bounds__(Tile<8>::kThreads, 1) moe_rs_kernel(MoeRsArgs 
       if constexpr (kBNK) kb = krows_strided<kW>(Be + n0 * a.I, a.H - n0, a.I);
       MfmaAcc<kW> acc;
       gemm_tile<kW, kBNK>(ka, kb, Be, a.H, n0, a.I, acc);
-      store_tile<kW, false, kCpolSc1>(a.Y, r_end, a.H, r0, n0, acc);
+      store_tile<kW, kYbf16, kCpolSc1>(a.Y, r_end, a.H, r0, n0, acc);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -177,7 +195,7 @@ __global__ void __launch_bounds__(Tile<8>::kThreads, 1) moe_rs_kernel(MoeRsArgs 
     const int64_t j = claimed;
     __syncthreads();
     if (j >= n_comb + n_red) break;
-    if (j < n_comb) do_combine_item(a, j, n_rt, &ok);
+    if (j < n_comb) do_combine_item<kYbf16>(a, j, n_rt, &ok);
     else do_reduce_item(a.rs, (int)(j - n_comb), &ok);
     if (!ok) return;
     __syncthreads();
@@ -191,10 +209,14 @@ hipError_t launch_moe_rs(const MoeRsArgs& a, int grid, hipStream_t stream) {
   if (pb < 1) pb = 1;
   if (pb > 1024) pb = 1024;
   hipLaunchKernelGGL(moe_rs_prep_kernel, dim3((unsigned)pb), dim3(256), 0, stream, a);
-  if (a.b_layout == 1)
-    hipLaunchKernelGGL(moe_rs_kernel<true>, dim3(grid), dim3(Tile<8>::kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(moe_rs_kernel<false>, dim3(grid), dim3(Tile<8>::kThreads), 0, stream, a);
+  const dim3 blk(Tile<8>::kThreads);
+  if (a.b_layout == 1) {
+    if (a.y_bf16) hipLaunchKernelGGL((moe_rs_kernel<true, true>), dim3(grid), blk, 0, stream, a);
+    else hipLaunchKernelGGL((moe_rs_kernel<true, false>), dim3(grid), blk, 0, stream, a);
+  } else {
+    if (a.y_bf16) hipLaunchKernelGGL((moe_rs_kernel<false, true>), dim3(grid), blk, 0, stream, a);
+    else hipLaunchKernelGGL((moe_rs_kernel<false, false>), dim3(grid), blk, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

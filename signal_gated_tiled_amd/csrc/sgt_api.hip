@@ -1056,7 +1056,7 @@ namespace {
 // into partials[p] band by band at the link rate).
 sgt_status moe_gemm_rs_impl(sgt_ctx* ctx, const void* Hg, const void* W2, const float* gate, const int32_t* topk_ids,
                             const int32_t* expert_off, const int32_t* row_token, const float* const* partials,
-                            const float* const* peer_blocks, float* Y, float* partial_out, float* C_shard,
+                            const float* const* peer_blocks, void* Y, float* partial_out, float* C_shard,
                             uint32_t* gflags, uint32_t* pflags, int W, int64_t T, int topk, int64_t I, int64_t H,
                             int E, const sgt_opts* opts, void* stream_) {
   if (!ctx) return fail(SGT_EINVAL, "ctx is NULL");
@@ -1064,7 +1064,8 @@ sgt_status moe_gemm_rs_impl(sgt_ctx* ctx, const void* Hg, const void* W2, const 
   if (st != SGT_OK) return st;
   const sgt_opts& o = *opts;
   if (o.in_dtype != SGT_BF16) return fail(SGT_EUNSUPPORTED, "MoE takes bf16 rows and weights");
-  if (o.out_dtype != SGT_F32) return fail(SGT_EUNSUPPORTED, "the combined partials are fp32");
+  // out_dtype is Y's: fp32, or bf16 (RNE) to halve its traffic; P and C_shard are fp32 either way
+  const bool y_bf16 = o.out_dtype == SGT_BF16;
   const bool paced = peer_blocks != nullptr;
   if (!paced && o.peer_gbps > 0)
     return fail(SGT_EUNSUPPORTED, "sgt_moe_gemm_rs takes resident peers; paced arrival is sgt_moe_gemm_rs_paced");
@@ -1156,7 +1157,8 @@ sgt_status moe_gemm_rs_impl(sgt_ctx* ctx, const void* Hg, const void* W2, const 
   MoeRsArgs a{};
   a.Hg = static_cast<const uint16_t*>(Hg);
   a.W2 = static_cast<const uint16_t*>(W2);
-  a.Y = Y; a.gate = gate; a.topk_ids = topk_ids; a.expert_off = expert_off; a.row_token = row_token;
+  a.Y = Y; a.y_bf16 = y_bf16 ? 1 : 0;
+  a.gate = gate; a.topk_ids = topk_ids; a.expert_off = expert_off; a.row_token = row_token;
   a.row_of = ctx->d_mrs_rowof; a.tiles = ctx->d_mrs_tiles;
   a.n_row_tiles = ctx->d_mrs_ctr; a.claim = ctx->d_mrs_ctr + 1; a.col_done = ctx->d_mrs_ctr + 4;
   a.T = T; a.I = I; a.H = H; a.rows = rows; a.E = E; a.k = topk; a.tiles_n = (int32_t)tiles_n;
@@ -1192,7 +1194,7 @@ extern "C" {
 
 sgt_status sgt_moe_gemm_rs(sgt_ctx* ctx, const void* Hg, const void* W2, const float* gate, const int32_t* topk_ids,
                            const int32_t* expert_off, const int32_t* row_token, const float* const* partials,
-                           float* Y, float* partial_out, float* C_shard, uint32_t* gflags, uint32_t* pflags, int W,
+                           void* Y, float* partial_out, float* C_shard, uint32_t* gflags, uint32_t* pflags, int W,
                            int64_t T, int topk, int64_t I, int64_t H, int E, const sgt_opts* opts, void* stream) {
   return moe_gemm_rs_impl(ctx, Hg, W2, gate, topk_ids, expert_off, row_token, partials, nullptr, Y, partial_out,
                           C_shard, gflags, pflags, W, T, topk, I, H, E, opts, stream);
@@ -1200,7 +1202,7 @@ sgt_status sgt_moe_gemm_rs(sgt_ctx* ctx, const void* Hg, const void* W2, const f
 
 sgt_status sgt_moe_gemm_rs_paced(sgt_ctx* ctx, const void* Hg, const void* W2, const float* gate,
                                  const int32_t* topk_ids, const int32_t* expert_off, const int32_t* row_token,
-                                 const float* const* peer_blocks, float* const* inbox, float* Y, float* partial_out,
+                                 const float* const* peer_blocks, float* const* inbox, void* Y, float* partial_out,
                                  float* C_shard, uint32_t* gflags, uint32_t* pflags, int W, int64_t T, int topk,
                                  int64_t I, int64_t H, int E, const sgt_opts* opts, void* stream) {
   if (!peer_blocks || !inbox) return fail(SGT_EINVAL, "NULL peer_blocks or inbox");

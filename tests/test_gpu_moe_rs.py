@@ -16,7 +16,7 @@ torch = pytest.importorskip("torch")
 
 import signal_gated_tiled_amd as sgt  # noqa: E402
 from signal_gated_tiled_amd import inputs as I  # noqa: E402
-from gpu_util import TOL_BF16, assert_close, dev, host, poison_like, sample_rows  # noqa: E402
+from gpu_util import TOL_BF16, assert_close, assert_close_bf16_out, dev, host, poison_like, sample_rows  # noqa: E402
 
 
 @pytest.fixture(scope="module")
@@ -35,7 +35,8 @@ def run_moe_rs(ctx, Hg, W2, gate, ids, off, rt, parts, rank, w_layout="kn", pace
     H = W2.shape[2] if w_layout == "kn" else W2.shape[1]
     rows = T * k
     ng, npf = sgt.rs_flag_count(W, T, H, rs_tile=128)
-    Y = poison_like(torch.empty((rows, H), dtype=torch.float32, device="cuda:0"))
+    y_dtype = kw.pop("y_dtype", torch.float32)
+    Y = poison_like(torch.empty((rows, H), dtype=y_dtype, device="cuda:0"))
     P = poison_like(torch.empty((T, H), dtype=torch.float32, device="cuda:0"))
     C = poison_like(torch.empty((T // W, H), dtype=torch.float32, device="cuda:0"))
     gf = torch.zeros(max(ng, 4), dtype=torch.int32, device="cuda:0")
@@ -210,3 +211,24 @@ def test_full_moe_rs_shape(ctx, orc):
     other = sample_rows(w.T, w.W, per_shard=2, seed=5)
     assert_close(P[other], orc.moe_gemm_rs_p(Hg, W2, gate, ids, off, rt, other, "nk"), what="P", **TOL_BF16)
     assert (gf == gf[0]).all() and (pf == gf[0]).all()
+
+
+@pytest.mark.parametrize("w_layout", ["kn", "nk"])
+@pytest.mark.parametrize("shape", [(512, 4, 8, 2, 256, 512), (1024, 8, 16, 4, 136, 264)])
+def test_moe_rs_bf16_y_parity(ctx, orc, shape, w_layout):
+    """Y stored in bf16: Y within its rounding of the fp64 product, P and C within the bf16 tolerance (the
+    combine sums the rounded rows), the same gathered flags as the fp32 call."""
+    T, W, E, k, n_in, H = shape
+    w = I.scaled(I.MOE_RS, T=T, W=W, E=E, topk=k, I=n_in, H=H, seed_index=33)
+    Hg, W2, gate, logits, parts = make(w, w_layout)
+    ids, off, rt = orc.moe_route(logits, k)
+    rank = W - 1
+    Y, P, C, gf, pf = run_moe_rs(ctx, Hg, W2, gate, ids, off, rt, parts, rank, w_layout, y_dtype=torch.bfloat16)
+    Y_ref = orc.moe_gemm(Hg, W2, off, np.arange(T * k, dtype=np.int32), w_layout)
+    assert_close_bf16_out(Y, Y_ref, what="Y bf16")
+    P_ref = orc.moe_gemm_rs_p(Hg, W2, gate, ids, off, rt, np.arange(T), w_layout)
+    assert_close(P, P_ref, what="P (bf16 Y)", **TOL_BF16)
+    C_ref = orc.moe_gemm_rs(Hg, W2, gate, ids, off, rt, parts, rank, w_layout)
+    assert_close(C, C_ref, what="C (bf16 Y)", **TOL_BF16)
+    _, _, _, gf32, pf32 = run_moe_rs(ctx, Hg, W2, gate, ids, off, rt, parts, rank, w_layout)
+    assert (gf == gf[0]).all() and (gf32 == gf32[0]).all()
