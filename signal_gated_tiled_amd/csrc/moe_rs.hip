@@ -35,6 +35,7 @@ namespace sgt {
 namespace {
 
 constexpr int kCombTile = 128;  // combine tile: tokens x columns (the GEMM+RS signal tile)
+constexpr int kCombPicks = 8;   // picks of a token whose rows are loaded together
 
 __global__ void moe_rs_prep_kernel(MoeRsArgs a) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -119,33 +120,33 @@ __device__ void do_combine_item(const MoeRsArgs& a, int64_t c, uint32_t n_rt, in
   const __amdgpu_buffer_rsrc_t rP = make_rsrc(a.rs.P, (uint64_t)a.T * (uint64_t)a.H * 4u);
   const __amdgpu_buffer_rsrc_t rG = make_rsrc(a.gate, (uint64_t)a.T * (uint64_t)a.k * 4u);
   const __amdgpu_buffer_rsrc_t rR = make_rsrc(a.row_of, (uint64_t)a.T * (uint64_t)a.k * 4u);
-  constexpr int R = 4;
-  for (int r0 = rr; r0 < kCombTile; r0 += R * rows_per_pass) {
-    f32x4_t s[R];
-    int64_t t[R];
-    // pick j's weighted row; the sum starts from pick 0's term (not from +0,
-    // which would turn a -0 term into +0)
-    auto term = [&](int64_t tok, int j) -> f32x4_t {
-      const uint32_t pick = (uint32_t)((tok * a.k + j) * 4);
-      const float g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rG, pick, 0, 0));
-      const int32_t row = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rR, pick, 0, 0);
-      return g * load_y4<kYbf16>(rY, row, a.H, col, col_ok);
-    };
+  // Per pass, two memory round trips per group of kCombPicks picks: the
+  // group's gates and rows first, then all of its Y rows (picks past k read
+  // zero through out-of-range offsets and are not added).
+  for (int r0 = rr; r0 < kCombTile; r0 += rows_per_pass) {
+    const int64_t t = cm * kCombTile + r0;  // < T: T is a multiple of the tile
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < a.k; j0 += kCombPicks) {
+      float g[kCombPicks];
+      int32_t row[kCombPicks];
 #pragma unroll
-    for (int u = 0; u < R; ++u) {
-      t[u] = cm * kCombTile + r0 + u * rows_per_pass;  // < T: T is a multiple of the tile
-      s[u] = term(t[u], 0);
-    }
-#pragma unroll 4
-    for (int j = 1; j < a.k; ++j) {
+      for (int j = 0; j < kCombPicks; ++j) {
+        const uint32_t pick = j0 + j < a.k ? (uint32_t)((t * a.k + j0 + j) * 4) : kOOB;
+        g[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rG, pick, 0, 0));
+        row[j] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rR, pick, 0, 0);
+      }
+      f32x4_t y[kCombPicks];
 #pragma unroll
-      for (int u = 0; u < R; ++u) s[u] += term(t[u], j);
-    }
+      for (int j = 0; j < kCombPicks; ++j) y[j] = load_y4<kYbf16>(rY, row[j], a.H, col, col_ok && j0 + j < a.k);
 #pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const uint32_t off = col_ok ? (uint32_t)((t[u] * a.H + col) * 4) : kOOB;
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, s[u]), rP, off, 0, kCpolSc1);
+      for (int j = 0; j < kCombPicks; ++j) {
+        // the sum starts from pick 0's term (not from +0, which would turn a -0 term into +0)
+        if (j0 + j == 0) s = g[0] * y[0];
+        else if (j0 + j < a.k) s += g[j] * y[j];
+      }
     }
+    const uint32_t off = col_ok ? (uint32_t)((t * a.H + col) * 4) : kOOB;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, s), rP, off, 0, kCpolSc1);
   }
   // every wave's device-scope stores acknowledged, then one lane publishes the tile
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
