@@ -122,6 +122,24 @@ def timed(fn, steps, warmup, torch, ctx):
     return step_ms, statistics.mean(kern), kern
 
 
+def timed_blocks(fn, steps, warmup, torch, ctx, blocks=3):
+    """timed() whose step time is the median over `blocks` event-free blocks: for calls of tens of
+    microseconds, where one host stall inside a single block would dominate its mean."""
+    step, mean_k, kern = timed(fn, steps, warmup, torch, ctx)
+    steps_ms = [step]
+    for b in range(blocks - 1):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(steps):
+            fn(warmup + (b + 2) * steps + i, None)
+        t1.record()
+        torch.cuda.synchronize()
+        ctx.sync()
+        steps_ms.append(t0.elapsed_time(t1) / steps)
+    return statistics.median(steps_ms), mean_k, kern
+
+
 def spread(vals):
     """Median and 10th / 90th percentiles of a list of times."""
     v = sorted(vals)
@@ -468,7 +486,7 @@ def bench_a2a(ctx, up, args, torch, sgt, I, tables):
     # dispatch
     d_link = {}
     for name, kw in (("paced_50GBps", dict(peer_gbps=w.peer_gbps)), ("unthrottled", dict())):
-        step, _, kern = timed(disp(**kw), n_steps, 3, torch, ctx)
+        step, _, kern = timed_blocks(disp(**kw), n_steps, 3, torch, ctx)
         d_link[name] = {"step_ms": step, "kernel_ms": spread(kern)}
     counts = (cnt.cpu().numpy() & 0xFFFFFFFF).astype(np.int64)           # E_l x W
     link_rows = counts.sum(axis=0)                                        # rows per source link
@@ -498,7 +516,7 @@ def bench_a2a(ctx, up, args, torch, sgt, I, tables):
     for name, kw in (("paced_50GBps", dict(peer_gbps=w.peer_gbps)),
                      ("serial_50GBps", dict(peer_gbps=w.peer_gbps, producer="serial")),
                      ("unthrottled", dict()), ("receiver_alone", dict(producer="preset"))):
-        step, _, kern = timed(comb(**kw), n_steps, 3, torch, ctx)
+        step, _, kern = timed_blocks(comb(**kw), n_steps, 3, torch, ctx)
         c_res[name] = {"step_ms": step, "kernel_ms": spread(kern)}
     ids_r = topk[rank].cpu().numpy()
     n_e = np.array([int(((ids_r == e).any(axis=1)).sum()) for e in range(E)])

@@ -37,20 +37,35 @@ namespace {
 constexpr int kCombTile = 128;  // combine tile: tokens x columns (the GEMM+RS signal tile)
 constexpr int kCombPicks = 8;   // picks of a token whose rows are loaded together
 
-__global__ void moe_rs_prep_kernel(MoeRsArgs a) {
+// One workgroup of kPrepThreads (>= the 256 experts the host allows).
+constexpr int kPrepThreads = 256;
+
+__global__ void __launch_bounds__(kPrepThreads) moe_rs_prep_kernel(MoeRsArgs a) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   if (blockIdx.x == 0) {
     for (int c = threadIdx.x; c < a.tiles_n; c += blockDim.x) a.col_done[c] = 0u;
-    if (threadIdx.x == 0) {
-      *a.claim = 0u;
-      // 256-row tiles of each expert's group, experts in order
-      uint32_t n = 0;
-      for (int e = 0; e < a.E; ++e)
-        for (int64_t r0 = a.expert_off[e]; r0 < a.expert_off[e + 1]; r0 += kBM)
-          if (n < (uint32_t)a.tiles_cap) a.tiles[n++] = MoeTile{e, (int32_t)r0};
-      *a.n_row_tiles = n;
+    if (threadIdx.x == 0) *a.claim = 0u;
+    // 256-row tiles of each expert's group, experts in order: thread e counts
+    // expert e's tiles, an exclusive prefix sum over the threads gives its
+    // first entry, and it writes its own tiles (entries past tiles_cap are
+    // dropped, as the host sized the table for every routing).
+    __shared__ int scan[kPrepThreads];
+    const int e = threadIdx.x;
+    const int64_t g0 = e < a.E ? a.expert_off[e] : 0, g1 = e < a.E ? a.expert_off[e + 1] : 0;
+    const int mine = g1 > g0 ? (int)((g1 - g0 + kBM - 1) / kBM) : 0;
+    scan[e] = mine;
+    __syncthreads();
+    for (int d = 1; d < kPrepThreads; d <<= 1) {  // inclusive Hillis-Steele scan
+      const int v = e >= d ? scan[e - d] : 0;
+      __syncthreads();
+      scan[e] += v;
+      __syncthreads();
     }
+    const int first = scan[e] - mine;
+    for (int i = 0; i < mine; ++i)
+      if (first + i < a.tiles_cap) a.tiles[first + i] = MoeTile{e, (int32_t)(g0 + (int64_t)i * kBM)};
+    if (e == kPrepThreads - 1) *a.n_row_tiles = (uint32_t)(scan[e] < a.tiles_cap ? scan[e] : a.tiles_cap);
   }
   // inverse routing: the row holding pick (t, j) is the row of group topk_ids[t][j] whose token is t
   for (int64_t r = gid; r < a.rows; r += stride) {
@@ -209,7 +224,7 @@ hipError_t launch_moe_rs(const MoeRsArgs& a, int grid, hipStream_t stream) {
   int64_t pb = (a.rows + 255) / 256;
   if (pb < 1) pb = 1;
   if (pb > 1024) pb = 1024;
-  hipLaunchKernelGGL(moe_rs_prep_kernel, dim3((unsigned)pb), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(moe_rs_prep_kernel, dim3((unsigned)pb), dim3(kPrepThreads), 0, stream, a);
   const dim3 blk(Tile<8>::kThreads);
   if (a.b_layout == 1) {
     if (a.y_bf16) hipLaunchKernelGGL((moe_rs_kernel<true, true>), dim3(grid), blk, 0, stream, a);
