@@ -43,6 +43,17 @@ __device__ inline __amdgpu_buffer_rsrc_t a2a_rsrc(const void* base, uint32_t byt
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Four expert ids at byte offset `off` of a routing table; an offset past the
+// table (a token past T_r, or the second half of a row of four ids) gives -1s,
+// which select no expert.  A value select, not a select of addresses: no
+// stack copy of the -1s.
+__device__ __forceinline__ int4 ids4(__amdgpu_buffer_rsrc_t rt, uint32_t off) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  const u4 w = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0));
+  const bool in = off != kOob;
+  return make_int4(in ? (int)w.x : -1, in ? (int)w.y : -1, in ? (int)w.z : -1, in ? (int)w.w : -1);
+}
+
 // Scan of one block's routing table (grid: one workgroup per block b).
 // Finds, in ascending order, the tokens of the table that picked the block's
 // expert: dispatch writes them to recv_token (the block's list) and the
@@ -71,6 +82,7 @@ __global__ void __launch_bounds__(kA2aThreads) a2a_scan_kernel(A2aArgs a) {
   const int32_t* tab = static_cast<const int32_t*>(combine ? a.table.p[0] : a.table.p[b % a.W]);
   const int k = a.k;
   const bool vec = (k == 4 || k == 8) && ((reinterpret_cast<uintptr_t>(tab) & 15u) == 0);
+  const __amdgpu_buffer_rsrc_t rt = a2a_rsrc(tab, (uint32_t)(a.T_r * k * 4));
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int running = 0;
   for (int64_t t0 = 0; t0 < a.T_r; t0 += kA2aThreads * kScanSub) {
@@ -81,10 +93,8 @@ __global__ void __launch_bounds__(kA2aThreads) a2a_scan_kernel(A2aArgs a) {
 #pragma unroll
       for (int i = 0; i < kScanSub; ++i) {
         const int64_t t = t0 + i * kA2aThreads + threadIdx.x;
-        const int4* row = reinterpret_cast<const int4*>(tab + t * k);
-        const int4 none = make_int4(-1, -1, -1, -1);
-        v[i][0] = t < a.T_r ? row[0] : none;
-        v[i][1] = t < a.T_r && k == 8 ? row[1] : none;
+        v[i][0] = ids4(rt, t < a.T_r ? (uint32_t)(t * k * 4) : kOob);
+        v[i][1] = ids4(rt, t < a.T_r && k == 8 ? (uint32_t)(t * k * 4 + 16) : kOob);
       }
 #pragma unroll
       for (int i = 0; i < kScanSub; ++i) {
@@ -123,13 +133,15 @@ __global__ void __launch_bounds__(kA2aThreads) a2a_scan_kernel(A2aArgs a) {
       if (hit[i] && !combine) a.lists[(int64_t)b * a.T_r + pos] = (int32_t)t;
       if (combine && t < a.T_r) {
         if (vec) {
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            if (q * 4 >= k) break;
-            scan_mark(a, b, e, true, t, q * 4 + 0, v[i][q].x, pos);
-            scan_mark(a, b, e, true, t, q * 4 + 1, v[i][q].y, pos);
-            scan_mark(a, b, e, true, t, q * 4 + 2, v[i][q].z, pos);
-            scan_mark(a, b, e, true, t, q * 4 + 3, v[i][q].w, pos);
+          scan_mark(a, b, e, true, t, 0, v[i][0].x, pos);
+          scan_mark(a, b, e, true, t, 1, v[i][0].y, pos);
+          scan_mark(a, b, e, true, t, 2, v[i][0].z, pos);
+          scan_mark(a, b, e, true, t, 3, v[i][0].w, pos);
+          if (k == 8) {
+            scan_mark(a, b, e, true, t, 4, v[i][1].x, pos);
+            scan_mark(a, b, e, true, t, 5, v[i][1].y, pos);
+            scan_mark(a, b, e, true, t, 6, v[i][1].z, pos);
+            scan_mark(a, b, e, true, t, 7, v[i][1].w, pos);
           }
         } else {
           for (int j = 0; j < k; ++j) scan_mark(a, b, e, true, t, j, tab[t * k + j], pos);
@@ -210,6 +222,146 @@ __device__ __forceinline__ void a2a_send(const A2aArgs& a, int item) {
     }
     // every load in flight before the first store
     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kA2aUnroll; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, dof[u], 0, kCpolSc1);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (paced)
+      while (clock_ticks() < s_t0 + release) __builtin_amdgcn_s_sleep(4);  // finite
+    if (link != a.withhold) flag_publish_coherent(a.flags + item, a.epoch);
+  }
+}
+
+// Dispatch sender with its own scan (the dispatch is one launch; up to 64
+// local experts, else the scan kernel runs first and a2a_send sends): the
+// workgroup of chunk c of block b = l * W + p reads source p's routing table
+// once (kScanSub x 256 tokens per pass, the ids of a pass loaded before any
+// is used) and derives, for p's tokens and this rank's local experts,
+//   the block's count (tokens that picked expert l),
+//   the rows link p carries before the block (tokens that picked each of the
+//     local experts before l, a token counted once per expert),
+//   the tokens at positions [c * chunk_rows, +chunk_rows) of the block's
+//     ascending list, which it writes to recv_token and copies;
+// chunk 0 also stores the block's count packet.  Then it sends like a2a_send.
+__device__ __forceinline__ void a2a_dispatch_send(const A2aArgs& a, int item) {
+  __shared__ int32_t s_tok[kA2aMaxChunkRows];
+  __shared__ int wsum[kScanSub][kA2aThreads / 64];
+  __shared__ int wbefore[kA2aThreads / 64];
+  __shared__ uint64_t s_t0;
+  const int b = item / a.n_chunks, c = item % a.n_chunks;
+  const int link = b % a.W, l = b / a.W;
+  const int ebase = a.rank * a.E_l;
+  const int32_t* tab = static_cast<const int32_t*>(a.table.p[link]);
+  const int k = a.k;
+  const bool vec = (k == 4 || k == 8) && ((reinterpret_cast<uintptr_t>(tab) & 15u) == 0);
+  const __amdgpu_buffer_rsrc_t rt = a2a_rsrc(tab, (uint32_t)(a.T_r * k * 4));
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t r0 = (int64_t)c * a.chunk_rows;
+  if (threadIdx.x == 0) s_t0 = clock_ticks();
+  int running = 0, before_mine = 0;
+  for (int64_t t0 = 0; t0 < a.T_r; t0 += kA2aThreads * kScanSub) {
+    uint64_t m[kScanSub];  // local experts each of the thread's tokens picked (bit d: expert ebase + d)
+#pragma unroll
+    for (int i = 0; i < kScanSub; ++i) m[i] = 0;
+    auto add = [&](int i, int v) {
+      const int d = v - ebase;
+      if (d >= 0 && d < a.E_l) m[i] |= 1ull << d;
+    };
+    if (vec) {
+      int4 v[kScanSub][2];
+#pragma unroll
+      for (int i = 0; i < kScanSub; ++i) {
+        const int64_t t = t0 + i * kA2aThreads + threadIdx.x;
+        v[i][0] = ids4(rt, t < a.T_r ? (uint32_t)(t * k * 4) : kOob);
+        v[i][1] = ids4(rt, t < a.T_r && k == 8 ? (uint32_t)(t * k * 4 + 16) : kOob);
+      }
+#pragma unroll
+      for (int i = 0; i < kScanSub; ++i)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          add(i, v[i][q].x); add(i, v[i][q].y); add(i, v[i][q].z); add(i, v[i][q].w);
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kScanSub; ++i) {
+        const int64_t t = t0 + i * kA2aThreads + threadIdx.x;
+        if (t < a.T_r)
+          for (int j = 0; j < k; ++j) add(i, tab[t * k + j]);
+      }
+    }
+    const uint64_t below = l > 0 ? (~0ull >> (64 - l)) : 0ull;  // local experts before l
+    bool hit[kScanSub];
+    int pre[kScanSub];
+#pragma unroll
+    for (int i = 0; i < kScanSub; ++i) {
+      hit[i] = ((m[i] >> l) & 1ull) != 0;
+      before_mine += __popcll(m[i] & below);
+      const uint64_t bal = __ballot(hit[i]);
+      pre[i] = __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) wsum[i][wave] = __popcll(bal);
+    }
+    __syncthreads();
+    int base = running;
+#pragma unroll
+    for (int i = 0; i < kScanSub; ++i) {
+      int off = base, tot = 0;
+      for (int w = 0; w < kA2aThreads / 64; ++w) {
+        if (w < wave) off += wsum[i][w];
+        tot += wsum[i][w];
+      }
+      const int pos = off + pre[i];
+      if (hit[i] && pos >= r0 && pos < r0 + a.chunk_rows) {
+        const int32_t t = (int32_t)(t0 + i * kA2aThreads + threadIdx.x);
+        s_tok[pos - r0] = t;
+        a.lists[(int64_t)b * a.T_r + pos] = t;
+      }
+      base += tot;
+    }
+    running = base;
+    __syncthreads();  // wsum is rewritten by the next pass
+  }
+  // rows of the link's earlier blocks: the sum of every thread's count
+  for (int sh = 32; sh > 0; sh >>= 1) before_mine += __shfl_xor(before_mine, sh);
+  if (lane == 0) wbefore[wave] = before_mine;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < kA2aThreads / 64; ++w) before += wbefore[w];
+  const int count = running;  // uniform
+  if (c == 0 && threadIdx.x == 0)
+    __hip_atomic_store(a.count_sig + b, ((uint64_t)a.epoch << 32) | (uint32_t)count, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  const int64_t rest = count - r0;
+  const int rows = rest < a.chunk_rows ? (int)rest : a.chunk_rows;
+  if (rows <= 0) return;  // uniform: past the block's count, nothing is sent and no flag is published
+  const bool paced = a.ticks_per_row > 0.0 && link != a.rank;
+  const uint64_t release = paced ? (uint64_t)((double)(before + r0 + rows) * a.ticks_per_row) : 0;
+  if (threadIdx.x == 0 && paced) {
+    const uint64_t lead = (uint64_t)rows * (uint64_t)a.row_bytes / 200u + 100u;
+    if (release > lead)
+      while (clock_ticks() < s_t0 + release - lead) __builtin_amdgcn_s_sleep(4);  // finite
+  }
+  __syncthreads();
+  const uint32_t block_bytes = (uint32_t)(a.T_r * a.row_bytes);
+  const __amdgpu_buffer_rsrc_t rs = a2a_rsrc(a.src.p[link], block_bytes);
+  const __amdgpu_buffer_rsrc_t rd = a2a_rsrc(a.dst + (int64_t)b * a.T_r * a.row_bytes, block_bytes);
+  const uint32_t upr = (uint32_t)(a.row_bytes >> 4);
+  const uint32_t total = (uint32_t)rows * upr;
+  for (uint32_t u0 = threadIdx.x; u0 < total; u0 += kA2aThreads * kA2aUnroll) {
+    u32x4 v[kA2aUnroll];
+    uint32_t dof[kA2aUnroll];
+#pragma unroll
+    for (int u = 0; u < kA2aUnroll; ++u) {
+      const uint32_t unit = u0 + (uint32_t)u * kA2aThreads;
+      const uint32_t row = unit / upr, col = unit - row * upr;
+      const bool in = unit < total;
+      const uint32_t srow = (uint32_t)s_tok[in ? row : 0];
+      const uint32_t sof = in ? srow * (uint32_t)a.row_bytes + col * 16u : kOob;
+      dof[u] = in ? ((uint32_t)r0 + row) * (uint32_t)a.row_bytes + col * 16u : kOob;
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, sof, 0, kCpolNt);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load in flight before the first store
 #pragma unroll
     for (int u = 0; u < kA2aUnroll; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, dof[u], 0, kCpolSc1);
   }
@@ -323,7 +475,8 @@ __device__ __forceinline__ void a2a_receive(const A2aArgs& a, int wave_id, int n
 // has been dispatched and runs to its end: each wait can end.
 __global__ void __launch_bounds__(kA2aThreads) a2a_kernel(A2aArgs a) {
   if ((int)blockIdx.x < a.n_send) {
-    a2a_send(a, blockIdx.x);
+    if (a.mode == 0 && a.fused_scan) a2a_dispatch_send(a, blockIdx.x);
+    else a2a_send(a, blockIdx.x);
   } else {
     const int per = kA2aThreads / 64;
     a2a_receive(a, ((int)blockIdx.x - a.n_send) * per + (int)(threadIdx.x >> 6), ((int)gridDim.x - a.n_send) * per);

@@ -10,6 +10,7 @@ namespace sgt {
 
 constexpr int kA2aMaxE = 4096;        // experts (size of the context's count table)
 constexpr int kA2aMaxChunkRows = 1024;
+constexpr int kA2aMaxFusedLocal = 64;  // local experts a dispatch sender's own scan covers (one 64-bit mask)
 
 // Block b of a call is one (link, expert) pair: the rows one link carries for
 // one expert.  Dispatch: b = l * W + p (local expert l, source rank p; the
@@ -31,6 +32,7 @@ struct A2aArgs {
   int32_t W, E, E_l, k, rank, chunk_rows, n_chunks, mode;  // mode 0 dispatch, 1 combine
   int32_t n_send;         // sender workgroups: E x n_chunks
   int32_t withhold;       // link whose chunk flags are never published (-1: none); a test hook
+  int32_t fused_scan;     // dispatch senders scan their source's table themselves (E_l <= 64)
   uint32_t epoch;
   double ticks_per_row;   // link pacing in 100 MHz ticks per row (0: unthrottled)
   uint64_t timeout_ticks;

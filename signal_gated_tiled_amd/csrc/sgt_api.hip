@@ -1474,6 +1474,7 @@ sgt_status a2a_plan(int W, int64_t T_r, int E, int k, const sgt_opts& o, int* cr
                                                   kA2aMaxE);
   if (k < 1 || k > 64) return fail(SGT_EINVAL, "k = %d outside [1, 64]", k);
   if (T_r < 0) return fail(SGT_EINVAL, "negative token count");
+  if (T_r * k * 4 >= ((int64_t)1 << 31)) return fail(SGT_EUNSUPPORTED, "a routing table of 2 GiB or more");
   *cr = o.flag_rows > 0 ? o.flag_rows : kA2aDefaultChunkRows;
   if (*cr > kA2aMaxChunkRows) return fail(SGT_EINVAL, "chunk rows %d above %d", *cr, kA2aMaxChunkRows);
   *nch = (T_r + *cr - 1) / *cr;
@@ -1566,8 +1567,11 @@ sgt_status sgt_a2a_dispatch(sgt_ctx* ctx, const void* const* X, const int32_t* c
   a.dst = static_cast<char*>(recv);
   a.lists = recv_token;
   a.count_sig = recv_count;
+  // up to 64 local experts each sender scans its source's table itself (one launch); beyond, a scan
+  // kernel writes the token lists and counts first (it also stores the count packets of T_r = 0)
+  a.fused_scan = (a.E_l <= kA2aMaxFusedLocal && a.n_send > 0) ? 1 : 0;
   if ((st = mark(o, 0, stream)) != SGT_OK) return st;
-  HIP_TRY(launch_a2a_scan(a, stream));
+  if (!a.fused_scan) HIP_TRY(launch_a2a_scan(a, stream));
   if (a.n_send > 0) HIP_TRY(launch_a2a(a, 0, stream));
   if ((st = mark(o, 1, stream)) != SGT_OK) return st;
   return finish(ctx, o, stream);

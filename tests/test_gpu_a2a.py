@@ -94,6 +94,8 @@ DISPATCH_CASES = [
     (4, 37, 72, 8, 3, 5, 2, 0.0, True),            # 144-byte rows, invalid ids
     (1, 20, 64, 4, 2, 32, 0, 0.0, False),          # one rank
     (2, 300, 8, 6, 6, 1, 1, 0.0, False),           # k = E / W * W (every expert), one-row chunks
+    (1, 40, 64, 80, 3, 8, 0, 0.0, False),          # 80 local experts: the scan kernel runs before the senders
+    (2, 24, 64, 130, 4, 8, 1, 10.0, False),        # 65 local experts, paced
 ]
 
 
