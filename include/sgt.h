@@ -451,7 +451,8 @@ SGT_API int64_t sgt_ring_flag_count(int W, int64_t N, int64_t* tile_elems);
  *   recv_token (E_l x W x T_r int32): token i of block (l, p); entries past the
  *     count are not written;
  *   recv_count (E_l x W uint64): packet (epoch << 32) | count, stored with
- *     device scope before the block's data;
+ *     device scope (a receiver polls it until it holds the call's epoch, then
+ *     waits on the block's first ceil(count / chunk rows) chunk flags);
  *   flags (sgt_a2a_flag_count words, zeroed once): chunk c of block b = l*W + p
  *     at b*n_chunks + c, set to the call's epoch once its rows have landed
  *     (chunks past the count are not written).
@@ -479,8 +480,10 @@ SGT_API int64_t sgt_ring_flag_count(int W, int64_t N, int64_t* tile_elems);
  * Requirements: 1 <= W <= 64, E a multiple of W with E <= 4096, 1 <= k <= 64,
  * rows of a multiple of 16 bytes, T_r*H*elem < 2^31; X, back, recv, cbuf, out
  * 16-byte aligned.  Ownership: every buffer is the caller's device memory; the
- * context keeps a table of E per-block row counts between the two kernels of
- * a call.  Errors: SGT_EINVAL / SGT_EUNSUPPORTED before any launch;
+ * context keeps a table of E per-block row counts between the scan kernel and
+ * the senders (the combine, and a dispatch with more than 64 local experts; up
+ * to 64, a dispatch is one launch whose senders scan the routing themselves),
+ * so calls sharing a context must be ordered on one stream.  Errors: SGT_EINVAL / SGT_EUNSUPPORTED before any launch;
  * SGT_ETIMEDOUT when a combine wait expires (a withheld link,
  * opts->withhold_peer = q, whose chunks are copied but never flagged).
  */
