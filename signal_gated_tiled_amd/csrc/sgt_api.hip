@@ -1543,10 +1543,11 @@ sgt_status sgt_a2a_dispatch(sgt_ctx* ctx, const void* const* X, const int32_t* c
   if ((st = a2a_plan(W, T_r, E, k, o, &cr, &nch)) != SGT_OK) return st;
   const int esz = elem_bytes(o.in_dtype);
   if ((st = a2a_rows_ok(T_r, H, esz)) != SGT_OK) return st;
-  if (!topk || !recv_count || !aligned_to(recv_count, 8)) return fail(SGT_EINVAL, "topk or recv_count NULL or misaligned");
-  for (int p = 0; p < W; ++p)
-    if (!topk[p] || !aligned_to(topk[p], 4)) return fail(SGT_EINVAL, "topk[%d] NULL or misaligned", p);
+  if (!recv_count || !aligned_to(recv_count, 8)) return fail(SGT_EINVAL, "recv_count NULL or misaligned");
   if (T_r > 0) {
+    if (!topk) return fail(SGT_EINVAL, "topk is NULL");
+    for (int p = 0; p < W; ++p)
+      if (!topk[p] || !aligned_to(topk[p], 4)) return fail(SGT_EINVAL, "topk[%d] NULL or misaligned", p);
     if (!X) return fail(SGT_EINVAL, "X is NULL");
     for (int p = 0; p < W; ++p)
       if (!X[p] || !aligned16(X[p])) return fail(SGT_EINVAL, "X[%d] NULL or not 16-byte aligned", p);
@@ -1562,7 +1563,7 @@ sgt_status sgt_a2a_dispatch(sgt_ctx* ctx, const void* const* X, const int32_t* c
   if ((st = a2a_pacing_ok(a)) != SGT_OK) return st;
   for (int p = 0; p < W; ++p) {
     a.src.p[p] = X ? X[p] : nullptr;
-    a.table.p[p] = topk[p];
+    a.table.p[p] = topk ? topk[p] : nullptr;  // not read when T_r = 0
   }
   a.dst = static_cast<char*>(recv);
   a.lists = recv_token;

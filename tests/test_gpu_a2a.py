@@ -264,3 +264,51 @@ def test_invalid_arguments_are_rejected(ctx):
     out = torch.zeros((8, 64), dtype=torch.float32, device="cuda:0")
     with pytest.raises(sgt.SgtError):
         ctx.a2a_combine([cbuf[:2], cbuf[:2]], t, g, cbuf, t.clone(), out, fl, 2, out_dtype=sgt.SGT_BF16)
+
+
+def test_dispatch_and_combine_of_zero_tokens(ctx):
+    """T_r = 0: the dispatch still stores every count packet (count 0, this call's epoch); the combine is a no-op."""
+    W, E, H, k = 4, 8, 64, 2
+    X = [torch.empty((0, H), dtype=torch.bfloat16, device="cuda:0") for _ in range(W)]
+    tk = [torch.empty((0, k), dtype=torch.int32, device="cuda:0") for _ in range(W)]
+    recv = torch.empty((E // W, W, 0, H), dtype=torch.bfloat16, device="cuda:0")
+    tok = torch.empty((E // W, W, 0), dtype=torch.int32, device="cuda:0")
+    cnt = torch.full((E // W, W), -1, dtype=torch.int64, device="cuda:0")
+    fl = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    assert sgt.a2a_flag_count(W, 0, E) == 0
+    ctx.a2a_dispatch(X, tk, recv, tok, cnt, fl, E, rank=1, blocking=True)
+    c = cnt.cpu().numpy().view(np.uint64)
+    assert ((c & np.uint64(0xFFFFFFFF)) == 0).all() and ((c >> np.uint64(32)) > 0).all()
+    assert len(set((c >> np.uint64(32)).ravel().tolist())) == 1
+    out = torch.empty((0, H), dtype=torch.float32, device="cuda:0")
+    ctx.a2a_combine([torch.empty((E // W, 0, H), dtype=torch.bfloat16, device="cuda:0")] * W, tk[0],
+                    torch.empty((0, k), dtype=torch.float32, device="cuda:0"),
+                    torch.empty((E, 0, H), dtype=torch.bfloat16, device="cuda:0"), tk[0].clone(), out, fl, W,
+                    blocking=True)
+
+
+@pytest.mark.parametrize("W,T_r,H,E,k,chunk,rank", [(4, 33, 64, 8, 1, 8, 3),     # one pick per token
+                                                     (8, 40, 128, 8, 3, 16, 2)])  # one expert per rank
+def test_a2a_degenerate_routings(ctx, orc, W, T_r, H, E, k, chunk, rank):
+    X, topk, gates, back = _case(orc, W, T_r, H, E, k, seed=40)
+    recv, tok, cnt, flags = run_dispatch(ctx, X, topk, E, rank=rank, flag_rows=chunk, peer_gbps=20.0)
+    check_dispatch(orc, X, topk, E, rank, chunk, recv, tok, cnt, flags)
+    cbuf, slot, out = run_combine(ctx, back, topk[rank], gates[rank], E, rank=rank, flag_rows=chunk, peer_gbps=20.0)
+    check_combine(orc, back, topk[rank], gates[rank], E, cbuf, slot, out)
+
+
+def test_a2a_every_token_to_one_expert(ctx, orc):
+    """All tokens of every rank pick expert 5 first (and distinct others): block (5 - r*E_l, p) holds all T_r rows,
+    the slot capacity, over a ragged last chunk."""
+    W, T_r, H, E, k, chunk = 4, 45, 64, 16, 3, 8
+    X, topk, gates, back = _case(orc, W, T_r, H, E, k, seed=41)
+    for tk in topk:
+        for t in range(T_r):
+            others = [e for e in tk[t] if e != 5][:k - 1]
+            tk[t] = [5] + others
+    rank = 5 // (E // W)
+    recv, tok, cnt, flags = run_dispatch(ctx, X, topk, E, rank=rank, flag_rows=chunk)
+    check_dispatch(orc, X, topk, E, rank, chunk, recv, tok, cnt, flags)
+    assert ((cnt[5 % (E // W)] & np.uint64(0xFFFFFFFF)) == T_r).all()
+    cbuf, slot, out = run_combine(ctx, back, topk[0], gates[0], E, rank=0, flag_rows=chunk)
+    check_combine(orc, back, topk[0], gates[0], E, cbuf, slot, out)
