@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 METRIC = "AG-GEMM/GEMM-RS bf16 TFLOP/s, % MFMA peak, overlap efficiency vs GEMM-only"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0
+K_CHUNKS = 8                # column chunks of K per AllGather signal tile on the headline workload
 
 
 # HBM traffic of the consumer from the committed counter summary: valid only
@@ -752,7 +753,10 @@ def main():
     B = up(B_h)
     Ag = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     C = torch.empty((M, N), dtype=torch.float32, device=dev)
-    flags = torch.zeros(sgt.ag_flag_count(W, M, K), dtype=torch.int32, device=dev)
+    # signal tiles of one 256-row panel x one of K_CHUNKS column chunks of K: a tile whose panel is still
+    # arriving starts on the chunks already in (the same bits as whole-row signal tiles)
+    kc = K_CHUNKS if lay == "nk" else 0
+    flags = torch.zeros(sgt.ag_flag_count(W, M, K, k_chunks=kc), dtype=torch.int32, device=dev)
     rank = 0
     flops = 2.0 * M * N * K
     ctx = sgt.Context(0)
@@ -760,7 +764,7 @@ def main():
     def ag(producer, **kw):
         def fn(i, ev):
             ctx.ag_gemm(shards, B, Ag, C, flags, rank=rank, b_layout=lay, producer=producer,
-                        consumer_events=ev, **kw)
+                        consumer_events=ev, k_chunks=kc, **kw)
         return fn
 
     link = dict(peer_gbps=w.peer_gbps, jitter_us=w.jitter_us)
@@ -978,6 +982,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "W": W, "M": M, "K": K, "N": N, "rank": rank, "b_layout": lay,
+                   "k_chunks": kc,
                    "peer_gbps": w.peer_gbps, "jitter_us": w.jitter_us, "out": "fp32",
                    "inputs": "bf16 ~N(0,0.02), SeedSequence(1003)"},
         "roofline": {"bound": "mfma", "kernel": "ag_consumer_bf16 (overlapped)", "achieved": kern_tflops,

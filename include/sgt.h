@@ -112,7 +112,10 @@ typedef struct sgt_opts {
   int32_t tile_waves;    /* bf16 consumer workgroup: 4 or 8 wave64s per tile; 0 = 8             */
   int32_t tile_rows;     /* MoE grouped tile height: 128 or 256 rows; 0 = 256 (AllGather and
                             GEMM+RS tiles are 256 x 256)                                          */
-  int32_t reserved0;     /* must be 0                                                             */
+  int32_t k_chunks;      /* sgt_ag_gemm, bf16: 0 = signal tiles of flag_rows rows x all K; n (1..64) =
+                            signal tiles of one 256-row consumer panel x one of n equal column
+                            chunks of K (K a multiple of 128 n), so a tile whose panel is still
+                            arriving computes it chunk by chunk (same bits)                      */
   uint64_t* trace;       /* optional device buffer, see sgt_trace_words(); NULL = off           */
   void* consumer_events[2]; /* optional hipEvent_t pair recorded on the consumer's stream right
                                before and after the consumer kernel launch (NULL = off)            */
@@ -172,9 +175,15 @@ SGT_API int64_t sgt_panel_order(int W, int rank, int64_t M, int32_t panel_rows, 
  * A_gathered: M x K, written by the producer (read-only for SGT_PROD_PRESET,
  *     where it must already hold the gathered rows).
  * flags: sgt_ag_flag_count() uint32 words, one per signal tile of flag_rows
- *     rows x K; zeroed once by the caller.
+ *     rows x K; zeroed once by the caller.  With opts->k_chunks = n > 0 (bf16)
+ *     a signal tile is one 256-row consumer panel x one of n column chunks of
+ *     K, flag pm * n + q for panel pm and chunk q; a tile whose panel has not
+ *     fully arrived computes the chunks in order as they land (8-wave tiles
+ *     with B stored N x K; the other tile shapes wait for the whole panel).
+ *     The results are the same bits as with whole-row signal tiles.
  * Requirements: 1 <= W <= 64, M % W == 0, (M/W) % flag_rows == 0, K, N >= 1;
- *     bf16: K % 8 == 0 and N % 8 == 0; all pointers 16-byte aligned.
+ *     bf16: K % 8 == 0 and N % 8 == 0; all pointers 16-byte aligned.  With
+ *     k_chunks = n: K % (128 n) == 0 and (M/W) % 256 == 0.
  * M = 0 or N = 0 is a no-op that still advances the epoch.
  */
 SGT_API sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B, void* A_gathered, void* C,

@@ -43,7 +43,7 @@ class Opts(ctypes.Structure):
         ("blocking", ctypes.c_int32), ("peer_gbps", ctypes.c_double), ("jitter_us", ctypes.c_double),
         ("timeout_ms", ctypes.c_double), ("arrival_seed", ctypes.c_uint64), ("withhold_peer", ctypes.c_int32),
         ("rs_tile", ctypes.c_int32), ("arrival_order", ctypes.c_int32), ("tile_waves", ctypes.c_int32),
-        ("tile_rows", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("tile_rows", ctypes.c_int32), ("k_chunks", ctypes.c_int32),
         ("trace", ctypes.c_void_p), ("consumer_events", ctypes.c_void_p * 2),
     ]
 
@@ -128,7 +128,7 @@ def make_opts(rank: int = 0, in_dtype: int = SGT_BF16, out_dtype: int = SGT_F32,
               consumer_cus: int = 0, blocking: bool = False, peer_gbps: float = 0.0, jitter_us: float = 0.0,
               timeout_ms: float = 2000.0, arrival_seed: int = 0, withhold_peer: int = -1, rs_tile: int = 0,
               trace: int = 0, consumer_events=None, arrival_order: str = "inorder", tile_waves: int = 0,
-              tile_rows: int = 0) -> Opts:
+              tile_rows: int = 0, k_chunks: int = 0) -> Opts:
     o = Opts()
     lib().sgt_opts_init(ctypes.byref(o))
     o.rank, o.in_dtype, o.out_dtype = rank, in_dtype, out_dtype
@@ -144,6 +144,7 @@ def make_opts(rank: int = 0, in_dtype: int = SGT_BF16, out_dtype: int = SGT_F32,
     o.arrival_order = ARRIVALS[arrival_order]
     o.tile_waves = tile_waves
     o.tile_rows = tile_rows
+    o.k_chunks = k_chunks
     o.trace = trace or None
     if consumer_events is not None:
         o.consumer_events[0] = _event_handle(consumer_events[0])

@@ -20,11 +20,10 @@ namespace sgt {
 
 namespace {
 
-// Wait for the flags covering rows [m0, m1) and record trace stamps.
-__device__ __forceinline__ bool gate_rows(const AgArgs& a, int64_t m0, int64_t m1, int* ok, int64_t tile_id,
-                                          uint64_t* t_wait) {
+// Wait for flags [f0, f1) and record trace stamps.
+__device__ __forceinline__ bool gate_flags(const AgArgs& a, int64_t f0, int64_t f1, int* ok, int64_t tile_id,
+                                           uint64_t* t_wait) {
   if (threadIdx.x == 0) *t_wait = clock_ticks();
-  const int64_t f0 = m0 / a.flag_rows, f1 = (m1 - 1) / a.flag_rows + 1;
   const bool good = wait_flags_block(a.flags, f0, f1, a.epoch, a.timeout_ticks, a.status, ok);
   if (a.trace && threadIdx.x == 0) {
     a.trace[tile_id * 4 + 0] = *t_wait;
@@ -34,9 +33,57 @@ __device__ __forceinline__ bool gate_rows(const AgArgs& a, int64_t m0, int64_t m
   return good;
 }
 
+// Wait for the flags covering rows [m0, m1) (signal tiles of flag_rows rows x all K).
+__device__ __forceinline__ bool gate_rows(const AgArgs& a, int64_t m0, int64_t m1, int* ok, int64_t tile_id,
+                                          uint64_t* t_wait) {
+  return gate_flags(a, m0 / a.flag_rows, (m1 - 1) / a.flag_rows + 1, ok, tile_id, t_wait);
+}
+
+// K-chunked signal tiles: are all n_kc chunk flags of panel pm set?  One peek
+// per chunk (lane q of wave 0), no waiting; when they are, the acquire follows
+// and the trace records the tile as ready at once.
+__device__ __forceinline__ bool panel_chunks_in(const AgArgs& a, int64_t pm, int* ok, int64_t tile_id,
+                                                uint64_t* t_wait) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const bool in = lane >= a.n_kc || flag_is_set(flag_peek(a.flags + pm * a.n_kc + lane), a.epoch);
+    const bool all = __all(in);
+    if (all) acquire_agent();
+    if (lane == 0) {
+      *ok = all ? 1 : 0;
+      *t_wait = clock_ticks();
+      if (a.trace) {
+        a.trace[tile_id * 4 + 0] = *t_wait;
+        a.trace[tile_id * 4 + 1] = *t_wait;
+        a.trace[tile_id * 4 + 3] = blockIdx.x;
+      }
+    }
+  }
+  __syncthreads();
+  return *ok != 0;
+}
+
+// K-chunked signal tiles: how many chunks q0, q0 + 1, ... of panel pm are
+// already in, counted up to the first that is not (one peek per lane of wave
+// 0, no waiting; an acquire when any is).  `n` must be a __shared__ int.
+__device__ __forceinline__ int chunks_in_after(const AgArgs& a, int64_t pm, int q0, int* n) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x, q = q0 + lane;
+    const bool in = q < a.n_kc && flag_is_set(flag_peek(a.flags + pm * a.n_kc + q), a.epoch);
+    const uint64_t missing = __ballot(!in);  // lanes past the panel's chunks count as missing
+    const int run = missing ? __builtin_ctzll(missing) : 64;
+    if (run > 0) acquire_agent();
+    if (lane == 0) *n = run;
+  }
+  __syncthreads();
+  return *n;
+}
+
 template <int kW, bool kBNK, bool kOutBf16>
 __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) ag_consumer_bf16(AgArgs a) {
   __shared__ int ok;
+  __shared__ int all_in;  // its own word: the chunk waits that may follow rewrite `ok` with no barrier between
+  __shared__ int n_more;  // likewise for the count of chunks already in
   __shared__ uint64_t t_wait;
   const int total = a.tiles_m * a.tiles_n;
   const int G = gridDim.x;
@@ -64,6 +111,34 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) ag_consumer_bf16(AgArgs
         a.trace[tile_id * 4 + 0] = now;
         a.trace[tile_id * 4 + 1] = now;
         a.trace[tile_id * 4 + 3] = blockIdx.x;
+      }
+    } else if (a.n_kc > 0) {
+      // K-chunked signal tiles: when every chunk of the panel is in, the tile
+      // runs at once; otherwise it takes the chunks in order as they land (the
+      // 8-wave tile with B stored N x K, the one whose registers leave room for
+      // a second K loop; the other variants wait for the whole panel).
+      if constexpr (kW != 8 || !kBNK) {
+        if (!gate_flags(a, pm * a.n_kc, (pm + 1) * a.n_kc, &ok, tile_id, &t_wait)) return;
+      } else if (!panel_chunks_in(a, pm, &all_in, tile_id, &t_wait)) {
+        const KRows ka = krows_strided<kW>(Abase, rows_valid, a.K);
+        KRows kb = ka;
+        if constexpr (kBNK) kb = krows_strided<kW>(B + n0 * a.K, a.N - n0, a.K);
+        MfmaAcc<kW> acc;
+        acc_zero<kW>(acc);
+        // each range: wait for the next chunk, then take it with every later
+        // chunk already in (a range pays one pipeline start, so few and long)
+        for (int q = 0; q < a.n_kc;) {
+          const int64_t f = pm * a.n_kc + q;
+          if (!wait_flags_block(a.flags, f, f + 1, a.epoch, a.timeout_ticks, a.status, &ok)) return;
+          if (q == 0 && a.trace && threadIdx.x == 0) a.trace[tile_id * 4 + 1] = clock_ticks();
+          const int q_end = q + 1 + chunks_in_after(a, pm, q + 1, &n_more);
+          gemm_tile_range<kW, kBNK>(ka, kb, B, a.N, n0, a.K, (int64_t)q * a.kc_cols, (int64_t)q_end * a.kc_cols,
+                                    acc);
+          q = q_end;
+        }
+        store_tile<kW, kOutBf16>(a.C, a.M, a.N, m0, n0, acc);
+        if (a.trace && threadIdx.x == 0) a.trace[tile_id * 4 + 2] = clock_ticks();
+        continue;
       }
     } else if (!gate_rows(a, m0, m1, &ok, tile_id, &t_wait)) {
       return;

@@ -42,6 +42,7 @@ struct AgArgs {
   int64_t M, N, K;
   int64_t rows_per_shard;
   int32_t flag_rows;
+  int32_t n_kc, kc_cols;  // K-chunked signal tiles: n_kc chunks of kc_cols columns per panel (0: whole rows)
   int32_t W, rank, order;
   int32_t tiles_m, tiles_n;
   int32_t b_layout, out_dtype;

@@ -322,39 +322,52 @@ __device__ __forceinline__ void mfma_stage(const uint8_t* sA, const uint8_t* sB,
 // the stage with zeros (which add nothing) without touching memory; a
 // conditional MFMA block would split the accumulators' live ranges and force
 // copies.  The caller must have passed a barrier since the previous use.
+// K steps [k_begin, k_end) of the tile, accumulated into acc (k_begin a
+// multiple of 2 kBK; a range of an even number of steps, except the last of
+// K, keeps the step sequence of one whole-K call, so the accumulation order,
+// and the bits, are the same however K is cut).  Operand loads stop at k_end:
+// columns of A past it are neither read nor needed.
 template <int kW, bool kBNK, int kR = kBM>
-__device__ __forceinline__ void gemm_tile(const KRows& ka, const KRows& kb_nk, const uint16_t* B_kn, int64_t N,
-                                          int64_t n0, int64_t K, MfmaAcc<kW, kR>& acc) {
+__device__ __forceinline__ void gemm_tile_range(const KRows& ka, const KRows& kb_nk, const uint16_t* B_kn, int64_t N,
+                                                int64_t n0, int64_t K, int64_t k_begin, int64_t k_end,
+                                                MfmaAcc<kW, kR>& acc) {
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[kR * kBK * 2];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sA1[kR * kBK * 2];
   __shared__ __attribute__((aligned(1024))) uint8_t sB1[kStageBytes];
-  acc_zero<kW, kR>(acc);
-  const int64_t nk2 = ((K + kBK - 1) / kBK + 1) & ~int64_t(1);
+  const int64_t nk2 = ((k_end - k_begin + kBK - 1) / kBK + 1) & ~int64_t(1);
   KNLoader<kW> kn;
   if constexpr (!kBNK) {
     kn.init(B_kn, K, N, n0);
-    kn.load(0);
+    kn.load(k_begin);
   }
-  dma_stage<kW, kR>(ka, sA0, 0, K);
-  if constexpr (kBNK) dma_stage<kW>(kb_nk, sB0, 0, K);
+  dma_stage<kW, kR>(ka, sA0, k_begin, k_end);
+  if constexpr (kBNK) dma_stage<kW>(kb_nk, sB0, k_begin, k_end);
   else kn.store(sB0);
   wait_dma();
   __syncthreads();
   for (int64_t kt = 0; kt < nk2; kt += 2) {
+    const int64_t k1 = k_begin + (kt + 1) * kBK, k2 = k_begin + (kt + 2) * kBK;
     // stage 0 computes while stage 1 fills
-    if constexpr (!kBNK) kn.load((kt + 1) * kBK);
-    mfma_stage<kW, kR>(sA0, sB0, acc, StepDma<kW, kR, kBNK>(ka, kb_nk, sA1, sB1, (kt + 1) * kBK, K));
+    if constexpr (!kBNK) kn.load(k1);
+    mfma_stage<kW, kR>(sA0, sB0, acc, StepDma<kW, kR, kBNK>(ka, kb_nk, sA1, sB1, k1, k_end));
     if constexpr (!kBNK) kn.store(sB1);
     wait_dma();
     __syncthreads();
     // stage 1 computes while stage 0 fills (past the end: zeros, unused)
-    if constexpr (!kBNK) kn.load((kt + 2) * kBK);
-    mfma_stage<kW, kR>(sA1, sB1, acc, StepDma<kW, kR, kBNK>(ka, kb_nk, sA0, sB0, (kt + 2) * kBK, K));
+    if constexpr (!kBNK) kn.load(k2);
+    mfma_stage<kW, kR>(sA1, sB1, acc, StepDma<kW, kR, kBNK>(ka, kb_nk, sA0, sB0, k2, k_end));
     if constexpr (!kBNK) kn.store(sB0);
     wait_dma();
     __syncthreads();
   }
+}
+
+template <int kW, bool kBNK, int kR = kBM>
+__device__ __forceinline__ void gemm_tile(const KRows& ka, const KRows& kb_nk, const uint16_t* B_kn, int64_t N,
+                                          int64_t n0, int64_t K, MfmaAcc<kW, kR>& acc) {
+  acc_zero<kW, kR>(acc);
+  gemm_tile_range<kW, kBNK, kR>(ka, kb_nk, B_kn, N, n0, K, 0, K, acc);
 }
 
 // fp32 -> bf16 bits, round to nearest even (NaN stays NaN).

@@ -60,6 +60,31 @@ __device__ inline bool copy_bytes(char* __restrict__ dst, const char* __restrict
   return false;
 }
 
+// Copy `rows` rows of `seg` bytes (a multiple of 16), `stride` bytes apart in
+// both buffers (a column block of row-major matrices of the same width), with
+// the loads and stores of copy_bytes; (rows - 1) * stride + seg < 2^31.
+template <int U>
+__device__ inline void copy_rows(char* __restrict__ dst, const char* __restrict__ src, uint32_t rows, uint32_t seg,
+                                 uint32_t stride) {
+  const uint32_t span = (rows - 1) * stride + seg;
+  const __amdgpu_buffer_rsrc_t rs = rsrc_of(src, span), rd = rsrc_of(dst, span);
+  const uint32_t upr = seg >> 4, total = rows * upr;
+  for (uint32_t u0 = threadIdx.x; u0 < total; u0 += blockDim.x * U) {
+    u32x4 v[U];
+    uint32_t off[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t unit = u0 + (uint32_t)u * blockDim.x;
+      const uint32_t r = unit / upr;
+      off[u] = unit < total ? r * stride + (unit - r * upr) * 16u : 0x80000000u;
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[u], 0, kCpolNt);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load in flight before the first store
+#pragma unroll
+    for (int u = 0; u < U; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, off[u], 0, kCpolSc1);
+  }
+}
+
 // 256 threads x 32 loads of 16 bytes = 128 KiB in flight per workgroup: a copy
 // is latency-bound, so bytes in flight set each workgroup's bandwidth.
 constexpr int kProdThreads = 256;
@@ -70,10 +95,14 @@ constexpr int kProdThreads = 256;
 // time (so the copy is done by the release), which keeps the producer's HBM
 // traffic close to the links' rate instead of front-loading it.
 // Producer role: this workgroup takes items first, first + stride, ...
+// seg_rows > 0: each item is a column block of seg_rows rows of seg_bytes,
+// row_stride apart (K-chunked signal tiles); else tile_bytes contiguous bytes.
 __device__ __forceinline__ void produce_items(int first, int stride, uint32_t* flags,
                                               const ProdItem* __restrict__ items, int n_items, int64_t tile_bytes,
                                               uint32_t epoch, int withhold_peer, uint64_t* trace_release,
-                                              uint64_t lead0, uint32_t* started, uint64_t* trace_issue) {
+                                              uint64_t lead0, uint32_t* started, uint64_t* trace_issue,
+                                              uint32_t seg_rows = 0, uint32_t seg_bytes = 0,
+                                              uint32_t row_stride = 0) {
   __shared__ uint64_t t0, lead;
   if (threadIdx.x == 0) {
     t0 = clock_ticks();
@@ -95,7 +124,9 @@ __device__ __forceinline__ void produce_items(int first, int stride, uint32_t* f
       if (trace_issue) trace_issue[2 * (int64_t)item.flag0] = c0;
     }
     __syncthreads();
-    const bool coherent = copy_bytes<32>(item.dst, item.src, tile_bytes);
+    bool coherent = true;
+    if (seg_rows > 0) copy_rows<32>(item.dst, item.src, seg_rows, seg_bytes, row_stride);
+    else coherent = copy_bytes<32>(item.dst, item.src, tile_bytes);
     // Every wave waits until its stores are acknowledged; after the barrier one
     // lane publishes the flag.  Device-scope stores leave nothing in the XCD's
     // L2 to write back, so the flag needs no release write-back; the plain
@@ -127,9 +158,10 @@ __global__ void __launch_bounds__(kProdThreads) ag_producer_kernel(uint32_t* fla
                                                                    int64_t tile_bytes, uint32_t epoch,
                                                                    int withhold_peer, uint64_t* trace_release,
                                                                    uint64_t lead0, uint32_t* started,
-                                                                   uint64_t* trace_issue) {
+                                                                   uint64_t* trace_issue, uint32_t seg_rows,
+                                                                   uint32_t seg_bytes, uint32_t row_stride) {
   produce_items(blockIdx.x, gridDim.x, flags, items, n_items, tile_bytes, epoch, withhold_peer, trace_release, lead0,
-                started, trace_issue);
+                started, trace_issue, seg_rows, seg_bytes, row_stride);
 }
 
 // Stand-alone flag-based AllGather in one launch: workgroups [0, n_prod_blocks)
@@ -187,13 +219,15 @@ hipError_t launch_rs_prepare(uint32_t* pflags, int64_t n, uint32_t v, uint32_t* 
 
 hipError_t launch_ag_producer(uint32_t* flags, const ProdItem* items, int n_items,
                               int64_t tile_bytes, uint32_t epoch, int withhold_peer, uint64_t* trace_release, int grid,
-                              hipStream_t stream, uint32_t* started, uint64_t* trace_issue) {
+                              hipStream_t stream, uint32_t* started, uint64_t* trace_issue, uint32_t seg_rows,
+                              uint32_t seg_bytes, uint32_t row_stride) {
   if (n_items <= 0) return hipSuccess;
   if (grid > n_items) grid = n_items;
   // first estimate of a tile's copy time: at 16 GB/s per workgroup (100 MHz ticks)
   const uint64_t lead0 = (uint64_t)(tile_bytes / 160) + 100;
   hipLaunchKernelGGL(ag_producer_kernel, dim3(grid), dim3(kProdThreads), 0, stream, flags, items, n_items, tile_bytes,
-                     epoch, withhold_peer, trace_release, lead0, started, trace_issue);
+                     epoch, withhold_peer, trace_release, lead0, started, trace_issue, seg_rows, seg_bytes,
+                     row_stride);
   return hipGetLastError();
 }
 

@@ -26,7 +26,8 @@
 namespace sgt {
 hipError_t launch_ag_producer(uint32_t* flags, const ProdItem* items, int n_items,
                               int64_t tile_bytes, uint32_t epoch, int withhold_peer, uint64_t* trace_release, int grid,
-                              hipStream_t stream, uint32_t* started = nullptr, uint64_t* trace_issue = nullptr);
+                              hipStream_t stream, uint32_t* started = nullptr, uint64_t* trace_issue = nullptr,
+                              uint32_t seg_rows = 0, uint32_t seg_bytes = 0, uint32_t row_stride = 0);
 hipError_t launch_ll_allgather(const ProdItem* items, int n_prod, int n_recv, int n_prod_blocks, int grid,
                                int64_t chunk_bytes, uint32_t epoch, int withhold_peer, uint64_t lead, int rank,
                                uint64_t timeout_ticks, uint32_t* status, uint64_t* trace, hipStream_t stream);
@@ -181,13 +182,14 @@ sgt_status check_opts(const sgt_opts* o, int W) {
     return fail(SGT_EINVAL, "tile_waves %d (0, 4 or 8)", o->tile_waves);
   if (o->tile_rows != 0 && o->tile_rows != 128 && o->tile_rows != 256)
     return fail(SGT_EINVAL, "tile_rows %d (0, 128 or 256)", o->tile_rows);
-  if (o->reserved0 != 0) return fail(SGT_EINVAL, "reserved0 must be 0");
+  if (o->k_chunks < 0 || o->k_chunks > 64) return fail(SGT_EINVAL, "k_chunks %d outside [0, 64]", o->k_chunks);
   return SGT_OK;
 }
 
 struct AgPlan {
   int64_t rows_per_shard, flag_rows, n_flags, tiles_per_shard;
   int panel_rows, panel_cols, tiles_m, tiles_n;
+  int n_kc = 0, kc_cols = 0;  // K-chunked signal tiles (opts.k_chunks): chunks per panel and their width
 };
 
 sgt_status plan_ag(int W, int64_t M, int64_t K, int64_t N, const sgt_opts& o, AgPlan* p) {
@@ -210,9 +212,21 @@ sgt_status plan_ag(int W, int64_t M, int64_t K, int64_t N, const sgt_opts& o, Ag
     return fail(SGT_EINVAL, "rows per shard %lld not a multiple of flag_rows %lld", (long long)p->rows_per_shard,
                 (long long)p->flag_rows);
   p->n_flags = M / p->flag_rows;
+  if (o.k_chunks > 0) {
+    // signal tiles of one consumer panel x one column chunk of K
+    if (o.in_dtype != SGT_BF16) return fail(SGT_EUNSUPPORTED, "k_chunks needs bf16 inputs");
+    if (K % (128 * (int64_t)o.k_chunks))
+      return fail(SGT_EINVAL, "K = %lld is not a multiple of 128 x k_chunks (%d)", (long long)K, o.k_chunks);
+    if (p->rows_per_shard % p->panel_rows)
+      return fail(SGT_EUNSUPPORTED, "k_chunks needs shards of whole %d-row panels", p->panel_rows);
+    p->flag_rows = p->panel_rows;
+    p->n_kc = o.k_chunks;
+    p->kc_cols = (int)(K / o.k_chunks);
+    p->n_flags = M / p->panel_rows * o.k_chunks;
+  }
   if (p->n_flags > kItemsCap) return fail(SGT_EINVAL, "%lld signal tiles exceed %lld", (long long)p->n_flags,
                                           (long long)kItemsCap);
-  p->tiles_per_shard = p->rows_per_shard / p->flag_rows;
+  p->tiles_per_shard = p->rows_per_shard / p->flag_rows * (p->n_kc > 0 ? p->n_kc : 1);
   if (p->flag_rows * K * esz >= ((int64_t)1 << 31)) return fail(SGT_EUNSUPPORTED, "signal tile of 2 GiB or more");
   const int64_t tm = (M + p->panel_rows - 1) / p->panel_rows, tn = (N + p->panel_cols - 1) / p->panel_cols;
   if (tm * tn > (int64_t)1 << 30) return fail(SGT_EINVAL, "too many tiles");
@@ -261,7 +275,8 @@ ProdItem sched_item(int64_t tile, int peer, double release) {
 int build_schedule(const AgPlan& p, int W, int rank, int64_t K, int esz, const sgt_opts& o,
                    const void* const* shards, void* gathered, ProdItem* items, bool local_first = false,
                    uint32_t* ranks = nullptr) {
-  const double tile_bytes = (double)p.flag_rows * (double)K * esz;
+  // a K-chunked signal tile is one panel's rows x one column chunk
+  const double tile_bytes = (double)p.flag_rows * (double)(p.n_kc > 0 ? p.kc_cols : K) * esz;
   const double ticks_per_tile = o.peer_gbps > 0 ? tile_bytes / (o.peer_gbps * 1e3) * kTicksPerUs : 0.0;
   const int64_t tps = p.tiles_per_shard;
   int n = 0;
@@ -308,8 +323,17 @@ int build_schedule(const AgPlan& p, int W, int rank, int64_t K, int esz, const s
     for (int64_t t = 0; t < tps; ++t) items[n++] = sched_item(rank * tps + t, rank, 0.0);
   for (int i = 0; i < n; ++i) {
     const int64_t tile = items[i].flag0, local_tile = tile - (int64_t)items[i].peer * tps;
-    items[i].src = static_cast<const char*>(shards[items[i].peer]) + local_tile * (int64_t)tile_bytes;
-    items[i].dst = static_cast<char*>(gathered) + tile * (int64_t)tile_bytes;
+    if (p.n_kc > 0) {
+      // panel j of the shard, column chunk q: rows [j * panel, +panel), columns [q * kc, +kc)
+      const int64_t j = local_tile / p.n_kc, q = local_tile % p.n_kc;
+      const int64_t src_el = j * p.flag_rows * K + q * p.kc_cols;
+      const int64_t dst_el = ((int64_t)items[i].peer * p.rows_per_shard + j * p.flag_rows) * K + q * p.kc_cols;
+      items[i].src = static_cast<const char*>(shards[items[i].peer]) + src_el * esz;
+      items[i].dst = static_cast<char*>(gathered) + dst_el * esz;
+    } else {
+      items[i].src = static_cast<const char*>(shards[items[i].peer]) + local_tile * (int64_t)tile_bytes;
+      items[i].dst = static_cast<char*>(gathered) + tile * (int64_t)tile_bytes;
+    }
     if (ranks) ranks[tile] = (uint32_t)i;
   }
   return n;
@@ -576,6 +600,7 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   a.A = A_gathered; a.A_local = A_shards[o.rank]; a.B = B; a.C = C; a.flags = flags; a.status = ctx->d_status;
   a.trace = o.trace;
   a.M = M; a.N = N; a.K = K; a.rows_per_shard = p.rows_per_shard; a.flag_rows = (int32_t)p.flag_rows;
+  a.n_kc = p.n_kc; a.kc_cols = p.kc_cols;
   a.W = W; a.rank = o.rank; a.order = o.order; a.tiles_m = p.tiles_m; a.tiles_n = p.tiles_n;
   a.b_layout = o.b_layout; a.out_dtype = o.out_dtype; a.epoch = e; a.timeout_ticks = timeout_ticks(o);
   a.tile_waves = o.tile_waves ? o.tile_waves : 8;
@@ -598,12 +623,15 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   const int n_items = build_schedule(p, W, o.rank, K, esz, o, A_shards, A_gathered, items);
   const int pwg = std::min(default_producer_wgs(o, ctx->n_cu), n_items);
   uint64_t* trace_rel = o.trace ? o.trace + (int64_t)total_tiles * 4 : nullptr;
-  const int64_t tile_bytes = p.flag_rows * K * esz;
+  const int64_t tile_bytes = p.flag_rows * (p.n_kc > 0 ? p.kc_cols : K) * esz;
+  // K-chunked signal tiles are column blocks: panel rows of kc_cols elements, K apart
+  const uint32_t seg_rows = p.n_kc > 0 ? (uint32_t)p.flag_rows : 0u;
+  const uint32_t seg_bytes = (uint32_t)(p.kc_cols * esz), row_stride = (uint32_t)(K * esz);
 
   if (o.producer == SGT_PROD_SERIAL) {
     if ((st = stage_items(ctx, items, n_items, stream, &slot)) != SGT_OK) return st;
     HIP_TRY(launch_ag_producer(flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
-                               trace_rel, pwg, stream));
+                               trace_rel, pwg, stream, nullptr, nullptr, seg_rows, seg_bytes, row_stride));
     HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
     ctx->slot_used[slot] = true;
     const int grid = std::min(total_tiles, o.consumer_cus > 0 ? o.consumer_cus
@@ -623,7 +651,7 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
   if ((st = stage_items(ctx, items, n_items, ctx->prod, &slot)) != SGT_OK) return st;
   HIP_TRY(launch_ag_producer(flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
-                             trace_rel, pwg, ctx->prod));
+                             trace_rel, pwg, ctx->prod, nullptr, nullptr, seg_rows, seg_bytes, row_stride));
   HIP_TRY(hipEventRecord(ctx->slot_ev[slot], ctx->prod));
   ctx->slot_used[slot] = true;
   int grid;
@@ -884,6 +912,7 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   if (st != SGT_OK) return st;
   const sgt_opts& o = *opts;
   if (o.in_dtype != SGT_BF16) return fail(SGT_EUNSUPPORTED, "MoE takes bf16 tokens and weights");
+  if (o.k_chunks) return fail(SGT_EUNSUPPORTED, "k_chunks applies to sgt_ag_gemm");
   if (E < 1 || E > 256 || topk < 1 || topk > E) return fail(SGT_EINVAL, "need 1 <= topk <= E <= 256 (E=%d topk=%d)", E, topk);
   if (T < 0 || H < 1 || I < 0) return fail(SGT_EINVAL, "bad shape T=%lld H=%lld I=%lld", (long long)T, (long long)H,
                                            (long long)I);
@@ -1228,6 +1257,7 @@ sgt_status allgather_impl(sgt_ctx* ctx, const void* const* shards, void* gathere
   if (st != SGT_OK) return st;
   const sgt_opts& o = *opts;
   if (o.producer == SGT_PROD_PRESET) return fail(SGT_EINVAL, "an AllGather needs a producer mode (CU or serial)");
+  if (o.k_chunks) return fail(SGT_EUNSUPPORTED, "k_chunks applies to sgt_ag_gemm");
   AgPlan p;
   if ((st = plan_ag(W, M, K, 0, o, &p)) != SGT_OK) return st;
   const int esz = elem_bytes(o.in_dtype);

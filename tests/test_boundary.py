@@ -43,7 +43,7 @@ def test_opts_struct_layout_matches(L):
     o = _sgt.Opts()
     L.sgt_opts_init(ctypes.byref(o))
     assert o.in_dtype == _sgt.SGT_BF16 and o.out_dtype == _sgt.SGT_F32 and o.timeout_ms == 2000.0
-    assert o.withhold_peer == -1 and o.trace is None and o.tile_rows == 0 and o.reserved0 == 0
+    assert o.withhold_peer == -1 and o.trace is None and o.tile_rows == 0 and o.k_chunks == 0
     L.sgt_opts_size.restype = ctypes.c_size_t
     assert ctypes.sizeof(_sgt.Opts) == L.sgt_opts_size() == 120
     # every field at the offset the C compiler gave it: the last field is the event pair

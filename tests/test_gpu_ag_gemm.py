@@ -252,3 +252,67 @@ def test_full_llama_shape(ctx, orc, dist):
 @pytest.mark.parametrize("b_layout", ["kn", "nk"])
 def test_full_qwen_shape(ctx, orc, b_layout):
     _full_size(ctx, orc, I.QWEN_AG, b_layout, "normal")
+
+
+# ---------------------------------------------------------------- K-chunked signal tiles
+def _run_kc(ctx, dA, dB, M, K, N, b_layout, **kw):
+    W = len(dA)
+    Ag = poison_like(torch.empty((M, K), dtype=torch.bfloat16, device="cuda:0"))
+    C = poison_like(torch.empty((M, N), dtype=torch.float32, device="cuda:0"))
+    nf = sgt.ag_flag_count(W, M, K, k_chunks=kw.get("k_chunks", 0))
+    flags = torch.zeros(nf, dtype=torch.int32, device="cuda:0")
+    ctx.ag_gemm(dA, dB, Ag, C, flags, b_layout=b_layout, blocking=True, **kw)
+    torch.cuda.synchronize()
+    return Ag, C, flags
+
+
+@pytest.mark.parametrize("b_layout", ["nk", "kn"])
+@pytest.mark.parametrize("link", [dict(peer_gbps=4.0, jitter_us=30.0, arrival_seed=3), dict()])
+def test_k_chunks_are_bit_identical_to_whole_rows(ctx, orc, b_layout, link):
+    """Signal tiles of one panel x one K chunk: with slow, jittered links most remote tiles start on a panel
+    whose later chunks are still in flight (B stored N x K: chunk by chunk; K x N: after the whole panel).
+    Gathered bits, C bits and the flags (all at the call's epoch) match the whole-row signal tiles."""
+    w = I.AGWorkload("t", W=4, M=4 * 512, K=1024, N=520, seed_index=34)
+    shards, B = I.make_ag(w, B_layout=b_layout)
+    dA, dB = [dev(s) for s in shards], dev(B)
+    assert sgt.ag_flag_count(w.W, w.M, w.K, k_chunks=8) == (w.M // 256) * 8
+    Ag0, C0, _ = _run_kc(ctx, dA, dB, w.M, w.K, w.N, b_layout, rank=2, **link)
+    Ag1, C1, fl = _run_kc(ctx, dA, dB, w.M, w.K, w.N, b_layout, rank=2, k_chunks=8, **link)
+    assert torch.equal(Ag1.view(torch.int16), torch.cat(dA).view(torch.int16)), "gathered buffer"
+    assert torch.equal(C1.view(torch.int32), C0.view(torch.int32)), "C bits differ from whole-row signal tiles"
+    f = fl.cpu().numpy()
+    assert (f == f[0]).all() and f[0] > 0
+    _, C_ref = orc.ag_gemm(shards, B, b_layout=b_layout, rows=sample_rows(w.M, w.W))
+    assert_close(host(C1)[sample_rows(w.M, w.W)], C_ref, what="k-chunked C", **TOL_BF16)
+
+
+@pytest.mark.slow
+def test_k_chunks_full_llama_shape(ctx):
+    """The Llama-3-70B share with 8 K chunks per panel at 153.6 GB/s per link + jitter: the same C bits as the
+    whole-row signal tiles."""
+    w = I.LLAMA_AG
+    shards, B = I.make_ag(w, B_layout="nk")
+    dA, dB = [dev(s) for s in shards], dev(B)
+    link = dict(peer_gbps=w.peer_gbps, jitter_us=w.jitter_us, arrival_seed=5)
+    _, C0, _ = _run_kc(ctx, dA, dB, w.M, w.K, w.N, "nk", **link)
+    Ag1, C1, fl = _run_kc(ctx, dA, dB, w.M, w.K, w.N, "nk", k_chunks=8, **link)
+    assert torch.equal(C1.view(torch.int32), C0.view(torch.int32))
+    assert torch.equal(Ag1.view(torch.int16), torch.cat(dA).view(torch.int16))
+    assert bool((fl == fl[0]).all())
+
+
+def test_k_chunks_rejections(ctx):
+    w = I.AGWorkload("t", W=4, M=4 * 256, K=1024, N=256, seed_index=35)
+    shards, B = I.make_ag(w, B_layout="nk")
+    dA, dB = [dev(s) for s in shards], dev(B)
+    for kw in (dict(k_chunks=3),                      # 1024 is not a multiple of 128 x 3
+               dict(k_chunks=65)):                    # above 64
+        with pytest.raises(sgt.SgtError):
+            _run_kc(ctx, dA, dB, w.M, w.K, w.N, "nk", **kw)
+    w2 = I.AGWorkload("t", W=4, M=4 * 200, K=1024, N=256, seed_index=35)   # shards of 200 rows: not whole panels
+    s2, B2 = I.make_ag(w2, B_layout="nk")
+    with pytest.raises(sgt.SgtError):
+        sgt.ag_flag_count(w2.W, w2.M, w2.K, k_chunks=8)
+    g = torch.empty((w.M, w.K), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(sgt.SgtError):
+        ctx.allgather(dA, g, torch.zeros(64, dtype=torch.int32, device="cuda:0"), k_chunks=8, blocking=True)
