@@ -262,8 +262,12 @@ def bench_ag_other(ctx, up, args, torch, sgt, I, lay):
         Ag = torch.empty((w.M, w.K), dtype=dt, device="cuda:0")
         C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda:0")
         fr = getattr(w, "flag_rows", 0)
-        flags = torch.zeros(sgt.ag_flag_count(w.W, w.M, w.K, flag_rows=fr), dtype=torch.int32, device="cuda:0")
-        link = dict(peer_gbps=w.peer_gbps, jitter_us=w.jitter_us, flag_rows=fr)
+        # K-chunked signal tiles where the tile supports them (bf16, B as N x K, whole 256-row panels per shard)
+        kc = K_CHUNKS if (w.dtype == "bf16" and kw["b_layout"] == "nk" and w.K % (128 * K_CHUNKS) == 0
+                          and (w.M // w.W) % 256 == 0) else 0
+        flags = torch.zeros(sgt.ag_flag_count(w.W, w.M, w.K, flag_rows=fr, k_chunks=kc), dtype=torch.int32,
+                            device="cuda:0")
+        link = dict(peer_gbps=w.peer_gbps, jitter_us=w.jitter_us, flag_rows=fr, k_chunks=kc)
         if w is I.TINY:
             link["arrival_order"] = "global"
 
@@ -285,19 +289,22 @@ def bench_ag_other(ctx, up, args, torch, sgt, I, lay):
         bm = 256 if w.dtype == "bf16" else 64
         grid = n_cu - max(8, n_cu // 8)
         tiles = -(-w.M // bm) * -(-w.N // bm)
+        # after the link floor the last panel's tiles still compute their last chunk (a whole tile without chunks)
+        tail = al * 1e3 * grid / tiles / (kc if kc else 1)
         out[w.name] = {
-            "M": w.M, "K": w.K, "N": w.N, "W": w.W, "dtype": w.dtype, "peer_gbps": w.peer_gbps or None,
+            "M": w.M, "K": w.K, "N": w.N, "W": w.W, "dtype": w.dtype, "k_chunks": kc,
+            "peer_gbps": w.peer_gbps or None,
             "jitter_us": w.jitter_us, "step_ms": over_ms, "tflops_step": flops / (over_ms * 1e-3) / 1e12,
             "overlapped_kernel_ms": spread(over_l), "pairs_alone_kernel_ms": spread(al_l),
             "overlap_efficiency": al / statistics.median(ov_l),
-            "overlap_efficiency_max": (al * 1e3 / max(al * 1e3, floor_us + al * 1e3 * grid / tiles)
-                                       if floor_us else 1.0),
+            "overlap_efficiency_max": (al * 1e3 / max(al * 1e3, floor_us + tail) if floor_us else 1.0),
             "link_floor_us": floor_us,
         }
         del shards, B, Ag, C, flags
-    out["note"] = ("overlap_efficiency_max estimates the ceiling: the GEMM alone over the link floor plus one "
-                   "tile time (the last panels cannot land earlier and then take a tile time; tiles that run "
-                   "alone at the end run faster, so a measured value can exceed it slightly); "
+    out["note"] = ("overlap_efficiency_max estimates the ceiling: the GEMM alone over the link floor plus the "
+                   "work left once the last data lands (one tile time, or one K chunk of it with K-chunked signal "
+                   "tiles; tiles that run alone at the end run faster, so a measured value can exceed it "
+                   "slightly); "
                    "the tiny fp32 case is latency-bound and checked mainly for correctness")
     return out
 
@@ -809,11 +816,11 @@ def main():
     n_tiles = (M // 256) * (-(-N // 256))
 
     def e_max(floor_us):
-        # ceiling on E: the last panel cannot start before its link delivers it (the link floor; jitter only
-        # delays releases), and then takes one tile time (its tiles run side by side); one tile time =
-        # T_alone * grid / tiles
+        # ceiling on E: the last panel's data cannot land before its link delivers it (the link floor; jitter
+        # only delays releases), and then its tiles (side by side) still compute what depends on the last
+        # signal tile: one tile time = T_alone * grid / tiles, or one K chunk of it with K-chunked tiles
         t_alone = al_k * 1e3
-        t_tile = t_alone * alone_grid / n_tiles
+        t_tile = t_alone * alone_grid / n_tiles / (kc if kc else 1)
         return t_alone / max(t_alone, floor_us + t_tile)
 
     # the arrival sweep: unthrottled, the xGMI link rate and 50 GB/s, jitter up to one signal tile's link time
