@@ -126,3 +126,18 @@ def test_rs_trace_words():
     assert sgt.rs_trace_words(4, 1024, 392, rs_tile=32) == 3 * (4 * 1 * 2 + 8 * 13)
     with pytest.raises(sgt.SgtError):
         sgt.rs_trace_words(4, 1000, 392)                               # M % W != 0
+
+
+def test_k_chunk_flag_counts():
+    import signal_gated_tiled_amd as sgt
+    # one flag per 256-row panel and K chunk
+    assert sgt.ag_flag_count(8, 16384, 8192, k_chunks=8) == 64 * 8
+    assert sgt.ag_flag_count(8, 8192, 5120, k_chunks=8) == 32 * 8          # Qwen: chunks of 640 columns
+    assert sgt.trace_words(8, 16384, 8192, 3584, k_chunks=8) == 64 * 14 * 4 + 64 * 8
+    for bad in (dict(W=8, M=16384, K=8192, k_chunks=3),                    # K not a multiple of 128 x 3
+                dict(W=8, M=8 * 200, K=1024, k_chunks=8),                  # shards of 200 rows: not whole panels
+                dict(W=8, M=16384, K=8192, k_chunks=65)):                  # above 64
+        with pytest.raises(sgt.SgtError):
+            sgt.ag_flag_count(bad["W"], bad["M"], bad["K"], k_chunks=bad["k_chunks"])
+    with pytest.raises(sgt.SgtError):
+        sgt.ag_flag_count(4, 256, 256, in_dtype=sgt.SGT_F32, k_chunks=1)    # fp32 inputs
