@@ -267,7 +267,8 @@ def _run_kc(ctx, dA, dB, M, K, N, b_layout, **kw):
 
 
 @pytest.mark.parametrize("b_layout", ["nk", "kn"])
-@pytest.mark.parametrize("link", [dict(peer_gbps=4.0, jitter_us=30.0, arrival_seed=3), dict()])
+@pytest.mark.parametrize("link", [dict(peer_gbps=4.0, jitter_us=30.0, arrival_seed=3), dict(),
+                                  dict(peer_gbps=4.0, arrival_seed=9, arrival_order="global")])
 def test_k_chunks_are_bit_identical_to_whole_rows(ctx, orc, b_layout, link):
     """Signal tiles of one panel x one K chunk: with slow, jittered links most remote tiles start on a panel
     whose later chunks are still in flight (B stored N x K: chunk by chunk; K x N: after the whole panel).
@@ -316,3 +317,18 @@ def test_k_chunks_rejections(ctx):
     g = torch.empty((w.M, w.K), dtype=torch.bfloat16, device="cuda:0")
     with pytest.raises(sgt.SgtError):
         ctx.allgather(dA, g, torch.zeros(64, dtype=torch.int32, device="cuda:0"), k_chunks=8, blocking=True)
+
+
+@pytest.mark.slow
+def test_k_chunks_full_qwen_shape(ctx):
+    """The Qwen3-32B share (K = 5120: 8 chunks of 640 columns) at 50 GB/s per link: the same C bits as the
+    whole-row signal tiles."""
+    w = I.QWEN_AG
+    shards, B = I.make_ag(w, B_layout="nk")
+    dA, dB = [dev(s) for s in shards], dev(B)
+    link = dict(peer_gbps=w.peer_gbps, arrival_seed=2)
+    _, C0, _ = _run_kc(ctx, dA, dB, w.M, w.K, w.N, "nk", rank=5, **link)
+    Ag1, C1, fl = _run_kc(ctx, dA, dB, w.M, w.K, w.N, "nk", rank=5, k_chunks=8, **link)
+    assert torch.equal(C1.view(torch.int32), C0.view(torch.int32))
+    assert torch.equal(Ag1.view(torch.int16), torch.cat(dA).view(torch.int16))
+    assert bool((fl == fl[0]).all())
