@@ -806,6 +806,14 @@ def main():
     serial_ms, _, _ = timed(lambda i, ev: ag("serial", arrival_seed=i + 1, **link)(i, ev), max(3, args.steps // 4),
                             2, torch, ctx)
     unthr_ms, _, _ = timed(ag("cu"), max(3, args.steps // 4), 2, torch, ctx)
+    # the same overlapped call with whole-row signal tiles (flag_rows rows x all K), for comparison
+    whole_ms = None
+    if kc:
+        flags_w = torch.zeros(sgt.ag_flag_count(W, M, K), dtype=torch.int32, device=dev)
+        whole_ms, _, _ = timed(lambda i, ev: ctx.ag_gemm(shards, B, Ag, C, flags_w, rank=rank, b_layout=lay,
+                                                         producer="cu", consumer_events=ev, arrival_seed=i + 1,
+                                                         **link), args.steps, args.warmup, torch, ctx)
+        del flags_w
     # correctness spot check of the last overlapped result against the gathered bits
     assert torch.equal(Ag.view(torch.int16), torch.cat(shards).view(torch.int16)), "gathered buffer mismatch"
 
@@ -863,6 +871,8 @@ def main():
         "producer_only_note": "serial call (paced producer, then the consumer on all CUs) minus the GEMM alone on "
                               "all CUs",
         "unthrottled_producer_ms": unthr_ms,
+        "overlapped_whole_row_signal_tiles_ms": whole_ms,
+        "overlapped_whole_row_signal_tiles_tflops": flops / (whole_ms * 1e-3) / 1e12 if whole_ms else None,
         "overlap_efficiency": al_k / ov_k,
         "overlap_efficiency_max": e_max(link_floor_us),
         "overlap_efficiency_note": "median consumer-kernel time of the GEMM alone over that of the overlapped call, "
