@@ -99,7 +99,10 @@ typedef struct sgt_opts {
   int32_t order;         /* enum sgt_order                                                      */
   int32_t flag_rows;     /* rows per AllGather signal tile; 0 = library default                 */
   int32_t producer_cus;  /* workgroups of the producer kernel; 0 = library default              */
-  int32_t consumer_cus;  /* workgroups of the persistent consumer; 0 = one per CU               */
+  int32_t consumer_cus;  /* workgroups of the persistent consumer; 0 = one per CU, less the
+                            producer's CUs beside an overlapped producer (its workgroup count
+                            rounded up to a multiple of CUs / 8, an equal share of every XCD);
+                            a caller's count must leave the producer room to start            */
   int32_t blocking;      /* nonzero: synchronize and return the device status                   */
   double peer_gbps;      /* simulated link rate per peer in GB/s; 0 = unthrottled               */
   double jitter_us;      /* each remote tile's release is delayed by U[0, jitter_us]            */
@@ -183,7 +186,7 @@ SGT_API int64_t sgt_panel_order(int W, int rank, int64_t M, int32_t panel_rows, 
  *     The results are the same bits as with whole-row signal tiles.
  * Requirements: 1 <= W <= 64, M % W == 0, (M/W) % flag_rows == 0, K, N >= 1;
  *     bf16: K % 8 == 0 and N % 8 == 0; all pointers 16-byte aligned.  With
- *     k_chunks = n: K % (128 n) == 0 and (M/W) % 256 == 0.
+ *     k_chunks = n: K % (128 n) == 0, (M/W) % 256 == 0 and flag_rows 0 (or 256).
  * M = 0 or N = 0 is a no-op that still advances the epoch.
  */
 SGT_API sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B, void* A_gathered, void* C,

@@ -203,6 +203,9 @@ sgt_status plan_ag(int W, int64_t M, int64_t K, int64_t N, const sgt_opts& o, Ag
   p->rows_per_shard = M / W;
   p->panel_rows = ag_panel_rows(o.in_dtype);
   p->panel_cols = ag_panel_cols(o.in_dtype);
+  if (o.k_chunks > 0 && o.flag_rows != 0 && o.flag_rows != p->panel_rows)
+    return fail(SGT_EINVAL, "flag_rows %d with k_chunks: a signal tile is one %d-row panel (pass 0)", o.flag_rows,
+                p->panel_rows);
   if (o.flag_rows > 0) {
     p->flag_rows = o.flag_rows;
   } else {
@@ -342,6 +345,20 @@ int build_schedule(const AgPlan& p, int W, int rank, int64_t K, int esz, const s
 int default_producer_wgs(const sgt_opts& o, int n_cu) {
   if (o.producer_cus > 0) return o.producer_cus;
   return std::max(8, n_cu / 8);
+}
+
+// Workgroups a persistent consumer may keep beside a producer kernel of pwg
+// workgroups.  Dispatch spreads each kernel's workgroups round-robin over the
+// XCDs, and within an XCD over its groups of CUs, and a consumer workgroup
+// fills a CU (its LDS allows one).  The producer's share is therefore rounded
+// up to a multiple of n_cu / 8 CUs (4 per XCD on 256 CUs): with an uneven
+// split (say 228 consumers beside 28 producers) one group of CUs can end up
+// fully held by consumers waiting on flags, and a producer workgroup sent
+// there never starts.
+int consumer_beside(const sgt_ctx* ctx, int pwg) {
+  const int unit = std::max(8, ctx->n_cu / 8);
+  const int reserve = (pwg + unit - 1) / unit * unit;
+  return std::max(1, ctx->n_cu - reserve);
 }
 
 sgt_status next_slot(sgt_ctx* ctx, int* slot) {
@@ -656,7 +673,7 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   ctx->slot_used[slot] = true;
   int grid;
   if (o.in_dtype == SGT_BF16)
-    grid = o.consumer_cus > 0 ? o.consumer_cus : std::max(1, ctx->n_cu - pwg);
+    grid = o.consumer_cus > 0 ? o.consumer_cus : consumer_beside(ctx, pwg);
   else
     grid = o.consumer_cus > 0 ? o.consumer_cus : 2 * ctx->n_cu;
   grid = std::min(grid, total_tiles);
@@ -858,7 +875,7 @@ sgt_status gemm_rs_impl(sgt_ctx* ctx, const void* A_local, const void* B, const 
   }
   // Overlapped: the GEMM+RS kernel on the CUs the producer leaves (one
   // workgroup per CU), so the reduction's waits cannot starve it.
-  const int grid = std::min(total, o.consumer_cus > 0 ? o.consumer_cus : std::max(1, ctx->n_cu - pwg));
+  const int grid = std::min(total, o.consumer_cus > 0 ? o.consumer_cus : consumer_beside(ctx, pwg));
   if ((st = mark(o, 0, stream)) != SGT_OK) return st;
   HIP_TRY(launch_gemm_rs(a, grid, stream));
   if ((st = mark(o, 1, stream)) != SGT_OK) return st;
@@ -1208,7 +1225,7 @@ sgt_status moe_gemm_rs_impl(sgt_ctx* ctx, const void* Hg, const void* W2, const 
                                stream, &pwg)) != SGT_OK)
     return st;
   const bool serial = o.producer == SGT_PROD_SERIAL;
-  const int avail = serial ? ctx->n_cu : std::max(1, ctx->n_cu - pwg);
+  const int avail = serial ? ctx->n_cu : consumer_beside(ctx, pwg);
   const int grid = o.consumer_cus > 0 ? std::min(o.consumer_cus, avail) : avail;
   if ((st = mark(o, 0, stream)) != SGT_OK) return st;
   HIP_TRY(launch_moe_rs(a, grid, stream));
@@ -1479,7 +1496,7 @@ sgt_status sgt_ring_allreduce(sgt_ctx* ctx, const float* x, const float* left_ms
   ctx->slot_used[slot] = true;
   // the ring's workgroups take the CUs the producer leaves, so every wait can end
   const int grid = (int)std::min<int64_t>(n_items, o.consumer_cus > 0 ? o.consumer_cus
-                                                                       : std::max(1, ctx->n_cu - pwg));
+                                                                       : consumer_beside(ctx, pwg));
   if ((st = mark(o, 0, stream)) != SGT_OK) return st;
   HIP_TRY(launch_ring_allreduce(a, grid, stream));
   if ((st = mark(o, 1, stream)) != SGT_OK) return st;
@@ -1588,9 +1605,10 @@ sgt_status sgt_a2a_dispatch(sgt_ctx* ctx, const void* const* X, const int32_t* c
   std::lock_guard<std::mutex> lock(ctx->mu);
   DeviceGuard g(ctx->device);
   hipStream_t stream = static_cast<hipStream_t>(stream_);
+  A2aArgs a = a2a_args(ctx, o, W, T_r, H * esz, E, k, cr, nch, 0, flags, 0);
+  if ((st = a2a_pacing_ok(a)) != SGT_OK) return st;  // rejected before the epoch advances
   const uint32_t e = ++ctx->epoch;
-  A2aArgs a = a2a_args(ctx, o, W, T_r, H * esz, E, k, cr, nch, 0, flags, e);
-  if ((st = a2a_pacing_ok(a)) != SGT_OK) return st;
+  a.epoch = e;
   for (int p = 0; p < W; ++p) {
     a.src.p[p] = X ? X[p] : nullptr;
     a.table.p[p] = topk ? topk[p] : nullptr;  // not read when T_r = 0
@@ -1636,10 +1654,11 @@ sgt_status sgt_a2a_combine(sgt_ctx* ctx, const void* const* back, const int32_t*
   std::lock_guard<std::mutex> lock(ctx->mu);
   DeviceGuard g(ctx->device);
   hipStream_t stream = static_cast<hipStream_t>(stream_);
+  A2aArgs a = a2a_args(ctx, o, W, T_r, H * 2, E, k, cr, nch, 1, flags, 0);
+  if ((st = a2a_pacing_ok(a)) != SGT_OK) return st;  // rejected before the epoch advances
   const uint32_t e = ++ctx->epoch;
+  a.epoch = e;
   if (T_r == 0) return finish(ctx, o, stream);
-  A2aArgs a = a2a_args(ctx, o, W, T_r, H * 2, E, k, cr, nch, 1, flags, e);
-  if ((st = a2a_pacing_ok(a)) != SGT_OK) return st;
   for (int q = 0; q < W; ++q) a.src.p[q] = back && !preset ? back[q] : nullptr;
   a.table.p[0] = topk;
   a.dst = static_cast<char*>(cbuf);

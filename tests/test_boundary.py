@@ -141,3 +141,6 @@ def test_k_chunk_flag_counts():
             sgt.ag_flag_count(bad["W"], bad["M"], bad["K"], k_chunks=bad["k_chunks"])
     with pytest.raises(sgt.SgtError):
         sgt.ag_flag_count(4, 256, 256, in_dtype=sgt.SGT_F32, k_chunks=1)    # fp32 inputs
+    with pytest.raises(sgt.SgtError):
+        sgt.ag_flag_count(8, 16384, 8192, k_chunks=8, flag_rows=128)        # signal tiles are whole panels
+    assert sgt.ag_flag_count(8, 16384, 8192, k_chunks=8, flag_rows=256) == 64 * 8

@@ -252,10 +252,17 @@ def test_invalid_arguments_are_rejected(ctx):
     tok = torch.zeros((2, 2, 8), dtype=torch.int32, device="cuda:0")
     cnt = torch.zeros((2, 2), dtype=torch.int64, device="cuda:0")
     fl = torch.zeros(64, dtype=torch.int32, device="cuda:0")
+
+    def epoch_of_valid_call():
+        ctx.a2a_dispatch([x, x], [t, t], recv, tok, cnt, fl, 4, blocking=True)
+        return int(cnt.cpu().numpy().view(np.uint64)[0, 0] >> np.uint64(32))
+
+    e0 = epoch_of_valid_call()
     for E, kw in ((5, {}), (4, {"producer": "preset"}), (4, {"flag_rows": 2048}), (4, {"peer_gbps": 1e-9})):
         with pytest.raises(sgt.SgtError) as ei:
             ctx.a2a_dispatch([x, x], [t, t], recv, tok, cnt, fl, E, **kw)
         assert ei.value.status in (sgt.SGT_EINVAL, sgt.SGT_EUNSUPPORTED)
+    assert epoch_of_valid_call() == e0 + 1, "a rejected call advanced the context's epoch"
     odd = torch.zeros((8, 60), dtype=torch.bfloat16, device="cuda:0")   # 120-byte rows
     with pytest.raises(sgt.SgtError):
         ctx.a2a_dispatch([odd, odd], [t, t], recv, tok, cnt, fl, 4)
