@@ -198,6 +198,39 @@ def test_moe_rs_bad_args(ctx, orc):
 
 
 @pytest.mark.slow
+def test_full_moe_rs_shape_paced_back_to_back(ctx, orc):
+    """The full shape with the peers at 50 GB/s from rank 0: 7 peers x 4 bands = 28 producer workgroups
+    beside the persistent consumer, twelve calls queued back to back; each call's P and C keep the bits of
+    the resident-peer call (no flag wait may expire)."""
+    w = I.MOE_RS
+    Hg, W2, gate, logits, parts = make(w, "nk")
+    ids, off, rt = orc.moe_route(logits, w.topk)
+    rank = 0
+    _, P0, C0, _, _ = run_moe_rs(ctx, Hg, W2, gate, ids, off, rt, parts, rank, "nk")
+    ng, npf = sgt.rs_flag_count(w.W, w.T, w.H, rs_tile=128)
+    Y = torch.empty((w.T * w.topk, w.H), dtype=torch.float32, device="cuda:0")
+    P = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda:0")
+    C = torch.empty((w.T // w.W, w.H), dtype=torch.float32, device="cuda:0")
+    gf = torch.zeros(ng, dtype=torch.int32, device="cuda:0")
+    pf = torch.zeros(npf, dtype=torch.int32, device="cuda:0")
+    dparts = [dev(p) if q != rank else None for q, p in enumerate(parts)]
+    inbox = [torch.empty_like(p) if p is not None else None for p in dparts]
+    args = (dev(Hg), dev(W2), dev(gate), dev(ids), dev(off), dev(rt), dparts, Y, P, C, gf, pf)
+    for i in range(12):
+        ctx.moe_gemm_rs(*args, rank=rank, b_layout="nk", inbox=inbox, peer_gbps=50.0, arrival_seed=i + 1)
+    torch.cuda.synchronize()
+    ctx.sync()
+    assert np.array_equal(host(C).view(np.uint32), C0.view(np.uint32))
+    assert np.array_equal(host(P).view(np.uint32), P0.view(np.uint32))
+    e = host(gf)[0]
+    assert (host(gf) == e).all()
+    nb = npf // w.W   # peer flags, one block per rank; this rank's own block is never sent
+    pfl = host(pf)
+    for q in range(1, w.W):
+        assert (pfl[q * nb:(q + 1) * nb] == e).all(), "peer %d flags" % q
+
+
+@pytest.mark.slow
 def test_full_moe_rs_shape(ctx, orc):
     w = I.MOE_RS
     Hg, W2, gate, logits, parts = make(w, "nk")
