@@ -102,7 +102,7 @@ typedef struct sgt_opts {
   int32_t consumer_cus;  /* workgroups of the persistent consumer; 0 = one per CU, less the
                             producer's CUs beside an overlapped producer (its workgroup count
                             rounded up to a multiple of CUs / 8, an equal share of every XCD);
-                            a caller's count must leave the producer room to start            */
+                            a caller's count is capped there, so the producer can always start */
   int32_t blocking;      /* nonzero: synchronize and return the device status                   */
   double peer_gbps;      /* simulated link rate per peer in GB/s; 0 = unthrottled               */
   double jitter_us;      /* each remote tile's release is delayed by U[0, jitter_us]            */

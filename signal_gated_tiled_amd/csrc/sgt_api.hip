@@ -673,7 +673,7 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   ctx->slot_used[slot] = true;
   int grid;
   if (o.in_dtype == SGT_BF16)
-    grid = o.consumer_cus > 0 ? o.consumer_cus : consumer_beside(ctx, pwg);
+    grid = o.consumer_cus > 0 ? std::min(o.consumer_cus, consumer_beside(ctx, pwg)) : consumer_beside(ctx, pwg);
   else
     grid = o.consumer_cus > 0 ? o.consumer_cus : 2 * ctx->n_cu;
   grid = std::min(grid, total_tiles);
@@ -875,7 +875,7 @@ sgt_status gemm_rs_impl(sgt_ctx* ctx, const void* A_local, const void* B, const 
   }
   // Overlapped: the GEMM+RS kernel on the CUs the producer leaves (one
   // workgroup per CU), so the reduction's waits cannot starve it.
-  const int grid = std::min(total, o.consumer_cus > 0 ? o.consumer_cus : consumer_beside(ctx, pwg));
+  const int grid = std::min(total, std::min(o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu, consumer_beside(ctx, pwg)));
   if ((st = mark(o, 0, stream)) != SGT_OK) return st;
   HIP_TRY(launch_gemm_rs(a, grid, stream));
   if ((st = mark(o, 1, stream)) != SGT_OK) return st;
@@ -1495,8 +1495,8 @@ sgt_status sgt_ring_allreduce(sgt_ctx* ctx, const float* x, const float* left_ms
   HIP_TRY(hipEventRecord(ctx->slot_ev[slot], ctx->prod));
   ctx->slot_used[slot] = true;
   // the ring's workgroups take the CUs the producer leaves, so every wait can end
-  const int grid = (int)std::min<int64_t>(n_items, o.consumer_cus > 0 ? o.consumer_cus
-                                                                       : consumer_beside(ctx, pwg));
+  const int grid = (int)std::min<int64_t>(n_items, std::min(o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu,
+                                                            consumer_beside(ctx, pwg)));
   if ((st = mark(o, 0, stream)) != SGT_OK) return st;
   HIP_TRY(launch_ring_allreduce(a, grid, stream));
   if ((st = mark(o, 1, stream)) != SGT_OK) return st;
