@@ -1082,8 +1082,12 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   ctx->moe_prod_started += (uint32_t)pwg;
   a.started = ctx->d_moe + 12;
   a.started_all = ctx->moe_prod_started;
-  a.late_blocks = o.consumer_cus > 0 ? 0 : std::min(pwg, ctx->n_cu - 1);
-  if ((st = route_and_compute(ctx->d_ranks[slot], o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu)) != SGT_OK)
+  // (the late share is the producer's rounded up as for the other overlapped
+  // calls, so the workgroups that never yield are spread evenly over the XCDs)
+  a.late_blocks = o.consumer_cus > 0 ? 0 : ctx->n_cu - consumer_beside(ctx, pwg);
+  if ((st = route_and_compute(ctx->d_ranks[slot], o.consumer_cus > 0
+                                                      ? std::min(o.consumer_cus, consumer_beside(ctx, pwg))
+                                                      : ctx->n_cu)) != SGT_OK)
     return st;
   HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
   HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
