@@ -61,7 +61,7 @@ extern "C" {
 typedef enum sgt_status {
   SGT_OK = 0,
   SGT_EINVAL = -1,        /* bad argument (shape, pointer, alignment, option) */
-  SGT_EUNSUPPORTED = -2,  /* valid request this build does not implement      */
+  SGT_EUNSUPPORTED = -2,  /* valid request the library does not implement     */
   SGT_ETIMEDOUT = -3,     /* a kernel's bounded wait on a flag expired         */
   SGT_EHIP = -4,          /* a HIP runtime call failed                          */
   SGT_ENOMEM = -5         /* context creation could not allocate               */
