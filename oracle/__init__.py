@@ -328,12 +328,18 @@ def ag_gemm_protocol(shards, B, rank: int, b_layout: str = "kn", flag_rows: int 
 
 # ---- ring AllReduce (semantics page, "Example: ring AllReduce with overlap") ----
 
-def allreduce(xs) -> np.ndarray:
-    """The plain definition: the elementwise sum of the ranks' vectors, in double precision."""
-    out = np.zeros(np.asarray(xs[0]).size, dtype=np.float64)
-    for x in xs:
-        out += np.asarray(x, dtype=np.float64).reshape(-1)
-    return out
+def allreduce(xs, planted: str = "") -> np.ndarray:
+    """The plain definition: the elementwise sum of the ranks' vectors, in double precision.
+
+    ``planted`` (tests only, to show the pins catch a plausible mistake): "drop_first" leaves out
+    rank 0's vector, "f32" accumulates in single precision."""
+    acc = np.float32 if planted == "f32" else np.float64
+    out = np.zeros(np.asarray(xs[0]).size, dtype=acc)
+    for q, x in enumerate(xs):
+        if planted == "drop_first" and q == 0:
+            continue
+        out += np.asarray(x, dtype=acc).reshape(-1)
+    return out.astype(np.float64)
 
 
 def _f32_add(a, b):

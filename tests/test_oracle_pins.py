@@ -479,6 +479,32 @@ def test_ring_closes_and_rank_view_matches(orc):
             assert np.array_equal(o, outs[q]) and np.array_equal(ob, outbox[q])
 
 
+def _allreduce_pins_hold(orc, planted=""):
+    """The pins of oracle.allreduce: (i) integer-valued fp32 vectors sum exactly, compared with an
+    int64 sum; (ii) a hand-worked example whose fp32 running sum would lose the small terms:
+    rank 0 holds 2^24, ranks 1..3 hold 1, so the exact sum 2^24 + 3 (representable in fp64) differs
+    from every fp32 accumulation order that starts at 2^24 (2^24 + 1 rounds back to 2^24), and
+    element 1 is rank 0's alone (-7.5, others 0)."""
+    xs = _ring_xs(6, 6 * 40, kind="int", seed=91)
+    ok_int = np.array_equal(orc.allreduce(xs, planted=planted), np.sum(np.stack(xs).astype(np.int64), axis=0))
+    hand = [np.array([2.0**24, -7.5], np.float32)] + [np.array([1.0, 0.0], np.float32) for _ in range(3)]
+    got = orc.allreduce(hand, planted=planted)
+    ok_hand = got[0] == 16777219.0 and got[1] == -7.5
+    return ok_int and ok_hand
+
+
+def test_allreduce_pins(orc):
+    assert _allreduce_pins_hold(orc)
+    # the result is fp64 and has one element per input element
+    out = orc.allreduce([np.ones(5, np.float32)] * 3)
+    assert out.dtype == np.float64 and out.shape == (5,) and np.all(out == 3.0)
+
+
+@pytest.mark.parametrize("planted", ["drop_first", "f32"])
+def test_allreduce_planted_mistake_is_caught(orc, planted):
+    assert not _allreduce_pins_hold(orc, planted=planted)
+
+
 def test_ring_planted_mistake_is_caught(orc):
     xs = _ring_xs(4, 16, kind="int")
     outs, _, _ = orc.ring_allreduce(xs, planted="rs_chunk")
