@@ -674,8 +674,8 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   int grid;
   if (o.in_dtype == SGT_BF16)
     grid = o.consumer_cus > 0 ? std::min(o.consumer_cus, consumer_beside(ctx, pwg)) : consumer_beside(ctx, pwg);
-  else
-    grid = o.consumer_cus > 0 ? o.consumer_cus : 2 * ctx->n_cu;
+  else  // fp32 tiles: small workgroups, two per CU by default (a caller's count is capped there)
+    grid = o.consumer_cus > 0 ? std::min(o.consumer_cus, 2 * ctx->n_cu) : 2 * ctx->n_cu;
   grid = std::min(grid, total_tiles);
   if (N > 0) {
       if ((st = mark(o, 0, stream)) != SGT_OK) return st;
@@ -776,16 +776,16 @@ sgt_status join_paced_peers(sgt_ctx* ctx, hipStream_t stream) {
   return SGT_OK;
 }
 
-// GEMM + ReduceScatter, shared by the resident and the paced entry points.
-// reduce_from[p]: what the reduction sums for peer p.  peer_blocks == NULL:
-// the peers' data is resident and their flags are preset.  Otherwise the
-// producer copies peer_blocks[p] into reduce_from[p] in bands of rs_tile rows,
-// each band released (its tiles' peer flags) when peer p's link would deliver it.
-sgt_status gemm_rs_impl(sgt_ctx* ctx, const void* A_local, const void* B, const float* const* reduce_from,
-                        const float* const* peer_blocks, float* partial_out, float* C_shard, uint32_t* gflags,
-                        uint32_t* pflags, int W, int64_t M, int64_t K, int64_t N, const sgt_opts* opts,
-                        void* stream_) {
-  if (!ctx) return fail(SGT_EINVAL, "ctx is NULL");
+// Validation and kernel arguments of a GEMM + ReduceScatter call, shared by
+// the context entry points and the static-scratch one.  peer_blocks != NULL:
+// paced peers.  caller_flags: gflags / pflags are the caller's (else they live
+// in the library's scratch and are filled in by the caller of this function).
+// Fills every field of *a except the epoch, the status word, the claim
+// counter and the flags; *np = peer flag words.
+sgt_status rs_plan(const void* A_local, const void* B, const float* const* reduce_from,
+                   const float* const* peer_blocks, float* partial_out, float* C_shard, const uint32_t* gflags,
+                   const uint32_t* pflags, bool caller_flags, int W, int64_t M, int64_t K, int64_t N,
+                   const sgt_opts* opts, RsArgs* a, int64_t* ng_out, int64_t* np_out) {
   sgt_status st = check_opts(opts, W < 1 ? 1 : W);
   if (st != SGT_OK) return st;
   const sgt_opts& o = *opts;
@@ -812,10 +812,10 @@ sgt_status gemm_rs_impl(sgt_ctx* ctx, const void* A_local, const void* B, const 
   if (paced && (band_bytes >= ((int64_t)1 << 31) || rs_tn > 65535 || (int64_t)(W - 1) * (br / rt) > kItemsCap))
     return fail(SGT_EUNSUPPORTED, "bands too large or too many for the producer");
   if (M > 0 && N > 0) {
-    if (!A_local || !B || !partial_out || !C_shard || !gflags || !pflags || !reduce_from)
+    if (!A_local || !B || !partial_out || !C_shard || !reduce_from || (caller_flags && (!gflags || !pflags)))
       return fail(SGT_EINVAL, "NULL pointer argument");
     if (!aligned16(A_local) || !aligned16(B) || !aligned16(partial_out) || !aligned16(C_shard) ||
-        !aligned16(gflags) || !aligned16(pflags))
+        (caller_flags && (!aligned16(gflags) || !aligned16(pflags))))
       return fail(SGT_EINVAL, "pointers must be 16-byte aligned");
     for (int p = 0; p < W; ++p) {
       if (p == o.rank) continue;
@@ -825,27 +825,51 @@ sgt_status gemm_rs_impl(sgt_ctx* ctx, const void* A_local, const void* B, const 
         return fail(SGT_EINVAL, "peer_blocks[%d] NULL or not 16-byte aligned", p);
     }
   }
+  *a = RsArgs{};
+  a->A = A_local; a->B = B; a->P = partial_out; a->C_shard = C_shard;
+  for (int p = 0; p < W; ++p) a->partials.p[p] = (p == o.rank) ? nullptr : reduce_from[p];
+  a->trace = o.trace;
+  a->M = M; a->N = N; a->K = K; a->block_rows = br; a->W = W; a->rank = o.rank;
+  const int bm = rs_gemm_tile();
+  a->tiles_n = (int)((N + bm - 1) / bm);
+  a->tiles_m = (int)(W * ((br + bm - 1) / bm));
+  a->rs_tile = rt; a->rs_tm = (int)(br / rt); a->rs_tn = (int)rs_tn;
+  a->b_layout = o.b_layout;
+  a->n_gemm_tiles = a->tiles_m * a->tiles_n;
+  a->red_split = rs_red_split(rt);
+  a->n_red_items = a->rs_tm * a->rs_tn * a->red_split;
+  a->timeout_ticks = timeout_ticks(o);
+  a->tile_waves = o.tile_waves ? o.tile_waves : 8;
+  *ng_out = ng;
+  *np_out = np;
+  return SGT_OK;
+}
+
+// GEMM + ReduceScatter, shared by the resident and the paced entry points.
+// reduce_from[p]: what the reduction sums for peer p.  peer_blocks == NULL:
+// the peers' data is resident and their flags are preset.  Otherwise the
+// producer copies peer_blocks[p] into reduce_from[p] in bands of rs_tile rows,
+// each band released (its tiles' peer flags) when peer p's link would deliver it.
+sgt_status gemm_rs_impl(sgt_ctx* ctx, const void* A_local, const void* B, const float* const* reduce_from,
+                        const float* const* peer_blocks, float* partial_out, float* C_shard, uint32_t* gflags,
+                        uint32_t* pflags, int W, int64_t M, int64_t K, int64_t N, const sgt_opts* opts,
+                        void* stream_) {
+  if (!ctx) return fail(SGT_EINVAL, "ctx is NULL");
+  const bool paced = peer_blocks != nullptr;
+  RsArgs a;
+  int64_t ng = 0, np = 0;
+  sgt_status st = rs_plan(A_local, B, reduce_from, peer_blocks, partial_out, C_shard, gflags, pflags, true, W, M, K,
+                          N, opts, &a, &ng, &np);
+  if (st != SGT_OK) return st;
+  const sgt_opts& o = *opts;
+  const int64_t band_bytes = (int64_t)a.rs_tile * N * 4;
   std::lock_guard<std::mutex> lock(ctx->mu);
   DeviceGuard g(ctx->device);
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   const uint32_t e = ++ctx->epoch;
   if (M == 0 || N == 0) return SGT_OK;
-
-  RsArgs a{};
-  a.A = A_local; a.B = B; a.P = partial_out; a.C_shard = C_shard;
-  for (int p = 0; p < W; ++p) a.partials.p[p] = (p == o.rank) ? nullptr : reduce_from[p];
-  a.gflags = gflags; a.pflags = pflags; a.status = ctx->d_status; a.trace = o.trace;
-  a.M = M; a.N = N; a.K = K; a.block_rows = br; a.W = W; a.rank = o.rank;
-  const int bm = rs_gemm_tile();
-  a.tiles_n = (int)((N + bm - 1) / bm);
-  a.tiles_m = (int)(W * ((br + bm - 1) / bm));
-  a.rs_tile = rt; a.rs_tm = (int)(br / rt); a.rs_tn = (int)rs_tn;
-  a.b_layout = o.b_layout;
-  a.n_gemm_tiles = a.tiles_m * a.tiles_n;
-  a.red_split = rs_red_split(rt);
-  a.n_red_items = a.rs_tm * a.rs_tn * a.red_split;
-  a.epoch = e; a.timeout_ticks = timeout_ticks(o);
-  a.tile_waves = o.tile_waves ? o.tile_waves : 8;
+  a.gflags = gflags; a.pflags = pflags; a.status = ctx->d_status;
+  a.epoch = e;
   a.red_counter = ctx->d_counters;
   const int total = a.n_gemm_tiles + a.n_red_items;
 
@@ -853,7 +877,9 @@ sgt_status gemm_rs_impl(sgt_ctx* ctx, const void* A_local, const void* B, const 
     // Peers' partials are resident: their flags are set before the kernel
     // starts, and the reduction-claim counter restarts (a fill kernel, not a memset).
     HIP_TRY(launch_rs_prepare(pflags, np, e, ctx->d_counters, stream));
-    const int grid = std::min(total, o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu);
+    // at most one workgroup per CU, so every workgroup is resident: a reduction
+    // item waits on GEMM tiles statically assigned to other workgroups
+    const int grid = std::min(total, o.consumer_cus > 0 ? std::min(o.consumer_cus, ctx->n_cu) : ctx->n_cu);
     if ((st = mark(o, 0, stream)) != SGT_OK) return st;
     HIP_TRY(launch_gemm_rs(a, grid, stream));
     if ((st = mark(o, 1, stream)) != SGT_OK) return st;
@@ -867,7 +893,7 @@ sgt_status gemm_rs_impl(sgt_ctx* ctx, const void* A_local, const void* B, const 
                                ctx->d_counters, stream, &pwg)) != SGT_OK)
     return st;
   if (o.producer == SGT_PROD_SERIAL) {
-    const int grid = std::min(total, o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu);
+    const int grid = std::min(total, o.consumer_cus > 0 ? std::min(o.consumer_cus, ctx->n_cu) : ctx->n_cu);
     if ((st = mark(o, 0, stream)) != SGT_OK) return st;
     HIP_TRY(launch_gemm_rs(a, grid, stream));
     if ((st = mark(o, 1, stream)) != SGT_OK) return st;
@@ -1024,16 +1050,22 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   uint64_t* trace_rel = o.trace ? o.trace + n_items_max * 4 : nullptr;
   const int64_t tile_bytes = p.flag_rows * H * esz;
 
-  // Routing and the grouped consumer, on the caller's stream.
-  auto route_and_compute = [&](const uint32_t* ranks, int grid) -> sgt_status {
+  // Routing and the grouped consumer, on the caller's stream.  keep > 0: an
+  // overlapped call, where only `keep` workgroups of the launched grid may wait
+  // for the producer; the others (the last launched - keep) yield unless every
+  // producer workgroup already runs.  The split is taken on the grid actually
+  // launched, so a grid of keep workgroups or fewer never yields.
+  auto route_and_compute = [&](const uint32_t* ranks, int grid, int keep) -> sgt_status {
     HIP_TRY(launch_moe_route(logits, T, E, topk, ranks, a.flag_rows, (uint32_t)p.n_flags, rows, tb, expert_off,
                              row_token, topk_ids, stream));
     ctx->moe_parity ^= 1;  // this call's top-k cleared the other counts buffer for the next call
     if (I > 0) {
+      const int launched = (int)std::max<int64_t>(1, std::min<int64_t>(grid, n_items_max));
+      a.late_blocks = keep > 0 ? std::max(0, launched - keep) : 0;
       sgt_status s2;
       if ((s2 = mark(o, 0, stream)) != SGT_OK) return s2;
-      HIP_TRY(launch_moe_consumer(a, o.b_layout, o.out_dtype, rows, o.tile_waves ? o.tile_waves : 8,
-                                  (int)std::min<int64_t>(grid, n_items_max), stream));
+      HIP_TRY(launch_moe_consumer(a, o.b_layout, o.out_dtype, rows, o.tile_waves ? o.tile_waves : 8, launched,
+                                  stream));
       if ((s2 = mark(o, 1, stream)) != SGT_OK) return s2;
     }
     return SGT_OK;
@@ -1042,7 +1074,9 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   if (o.producer == SGT_PROD_PRESET) {
     // X_gathered already holds every shard: all flags take the epoch.
     HIP_TRY(launch_fill_u32(shard_flags, p.n_flags, e, stream));
-    if ((st = route_and_compute(nullptr, o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu)) != SGT_OK) return st;
+    if ((st = route_and_compute(nullptr, o.consumer_cus > 0 ? std::min(o.consumer_cus, ctx->n_cu) : ctx->n_cu, 0)) !=
+        SGT_OK)
+      return st;
     return finish(ctx, o, stream);
   }
 
@@ -1058,7 +1092,8 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
     if ((st = upload_items(ctx, slot, ctx->h_items[slot], n_items, stream)) != SGT_OK) return st;
     HIP_TRY(launch_ag_producer(shard_flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
                                trace_rel, pwg, stream));
-    if ((st = route_and_compute(ctx->d_ranks[slot], o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu)) != SGT_OK)
+    if ((st = route_and_compute(ctx->d_ranks[slot], o.consumer_cus > 0 ? std::min(o.consumer_cus, ctx->n_cu)
+                                                                         : ctx->n_cu, 0)) != SGT_OK)
       return st;
     HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
     ctx->slot_used[slot] = true;
@@ -1082,12 +1117,12 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   ctx->moe_prod_started += (uint32_t)pwg;
   a.started = ctx->d_moe + 12;
   a.started_all = ctx->moe_prod_started;
-  // (the late share is the producer's rounded up as for the other overlapped
-  // calls, so the workgroups that never yield are spread evenly over the XCDs)
-  a.late_blocks = o.consumer_cus > 0 ? 0 : ctx->n_cu - consumer_beside(ctx, pwg);
-  if ((st = route_and_compute(ctx->d_ranks[slot], o.consumer_cus > 0
-                                                      ? std::min(o.consumer_cus, consumer_beside(ctx, pwg))
-                                                      : ctx->n_cu)) != SGT_OK)
+  // (the workgroups that never yield are consumer_beside(pwg), the CUs left
+  // beside the producer's share rounded up as for the other overlapped calls,
+  // so they are spread evenly over the XCDs; a caller's count is capped there)
+  const int keep = consumer_beside(ctx, pwg);
+  if ((st = route_and_compute(ctx->d_ranks[slot], o.consumer_cus > 0 ? std::min(o.consumer_cus, keep) : ctx->n_cu,
+                              keep)) != SGT_OK)
     return st;
   HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
   HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
