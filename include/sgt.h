@@ -241,6 +241,39 @@ SGT_API sgt_status sgt_gemm_rs_paced(sgt_ctx* ctx, const void* A_local, const vo
                                      uint32_t* pflags, int W, int64_t M, int64_t K, int64_t N, const sgt_opts* opts,
                                      void* stream);
 
+/*
+ * sgt_gemm_rs without any allocation, for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same operation, arguments, kernels and results as
+ * sgt_gemm_rs with resident peers (producer SGT_PROD_CU or SGT_PROD_PRESET,
+ * peer_gbps 0), but there is no context and no flag array: the status word,
+ * the reduction's claim counter and every GEMM and peer flag live in the
+ * library's static scratch, a device array of sgt_gemm_rs_static_scratch_bytes()
+ * (64 KiB) that each GPU the library runs on holds until the process ends.
+ * The call runs on the calling thread's current device; the first call on a
+ * device looks up that device's copy of the array (no allocation), and the
+ * call itself launches two kernels and calls no hipMalloc, hipFree or other
+ * allocating routine.  Epochs are kept per device by the library.
+ * Limits: a call needing more than the scratch's flag words (GEMM flags
+ * ceil(M/rs_tile) * ceil(N/rs_tile) plus peer flags W * (M/W/rs_tile) *
+ * ceil(N/rs_tile), at most 16320) returns SGT_EINVAL and launches nothing;
+ * opts->trace must be NULL (SGT_EUNSUPPORTED).
+ * Sharing: every call on a GPU uses that GPU's one array and leaves its
+ * contents for the next call (the counter is cleared by the call's first
+ * kernel; flags carry the epoch).  Calls on one stream are ordered; calls that
+ * overlap in time on one GPU (other streams, other threads) race and are not
+ * supported.  Errors: SGT_EINVAL / SGT_EUNSUPPORTED before any launch; with
+ * opts->blocking the call synchronizes `stream` and returns SGT_ETIMEDOUT if a
+ * bounded wait expired (in this call or an earlier non-blocking one), clearing
+ * the status.
+ */
+SGT_API sgt_status sgt_gemm_rs_static(const void* A_local, const void* B, const float* const* partials,
+                                      float* partial_out, float* C_shard, int W, int64_t M, int64_t K, int64_t N,
+                                      const sgt_opts* opts, void* stream);
+
+/* Bytes of the static scratch sgt_gemm_rs_static uses on each device (64 KiB). */
+SGT_API int64_t sgt_gemm_rs_static_scratch_bytes(void);
+
 /* Flag counts for sgt_gemm_rs: *gflags_n and *pflags_n (either may be NULL). */
 SGT_API sgt_status sgt_rs_flag_count(int W, int64_t M, int64_t N, const sgt_opts* opts, int64_t* gflags_n, int64_t* pflags_n);
 

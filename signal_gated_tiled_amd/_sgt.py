@@ -105,10 +105,13 @@ def lib() -> ctypes.CDLL:
         L.sgt_a2a_flag_count.restype = I64
         L.sgt_rs_trace_words.argtypes = [ctypes.c_int, I64, I64, ctypes.POINTER(Opts)]
         L.sgt_rs_trace_words.restype = I64
+        L.sgt_gemm_rs_static.argtypes = [P, P, P, P, P, ctypes.c_int, I64, I64, I64, ctypes.POINTER(Opts), P]
+        L.sgt_gemm_rs_static_scratch_bytes.argtypes = []
+        L.sgt_gemm_rs_static_scratch_bytes.restype = I64
         for f in ("sgt_ctx_create", "sgt_ctx_destroy", "sgt_sync", "sgt_ag_gemm", "sgt_rs_flag_count", "sgt_gemm_rs",
                   "sgt_gemm_rs_paced", "sgt_moe_ag_gemm", "sgt_moe_gemm_rs",
                   "sgt_moe_gemm_rs_paced", "sgt_allgather", "sgt_ll_allgather", "sgt_ring_allreduce",
-                  "sgt_a2a_dispatch", "sgt_a2a_combine"):
+                  "sgt_a2a_dispatch", "sgt_a2a_combine", "sgt_gemm_rs_static"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -270,6 +273,31 @@ def rs_flag_count(W: int, M: int, N: int, rs_tile: int = 0):
     g, p = I64(), I64()
     _check(lib().sgt_rs_flag_count(W, M, N, ctypes.byref(o), ctypes.byref(g), ctypes.byref(p)))
     return int(g.value), int(p.value)
+
+
+def gemm_rs_static(A_local, B, partials: Sequence, partial_out, C_shard, *, stream=None, **kw):
+    """sgt_gemm_rs_static: GEMM + ReduceScatter with resident peers and no allocation (flags, counter and
+    status in the library's per-device static scratch; no context).  Runs on the tensors' device, which must
+    be the current one."""
+    import torch
+    dev = B.device
+    if torch.cuda.current_device() != dev.index:
+        raise ValueError("gemm_rs_static runs on the current device (%d); the tensors are on %s" %
+                         (torch.cuda.current_device(), dev))
+    W = len(partials)
+    M, K = A_local.shape
+    lay = kw.get("b_layout", "kn")
+    N = B.shape[1] if lay == "kn" else B.shape[0]
+    kw.setdefault("in_dtype", _dtype_code(B))
+    o = make_opts(**kw)
+    ptrs = (P * W)(*[_dev_ptr(p, "partials[%d]" % i, dev) if p is not None else 0 for i, p in enumerate(partials)])
+    _check(lib().sgt_gemm_rs_static(_dev_ptr(A_local, "A_local", dev), _dev_ptr(B, "B", dev), ctypes.cast(ptrs, P),
+                                    _dev_ptr(partial_out, "partial_out", dev), _dev_ptr(C_shard, "C_shard", dev), W,
+                                    M, K, N, ctypes.byref(o), _stream_handle(stream)))
+
+
+def gemm_rs_static_scratch_bytes() -> int:
+    return int(lib().sgt_gemm_rs_static_scratch_bytes())
 
 
 class Context:

@@ -929,6 +929,102 @@ sgt_status sgt_gemm_rs_paced(sgt_ctx* ctx, const void* A_local, const void* B, c
                       stream);
 }
 
+}  // extern "C"
+
+// ---- GEMM + ReduceScatter with no allocation: the library's static scratch ----
+//
+// For callers that cannot allocate device memory (code under stream capture,
+// tight serving loops): the status word, the reduction's claim counter and
+// every signal flag of the call live in `scratch`, a file-scope device array
+// of 64 KiB that each GPU holds until the process ends.  Its device
+// address is taken once per device with hipGetSymbolAddress (the array's name
+// in host code is not a device address) and only that address is used.
+namespace {
+
+constexpr int kScratchWords = 16384;                  // 64 KiB
+constexpr int kScratchHead = 64;                      // status (4 words), claim counter, padding
+constexpr int kScratchFlagWords = kScratchWords - kScratchHead;
+constexpr int kMaxDevices = 64;
+
+__device__ __align__(256) uint32_t scratch[kScratchWords];
+
+struct StaticDev {
+  uint32_t* ptr = nullptr;  // device address of this device's copy of scratch
+  int n_cu = 0;
+  uint32_t epoch = 0;       // flags in scratch hold earlier epochs of this device's calls
+};
+StaticDev g_static[kMaxDevices];
+std::mutex g_static_mu;
+
+}  // namespace
+
+extern "C" {
+
+int64_t sgt_gemm_rs_static_scratch_bytes(void) { return (int64_t)kScratchWords * 4; }
+
+sgt_status sgt_gemm_rs_static(const void* A_local, const void* B, const float* const* partials, float* partial_out,
+                              float* C_shard, int W, int64_t M, int64_t K, int64_t N, const sgt_opts* opts,
+                              void* stream_) {
+  RsArgs a;
+  int64_t ng = 0, np = 0;
+  sgt_status st = rs_plan(A_local, B, partials, nullptr, partial_out, C_shard, nullptr, nullptr, false, W, M, K, N,
+                          opts, &a, &ng, &np);
+  if (st != SGT_OK) return st;
+  const sgt_opts& o = *opts;
+  if (o.producer != SGT_PROD_PRESET && o.producer != SGT_PROD_CU)
+    return fail(SGT_EINVAL, "sgt_gemm_rs_static takes resident peers (producer CU or preset)");
+  if (o.trace) return fail(SGT_EUNSUPPORTED, "sgt_gemm_rs_static records no trace");
+  if (ng + np > kScratchFlagWords)
+    return fail(SGT_EINVAL, "%lld signal flags (%lld GEMM + %lld peer) exceed the %d words of static scratch",
+                (long long)(ng + np), (long long)ng, (long long)np, kScratchFlagWords);
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SGT_EUNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  StaticDev& sd = g_static[dev];
+  if (!sd.ptr) {
+    // once per device, with that device current: its copy of the array
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(SGT_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    int n_cu = 0;
+    HIP_TRY(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
+    sd.ptr = static_cast<uint32_t*>(p);
+    sd.n_cu = n_cu > 0 ? n_cu : 1;
+  }
+  if (M == 0 || N == 0) return SGT_OK;
+  uint32_t* flags = sd.ptr + kScratchHead;
+  if (++sd.epoch >= 0x40000000u) {
+    // before any flag could alias a later epoch: clear them (a fill kernel) and restart
+    HIP_TRY(launch_fill_u32(flags, kScratchFlagWords, 0u, stream));
+    sd.epoch = 1;
+  }
+  uint32_t* pflags = flags + ng;
+  a.gflags = flags;
+  a.pflags = pflags;
+  a.status = sd.ptr;
+  a.red_counter = sd.ptr + 4;
+  a.epoch = sd.epoch;
+  // the resident peers' flags take the epoch and the claim counter restarts (one fill kernel, no memset)
+  HIP_TRY(launch_rs_prepare(pflags, np, a.epoch, a.red_counter, stream));
+  const int grid = std::min(a.n_gemm_tiles + a.n_red_items,
+                            o.consumer_cus > 0 ? std::min(o.consumer_cus, sd.n_cu) : sd.n_cu);
+  if ((st = mark(o, 0, stream)) != SGT_OK) return st;
+  HIP_TRY(launch_gemm_rs(a, grid, stream));
+  if ((st = mark(o, 1, stream)) != SGT_OK) return st;
+  if (!o.blocking) return SGT_OK;
+  HIP_TRY(hipStreamSynchronize(stream));
+  uint32_t s4[4] = {0, 0, 0, 0};
+  HIP_TRY(hipMemcpy(s4, sd.ptr, sizeof s4, hipMemcpyDeviceToHost));
+  if (s4[0] == kStatusTimeout) {
+    static const uint32_t zero4[4] = {0, 0, 0, 0};
+    HIP_TRY(hipMemcpy(sd.ptr, zero4, sizeof zero4, hipMemcpyHostToDevice));
+    return fail(SGT_ETIMEDOUT, "wait on flag %u timed out: saw %u, expected %u", s4[1], s4[2], s4[3]);
+  }
+  return SGT_OK;
+}
+
 static int moe_tile_rows(const sgt_opts& o) { return o.tile_rows > 0 ? o.tile_rows : 256; }
 
 // Upper bound of the grouped row tiles of a routing: sum over experts of
