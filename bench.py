@@ -250,12 +250,13 @@ def cpu_baseline(shards, B, M, N, K, seconds: float, b_layout: str = "kn"):
             "seconds": dt}
 
 
-def release_times(ctx, call, trace_words, n_tiles, torch, n=3):
+def release_times(ctx, call, trace_words, n_tiles, torch, n=3, local_flags=0):
     """The last signal tile's release, in microseconds from the call's first in-kernel stamp (a consumer
-    tile's wait start or a release, whichever is earlier), median over n traced calls.  The trace holds
-    4 words per consumer tile, then one release stamp per signal tile (100 MHz clock)."""
+    tile's wait start or a release, whichever is earlier), median over n traced calls; also the first
+    release of a remote signal tile (flags from local_flags on: rank 0's shard holds the first ones).  The
+    trace holds 4 words per consumer tile, then one release stamp per signal tile (100 MHz clock)."""
     import numpy as np
-    last, span = [], []
+    last, span, first = [], [], []
     tr = torch.zeros(trace_words, dtype=torch.int64, device="cuda:0")
     for i in range(n):
         tr.zero_()
@@ -268,8 +269,36 @@ def release_times(ctx, call, trace_words, n_tiles, torch, n=3):
         t0 = min(tiles[:, 0].min(), rel.min())
         last.append((rel.max() - t0) / 100.0)
         span.append((tiles[:, 2].max() - t0) / 100.0)
+        first.append((rel[local_flags:].min() - t0) / 100.0)
     del tr
-    return {"last_release_us": statistics.median(last), "consumer_end_us": statistics.median(span), "n": n}
+    return {"last_release_us": statistics.median(last), "first_remote_release_us": statistics.median(first),
+            "consumer_end_us": statistics.median(span), "n": n}
+
+
+def bench_engines(ctx, shards, B, Ag, C, flags, rank, lay, kc, link, alone_ms, flops, shape, args, torch, sgt):
+    """The headline's overlapped step with the copy-engine producer (SGT_PROD_SDMA): every remote peer through
+    the copy engines, and hybrids where the first sdma_peers peers go through the copy engines and the others
+    through CU producer workgroups; per variant the step time, its overlap efficiency against the GEMM alone,
+    the consumer kernel's time and when the first remote and the last signal tile were released."""
+    W, M, K, N = shape
+    engines = {}
+    for name, kw in (("engines_all_peers", dict(producer="sdma")),
+                     ("engines_2_peers_cu_5", dict(producer="sdma", sdma_peers=2)),
+                     ("engines_3_peers_cu_4", dict(producer="sdma", sdma_peers=3))):
+        e_ms, e_k, e_l = timed(lambda i, ev: ctx.ag_gemm(shards, B, Ag, C, flags, rank=rank, b_layout=lay,
+                                                         consumer_events=ev, k_chunks=kc, arrival_seed=5000 + i,
+                                                         **link, **kw), max(6, args.steps // 2), 3, torch, ctx)
+        e_rel = release_times(ctx, lambda i, tr: ctx.ag_gemm(shards, B, Ag, C, flags, rank=rank, b_layout=lay,
+                                                              k_chunks=kc, arrival_seed=6000 + i, trace=tr,
+                                                              **link, **kw),
+                              sgt.trace_words(W, M, K, N, k_chunks=kc), (M // 256) * (-(-N // 256)), torch,
+                              local_flags=sgt.ag_flag_count(W, M, K, k_chunks=kc) // W)
+        engines[name] = {"step_ms": e_ms, "tflops_step": flops / (e_ms * 1e-3) / 1e12,
+                         "overlap_efficiency_step": alone_ms / e_ms, "consumer_kernel_ms": spread(e_l),
+                         "first_remote_release_us": e_rel["first_remote_release_us"],
+                         "last_release_us": e_rel["last_release_us"], "consumer_end_us": e_rel["consumer_end_us"]}
+    assert torch.equal(Ag.view(torch.int16), torch.cat(shards).view(torch.int16)), "gathered buffer (copy engines)"
+    return engines
 
 
 def bench_ag_other(ctx, up, args, torch, sgt, I, lay):
@@ -398,7 +427,7 @@ def bench_ll(ctx, up, args, torch, sgt, I):
     return out
 
 
-def bench_ring(ctx, up, args, torch, sgt, I):
+def bench_ring(ctx, up, args, torch, sgt, I, resident_only=False):
     """One rank's share of the signal-gated ring AllReduce: 2048 x 8192 fp32 per rank, W = 8, the left
     neighbour's link at 153.6 GB/s.
 
@@ -431,6 +460,8 @@ def bench_ring(ctx, up, args, torch, sgt, I):
     k = spread(kern)
     res["resident"] = {"step_ms": step, "kernel_ms": k, "hbm_gbps": alg / (k["median"] * 1e-3) / 1e9,
                        "hbm_frac": alg / (k["median"] * 1e-3) / 8e12, "algorithmic_mb": alg / 1e6}
+    if resident_only:
+        return res
     floor_us = 2 * (W - 1) * C * 4 / (w.peer_gbps * 1e3)
     for name, kw in (("overlapped_153.6GBps", dict(peer_gbps=w.peer_gbps)),
                      ("serial_153.6GBps", dict(peer_gbps=w.peer_gbps)),
@@ -618,7 +649,9 @@ def bench_moe(ctx, up, args, torch, sgt, I, lay):
     flops = m.flops
     hbm = m.E * m.H * m.I * 2 + m.T * m.H * 2 + m.T * m.topk * m.I * 4   # weights + tokens once + Y (fp32)
     groups = np.diff(off_h)
-    used_rows = int(np.sum(-(-groups // 256)) * 256)
+    # rows the matrix cores compute: 256-row tiles, the last tile of a group 128 rows when at most 128 are left
+    rem = groups % 256
+    used_rows = int(np.sum(groups // 256) * 256 + np.sum(np.where(rem == 0, 0, np.where(rem <= 128, 128, 256))))
     out = {
         "workload": m.name, "T": m.T, "H": m.H, "I": m.I, "E": m.E, "topk": m.topk, "W": m.W,
         "peer_gbps": m.peer_gbps, "gflop": flops / 1e9, "algorithmic_hbm_bytes": hbm,
@@ -642,7 +675,7 @@ def bench_moe(ctx, up, args, torch, sgt, I, lay):
     return out, (off, rt, ids)
 
 
-def bench_moe_rs(ctx, up, args, torch, sgt, I, lay, tables):
+def bench_moe_rs(ctx, up, args, torch, sgt, I, lay, tables, resident_only=False):
     """MoE GEMM + ReduceScatter (combine side) of the same layer: T 4096 tokens, top-8 of 64 experts, I 768 ->
     H 2048, W 8; routing tables from the AllGather side's GPU routing; peers' partials resident."""
     import numpy as np
@@ -665,6 +698,8 @@ def bench_moe_rs(ctx, up, args, torch, sgt, I, lay, tables):
         ctx.moe_gemm_rs(Hg, W2, gate, ids, off, rt, parts, Y, P, Cs, gf, pf, rank=rank, b_layout=lay,
                         consumer_events=ev)
     step_ms, kern_ms, kern = timed(fn, args.steps, args.warmup, torch, ctx)
+    if resident_only:
+        return {"step_ms": step_ms, "kernel_ms": spread(kern)}
     # the peers' partials arriving at 50 GB/s per link into an inbox
     gbps = 50.0
     inbox = [torch.empty_like(p) if p is not None else None for p in parts]
@@ -710,6 +745,55 @@ def bench_moe_rs(ctx, up, args, torch, sgt, I, lay, tables):
     }
 
 
+def kernel_pass(name, ctx, up, args, torch, sgt, I, lay):
+    """One workload's kernels with resident data and preset flags only, for counter passes (a counter run
+    serializes kernels, so a call whose consumer waits on a producer on another stream cannot run under it).
+    Prints the per-call kernel times."""
+    dev = "cuda:0"
+    res = {"kernel_pass": name}
+    if name in ("moe", "moe_rs", "a2a"):
+        m = I.MOE
+        sh_h, We_h, lg_h = I.make_moe(m, W_layout=lay)
+        sh = [up(x) for x in sh_h]
+        We, lg = up(We_h), up(lg_h)
+        Xg = torch.cat(sh)
+        Y = torch.empty((m.T * m.topk, m.I), dtype=torch.float32, device=dev)
+        off = torch.empty(m.E + 1, dtype=torch.int32, device=dev)
+        rt = torch.empty(m.T * m.topk, dtype=torch.int32, device=dev)
+        ids = torch.empty((m.T, m.topk), dtype=torch.int32, device=dev)
+        fl = torch.zeros(sgt.ag_flag_count(m.W, m.T, m.H), dtype=torch.int32, device=dev)
+
+        def moe(i, ev):
+            ctx.moe_ag_gemm(sh, We, lg, Xg, Y, off, rt, ids, fl, topk=m.topk, b_layout=lay, producer="preset",
+                            consumer_events=ev)
+        step, _, kern = timed(moe, args.steps, args.warmup, torch, ctx)
+        res["moe_ag_grouped_preset"] = {"step_ms": step, "consumer_kernel_ms": spread(kern)}
+        tables = (off, rt, ids)
+        if name == "moe_rs":
+            res["moe_gemm_rs"] = bench_moe_rs(ctx, up, args, torch, sgt, I, lay, tables, resident_only=True)
+        if name == "a2a":
+            # every AllToAll call is one stream's work (its senders run in the same launch or before it)
+            res["a2a"] = bench_a2a(ctx, up, args, torch, sgt, I, tables)
+    elif name == "gemm_rs":
+        r = I.GEMM_RS
+        A_h, B_h, parts_h = I.make_rs(r, B_layout=lay)
+        A, B = up(A_h), up(B_h)
+        parts = [up(p) if q != 0 else None for q, p in enumerate(parts_h)]
+        ng, npf = sgt.rs_flag_count(r.W, r.M, r.N)
+        P = torch.empty((r.M, r.N), dtype=torch.float32, device=dev)
+        Cs = torch.empty((r.M // r.W, r.N), dtype=torch.float32, device=dev)
+        gf = torch.zeros(ng, dtype=torch.int32, device=dev)
+        pf = torch.zeros(npf, dtype=torch.int32, device=dev)
+        step, _, kern = timed(lambda i, ev: ctx.gemm_rs(A, B, parts, P, Cs, gf, pf, rank=0, b_layout=lay,
+                                                        consumer_events=ev), args.steps, args.warmup, torch, ctx)
+        res["gemm_rs"] = {"step_ms": step, "kernel_ms": spread(kern)}
+    elif name == "ring":
+        res["ring"] = bench_ring(ctx, up, args, torch, sgt, I, resident_only=True)
+    else:
+        raise SystemExit("unknown kernel pass %r" % name)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -733,6 +817,11 @@ def main():
                     help="only the headline's consumer kernel on resident data with flags preset, on the grid the "
                          "overlapped call gives it (for counter passes, which serialize kernels and so cannot "
                          "run the overlapped call)")
+    ap.add_argument("--kernel-pass", default=None, choices=["moe", "moe_rs", "gemm_rs", "ring", "a2a"],
+                    help="only one workload's kernels with resident data and preset flags (for counter passes)")
+    ap.add_argument("--moe-only", action="store_true", help="only the MoE AllGather and combine workloads")
+    ap.add_argument("--engines-only", action="store_true",
+                    help="only the headline's overlapped step with the CU producer and the copy-engine variants")
     ap.add_argument("--headline-only", action="store_true",
                     help="only the overlapped steps (for a profiler run whose kernel list is exactly the timed one)")
     args = ap.parse_args()
@@ -761,6 +850,17 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
+    if args.kernel_pass:
+        with sgt.Context(0) as c:
+            kernel_pass(args.kernel_pass, c, up, args, torch, sgt, I, args.b_layout)
+        return
+    if args.moe_only:
+        with sgt.Context(0) as c:
+            moe, tables = bench_moe(c, up, args, torch, sgt, I, args.b_layout)
+            print(json.dumps({"moe_ag_grouped": moe}), flush=True)
+            print(json.dumps({"moe_gemm_rs": bench_moe_rs(c, up, args, torch, sgt, I, args.b_layout, tables)}),
+                  flush=True)
+        return
     if args.a2a_only:
         with sgt.Context(0) as c:
             print(json.dumps({"a2a": bench_a2a(c, up, args, torch, sgt, I, moe_routing(c, up, torch, sgt, I))}),
@@ -813,6 +913,21 @@ def main():
                           "tflops": flops / (over_ms * 1e-3) / 1e12}), flush=True)
         ctx.close()
         return
+    if args.engines_only:
+        n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+        a_ms, _, _ = timed(ag("preset", consumer_cus=n_cu - max(8, n_cu // 8)), args.steps, args.warmup, torch, ctx)
+        rel = release_times(ctx, lambda i, tr: ctx.ag_gemm(shards, B, Ag, C, flags, rank=rank, b_layout=lay,
+                                                           producer="cu", k_chunks=kc, arrival_seed=7000 + i,
+                                                           trace=tr, **link),
+                            sgt.trace_words(W, M, K, N, k_chunks=kc), (M // 256) * (-(-N // 256)), torch,
+                            local_flags=sgt.ag_flag_count(W, M, K, k_chunks=kc) // W)
+        out = {"cu_producer": {"step_ms": over_ms, "overlap_efficiency_step": a_ms / over_ms, **rel},
+               "gemm_alone_ms": a_ms}
+        out.update(bench_engines(ctx, shards, B, Ag, C, flags, rank, lay, kc, link, a_ms, flops, (W, M, K, N), args,
+                                 torch, sgt))
+        print(json.dumps(out), flush=True)
+        ctx.close()
+        return
     # the same consumer with data resident and flags preset, on all CUs and on the grid the overlapped
     # run leaves it (all CUs but the producer's); the better of the two is "the GEMM alone"
     alone_all = timed(ag("preset"), args.steps, args.warmup, torch, ctx)
@@ -842,7 +957,8 @@ def main():
     rel = release_times(ctx, lambda i, tr: ctx.ag_gemm(shards, B, Ag, C, flags, rank=rank, b_layout=lay,
                                                        producer="cu", k_chunks=kc, arrival_seed=7000 + i,
                                                        trace=tr, **link),
-                        sgt.trace_words(W, M, K, N, k_chunks=kc), (M // 256) * (-(-N // 256)), torch)
+                        sgt.trace_words(W, M, K, N, k_chunks=kc), (M // 256) * (-(-N // 256)), torch,
+                        local_flags=sgt.ag_flag_count(W, M, K, k_chunks=kc) // W)
 
     shard_bytes = (M // W) * K * 2
     link_floor_us = shard_bytes / (w.peer_gbps * 1e9) * 1e6
@@ -872,6 +988,8 @@ def main():
                       "tflops_median": flops / (statistics.median(o_l) * 1e-3) / 1e12,
                       "overlap_efficiency": statistics.median(a_l) / statistics.median(o_l),
                       "overlap_efficiency_max": e_max(floor)})
+    engines = bench_engines(ctx, shards, B, Ag, C, flags, rank, lay, kc, link, alone_ms, flops, (W, M, K, N), args,
+                            torch, sgt)
     # MALL-flushed (a 512 MiB scrub buffer written before each call) against warm back-to-back calls
     scrub = torch.empty(1 << 27, dtype=torch.float32, device=dev)
     fl_n = max(4, args.steps // 2)
@@ -922,6 +1040,11 @@ def main():
         "jitter_us": w.jitter_us,
         "pct_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "arrival_sweep": sweep,
+        "copy_engine_producer": engines,
+        "copy_engine_note": "SGT_PROD_SDMA: copy-engine copies of whole 256-row panels gated on the call's stream "
+                            "position, a releaser workgroup publishing each K chunk's flag once its panel has "
+                            "landed and its link time has come; the CU producer's last release is in "
+                            "release_trace",
         "mall_flushed_call_ms": spread(cold),
         "mall_flushed_alone_call_ms": spread(cold_alone),
         "mall_flushed_tflops_median": flops / (statistics.median(cold) * 1e-3) / 1e12,

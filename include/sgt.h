@@ -78,8 +78,16 @@ enum sgt_producer {
   SGT_PROD_CU = 0,      /* producer kernel on a second stream, paced per peer        */
   SGT_PROD_PRESET = 1,  /* data already resident: flags are set up front, then the
                            consumer runs (the "GEMM alone" baseline)                */
-  SGT_PROD_SERIAL = 2   /* producer, then consumer, on one stream (debug: barrier
+  SGT_PROD_SERIAL = 2,  /* producer, then consumer, on one stream (debug: barrier
                            semantics instead of fine-grained signals)               */
+  SGT_PROD_SDMA = 3     /* sgt_ag_gemm: the copy engines move the data, off the
+                           compute units (paper summary, "Method": intra-node
+                           AllGather by copy engines, communication and compute on
+                           separate resources); a one-workgroup releaser publishes
+                           each flag once its copy has landed and its link time has
+                           come.  opts->sdma_peers > 0 sends only that many remote
+                           peers (rank+1, rank+2, ...) through the copy engines and
+                           the others through producer_cus CU workgroups           */
 };
 
 /* Consumer order over the row panels of the gathered matrix. */
@@ -119,6 +127,7 @@ typedef struct sgt_opts {
                             signal tiles of one 256-row consumer panel x one of n equal column
                             chunks of K (K a multiple of 128 n), so a tile whose panel is still
                             arriving computes it chunk by chunk (same bits)                      */
+  int32_t sdma_peers;    /* SGT_PROD_SDMA: remote peers moved by the copy engines; 0 = all      */
   uint64_t* trace;       /* optional device buffer, see sgt_trace_words(); NULL = off           */
   void* consumer_events[2]; /* optional hipEvent_t pair recorded on the consumer's stream right
                                before and after the consumer kernel launch (NULL = off)            */

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libsgt.so")
 SGT_OK, SGT_EINVAL, SGT_EUNSUPPORTED, SGT_ETIMEDOUT, SGT_EHIP, SGT_ENOMEM = 0, -1, -2, -3, -4, -5
 SGT_F32, SGT_BF16 = 0, 1
 SGT_KN, SGT_NK = 0, 1
-PRODUCERS = {"cu": 0, "preset": 1, "serial": 2}
+PRODUCERS = {"cu": 0, "preset": 1, "serial": 2, "sdma": 3}
 ORDERS = {"mesh": 0, "shard": 1}
 LAYOUTS = {"kn": SGT_KN, "nk": SGT_NK}
 ARRIVALS = {"inorder": 0, "per_peer": 1, "global": 2}
@@ -43,7 +43,7 @@ class Opts(ctypes.Structure):
         ("blocking", ctypes.c_int32), ("peer_gbps", ctypes.c_double), ("jitter_us", ctypes.c_double),
         ("timeout_ms", ctypes.c_double), ("arrival_seed", ctypes.c_uint64), ("withhold_peer", ctypes.c_int32),
         ("rs_tile", ctypes.c_int32), ("arrival_order", ctypes.c_int32), ("tile_waves", ctypes.c_int32),
-        ("tile_rows", ctypes.c_int32), ("k_chunks", ctypes.c_int32),
+        ("tile_rows", ctypes.c_int32), ("k_chunks", ctypes.c_int32), ("sdma_peers", ctypes.c_int32),
         ("trace", ctypes.c_void_p), ("consumer_events", ctypes.c_void_p * 2),
     ]
 
@@ -131,7 +131,7 @@ def make_opts(rank: int = 0, in_dtype: int = SGT_BF16, out_dtype: int = SGT_F32,
               consumer_cus: int = 0, blocking: bool = False, peer_gbps: float = 0.0, jitter_us: float = 0.0,
               timeout_ms: float = 2000.0, arrival_seed: int = 0, withhold_peer: int = -1, rs_tile: int = 0,
               trace: int = 0, consumer_events=None, arrival_order: str = "inorder", tile_waves: int = 0,
-              tile_rows: int = 0, k_chunks: int = 0) -> Opts:
+              tile_rows: int = 0, k_chunks: int = 0, sdma_peers: int = 0) -> Opts:
     o = Opts()
     lib().sgt_opts_init(ctypes.byref(o))
     o.rank, o.in_dtype, o.out_dtype = rank, in_dtype, out_dtype
@@ -148,6 +148,7 @@ def make_opts(rank: int = 0, in_dtype: int = SGT_BF16, out_dtype: int = SGT_F32,
     o.tile_waves = tile_waves
     o.tile_rows = tile_rows
     o.k_chunks = k_chunks
+    o.sdma_peers = sdma_peers
     o.trace = trace or None
     if consumer_events is not None:
         o.consumer_events[0] = _event_handle(consumer_events[0])

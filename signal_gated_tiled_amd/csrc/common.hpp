@@ -30,6 +30,18 @@ struct ProdItem {
   uint16_t peer;
 };
 
+// One release of the copy-engine producer: once the copy engine has written
+// the bytes of copy unit `mark` (marks[mark] holds the call's epoch), and no
+// earlier than `release` ticks after the releaser started, flags [flag0,
+// flag0 + nflags) take the epoch.  Items are in release order.
+struct RelItem {
+  uint64_t release;
+  uint32_t flag0;
+  uint32_t nflags;
+  uint32_t mark;
+  uint32_t peer;
+};
+
 // Arguments of the AllGather consumer (both the bf16 MFMA and fp32 kernels).
 struct AgArgs {
   const void* A;          // gathered M x K
@@ -107,6 +119,38 @@ struct MoeRsArgs {
   RsArgs rs;
 };
 
+// XCD-partitioned work lists of the MoE grouped consumer.  The row tiles,
+// sorted by readiness, are cut into chunks of kMoeXcdGroup consecutive tiles;
+// chunk c goes to the list of XCD c % kXcds (the XCD that runs workgroups
+// b with b % kXcds == c % kXcds), in order.  So every XCD gets an even share of
+// each readiness window, and the tiles it runs together (the column tiles of
+// one row tile, neighbouring row tiles of one expert) share operands in its L2.
+constexpr int kXcds = 8;
+constexpr int kXcdClaimStride = 16;  // words between the per-XCD claim counters
+constexpr uint32_t kMoeXcdGroup = 4;
+
+// Row tiles in XCD x's list, for n tiles in total.
+__host__ __device__ inline uint32_t xcd_list_len(uint32_t n, int x) {
+  const uint32_t G = kMoeXcdGroup, nf = n / G, r = n % G;
+  uint32_t len = G * (nf / kXcds + ((uint32_t)x < nf % kXcds ? 1u : 0u));
+  if (r && nf % kXcds == (uint32_t)x) len += r;
+  return len;
+}
+
+// First entry of XCD x's list.
+__host__ __device__ inline uint32_t xcd_list_start(uint32_t n, int x) {
+  uint32_t s = 0;
+  for (int y = 0; y < x; ++y) s += xcd_list_len(n, y);
+  return s;
+}
+
+// Entry of the partitioned list that holds the row tile at sorted position p.
+__host__ __device__ inline uint32_t xcd_list_pos(uint32_t p, uint32_t n) {
+  const uint32_t G = kMoeXcdGroup, c = p / G;
+  const int x = (int)(c % kXcds);
+  return xcd_list_start(n, x) + (c / kXcds) * G + p % G;
+}
+
 // Routing and work-list tables of one MoE call (device memory owned by the context).
 struct MoeTables {
   uint32_t* masks;        // ceil(E / 32) x T: bit e % 32 of word e / 32 set when token t chose e
@@ -117,11 +161,12 @@ struct MoeTables {
   uint32_t* n_tiles;      // 1: number of grouped row tiles
   uint32_t tiles_cap;     // entries of tiles / keys / order
   uint32_t* claim;        // 1: next consumer work item to claim
+  uint32_t* xcd_claim;    // kXcds counters, kXcdClaimStride words apart: next item of each XCD's list
   uint32_t* done;         // 1: placement workgroups finished (cleared by the top-k kernel)
   uint32_t* ranks;        // arrival rank of each signal tile, device copy (written by the top-k kernel)
   MoeTile* tiles;         // grouped row tiles, expert-major (written by the placement kernel)
   uint32_t* keys;         // readiness key per entry of `tiles`
-  MoeTile* order;         // the same tiles sorted by key (the consumer's work order)
+  MoeTile* order;         // the same tiles sorted by key, in the XCD-partitioned lists (xcd_list_pos)
 };
 
 // Arguments of the MoE grouped consumer.
@@ -134,7 +179,8 @@ struct MoeArgs {
   const MoeTile* order;
   const uint32_t* n_tiles;
   uint32_t tiles_cap;         // entries of `order`
-  uint32_t* claim;
+  uint32_t* claim;            // (unused by the consumer: it claims from xcd_claim)
+  uint32_t* xcd_claim;        // per-XCD claim counters (MoeTables::xcd_claim)
   const uint32_t* flags;      // one per signal tile of X
   uint32_t* status;
   uint64_t* trace;            // optional: 4 words per work item in claim order

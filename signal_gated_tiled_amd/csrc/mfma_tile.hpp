@@ -327,14 +327,15 @@ __device__ __forceinline__ void mfma_stage(const uint8_t* sA, const uint8_t* sB,
 // K, keeps the step sequence of one whole-K call, so the accumulation order,
 // and the bits, are the same however K is cut).  Operand loads stop at k_end:
 // columns of A past it are neither read nor needed.
-template <int kW, bool kBNK, int kR = kBM>
-__device__ __forceinline__ void gemm_tile_range(const KRows& ka, const KRows& kb_nk, const uint16_t* B_kn, int64_t N,
-                                                int64_t n0, int64_t K, int64_t k_begin, int64_t k_end,
-                                                MfmaAcc<kW, kR>& acc) {
-  __shared__ __attribute__((aligned(1024))) uint8_t sA0[kR * kBK * 2];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t sA1[kR * kBK * 2];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB1[kStageBytes];
+// The stages are LDS arrays of the caller (sA* at least kR x kBK bf16, sB*
+// kStageBytes): a kernel that runs tiles of two heights passes the same four
+// arrays to both, so they share one allocation.  Everything here is inlined,
+// so the compiler still sees four distinct objects.
+template <int kW, bool kBNK, int kR>
+__device__ __forceinline__ void gemm_tile_range_lds(const KRows& ka, const KRows& kb_nk, const uint16_t* B_kn,
+                                                    int64_t N, int64_t n0, int64_t K, int64_t k_begin, int64_t k_end,
+                                                    MfmaAcc<kW, kR>& acc, uint8_t* sA0, uint8_t* sB0, uint8_t* sA1,
+                                                    uint8_t* sB1) {
   const int64_t nk2 = ((k_end - k_begin + kBK - 1) / kBK + 1) & ~int64_t(1);
   KNLoader<kW> kn;
   if constexpr (!kBNK) {
@@ -361,6 +362,17 @@ __device__ __forceinline__ void gemm_tile_range(const KRows& ka, const KRows& kb
     wait_dma();
     __syncthreads();
   }
+}
+
+template <int kW, bool kBNK, int kR = kBM>
+__device__ __forceinline__ void gemm_tile_range(const KRows& ka, const KRows& kb_nk, const uint16_t* B_kn, int64_t N,
+                                                int64_t n0, int64_t K, int64_t k_begin, int64_t k_end,
+                                                MfmaAcc<kW, kR>& acc) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[kR * kBK * 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[kR * kBK * 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[kStageBytes];
+  gemm_tile_range_lds<kW, kBNK, kR>(ka, kb_nk, B_kn, N, n0, K, k_begin, k_end, acc, sA0, sB0, sA1, sB1);
 }
 
 template <int kW, bool kBNK, int kR = kBM>

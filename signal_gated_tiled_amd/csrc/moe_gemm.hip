@@ -5,10 +5,13 @@
 //
 // Work item = (grouped row tile, column tile): rows [r0, r0 + kR) of one
 // expert's group (clipped to the group; kR = 128 or 256) times 256 columns of that expert's
-// weight.  Persistent workgroups claim items from the readiness-ordered list
-// with an atomic counter.  Before loading, wave 0 polls, lane by lane, the
-// flag of the signal tile that holds each row's token (a tile waits for
-// exactly the tokens it reads); then the rows are gathered straight into LDS
+// weight.  Persistent workgroups claim items from their XCD's share of the
+// readiness-ordered list with an atomic counter per XCD (the column tiles of a
+// row tile are consecutive items, so they run side by side on one XCD and
+// read the gathered rows from its L2), then help the other XCDs.  Before
+// loading, wave 0 polls, lane by lane, the flag of the signal tile that holds
+// each row's token (a tile waits for exactly the tokens it reads); then the
+// rows are gathered straight into LDS
 // (the DMA takes one row offset per load) and the MFMA tile core computes
 // Y[r0 .., n0 ..] = X[row_token[r0 ..]] * W_e[:, n0 ..].
 #include <hip/hip_runtime.h>
@@ -69,8 +72,40 @@ __device__ __forceinline__ bool wait_tile_rows(const MoeArgs& a, const int32_t* 
   return *ok != 0;
 }
 
+// One tile of rows [r0, r0 + rows_valid) of expert e's group (rows_valid <= kR)
+// times 256 columns of W_e, on the workgroup's LDS stages.
 template <int kW, int kR, bool kBNK, bool kOutBf16>
+__device__ __forceinline__ void moe_tile(const MoeArgs& a, const int32_t* tok, int rows_valid, int e, int64_t r0,
+                                         int64_t n0, uint8_t* sA0, uint8_t* sB0, uint8_t* sA1, uint8_t* sB1) {
+  // A: gathered rows of X (row offsets < T * H * 2 < 2^31).
+  KRows ka;
+  ka.rsrc = make_rsrc(a.X, (uint64_t)a.T * (uint64_t)a.H * 2u);
+#pragma unroll
+  for (int i = 0; i < kR / kW / 8; ++i) {
+    const int r = dma_row<kW, kR>(i);
+    ka.row_off[i] = r < rows_valid ? (uint32_t)((int64_t)tok[r] * a.H * 2) : kOOB;
+  }
+  krows_chunks<kW, kR>(ka);
+  // B: expert e's weight, H x I (KN) or I x H (NK).
+  const uint16_t* Be = a.We + (int64_t)e * a.H * a.I;
+  KRows kb = ka;
+  if constexpr (kBNK) kb = krows_strided<kW>(Be + n0 * a.H, a.I - n0, a.H);
+  MfmaAcc<kW, kR> acc;
+  acc_zero<kW, kR>(acc);
+  gemm_tile_range_lds<kW, kBNK, kR>(ka, kb, Be, a.I, n0, a.H, 0, a.H, acc, sA0, sB0, sA1, sB1);
+  store_tile<kW, kOutBf16, 0, kR>(a.Y, r0 + rows_valid, a.I, r0, n0, acc);
+}
+
+// kRmax = 256: a row tile of more than 128 valid rows runs as a 256-row tile,
+// a shorter one (the tail of a group) as a 128-row tile, so short groups do
+// not pay for 256 rows; kRmax = 128: every tile is 128 rows.  Both tile
+// heights share the workgroup's four LDS stages.
+template <int kW, int kRmax, bool kBNK, bool kOutBf16>
 __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) moe_consumer_bf16(MoeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[kBM * kBK * 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[kBM * kBK * 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[kStageBytes];
   __shared__ int item_s, ok;
   if (a.late_blocks > 0 && (int)blockIdx.x >= (int)gridDim.x - a.late_blocks) {
     // a workgroup that may sit on a CU the producer needs: run only if every
@@ -80,13 +115,29 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) moe_consumer_bf16(MoeAr
     __syncthreads();
     if (!ok) return;
   }
-  const uint32_t nt = *a.n_tiles;
-  const int64_t n_items = (int64_t)(nt < a.tiles_cap ? nt : a.tiles_cap) * a.tiles_n;
+  const uint32_t nt_raw = *a.n_tiles;
+  const uint32_t nt = nt_raw < a.tiles_cap ? nt_raw : a.tiles_cap;
+  // Work items come from the list of this workgroup's XCD (workgroup b runs on
+  // XCD b % kXcds), then, once it is used up, from the other XCDs' lists in turn.
+  int x = (int)(blockIdx.x % kXcds), lists_left = kXcds;
   while (true) {
-    if (threadIdx.x == 0) item_s = (int)atomicAdd(a.claim, 1u);
+    if (threadIdx.x == 0) {
+      int item = -1;
+      while (lists_left > 0) {
+        const uint32_t len = xcd_list_len(nt, x) * (uint32_t)a.tiles_n;
+        const uint32_t c = len ? atomicAdd(a.xcd_claim + x * kXcdClaimStride, 1u) : len;
+        if (c < len) {
+          item = (int)(xcd_list_start(nt, x) * (uint32_t)a.tiles_n + c);
+          break;
+        }
+        x = (x + 1) % kXcds;
+        --lists_left;
+      }
+      item_s = item;
+    }
     __syncthreads();
     const int64_t item = item_s;
-    if (item >= n_items) break;
+    if (item < 0) break;
     const MoeTile mt = a.order[item / a.tiles_n];
     const int64_t n0 = (item % a.tiles_n) * kBN;
     const int e = mt.expert;
@@ -97,33 +148,20 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) moe_consumer_bf16(MoeAr
       __syncthreads();
       continue;
     }
-    const int rows_valid = (int)(r_end - r0 < kR ? r_end - r0 : kR);
+    const int rows_valid = (int)(r_end - r0 < kRmax ? r_end - r0 : kRmax);
     const int32_t* tok = a.row_token + r0;
     uint64_t t_wait = 0;
     if (a.trace && threadIdx.x == 0) t_wait = clock_ticks();
-    if (!wait_tile_rows<kR>(a, tok, rows_valid, &ok)) return;
+    if (!wait_tile_rows<kRmax>(a, tok, rows_valid, &ok)) return;
     if (a.trace && threadIdx.x == 0) {
       a.trace[item * 4 + 0] = t_wait;
       a.trace[item * 4 + 1] = clock_ticks();
       a.trace[item * 4 + 3] = blockIdx.x;
     }
-
-    // A: gathered rows of X (row offsets < T * H * 2 < 2^31).
-    KRows ka;
-    ka.rsrc = make_rsrc(a.X, (uint64_t)a.T * (uint64_t)a.H * 2u);
-#pragma unroll
-    for (int i = 0; i < kR / kW / 8; ++i) {
-      const int r = dma_row<kW, kR>(i);
-      ka.row_off[i] = r < rows_valid ? (uint32_t)((int64_t)tok[r] * a.H * 2) : kOOB;
-    }
-    krows_chunks<kW, kR>(ka);
-    // B: expert e's weight, H x I (KN) or I x H (NK).
-    const uint16_t* Be = a.We + (int64_t)e * a.H * a.I;
-    KRows kb = ka;
-    if constexpr (kBNK) kb = krows_strided<kW>(Be + n0 * a.H, a.I - n0, a.H);
-    MfmaAcc<kW, kR> acc;
-    gemm_tile<kW, kBNK, kR>(ka, kb, Be, a.I, n0, a.H, acc);
-    store_tile<kW, kOutBf16, 0, kR>(a.Y, r0 + rows_valid, a.I, r0, n0, acc);
+    if (kRmax == 256 && rows_valid > 128)
+      moe_tile<kW, kRmax, kBNK, kOutBf16>(a, tok, rows_valid, e, r0, n0, sA0, sB0, sA1, sB1);
+    else
+      moe_tile<kW, 128, kBNK, kOutBf16>(a, tok, rows_valid, e, r0, n0, sA0, sB0, sA1, sB1);
     if (a.trace && threadIdx.x == 0) a.trace[item * 4 + 2] = clock_ticks();
   }
 }

@@ -20,7 +20,8 @@
 //     is the latest arrival rank among the signal tiles its rows come from.
 //  3. the last placement workgroup to finish sorts the row tiles by readiness
 //     key (stable counting sort), so the consumer claims first the tiles whose
-//     rows land first.
+//     rows land first, and deals the sorted tiles out to per-XCD lists in
+//     chunks of a few consecutive tiles (xcd_list_pos).
 // No table depends on the order of concurrent updates: counts are integer
 // sums, positions are prefix sums over tokens.  The counts are double-buffered
 // by call parity: each call's top-k kernel clears the next call's buffer.
@@ -222,7 +223,7 @@ __device__ void sort_row_tiles(const MoeTables& tb, uint32_t n_keys, uint32_t* b
     if (i < n) {
       uint32_t rank = 0;
       for (int j = 0; j < tid; ++j) rank += chunk_b[j] == b;
-      tb.order[base[b] + rank] = tb.tiles[i];
+      tb.order[xcd_list_pos(base[b] + rank, n)] = tb.tiles[i];
     }
     __syncthreads();
     if (i < n) atomicAdd(&base[b], 1u);
@@ -266,6 +267,7 @@ __global__ void __launch_bounds__(256) moe_place_kernel(const uint32_t* __restri
       *tb.n_tiles = tiles_total;
       *tb.claim = 0u;
     }
+    if (tid < kXcds) tb.xcd_claim[tid * kXcdClaimStride] = 0u;
   }
   __syncthreads();
   const uint32_t n_e = my_count, base_row = my_row0, base_tile = my_tile0;

@@ -153,14 +153,55 @@ __device__ __forceinline__ void produce_items(int first, int stride, uint32_t* f
   }
 }
 
+// Releaser of the copy-engine producer (one thread): the copy engines move the
+// data on their own; a copy unit's mark word takes the call's epoch once its
+// bytes are written (a dependent 4-byte copy on the same engine, started
+// after the data copy has completed).  For each item, in release order: wait
+// until its unit's mark holds the epoch (system-scope loads: the mark is
+// written by the copy engine, not through this XCD's L2), then until its
+// release time, then publish its flags.  Every wait is bounded.
+__device__ void release_items(uint32_t* flags, const RelItem* __restrict__ rel, int n_rel,
+                              const uint32_t* marks, uint32_t epoch, int withhold_peer, uint64_t* trace_release,
+                              uint64_t timeout_ticks, uint32_t* status) {
+  if (threadIdx.x != 0) return;
+  const uint64_t t0 = clock_ticks();
+  for (int i = 0; i < n_rel; ++i) {
+    const RelItem r = rel[i];
+    uint32_t v = __hip_atomic_load(marks + r.mark, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    while (!flag_is_set(v, epoch)) {
+      if (clock_ticks() - t0 > timeout_ticks) {
+        report_timeout(status, r.flag0, v, epoch);
+        return;
+      }
+      __builtin_amdgcn_s_sleep(2);
+      v = __hip_atomic_load(marks + r.mark, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    // pace: the link delivers the item at t0 + release (a finite schedule, so this ends)
+    while (clock_ticks() < t0 + r.release) __builtin_amdgcn_s_sleep(4);
+    if ((int)r.peer != withhold_peer)
+      for (uint32_t f = 0; f < r.nflags; ++f) flag_publish_coherent(flags + r.flag0 + f, epoch);
+    if (trace_release) trace_release[r.flag0] = clock_ticks();
+  }
+}
+
+// Workgroups [0, gridDim - (n_rel > 0)) copy items (CU producer); with
+// copy-engine items (n_rel > 0) the last workgroup is their releaser.
 __global__ void __launch_bounds__(kProdThreads) ag_producer_kernel(uint32_t* flags,
                                                                    const ProdItem* __restrict__ items, int n_items,
                                                                    int64_t tile_bytes, uint32_t epoch,
                                                                    int withhold_peer, uint64_t* trace_release,
                                                                    uint64_t lead0, uint32_t* started,
                                                                    uint64_t* trace_issue, uint32_t seg_rows,
-                                                                   uint32_t seg_bytes, uint32_t row_stride) {
-  produce_items(blockIdx.x, gridDim.x, flags, items, n_items, tile_bytes, epoch, withhold_peer, trace_release, lead0,
+                                                                   uint32_t seg_bytes, uint32_t row_stride,
+                                                                   const RelItem* __restrict__ rel, int n_rel,
+                                                                   const uint32_t* marks, uint64_t timeout_ticks,
+                                                                   uint32_t* status) {
+  const int pwg = (int)gridDim.x - (n_rel > 0 ? 1 : 0);
+  if ((int)blockIdx.x >= pwg) {
+    release_items(flags, rel, n_rel, marks, epoch, withhold_peer, trace_release, timeout_ticks, status);
+    return;
+  }
+  produce_items(blockIdx.x, pwg, flags, items, n_items, tile_bytes, epoch, withhold_peer, trace_release, lead0,
                 started, trace_issue, seg_rows, seg_bytes, row_stride);
 }
 
@@ -220,14 +261,16 @@ hipError_t launch_rs_prepare(uint32_t* pflags, int64_t n, uint32_t v, uint32_t* 
 hipError_t launch_ag_producer(uint32_t* flags, const ProdItem* items, int n_items,
                               int64_t tile_bytes, uint32_t epoch, int withhold_peer, uint64_t* trace_release, int grid,
                               hipStream_t stream, uint32_t* started, uint64_t* trace_issue, uint32_t seg_rows,
-                              uint32_t seg_bytes, uint32_t row_stride) {
-  if (n_items <= 0) return hipSuccess;
-  if (grid > n_items) grid = n_items;
+                              uint32_t seg_bytes, uint32_t row_stride, const RelItem* rel, int n_rel,
+                              const uint32_t* marks, uint64_t timeout_ticks, uint32_t* status) {
+  if (n_items <= 0 && n_rel <= 0) return hipSuccess;
+  if (grid > n_items) grid = n_items > 0 ? n_items : 0;
+  if (n_rel > 0) grid += 1;  // the releaser
   // first estimate of a tile's copy time: at 16 GB/s per workgroup (100 MHz ticks)
   const uint64_t lead0 = (uint64_t)(tile_bytes / 160) + 100;
   hipLaunchKernelGGL(ag_producer_kernel, dim3(grid), dim3(kProdThreads), 0, stream, flags, items, n_items, tile_bytes,
                      epoch, withhold_peer, trace_release, lead0, started, trace_issue, seg_rows, seg_bytes,
-                     row_stride);
+                     row_stride, rel, n_rel, marks, timeout_ticks, status);
   return hipGetLastError();
 }
 

@@ -7,6 +7,8 @@
 //   ctx->prod        -- producer kernel; forked from and joined back into the
 //                       caller's stream with events, so calls stay ordered.
 #include <hip/hip_runtime.h>
+#include <hsa/hsa.h>
+#include <hsa/hsa_ext_amd.h>
 
 #include <algorithm>
 #include <cmath>
@@ -27,7 +29,9 @@ namespace sgt {
 hipError_t launch_ag_producer(uint32_t* flags, const ProdItem* items, int n_items,
                               int64_t tile_bytes, uint32_t epoch, int withhold_peer, uint64_t* trace_release, int grid,
                               hipStream_t stream, uint32_t* started = nullptr, uint64_t* trace_issue = nullptr,
-                              uint32_t seg_rows = 0, uint32_t seg_bytes = 0, uint32_t row_stride = 0);
+                              uint32_t seg_rows = 0, uint32_t seg_bytes = 0, uint32_t row_stride = 0,
+                              const RelItem* rel = nullptr, int n_rel = 0, const uint32_t* marks = nullptr,
+                              uint64_t timeout_ticks = 0, uint32_t* status = nullptr);
 hipError_t launch_ll_allgather(const ProdItem* items, int n_prod, int n_recv, int n_prod_blocks, int grid,
                                int64_t chunk_bytes, uint32_t epoch, int withhold_peer, uint64_t lead, int rank,
                                uint64_t timeout_ticks, uint32_t* status, uint64_t* trace, hipStream_t stream);
@@ -80,6 +84,8 @@ sgt_status fail(sgt_status st, const char* fmt, ...) {
   } while (0)
 
 constexpr int kSlots = 4;                 // producer schedule tables in flight
+constexpr int kSdmaMaxUnits = 4096;       // copy-engine copies per call
+constexpr int64_t kSdmaUnitBytes = 4 << 20;  // bytes per copy-engine copy (whole-row signal tiles grouped up to this)
 constexpr int64_t kItemsCap = 1 << 18;    // signal tiles per call
 constexpr double kTicksPerUs = 100.0;     // constant GPU clock: 100 MHz
 
@@ -97,7 +103,8 @@ struct sgt_ctx {
   ProdItem* d_items[kSlots] = {};
   uint32_t* h_ranks[kSlots] = {};  // arrival rank of each signal tile (MoE work ordering), pinned host
   uint32_t* d_ranks[kSlots] = {};  // the same memory as the GPU addresses it (read in place, no copy)
-  uint32_t* d_moe = nullptr;       // MoE: tile count, claim counter, done count, counts[2][256] by call parity
+  uint32_t* d_moe = nullptr;       // MoE: tile count, claim counter, done count, started count, per-XCD claim
+                                   // counters (words 64 + 16 x), counts[2][256] by call parity (words 256..767)
   int moe_parity = 0;
   uint32_t moe_prod_started = 0;   // producer workgroups launched by overlapped MoE calls (cumulative)
   MoeTile* d_moe_tiles = nullptr;  // MoE row tiles, expert-major and sorted; grow on demand
@@ -121,6 +128,29 @@ struct sgt_ctx {
   std::vector<ProdItem> slot_items[kSlots];  // what d_items[slot] holds since its last upload
   std::vector<ProdItem> build;               // host scratch for building a schedule (grows only)
   int slot = 0;
+  // Copy-engine producer (SGT_PROD_SDMA), set up on its first use: the HSA
+  // agent of this device and its copy engines, a mark word per copy unit
+  // (device memory, written by the engines), and per call slot a gate signal
+  // (opened by a host function when the caller's stream reaches the call), the
+  // epoch word the mark copies read (pinned host memory), the copies'
+  // completion signals and the releaser's item table.
+  bool sdma_ready = false;
+  hsa_agent_t sdma_agent{};
+  std::vector<uint32_t> sdma_engines;     // engine id bits (hsa_amd_sdma_engine_id_t)
+  uint32_t* d_marks = nullptr;            // kSdmaMaxUnits words
+  uint32_t* h_sdma_epoch = nullptr;       // kSlots words, pinned
+  hsa_signal_t sdma_gate[kSlots] = {};
+  std::vector<hsa_signal_t> sdma_sig[kSlots];  // 2 per unit: data copy, mark copy
+  int sdma_used[kSlots] = {};             // signals of the slot's last call
+  RelItem* h_rel[kSlots] = {};
+  RelItem* d_rel[kSlots] = {};
+  int64_t rel_cap = 0;
+  hipEvent_t sdma_ev[kSlots] = {};
+  bool sdma_ev_used[kSlots] = {};
+  int sdma_slot = 0;
+  bool sdma_hsa = false;                  // hsa_init taken (released by sgt_ctx_destroy)
+  hipEvent_t ev_done = nullptr;           // recorded at the end of each call's work
+  bool ev_done_used = false;
   std::mutex mu;
 };
 
@@ -165,13 +195,16 @@ int64_t default_flag_rows(int64_t rows_per_shard, int64_t K, int esz, int panel)
   return 1;
 }
 
-sgt_status check_opts(const sgt_opts* o, int W) {
+sgt_status check_opts(const sgt_opts* o, int W, bool sdma_ok = false) {
   if (!o) return fail(SGT_EINVAL, "opts is NULL");
   if (o->rank < 0 || o->rank >= W) return fail(SGT_EINVAL, "rank %d outside [0, %d)", o->rank, W);
   if (o->in_dtype != SGT_F32 && o->in_dtype != SGT_BF16) return fail(SGT_EINVAL, "in_dtype %d", o->in_dtype);
   if (o->out_dtype != SGT_F32 && o->out_dtype != SGT_BF16) return fail(SGT_EINVAL, "out_dtype %d", o->out_dtype);
   if (o->b_layout != SGT_KN && o->b_layout != SGT_NK) return fail(SGT_EINVAL, "b_layout %d", o->b_layout);
-  if (o->producer < SGT_PROD_CU || o->producer > SGT_PROD_SERIAL) return fail(SGT_EINVAL, "producer %d", o->producer);
+  if (o->producer < SGT_PROD_CU || o->producer > SGT_PROD_SDMA) return fail(SGT_EINVAL, "producer %d", o->producer);
+  if (o->sdma_peers < 0) return fail(SGT_EINVAL, "sdma_peers %d", o->sdma_peers);
+  if (o->producer == SGT_PROD_SDMA && !sdma_ok)
+    return fail(SGT_EUNSUPPORTED, "the copy-engine producer (SGT_PROD_SDMA) applies to sgt_ag_gemm");
   if (o->order != SGT_ORDER_MESH && o->order != SGT_ORDER_SHARD) return fail(SGT_EINVAL, "order %d", o->order);
   if (o->flag_rows < 0 || o->producer_cus < 0 || o->consumer_cus < 0) return fail(SGT_EINVAL, "negative count");
   if (!(o->peer_gbps >= 0) || !(o->jitter_us >= 0) || !(o->timeout_ms >= 0))
@@ -423,10 +456,290 @@ sgt_status mark(const sgt_opts& o, int which, hipStream_t stream) {
   return SGT_OK;
 }
 
+sgt_status sdma_drain_all(sgt_ctx* c);
+
+// Wait for the context's own work -- its producer stream, the end of its last
+// call on the caller's stream, and any copy-engine copies still in flight --
+// and return the device status (SGT_ETIMEDOUT after an expired wait, then
+// cleared).  The caller holds the context's lock.
+sgt_status sync_locked(sgt_ctx* c) {
+  DeviceGuard g(c->device);
+  HIP_TRY(hipStreamSynchronize(c->prod));
+  if (c->ev_done_used) HIP_TRY(hipEventSynchronize(c->ev_done));
+  sgt_status s = sdma_drain_all(c);
+  if (s != SGT_OK) return s;
+  uint32_t st[4] = {0, 0, 0, 0};
+  HIP_TRY(hipMemcpy(st, c->d_status, sizeof st, hipMemcpyDeviceToHost));
+  if (st[0] == kStatusTimeout) {
+    HIP_TRY(hipMemset(c->d_status, 0, sizeof st));
+    return fail(SGT_ETIMEDOUT, "wait on flag %u timed out: saw %u, expected %u", st[1], st[2], st[3]);
+  }
+  return SGT_OK;
+}
+
+// End of a call that launched work on `stream`: remember where the call's work
+// ends (sgt_sync waits for it), and in blocking mode wait and report.
 sgt_status finish(sgt_ctx* ctx, const sgt_opts& o, hipStream_t stream) {
+  HIP_TRY(hipEventRecord(ctx->ev_done, stream));
+  ctx->ev_done_used = true;
   if (!o.blocking) return SGT_OK;
   HIP_TRY(hipStreamSynchronize(stream));
-  return sgt_sync(ctx);
+  return sync_locked(ctx);
+}
+
+// ---- copy-engine producer (SGT_PROD_SDMA) ----
+
+struct AgentMatch {
+  unsigned domain, bus, device;
+  hsa_agent_t agent;
+  bool found;
+};
+
+hsa_status_t match_agent(hsa_agent_t a, void* data) {
+  AgentMatch* m = static_cast<AgentMatch*>(data);
+  hsa_device_type_t t;
+  if (hsa_agent_get_info(a, HSA_AGENT_INFO_DEVICE, &t) != HSA_STATUS_SUCCESS || t != HSA_DEVICE_TYPE_GPU)
+    return HSA_STATUS_SUCCESS;
+  uint32_t bdf = 0, dom = 0;
+  if (hsa_agent_get_info(a, (hsa_agent_info_t)HSA_AMD_AGENT_INFO_BDFID, &bdf) != HSA_STATUS_SUCCESS ||
+      hsa_agent_get_info(a, (hsa_agent_info_t)HSA_AMD_AGENT_INFO_DOMAIN, &dom) != HSA_STATUS_SUCCESS)
+    return HSA_STATUS_SUCCESS;
+  if (dom == m->domain && ((bdf >> 8) & 0xFFu) == m->bus && ((bdf >> 3) & 0x1Fu) == m->device) {
+    m->agent = a;
+    m->found = true;
+    return HSA_STATUS_INFO_BREAK;
+  }
+  return HSA_STATUS_SUCCESS;
+}
+
+// Wait (on the host, bounded) until every completion signal of an SDMA slot's
+// last call reads 0: its copies are done and their signals may be reused.
+sgt_status sdma_slot_drain(sgt_ctx* c, int slot) {
+  const int n = 2 * c->sdma_used[slot];
+  for (int i = 0; i < n; ++i) {
+    hsa_signal_t sg = c->sdma_sig[slot][(size_t)i];
+    int64_t left_us = 10 * 1000 * 1000;
+    while (hsa_signal_load_scacquire(sg) != 0) {
+      if (left_us <= 0) return fail(SGT_EHIP, "copy-engine copies of an earlier call did not complete");
+      hsa_signal_wait_scacquire(sg, HSA_SIGNAL_CONDITION_EQ, 0, 1000000, HSA_WAIT_STATE_BLOCKED);
+      left_us -= 1000;
+    }
+  }
+  c->sdma_used[slot] = 0;
+  return SGT_OK;
+}
+
+sgt_status sdma_drain_all(sgt_ctx* c) {
+  if (!c->sdma_ready) return SGT_OK;
+  for (int s = 0; s < kSlots; ++s) {
+    if (c->sdma_ev_used[s]) HIP_TRY(hipEventSynchronize(c->sdma_ev[s]));
+    sgt_status st = sdma_slot_drain(c, s);
+    if (st != SGT_OK) return st;
+  }
+  return SGT_OK;
+}
+
+// First use of the copy-engine producer on a context: the HSA agent of the
+// context's device (matched by PCI location), its available copy engines, the
+// mark words, the pinned epoch words and the slots' gate signals and events.
+sgt_status sdma_setup(sgt_ctx* c) {
+  if (c->sdma_ready) return SGT_OK;
+  if (hsa_init() != HSA_STATUS_SUCCESS) return fail(SGT_EHIP, "hsa_init failed");
+  c->sdma_hsa = true;
+  char pci[64] = {0};
+  HIP_TRY(hipDeviceGetPCIBusId(pci, (int)sizeof pci, c->device));
+  AgentMatch m{};
+  unsigned fn = 0;
+  if (std::sscanf(pci, "%x:%x:%x.%x", &m.domain, &m.bus, &m.device, &fn) != 4)
+    return fail(SGT_EHIP, "unexpected PCI bus id '%s'", pci);
+  hsa_iterate_agents(match_agent, &m);
+  if (!m.found) return fail(SGT_EUNSUPPORTED, "no HSA agent for device %d (%s)", c->device, pci);
+  // The device's copy engines for copies within its memory.  Some runtime
+  // versions answer this query only for copies between a GPU and the host:
+  // then the engines of that direction are used, less the first two (which
+  // carry the host's transfers) when others exist.
+  uint32_t mask = 0;
+  hsa_status_t hs = hsa_amd_memory_copy_engine_status(m.agent, m.agent, &mask);
+  if (hs != HSA_STATUS_SUCCESS || mask == 0) {
+    hsa_agent_t cpu{};
+    hsa_iterate_agents(
+        [](hsa_agent_t a, void* d) -> hsa_status_t {
+          hsa_device_type_t t;
+          if (hsa_agent_get_info(a, HSA_AGENT_INFO_DEVICE, &t) == HSA_STATUS_SUCCESS && t == HSA_DEVICE_TYPE_CPU) {
+            *static_cast<hsa_agent_t*>(d) = a;
+            return HSA_STATUS_INFO_BREAK;
+          }
+          return HSA_STATUS_SUCCESS;
+        },
+        &cpu);
+    mask = 0;
+    hs = cpu.handle ? hsa_amd_memory_copy_engine_status(m.agent, cpu, &mask) : HSA_STATUS_ERROR_INVALID_AGENT;
+    if (hs == HSA_STATUS_SUCCESS && (mask & ~3u)) mask &= ~3u;
+  }
+  if (hs != HSA_STATUS_SUCCESS || mask == 0)
+    return fail(SGT_EUNSUPPORTED, "no copy engine available on device %d (%s, status %d, mask 0x%x)", c->device, pci,
+                (int)hs, mask);
+  c->sdma_agent = m.agent;
+  c->sdma_engines.clear();
+  for (int b = 0; b < 32; ++b)
+    if (mask & (1u << b)) c->sdma_engines.push_back(1u << b);
+  HIP_TRY(hipMalloc(&c->d_marks, kSdmaMaxUnits * sizeof(uint32_t)));
+  HIP_TRY(hipMemset(c->d_marks, 0, kSdmaMaxUnits * sizeof(uint32_t)));
+  HIP_TRY(hipHostMalloc(&c->h_sdma_epoch, kSlots * 16 * sizeof(uint32_t), hipHostMallocDefault));
+  for (int s = 0; s < kSlots; ++s) {
+    if (hsa_signal_create(0, 0, nullptr, &c->sdma_gate[s]) != HSA_STATUS_SUCCESS)
+      return fail(SGT_ENOMEM, "hsa_signal_create");
+    HIP_TRY(hipEventCreateWithFlags(&c->sdma_ev[s], hipEventDisableTiming));
+  }
+  HIP_TRY(hipDeviceSynchronize());
+  c->sdma_ready = true;
+  return SGT_OK;
+}
+
+// Runs on the runtime's host thread when the producer stream reaches the call:
+// the copy engines may start (their copies wait on this gate).
+void open_gate(void* gate) { hsa_signal_store_screlease(*static_cast<hsa_signal_t*>(gate), 0); }
+
+// The copy-engine producer of one AllGather+GEMM call (SGT_PROD_SDMA), up to
+// and including its producer-stream launch; the caller launches the consumer
+// beside it and joins.  items: the call's schedule (release order).  Items of
+// the local shard and of the first n_sd remote peers in mesh order (rank+1,
+// rank+2, ...) go to the copy engines: each copy unit (a whole 256-row panel
+// with K-chunked signal tiles, else up to kSdmaUnitBytes of consecutive signal
+// tiles of one peer) is one engine copy, gated on the call's host-function gate
+// (so no copy starts before the caller's stream reaches the call) and followed
+// on the same engine by a 4-byte copy of the epoch into the unit's mark word.
+// The other items go to *cu_wgs CU producer workgroups; one more workgroup of
+// the same launch releases the copy-engine items.
+sgt_status ag_sdma_launch(sgt_ctx* ctx, const sgt_opts& o, const AgPlan& p, int W, int64_t K, int esz,
+                          const void* const* shards, void* gathered, uint32_t* flags, const ProdItem* items,
+                          int n_items, int64_t tile_bytes, uint32_t seg_rows, uint32_t seg_bytes,
+                          uint32_t row_stride, uint64_t* trace_rel, uint32_t e, hipStream_t stream, int* cu_wgs) {
+  sgt_status st = sdma_setup(ctx);
+  if (st != SGT_OK) return st;
+  const int n_sd = o.sdma_peers > 0 ? std::min(o.sdma_peers, W - 1) : W - 1;
+  const int64_t tps = p.tiles_per_shard;
+  // copy units: with K-chunked signal tiles a unit is a panel of one peer, else
+  // a run of upu consecutive signal tiles of one peer
+  const int64_t upu = p.n_kc > 0 ? p.n_kc : std::max<int64_t>(1, kSdmaUnitBytes / tile_bytes);
+  const int64_t units_per_shard = (tps + upu - 1) / upu;
+  std::vector<int> unit_of((size_t)(W * units_per_shard), -1);
+  struct Unit { const char* src; char* dst; int64_t bytes; };
+  std::vector<Unit> units;
+  std::vector<RelItem> rel;
+  std::vector<ProdItem> cu;
+  rel.reserve((size_t)n_items);
+  for (int i = 0; i < n_items; ++i) {
+    const ProdItem& it = items[i];
+    const int d = ((int)it.peer - o.rank + W) % W;  // 0: the local shard
+    if (d > n_sd) {
+      cu.push_back(it);
+      continue;
+    }
+    const int64_t local_tile = (int64_t)it.flag0 - (int64_t)it.peer * tps;
+    const int64_t u = local_tile / upu;
+    int& id = unit_of[(size_t)(it.peer * units_per_shard + u)];
+    if (id < 0) {
+      if ((int)units.size() >= kSdmaMaxUnits)
+        return fail(SGT_EUNSUPPORTED, "more than %d copy-engine copies in one call", kSdmaMaxUnits);
+      id = (int)units.size();
+      // the unit's rows: panel u (K-chunked) or signal tiles [u upu, +upu) of the shard
+      const int64_t row0 = p.n_kc > 0 ? u * p.flag_rows : u * upu * p.flag_rows;
+      const int64_t rows = p.n_kc > 0 ? p.flag_rows : std::min(upu, tps - u * upu) * p.flag_rows;
+      const int64_t row_bytes = K * esz;
+      units.push_back(Unit{static_cast<const char*>(shards[it.peer]) + row0 * row_bytes,
+                           static_cast<char*>(gathered) + ((int64_t)it.peer * p.rows_per_shard + row0) * row_bytes,
+                           rows * row_bytes});
+    }
+    rel.push_back(RelItem{it.release, it.flag0, it.nflags, (uint32_t)id, it.peer});
+  }
+  const int n_units = (int)units.size(), n_rel = (int)rel.size(), n_cu = (int)cu.size();
+  // this call's slot: its previous call's copies must be done before its signals are reused
+  const int ss = ctx->sdma_slot;
+  ctx->sdma_slot = (ss + 1) % kSlots;
+  if (ctx->sdma_ev_used[ss]) HIP_TRY(hipEventSynchronize(ctx->sdma_ev[ss]));
+  if ((st = sdma_slot_drain(ctx, ss)) != SGT_OK) return st;
+  std::vector<hsa_signal_t>& sig = ctx->sdma_sig[ss];
+  while ((int)sig.size() < 2 * n_units) {
+    hsa_signal_t sg;
+    if (hsa_signal_create(0, 0, nullptr, &sg) != HSA_STATUS_SUCCESS) return fail(SGT_ENOMEM, "hsa_signal_create");
+    sig.push_back(sg);
+  }
+  if (n_rel > ctx->rel_cap) {
+    // grow every slot's releaser table (no call of this context is in flight after the drain)
+    if ((st = sdma_drain_all(ctx)) != SGT_OK) return st;
+    HIP_TRY(hipStreamSynchronize(ctx->prod));
+    const int64_t cap = std::max<int64_t>(n_rel, 4096);
+    for (int s2 = 0; s2 < kSlots; ++s2) {
+      if (ctx->h_rel[s2]) (void)hipHostFree(ctx->h_rel[s2]);
+      if (ctx->d_rel[s2]) (void)hipFree(ctx->d_rel[s2]);
+      ctx->h_rel[s2] = nullptr;
+      ctx->d_rel[s2] = nullptr;
+    }
+    ctx->rel_cap = 0;
+    for (int s2 = 0; s2 < kSlots; ++s2) {
+      HIP_TRY(hipHostMalloc(&ctx->h_rel[s2], cap * sizeof(RelItem), hipHostMallocDefault));
+      HIP_TRY(hipMalloc(&ctx->d_rel[s2], cap * sizeof(RelItem)));
+    }
+    ctx->rel_cap = cap;
+  }
+  // the copies, gated; each followed by its mark copy (the pinned epoch word of this slot)
+  uint32_t* ep = ctx->h_sdma_epoch + 16 * ss;
+  *ep = e;
+  hsa_signal_store_relaxed(ctx->sdma_gate[ss], 1);
+  const int n_eng = (int)ctx->sdma_engines.size();
+  for (int u = 0; u < n_units; ++u) {
+    hsa_signal_store_relaxed(sig[(size_t)(2 * u)], 1);
+    hsa_signal_store_relaxed(sig[(size_t)(2 * u + 1)], 1);
+  }
+  ctx->sdma_used[ss] = n_units;
+  for (int u = 0; u < n_units; ++u) {
+    const hsa_amd_sdma_engine_id_t eng = (hsa_amd_sdma_engine_id_t)ctx->sdma_engines[(size_t)(u % n_eng)];
+    hsa_status_t h1 = hsa_amd_memory_async_copy_on_engine(units[(size_t)u].dst, ctx->sdma_agent, units[(size_t)u].src,
+                                                          ctx->sdma_agent, (size_t)units[(size_t)u].bytes, 1,
+                                                          &ctx->sdma_gate[ss], sig[(size_t)(2 * u)], eng, true);
+    hsa_status_t h2 = h1 == HSA_STATUS_SUCCESS
+                          ? hsa_amd_memory_async_copy_on_engine(ctx->d_marks + u, ctx->sdma_agent, ep,
+                                                                ctx->sdma_agent, sizeof(uint32_t), 1,
+                                                                &sig[(size_t)(2 * u)], sig[(size_t)(2 * u + 1)], eng,
+                                                                true)
+                          : h1;
+    if (h2 != HSA_STATUS_SUCCESS) {
+      // nothing of this call has reached the stream yet: let the copies already
+      // queued run once the stream's earlier work is done, then report
+      for (int v = u; v < n_units; ++v) {
+        hsa_signal_store_relaxed(sig[(size_t)(2 * v)], 0);
+        hsa_signal_store_relaxed(sig[(size_t)(2 * v + 1)], 0);
+      }
+      (void)hipStreamSynchronize(stream);
+      hsa_signal_store_screlease(ctx->sdma_gate[ss], 0);
+      return fail(SGT_EHIP, "copy-engine copy %d of %d could not be queued (HSA status %d)", u, n_units, (int)h2);
+    }
+  }
+  // producer stream: fork, open the gate when the stream gets there, then the
+  // CU producer workgroups (if any) and the releaser in one launch
+  HIP_TRY(hipEventRecord(ctx->ev_fork, stream));
+  HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
+  HIP_TRY(hipLaunchHostFunc(ctx->prod, open_gate, &ctx->sdma_gate[ss]));
+  std::memcpy(ctx->h_rel[ss], rel.data(), (size_t)n_rel * sizeof(RelItem));
+  HIP_TRY(hipMemcpyAsync(ctx->d_rel[ss], ctx->h_rel[ss], (size_t)n_rel * sizeof(RelItem), hipMemcpyHostToDevice,
+                         ctx->prod));
+  int slot = -1;
+  if (n_cu > 0 && (st = stage_items(ctx, cu.data(), n_cu, ctx->prod, &slot)) != SGT_OK) return st;
+  // the releaser is one more workgroup of the same launch: the CU share takes one fewer, so the two
+  // together hold the CUs a CU producer alone would
+  const int pwg = n_cu > 0 ? std::max(1, std::min(default_producer_wgs(o, ctx->n_cu) - 1, n_cu)) : 0;
+  HIP_TRY(launch_ag_producer(flags, slot >= 0 ? ctx->d_items[slot] : nullptr, n_cu, tile_bytes, e, o.withhold_peer,
+                             trace_rel, pwg, ctx->prod, nullptr, nullptr, seg_rows, seg_bytes, row_stride,
+                             ctx->d_rel[ss], n_rel, ctx->d_marks, timeout_ticks(o), ctx->d_status));
+  if (slot >= 0) {
+    HIP_TRY(hipEventRecord(ctx->slot_ev[slot], ctx->prod));
+    ctx->slot_used[slot] = true;
+  }
+  HIP_TRY(hipEventRecord(ctx->sdma_ev[ss], ctx->prod));
+  ctx->sdma_ev_used[ss] = true;
+  *cu_wgs = pwg + (n_rel > 0 ? 1 : 0);
+  return SGT_OK;
 }
 
 }  // namespace
@@ -488,6 +801,7 @@ sgt_status sgt_ctx_create(sgt_ctx** out, int device) {
   chk(hipStreamCreateWithFlags(&c->prod, hipStreamNonBlocking), "hipStreamCreate");
   chk(hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming), "hipEventCreate");
   chk(hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming), "hipEventCreate");
+  chk(hipEventCreateWithFlags(&c->ev_done, hipEventDisableTiming), "hipEventCreate");
   chk(hipMalloc(&c->d_status, 4 * sizeof(uint32_t)), "hipMalloc(status)");
   chk(hipMalloc(&c->d_counters, 64 * sizeof(uint32_t)), "hipMalloc(counters)");
   chk(hipMalloc(&c->d_moe, 1024 * sizeof(uint32_t)), "hipMalloc(moe)");
@@ -517,6 +831,21 @@ sgt_status sgt_ctx_destroy(sgt_ctx* c) {
   DeviceGuard g(c->device);
   if (c->prod) (void)hipStreamSynchronize(c->prod);
   (void)hipDeviceSynchronize();
+  if (c->sdma_ready) {
+    (void)sdma_drain_all(c);
+    for (int s = 0; s < kSlots; ++s) {
+      for (hsa_signal_t sg : c->sdma_sig[s]) hsa_signal_destroy(sg);
+      c->sdma_sig[s].clear();
+      if (c->sdma_gate[s].handle) hsa_signal_destroy(c->sdma_gate[s]);
+      if (c->sdma_ev[s]) (void)hipEventDestroy(c->sdma_ev[s]);
+      if (c->h_rel[s]) (void)hipHostFree(c->h_rel[s]);
+      if (c->d_rel[s]) (void)hipFree(c->d_rel[s]);
+    }
+    if (c->d_marks) (void)hipFree(c->d_marks);
+    if (c->h_sdma_epoch) (void)hipHostFree(c->h_sdma_epoch);
+  }
+  if (c->sdma_hsa) (void)hsa_shut_down();
+  if (c->ev_done) (void)hipEventDestroy(c->ev_done);
   for (int s = 0; s < kSlots; ++s) {
     if (c->h_items[s]) (void)hipHostFree(c->h_items[s]);
     if (c->d_items[s]) (void)hipFree(c->d_items[s]);
@@ -544,15 +873,8 @@ sgt_status sgt_ctx_destroy(sgt_ctx* c) {
 
 sgt_status sgt_sync(sgt_ctx* c) {
   if (!c) return fail(SGT_EINVAL, "ctx is NULL");
-  DeviceGuard g(c->device);
-  HIP_TRY(hipDeviceSynchronize());
-  uint32_t st[4] = {0, 0, 0, 0};
-  HIP_TRY(hipMemcpy(st, c->d_status, sizeof st, hipMemcpyDeviceToHost));
-  if (st[0] == kStatusTimeout) {
-    HIP_TRY(hipMemset(c->d_status, 0, sizeof st));
-    return fail(SGT_ETIMEDOUT, "wait on flag %u timed out: saw %u, expected %u", st[1], st[2], st[3]);
-  }
-  return SGT_OK;
+  std::lock_guard<std::mutex> lock(c->mu);
+  return sync_locked(c);
 }
 
 int64_t sgt_ag_flag_count(int W, int64_t M, int64_t K, const sgt_opts* opts) {
@@ -592,7 +914,7 @@ int64_t sgt_trace_words(int W, int64_t M, int64_t K, int64_t N, const sgt_opts* 
 sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B, void* A_gathered, void* C,
                        uint32_t* flags, int W, int64_t M, int64_t K, int64_t N, const sgt_opts* opts, void* stream_) {
   if (!ctx) return fail(SGT_EINVAL, "ctx is NULL");
-  sgt_status st = check_opts(opts, W < 1 ? 1 : W);
+  sgt_status st = check_opts(opts, W < 1 ? 1 : W, true);
   if (st != SGT_OK) return st;
   const sgt_opts& o = *opts;
   AgPlan p;
@@ -664,16 +986,24 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   // Overlapped: the producer runs on its own stream.  The consumer keeps one
   // workgroup per CU (its LDS use allows no more) on all but the producer's
   // share of CUs, so both kernels are resident at once and no wait can starve.
-  HIP_TRY(hipEventRecord(ctx->ev_fork, stream));
-  HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
-  if ((st = stage_items(ctx, items, n_items, ctx->prod, &slot)) != SGT_OK) return st;
-  HIP_TRY(launch_ag_producer(flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
-                             trace_rel, pwg, ctx->prod, nullptr, nullptr, seg_rows, seg_bytes, row_stride));
-  HIP_TRY(hipEventRecord(ctx->slot_ev[slot], ctx->prod));
-  ctx->slot_used[slot] = true;
+  int prod_wgs = pwg;
+  if (o.producer == SGT_PROD_SDMA) {
+    if ((st = ag_sdma_launch(ctx, o, p, W, K, esz, A_shards, A_gathered, flags, items, n_items, tile_bytes, seg_rows,
+                             seg_bytes, row_stride, trace_rel, e, stream, &prod_wgs)) != SGT_OK)
+      return st;
+  } else {
+    HIP_TRY(hipEventRecord(ctx->ev_fork, stream));
+    HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
+    if ((st = stage_items(ctx, items, n_items, ctx->prod, &slot)) != SGT_OK) return st;
+    HIP_TRY(launch_ag_producer(flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
+                               trace_rel, pwg, ctx->prod, nullptr, nullptr, seg_rows, seg_bytes, row_stride));
+    HIP_TRY(hipEventRecord(ctx->slot_ev[slot], ctx->prod));
+    ctx->slot_used[slot] = true;
+  }
   int grid;
   if (o.in_dtype == SGT_BF16)
-    grid = o.consumer_cus > 0 ? std::min(o.consumer_cus, consumer_beside(ctx, pwg)) : consumer_beside(ctx, pwg);
+    grid = o.consumer_cus > 0 ? std::min(o.consumer_cus, consumer_beside(ctx, prod_wgs))
+                              : consumer_beside(ctx, prod_wgs);
   else  // fp32 tiles: small workgroups, two per CU by default (a caller's count is capped there)
     grid = o.consumer_cus > 0 ? std::min(o.consumer_cus, 2 * ctx->n_cu) : 2 * ctx->n_cu;
   grid = std::min(grid, total_tiles);
@@ -1127,6 +1457,7 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   tb.n_tiles = ctx->d_moe;
   tb.tiles_cap = (uint32_t)ctx->moe_cap;
   tb.claim = ctx->d_moe + 4;
+  tb.xcd_claim = ctx->d_moe + 64;  // kXcds counters at words 64, 80, ..., 176
   tb.done = ctx->d_moe + 8;
   tb.ranks = ctx->d_moe_ranks;
   tb.tiles = ctx->d_moe_tiles;
@@ -1139,7 +1470,7 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   a.We = static_cast<const uint16_t*>(W_experts);
   a.Y = Y; a.row_token = row_token; a.expert_off = expert_off; a.order = tb.order; a.n_tiles = tb.n_tiles;
   a.tiles_cap = tb.tiles_cap;
-  a.claim = tb.claim; a.flags = shard_flags; a.status = ctx->d_status; a.trace = o.trace;
+  a.claim = tb.claim; a.xcd_claim = tb.xcd_claim; a.flags = shard_flags; a.status = ctx->d_status; a.trace = o.trace;
   a.T = T; a.H = H; a.I = I; a.rows = T * topk; a.E = E; a.flag_rows = (int32_t)p.flag_rows; a.tiles_n = p.tiles_n;
   a.epoch = e; a.timeout_ticks = timeout_ticks(o);
   const int64_t n_items_max = max_tiles * p.tiles_n;

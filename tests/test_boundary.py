@@ -45,9 +45,10 @@ def test_opts_struct_layout_matches(L):
     assert o.in_dtype == _sgt.SGT_BF16 and o.out_dtype == _sgt.SGT_F32 and o.timeout_ms == 2000.0
     assert o.withhold_peer == -1 and o.trace is None and o.tile_rows == 0 and o.k_chunks == 0
     L.sgt_opts_size.restype = ctypes.c_size_t
-    assert ctypes.sizeof(_sgt.Opts) == L.sgt_opts_size() == 120
+    assert ctypes.sizeof(_sgt.Opts) == L.sgt_opts_size() == 128
     # every field at the offset the C compiler gave it: the last field is the event pair
-    assert _sgt.Opts.consumer_events.offset == 120 - 2 * ctypes.sizeof(ctypes.c_void_p)
+    assert _sgt.Opts.consumer_events.offset == 128 - 2 * ctypes.sizeof(ctypes.c_void_p)
+    assert o.sdma_peers == 0
 
 
 def test_version_and_status_strings(L):

@@ -332,3 +332,59 @@ def test_k_chunks_full_qwen_shape(ctx):
     assert torch.equal(C1.view(torch.int32), C0.view(torch.int32))
     assert torch.equal(Ag1.view(torch.int16), torch.cat(dA).view(torch.int16))
     assert bool((fl == fl[0]).all())
+
+
+# ---------------------------------------------------------------- copy-engine producer
+@pytest.mark.parametrize("k_chunks", [0, 8])
+@pytest.mark.parametrize("sdma", [dict(producer="sdma"), dict(producer="sdma", sdma_peers=1, producer_cus=8)],
+                         ids=["engines", "engines+cu"])
+def test_sdma_producer_bits_match_cu_producer(ctx, orc, k_chunks, sdma):
+    """The copy engines move the shards (or, with sdma_peers, the first peers' shards while CU workgroups move the
+    rest); the releaser publishes each signal tile once its copy has landed and its link time has come.  Gathered
+    bits, C bits and flags equal those of the CU producer under the same slow, jittered links."""
+    w = I.AGWorkload("t", W=4, M=4 * 512, K=1024, N=520, seed_index=36)
+    shards, B = I.make_ag(w, B_layout="nk")
+    dA, dB = [dev(s) for s in shards], dev(B)
+    link = dict(peer_gbps=8.0, jitter_us=20.0, arrival_seed=4, rank=1, k_chunks=k_chunks)
+    _, C0, _ = _run_kc(ctx, dA, dB, w.M, w.K, w.N, "nk", **link)
+    for rep in range(2):   # the second call reuses the context's copy-engine state
+        Ag1, C1, fl = _run_kc(ctx, dA, dB, w.M, w.K, w.N, "nk", **link, **sdma)
+        assert torch.equal(Ag1.view(torch.int16), torch.cat(dA).view(torch.int16)), "gathered buffer"
+        assert torch.equal(C1.view(torch.int32), C0.view(torch.int32)), "C bits differ from the CU producer"
+        f = fl.cpu().numpy()
+        assert (f == f[0]).all() and f[0] > 0
+    rows = sample_rows(w.M, w.W)
+    _, C_ref = orc.ag_gemm(shards, B, b_layout="nk", rows=rows)
+    assert_close(host(C1)[rows], C_ref, what="copy-engine C", **TOL_BF16)
+
+
+def test_sdma_producer_tiny_f32(ctx, orc):
+    w = I.TINY
+    shards, B = I.make_ag(w)
+    A_ref, C_ref = orc.ag_gemm(shards, B)
+    Ag, C, fl = run_ag(ctx, shards, B, rank=3, flag_rows=w.flag_rows, producer="sdma", arrival_seed=2,
+                       arrival_order="global", jitter_us=w.jitter_us)
+    assert np.array_equal(Ag, A_ref)
+    assert (fl == fl[0]).all() and fl[0] > 0
+    assert_close(C, C_ref, what="tiny f32 C, copy engines", **TOL_F32)
+
+
+def test_sdma_producer_withheld_peer_times_out(ctx):
+    w = I.AGWorkload("t", W=4, M=4 * 256, K=512, N=256, seed_index=37)
+    shards, B = I.make_ag(w)
+    with pytest.raises(sgt.SgtError) as ei:
+        run_ag(ctx, shards, B, producer="sdma", withhold_peer=2, timeout_ms=30.0)
+    assert ei.value.status == sgt.SGT_ETIMEDOUT
+    Ag, C, _ = run_ag(ctx, shards, B, producer="sdma")   # the context stays usable
+    assert np.array_equal(Ag, np.concatenate(shards))
+
+
+def test_sdma_producer_only_for_ag_gemm(ctx):
+    w = I.RSWorkload("t", W=4, M=1024, K=64, N=256, seed_index=38)
+    A, B, parts = I.make_rs(w)
+    ng, npf = sgt.rs_flag_count(w.W, w.M, w.N)
+    with pytest.raises(sgt.SgtError) as ei:
+        ctx.gemm_rs(dev(A), dev(B), [dev(p) for p in parts], torch.empty((w.M, w.N), device="cuda:0"),
+                    torch.empty((w.M // w.W, w.N), device="cuda:0"), torch.zeros(ng, dtype=torch.int32, device="cuda:0"),
+                    torch.zeros(npf, dtype=torch.int32, device="cuda:0"), producer="sdma", blocking=True)
+    assert ei.value.status == sgt.SGT_EUNSUPPORTED

@@ -92,6 +92,23 @@ def test_headline_call_every_row(ctx, orc, rank):
     print("headline rank %d: relative Frobenius %.3e over %d x %d" % (rank, rf, w.M, w.N), flush=True)
 
 
+@pytest.mark.parametrize("sdma", [dict(producer="sdma"), dict(producer="sdma", sdma_peers=3)],
+                         ids=["engines", "engines+cu"])
+def test_headline_call_copy_engines_every_row(ctx, orc, sdma):
+    """The headline call with the copy-engine producer (all remote peers, or three of them with CU
+    workgroups moving the other four): every row against the oracle."""
+    w, shards, B, A_ref, C_ref = _llama(orc, "normal")
+    dA, dB = [dev(s) for s in shards], dev(B)
+    Ag = poison_like(torch.empty((w.M, w.K), dtype=torch.bfloat16, device="cuda:0"))
+    C = poison_like(torch.empty((w.M, w.N), dtype=torch.float32, device="cuda:0"))
+    flags = torch.zeros(sgt.ag_flag_count(w.W, w.M, w.K, k_chunks=K_CHUNKS), dtype=torch.int32, device="cuda:0")
+    ctx.ag_gemm(dA, dB, Ag, C, flags, rank=2, b_layout="nk", k_chunks=K_CHUNKS, peer_gbps=w.peer_gbps,
+                jitter_us=w.jitter_us, arrival_seed=31, blocking=True, **sdma)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(Ag), A_ref), "gathered buffer"
+    _compare_all_rows(host(C), C_ref, exact=False, what="headline C, copy engines")
+
+
 @pytest.mark.parametrize("rank", [0, 5])
 def test_headline_call_integer_inputs_bit_exact(ctx, orc, rank):
     """Inputs in [-3, 3] are exact in bf16 and every partial sum is an integer below 2^24, so fp32
