@@ -79,17 +79,55 @@ __device__ __forceinline__ int chunks_in_after(const AgArgs& a, int64_t pm, int 
   return *n;
 }
 
+// The next tile of this workgroup, or -1: the static schedule (tile t, then
+// t + G, ...) or, with dynamic claiming, the next claim from this XCD's list
+// and then from the other XCDs' lists (thread 0 claims; `x`, `left` and
+// `next` are its state; the result goes through a shared word).
+__device__ __forceinline__ int next_tile(const AgArgs& a, int total, int* x, int* left, int* next, int* tile_s) {
+  if (!a.xcd_claim) {
+    const int t = *next;
+    *next += gridDim.x;
+    return t < total ? t : -1;
+  }
+  if (threadIdx.x == 0) {
+    int t = -1;
+    while (*left > 0) {
+      const uint32_t c = atomicAdd(a.xcd_claim + *x * kXcdClaimStride, 1u);
+      t = (int)xcd_seq_tile(*x, c, a.base_grid, total);
+      if (t >= 0) break;
+      *x = (*x + 1) % kXcds;
+      --*left;
+    }
+    *tile_s = t;
+  }
+  __syncthreads();
+  const int t = *tile_s;
+  __syncthreads();  // every thread has read tile_s before thread 0 may claim again
+  return t;
+}
+
 template <int kW, bool kBNK, bool kOutBf16>
 __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) ag_consumer_bf16(AgArgs a) {
   __shared__ int ok;
   __shared__ int all_in;  // its own word: the chunk waits that may follow rewrite `ok` with no barrier between
   __shared__ int n_more;  // likewise for the count of chunks already in
+  __shared__ int tile_s;
   __shared__ uint64_t t_wait;
   const int total = a.tiles_m * a.tiles_n;
-  const int G = gridDim.x;
   const uint16_t* A = static_cast<const uint16_t*>(a.A);
   const uint16_t* B = static_cast<const uint16_t*>(a.B);
-  for (int t = xcd_remap(blockIdx.x, G); t < total; t += G) {
+  if (a.late_blocks > 0 && (int)blockIdx.x >= (int)gridDim.x - a.late_blocks) {
+    // a workgroup that may sit on a CU the producer needs: run only if every
+    // producer workgroup is already running (one check, no wait); it then
+    // claims tiles like the others
+    if (threadIdx.x == 0)
+      ok = __hip_atomic_load(a.started, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.started_all ? 1 : 0;
+    __syncthreads();
+    if (!ok) return;
+  }
+  int xq = (int)(blockIdx.x % kXcds), left = kXcds, next = xcd_remap(blockIdx.x, gridDim.x);
+  for (int t = next_tile(a, total, &xq, &left, &next, &tile_s); t >= 0;
+       t = next_tile(a, total, &xq, &left, &next, &tile_s)) {
     int64_t seq_m, pn;
     tile_at(t, a.tiles_m, a.tiles_n, &seq_m, &pn);
     const int64_t pm = panel_at(seq_m, a.tiles_m, a.rows_per_shard, kBM, a.W, a.rank, a.order);

@@ -7,6 +7,8 @@
 namespace sgt {
 
 constexpr int kMaxW = 64;
+constexpr int kXcds = 8;             // XCDs of the device; workgroup b of a grid runs on XCD b % kXcds
+constexpr int kXcdClaimStride = 16;  // words between per-XCD claim counters
 
 // Device status word written by a kernel whose bounded wait expired.
 // status[0] = code (0 ok, 3 timeout), [1] = flag index, [2] = value seen, [3] = value expected.
@@ -61,6 +63,16 @@ struct AgArgs {
   uint32_t epoch;
   int32_t tile_waves;     // 4 or 8 wave64s per bf16 workgroup
   uint64_t timeout_ticks;
+  // bf16 tiles claimed dynamically (xcd_claim != null): the tiles the static
+  // schedule of a base_grid-workgroup grid gives XCD x are claimed in that
+  // order from counter xcd_claim[x * kXcdClaimStride], then the other XCDs'
+  // lists; the last late_blocks workgroups run only if every producer
+  // workgroup already runs (*started == started_all), else they exit at once.
+  uint32_t* xcd_claim;
+  int32_t base_grid;
+  int32_t late_blocks;
+  const uint32_t* started;
+  uint32_t started_all;
 };
 
 // Arguments of the GEMM+ReduceScatter kernel.
@@ -125,8 +137,6 @@ struct MoeRsArgs {
 // b with b % kXcds == c % kXcds), in order.  So every XCD gets an even share of
 // each readiness window, and the tiles it runs together (the column tiles of
 // one row tile, neighbouring row tiles of one expert) share operands in its L2.
-constexpr int kXcds = 8;
-constexpr int kXcdClaimStride = 16;  // words between the per-XCD claim counters
 constexpr uint32_t kMoeXcdGroup = 4;
 
 // Row tiles in XCD x's list, for n tiles in total.

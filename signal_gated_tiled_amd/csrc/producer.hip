@@ -162,8 +162,10 @@ __device__ __forceinline__ void produce_items(int first, int stride, uint32_t* f
 // release time, then publish its flags.  Every wait is bounded.
 __device__ void release_items(uint32_t* flags, const RelItem* __restrict__ rel, int n_rel,
                               const uint32_t* marks, uint32_t epoch, int withhold_peer, uint64_t* trace_release,
-                              uint64_t timeout_ticks, uint32_t* status) {
+                              uint64_t timeout_ticks, uint32_t* status, uint32_t* started) {
   if (threadIdx.x != 0) return;
+  // counted as running, like the copying workgroups (see produce_items)
+  if (started) __hip_atomic_fetch_add(started, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint64_t t0 = clock_ticks();
   for (int i = 0; i < n_rel; ++i) {
     const RelItem r = rel[i];
@@ -198,7 +200,7 @@ __global__ void __launch_bounds__(kProdThreads) ag_producer_kernel(uint32_t* fla
                                                                    uint32_t* status) {
   const int pwg = (int)gridDim.x - (n_rel > 0 ? 1 : 0);
   if ((int)blockIdx.x >= pwg) {
-    release_items(flags, rel, n_rel, marks, epoch, withhold_peer, trace_release, timeout_ticks, status);
+    release_items(flags, rel, n_rel, marks, epoch, withhold_peer, trace_release, timeout_ticks, status, started);
     return;
   }
   produce_items(blockIdx.x, pwg, flags, items, n_items, tile_bytes, epoch, withhold_peer, trace_release, lead0,

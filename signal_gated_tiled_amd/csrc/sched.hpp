@@ -44,6 +44,16 @@ __host__ __device__ inline void tile_at(int64_t t, int64_t tiles_m, int64_t tile
   *seq_m = grp * kPanelGroup + idx % gm;
 }
 
+// Dynamic claiming in the static schedule's XCD order: with a grid of G
+// workgroups (G % 8 == 0), XCD x runs, round after round, the G / 8
+// consecutive tiles [r G + x G / 8, r G + (x + 1) G / 8).  xcd_seq_tile gives
+// the i-th of them (or -1 past the last of `total` tiles).
+__host__ __device__ inline int64_t xcd_seq_tile(int x, int64_t i, int64_t G, int64_t total) {
+  const int64_t per = G / 8;
+  const int64_t t = (i / per) * G + (int64_t)x * per + i % per;
+  return t < total ? t : -1;
+}
+
 // Workgroup b of a persistent grid of G workgroups is dispatched to XCD b % 8.
 // Renumber so that the workgroups sharing an XCD take consecutive tiles of each
 // round (tiles sharing an A panel then hit the same XCD-private L2).

@@ -84,6 +84,11 @@ sgt_status fail(sgt_status st, const char* fmt, ...) {
   } while (0)
 
 constexpr int kSlots = 4;                 // producer schedule tables in flight
+// Counter words of a context: [0] GEMM+RS reduction claims, [32] AllGather
+// producer workgroups started (cumulative), [64 + 16 x] claim counter of XCD x
+// for the AllGather consumer (cleared by a fill kernel before each launch).
+constexpr int kCounterWords = 512;
+constexpr int kAgStartedWord = 32, kAgClaimWord = 64;
 constexpr int kSdmaMaxUnits = 4096;       // copy-engine copies per call
 constexpr int64_t kSdmaUnitBytes = 4 << 20;  // bytes per copy-engine copy (whole-row signal tiles grouped up to this)
 constexpr int64_t kItemsCap = 1 << 18;    // signal tiles per call
@@ -99,6 +104,7 @@ struct sgt_ctx {
   uint32_t epoch = 0;
   uint32_t* d_status = nullptr;  // 4 words
   uint32_t* d_counters = nullptr;  // work-claim counters, zeroed before each launch that uses them
+  uint32_t ag_prod_started = 0;    // AllGather producer workgroups launched so far (cumulative)
   ProdItem* h_items[kSlots] = {};
   ProdItem* d_items[kSlots] = {};
   uint32_t* h_ranks[kSlots] = {};  // arrival rank of each signal tile (MoE work ordering), pinned host
@@ -614,7 +620,8 @@ void open_gate(void* gate) { hsa_signal_store_screlease(*static_cast<hsa_signal_
 sgt_status ag_sdma_launch(sgt_ctx* ctx, const sgt_opts& o, const AgPlan& p, int W, int64_t K, int esz,
                           const void* const* shards, void* gathered, uint32_t* flags, const ProdItem* items,
                           int n_items, int64_t tile_bytes, uint32_t seg_rows, uint32_t seg_bytes,
-                          uint32_t row_stride, uint64_t* trace_rel, uint32_t e, hipStream_t stream, int* cu_wgs) {
+                          uint32_t row_stride, uint64_t* trace_rel, uint32_t e, hipStream_t stream, int* cu_wgs,
+                          uint32_t* started) {
   sgt_status st = sdma_setup(ctx);
   if (st != SGT_OK) return st;
   const int n_sd = o.sdma_peers > 0 ? std::min(o.sdma_peers, W - 1) : W - 1;
@@ -730,7 +737,7 @@ sgt_status ag_sdma_launch(sgt_ctx* ctx, const sgt_opts& o, const AgPlan& p, int 
   // together hold the CUs a CU producer alone would
   const int pwg = n_cu > 0 ? std::max(1, std::min(default_producer_wgs(o, ctx->n_cu) - 1, n_cu)) : 0;
   HIP_TRY(launch_ag_producer(flags, slot >= 0 ? ctx->d_items[slot] : nullptr, n_cu, tile_bytes, e, o.withhold_peer,
-                             trace_rel, pwg, ctx->prod, nullptr, nullptr, seg_rows, seg_bytes, row_stride,
+                             trace_rel, pwg, ctx->prod, started, nullptr, seg_rows, seg_bytes, row_stride,
                              ctx->d_rel[ss], n_rel, ctx->d_marks, timeout_ticks(o), ctx->d_status));
   if (slot >= 0) {
     HIP_TRY(hipEventRecord(ctx->slot_ev[slot], ctx->prod));
@@ -803,7 +810,8 @@ sgt_status sgt_ctx_create(sgt_ctx** out, int device) {
   chk(hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming), "hipEventCreate");
   chk(hipEventCreateWithFlags(&c->ev_done, hipEventDisableTiming), "hipEventCreate");
   chk(hipMalloc(&c->d_status, 4 * sizeof(uint32_t)), "hipMalloc(status)");
-  chk(hipMalloc(&c->d_counters, 64 * sizeof(uint32_t)), "hipMalloc(counters)");
+  chk(hipMalloc(&c->d_counters, kCounterWords * sizeof(uint32_t)), "hipMalloc(counters)");
+  if (st == SGT_OK) chk(hipMemset(c->d_counters, 0, kCounterWords * sizeof(uint32_t)), "hipMemset(counters)");
   chk(hipMalloc(&c->d_moe, 1024 * sizeof(uint32_t)), "hipMalloc(moe)");
   if (st == SGT_OK) chk(hipMemset(c->d_moe, 0, 1024 * sizeof(uint32_t)), "hipMemset(moe)");
   chk(hipMalloc(&c->d_moe_ranks, kItemsCap * sizeof(uint32_t)), "hipMalloc(moe ranks)");
@@ -944,11 +952,27 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   a.b_layout = o.b_layout; a.out_dtype = o.out_dtype; a.epoch = e; a.timeout_ticks = timeout_ticks(o);
   a.tile_waves = o.tile_waves ? o.tile_waves : 8;
   const int total_tiles = p.tiles_m * p.tiles_n;
+  uint32_t* started = ctx->d_counters + kAgStartedWord;
+  // bf16 tiles are claimed dynamically, XCD by XCD in the order the static
+  // schedule of a `base`-workgroup grid gives them (a grid that is not a
+  // multiple of the XCD count keeps the static schedule); the claim counters
+  // are cleared by a fill kernel on the consumer's stream.
+  auto claim_setup = [&](int base, int late) -> sgt_status {
+    if (o.in_dtype != SGT_BF16 || base % kXcds) return SGT_OK;
+    a.xcd_claim = ctx->d_counters + kAgClaimWord;
+    a.base_grid = base;
+    a.late_blocks = late;
+    a.started = started;
+    a.started_all = ctx->ag_prod_started;
+    HIP_TRY(launch_fill_u32(a.xcd_claim, kXcds * kXcdClaimStride, 0u, stream));
+    return SGT_OK;
+  };
 
   if (o.producer == SGT_PROD_PRESET) {
     HIP_TRY(launch_fill_u32(flags, p.n_flags, e, stream));
     const int grid = std::min(total_tiles, o.consumer_cus > 0 ? o.consumer_cus
                                             : (o.in_dtype == SGT_BF16 ? ctx->n_cu : 4 * ctx->n_cu));
+    if ((st = claim_setup(grid, 0)) != SGT_OK) return st;
     if (N > 0) {
       if ((st = mark(o, 0, stream)) != SGT_OK) return st;
       HIP_TRY(launch_ag_consumer(a, o.in_dtype, grid, stream));
@@ -975,6 +999,7 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
     ctx->slot_used[slot] = true;
     const int grid = std::min(total_tiles, o.consumer_cus > 0 ? o.consumer_cus
                                             : (o.in_dtype == SGT_BF16 ? ctx->n_cu : 4 * ctx->n_cu));
+    if ((st = claim_setup(grid, 0)) != SGT_OK) return st;
     if (N > 0) {
       if ((st = mark(o, 0, stream)) != SGT_OK) return st;
       HIP_TRY(launch_ag_consumer(a, o.in_dtype, grid, stream));
@@ -989,24 +1014,39 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   int prod_wgs = pwg;
   if (o.producer == SGT_PROD_SDMA) {
     if ((st = ag_sdma_launch(ctx, o, p, W, K, esz, A_shards, A_gathered, flags, items, n_items, tile_bytes, seg_rows,
-                             seg_bytes, row_stride, trace_rel, e, stream, &prod_wgs)) != SGT_OK)
+                             seg_bytes, row_stride, trace_rel, e, stream, &prod_wgs, started)) != SGT_OK)
       return st;
   } else {
     HIP_TRY(hipEventRecord(ctx->ev_fork, stream));
     HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
     if ((st = stage_items(ctx, items, n_items, ctx->prod, &slot)) != SGT_OK) return st;
     HIP_TRY(launch_ag_producer(flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
-                               trace_rel, pwg, ctx->prod, nullptr, nullptr, seg_rows, seg_bytes, row_stride));
+                               trace_rel, pwg, ctx->prod, started, nullptr, seg_rows, seg_bytes, row_stride));
     HIP_TRY(hipEventRecord(ctx->slot_ev[slot], ctx->prod));
     ctx->slot_used[slot] = true;
   }
+  ctx->ag_prod_started += (uint32_t)prod_wgs;
   int grid;
-  if (o.in_dtype == SGT_BF16)
-    grid = o.consumer_cus > 0 ? std::min(o.consumer_cus, consumer_beside(ctx, prod_wgs))
-                              : consumer_beside(ctx, prod_wgs);
-  else  // fp32 tiles: small workgroups, two per CU by default (a caller's count is capped there)
+  if (o.in_dtype == SGT_BF16) {
+    // The consumer keeps consumer_beside() workgroups that never yield (an
+    // equal share of every XCD beside the producer's).  With no caller count
+    // it launches one workgroup per CU: the others wait in the dispatcher for
+    // the producer's CUs and, once there, run only if the whole producer is
+    // already running (else they exit and leave the CUs to it), then claim
+    // tiles like the rest.
+    const int keep = consumer_beside(ctx, prod_wgs);
+    if (o.consumer_cus > 0) {
+      grid = std::min(std::min(o.consumer_cus, keep), total_tiles);
+      if ((st = claim_setup(grid, 0)) != SGT_OK) return st;
+    } else {
+      grid = std::min(ctx->n_cu, total_tiles);
+      if ((st = claim_setup(std::min(keep, grid), std::max(0, grid - keep))) != SGT_OK) return st;
+      if (!a.xcd_claim) grid = std::min(grid, keep);   // a static schedule keeps off the producer's CUs
+    }
+  } else {  // fp32 tiles: small workgroups, two per CU by default (a caller's count is capped there)
     grid = o.consumer_cus > 0 ? std::min(o.consumer_cus, 2 * ctx->n_cu) : 2 * ctx->n_cu;
-  grid = std::min(grid, total_tiles);
+    grid = std::min(grid, total_tiles);
+  }
   if (N > 0) {
       if ((st = mark(o, 0, stream)) != SGT_OK) return st;
       HIP_TRY(launch_ag_consumer(a, o.in_dtype, grid, stream));
