@@ -23,6 +23,8 @@ ceilings, and the CPU oracle timed on a bounded sample of rows.
 from __future__ import annotations
 
 import argparse
+import contextlib
+import gc
 import json
 import os
 import statistics
@@ -91,6 +93,21 @@ def _events(n, torch):
     return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
 
 
+LAST_HOST_MS = []
+
+
+@contextlib.contextmanager
+def no_gc():
+    """Python's cyclic garbage collector off inside a timed loop (as timeit does): in a process holding
+    torch's objects one full collection takes tens of milliseconds, which would land inside one call."""
+    gc.collect()
+    gc.disable()
+    try:
+        yield
+    finally:
+        gc.enable()
+
+
 def timed(fn, steps, warmup, torch, ctx):
     """Run fn(i, events) warmup times, then two blocks of `steps` calls.
 
@@ -106,20 +123,27 @@ def timed(fn, steps, warmup, torch, ctx):
     ctx.sync()
     evk = _events(steps, torch)
     torch.cuda.synchronize()
-    for i in range(steps):
-        fn(warmup + i, evk[i])
+    with no_gc():
+        for i in range(steps):
+            fn(warmup + i, evk[i])
     torch.cuda.synchronize()
     ctx.sync()
     kern = [a.elapsed_time(b) for a, b in evk]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    host = [0.0] * steps
     torch.cuda.synchronize()
-    t0.record()
-    for i in range(steps):
-        fn(warmup + steps + i, None)
-    t1.record()
+    with no_gc():
+        t0.record()
+        for i in range(steps):
+            h0 = time.perf_counter()
+            fn(warmup + steps + i, None)
+            host[i] = time.perf_counter() - h0
+        t1.record()
     torch.cuda.synchronize()
     ctx.sync()
     step_ms = t0.elapsed_time(t1) / steps
+    # host time of each call in the step-timed block (ms): a call whose host side stalls shows here
+    LAST_HOST_MS[:] = [h * 1e3 for h in host]
     return step_ms, statistics.mean(kern), kern
 
 
@@ -131,10 +155,11 @@ def timed_blocks(fn, steps, warmup, torch, ctx, blocks=3):
     for b in range(blocks - 1):
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        t0.record()
-        for i in range(steps):
-            fn(warmup + (b + 2) * steps + i, None)
-        t1.record()
+        with no_gc():
+            t0.record()
+            for i in range(steps):
+                fn(warmup + (b + 2) * steps + i, None)
+            t1.record()
         torch.cuda.synchronize()
         ctx.sync()
         steps_ms.append(t0.elapsed_time(t1) / steps)
@@ -155,9 +180,10 @@ def pairs(fn_a, fn_b, n, torch, ctx):
     between two blocks of runs."""
     ev = _events(2 * n, torch)
     torch.cuda.synchronize()
-    for i in range(n):
-        fn_a(i, ev[2 * i])
-        fn_b(i, ev[2 * i + 1])
+    with no_gc():
+        for i in range(n):
+            fn_a(i, ev[2 * i])
+            fn_b(i, ev[2 * i + 1])
     torch.cuda.synchronize()
     ctx.sync()
     return [a.elapsed_time(b) for a, b in ev[0::2]], [a.elapsed_time(b) for a, b in ev[1::2]]
@@ -908,9 +934,12 @@ def main():
         return
     over_ms, over_kern_ms, over_list = timed(lambda i, ev: ag("cu", arrival_seed=i + 1, **link)(i, ev),
                                              args.steps, args.warmup, torch, ctx)
+    over_host = spread(LAST_HOST_MS) if LAST_HOST_MS else None
+    over_host_max = max(LAST_HOST_MS) if LAST_HOST_MS else None
     if args.headline_only:
         print(json.dumps({"workload": w.name, "overlapped_ms": over_ms, "consumer_kernel_ms": over_kern_ms,
-                          "tflops": flops / (over_ms * 1e-3) / 1e12}), flush=True)
+                          "tflops": flops / (over_ms * 1e-3) / 1e12,
+                          "host_call_ms": [round(h, 3) for h in LAST_HOST_MS]}), flush=True)
         ctx.close()
         return
     if args.engines_only:
@@ -1012,6 +1041,8 @@ def main():
         "release_trace": rel,
         "overlapped_ms": over_ms,
         "overlapped_kernel_ms": spread(over_list),
+        "overlapped_host_call_ms": over_host,
+        "overlapped_host_call_max_ms": over_host_max,
         "gemm_alone_ms": alone_ms,
         "gemm_alone_tflops": flops / (alone_ms * 1e-3) / 1e12,
         "gemm_alone_kernel_ms": alone_kern_ms,

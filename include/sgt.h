@@ -107,10 +107,13 @@ typedef struct sgt_opts {
   int32_t order;         /* enum sgt_order                                                      */
   int32_t flag_rows;     /* rows per AllGather signal tile; 0 = library default                 */
   int32_t producer_cus;  /* workgroups of the producer kernel; 0 = library default              */
-  int32_t consumer_cus;  /* workgroups of the persistent consumer; 0 = one per CU, less the
-                            producer's CUs beside an overlapped producer (its workgroup count
-                            rounded up to a multiple of CUs / 8, an equal share of every XCD);
-                            a caller's count is capped there, so the producer can always start */
+  int32_t consumer_cus;  /* workgroups of the persistent consumer; 0 = one per CU.  Beside an
+                            overlapped producer at most the CUs less the producer's share (its
+                            workgroup count rounded up to a multiple of CUs / 8, an equal share
+                            of every XCD) run unconditionally, and a caller's count is capped
+                            there, so the producer can always start; with no caller count the
+                            bf16 AllGather and MoE consumers launch one per CU and run the rest
+                            only if every producer workgroup is already running              */
   int32_t blocking;      /* nonzero: synchronize and return the device status                   */
   double peer_gbps;      /* simulated link rate per peer in GB/s; 0 = unthrottled               */
   double jitter_us;      /* each remote tile's release is delayed by U[0, jitter_us]            */

@@ -1043,8 +1043,10 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
       if ((st = claim_setup(std::min(keep, grid), std::max(0, grid - keep))) != SGT_OK) return st;
       if (!a.xcd_claim) grid = std::min(grid, keep);   // a static schedule keeps off the producer's CUs
     }
-  } else {  // fp32 tiles: small workgroups, two per CU by default (a caller's count is capped there)
-    grid = o.consumer_cus > 0 ? std::min(o.consumer_cus, 2 * ctx->n_cu) : 2 * ctx->n_cu;
+  } else {  // fp32 tiles: at most one workgroup per CU beside the producer's share, so even at one resident
+            // workgroup per CU the waiting consumers leave every XCD the CUs the producer needs
+    const int keep = consumer_beside(ctx, prod_wgs);
+    grid = o.consumer_cus > 0 ? std::min(o.consumer_cus, keep) : keep;
     grid = std::min(grid, total_tiles);
   }
   if (N > 0) {

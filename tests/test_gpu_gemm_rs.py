@@ -89,6 +89,20 @@ def test_gemm_rs_bits_repeat(ctx):
     assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
 
 
+def test_gemm_rs_grid_request_above_cu_count(ctx, orc):
+    """A consumer_cus of twice the CU count is capped at one workgroup per CU (a reduction item waits on GEMM
+    tiles other workgroups own, so every workgroup must be resident): the call succeeds with the bits of the
+    default grid.  320 GEMM tiles and 2560 reduction items, more than 2 x 256 work items."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    w = I.RSWorkload("t", W=8, M=8192, K=128, N=2560, seed_index=31)
+    A, B, parts = I.make_rs(w, B_layout="nk")
+    a = run_rs(ctx, A, B, parts, 6, b_layout="nk")
+    b = run_rs(ctx, A, B, parts, 6, b_layout="nk", consumer_cus=2 * n_cu)
+    assert np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32))
+    assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    assert_close(b[1], orc.gemm_rs(A, B, parts, 6, b_layout="nk"), what="C_shard", **TOL_BF16)
+
+
 @pytest.mark.parametrize("rs_tile", [128, 64])
 def test_gemm_rs_trace_fills_exactly_its_words(ctx, rs_tile):
     """A traced call writes every one of sgt_rs_trace_words' words (one record per GEMM tile and reduction
