@@ -820,6 +820,85 @@ def kernel_pass(name, ctx, up, args, torch, sgt, I, lay):
     print(json.dumps(res), flush=True)
 
 
+def bench_gemm_rs(ctx, up, args, torch, sgt, I, lay, rank):
+    """GEMM + ReduceScatter on the Qwen-32B MLP share (M 8192, K 3200, N 5120, W 8): the call with the peers'
+    partials resident, the same GEMM alone, interleaved pairs, the reduction window from the kernel's own
+    stamps, and the call with the peers paced at 50 GB/s per link."""
+    import numpy as np
+    dev = "cuda:0"
+    r = I.GEMM_RS
+    A_h, Brs_h, parts_h = I.make_rs(r, B_layout=lay)
+    A = up(A_h)
+    Brs = up(Brs_h)
+    parts = [up(p) if q != rank else None for q, p in enumerate(parts_h)]
+    ng, npf = sgt.rs_flag_count(r.W, r.M, r.N)
+    P = torch.empty((r.M, r.N), dtype=torch.float32, device=dev)
+    Cs = torch.empty((r.M // r.W, r.N), dtype=torch.float32, device=dev)
+    gf = torch.zeros(ng, dtype=torch.int32, device=dev)
+    pf = torch.zeros(npf, dtype=torch.int32, device=dev)
+    rs_ms, rs_kern_ms, _ = timed(lambda i, ev: ctx.gemm_rs(A, Brs, parts, P, Cs, gf, pf, rank=rank, b_layout=lay,
+                                                           consumer_events=ev), args.steps, args.warmup, torch,
+                                 ctx)
+    # the same GEMM alone (no signalling epilogue, no reduction): the AllGather consumer on resident data
+    A_shards = list(A.view(r.W, r.M // r.W, r.K).unbind(0))
+    fl2 = torch.zeros(sgt.ag_flag_count(r.W, r.M, r.K), dtype=torch.int32, device=dev)
+    Cg = torch.empty((r.M, r.N), dtype=torch.float32, device=dev)
+    A_parts = [a.contiguous() for a in A_shards]
+    g_ms, _, _ = timed(lambda i, ev: ctx.ag_gemm(A_parts, Brs, A, Cg, fl2, rank=rank, b_layout=lay,
+                                                 producer="preset", consumer_events=ev), args.steps,
+                       args.warmup, torch, ctx)
+    # interleaved pairs: GEMM+RS call, then the same GEMM alone
+    rs_l, g_l = pairs(lambda i, ev: ctx.gemm_rs(A, Brs, parts, P, Cs, gf, pf, rank=rank, b_layout=lay,
+                                                consumer_events=ev),
+                      lambda i, ev: ctx.ag_gemm(A_parts, Brs, A, Cg, fl2, rank=rank, b_layout=lay,
+                                                producer="preset", consumer_events=ev), args.steps, torch, ctx)
+    rs_pair, g_pair = statistics.median(rs_l), statistics.median(g_l)
+    red_bytes = (r.M // r.W) * r.N * 4 * (r.W + 1)   # read local block + W-1 peers, write C_shard
+    # reduction window from the kernel's own stamps (100 MHz clock): first reduction start to last end
+    nw = sgt.rs_trace_words(r.W, r.M, r.N)
+    tr = torch.zeros(nw, dtype=torch.int64, device=dev)
+    ctx.gemm_rs(A, Brs, parts, P, Cs, gf, pf, rank=rank, b_layout=lay, trace=tr.data_ptr(), blocking=True)
+    t = tr.cpu().numpy().view(np.uint64).reshape(-1, 3)
+    n_g = (r.W * (-(-(r.M // r.W) // 256))) * (-(-r.N // 256))
+    red_t, gem_t = t[n_g:].astype(np.int64), t[:n_g].astype(np.int64)
+    red_win_us = (red_t[:, 1].max() - red_t[:, 0].min()) / 100.0
+    red_item_us = (red_t[:, 1] - red_t[:, 0]) / 100.0
+    # paced peers at 50 GB/s per link (the comm-bound variant): peers' blocks copied into an inbox
+    gbps_rs = 50.0
+    inbox = [torch.empty_like(p) if p is not None else None for p in parts]
+    pc_ms, pc_k, pc_l = timed(lambda i, ev: ctx.gemm_rs_paced(A, Brs, parts, inbox, P, Cs, gf, pf, rank=rank,
+                                                              b_layout=lay, peer_gbps=gbps_rs,
+                                                              consumer_events=ev),
+                              max(4, args.steps // 2), 2, torch, ctx)
+    res = {
+        "workload": r.name, "M": r.M, "K": r.K, "N": r.N, "W": r.W,
+        "step_ms": rs_ms, "kernel_ms": rs_kern_ms,
+        "tflops": r.flops / (rs_ms * 1e-3) / 1e12,
+        "pct_peak": 100.0 * r.flops / (rs_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "gemm_alone_ms": g_ms,
+        "overlap_efficiency": g_pair / rs_pair,
+        "overlap_efficiency_note": "median kernel time of the GEMM alone over that of GEMM+RS, interleaved pairs",
+        "overlap_efficiency_blocks": g_ms / rs_ms,
+        "pairs_kernel_ms": spread(rs_l), "pairs_gemm_alone_kernel_ms": spread(g_l),
+        "reduction_algorithmic_bytes": red_bytes,
+        "reduction_window_us": float(red_win_us),
+        "reduction_window_gbs": red_bytes / (red_win_us * 1e-6) / 1e9,
+        "reduction_item_us": spread(red_item_us.tolist()),
+        "reduction_note": "window = first reduction-item start to last end in one traced call (the items run "
+                          "while other workgroups finish GEMM tiles, so the rate is a lower bound); an item is "
+                          "a 32-row band of a 128 x 128 signal tile; its stamps cover its stream (the claim and "
+                          "the flag peek of the next item overlap it)",
+        "gemm_tiles_end_us": float((gem_t[:, 1].max() - gem_t[:, 0].min()) / 100.0),
+        "paced_50gbps": {"peer_gbps": gbps_rs, "step_ms": pc_ms, "kernel_ms": spread(pc_l),
+                         "tflops": r.flops / (pc_ms * 1e-3) / 1e12,
+                         "link_floor_us": (r.M // r.W) * r.N * 4 / (gbps_rs * 1e9) * 1e6},
+    }
+    assert torch.equal(inbox[(rank + 1) % r.W], parts[(rank + 1) % r.W]), "paced inbox mismatch"
+    del inbox, tr
+    del A, Brs, parts, P, Cs, Cg
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -828,6 +907,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rs", action="store_true", help="skip the GEMM+ReduceScatter workload")
+    ap.add_argument("--rs-only", action="store_true", help="only the GEMM+ReduceScatter workload")
     ap.add_argument("--no-moe", action="store_true", help="skip the MoE AllGather + grouped GEMM workload")
     ap.add_argument("--no-ll", action="store_true", help="skip the low-latency AllGather comparison")
     ap.add_argument("--ll-only", action="store_true", help="only the low-latency AllGather comparison")
@@ -886,6 +966,10 @@ def main():
             print(json.dumps({"moe_ag_grouped": moe}), flush=True)
             print(json.dumps({"moe_gemm_rs": bench_moe_rs(c, up, args, torch, sgt, I, args.b_layout, tables)}),
                   flush=True)
+        return
+    if args.rs_only:
+        with sgt.Context(0) as c:
+            print(json.dumps({"gemm_rs": bench_gemm_rs(c, up, args, torch, sgt, I, args.b_layout, 0)}), flush=True)
         return
     if args.a2a_only:
         with sgt.Context(0) as c:
@@ -1086,75 +1170,7 @@ def main():
     }
 
     if not args.no_rs:
-        r = I.GEMM_RS
-        A_h, Brs_h, parts_h = I.make_rs(r, B_layout=lay)
-        A = up(A_h)
-        Brs = up(Brs_h)
-        parts = [up(p) if q != rank else None for q, p in enumerate(parts_h)]
-        ng, npf = sgt.rs_flag_count(r.W, r.M, r.N)
-        P = torch.empty((r.M, r.N), dtype=torch.float32, device=dev)
-        Cs = torch.empty((r.M // r.W, r.N), dtype=torch.float32, device=dev)
-        gf = torch.zeros(ng, dtype=torch.int32, device=dev)
-        pf = torch.zeros(npf, dtype=torch.int32, device=dev)
-        rs_ms, rs_kern_ms, _ = timed(lambda i, ev: ctx.gemm_rs(A, Brs, parts, P, Cs, gf, pf, rank=rank, b_layout=lay,
-                                                               consumer_events=ev), args.steps, args.warmup, torch,
-                                     ctx)
-        # the same GEMM alone (no signalling epilogue, no reduction): the AllGather consumer on resident data
-        A_shards = list(A.view(r.W, r.M // r.W, r.K).unbind(0))
-        fl2 = torch.zeros(sgt.ag_flag_count(r.W, r.M, r.K), dtype=torch.int32, device=dev)
-        Cg = torch.empty((r.M, r.N), dtype=torch.float32, device=dev)
-        A_parts = [a.contiguous() for a in A_shards]
-        g_ms, _, _ = timed(lambda i, ev: ctx.ag_gemm(A_parts, Brs, A, Cg, fl2, rank=rank, b_layout=lay,
-                                                     producer="preset", consumer_events=ev), args.steps,
-                           args.warmup, torch, ctx)
-        # interleaved pairs: GEMM+RS call, then the same GEMM alone
-        rs_l, g_l = pairs(lambda i, ev: ctx.gemm_rs(A, Brs, parts, P, Cs, gf, pf, rank=rank, b_layout=lay,
-                                                    consumer_events=ev),
-                          lambda i, ev: ctx.ag_gemm(A_parts, Brs, A, Cg, fl2, rank=rank, b_layout=lay,
-                                                    producer="preset", consumer_events=ev), args.steps, torch, ctx)
-        rs_pair, g_pair = statistics.median(rs_l), statistics.median(g_l)
-        red_bytes = (r.M // r.W) * r.N * 4 * (r.W + 1)   # read local block + W-1 peers, write C_shard
-        # reduction window from the kernel's own stamps (100 MHz clock): first reduction start to last end
-        nw = sgt.rs_trace_words(r.W, r.M, r.N)
-        tr = torch.zeros(nw, dtype=torch.int64, device=dev)
-        ctx.gemm_rs(A, Brs, parts, P, Cs, gf, pf, rank=rank, b_layout=lay, trace=tr.data_ptr(), blocking=True)
-        t = tr.cpu().numpy().view(np.uint64).reshape(-1, 3)
-        n_g = (r.W * (-(-(r.M // r.W) // 256))) * (-(-r.N // 256))
-        red_t, gem_t = t[n_g:].astype(np.int64), t[:n_g].astype(np.int64)
-        red_win_us = (red_t[:, 1].max() - red_t[:, 0].min()) / 100.0
-        red_item_us = (red_t[:, 1] - red_t[:, 0]) / 100.0
-        # paced peers at 50 GB/s per link (the comm-bound variant): peers' blocks copied into an inbox
-        gbps_rs = 50.0
-        inbox = [torch.empty_like(p) if p is not None else None for p in parts]
-        pc_ms, pc_k, pc_l = timed(lambda i, ev: ctx.gemm_rs_paced(A, Brs, parts, inbox, P, Cs, gf, pf, rank=rank,
-                                                                  b_layout=lay, peer_gbps=gbps_rs,
-                                                                  consumer_events=ev),
-                                  max(4, args.steps // 2), 2, torch, ctx)
-        detail["gemm_rs"] = {
-            "workload": r.name, "M": r.M, "K": r.K, "N": r.N, "W": r.W,
-            "step_ms": rs_ms, "kernel_ms": rs_kern_ms,
-            "tflops": r.flops / (rs_ms * 1e-3) / 1e12,
-            "pct_peak": 100.0 * r.flops / (rs_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-            "gemm_alone_ms": g_ms,
-            "overlap_efficiency": g_pair / rs_pair,
-            "overlap_efficiency_note": "median kernel time of the GEMM alone over that of GEMM+RS, interleaved pairs",
-            "overlap_efficiency_blocks": g_ms / rs_ms,
-            "pairs_kernel_ms": spread(rs_l), "pairs_gemm_alone_kernel_ms": spread(g_l),
-            "reduction_algorithmic_bytes": red_bytes,
-            "reduction_window_us": float(red_win_us),
-            "reduction_window_gbs": red_bytes / (red_win_us * 1e-6) / 1e9,
-            "reduction_item_us": spread(red_item_us.tolist()),
-            "reduction_note": "window = first reduction-item start to last end in one traced call (the items run "
-                              "while other workgroups finish GEMM tiles, so the rate is a lower bound); an item is "
-                              "a 32-row band of a 128 x 128 signal tile, its time includes its flag wait",
-            "gemm_tiles_end_us": float((gem_t[:, 1].max() - gem_t[:, 0].min()) / 100.0),
-            "paced_50gbps": {"peer_gbps": gbps_rs, "step_ms": pc_ms, "kernel_ms": spread(pc_l),
-                             "tflops": r.flops / (pc_ms * 1e-3) / 1e12,
-                             "link_floor_us": (r.M // r.W) * r.N * 4 / (gbps_rs * 1e9) * 1e6},
-        }
-        assert torch.equal(inbox[(rank + 1) % r.W], parts[(rank + 1) % r.W]), "paced inbox mismatch"
-        del inbox, tr
-        del A, Brs, parts, P, Cs, Cg
+        detail["gemm_rs"] = bench_gemm_rs(ctx, up, args, torch, sgt, I, lay, rank)
 
     detail["ag_other_workloads"] = bench_ag_other(ctx, up, args, torch, sgt, I, lay)
     if not args.no_ll:

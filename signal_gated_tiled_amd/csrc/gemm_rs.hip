@@ -87,24 +87,58 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) gemm_rs_kernel(RsArgs a
       a.trace[3 * t + 2] = blockIdx.x;
     }
   }
-  // Reduction tiles: claimed one at a time by whichever workgroups finish their
+  // Reduction items: claimed one at a time by whichever workgroups finish their
   // GEMM tiles first (the ones with one tile fewer in the last partial round).
+  // One item ahead: while the workgroup streams item j, thread 0 claims the
+  // item after the next one and wave 0 peeks at the next one's flags, so the
+  // round trips of the claim and of the flags overlap the stream.
+  if (threadIdx.x == 0) claimed = (int)atomicAdd(a.red_counter, 1u);
+  __syncthreads();
+  int j = claimed;
+  __syncthreads();
+  if (j >= a.n_red_items) return;
+  if (threadIdx.x < 64) {
+    const RedFlag rf = red_flag(a, j, threadIdx.x);
+    const bool good = red_wait(a, rf, rf.f ? flag_peek(rf.f) : 0u);
+    if (threadIdx.x == 0) {
+      ok = good ? 1 : 0;
+      claimed = (int)atomicAdd(a.red_counter, 1u);
+    }
+  }
+  __syncthreads();
+  if (!ok) return;
+  int jn = claimed;  // claimed, flags not yet seen
+  __syncthreads();
   while (true) {
-    if (threadIdx.x == 0) claimed = (int)atomicAdd(a.red_counter, 1u);
-    __syncthreads();
-    const int j = claimed;
-    __syncthreads();
-    if (j >= a.n_red_items) break;
+    RedFlag rf{nullptr, 0};
+    uint32_t v = 0;
+    int jnn = 0;
+    if (jn < a.n_red_items && threadIdx.x < 64) {
+      rf = red_flag(a, jn, threadIdx.x);
+      if (rf.f) v = flag_peek(rf.f);
+      if (threadIdx.x == 0) jnn = (int)atomicAdd(a.red_counter, 1u);
+    }
     const uint64_t t_start = clock_ticks();
-    do_reduce_item(a, j, &ok);
-    if (!ok) return;
-    __syncthreads();
+    red_stream(a, j);
     if (a.trace && threadIdx.x == 0) {
       const int t = a.n_gemm_tiles + j;
       a.trace[3 * t + 0] = t_start;
       a.trace[3 * t + 1] = clock_ticks();
       a.trace[3 * t + 2] = blockIdx.x;
     }
+    if (jn >= a.n_red_items) break;
+    if (threadIdx.x < 64) {
+      const bool good = red_wait(a, rf, v);
+      if (threadIdx.x == 0) {
+        ok = good ? 1 : 0;
+        claimed = jnn;
+      }
+    }
+    __syncthreads();
+    if (!ok) return;
+    j = jn;
+    jn = claimed;
+    __syncthreads();  // every thread has read `claimed` before thread 0 writes it again
   }
 }
 

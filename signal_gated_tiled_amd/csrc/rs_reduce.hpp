@@ -22,41 +22,53 @@ namespace sgt {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ inline void do_reduce_item(const RsArgs& a, int j, int* ok) {
-  // item j: row band `rband` of signal tile jt (red_split bands per tile)
-  const int jt = j / a.red_split, rband = j % a.red_split;
+// The flag lane `lane` of wave 0 watches for item j: lane `rank` the GEMM flag
+// of the local tile (in gflags), lane p < W peer p's flag of the tile (in
+// pflags), the other lanes none.  `idx` is the flag's index for a timeout
+// report.
+struct RedFlag {
+  const uint32_t* f;
+  int64_t idx;
+};
+
+__device__ inline RedFlag red_flag(const RsArgs& a, int j, int lane) {
+  const int jt = j / a.red_split;
   const int ti = jt / a.rs_tn, tj = jt % a.rs_tn;
   const int64_t gtn = (a.N + a.rs_tile - 1) / a.rs_tile;
   const int64_t row0 = (int64_t)a.rank * a.block_rows + (int64_t)ti * a.rs_tile;  // row in P
-  if (threadIdx.x < 64) {
-    // One lane per contribution, all polled at once: lane `rank` waits on the
-    // GEMM flag of the local tile, lane p on peer p's flag of the tile.
-    const int lane = threadIdx.x;
-    const int64_t per = (int64_t)a.rs_tm * a.rs_tn;
-    const int64_t gidx = (row0 / a.rs_tile) * gtn + tj, pidx = lane * per + jt;
-    const uint32_t* f = lane < a.W ? (lane == a.rank ? a.gflags + gidx : a.pflags + pidx) : nullptr;
-    bool mine = f == nullptr;
-    uint32_t v = 0;
-    bool good = true;
-    const uint64_t t0 = clock_ticks();
-    while (true) {
-      if (!mine) {
-        v = flag_peek(f);
-        mine = flag_is_set(v, a.epoch);
-      }
-      if (__all(mine)) break;
-      if (clock_ticks() - t0 > a.timeout_ticks) {  // the clock is a scalar read: uniform over the wave
-        if (!mine) report_timeout(a.status, lane == a.rank ? gidx : pidx, v, a.epoch);
-        good = false;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
+  const int64_t per = (int64_t)a.rs_tm * a.rs_tn;
+  const int64_t gidx = (row0 / a.rs_tile) * gtn + tj, pidx = lane * per + jt;
+  if (lane >= a.W) return RedFlag{nullptr, 0};
+  return lane == a.rank ? RedFlag{a.gflags + gidx, gidx} : RedFlag{a.pflags + pidx, pidx};
+}
+
+// Wave 0: wait until every flag of an item is set, given `v`, the value of a
+// peek already taken (so a peek issued early costs no round trip here); then
+// the acquire.  False after a timeout (recorded in the status word).
+__device__ inline bool red_wait(const RsArgs& a, RedFlag rf, uint32_t v) {
+  bool mine = rf.f == nullptr || flag_is_set(v, a.epoch);
+  const uint64_t t0 = clock_ticks();
+  while (!__all(mine)) {
+    if (clock_ticks() - t0 > a.timeout_ticks) {  // the clock is a scalar read: uniform over the wave
+      if (!mine) report_timeout(a.status, rf.idx, v, a.epoch);
+      return false;
     }
-    if (good) acquire_agent();
-    if (lane == 0) *ok = good ? 1 : 0;
+    __builtin_amdgcn_s_sleep(1);
+    if (!mine) {
+      v = flag_peek(rf.f);
+      mine = flag_is_set(v, a.epoch);
+    }
   }
-  __syncthreads();
-  if (!*ok) return;
+  acquire_agent();
+  return true;
+}
+
+// The workgroup's part of item j once its flags are in: row band j % red_split
+// of signal tile j / red_split, C_shard = P[local] + the peers' partials.
+__device__ inline void red_stream(const RsArgs& a, int j) {
+  const int jt = j / a.red_split, rband = j % a.red_split;
+  const int ti = jt / a.rs_tn, tj = jt % a.rs_tn;
+  const int64_t row0 = (int64_t)a.rank * a.block_rows + (int64_t)ti * a.rs_tile;  // row in P
   // float4 columns: rs_tile / 4 per row; a pass of the workgroup covers
   // blockDim / (rs_tile / 4) rows.  Four passes are issued together so each
   // thread has 4 x W loads in flight (the reduction is bound by HBM latency
@@ -100,6 +112,19 @@ __device__ inline void do_reduce_item(const RsArgs& a, int j, int* ok) {
     for (int u = 0; u < R; ++u)
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, s[u]), rC, off[u], 0, kCpolNt);
   }
+}
+
+// Item j, whole: wave 0 polls the item's W flags at once (one lane per
+// contribution), then the workgroup streams the band.  *ok = 0 after a timeout.
+__device__ inline void do_reduce_item(const RsArgs& a, int j, int* ok) {
+  if (threadIdx.x < 64) {
+    const RedFlag rf = red_flag(a, j, threadIdx.x);
+    const bool good = red_wait(a, rf, rf.f ? flag_peek(rf.f) : 0u);
+    if (threadIdx.x == 0) *ok = good ? 1 : 0;
+  }
+  __syncthreads();
+  if (!*ok) return;
+  red_stream(a, j);
 }
 
 }  // namespace sgt
