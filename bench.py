@@ -446,6 +446,24 @@ def bench_ll(ctx, up, args, torch, sgt, I):
         row["best"] = {k: {"chunk_kib": v[0], "workgroups_each_side": v[1], "first_write_to_last_seen_us": v[2],
                            "chunk_latency_median_us": v[3], "call_us": v[4]} for k, v in best.items()}
         out["ll_ag_decode_%dtok" % tokens] = row
+    # where LL stops paying: per token count, each method at its best chunk and grid (unthrottled links)
+    cross = {}
+    for key, row in out.items():
+        b = row.get("best", {})
+        if "ll_unthrottled" in b and "flag_unthrottled" in b:
+            cross[row["tokens_per_rank"]] = (b["ll_unthrottled"]["first_write_to_last_seen_us"],
+                                             b["flag_unthrottled"]["first_write_to_last_seen_us"])
+    up_to = 0   # the largest size up to which LL wins at every measured size
+    for tk, (l_us, f_us) in sorted(cross.items()):
+        if l_us >= f_us:
+            break
+        up_to = tk
+    out["crossover"] = {
+        "per_tokens_per_rank": {str(tk): {"ll_us": v[0], "flag_us": v[1]} for tk, v in sorted(cross.items())},
+        "ll_faster_up_to_tokens_per_rank": up_to,
+        "note": "first write to last chunk seen, in-kernel; above this size the flag-based AllGather is the one "
+                "to use",
+    }
     out["note"] = ("LL packets carry their epoch, so the receiver reads data and arrival in one load; the flag path "
                    "copies, waits for the stores' acknowledgement, publishes a flag, and the receiver polls it. "
                    "LL moves twice the bytes on the link and unpacks on the receiver. call_us is host-bound "
@@ -1226,6 +1244,8 @@ def main():
                       "hbm_frac": round(rs["reduction_window_gbs"] / PEAK_HBM_GBS, 4) if rs else None,
                       "window_us": round(rs["reduction_window_us"], 1) if rs else None,
                       "step_ms": round(rs["step_ms"], 4) if rs else None},
+        "ll_allgather": {"ll_faster_up_to_tokens_per_rank":
+                         detail.get("ll_allgather", {}).get("crossover", {}).get("ll_faster_up_to_tokens_per_rank")},
         "cpu_baseline": cpu,
         "detail_file": os.path.relpath(detail_path, ROOT) if detail_path else None,
     }

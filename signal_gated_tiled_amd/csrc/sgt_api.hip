@@ -314,6 +314,20 @@ ProdItem sched_item(int64_t tile, int peer, double release) {
   return it;
 }
 
+// The k-th signal tile a link delivers, in link order.  Whole-row signal tiles
+// go in order.  K-chunked ones go two panels at a time, chunk-major within the
+// pair (panel 0 chunk 0, panel 1 chunk 0, panel 0 chunk 1, ...): two panels'
+// tiles can start together, and each panel's chunks land at half the link
+// rate, near the rate at which a tile computes them, so a panel's tiles spend
+// less time waiting on its last chunks than when it arrives in one burst.
+int64_t interleaved_chunk(const AgPlan& p, int64_t k) {
+  if (p.n_kc <= 0) return k;
+  const int64_t per_pair = 2 * (int64_t)p.n_kc, panels = p.tiles_per_shard / p.n_kc;
+  const int64_t j0 = 2 * (k / per_pair), within = k % per_pair;
+  const int64_t np = panels - j0 < 2 ? panels - j0 : 2;  // the last panel of an odd count goes alone
+  return (j0 + within % np) * p.n_kc + within / np;
+}
+
 int build_schedule(const AgPlan& p, int W, int rank, int64_t K, int esz, const sgt_opts& o,
                    const void* const* shards, void* gathered, ProdItem* items, bool local_first = false,
                    uint32_t* ranks = nullptr) {
@@ -344,7 +358,7 @@ int build_schedule(const AgPlan& p, int W, int rank, int64_t K, int esz, const s
     std::vector<std::vector<int64_t>> order((size_t)W - 1, std::vector<int64_t>((size_t)tps));
     for (int d = 1; d < W; ++d) {
       std::vector<int64_t>& od = order[(size_t)d - 1];
-      for (int64_t t = 0; t < tps; ++t) od[(size_t)t] = t;
+      for (int64_t t = 0; t < tps; ++t) od[(size_t)t] = interleaved_chunk(p, t);
       if (o.arrival_order == 1) shuffle(od, s);
     }
     const bool mesh = o.order == SGT_ORDER_MESH;
