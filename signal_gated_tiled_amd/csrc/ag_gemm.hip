@@ -190,6 +190,7 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) ag_consumer_bf16(AgArgs
     store_tile<kW, kOutBf16>(a.C, a.M, a.N, m0, n0, acc);
     if (a.trace && threadIdx.x == 0) a.trace[tile_id * 4 + 2] = clock_ticks();
   }
+  wait_producer_done(a.prod_done, a.prod_done_all, a.timeout_ticks, a.status);
 }
 
 // fp32 path: 64 x 64 tiles, BK = 16, each thread a 4 x 4 block of outputs.

@@ -73,6 +73,12 @@ struct AgArgs {
   int32_t late_blocks;
   const uint32_t* started;
   uint32_t started_all;
+  // overlapped call (prod_done != null): before it exits, each workgroup that
+  // took work waits until the producer workgroups finished so far (cumulative)
+  // reach prod_done_all, so the caller's stream is ordered after the whole
+  // AllGather without a cross-stream event wait
+  const uint32_t* prod_done;
+  uint32_t prod_done_all;
 };
 
 // Arguments of the GEMM+ReduceScatter kernel.
@@ -199,6 +205,8 @@ struct MoeArgs {
   const uint32_t* started;    // producer workgroups started so far (cumulative over calls), or null
   uint32_t started_all;       // its value once every producer workgroup of this call runs
   int32_t late_blocks;        // the last late_blocks workgroups run only when started == started_all
+  const uint32_t* prod_done;  // as in AgArgs: the producer's finished count to wait for before exit, or null
+  uint32_t prod_done_all;
   int32_t E, flag_rows, tiles_n;
   uint32_t epoch;
   uint64_t timeout_ticks;

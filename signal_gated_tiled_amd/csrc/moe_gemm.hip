@@ -164,6 +164,7 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) moe_consumer_bf16(MoeAr
       moe_tile<kW, 128, kBNK, kOutBf16>(a, tok, rows_valid, e, r0, n0, sA0, sB0, sA1, sB1);
     if (a.trace && threadIdx.x == 0) a.trace[item * 4 + 2] = clock_ticks();
   }
+  wait_producer_done(a.prod_done, a.prod_done_all, a.timeout_ticks, a.status);
 }
 
 }  // namespace

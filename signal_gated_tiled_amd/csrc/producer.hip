@@ -197,7 +197,7 @@ __global__ void __launch_bounds__(kProdThreads) ag_producer_kernel(uint32_t* fla
                                                                    uint32_t seg_bytes, uint32_t row_stride,
                                                                    const RelItem* __restrict__ rel, int n_rel,
                                                                    const uint32_t* marks, uint64_t timeout_ticks,
-                                                                   uint32_t* status) {
+                                                                   uint32_t* status, uint32_t* finished) {
   const int pwg = (int)gridDim.x - (n_rel > 0 ? 1 : 0);
   if ((int)blockIdx.x >= pwg) {
     release_items(flags, rel, n_rel, marks, epoch, withhold_peer, trace_release, timeout_ticks, status, started);
@@ -205,6 +205,7 @@ __global__ void __launch_bounds__(kProdThreads) ag_producer_kernel(uint32_t* fla
   }
   produce_items(blockIdx.x, pwg, flags, items, n_items, tile_bytes, epoch, withhold_peer, trace_release, lead0,
                 started, trace_issue, seg_rows, seg_bytes, row_stride);
+  if (finished) count_finished(finished);
 }
 
 // Stand-alone flag-based AllGather in one launch: workgroups [0, n_prod_blocks)
@@ -264,7 +265,7 @@ hipError_t launch_ag_producer(uint32_t* flags, const ProdItem* items, int n_item
                               int64_t tile_bytes, uint32_t epoch, int withhold_peer, uint64_t* trace_release, int grid,
                               hipStream_t stream, uint32_t* started, uint64_t* trace_issue, uint32_t seg_rows,
                               uint32_t seg_bytes, uint32_t row_stride, const RelItem* rel, int n_rel,
-                              const uint32_t* marks, uint64_t timeout_ticks, uint32_t* status) {
+                              const uint32_t* marks, uint64_t timeout_ticks, uint32_t* status, uint32_t* finished) {
   if (n_items <= 0 && n_rel <= 0) return hipSuccess;
   if (grid > n_items) grid = n_items > 0 ? n_items : 0;
   if (n_rel > 0) grid += 1;  // the releaser
@@ -272,7 +273,7 @@ hipError_t launch_ag_producer(uint32_t* flags, const ProdItem* items, int n_item
   const uint64_t lead0 = (uint64_t)(tile_bytes / 160) + 100;
   hipLaunchKernelGGL(ag_producer_kernel, dim3(grid), dim3(kProdThreads), 0, stream, flags, items, n_items, tile_bytes,
                      epoch, withhold_peer, trace_release, lead0, started, trace_issue, seg_rows, seg_bytes,
-                     row_stride, rel, n_rel, marks, timeout_ticks, status);
+                     row_stride, rel, n_rel, marks, timeout_ticks, status, finished);
   return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ hipError_t launch_ag_producer(uint32_t* flags, const ProdItem* items, int n_item
                               hipStream_t stream, uint32_t* started = nullptr, uint64_t* trace_issue = nullptr,
                               uint32_t seg_rows = 0, uint32_t seg_bytes = 0, uint32_t row_stride = 0,
                               const RelItem* rel = nullptr, int n_rel = 0, const uint32_t* marks = nullptr,
-                              uint64_t timeout_ticks = 0, uint32_t* status = nullptr);
+                              uint64_t timeout_ticks = 0, uint32_t* status = nullptr, uint32_t* finished = nullptr);
 hipError_t launch_ll_allgather(const ProdItem* items, int n_prod, int n_recv, int n_prod_blocks, int grid,
                                int64_t chunk_bytes, uint32_t epoch, int withhold_peer, uint64_t lead, int rank,
                                uint64_t timeout_ticks, uint32_t* status, uint64_t* trace, hipStream_t stream);
@@ -88,7 +88,7 @@ constexpr int kSlots = 4;                 // producer schedule tables in flight
 // producer workgroups started (cumulative), [64 + 16 x] claim counter of XCD x
 // for the AllGather consumer (cleared by a fill kernel before each launch).
 constexpr int kCounterWords = 512;
-constexpr int kAgStartedWord = 32, kAgClaimWord = 64;
+constexpr int kAgStartedWord = 32, kAgDoneWord = 48, kAgClaimWord = 64;
 constexpr int kSdmaMaxUnits = 4096;       // copy-engine copies per call
 constexpr int64_t kSdmaUnitBytes = 4 << 20;  // bytes per copy-engine copy (whole-row signal tiles grouped up to this)
 constexpr int64_t kItemsCap = 1 << 18;    // signal tiles per call
@@ -105,14 +105,17 @@ struct sgt_ctx {
   uint32_t* d_status = nullptr;  // 4 words
   uint32_t* d_counters = nullptr;  // work-claim counters, zeroed before each launch that uses them
   uint32_t ag_prod_started = 0;    // AllGather producer workgroups launched so far (cumulative)
+  uint32_t ag_prod_done = 0;       // of those, the ones that count themselves finished (cumulative)
   ProdItem* h_items[kSlots] = {};
   ProdItem* d_items[kSlots] = {};
   uint32_t* h_ranks[kSlots] = {};  // arrival rank of each signal tile (MoE work ordering), pinned host
   uint32_t* d_ranks[kSlots] = {};  // the same memory as the GPU addresses it (read in place, no copy)
-  uint32_t* d_moe = nullptr;       // MoE: tile count, claim counter, done count, started count, per-XCD claim
+  uint32_t* d_moe = nullptr;       // MoE: tile count, claim counter, done count, producer started and finished
+                                   // counts, per-XCD claim
                                    // counters (words 64 + 16 x), counts[2][256] by call parity (words 256..767)
   int moe_parity = 0;
   uint32_t moe_prod_started = 0;   // producer workgroups launched by overlapped MoE calls (cumulative)
+  uint32_t moe_prod_done = 0;      // of those, the ones that count themselves finished (cumulative)
   MoeTile* d_moe_tiles = nullptr;  // MoE row tiles, expert-major and sorted; grow on demand
   MoeTile* d_moe_order = nullptr;
   uint32_t* d_moe_keys = nullptr;
@@ -492,6 +495,8 @@ sgt_status sync_locked(sgt_ctx* c) {
   HIP_TRY(hipMemcpy(st, c->d_status, sizeof st, hipMemcpyDeviceToHost));
   if (st[0] == kStatusTimeout) {
     HIP_TRY(hipMemset(c->d_status, 0, sizeof st));
+    if (st[1] == 0xFFFFFFFFu)
+      return fail(SGT_ETIMEDOUT, "waiting for the producer to finish timed out: count %u, expected %u", st[2], st[3]);
     return fail(SGT_ETIMEDOUT, "wait on flag %u timed out: saw %u, expected %u", st[1], st[2], st[3]);
   }
   return SGT_OK;
@@ -1026,6 +1031,7 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   // workgroup per CU (its LDS use allows no more) on all but the producer's
   // share of CUs, so both kernels are resident at once and no wait can starve.
   int prod_wgs = pwg;
+  uint32_t* gpu_join = nullptr;
   if (o.producer == SGT_PROD_SDMA) {
     if ((st = ag_sdma_launch(ctx, o, p, W, K, esz, A_shards, A_gathered, flags, items, n_items, tile_bytes, seg_rows,
                              seg_bytes, row_stride, trace_rel, e, stream, &prod_wgs, started)) != SGT_OK)
@@ -1034,8 +1040,17 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
     HIP_TRY(hipEventRecord(ctx->ev_fork, stream));
     HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
     if ((st = stage_items(ctx, items, n_items, ctx->prod, &slot)) != SGT_OK) return st;
+    // the bf16 consumer joins the producer itself: its workgroups wait, before
+    // they exit, until every producer workgroup has counted itself finished
+    if (o.in_dtype == SGT_BF16 && N > 0) gpu_join = ctx->d_counters + kAgDoneWord;
     HIP_TRY(launch_ag_producer(flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
-                               trace_rel, pwg, ctx->prod, started, nullptr, seg_rows, seg_bytes, row_stride));
+                               trace_rel, pwg, ctx->prod, started, nullptr, seg_rows, seg_bytes, row_stride, nullptr,
+                               0, nullptr, 0, nullptr, gpu_join));
+    if (gpu_join) {  // counted once the launch has gone in
+      ctx->ag_prod_done += (uint32_t)pwg;
+      a.prod_done = gpu_join;
+      a.prod_done_all = ctx->ag_prod_done;
+    }
     HIP_TRY(hipEventRecord(ctx->slot_ev[slot], ctx->prod));
     ctx->slot_used[slot] = true;
   }
@@ -1068,8 +1083,10 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
       HIP_TRY(launch_ag_consumer(a, o.in_dtype, grid, stream));
       if ((st = mark(o, 1, stream)) != SGT_OK) return st;
     }
-  HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
-  HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
+  if (!gpu_join) {
+    HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
+    HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
+  }
   return finish(ctx, o, stream);
 }
 
@@ -1588,8 +1605,18 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   HIP_TRY(hipEventRecord(ctx->ev_fork, stream));
   HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
   if ((st = upload_items(ctx, slot, ctx->h_items[slot], n_items, ctx->prod)) != SGT_OK) return st;
+  // The grouped consumer joins the producer itself (its workgroups wait, before
+  // they exit, until every producer workgroup has counted itself finished);
+  // with no consumer launched (I == 0) the stream waits for the producer instead.
+  uint32_t* gpu_join = I > 0 ? ctx->d_moe + 16 : nullptr;
   HIP_TRY(launch_ag_producer(shard_flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
-                             trace_rel, pwg, ctx->prod, ctx->d_moe + 12));
+                             trace_rel, pwg, ctx->prod, ctx->d_moe + 12, nullptr, 0, 0, 0, nullptr, 0, nullptr, 0,
+                             nullptr, gpu_join));
+  if (gpu_join) {  // counted once the launch has gone in
+    ctx->moe_prod_done += (uint32_t)pwg;
+    a.prod_done = gpu_join;
+    a.prod_done_all = ctx->moe_prod_done;
+  }
   HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
   // The consumer takes the whole chip: its last pwg workgroups land on the
   // producer's CUs as the producer finishes (they claim work dynamically, so
@@ -1607,7 +1634,7 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   if ((st = route_and_compute(ctx->d_ranks[slot], o.consumer_cus > 0 ? std::min(o.consumer_cus, keep) : ctx->n_cu,
                               keep)) != SGT_OK)
     return st;
-  HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
+  if (!gpu_join) HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
   HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
   ctx->slot_used[slot] = true;
   return finish(ctx, o, stream);

@@ -45,6 +45,14 @@ __device__ __forceinline__ void flag_release(uint32_t* f, uint32_t epoch) {
 
 __device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
+// Producer workgroup, at its end: once every wave's stores are acknowledged,
+// count the workgroup finished (a release, so its plain stores go with it).
+__device__ __forceinline__ void count_finished(uint32_t* finished) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(finished, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Cache-policy bits of the buffer load/store builtins on gfx950.
 constexpr int kCpolSc0 = 1, kCpolNt = 2, kCpolSc1 = 16;
 
@@ -64,6 +72,26 @@ __device__ inline void report_timeout(uint32_t* status, int64_t flag, uint32_t s
     status[3] = expected;
     __threadfence();
   }
+}
+
+// Consumer workgroup of an overlapped call, at its end: thread 0 waits until
+// the producer's finished count (cumulative over calls, compared as a wrapping
+// difference) reaches `all`, then the acquire.  Bounded: on expiry the status
+// records flag index 0xFFFFFFFF (no flag) with the count seen.
+__device__ inline void wait_producer_done(const uint32_t* done, uint32_t all, uint64_t timeout_ticks,
+                                          uint32_t* status) {
+  if (!done || threadIdx.x != 0) return;
+  const uint64_t t0 = clock_ticks();
+  uint32_t v = __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  while ((int32_t)(v - all) < 0) {
+    if (clock_ticks() - t0 > timeout_ticks) {
+      report_timeout(status, 0xFFFFFFFFll, v, all);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+    v = __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  acquire_agent();
 }
 
 // Single-thread wait for flags[f0 .. f1) (pages' wait(ptr, n) with n = f1 - f0).
