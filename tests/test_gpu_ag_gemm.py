@@ -388,3 +388,31 @@ def test_sdma_producer_only_for_ag_gemm(ctx):
                     torch.empty((w.M // w.W, w.N), device="cuda:0"), torch.zeros(ng, dtype=torch.int32, device="cuda:0"),
                     torch.zeros(npf, dtype=torch.int32, device="cuda:0"), producer="sdma", blocking=True)
     assert ei.value.status == sgt.SGT_EUNSUPPORTED
+
+
+# ---------------------------------------------------------------- stream order after an overlapped call
+@pytest.mark.parametrize("producer", ["cu", "sdma"])
+def test_stream_order_covers_the_whole_allgather(ctx, orc, producer):
+    """After a non-blocking overlapped call, work queued on the caller's stream sees the whole gathered buffer,
+    the local shard's copy (the producer's last items, which the consumer never waits on) included: the
+    bf16 consumer joins the producer on the GPU, the copy-engine path with an event.  The check runs on the
+    caller's stream before any synchronization, for several calls back to back."""
+    w = I.AGWorkload("t", W=8, M=4096, K=2048, N=256, seed_index=52)
+    shards, B = I.make_ag(w, B_layout="nk")
+    dA = [dev(s) for s in shards]
+    dB = dev(B)
+    Ag = torch.empty((w.M, w.K), dtype=torch.bfloat16, device="cuda:0")
+    C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda:0")
+    flags = torch.zeros(sgt.ag_flag_count(w.W, w.M, w.K), dtype=torch.int32, device="cuda:0")
+    ref = torch.cat(dA).view(torch.int16)
+    oks = []
+    for i in range(4):
+        poison_like(Ag)
+        ctx.ag_gemm(dA, dB, Ag, C, flags, rank=3, b_layout="nk", producer=producer, arrival_seed=i + 1)
+        oks.append(torch.equal(Ag.view(torch.int16), ref))   # queued on the caller's stream
+    torch.cuda.synchronize()
+    ctx.sync()
+    assert all(oks)
+    rows = sample_rows(w.M, w.W, per_shard=2, seed=3)
+    _, C_ref = orc.ag_gemm(shards, B, b_layout="nk", rows=rows)
+    assert_close(host(C)[rows], C_ref, what="C", **TOL_BF16)
