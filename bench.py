@@ -282,7 +282,7 @@ def release_times(ctx, call, trace_words, n_tiles, torch, n=3, local_flags=0):
     release of a remote signal tile (flags from local_flags on: rank 0's shard holds the first ones).  The
     trace holds 4 words per consumer tile, then one release stamp per signal tile (100 MHz clock)."""
     import numpy as np
-    last, span, first = [], [], []
+    last, span, first, clock = [], [], [], []
     tr = torch.zeros(trace_words, dtype=torch.int64, device="cuda:0")
     for i in range(n):
         tr.zero_()
@@ -296,9 +296,50 @@ def release_times(ctx, call, trace_words, n_tiles, torch, n=3, local_flags=0):
         last.append((rel.max() - t0) / 100.0)
         span.append((tiles[:, 2].max() - t0) / 100.0)
         first.append((rel[local_flags:].min() - t0) / 100.0)
+        # engine clock: each tile's cycles (bits 16.. of its last word) over its duration
+        dur_us = (tiles[:, 2] - tiles[:, 0]) / 100.0
+        cyc = tiles[:, 3] >> 16
+        ok = (dur_us > 0) & (cyc > 0)
+        if ok.any():
+            clock.append(float(np.median(cyc[ok] / dur_us[ok])))
     del tr
     return {"last_release_us": statistics.median(last), "first_remote_release_us": statistics.median(first),
-            "consumer_end_us": statistics.median(span), "n": n}
+            "consumer_end_us": statistics.median(span), "n": n,
+            "clock_mhz": statistics.median(clock) if clock else None}
+
+
+def trace_clocks(traces, n_tiles):
+    """Engine clock (MHz) of each traced call in `traces` (one AllGather trace per row): the median over its
+    tiles of cycles / duration; None for a call without cycle counts."""
+    import numpy as np
+    out = []
+    for row in traces.cpu().numpy().view(np.uint64).astype(np.int64):
+        tiles = row[:4 * n_tiles].reshape(-1, 4)
+        dur_us = (tiles[:, 2] - tiles[:, 0]) / 100.0
+        cyc = tiles[:, 3] >> 16
+        ok = (dur_us > 0) & (cyc > 0)
+        out.append(float(np.median(cyc[ok] / dur_us[ok])) if ok.any() else None)
+    return out
+
+
+def trace_clock(call, trace_words, n_tiles, torch, ctx, n=3):
+    """Median engine clock (MHz) over n traced calls: each tile's cycle count over its duration."""
+    import numpy as np
+    tr = torch.zeros(trace_words, dtype=torch.int64, device="cuda:0")
+    out = []
+    for i in range(n):
+        tr.zero_()
+        call(i, tr.data_ptr())
+        torch.cuda.synchronize()
+        ctx.sync()
+        tiles = tr.cpu().numpy().view(np.uint64).astype(np.int64)[:4 * n_tiles].reshape(-1, 4)
+        dur_us = (tiles[:, 2] - tiles[:, 0]) / 100.0
+        cyc = tiles[:, 3] >> 16
+        ok = (dur_us > 0) & (cyc > 0)
+        if ok.any():
+            out.append(float(np.median(cyc[ok] / dur_us[ok])))
+    del tr
+    return statistics.median(out) if out else None
 
 
 def bench_engines(ctx, shards, B, Ag, C, flags, rank, lay, kc, link, alone_ms, flops, shape, args, torch, sgt):
@@ -1034,13 +1075,23 @@ def main():
                           "tflops": flops / (kern_ms * 1e-3) / 1e12}), flush=True)
         ctx.close()
         return
-    over_ms, over_kern_ms, over_list = timed(lambda i, ev: ag("cu", arrival_seed=i + 1, **link)(i, ev),
-                                             args.steps, args.warmup, torch, ctx)
+    # the instrumented block's calls also write a trace each, whose per-tile cycle counts give the engine clock
+    # of exactly the calls the kernel times come from
+    n_tr = sgt.trace_words(W, M, K, N, k_chunks=kc)
+    over_tr = torch.zeros((args.steps, n_tr), dtype=torch.int64, device=dev)
+
+    def over_fn(i, ev):
+        tr = over_tr[i - args.warmup].data_ptr() if ev is not None else 0
+        ag("cu", arrival_seed=i + 1, trace=tr, **link)(i, ev)
+    over_ms, over_kern_ms, over_list = timed(over_fn, args.steps, args.warmup, torch, ctx)
+    over_clock = trace_clocks(over_tr, (M // 256) * (-(-N // 256)))
+    del over_tr
     over_host = spread(LAST_HOST_MS) if LAST_HOST_MS else None
     over_host_max = max(LAST_HOST_MS) if LAST_HOST_MS else None
     if args.headline_only:
         print(json.dumps({"workload": w.name, "overlapped_ms": over_ms, "consumer_kernel_ms": over_kern_ms,
                           "tflops": flops / (over_ms * 1e-3) / 1e12,
+                          "clock_mhz": [round(c) if c else None for c in over_clock],
                           "host_call_ms": [round(h, 3) for h in LAST_HOST_MS]}), flush=True)
         ctx.close()
         return
@@ -1090,11 +1141,19 @@ def main():
                                                        trace=tr, **link),
                         sgt.trace_words(W, M, K, N, k_chunks=kc), (M // 256) * (-(-N // 256)), torch,
                         local_flags=sgt.ag_flag_count(W, M, K, k_chunks=kc) // W)
+    # the engine clock of the same GEMM with the data resident (flags preset), on the grid it was timed on
+    alone_clock = trace_clock(lambda i, tr: ctx.ag_gemm(shards, B, Ag, C, flags, rank=rank, b_layout=lay,
+                                                        producer="preset", k_chunks=kc, consumer_cus=alone_grid,
+                                                        trace=tr),
+                              sgt.trace_words(W, M, K, N, k_chunks=kc), (M // 256) * (-(-N // 256)), torch, ctx)
 
     shard_bytes = (M // W) * K * 2
     link_floor_us = shard_bytes / (w.peer_gbps * 1e9) * 1e6
     tflops = flops / (over_ms * 1e-3) / 1e12
     kern_tflops = flops / (over_kern_ms * 1e-3) / 1e12
+    # the engine clock over the instrumented block: each call's clock weighted by its kernel time
+    pairs_ck = [(c, k) for c, k in zip(over_clock, over_list) if c]
+    block_clock = sum(c * k for c, k in pairs_ck) / sum(k for _, k in pairs_ck) if pairs_ck else None
     n_tiles = (M // 256) * (-(-N // 256))
 
     def e_max(floor_us):
@@ -1144,6 +1203,13 @@ def main():
         "overlapped_ms": over_ms,
         "overlapped_kernel_ms": spread(over_list),
         "overlapped_host_call_ms": over_host,
+        "overlapped_clock_mhz": block_clock,
+        "overlapped_clock_mhz_per_call": spread([c for c in over_clock if c]) if any(over_clock) else None,
+        "traced_overlapped_clock_mhz": rel.get("clock_mhz"),
+        "gemm_alone_clock_mhz": alone_clock,
+        "clock_note": "engine clock from traced calls: each tile's s_memtime cycles over its 100 MHz duration "
+                      "(median over tiles, then over 3 calls); it moves with the board's power state from call "
+                      "to call and box to box",
         "overlapped_host_call_max_ms": over_host_max,
         "gemm_alone_ms": alone_ms,
         "gemm_alone_tflops": flops / (alone_ms * 1e-3) / 1e12,
@@ -1236,7 +1302,12 @@ def main():
                    "k_chunks": kc, "peer_gbps": w.peer_gbps, "jitter_us": w.jitter_us, "out": "fp32"},
         "roofline": {"bound": "mfma", "kernel": "ag_consumer_bf16", "achieved": round(kern_tflops, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_from_profile(), "algorithmic_bytes": (M * K + K * N) * 2 + M * N * 4},
+                     "traffic": traffic_from_profile(), "algorithmic_bytes": (M * K + K * N) * 2 + M * N * 4,
+                     # the engine clock of traced overlapped calls (per-tile cycle counts over durations) and the
+                     # fraction of the peak the chip has at that clock (256 CUs x 4096 flop per cycle)
+                     "clock_mhz": round(block_clock) if block_clock else None,
+                     "frac_at_clock": round(kern_tflops / (256 * 4096 * block_clock / 1e6), 4)
+                     if block_clock else None},
         "overlap": {"efficiency": round(e_step, 4), "efficiency_max": round(e_step_max, 4),
                     "last_release_us": round(rel["last_release_us"], 1), "link_floor_us": round(link_floor_us, 1),
                     "gemm_alone_ms": round(alone_ms, 4), "gemm_alone_tflops": round(flops / alone_ms / 1e9, 1)},

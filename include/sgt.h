@@ -557,7 +557,10 @@ SGT_API int64_t sgt_a2a_flag_count(int W, int64_t T_r, int E, const sgt_opts* op
 
 /* Words of the optional trace buffer for an AllGather call: per consumer tile
  * 4 x uint64 {wait start, flag seen, tile end, workgroup}; then per signal tile
- * 1 x uint64 release time.  Times are the 100 MHz constant GPU clock.
+ * 1 x uint64 release time.  Times are the 100 MHz constant GPU clock.  The bf16
+ * consumer puts the workgroup in bits 0..15 of the last word and the tile's
+ * engine-clock cycles (s_memtime, from the tile's start to its end, waits
+ * included) in bits 16..63, so cycles / duration is the engine clock.
  * (A GEMM+ReduceScatter call's trace is sized by sgt_rs_trace_words.) */
 SGT_API int64_t sgt_trace_words(int W, int64_t M, int64_t K, int64_t N, const sgt_opts* opts);
 

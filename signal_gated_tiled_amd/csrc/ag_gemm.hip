@@ -79,6 +79,13 @@ __device__ __forceinline__ int chunks_in_after(const AgArgs& a, int64_t pm, int 
   return *n;
 }
 
+// A traced tile's end: its end time, and in the last word the workgroup
+// (bits 0..15) with the engine-clock cycles since cyc0 (bits 16..63).
+__device__ __forceinline__ void trace_tile_end(uint64_t* rec, uint64_t cyc0) {
+  rec[2] = clock_ticks();
+  rec[3] = (uint64_t)blockIdx.x | ((__builtin_amdgcn_s_memtime() - cyc0) << 16);
+}
+
 // The next tile of this workgroup, or -1: the static schedule (tile t, then
 // t + G, ...) or, with dynamic claiming, the next claim from this XCD's list
 // and then from the other XCDs' lists (thread 0 claims; `x`, `left` and
@@ -128,6 +135,9 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) ag_consumer_bf16(AgArgs
   int xq = (int)(blockIdx.x % kXcds), left = kXcds, next = xcd_remap(blockIdx.x, gridDim.x);
   for (int t = next_tile(a, total, &xq, &left, &next, &tile_s); t >= 0;
        t = next_tile(a, total, &xq, &left, &next, &tile_s)) {
+    // traced: the tile's engine-clock cycles (waits included) go beside the
+    // workgroup in its last trace word, so a trace also gives the clock
+    const uint64_t cyc0 = a.trace && threadIdx.x == 0 ? __builtin_amdgcn_s_memtime() : 0;
     int64_t seq_m, pn;
     tile_at(t, a.tiles_m, a.tiles_n, &seq_m, &pn);
     const int64_t pm = panel_at(seq_m, a.tiles_m, a.rows_per_shard, kBM, a.W, a.rank, a.order);
@@ -175,7 +185,7 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) ag_consumer_bf16(AgArgs
           q = q_end;
         }
         store_tile<kW, kOutBf16>(a.C, a.M, a.N, m0, n0, acc);
-        if (a.trace && threadIdx.x == 0) a.trace[tile_id * 4 + 2] = clock_ticks();
+        if (a.trace && threadIdx.x == 0) trace_tile_end(a.trace + tile_id * 4, cyc0);
         continue;
       }
     } else if (!gate_rows(a, m0, m1, &ok, tile_id, &t_wait)) {
@@ -188,7 +198,7 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) ag_consumer_bf16(AgArgs
     MfmaAcc<kW> acc;
     gemm_tile<kW, kBNK>(ka, kb, B, a.N, n0, a.K, acc);
     store_tile<kW, kOutBf16>(a.C, a.M, a.N, m0, n0, acc);
-    if (a.trace && threadIdx.x == 0) a.trace[tile_id * 4 + 2] = clock_ticks();
+    if (a.trace && threadIdx.x == 0) trace_tile_end(a.trace + tile_id * 4, cyc0);
   }
   wait_producer_done(a.prod_done, a.prod_done_all, a.timeout_ticks, a.status);
 }
