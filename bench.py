@@ -276,6 +276,32 @@ def cpu_baseline(shards, B, M, N, K, seconds: float, b_layout: str = "kn"):
             "seconds": dt}
 
 
+def cpu_host_details(I):
+    """The host the CPU oracle ran on (model, threads) and the oracle on the tiny fp32 workload with one
+    thread and with all (whole workload, median of 5)."""
+    import oracle
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    w = I.TINY
+    shards, B = I.make_ag(w)
+    out = {"cpu_model": model, "threads": oracle.max_threads(), "os_cpus": os.cpu_count()}
+    for name, th in (("tiny_ag_gemm_1_thread_ms", 1), ("tiny_ag_gemm_all_threads_ms", 0)):
+        ts = []
+        for _ in range(5):
+            t = time.perf_counter()
+            oracle.gemm(oracle.allgather(shards), B, threads=th)
+            ts.append((time.perf_counter() - t) * 1e3)
+        out[name] = statistics.median(ts)
+    return out
+
+
 def release_times(ctx, call, trace_words, n_tiles, torch, n=3, local_flags=0):
     """The last signal tile's release, in microseconds from the call's first in-kernel stamp (a consumer
     tile's wait start or a release, whichever is earlier), median over n traced calls; also the first
@@ -1273,6 +1299,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(shards_h, B_h, M, N, K, args.cpu_seconds, b_layout=lay)
         cpu.pop("seconds", None)
+        detail["cpu_oracle_host"] = cpu_host_details(I)
 
     # the full detail goes to a file and to earlier lines; the last line stays short (under 2 KB)
     detail_path = os.path.join(ROOT, "gpurun_out", "bench_detail.json")
