@@ -123,6 +123,8 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) ag_consumer_bf16(AgArgs
   const int total = a.tiles_m * a.tiles_n;
   const uint16_t* A = static_cast<const uint16_t*>(a.A);
   const uint16_t* B = static_cast<const uint16_t*>(a.B);
+  // the next launch's claim counters start at zero (stream order publishes them)
+  if (a.xcd_claim_next && blockIdx.x == 0 && threadIdx.x < kXcds) a.xcd_claim_next[threadIdx.x * kXcdClaimStride] = 0u;
   if (a.late_blocks > 0 && (int)blockIdx.x >= (int)gridDim.x - a.late_blocks) {
     // a workgroup that may sit on a CU the producer needs: run only if every
     // producer workgroup is already running (one check, no wait); it then

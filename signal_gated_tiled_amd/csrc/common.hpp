@@ -69,6 +69,7 @@ struct AgArgs {
   // lists; the last late_blocks workgroups run only if every producer
   // workgroup already runs (*started == started_all), else they exit at once.
   uint32_t* xcd_claim;
+  uint32_t* xcd_claim_next;   // the other counter set: zeroed by workgroup 0 at the start, for the next launch
   int32_t base_grid;
   int32_t late_blocks;
   const uint32_t* started;

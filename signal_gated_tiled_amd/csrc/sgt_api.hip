@@ -88,7 +88,7 @@ constexpr int kSlots = 4;                 // producer schedule tables in flight
 // producer workgroups started (cumulative), [64 + 16 x] claim counter of XCD x
 // for the AllGather consumer (cleared by a fill kernel before each launch).
 constexpr int kCounterWords = 512;
-constexpr int kAgStartedWord = 32, kAgDoneWord = 48, kAgClaimWord = 64;
+constexpr int kAgStartedWord = 32, kAgDoneWord = 48, kAgClaimWord = 64;  // claim sets: 64.. and 192..
 constexpr int kSdmaMaxUnits = 4096;       // copy-engine copies per call
 constexpr int64_t kSdmaUnitBytes = 4 << 20;  // bytes per copy-engine copy (whole-row signal tiles grouped up to this)
 constexpr int64_t kItemsCap = 1 << 18;    // signal tiles per call
@@ -106,6 +106,7 @@ struct sgt_ctx {
   uint32_t* d_counters = nullptr;  // work-claim counters, zeroed before each launch that uses them
   uint32_t ag_prod_started = 0;    // AllGather producer workgroups launched so far (cumulative)
   uint32_t ag_prod_done = 0;       // of those, the ones that count themselves finished (cumulative)
+  int ag_claim_parity = 0;         // which of the two AllGather claim-counter sets the next consumer uses
   ProdItem* h_items[kSlots] = {};
   ProdItem* d_items[kSlots] = {};
   uint32_t* h_ranks[kSlots] = {};  // arrival rank of each signal tile (MoE work ordering), pinned host
@@ -974,17 +975,28 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   uint32_t* started = ctx->d_counters + kAgStartedWord;
   // bf16 tiles are claimed dynamically, XCD by XCD in the order the static
   // schedule of a `base`-workgroup grid gives them (a grid that is not a
-  // multiple of the XCD count keeps the static schedule); the claim counters
-  // are cleared by a fill kernel on the consumer's stream.
+  // multiple of the XCD count keeps the static schedule).  The claim counters
+  // come in two sets used by alternate consumer launches: each launch claims
+  // from one set (zeroed by the launch before it, or at context creation) and
+  // zeroes the other at its start, so no clearing launch is needed.
   auto claim_setup = [&](int base, int late) -> sgt_status {
-    if (o.in_dtype != SGT_BF16 || base % kXcds) return SGT_OK;
-    a.xcd_claim = ctx->d_counters + kAgClaimWord;
+    if (o.in_dtype != SGT_BF16 || base % kXcds || N <= 0) return SGT_OK;
+    const int set = ctx->ag_claim_parity, words = kXcds * kXcdClaimStride;
+    a.xcd_claim = ctx->d_counters + kAgClaimWord + set * words;
+    a.xcd_claim_next = ctx->d_counters + kAgClaimWord + (1 - set) * words;
     a.base_grid = base;
     a.late_blocks = late;
     a.started = started;
     a.started_all = ctx->ag_prod_started;
-    HIP_TRY(launch_fill_u32(a.xcd_claim, kXcds * kXcdClaimStride, 0u, stream));
     return SGT_OK;
+  };
+  // the consumer launch; a launch that claims from a counter set hands the
+  // other set to the next one
+  auto launch_consumer = [&](int grid) -> sgt_status {
+    if ((st = mark(o, 0, stream)) != SGT_OK) return st;
+    HIP_TRY(launch_ag_consumer(a, o.in_dtype, grid, stream));
+    if (a.xcd_claim) ctx->ag_claim_parity ^= 1;
+    return mark(o, 1, stream);
   };
 
   if (o.producer == SGT_PROD_PRESET) {
@@ -992,11 +1004,7 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
     const int grid = std::min(total_tiles, o.consumer_cus > 0 ? o.consumer_cus
                                             : (o.in_dtype == SGT_BF16 ? ctx->n_cu : 4 * ctx->n_cu));
     if ((st = claim_setup(grid, 0)) != SGT_OK) return st;
-    if (N > 0) {
-      if ((st = mark(o, 0, stream)) != SGT_OK) return st;
-      HIP_TRY(launch_ag_consumer(a, o.in_dtype, grid, stream));
-      if ((st = mark(o, 1, stream)) != SGT_OK) return st;
-    }
+    if (N > 0 && (st = launch_consumer(grid)) != SGT_OK) return st;
     return finish(ctx, o, stream);
   }
 
@@ -1019,11 +1027,7 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
     const int grid = std::min(total_tiles, o.consumer_cus > 0 ? o.consumer_cus
                                             : (o.in_dtype == SGT_BF16 ? ctx->n_cu : 4 * ctx->n_cu));
     if ((st = claim_setup(grid, 0)) != SGT_OK) return st;
-    if (N > 0) {
-      if ((st = mark(o, 0, stream)) != SGT_OK) return st;
-      HIP_TRY(launch_ag_consumer(a, o.in_dtype, grid, stream));
-      if ((st = mark(o, 1, stream)) != SGT_OK) return st;
-    }
+    if (N > 0 && (st = launch_consumer(grid)) != SGT_OK) return st;
     return finish(ctx, o, stream);
   }
 
@@ -1078,11 +1082,7 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
     grid = o.consumer_cus > 0 ? std::min(o.consumer_cus, keep) : keep;
     grid = std::min(grid, total_tiles);
   }
-  if (N > 0) {
-      if ((st = mark(o, 0, stream)) != SGT_OK) return st;
-      HIP_TRY(launch_ag_consumer(a, o.in_dtype, grid, stream));
-      if ((st = mark(o, 1, stream)) != SGT_OK) return st;
-    }
+  if (N > 0 && (st = launch_consumer(grid)) != SGT_OK) return st;
   if (!gpu_join) {
     HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
     HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
