@@ -99,7 +99,12 @@ LAST_HOST_MS = []
 @contextlib.contextmanager
 def no_gc():
     """Python's cyclic garbage collector off inside a timed loop (as timeit does): in a process holding
-    torch's objects one full collection takes tens of milliseconds, which would land inside one call."""
+    torch's objects one full collection takes tens of milliseconds, which would land inside one call.  The
+    collection runs once, before the warm-up (a collection between the warm-up and a timed block leaves the
+    GPU idle long enough for its clock to drop); inside an outer no_gc() this does nothing."""
+    if not gc.isenabled():
+        yield
+        return
     gc.collect()
     gc.disable()
     try:
@@ -108,8 +113,31 @@ def no_gc():
         gc.enable()
 
 
+# Under sustained load the engine clock settles within about a tenth of a second: after an idle gap (a
+# workload's host-side setup, or a garbage collection of tens of milliseconds) the first ~100 calls of the
+# Llama GEMM ran 3% slower than the rest, and the first 30 up to 10%.  Every warm-up therefore runs for at
+# least this long (and at least its W calls), and nothing idles the GPU between it and the timed blocks.
+WARM_S = 0.25
+
+
+def warm(fn, warmup, torch, ctx):
+    """fn(i, None) for i = 0, 1, ... until at least `warmup` calls and WARM_S seconds have passed (the host
+    waits for the GPU after every 32 calls, so the seconds are the GPU's); returns the number of calls."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < warmup or time.perf_counter() - t0 < WARM_S:
+        fn(i, None)
+        i += 1
+        if i % 32 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    if ctx is not None:
+        ctx.sync()
+    return i
+
+
 def timed(fn, steps, warmup, torch, ctx):
-    """Run fn(i, events) warmup times, then two blocks of `steps` calls.
+    """Run fn(i, events) warmup times (and for at least WARM_S seconds), then two blocks of `steps` calls.
 
     The first block records HIP events around every consumer launch (the kernel times).  The second passes
     no events: its wall time between two synchronizations is the step time (a timing event recorded around
@@ -117,28 +145,26 @@ def timed(fn, steps, warmup, torch, ctx):
     it second also lets the clocks settle under the load first).
     Returns (ms per step, mean consumer-kernel ms, per-call kernel ms).
     """
-    for i in range(warmup):
-        fn(i, None)
-    torch.cuda.synchronize()
-    ctx.sync()
-    evk = _events(steps, torch)
-    torch.cuda.synchronize()
     with no_gc():
-        for i in range(steps):
-            fn(warmup + i, evk[i])
+        return _timed(fn, steps, warmup, torch, ctx)
+
+
+def _timed(fn, steps, warmup, torch, ctx):
+    evk = _events(steps, torch)
+    warm(fn, warmup, torch, ctx)
+    for i in range(steps):
+        fn(warmup + i, evk[i])
     torch.cuda.synchronize()
     ctx.sync()
     kern = [a.elapsed_time(b) for a, b in evk]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     host = [0.0] * steps
-    torch.cuda.synchronize()
-    with no_gc():
-        t0.record()
-        for i in range(steps):
-            h0 = time.perf_counter()
-            fn(warmup + steps + i, None)
-            host[i] = time.perf_counter() - h0
-        t1.record()
+    t0.record()
+    for i in range(steps):
+        h0 = time.perf_counter()
+        fn(warmup + steps + i, None)
+        host[i] = time.perf_counter() - h0
+    t1.record()
     torch.cuda.synchronize()
     ctx.sync()
     step_ms = t0.elapsed_time(t1) / steps
@@ -150,19 +176,18 @@ def timed(fn, steps, warmup, torch, ctx):
 def timed_blocks(fn, steps, warmup, torch, ctx, blocks=3):
     """timed() whose step time is the median over `blocks` event-free blocks: for calls of tens of
     microseconds, where one host stall inside a single block would dominate its mean."""
-    step, mean_k, kern = timed(fn, steps, warmup, torch, ctx)
-    steps_ms = [step]
-    for b in range(blocks - 1):
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        with no_gc():
+    with no_gc():
+        step, mean_k, kern = _timed(fn, steps, warmup, torch, ctx)
+        steps_ms = [step]
+        for b in range(blocks - 1):
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             t0.record()
             for i in range(steps):
                 fn(warmup + (b + 2) * steps + i, None)
             t1.record()
-        torch.cuda.synchronize()
-        ctx.sync()
-        steps_ms.append(t0.elapsed_time(t1) / steps)
+            torch.cuda.synchronize()
+            ctx.sync()
+            steps_ms.append(t0.elapsed_time(t1) / steps)
     return statistics.median(steps_ms), mean_k, kern
 
 
@@ -178,9 +203,9 @@ def pairs(fn_a, fn_b, n, torch, ctx):
 
     Pairs taken back to back see the same clock and thermal state, so their ratio is not biased by drift
     between two blocks of runs."""
-    ev = _events(2 * n, torch)
-    torch.cuda.synchronize()
     with no_gc():
+        ev = _events(2 * n, torch)
+        warm(lambda i, _: (fn_a(i, None), fn_b(i, None)), 1, torch, ctx)
         for i in range(n):
             fn_a(i, ev[2 * i])
             fn_b(i, ev[2 * i + 1])
@@ -223,8 +248,8 @@ def microbench(torch, A, B_kn, steps):
     x = torch.empty(n, dtype=torch.float32, device="cuda:0")
     y = torch.empty_like(x)
     x.fill_(1.0)
-    for _ in range(2):
-        y.copy_(x)
+    with no_gc():
+        warm(lambda i, _: y.copy_(x), 2, torch, None)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(steps):
@@ -235,8 +260,8 @@ def microbench(torch, A, B_kn, steps):
     del x, y
     M, K = A.shape
     N = B_kn.shape[1]
-    for _ in range(2):
-        C = torch.matmul(A, B_kn)
+    with no_gc():
+        warm(lambda i, _: torch.matmul(A, B_kn), 2, torch, None)
     a.record()
     for _ in range(steps):
         C = torch.matmul(A, B_kn)
@@ -1319,6 +1344,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_min_s": WARM_S,
         "ms_per_step": over_ms,
         "higher_is_better": True,
         "scaling": "weak",
