@@ -241,6 +241,47 @@ def device_clocks():
     return lines or None
 
 
+def power_under_load(fn, torch, ctx, min_s=0.6):
+    """Board power and per-XCD engine clocks as amd-smi reads them while fn runs back to back (after a warm-up):
+    under sustained dense MFMA load the package sits at its power limit, which sets the clock.  None if the
+    tool is unavailable."""
+    import re
+    import subprocess
+    with no_gc():
+        warm(fn, 1, torch, ctx)
+        t0 = time.perf_counter()
+        proc, i, out = None, 0, None
+        try:
+            while True:
+                fn(i, None)
+                i += 1
+                if i % 8:
+                    continue
+                torch.cuda.synchronize()
+                el = time.perf_counter() - t0
+                if proc is None and el > 0.2:
+                    proc = subprocess.Popen(["amd-smi", "metric", "-g", "0", "-p", "-c"], stdout=subprocess.PIPE,
+                                            stderr=subprocess.DEVNULL, text=True)
+                if (proc is not None and proc.poll() is not None and el > min_s) or el > 15.0:
+                    break
+        except OSError:  # no amd-smi: only this field is dropped
+            proc = None
+        torch.cuda.synchronize()
+        ctx.sync()
+    if proc is None:
+        return None
+    try:
+        out = proc.communicate(timeout=20)[0]
+    except subprocess.TimeoutExpired:
+        proc.kill()
+        return None
+    pw = re.search(r"SOCKET_POWER:\s*(\d+)", out or "")
+    clks = [int(c) for c in re.findall(r"GFX_\d+:\s*CLK:\s*(\d+)\s*MHz", out or "")]
+    return {"socket_power_w": int(pw.group(1)) if pw else None, "gfx_clk_mhz": clks,
+            "gfx_clk_mhz_mean": round(sum(clks) / len(clks)) if clks else None, "calls": i,
+            "note": "amd-smi read once while the overlapped Llama call ran back to back"}
+
+
 def microbench(torch, A, B_kn, steps):
     """Measured ceilings on this device: a 1 GiB device copy and hipBLASLt's bf16 GEMM (torch.matmul) at the
     headline shape, both timed with events; context for the hand-written kernels, not part of the method."""
@@ -1161,6 +1202,8 @@ def main():
         print(json.dumps(out), flush=True)
         ctx.close()
         return
+    # board power and engine clocks while the overlapped call runs back to back
+    power = power_under_load(lambda i, ev: ag("cu", arrival_seed=5000 + i, **link)(i, ev), torch, ctx)
     # the same consumer with data resident and flags preset, on all CUs and on the grid the overlapped
     # run leaves it (all CUs but the producer's); the better of the two is "the GEMM alone"
     alone_all = timed(ag("preset"), args.steps, args.warmup, torch, ctx)
@@ -1255,6 +1298,7 @@ def main():
         "overlapped_kernel_ms": spread(over_list),
         "overlapped_host_call_ms": over_host,
         "overlapped_clock_mhz": block_clock,
+        "power_under_load": power,
         "overlapped_clock_mhz_per_call": spread([c for c in over_clock if c]) if any(over_clock) else None,
         "traced_overlapped_clock_mhz": rel.get("clock_mhz"),
         "gemm_alone_clock_mhz": alone_clock,
@@ -1360,7 +1404,9 @@ def main():
                      # fraction of the peak the chip has at that clock (256 CUs x 4096 flop per cycle)
                      "clock_mhz": round(block_clock) if block_clock else None,
                      "frac_at_clock": round(kern_tflops / (256 * 4096 * block_clock / 1e6), 4)
-                     if block_clock else None},
+                     if block_clock else None,
+                     # amd-smi under the same load: the package's power limit is what sets that clock
+                     "board_power_w": power.get("socket_power_w") if power else None},
         "overlap": {"efficiency": round(e_step, 4), "efficiency_max": round(e_step_max, 4),
                     "last_release_us": round(rel["last_release_us"], 1), "link_floor_us": round(link_floor_us, 1),
                     "gemm_alone_ms": round(alone_ms, 4), "gemm_alone_tflops": round(flops / alone_ms / 1e9, 1)},
