@@ -21,12 +21,11 @@ namespace sgt {
 namespace {
 
 // Wait for flags [f0, f1) and record trace stamps.
-__device__ __forceinline__ bool gate_flags(const AgArgs& a, int64_t f0, int64_t f1, int* ok, int64_t tile_id,
-                                           uint64_t* t_wait) {
-  if (threadIdx.x == 0) *t_wait = clock_ticks();
+__device__ __forceinline__ bool gate_flags(const AgArgs& a, int64_t f0, int64_t f1, int* ok, int64_t tile_id) {
+  const uint64_t t_wait = a.trace && threadIdx.x == 0 ? clock_ticks() : 0;
   const bool good = wait_flags_block(a.flags, f0, f1, a.epoch, a.timeout_ticks, a.status, ok);
   if (a.trace && threadIdx.x == 0) {
-    a.trace[tile_id * 4 + 0] = *t_wait;
+    a.trace[tile_id * 4 + 0] = t_wait;
     a.trace[tile_id * 4 + 1] = clock_ticks();
     a.trace[tile_id * 4 + 3] = blockIdx.x;
   }
@@ -34,16 +33,14 @@ __device__ __forceinline__ bool gate_flags(const AgArgs& a, int64_t f0, int64_t 
 }
 
 // Wait for the flags covering rows [m0, m1) (signal tiles of flag_rows rows x all K).
-__device__ __forceinline__ bool gate_rows(const AgArgs& a, int64_t m0, int64_t m1, int* ok, int64_t tile_id,
-                                          uint64_t* t_wait) {
-  return gate_flags(a, m0 / a.flag_rows, (m1 - 1) / a.flag_rows + 1, ok, tile_id, t_wait);
+__device__ __forceinline__ bool gate_rows(const AgArgs& a, int64_t m0, int64_t m1, int* ok, int64_t tile_id) {
+  return gate_flags(a, m0 / a.flag_rows, (m1 - 1) / a.flag_rows + 1, ok, tile_id);
 }
 
 // K-chunked signal tiles: are all n_kc chunk flags of panel pm set?  One peek
 // per chunk (lane q of wave 0), no waiting; when they are, the acquire follows
 // and the trace records the tile as ready at once.
-__device__ __forceinline__ bool panel_chunks_in(const AgArgs& a, int64_t pm, int* ok, int64_t tile_id,
-                                                uint64_t* t_wait) {
+__device__ __forceinline__ bool panel_chunks_in(const AgArgs& a, int64_t pm, int* ok, int64_t tile_id) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const bool in = lane >= a.n_kc || flag_is_set(flag_peek(a.flags + pm * a.n_kc + lane), a.epoch);
@@ -51,10 +48,10 @@ __device__ __forceinline__ bool panel_chunks_in(const AgArgs& a, int64_t pm, int
     if (all) acquire_agent();
     if (lane == 0) {
       *ok = all ? 1 : 0;
-      *t_wait = clock_ticks();
       if (a.trace) {
-        a.trace[tile_id * 4 + 0] = *t_wait;
-        a.trace[tile_id * 4 + 1] = *t_wait;
+        const uint64_t now = clock_ticks();
+        a.trace[tile_id * 4 + 0] = now;
+        a.trace[tile_id * 4 + 1] = now;
         a.trace[tile_id * 4 + 3] = blockIdx.x;
       }
     }
@@ -113,13 +110,27 @@ __device__ __forceinline__ int next_tile(const AgArgs& a, int total, int* x, int
   return t;
 }
 
+// The workgroup's shared words.  all_in and n_more have words of their own:
+// the chunk waits that may follow rewrite `ok` with no barrier between.
+struct AgWords {
+  int ok, all_in, n_more, tile_s;
+};
+
 template <int kW, bool kBNK, bool kOutBf16>
 __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) ag_consumer_bf16(AgArgs a) {
-  __shared__ int ok;
-  __shared__ int all_in;  // its own word: the chunk waits that may follow rewrite `ok` with no barrier between
-  __shared__ int n_more;  // likewise for the count of chunks already in
-  __shared__ int tile_s;
-  __shared__ uint64_t t_wait;
+  // LDS: the K loop's stages (the step loop's four, or the ring's five slots
+  // of 32 KiB, 160 KiB in all).  With the ring the shared words live at the
+  // start of the fifth slot: they are used only between K ranges, when no
+  // load is in flight, and the ring writes that slot first in its first step,
+  // after a barrier every wave passes once it has read them.
+  constexpr bool kRing = kW == 8 && kBNK;
+  __shared__ __attribute__((aligned(1024))) uint8_t s0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s3[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s4[kRing ? kStageBytes : sizeof(AgWords)];
+  AgWords* const wd = reinterpret_cast<AgWords*>(s4);
+  int& ok = wd->ok;
   const int total = a.tiles_m * a.tiles_n;
   const uint16_t* A = static_cast<const uint16_t*>(a.A);
   const uint16_t* B = static_cast<const uint16_t*>(a.B);
@@ -135,8 +146,13 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) ag_consumer_bf16(AgArgs
     if (!ok) return;
   }
   int xq = (int)(blockIdx.x % kXcds), left = kXcds, next = xcd_remap(blockIdx.x, gridDim.x);
-  for (int t = next_tile(a, total, &xq, &left, &next, &tile_s); t >= 0;
-       t = next_tile(a, total, &xq, &left, &next, &tile_s)) {
+  // K steps [k0, k1) of the tile at column n0 into acc
+  auto k_range = [&](const KRows& ka, const KRows& kb, int64_t n0, int64_t k0, int64_t k1, MfmaAcc<kW>& acc) {
+    if constexpr (kRing) gemm_tile_range_r5(ka, kb, k0, k1, acc, s0, s1, s2, s3, s4);
+    else gemm_tile_range_lds<kW, kBNK, kBM>(ka, kb, B, a.N, n0, a.K, k0, k1, acc, s0, s1, s2, s3);
+  };
+  for (int t = next_tile(a, total, &xq, &left, &next, &wd->tile_s); t >= 0;
+       t = next_tile(a, total, &xq, &left, &next, &wd->tile_s)) {
     // traced: the tile's engine-clock cycles (waits included) go beside the
     // workgroup in its last trace word, so a trace also gives the clock
     const uint64_t cyc0 = a.trace && threadIdx.x == 0 ? __builtin_amdgcn_s_memtime() : 0;
@@ -168,8 +184,8 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) ag_consumer_bf16(AgArgs
       // 8-wave tile with B stored N x K, the one whose registers leave room for
       // a second K loop; the other variants wait for the whole panel).
       if constexpr (kW != 8 || !kBNK) {
-        if (!gate_flags(a, pm * a.n_kc, (pm + 1) * a.n_kc, &ok, tile_id, &t_wait)) return;
-      } else if (!panel_chunks_in(a, pm, &all_in, tile_id, &t_wait)) {
+        if (!gate_flags(a, pm * a.n_kc, (pm + 1) * a.n_kc, &ok, tile_id)) return;
+      } else if (!panel_chunks_in(a, pm, &wd->all_in, tile_id)) {
         const KRows ka = krows_strided<kW>(Abase, rows_valid, a.K);
         KRows kb = ka;
         if constexpr (kBNK) kb = krows_strided<kW>(B + n0 * a.K, a.N - n0, a.K);
@@ -181,16 +197,15 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) ag_consumer_bf16(AgArgs
           const int64_t f = pm * a.n_kc + q;
           if (!wait_flags_block(a.flags, f, f + 1, a.epoch, a.timeout_ticks, a.status, &ok)) return;
           if (q == 0 && a.trace && threadIdx.x == 0) a.trace[tile_id * 4 + 1] = clock_ticks();
-          const int q_end = q + 1 + chunks_in_after(a, pm, q + 1, &n_more);
-          gemm_tile_range<kW, kBNK>(ka, kb, B, a.N, n0, a.K, (int64_t)q * a.kc_cols, (int64_t)q_end * a.kc_cols,
-                                    acc);
+          const int q_end = q + 1 + chunks_in_after(a, pm, q + 1, &wd->n_more);
+          k_range(ka, kb, n0, (int64_t)q * a.kc_cols, (int64_t)q_end * a.kc_cols, acc);
           q = q_end;
         }
         store_tile<kW, kOutBf16>(a.C, a.M, a.N, m0, n0, acc);
         if (a.trace && threadIdx.x == 0) trace_tile_end(a.trace + tile_id * 4, cyc0);
         continue;
       }
-    } else if (!gate_rows(a, m0, m1, &ok, tile_id, &t_wait)) {
+    } else if (!gate_rows(a, m0, m1, &ok, tile_id)) {
       return;
     }
 
@@ -198,7 +213,8 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) ag_consumer_bf16(AgArgs
     KRows kb = ka;
     if constexpr (kBNK) kb = krows_strided<kW>(B + n0 * a.K, a.N - n0, a.K);
     MfmaAcc<kW> acc;
-    gemm_tile<kW, kBNK>(ka, kb, B, a.N, n0, a.K, acc);
+    acc_zero<kW>(acc);
+    k_range(ka, kb, n0, 0, a.K, acc);
     store_tile<kW, kOutBf16>(a.C, a.M, a.N, m0, n0, acc);
     if (a.trace && threadIdx.x == 0) trace_tile_end(a.trace + tile_id * 4, cyc0);
   }
@@ -212,7 +228,6 @@ __global__ void __launch_bounds__(256) ag_consumer_f32(AgArgs a) {
   __shared__ float As[kF32BK][kF32BM + 4];
   __shared__ float Bs[kF32BK][kF32BN + 4];
   __shared__ int ok;
-  __shared__ uint64_t t_wait;
   const float* A = static_cast<const float*>(a.A);
   const float* B = static_cast<const float*>(a.B);
   const int total = a.tiles_m * a.tiles_n;
@@ -224,7 +239,7 @@ __global__ void __launch_bounds__(256) ag_consumer_f32(AgArgs a) {
     const int64_t m0 = pm * kF32BM, n0 = pn * kF32BN;
     const int64_t m1 = m0 + kF32BM < a.M ? m0 + kF32BM : a.M;
     const int64_t tile_id = pm * a.tiles_n + pn;
-    if (!gate_rows(a, m0, m1, &ok, tile_id, &t_wait)) return;
+    if (!gate_rows(a, m0, m1, &ok, tile_id)) return;
 
     float acc[4][4];
 #pragma unroll

@@ -70,10 +70,11 @@ def test_every_tile_kernel_keeps_its_mfma_loop(kernels):
         mi = kr // (kw // 2) // 32
         n = sum(1 for ln in body if ln.startswith("v_mfma_f32_32x32x16_bf16"))
         # the K loop is unrolled over the two LDS stages: 2 x 4 substeps x (MI x 4) MFMAs; the AllGather
-        # consumer's 8-wave N x K tile holds two K loops (a whole panel at once, or K chunk by K chunk); the
-        # MoE consumer with 256-row tiles holds a 256-row and a 128-row loop (the short tail of a group)
-        loops = 2 if "ag_consumer_bf16ILi8ELb1E" in name else 1
-        want = loops * 2 * 4 * mi * 4
+        # consumer's 8-wave N x K tile holds two K loops (a whole panel at once, or K chunk by K chunk), each
+        # on the five-slot ring, unrolled over five steps; the MoE consumer with 256-row tiles holds a
+        # 256-row and a 128-row loop (the short tail of a group)
+        ring = "ag_consumer_bf16ILi8ELb1E" in name
+        want = (2 * 5 if ring else 2) * 4 * mi * 4
         if "moe_consumer_bf16" in name and kr == 256:
             want += 2 * 4 * (128 // (kw // 2) // 32) * 4
         assert n == want, "%s: %d MFMAs, expected %d" % (name, n, want)
