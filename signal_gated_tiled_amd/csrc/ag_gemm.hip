@@ -148,7 +148,7 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) ag_consumer_bf16(AgArgs
   int xq = (int)(blockIdx.x % kXcds), left = kXcds, next = xcd_remap(blockIdx.x, gridDim.x);
   // K steps [k0, k1) of the tile at column n0 into acc
   auto k_range = [&](const KRows& ka, const KRows& kb, int64_t n0, int64_t k0, int64_t k1, MfmaAcc<kW>& acc) {
-    if constexpr (kRing) gemm_tile_range_r5(ka, kb, k0, k1, acc, s0, s1, s2, s3, s4);
+    if constexpr (kRing) gemm_tile_range_r5<kBM, true>(ka, kb, k0, k1, acc, s0, s1, s2, s3, s4);
     else gemm_tile_range_lds<kW, kBNK, kBM>(ka, kb, B, a.N, n0, a.K, k0, k1, acc, s0, s1, s2, s3);
   };
   for (int t = next_tile(a, total, &xq, &left, &next, &wd->tile_s); t >= 0;

@@ -369,26 +369,38 @@ __device__ __forceinline__ void gemm_tile_range_lds(const KRows& ka, const KRows
 
 // ---- five-slot ring: the 8-wave tile with both operands by DMA ----
 // LDS holds five 32 KiB slots, each one operand's K step in the step loop's
-// layout.  The operands go to the slots in the order A_0 B_0 A_1 B_1 A_2 ...
-// (item i in slot i % 5), so while step s reads A_s and B_s the loads of
-// B_{s+1} and A_{s+2} are in flight: A is loaded two steps ahead and B one.
-// (A, the gathered rows, is mostly read from HBM; the weight slabs of B are
-// refetched by every XCD and mostly hit the MALL.  A ahead measured 2% faster
-// than B ahead on the Llama share.)  Each step's eight loads per wave are still
+// layout.  One operand leads: the slots take lead_0 follow_0 lead_1 follow_1
+// ... (item i in slot i % 5), so while step s reads both operands of step s
+// the loads of follow_{s+1} and lead_{s+2} are in flight: the lead operand is
+// loaded two steps ahead and the other one.  Each step's loads are still
 // interleaved with the first substep's MFMAs, and each step ends with one
-// barrier.
+// barrier.  The lead goes to the operand whose loads miss the L2 and the MALL
+// more (measured per kernel: the gathered rows of the AllGather consumer).
 __device__ __forceinline__ void bar_raw() { asm volatile("s_barrier" ::: "memory"); }
 
-// At most four of this wave's vector memory operations in flight.  The
+// At most N (2, 4) of this wave's vector memory operations in flight.  The
 // compiler's own wait counting sees this builtin (it does not see an asm
 // wait), so it knows which loads are in when the next step reads their slots.
-// Encoding (gfx9): vmcnt 4 in bits 3:0, expcnt and lgkmcnt at their maxima.
-__device__ __forceinline__ void wait_vm4() { __builtin_amdgcn_s_waitcnt(0x0F74); }
+// Encoding (gfx9): vmcnt in bits 3:0, expcnt (bits 6:4) and lgkmcnt (11:8) at
+// their maxima.
+template <int N>
+__device__ __forceinline__ void wait_vm_ring() {
+  static_assert(N == 2 || N == 4, "loads left in flight");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
-// A ring step's loads: this wave's 4 loads of B's rows for step s + 1, then
-// its 4 of A's rows for step s + 2 (8 waves, 256 rows each).
+// Loads per wave of one operand's K step (8 waves): 8 rows each.
+template <int kRows>
+constexpr int ring_loads() {
+  return kRows / 8 / 8;
+}
+
+// A ring step's loads: this wave's loads of the follow operand for step s + 1,
+// then its loads of the lead operand for step s + 2.
+template <int kR, bool kLeadA>
 struct StepDmaR5 {
-  static constexpr int kN = 8;
+  static constexpr int kLA = ring_loads<kR>(), kLB = ring_loads<kBM>();
+  static constexpr int kLF = kLeadA ? kLB : kLA, kN = kLA + kLB;  // follow loads go first
   const KRows* ka;
   const KRows* kb;
   uint8_t* sA;
@@ -402,59 +414,80 @@ struct StepDmaR5 {
                                        int64_t kB, int64_t K)
       : ka(&a), kb(&b), sA(stA), sB(stB), kbA((uint32_t)(kA * 2)), limA(lim_of(kA, K)), kbB((uint32_t)(kB * 2)),
         limB(lim_of(kB, K)) {}
+  template <int L>
   __device__ __forceinline__ void one(const KRows& kr, uint8_t* stage, int i, uint32_t kbyte, uint32_t lim) const {
     const uint32_t c = kr.chunk[i & 3];
     // kOOB + (k0 + c) stays >= 2^31, past every record range
     const uint32_t off = c < lim ? kr.row_off[i] + kbyte + c : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr.rsrc, (lds_ptr_t)(stage + (wave_id() * 4 + i) * 1024), 16, off, 0,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr.rsrc, (lds_ptr_t)(stage + (wave_id() * L + i) * 1024), 16, off, 0,
                                              0, 0);
   }
   __device__ __forceinline__ void issue(int j) const {
-    if (j < 4) one(*kb, sB, j, kbB, limB);
-    else one(*ka, sA, j - 4, kbA, limA);
+    if constexpr (kLeadA) {
+      if (j < kLB) one<kLB>(*kb, sB, j, kbB, limB);
+      else one<kLA>(*ka, sA, j - kLB, kbA, limA);
+    } else {
+      if (j < kLA) one<kLA>(*ka, sA, j, kbA, limA);
+      else one<kLB>(*kb, sB, j - kLA, kbB, limB);
+    }
   }
 };
 
-// Step s of the ring: read A_s from slot RA and B_s from RB; load B_{s+1} into
-// WB and A_{s+2} into WA (the slots step s - 1 read, free since its barrier);
-// then wait until at most this step's A loads (the last four issued) are in
-// flight, so B_{s+1} and A_{s+1} are in, and pass the barrier.  False after
-// the range's last step.
-template <int RA, int RB, int WB, int WA>
+// Step s of the ring: read the lead operand of step s from slot RL and the
+// follow operand from RF; load follow_{s+1} into WF and lead_{s+2} into WL (the
+// slots step s - 1 read, free since its barrier); then wait until at most this
+// step's lead loads (the last issued) are in flight, so both operands of step
+// s + 1 are in, and pass the barrier.  False after the range's last step.
+template <int kR, bool kLeadA, int RL, int RF, int WF, int WL>
 __device__ __forceinline__ bool r5_step(uint8_t* const (&slot)[5], const KRows& ka, const KRows& kb, int64_t k_begin,
-                                        int64_t k_end, int64_t& s, int64_t nk2, MfmaAcc<8>& acc) {
-  const int64_t kB = k_begin + (s + 1) * kBK, kA = k_begin + (s + 2) * kBK;
-  mfma_stage<8, kBM>(slot[RA], slot[RB], acc, StepDmaR5(ka, kb, slot[WA], slot[WB], kA, kB, k_end));
-  wait_vm4();
+                                        int64_t k_end, int64_t& s, int64_t nk2, MfmaAcc<8, kR>& acc) {
+  using D = StepDmaR5<kR, kLeadA>;
+  const int64_t kF = k_begin + (s + 1) * kBK, kL = k_begin + (s + 2) * kBK;
+  uint8_t* const rA = kLeadA ? slot[RL] : slot[RF];
+  uint8_t* const rB = kLeadA ? slot[RF] : slot[RL];
+  if constexpr (kLeadA) mfma_stage<8, kR>(rA, rB, acc, D(ka, kb, slot[WL], slot[WF], kL, kF, k_end));
+  else mfma_stage<8, kR>(rA, rB, acc, D(ka, kb, slot[WF], slot[WL], kF, kL, k_end));
+  wait_vm_ring<kLeadA ? D::kLA : D::kLB>();
   bar_raw();
   return ++s < nk2;
 }
 
-// K steps [k_begin, k_end) of a 256 x 256 tile on the ring (A and B stored
+// K steps [k_begin, k_end) of a kR x 256 tile on the ring (A and B stored
 // N x K, KRows in the step loop's 8-wave layout), accumulated into acc.  The
 // step count is rounded up to even and the steps past K load zeros, as in the
 // step loop, so the MFMAs and their order, and the bits, are the same.  The
 // slots are 32 KiB LDS arrays of the caller, who must have passed a barrier
 // since their previous use; the first loads go to slots 0-2, the first step's
 // to 3 and 4.  On return no load is in flight and every wave has passed a
-// barrier after its last read.  Item i = 2 s (A_s) or 2 s + 1 (B_s) sits in
-// slot i % 5, so the slots repeat every five steps (the loop body).
+// barrier after its last read.  Item i = 2 s (lead) or 2 s + 1 (follow) of
+// step s sits in slot i % 5, so the slots repeat every five steps (the loop
+// body).
+template <int kR, bool kLeadA>
 __device__ __forceinline__ void gemm_tile_range_r5(const KRows& ka, const KRows& kb, int64_t k_begin, int64_t k_end,
-                                                   MfmaAcc<8>& acc, uint8_t* s0, uint8_t* s1, uint8_t* s2,
+                                                   MfmaAcc<8, kR>& acc, uint8_t* s0, uint8_t* s1, uint8_t* s2,
                                                    uint8_t* s3, uint8_t* s4) {
+  using D = StepDmaR5<kR, kLeadA>;
   uint8_t* const slot[5] = {s0, s1, s2, s3, s4};
   const int64_t nk2 = ((k_end - k_begin + kBK - 1) / kBK + 1) & ~int64_t(1);
-  dma_stage<8>(ka, s0, k_begin, k_end);
-  dma_stage<8>(kb, s1, k_begin, k_end);
-  dma_stage<8>(ka, s2, k_begin + kBK, k_end);
-  wait_vm4();  // A_0 and B_0 in; A_1 may be in flight
+  auto dma_lead = [&](uint8_t* st, int64_t k0) {
+    if constexpr (kLeadA) dma_stage<8, kR>(ka, st, k0, k_end);
+    else dma_stage<8>(kb, st, k0, k_end);
+  };
+  auto dma_follow = [&](uint8_t* st, int64_t k0) {
+    if constexpr (kLeadA) dma_stage<8>(kb, st, k0, k_end);
+    else dma_stage<8, kR>(ka, st, k0, k_end);
+  };
+  dma_lead(s0, k_begin);
+  dma_follow(s1, k_begin);
+  dma_lead(s2, k_begin + kBK);
+  wait_vm_ring<kLeadA ? D::kLA : D::kLB>();  // step 0's operands in; lead_1 may be in flight
   bar_raw();
   int64_t s = 0;
-  while (r5_step<0, 1, 3, 4>(slot, ka, kb, k_begin, k_end, s, nk2, acc) &&
-         r5_step<2, 3, 0, 1>(slot, ka, kb, k_begin, k_end, s, nk2, acc) &&
-         r5_step<4, 0, 2, 3>(slot, ka, kb, k_begin, k_end, s, nk2, acc) &&
-         r5_step<1, 2, 4, 0>(slot, ka, kb, k_begin, k_end, s, nk2, acc) &&
-         r5_step<3, 4, 1, 2>(slot, ka, kb, k_begin, k_end, s, nk2, acc)) {
+  while (r5_step<kR, kLeadA, 0, 1, 3, 4>(slot, ka, kb, k_begin, k_end, s, nk2, acc) &&
+         r5_step<kR, kLeadA, 2, 3, 0, 1>(slot, ka, kb, k_begin, k_end, s, nk2, acc) &&
+         r5_step<kR, kLeadA, 4, 0, 2, 3>(slot, ka, kb, k_begin, k_end, s, nk2, acc) &&
+         r5_step<kR, kLeadA, 1, 2, 4, 0>(slot, ka, kb, k_begin, k_end, s, nk2, acc) &&
+         r5_step<kR, kLeadA, 3, 4, 1, 2>(slot, ka, kb, k_begin, k_end, s, nk2, acc)) {
   }
   // the loads issued by the last steps (zeros past k_end) land before the slots are used again
   wait_dma();

@@ -20,6 +20,10 @@
 #include "mfma_tile.hpp"
 #include "signal.hpp"
 
+#ifndef MOE_RING_LEAD_A
+#define MOE_RING_LEAD_A false
+#endif
+
 namespace sgt {
 
 namespace {
@@ -74,9 +78,14 @@ __device__ __forceinline__ bool wait_tile_rows(const MoeArgs& a, const int32_t* 
 
 // One tile of rows [r0, r0 + rows_valid) of expert e's group (rows_valid <= kR)
 // times 256 columns of W_e, on the workgroup's LDS stages.
+// The 8-wave tile with W_e stored I x H runs on the five-slot ring; which
+// operand leads (is loaded two steps ahead) is set here.
+constexpr bool kMoeRingLeadA = MOE_RING_LEAD_A;
+
 template <int kW, int kR, bool kBNK, bool kOutBf16>
 __device__ __forceinline__ void moe_tile(const MoeArgs& a, const int32_t* tok, int rows_valid, int e, int64_t r0,
-                                         int64_t n0, uint8_t* sA0, uint8_t* sB0, uint8_t* sA1, uint8_t* sB1) {
+                                         int64_t n0, uint8_t* s0, uint8_t* s1, uint8_t* s2, uint8_t* s3,
+                                         uint8_t* s4) {
   // A: gathered rows of X (row offsets < T * H * 2 < 2^31).
   KRows ka;
   ka.rsrc = make_rsrc(a.X, (uint64_t)a.T * (uint64_t)a.H * 2u);
@@ -92,7 +101,8 @@ __device__ __forceinline__ void moe_tile(const MoeArgs& a, const int32_t* tok, i
   if constexpr (kBNK) kb = krows_strided<kW>(Be + n0 * a.H, a.I - n0, a.H);
   MfmaAcc<kW, kR> acc;
   acc_zero<kW, kR>(acc);
-  gemm_tile_range_lds<kW, kBNK, kR>(ka, kb, Be, a.I, n0, a.H, 0, a.H, acc, sA0, sB0, sA1, sB1);
+  if constexpr (kW == 8 && kBNK) gemm_tile_range_r5<kR, kMoeRingLeadA>(ka, kb, 0, a.H, acc, s0, s1, s2, s3, s4);
+  else gemm_tile_range_lds<kW, kBNK, kR>(ka, kb, Be, a.I, n0, a.H, 0, a.H, acc, s0, s1, s2, s3);
   store_tile<kW, kOutBf16, 0, kR>(a.Y, r0 + rows_valid, a.I, r0, n0, acc);
 }
 
@@ -102,11 +112,23 @@ __device__ __forceinline__ void moe_tile(const MoeArgs& a, const int32_t* tok, i
 // heights share the workgroup's four LDS stages.
 template <int kW, int kRmax, bool kBNK, bool kOutBf16>
 __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) moe_consumer_bf16(MoeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t sA0[kBM * kBK * 2];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t sA1[kBM * kBK * 2];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB1[kStageBytes];
-  __shared__ int item_s, ok;
+  // LDS: the K loop's stages (the step loop's four, or the ring's five slots of
+  // 32 KiB).  With the ring the two shared words live at the start of the fifth
+  // slot: they are used only between tiles, when no load is in flight, and the
+  // ring writes that slot first in its first step, after a barrier every wave
+  // passes once it has read them.
+  constexpr bool kRing = kW == 8 && kBNK;
+  struct Words {
+    int item_s, ok;
+  };
+  __shared__ __attribute__((aligned(1024))) uint8_t s0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s3[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s4[kRing ? kStageBytes : sizeof(Words)];
+  Words* const wd = reinterpret_cast<Words*>(s4);
+  int& item_s = wd->item_s;
+  int& ok = wd->ok;
   if (a.late_blocks > 0 && (int)blockIdx.x >= (int)gridDim.x - a.late_blocks) {
     // a workgroup that may sit on a CU the producer needs: run only if every
     // producer workgroup is already running (one check, no wait)
@@ -159,9 +181,9 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) moe_consumer_bf16(MoeAr
       a.trace[item * 4 + 3] = blockIdx.x;
     }
     if (kRmax == 256 && rows_valid > 128)
-      moe_tile<kW, kRmax, kBNK, kOutBf16>(a, tok, rows_valid, e, r0, n0, sA0, sB0, sA1, sB1);
+      moe_tile<kW, kRmax, kBNK, kOutBf16>(a, tok, rows_valid, e, r0, n0, s0, s1, s2, s3, s4);
     else
-      moe_tile<kW, 128, kBNK, kOutBf16>(a, tok, rows_valid, e, r0, n0, sA0, sB0, sA1, sB1);
+      moe_tile<kW, 128, kBNK, kOutBf16>(a, tok, rows_valid, e, r0, n0, s0, s1, s2, s3, s4);
     if (a.trace && threadIdx.x == 0) a.trace[item * 4 + 2] = clock_ticks();
   }
   wait_producer_done(a.prod_done, a.prod_done_all, a.timeout_ticks, a.status);

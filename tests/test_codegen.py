@@ -69,14 +69,16 @@ def test_every_tile_kernel_keeps_its_mfma_loop(kernels):
         kw, kr = shape
         mi = kr // (kw // 2) // 32
         n = sum(1 for ln in body if ln.startswith("v_mfma_f32_32x32x16_bf16"))
-        # the K loop is unrolled over the two LDS stages: 2 x 4 substeps x (MI x 4) MFMAs; the AllGather
-        # consumer's 8-wave N x K tile holds two K loops (a whole panel at once, or K chunk by K chunk), each
-        # on the five-slot ring, unrolled over five steps; the MoE consumer with 256-row tiles holds a
-        # 256-row and a 128-row loop (the short tail of a group)
-        ring = "ag_consumer_bf16ILi8ELb1E" in name
-        want = (2 * 5 if ring else 2) * 4 * mi * 4
+        # the K loop is unrolled over the two LDS stages: 2 x 4 substeps x (MI x 4) MFMAs, or over five steps
+        # on the five-slot ring (the 8-wave tiles with both operands stored k-contiguous in the AllGather and
+        # MoE consumers); the AllGather consumer's ring tile holds two K loops (a whole panel at once, or K
+        # chunk by K chunk); the MoE consumer with 256-row tiles holds a 256-row and a 128-row loop (the
+        # short tail of a group)
+        ring = "ag_consumer_bf16ILi8ELb1E" in name or re.search(r"moe_consumer_bf16ILi8ELi\d+ELb1E", name)
+        steps = 5 if ring else 2
+        want = (2 if "ag_consumer" in name and ring else 1) * steps * 4 * mi * 4
         if "moe_consumer_bf16" in name and kr == 256:
-            want += 2 * 4 * (128 // (kw // 2) // 32) * 4
+            want += steps * 4 * (128 // (kw // 2) // 32) * 4
         assert n == want, "%s: %d MFMAs, expected %d" % (name, n, want)
         seen += 1
     # 8 AllGather, 16 MoE, 4 GEMM+RS and 4 MoE combine (B layout x Y dtype) instantiations
