@@ -20,10 +20,6 @@
 #include "mfma_tile.hpp"
 #include "signal.hpp"
 
-#ifndef MOE_RING_LEAD_A
-#define MOE_RING_LEAD_A false
-#endif
-
 namespace sgt {
 
 namespace {
@@ -76,12 +72,14 @@ __device__ __forceinline__ bool wait_tile_rows(const MoeArgs& a, const int32_t* 
   return *ok != 0;
 }
 
+// The 8-wave tile with W_e stored I x H runs on the five-slot ring with the
+// expert weights leading (loaded two steps ahead): they are the first touches
+// here (each expert's slab is read by its few row tiles), while the gathered
+// token rows are read by up to eight experts' tiles and mostly hit the caches.
+constexpr bool kMoeRingLeadA = false;
+
 // One tile of rows [r0, r0 + rows_valid) of expert e's group (rows_valid <= kR)
 // times 256 columns of W_e, on the workgroup's LDS stages.
-// The 8-wave tile with W_e stored I x H runs on the five-slot ring; which
-// operand leads (is loaded two steps ahead) is set here.
-constexpr bool kMoeRingLeadA = MOE_RING_LEAD_A;
-
 template <int kW, int kR, bool kBNK, bool kOutBf16>
 __device__ __forceinline__ void moe_tile(const MoeArgs& a, const int32_t* tok, int rows_valid, int e, int64_t r0,
                                          int64_t n0, uint8_t* s0, uint8_t* s1, uint8_t* s2, uint8_t* s3,
