@@ -138,12 +138,12 @@ struct MoeRsArgs {
   RsArgs rs;
 };
 
-// XCD-partitioned work lists of the MoE grouped consumer.  The row tiles,
-// sorted by readiness, are cut into chunks of kMoeXcdGroup consecutive tiles;
+// XCD-partitioned work lists of the MoE grouped consumer.  The row tiles, in
+// expert-major order, are cut into chunks of kMoeXcdGroup consecutive tiles;
 // chunk c goes to the list of XCD c % kXcds (the XCD that runs workgroups
 // b with b % kXcds == c % kXcds), in order.  So every XCD gets an even share of
-// each readiness window, and the tiles it runs together (the column tiles of
-// one row tile, neighbouring row tiles of one expert) share operands in its L2.
+// the list, and the tiles it runs together (the column tiles of one row tile,
+// neighbouring row tiles of one expert) share operands in its L2.
 constexpr uint32_t kMoeXcdGroup = 4;
 
 // Row tiles in XCD x's list, for n tiles in total.
@@ -176,14 +176,10 @@ struct MoeTables {
   int32_t n_groups;       // workgroups of the top-k kernel (tokens_per_group tokens each, the last ragged)
   int32_t tokens_per_group;
   uint32_t* n_tiles;      // 1: number of grouped row tiles
-  uint32_t tiles_cap;     // entries of tiles / keys / order
+  uint32_t tiles_cap;     // entries of order
   uint32_t* claim;        // 1: next consumer work item to claim
   uint32_t* xcd_claim;    // kXcds counters, kXcdClaimStride words apart: next item of each XCD's list
-  uint32_t* done;         // 1: placement workgroups finished (cleared by the top-k kernel)
-  uint32_t* ranks;        // arrival rank of each signal tile, device copy (written by the top-k kernel)
-  MoeTile* tiles;         // grouped row tiles, expert-major (written by the placement kernel)
-  uint32_t* keys;         // readiness key per entry of `tiles`
-  MoeTile* order;         // the same tiles sorted by key, in the XCD-partitioned lists (xcd_list_pos)
+  MoeTile* order;         // the row tiles, expert-major, in the XCD-partitioned lists (xcd_list_pos)
 };
 
 // Arguments of the MoE grouped consumer.

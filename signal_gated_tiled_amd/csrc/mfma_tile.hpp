@@ -378,14 +378,14 @@ __device__ __forceinline__ void gemm_tile_range_lds(const KRows& ka, const KRows
 // more (measured per kernel: the gathered rows of the AllGather consumer).
 __device__ __forceinline__ void bar_raw() { asm volatile("s_barrier" ::: "memory"); }
 
-// At most N (2, 4) of this wave's vector memory operations in flight.  The
+// At most N (0, 2, 4) of this wave's vector memory operations in flight.  The
 // compiler's own wait counting sees this builtin (it does not see an asm
 // wait), so it knows which loads are in when the next step reads their slots.
 // Encoding (gfx9): vmcnt in bits 3:0, expcnt (bits 6:4) and lgkmcnt (11:8) at
 // their maxima.
 template <int N>
 __device__ __forceinline__ void wait_vm_ring() {
-  static_assert(N == 2 || N == 4, "loads left in flight");
+  static_assert(N == 0 || N == 2 || N == 4, "loads left in flight");
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
@@ -480,7 +480,11 @@ __device__ __forceinline__ void gemm_tile_range_r5(const KRows& ka, const KRows&
   dma_lead(s0, k_begin);
   dma_follow(s1, k_begin);
   dma_lead(s2, k_begin + kBK);
-  wait_vm_ring<kLeadA ? D::kLA : D::kLB>();  // step 0's operands in; lead_1 may be in flight
+  // All three in before the loop.  Leaving lead_1 in flight here (it lands soon
+  // after follow_0) makes the compiler's wait counting, which cannot tell
+  // these loads from the loop's own at the loop head, wait for every load at
+  // the head of each five-step body instead.
+  wait_vm_ring<0>();
   bar_raw();
   int64_t s = 0;
   while (r5_step<kR, kLeadA, 0, 1, 3, 4>(slot, ka, kb, k_begin, k_end, s, nk2, acc) &&

@@ -6,9 +6,10 @@
 // Work item = (grouped row tile, column tile): rows [r0, r0 + kR) of one
 // expert's group (clipped to the group; kR = 128 or 256) times 256 columns of that expert's
 // weight.  Persistent workgroups claim items from their XCD's share of the
-// readiness-ordered list with an atomic counter per XCD (the column tiles of a
-// row tile are consecutive items, so they run side by side on one XCD and
-// read the gathered rows from its L2), then help the other XCDs.  Before
+// expert-major list with an atomic counter per XCD (the column tiles of a row
+// tile are consecutive items, and so are an expert's row tiles, so they run
+// side by side on one XCD and read the gathered rows and the expert's weight
+// columns from its L2), then help the other XCDs.  Before
 // loading, wave 0 polls, lane by lane, the flag of the signal tile that holds
 // each row's token (a tile waits for exactly the tokens it reads); then the
 // rows are gathered straight into LDS

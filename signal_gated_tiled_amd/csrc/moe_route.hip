@@ -1,9 +1,8 @@
 // MoE routing on the GPU: top-k experts per token, rows grouped by expert, and
-// the grouped consumer's work list ordered by when its rows can arrive
-// (paper summary, "Experiments": MoE routing operations among the
-// communication-bound kernels; DITRON article, "three-level tiling": the
-// device-level tiles of an MoE layer take their sizes from how many tokens each
-// expert receives, known only at run time).
+// the grouped consumer's work list (paper summary, "Experiments": MoE routing
+// operations among the communication-bound kernels; DITRON article,
+// "three-level tiling": the device-level tiles of an MoE layer take their
+// sizes from how many tokens each expert receives, known only at run time).
 //
 // Two launches:
 //  1. moe_topk_kernel  -- one wave per token, one lane per expert (up to four
@@ -12,16 +11,14 @@
 //     (one bit per expert), and each workgroup adds how many of its tokens
 //     chose each expert to the call's counts.
 //  2. moe_place_kernel -- one workgroup per expert: prefix sums of the counts
-//     over experts give its first row
-//     (expert_off) and first row tile; one pass over the tokens' mask words in
-//     ascending token order (a prefix sum over threads) places each token that
-//     chose the expert at the next row of its group.  Each group is cut into
-//     row tiles of the consumer's tile height; the readiness key of a row tile
-//     is the latest arrival rank among the signal tiles its rows come from.
-//  3. the last placement workgroup to finish sorts the row tiles by readiness
-//     key (stable counting sort), so the consumer claims first the tiles whose
-//     rows land first, and deals the sorted tiles out to per-XCD lists in
-//     chunks of a few consecutive tiles (xcd_list_pos).
+//     over experts give its first row (expert_off) and first row tile; one
+//     pass over the tokens' mask words in ascending token order (a prefix sum
+//     over threads) places each token that chose the expert at the next row of
+//     its group.  Each group is cut into row tiles of the consumer's tile
+//     height, and the workgroup writes its expert's tiles into the work list
+//     in expert-major order, dealt out to per-XCD lists in chunks of a few
+//     consecutive tiles (xcd_list_pos): the tiles of one expert that an XCD
+//     runs side by side read the same weight columns through its L2.
 // No table depends on the order of concurrent updates: counts are integer
 // sums, positions are prefix sums over tokens.  The counts are double-buffered
 // by call parity: each call's top-k kernel clears the next call's buffer.
@@ -32,10 +29,6 @@
 namespace sgt {
 
 namespace {
-
-constexpr int kMaxTilesPerExpert = 4096;
-constexpr int kSortBuckets = 256;
-constexpr int kRankCache = 4096;       // arrival ranks staged in LDS (signal tiles per call)
 
 // Order-preserving map of an fp32 value to uint32 (total order; -0 and +0
 // compare equal, as floating-point comparison has them).
@@ -91,21 +84,11 @@ template <int kSlots>
 __global__ void __launch_bounds__(64 * kTopkWaves) moe_topk_kernel(const float* __restrict__ logits, int64_t T, int E,
                                                                   int k, int tpg, int32_t* __restrict__ topk_ids,
                                                                   uint32_t* __restrict__ masks, uint32_t* counts,
-                                                                  uint32_t* counts_next, uint32_t* done,
-                                                                  const uint32_t* rank_host, uint32_t* rank_dev,
-                                                                  uint32_t n_flags) {
+                                                                  uint32_t* counts_next) {
   __shared__ uint32_t cnt[256];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  // The arrival ranks come from pinned host memory: each workgroup copies a
-  // slice to device memory, so the placement reads them from HBM.
-  if (rank_host) {
-    const uint32_t per = (n_flags + gridDim.x - 1) / gridDim.x, f0 = blockIdx.x * per;
-    for (uint32_t f = f0 + tid; f < f0 + per && f < n_flags; f += blockDim.x) rank_dev[f] = rank_host[f];
-  }
-  if (blockIdx.x == 0) {
-    if (tid == 0) *done = 0u;                  // the placement's completion count for this call
-    if (tid < 256) counts_next[tid] = 0u;      // all 256 entries: the next call may have more experts
-  }
+  // all 256 entries: the next call may have more experts
+  if (blockIdx.x == 0 && tid < 256) counts_next[tid] = 0u;
   const int nw = (E + 31) >> 5;
   if (tid < 256) cnt[tid] = 0u;
   __syncthreads();
@@ -193,61 +176,15 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* s
   return before + incl - x;
 }
 
-// Stable counting sort of the row tiles by readiness key (keys < n_keys,
-// folded into 256 buckets) by one workgroup of 256 threads; base and chunk_b
-// are 256 words of LDS each, sh the scan scratch.
-__device__ void sort_row_tiles(const MoeTables& tb, uint32_t n_keys, uint32_t* base, uint32_t* chunk_b,
-                               uint32_t* sh) {
-  const int tid = threadIdx.x;
-  const uint32_t n = *tb.n_tiles < tb.tiles_cap ? *tb.n_tiles : tb.tiles_cap;
-  auto bucket = [&](uint32_t key) -> uint32_t {
-    if (n_keys <= kSortBuckets) return key < n_keys ? key : n_keys - 1;
-    const uint64_t b = (uint64_t)key * kSortBuckets / n_keys;
-    return b < kSortBuckets ? (uint32_t)b : kSortBuckets - 1;
-  };
-  base[tid] = 0u;
-  __syncthreads();
-  for (uint32_t i = tid; i < n; i += 256) atomicAdd(&base[bucket(tb.keys[i])], 1u);
-  __syncthreads();
-  uint32_t total;
-  const uint32_t first = block_exclusive_scan(base[tid], sh, &total);
-  base[tid] = first;
-  __syncthreads();
-  // Stable placement, 256 entries at a time: an entry's rank inside its bucket
-  // is the number of earlier entries of the chunk with the same bucket.
-  for (uint32_t c0 = 0; c0 < n; c0 += 256) {
-    const uint32_t i = c0 + tid;
-    const uint32_t b = i < n ? bucket(tb.keys[i]) : 0xFFFFFFFFu;
-    chunk_b[tid] = b;
-    __syncthreads();
-    if (i < n) {
-      uint32_t rank = 0;
-      for (int j = 0; j < tid; ++j) rank += chunk_b[j] == b;
-      tb.order[xcd_list_pos(base[b] + rank, n)] = tb.tiles[i];
-    }
-    __syncthreads();
-    if (i < n) atomicAdd(&base[b], 1u);
-    __syncthreads();
-  }
-}
-
 // One workgroup (256 threads) per expert.
 __global__ void __launch_bounds__(256) moe_place_kernel(const uint32_t* __restrict__ masks, int64_t T, int E,
-                                                        const uint32_t* __restrict__ rank_of_flag, int32_t flag_rows,
-                                                        int tile_rows, int tile_shift, int64_t rows_cap, MoeTables tb,
+                                                        int tile_rows, int64_t rows_cap, MoeTables tb,
                                                         int32_t* __restrict__ expert_off,
                                                         int32_t* __restrict__ row_token) {
   __shared__ uint32_t sh[256];
-  __shared__ uint32_t keys[kMaxTilesPerExpert];
-  __shared__ uint32_t ranks[kRankCache];
-  __shared__ uint32_t my_row0, my_tile0, my_count;
+  __shared__ uint32_t my_row0, my_tile0, my_count, n_tiles;
   const int tid = threadIdx.x;
   const int e = blockIdx.x;
-  // The arrival ranks may live in host memory: read each once into LDS.
-  const int64_t n_flags = (T + flag_rows - 1) / flag_rows;
-  const bool cached = rank_of_flag && n_flags <= kRankCache;
-  if (cached)
-    for (int64_t f = tid; f < n_flags; f += 256) ranks[f] = rank_of_flag[f];
 
   // First row and first row tile of every expert: prefix sums over experts.
   const uint32_t c = tid < E ? tb.counts[tid] : 0u;
@@ -260,6 +197,7 @@ __global__ void __launch_bounds__(256) moe_place_kernel(const uint32_t* __restri
     my_tile0 = tile0;
     my_count = c;
   }
+  if (tid == 0) n_tiles = tiles_total;
   if (e == 0) {
     if (tid < E) expert_off[tid] = (int32_t)row0;
     if (tid == 0) {
@@ -270,13 +208,14 @@ __global__ void __launch_bounds__(256) moe_place_kernel(const uint32_t* __restri
     if (tid < kXcds) tb.xcd_claim[tid * kXcdClaimStride] = 0u;
   }
   __syncthreads();
-  const uint32_t n_e = my_count, base_row = my_row0, base_tile = my_tile0;
-  // (counts are exact by construction; the clamps only keep every index inside
-  // its buffer whatever the tables hold)
-  uint32_t nt_e = (n_e + tile_rows - 1) / tile_rows;
-  nt_e = nt_e < (uint32_t)kMaxTilesPerExpert ? nt_e : (uint32_t)kMaxTilesPerExpert;
-  for (uint32_t j = tid; j < nt_e; j += 256) keys[j] = 0u;
-  __syncthreads();
+  const uint32_t n_e = my_count, base_row = my_row0, base_tile = my_tile0, nt = n_tiles;
+
+  // This expert's row tiles, in row order, at their places in the XCD lists.
+  const uint32_t nt_e = (n_e + tile_rows - 1) / tile_rows;
+  for (uint32_t j = tid; j < nt_e; j += 256) {
+    const uint32_t q = xcd_list_pos(base_tile + j, nt);  // < nt (base_tile + j < nt)
+    if (q < tb.tiles_cap) tb.order[q] = MoeTile{e, (int32_t)(base_row + j * tile_rows)};
+  }
 
   // Place the tokens that chose e, in ascending token order: thread i takes
   // 16 consecutive tokens of each 4096-token round.
@@ -293,56 +232,19 @@ __global__ void __launch_bounds__(256) moe_place_kernel(const uint32_t* __restri
     for (int u = 0; u < 16; ++u) sel |= ((m[u] >> bit) & 1u) << u;
     uint32_t total;
     uint32_t pos = placed + block_exclusive_scan((uint32_t)__popc(sel), sh, &total);
-    // A thread's (at most 16) rows are consecutive, so they touch at most two
-    // row tiles: reduce the keys locally and update each tile once.
-    uint32_t cur_tile = 0xFFFFFFFFu, cur_key = 0u;
+    // (counts are exact by construction; the bound only keeps every store
+    // inside row_token whatever the tables hold)
     while (sel) {
       const int u = __ffs(sel) - 1;
       sel &= sel - 1u;
-      const uint32_t t = (uint32_t)(t0 + u);  // T <= 2^20
-      if ((int64_t)base_row + pos < rows_cap) row_token[base_row + pos] = (int32_t)t;
-      const uint32_t f = t / (uint32_t)flag_rows;
-      const uint32_t key = cached ? ranks[f] : (rank_of_flag ? rank_of_flag[f] : 0u);
-      uint32_t tile = pos >> tile_shift;
-      tile = tile < nt_e ? tile : nt_e - 1;
-      if (tile != cur_tile) {
-        if (cur_tile != 0xFFFFFFFFu) atomicMax(&keys[cur_tile], cur_key);
-        cur_tile = tile;
-        cur_key = key;
-      } else {
-        cur_key = key > cur_key ? key : cur_key;
-      }
+      if ((int64_t)base_row + pos < rows_cap) row_token[base_row + pos] = (int32_t)(t0 + u);  // T <= 2^20
       ++pos;
     }
-    if (cur_tile != 0xFFFFFFFFu) atomicMax(&keys[cur_tile], cur_key);
     placed += total;
   }
-  __syncthreads();
-  // The tiles and keys the sorting workgroup reads go out with device-scope
-  // stores (written through to the coherence point), so publishing them needs
-  // no L2 write-back: each wave waits for its stores' acknowledgement, then one
-  // relaxed device-scope increment counts the workgroup done.
-  for (uint32_t j = tid; j < nt_e && base_tile + j < tb.tiles_cap; j += 256) {
-    int32_t* tile = reinterpret_cast<int32_t*>(tb.tiles + base_tile + j);
-    __hip_atomic_store(tile, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(tile + 1, (int32_t)(base_row + j * tile_rows), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(tb.keys + base_tile + j, keys[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __shared__ int last;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (tid == 0)
-    last = __hip_atomic_fetch_add(tb.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(E - 1);
-  __syncthreads();
-  if (!last) return;
-  // the last workgroup: drop any stale cached copy before reading the others' tables
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  sort_row_tiles(tb, (uint32_t)n_flags, keys, keys + kSortBuckets, sh);
 }
 
 }  // namespace
-
-int moe_max_tiles_per_expert() { return kMaxTilesPerExpert; }
 
 // Tokens per top-k workgroup: 64 (four per wave), or more when that would
 // make over 4096 groups.
@@ -353,24 +255,21 @@ int moe_tokens_per_group(int64_t T, int k) {
   return (int)tpg;
 }
 
-hipError_t launch_moe_route(const float* logits, int64_t T, int E, int k, const uint32_t* rank_of_flag,
-                            int32_t flag_rows, uint32_t n_flags, int tile_rows, const MoeTables& tb,
+hipError_t launch_moe_route(const float* logits, int64_t T, int E, int k, int tile_rows, const MoeTables& tb,
                             int32_t* expert_off, int32_t* row_token, int32_t* topk_ids, hipStream_t stream) {
   const dim3 g((unsigned)tb.n_groups), b(64 * kTopkWaves);
   const int slots = (E + 63) / 64;
-  uint32_t* rank_dev = rank_of_flag ? tb.ranks : nullptr;
   if (slots == 1)
     hipLaunchKernelGGL(moe_topk_kernel<1>, g, b, 0, stream, logits, T, E, k, tb.tokens_per_group, topk_ids, tb.masks,
-                       tb.counts, tb.counts_next, tb.done, rank_of_flag, rank_dev, n_flags);
+                       tb.counts, tb.counts_next);
   else if (slots == 2)
     hipLaunchKernelGGL(moe_topk_kernel<2>, g, b, 0, stream, logits, T, E, k, tb.tokens_per_group, topk_ids, tb.masks,
-                       tb.counts, tb.counts_next, tb.done, rank_of_flag, rank_dev, n_flags);
+                       tb.counts, tb.counts_next);
   else
     hipLaunchKernelGGL(moe_topk_kernel<4>, g, b, 0, stream, logits, T, E, k, tb.tokens_per_group, topk_ids, tb.masks,
-                       tb.counts, tb.counts_next, tb.done, rank_of_flag, rank_dev, n_flags);
-  const int shift = tile_rows == 128 ? 7 : 8;
-  hipLaunchKernelGGL(moe_place_kernel, dim3((unsigned)E), dim3(256), 0, stream, tb.masks, T, E,
-                     (const uint32_t*)rank_dev, flag_rows, tile_rows, shift, T * k, tb, expert_off, row_token);
+                       tb.counts, tb.counts_next);
+  hipLaunchKernelGGL(moe_place_kernel, dim3((unsigned)E), dim3(256), 0, stream, tb.masks, T, E, tile_rows, T * k, tb,
+                     expert_off, row_token);
   return hipGetLastError();
 }
 

@@ -46,10 +46,8 @@ int ag_panel_rows(int in_dtype);
 int ag_panel_cols(int in_dtype);
 hipError_t launch_gemm_rs(const RsArgs& a, int grid, hipStream_t stream);
 int rs_gemm_tile();
-int moe_max_tiles_per_expert();
 int moe_tokens_per_group(int64_t T, int k);
-hipError_t launch_moe_route(const float* logits, int64_t T, int E, int k, const uint32_t* rank_of_flag,
-                            int32_t flag_rows, uint32_t n_flags, int tile_rows, const MoeTables& tb,
+hipError_t launch_moe_route(const float* logits, int64_t T, int E, int k, int tile_rows, const MoeTables& tb,
                             int32_t* expert_off, int32_t* row_token, int32_t* topk_ids, hipStream_t stream);
 hipError_t launch_moe_rs(const MoeRsArgs& a, int grid, hipStream_t stream);
 hipError_t launch_moe_consumer(const MoeArgs& a, int b_layout, int out_dtype, int tile_rows, int tile_waves, int grid,
@@ -92,6 +90,7 @@ constexpr int kAgStartedWord = 32, kAgDoneWord = 48, kAgClaimWord = 64;  // clai
 constexpr int kSdmaMaxUnits = 4096;       // copy-engine copies per call
 constexpr int64_t kSdmaUnitBytes = 4 << 20;  // bytes per copy-engine copy (whole-row signal tiles grouped up to this)
 constexpr int64_t kItemsCap = 1 << 18;    // signal tiles per call
+constexpr int64_t kMoeMaxTokens = 1 << 20;  // tokens of one MoE AllGather call
 constexpr double kTicksPerUs = 100.0;     // constant GPU clock: 100 MHz
 
 }  // namespace
@@ -109,19 +108,14 @@ struct sgt_ctx {
   int ag_claim_parity = 0;         // which of the two AllGather claim-counter sets the next consumer uses
   ProdItem* h_items[kSlots] = {};
   ProdItem* d_items[kSlots] = {};
-  uint32_t* h_ranks[kSlots] = {};  // arrival rank of each signal tile (MoE work ordering), pinned host
-  uint32_t* d_ranks[kSlots] = {};  // the same memory as the GPU addresses it (read in place, no copy)
-  uint32_t* d_moe = nullptr;       // MoE: tile count, claim counter, done count, producer started and finished
-                                   // counts, per-XCD claim
-                                   // counters (words 64 + 16 x), counts[2][256] by call parity (words 256..767)
+  uint32_t* d_moe = nullptr;       // MoE: tile count, claim counter, producer started and finished counts,
+                                   // per-XCD claim counters (words 64 + 16 x), counts[2][256] by call parity
+                                   // (words 256..767)
   int moe_parity = 0;
   uint32_t moe_prod_started = 0;   // producer workgroups launched by overlapped MoE calls (cumulative)
   uint32_t moe_prod_done = 0;      // of those, the ones that count themselves finished (cumulative)
-  MoeTile* d_moe_tiles = nullptr;  // MoE row tiles, expert-major and sorted; grow on demand
-  MoeTile* d_moe_order = nullptr;
-  uint32_t* d_moe_keys = nullptr;
+  MoeTile* d_moe_order = nullptr;  // MoE row tiles in the XCD-partitioned work lists; grow on demand
   int64_t moe_cap = 0;
-  uint32_t* d_moe_ranks = nullptr; // MoE: device copy of a call's arrival ranks (kItemsCap words)
   uint32_t* d_moe_masks = nullptr; // MoE token bitmasks; grow on demand
   int64_t moe_masks_cap = 0;
   // MoE combine side: inverse routing table, group row tiles, counters (tile
@@ -333,8 +327,7 @@ int64_t interleaved_chunk(const AgPlan& p, int64_t k) {
 }
 
 int build_schedule(const AgPlan& p, int W, int rank, int64_t K, int esz, const sgt_opts& o,
-                   const void* const* shards, void* gathered, ProdItem* items, bool local_first = false,
-                   uint32_t* ranks = nullptr) {
+                   const void* const* shards, void* gathered, ProdItem* items, bool local_first = false) {
   // a K-chunked signal tile is one panel's rows x one column chunk
   const double tile_bytes = (double)p.flag_rows * (double)(p.n_kc > 0 ? p.kc_cols : K) * esz;
   const double ticks_per_tile = o.peer_gbps > 0 ? tile_bytes / (o.peer_gbps * 1e3) * kTicksPerUs : 0.0;
@@ -394,7 +387,6 @@ int build_schedule(const AgPlan& p, int W, int rank, int64_t K, int esz, const s
       items[i].src = static_cast<const char*>(shards[items[i].peer]) + local_tile * (int64_t)tile_bytes;
       items[i].dst = static_cast<char*>(gathered) + tile * (int64_t)tile_bytes;
     }
-    if (ranks) ranks[tile] = (uint32_t)i;
   }
   return n;
 }
@@ -834,14 +826,11 @@ sgt_status sgt_ctx_create(sgt_ctx** out, int device) {
   if (st == SGT_OK) chk(hipMemset(c->d_counters, 0, kCounterWords * sizeof(uint32_t)), "hipMemset(counters)");
   chk(hipMalloc(&c->d_moe, 1024 * sizeof(uint32_t)), "hipMalloc(moe)");
   if (st == SGT_OK) chk(hipMemset(c->d_moe, 0, 1024 * sizeof(uint32_t)), "hipMemset(moe)");
-  chk(hipMalloc(&c->d_moe_ranks, kItemsCap * sizeof(uint32_t)), "hipMalloc(moe ranks)");
   chk(hipMalloc(&c->d_a2a_counts, kA2aMaxE * sizeof(int32_t)), "hipMalloc(a2a counts)");
   if (st == SGT_OK) chk(hipMemset(c->d_status, 0, 4 * sizeof(uint32_t)), "hipMemset");
   for (int s = 0; s < kSlots && st == SGT_OK; ++s) {
     chk(hipHostMalloc(&c->h_items[s], kItemsCap * sizeof(ProdItem), hipHostMallocDefault), "hipHostMalloc");
     chk(hipMalloc(&c->d_items[s], kItemsCap * sizeof(ProdItem)), "hipMalloc(items)");
-    chk(hipHostMalloc(&c->h_ranks[s], kItemsCap * sizeof(uint32_t), hipHostMallocDefault), "hipHostMalloc");
-    if (st == SGT_OK) chk(hipHostGetDevicePointer((void**)&c->d_ranks[s], c->h_ranks[s], 0), "hipHostGetDevicePointer");
     chk(hipEventCreateWithFlags(&c->slot_ev[s], hipEventDisableTiming), "hipEventCreate");
   }
   if (st != SGT_OK) {
@@ -877,17 +866,13 @@ sgt_status sgt_ctx_destroy(sgt_ctx* c) {
   for (int s = 0; s < kSlots; ++s) {
     if (c->h_items[s]) (void)hipHostFree(c->h_items[s]);
     if (c->d_items[s]) (void)hipFree(c->d_items[s]);
-    if (c->h_ranks[s]) (void)hipHostFree(c->h_ranks[s]);
     if (c->slot_ev[s]) (void)hipEventDestroy(c->slot_ev[s]);
   }
   if (c->d_status) (void)hipFree(c->d_status);
   if (c->d_counters) (void)hipFree(c->d_counters);
   if (c->d_moe) (void)hipFree(c->d_moe);
-  if (c->d_moe_tiles) (void)hipFree(c->d_moe_tiles);
   if (c->d_moe_order) (void)hipFree(c->d_moe_order);
-  if (c->d_moe_keys) (void)hipFree(c->d_moe_keys);
   if (c->d_moe_masks) (void)hipFree(c->d_moe_masks);
-  if (c->d_moe_ranks) (void)hipFree(c->d_moe_ranks);
   if (c->d_mrs_rowof) (void)hipFree(c->d_mrs_rowof);
   if (c->d_mrs_tiles) (void)hipFree(c->d_mrs_tiles);
   if (c->d_mrs_ctr) (void)hipFree(c->d_mrs_ctr);
@@ -1459,9 +1444,8 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   if (T < 0 || H < 1 || I < 0) return fail(SGT_EINVAL, "bad shape T=%lld H=%lld I=%lld", (long long)T, (long long)H,
                                            (long long)I);
   const int rows = moe_tile_rows(o);
-  if (T > (int64_t)moe_max_tiles_per_expert() * rows)
-    return fail(SGT_EUNSUPPORTED, "T = %lld tokens exceeds %lld", (long long)T,
-                (long long)moe_max_tiles_per_expert() * rows);
+  if (T > kMoeMaxTokens) return fail(SGT_EUNSUPPORTED, "T = %lld tokens exceeds %lld", (long long)T,
+                                     (long long)kMoeMaxTokens);
   AgPlan p;
   if ((st = plan_ag(W, T, H, I, o, &p)) != SGT_OK) return st;
   const int64_t lim = (int64_t)1 << 31;
@@ -1500,16 +1484,11 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   if (ctx->moe_cap < max_tiles || ctx->moe_masks_cap < mask_words) {
     HIP_TRY(hipDeviceSynchronize());
     if (ctx->moe_cap < max_tiles) {
-      if (ctx->d_moe_tiles) (void)hipFree(ctx->d_moe_tiles);
       if (ctx->d_moe_order) (void)hipFree(ctx->d_moe_order);
-      if (ctx->d_moe_keys) (void)hipFree(ctx->d_moe_keys);
-      ctx->d_moe_tiles = ctx->d_moe_order = nullptr;
-      ctx->d_moe_keys = nullptr;
+      ctx->d_moe_order = nullptr;
       ctx->moe_cap = 0;
       const int64_t cap = std::max<int64_t>(max_tiles, 1024);
-      HIP_TRY(hipMalloc(&ctx->d_moe_tiles, cap * sizeof(MoeTile)));
       HIP_TRY(hipMalloc(&ctx->d_moe_order, cap * sizeof(MoeTile)));
-      HIP_TRY(hipMalloc(&ctx->d_moe_keys, cap * sizeof(uint32_t)));
       ctx->moe_cap = cap;
     }
     if (ctx->moe_masks_cap < mask_words) {
@@ -1531,10 +1510,6 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   tb.tiles_cap = (uint32_t)ctx->moe_cap;
   tb.claim = ctx->d_moe + 4;
   tb.xcd_claim = ctx->d_moe + 64;  // kXcds counters at words 64, 80, ..., 176
-  tb.done = ctx->d_moe + 8;
-  tb.ranks = ctx->d_moe_ranks;
-  tb.tiles = ctx->d_moe_tiles;
-  tb.keys = ctx->d_moe_keys;
   tb.order = ctx->d_moe_order;
 
   const int esz = 2;
@@ -1555,9 +1530,8 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   // for the producer; the others (the last launched - keep) yield unless every
   // producer workgroup already runs.  The split is taken on the grid actually
   // launched, so a grid of keep workgroups or fewer never yields.
-  auto route_and_compute = [&](const uint32_t* ranks, int grid, int keep) -> sgt_status {
-    HIP_TRY(launch_moe_route(logits, T, E, topk, ranks, a.flag_rows, (uint32_t)p.n_flags, rows, tb, expert_off,
-                             row_token, topk_ids, stream));
+  auto route_and_compute = [&](int grid, int keep) -> sgt_status {
+    HIP_TRY(launch_moe_route(logits, T, E, topk, rows, tb, expert_off, row_token, topk_ids, stream));
     ctx->moe_parity ^= 1;  // this call's top-k cleared the other counts buffer for the next call
     if (I > 0) {
       const int launched = (int)std::max<int64_t>(1, std::min<int64_t>(grid, n_items_max));
@@ -1574,26 +1548,21 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   if (o.producer == SGT_PROD_PRESET) {
     // X_gathered already holds every shard: all flags take the epoch.
     HIP_TRY(launch_fill_u32(shard_flags, p.n_flags, e, stream));
-    if ((st = route_and_compute(nullptr, o.consumer_cus > 0 ? std::min(o.consumer_cus, ctx->n_cu) : ctx->n_cu, 0)) !=
-        SGT_OK)
+    if ((st = route_and_compute(o.consumer_cus > 0 ? std::min(o.consumer_cus, ctx->n_cu) : ctx->n_cu, 0)) != SGT_OK)
       return st;
     return finish(ctx, o, stream);
   }
 
   int slot;
   if ((st = next_slot(ctx, &slot)) != SGT_OK) return st;
-  const int n_items =
-      build_schedule(p, W, o.rank, H, esz, o, X_shards, X_gathered, ctx->h_items[slot], true, ctx->h_ranks[slot]);
+  const int n_items = build_schedule(p, W, o.rank, H, esz, o, X_shards, X_gathered, ctx->h_items[slot], true);
   const int pwg = std::min(default_producer_wgs(o, ctx->n_cu), n_items);
-  // The placement kernel reads the arrival ranks straight from pinned host
-  // memory (a few words per workgroup); the producer's schedule is copied on
-  // the stream that runs the producer.
+  // The producer's schedule is copied on the stream that runs the producer.
   if (o.producer == SGT_PROD_SERIAL) {
     if ((st = upload_items(ctx, slot, ctx->h_items[slot], n_items, stream)) != SGT_OK) return st;
     HIP_TRY(launch_ag_producer(shard_flags, ctx->d_items[slot], n_items, tile_bytes, e, o.withhold_peer,
                                trace_rel, pwg, stream));
-    if ((st = route_and_compute(ctx->d_ranks[slot], o.consumer_cus > 0 ? std::min(o.consumer_cus, ctx->n_cu)
-                                                                         : ctx->n_cu, 0)) != SGT_OK)
+    if ((st = route_and_compute(o.consumer_cus > 0 ? std::min(o.consumer_cus, ctx->n_cu) : ctx->n_cu, 0)) != SGT_OK)
       return st;
     HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
     ctx->slot_used[slot] = true;
@@ -1631,8 +1600,7 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   // beside the producer's share rounded up as for the other overlapped calls,
   // so they are spread evenly over the XCDs; a caller's count is capped there)
   const int keep = consumer_beside(ctx, pwg);
-  if ((st = route_and_compute(ctx->d_ranks[slot], o.consumer_cus > 0 ? std::min(o.consumer_cus, keep) : ctx->n_cu,
-                              keep)) != SGT_OK)
+  if ((st = route_and_compute(o.consumer_cus > 0 ? std::min(o.consumer_cus, keep) : ctx->n_cu, keep)) != SGT_OK)
     return st;
   if (!gpu_join) HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
   HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
