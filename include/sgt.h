@@ -386,9 +386,12 @@ SGT_API sgt_status sgt_moe_gemm_rs_paced(sgt_ctx* ctx, const void* Hg, const voi
                                          const sgt_opts* opts, void* stream);
 
 /* Words of the optional trace buffer of an sgt_moe_ag_gemm call: 4 x uint64
- * {wait start, flags seen, tile end, workgroup} per work item in claim order
- * (room for the largest possible routing), then 1 x uint64 release time per
- * signal tile. */
+ * {wait start, flags seen, tile end, workgroup} per work item, indexed by the
+ * item's place in the consumer's work list (room for the largest possible
+ * routing), then 1 x uint64 release time per signal tile.  Times are the
+ * 100 MHz constant GPU clock; the last word holds the workgroup in bits 0..15
+ * and the item's engine-clock cycles (from its wait start to its end) in bits
+ * 16..63. */
 SGT_API int64_t sgt_moe_trace_words(int W, int64_t T, int64_t H, int64_t I, int E, int topk, const sgt_opts* opts);
 
 /*

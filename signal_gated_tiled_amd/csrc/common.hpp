@@ -108,11 +108,12 @@ struct RsArgs {
   uint64_t timeout_ticks;
 };
 
-// One grouped row tile of the MoE consumer: rows [r0, r0 + tile rows) of
-// expert e's group (clipped to the group's end).
+// One grouped row tile: rows [r0, r0 + rows) of expert e's group (rows at
+// most the tile height; the tile ends at the group's end or earlier).
 struct MoeTile {
   int32_t expert;
   int32_t r0;       // first row (index into the grouped rows of Y)
+  int32_t rows;
 };
 
 // MoE GEMM + ReduceScatter (the combine side).  `rs` carries the

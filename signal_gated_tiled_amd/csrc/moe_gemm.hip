@@ -80,11 +80,12 @@ __device__ __forceinline__ bool wait_tile_rows(const MoeArgs& a, const int32_t* 
 constexpr bool kMoeRingLeadA = false;
 
 // One tile of rows [r0, r0 + rows_valid) of expert e's group (rows_valid <= kR)
-// times 256 columns of W_e, on the workgroup's LDS stages.
-template <int kW, int kR, bool kBNK, bool kOutBf16>
+// times 256 columns of W_e, on the workgroup's LDS stages; between() runs after
+// the K loop, before the results are stored.
+template <int kW, int kR, bool kBNK, bool kOutBf16, class Between>
 __device__ __forceinline__ void moe_tile(const MoeArgs& a, const int32_t* tok, int rows_valid, int e, int64_t r0,
                                          int64_t n0, uint8_t* s0, uint8_t* s1, uint8_t* s2, uint8_t* s3,
-                                         uint8_t* s4) {
+                                         uint8_t* s4, Between&& between) {
   // A: gathered rows of X (row offsets < T * H * 2 < 2^31).
   KRows ka;
   ka.rsrc = make_rsrc(a.X, (uint64_t)a.T * (uint64_t)a.H * 2u);
@@ -102,7 +103,45 @@ __device__ __forceinline__ void moe_tile(const MoeArgs& a, const int32_t* tok, i
   acc_zero<kW, kR>(acc);
   if constexpr (kW == 8 && kBNK) gemm_tile_range_r5<kR, kMoeRingLeadA>(ka, kb, 0, a.H, acc, s0, s1, s2, s3, s4);
   else gemm_tile_range_lds<kW, kBNK, kR>(ka, kb, Be, a.I, n0, a.H, 0, a.H, acc, s0, s1, s2, s3);
+  between();
   store_tile<kW, kOutBf16, 0, kR>(a.Y, r0 + rows_valid, a.I, r0, n0, acc);
+}
+
+// The next work item for wave 0 (the same value in all its lanes), or -1 once
+// every list is used up: one atomic on the home XCD's list while it has items;
+// after that, every list's counter read at once (one lane each) and an atomic
+// only on those that still show items.  home_left is wave 0's record that its
+// home list may still have items.
+__device__ __forceinline__ int claim_item(const MoeArgs& a, uint32_t nt, int home, bool& home_left) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t tn = (uint32_t)a.tiles_n;
+  int item = -1;
+  if (home_left) {
+    if (lane == 0) {
+      const uint32_t len = xcd_list_len(nt, home) * tn;
+      const uint32_t c = len ? atomicAdd(a.xcd_claim + home * kXcdClaimStride, 1u) : len;
+      if (c < len) item = (int)(xcd_list_start(nt, home) * tn + c);
+    }
+    item = __shfl(item, 0);
+    home_left = item >= 0;
+    if (home_left) return item;
+  }
+  const uint32_t len = lane < kXcds ? xcd_list_len(nt, lane) * tn : 0u;
+  const uint32_t seen = lane < kXcds && lane != home
+                            ? __hip_atomic_load(a.xcd_claim + lane * kXcdClaimStride, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT)
+                            : len;
+  const uint64_t open = __ballot(seen < len);
+  if (lane == 0) {
+    for (int k = 1; k < kXcds && item < 0; ++k) {
+      const int x = (home + k) % kXcds;
+      if (!((open >> x) & 1u)) continue;
+      const uint32_t lx = xcd_list_len(nt, x) * tn;
+      const uint32_t c = atomicAdd(a.xcd_claim + x * kXcdClaimStride, 1u);
+      if (c < lx) item = (int)(xcd_list_start(nt, x) * tn + c);
+    }
+  }
+  return __shfl(item, 0);
 }
 
 // kRmax = 256: a row tile of more than 128 valid rows runs as a 256-row tile,
@@ -139,51 +178,59 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) moe_consumer_bf16(MoeAr
   const uint32_t nt_raw = *a.n_tiles;
   const uint32_t nt = nt_raw < a.tiles_cap ? nt_raw : a.tiles_cap;
   // Work items come from the list of this workgroup's XCD (workgroup b runs on
-  // XCD b % kXcds), then, once it is used up, from the other XCDs' lists in turn.
-  int x = (int)(blockIdx.x % kXcds), lists_left = kXcds;
-  while (true) {
-    if (threadIdx.x == 0) {
-      int item = -1;
-      while (lists_left > 0) {
-        const uint32_t len = xcd_list_len(nt, x) * (uint32_t)a.tiles_n;
-        const uint32_t c = len ? atomicAdd(a.xcd_claim + x * kXcdClaimStride, 1u) : len;
-        if (c < len) {
-          item = (int)(xcd_list_start(nt, x) * (uint32_t)a.tiles_n + c);
-          break;
-        }
-        x = (x + 1) % kXcds;
-        --lists_left;
-      }
-      item_s = item;
-    }
-    __syncthreads();
-    const int64_t item = item_s;
-    if (item < 0) break;
+  // XCD b % kXcds), then, once it is used up, from the other XCDs' lists.  The
+  // claim of the next item goes out while the current tile's results are
+  // stored; item_s hands it to every wave.
+  const int home = (int)(blockIdx.x % kXcds);
+  bool home_left = true;
+  if (threadIdx.x < 64) {
+    const int first = claim_item(a, nt, home, home_left);
+    if (threadIdx.x == 0) item_s = first;
+  }
+  __syncthreads();
+  int item = item_s;
+  while (item >= 0) {
     const MoeTile mt = a.order[item / a.tiles_n];
-    const int64_t n0 = (item % a.tiles_n) * kBN;
+    const int64_t n0 = (int64_t)(item % a.tiles_n) * kBN;
     const int e = mt.expert;
     const int64_t r0 = mt.r0;
-    int64_t r_end = a.expert_off[e + 1];
-    r_end = r_end < a.rows ? r_end : a.rows;  // the tables are exact; this only bounds every access
-    if (r0 >= r_end) {  // (uniform) the barrier keeps item_s from being overwritten before all read it
-      __syncthreads();
-      continue;
+    // (the tables are exact; the clamps only bound every access)
+    int64_t rv = mt.rows < kRmax ? mt.rows : kRmax;
+    rv = r0 + rv <= a.rows ? rv : a.rows - r0;
+    int next = -1;
+    auto claim_next = [&]() {
+      if (threadIdx.x < 64) next = claim_item(a, nt, home, home_left);
+    };
+    if (rv > 0 && e >= 0 && e < a.E) {  // (uniform)
+      const int rows_valid = (int)rv;
+      const int32_t* tok = a.row_token + r0;
+      uint64_t t_wait = 0, cyc0 = 0;
+      if (a.trace && threadIdx.x == 0) {
+        t_wait = clock_ticks();
+        cyc0 = __builtin_amdgcn_s_memtime();
+      }
+      if (!wait_tile_rows<kRmax>(a, tok, rows_valid, &ok)) return;
+      if (a.trace && threadIdx.x == 0) {
+        a.trace[item * 4 + 0] = t_wait;
+        a.trace[item * 4 + 1] = clock_ticks();
+      }
+      if (kRmax == 256 && rows_valid > 128)
+        moe_tile<kW, kRmax, kBNK, kOutBf16>(a, tok, rows_valid, e, r0, n0, s0, s1, s2, s3, s4, claim_next);
+      else
+        moe_tile<kW, 128, kBNK, kOutBf16>(a, tok, rows_valid, e, r0, n0, s0, s1, s2, s3, s4, claim_next);
+      if (a.trace && threadIdx.x == 0) {  // end time; workgroup and engine-clock cycles since the wait began
+        a.trace[item * 4 + 2] = clock_ticks();
+        a.trace[item * 4 + 3] = (uint64_t)blockIdx.x | ((__builtin_amdgcn_s_memtime() - cyc0) << 16);
+      }
+    } else {
+      __syncthreads();  // every wave has read item_s before it is written again
+      claim_next();
     }
-    const int rows_valid = (int)(r_end - r0 < kRmax ? r_end - r0 : kRmax);
-    const int32_t* tok = a.row_token + r0;
-    uint64_t t_wait = 0;
-    if (a.trace && threadIdx.x == 0) t_wait = clock_ticks();
-    if (!wait_tile_rows<kRmax>(a, tok, rows_valid, &ok)) return;
-    if (a.trace && threadIdx.x == 0) {
-      a.trace[item * 4 + 0] = t_wait;
-      a.trace[item * 4 + 1] = clock_ticks();
-      a.trace[item * 4 + 3] = blockIdx.x;
-    }
-    if (kRmax == 256 && rows_valid > 128)
-      moe_tile<kW, kRmax, kBNK, kOutBf16>(a, tok, rows_valid, e, r0, n0, s0, s1, s2, s3, s4);
-    else
-      moe_tile<kW, 128, kBNK, kOutBf16>(a, tok, rows_valid, e, r0, n0, s0, s1, s2, s3, s4);
-    if (a.trace && threadIdx.x == 0) a.trace[item * 4 + 2] = clock_ticks();
+    // (with a tile, the barriers of its K loop lie between every wave's read of
+    // item_s and this write)
+    if (threadIdx.x == 0) item_s = next;
+    __syncthreads();
+    item = item_s;
   }
   wait_producer_done(a.prod_done, a.prod_done_all, a.timeout_ticks, a.status);
 }

@@ -214,7 +214,8 @@ __global__ void __launch_bounds__(256) moe_place_kernel(const uint32_t* __restri
   const uint32_t nt_e = (n_e + tile_rows - 1) / tile_rows;
   for (uint32_t j = tid; j < nt_e; j += 256) {
     const uint32_t q = xcd_list_pos(base_tile + j, nt);  // < nt (base_tile + j < nt)
-    if (q < tb.tiles_cap) tb.order[q] = MoeTile{e, (int32_t)(base_row + j * tile_rows)};
+    const uint32_t r = j * tile_rows, rows = n_e - r < (uint32_t)tile_rows ? n_e - r : (uint32_t)tile_rows;
+    if (q < tb.tiles_cap) tb.order[q] = MoeTile{e, (int32_t)(base_row + r), (int32_t)rows};
   }
 
   // Place the tokens that chose e, in ascending token order: thread i takes

@@ -64,7 +64,10 @@ __global__ void __launch_bounds__(kPrepThreads) moe_rs_prep_kernel(MoeRsArgs a) 
     }
     const int first = scan[e] - mine;
     for (int i = 0; i < mine; ++i)
-      if (first + i < a.tiles_cap) a.tiles[first + i] = MoeTile{e, (int32_t)(g0 + (int64_t)i * kBM)};
+      if (first + i < a.tiles_cap) {
+        const int64_t r0 = g0 + (int64_t)i * kBM;
+        a.tiles[first + i] = MoeTile{e, (int32_t)r0, (int32_t)(g1 - r0 < kBM ? g1 - r0 : kBM)};
+      }
     if (e == kPrepThreads - 1) *a.n_row_tiles = (uint32_t)(scan[e] < a.tiles_cap ? scan[e] : a.tiles_cap);
   }
   // inverse routing: the row holding pick (t, j) is the row of group topk_ids[t][j] whose token is t
