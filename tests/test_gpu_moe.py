@@ -177,6 +177,34 @@ def test_moe_bits_independent_of_arrival(ctx):
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
+def test_moe_trace_covers_every_item(ctx, orc):
+    """A traced overlapped call: one record per work item of the list (row tiles x column tiles), each with
+    wait <= flags seen <= end, its workgroup and a plausible engine-clock cycle count; nothing past the list;
+    a release time for every signal tile.  The results stay those of the oracle."""
+    W, T, H, Ic, E, k = 8, 1024, 256, 768, 64, 8
+    w = I.scaled(I.MOE, W=W, T=T, H=H, I=Ic, E=E, topk=k)
+    shards, We, logits = I.make_moe(w, salt=3, W_layout="nk")
+    nw = sgt.moe_trace_words(W, T, H, Ic, E, k, b_layout="nk")
+    tr = torch.zeros(nw, dtype=torch.int64, device="cuda:0")
+    res = run_moe(ctx, shards, We, logits, k, w_layout="nk", peer_gbps=10.0, trace=tr.data_ptr())
+    check_moe(orc, shards, We, logits, k, res, w_layout="nk", what="traced moe")
+    off = res[3]
+    groups = np.diff(off.astype(np.int64))
+    n_items = int(np.sum((groups + 255) // 256)) * (Ic // 256)
+    nf = sgt.ag_flag_count(W, T, H)
+    t = host(tr).astype(np.uint64)
+    rec = t[: n_items * 4].reshape(-1, 4)
+    wait, seen, end = rec[:, 0].astype(np.int64), rec[:, 1].astype(np.int64), rec[:, 2].astype(np.int64)
+    assert (wait > 0).all() and (seen >= wait).all() and (end > seen).all(), "an item is missing or out of order"
+    wg = (rec[:, 3] & np.uint64(0xFFFF)).astype(np.int64)
+    cyc = (rec[:, 3] >> np.uint64(16)).astype(np.float64)
+    assert (wg < 1024).all() and (cyc > 0).all()
+    mhz = cyc / ((end - wait) / 100.0)   # the 100 MHz clock: (end - wait) / 100 microseconds
+    assert (mhz > 300).all() and (mhz < 3000).all(), (mhz.min(), mhz.max())
+    assert not t[n_items * 4: nw - nf].any(), "records past the work list"
+    assert (t[nw - nf:] > 0).all(), "a signal tile without a release time"
+
+
 def test_moe_withheld_peer_times_out(ctx):
     w = I.scaled(I.MOE, W=4, T=256, H=64, I=64, E=8, topk=2)
     shards, We, logits = I.make_moe(w)
