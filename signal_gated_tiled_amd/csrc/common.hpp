@@ -178,7 +178,6 @@ struct MoeTables {
   int32_t tokens_per_group;
   uint32_t* n_tiles;      // 1: number of grouped row tiles
   uint32_t tiles_cap;     // entries of order
-  uint32_t* claim;        // 1: next consumer work item to claim
   uint32_t* xcd_claim;    // kXcds counters, kXcdClaimStride words apart: next item of each XCD's list
   MoeTile* order;         // the row tiles, expert-major, in the XCD-partitioned lists (xcd_list_pos)
 };
@@ -193,7 +192,6 @@ struct MoeArgs {
   const MoeTile* order;
   const uint32_t* n_tiles;
   uint32_t tiles_cap;         // entries of `order`
-  uint32_t* claim;            // (unused by the consumer: it claims from xcd_claim)
   uint32_t* xcd_claim;        // per-XCD claim counters (MoeTables::xcd_claim)
   const uint32_t* flags;      // one per signal tile of X
   uint32_t* status;

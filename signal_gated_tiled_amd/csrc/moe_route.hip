@@ -203,7 +203,6 @@ __global__ void __launch_bounds__(256) moe_place_kernel(const uint32_t* __restri
     if (tid == 0) {
       expert_off[E] = (int32_t)rows_total;
       *tb.n_tiles = tiles_total;
-      *tb.claim = 0u;
     }
     if (tid < kXcds) tb.xcd_claim[tid * kXcdClaimStride] = 0u;
   }

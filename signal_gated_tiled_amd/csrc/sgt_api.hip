@@ -108,7 +108,7 @@ struct sgt_ctx {
   int ag_claim_parity = 0;         // which of the two AllGather claim-counter sets the next consumer uses
   ProdItem* h_items[kSlots] = {};
   ProdItem* d_items[kSlots] = {};
-  uint32_t* d_moe = nullptr;       // MoE: tile count, claim counter, producer started and finished counts,
+  uint32_t* d_moe = nullptr;       // MoE: tile count (word 0), producer started (12) and finished (16) counts,
                                    // per-XCD claim counters (words 64 + 16 x), counts[2][256] by call parity
                                    // (words 256..767)
   int moe_parity = 0;
@@ -1508,7 +1508,6 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   tb.tokens_per_group = tpg;
   tb.n_tiles = ctx->d_moe;
   tb.tiles_cap = (uint32_t)ctx->moe_cap;
-  tb.claim = ctx->d_moe + 4;
   tb.xcd_claim = ctx->d_moe + 64;  // kXcds counters at words 64, 80, ..., 176
   tb.order = ctx->d_moe_order;
 
@@ -1518,7 +1517,7 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   a.We = static_cast<const uint16_t*>(W_experts);
   a.Y = Y; a.row_token = row_token; a.expert_off = expert_off; a.order = tb.order; a.n_tiles = tb.n_tiles;
   a.tiles_cap = tb.tiles_cap;
-  a.claim = tb.claim; a.xcd_claim = tb.xcd_claim; a.flags = shard_flags; a.status = ctx->d_status; a.trace = o.trace;
+  a.xcd_claim = tb.xcd_claim; a.flags = shard_flags; a.status = ctx->d_status; a.trace = o.trace;
   a.T = T; a.H = H; a.I = I; a.rows = T * topk; a.E = E; a.flag_rows = (int32_t)p.flag_rows; a.tiles_n = p.tiles_n;
   a.epoch = e; a.timeout_ticks = timeout_ticks(o);
   const int64_t n_items_max = max_tiles * p.tiles_n;
