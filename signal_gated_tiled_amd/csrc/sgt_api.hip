@@ -1585,6 +1585,11 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
     a.prod_done = gpu_join;
     a.prod_done_all = ctx->moe_prod_done;
   }
+  // the slot's schedule is read only on the producer's stream (its upload and
+  // the producer), so its reuse waits on that stream, and the caller's stream
+  // carries no extra marker between one call's consumer and the next call
+  HIP_TRY(hipEventRecord(ctx->slot_ev[slot], ctx->prod));
+  ctx->slot_used[slot] = true;
   HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
   // The consumer takes the whole chip: its last pwg workgroups land on the
   // producer's CUs as the producer finishes (they claim work dynamically, so
@@ -1602,8 +1607,6 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   if ((st = route_and_compute(o.consumer_cus > 0 ? std::min(o.consumer_cus, keep) : ctx->n_cu, keep)) != SGT_OK)
     return st;
   if (!gpu_join) HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
-  HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
-  ctx->slot_used[slot] = true;
   return finish(ctx, o, stream);
 }
 
