@@ -19,6 +19,8 @@ struct RingArgs {
   int32_t W, rank, T, tile;  // T tiles of `tile` elements (a multiple of 4) per chunk
   uint32_t epoch;
   uint64_t timeout_ticks;
+  const uint32_t* prod_done;  // the producer's finished count to wait for before exit (overlapped), or null
+  uint32_t prod_done_all;
 };
 
 }  // namespace sgt

@@ -125,6 +125,9 @@ __global__ void __launch_bounds__(kRingThreads) ring_allreduce_kernel(RingArgs a
       if (a.trace) a.trace[it * 3 + 2] = clock_ticks();
     }
   }
+  // the join with an overlapped producer: its workgroups count themselves
+  // finished, and the kernel ends after all of them
+  wait_producer_done(a.prod_done, a.prod_done_all, a.timeout_ticks, a.status);
 }
 
 }  // namespace

@@ -87,6 +87,7 @@ constexpr int kSlots = 4;                 // producer schedule tables in flight
 // for the AllGather consumer (cleared by a fill kernel before each launch).
 constexpr int kCounterWords = 512;
 constexpr int kAgStartedWord = 32, kAgDoneWord = 48, kAgClaimWord = 64;  // claim sets: 64.. and 192..
+constexpr int kRingDoneWord = 56;  // the ring AllReduce producer's finished count
 constexpr int kSdmaMaxUnits = 4096;       // copy-engine copies per call
 constexpr int64_t kSdmaUnitBytes = 4 << 20;  // bytes per copy-engine copy (whole-row signal tiles grouped up to this)
 constexpr int64_t kItemsCap = 1 << 18;    // signal tiles per call
@@ -105,6 +106,7 @@ struct sgt_ctx {
   uint32_t* d_counters = nullptr;  // work-claim counters, zeroed before each launch that uses them
   uint32_t ag_prod_started = 0;    // AllGather producer workgroups launched so far (cumulative)
   uint32_t ag_prod_done = 0;       // of those, the ones that count themselves finished (cumulative)
+  uint32_t ring_prod_done = 0;     // ring AllReduce producer workgroups finished (cumulative)
   int ag_claim_parity = 0;         // which of the two AllGather claim-counter sets the next consumer uses
   ProdItem* h_items[kSlots] = {};
   ProdItem* d_items[kSlots] = {};
@@ -2009,8 +2011,17 @@ sgt_status sgt_ring_allreduce(sgt_ctx* ctx, const float* x, const float* left_ms
   HIP_TRY(hipEventRecord(ctx->ev_fork, stream));
   HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
   if ((st = stage_items(ctx, items, n, ctx->prod, &slot)) != SGT_OK) return st;
+  // The ring kernel joins the producer on the GPU: each producer workgroup
+  // counts itself finished and every ring workgroup waits for the call's total
+  // before it exits, so no event wait sits on the caller's stream.
+  uint32_t* done = n > 0 && pwg > 0 ? ctx->d_counters + kRingDoneWord : nullptr;
   HIP_TRY(launch_ag_producer(flags, ctx->d_items[slot], n, (int64_t)tile * 4, e, o.withhold_peer, nullptr, pwg,
-                             ctx->prod));
+                             ctx->prod, nullptr, nullptr, 0, 0, 0, nullptr, 0, nullptr, 0, nullptr, done));
+  if (done) {  // counted once the launch has gone in
+    ctx->ring_prod_done += (uint32_t)pwg;
+    a.prod_done = done;
+    a.prod_done_all = ctx->ring_prod_done;
+  }
   HIP_TRY(hipEventRecord(ctx->slot_ev[slot], ctx->prod));
   ctx->slot_used[slot] = true;
   // the ring's workgroups take the CUs the producer leaves, so every wait can end
@@ -2019,8 +2030,10 @@ sgt_status sgt_ring_allreduce(sgt_ctx* ctx, const float* x, const float* left_ms
   if ((st = mark(o, 0, stream)) != SGT_OK) return st;
   HIP_TRY(launch_ring_allreduce(a, grid, stream));
   if ((st = mark(o, 1, stream)) != SGT_OK) return st;
-  HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
-  HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
+  if (!done) {
+    HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
+    HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
+  }
   return finish(ctx, o, stream);
 }
 
