@@ -106,6 +106,8 @@ struct RsArgs {
   uint32_t epoch;
   int32_t tile_waves;
   uint64_t timeout_ticks;
+  const uint32_t* prod_done;  // paced peers: the producer's finished count to wait for before exit, or null
+  uint32_t prod_done_all;
 };
 
 // One grouped row tile: rows [r0, r0 + rows) of expert e's group (rows at

@@ -140,6 +140,8 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) gemm_rs_kernel(RsArgs a
     jn = claimed;
     __syncthreads();  // every thread has read `claimed` before thread 0 writes it again
   }
+  // paced peers: the join with the producer (its workgroups count themselves finished)
+  wait_producer_done(a.prod_done, a.prod_done_all, a.timeout_ticks, a.status);
 }
 
 }  // namespace

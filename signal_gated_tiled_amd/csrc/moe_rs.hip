@@ -219,6 +219,8 @@ __global__ void __launch_bounds__(Tile<8>::kThreads, 1) moe_rs_kernel(MoeRsArgs 
     if (!ok) return;
     __syncthreads();
   }
+  // paced peers: the join with the producer (its workgroups count themselves finished)
+  wait_producer_done(a.rs.prod_done, a.rs.prod_done_all, a.rs.timeout_ticks, a.rs.status);
 }
 
 }  // namespace

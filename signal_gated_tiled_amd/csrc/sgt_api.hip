@@ -88,6 +88,7 @@ constexpr int kSlots = 4;                 // producer schedule tables in flight
 constexpr int kCounterWords = 512;
 constexpr int kAgStartedWord = 32, kAgDoneWord = 48, kAgClaimWord = 64;  // claim sets: 64.. and 192..
 constexpr int kRingDoneWord = 56;  // the ring AllReduce producer's finished count
+constexpr int kRsDoneWord = 60;    // the paced ReduceScatter peers' producer's finished count
 constexpr int kSdmaMaxUnits = 4096;       // copy-engine copies per call
 constexpr int64_t kSdmaUnitBytes = 4 << 20;  // bytes per copy-engine copy (whole-row signal tiles grouped up to this)
 constexpr int64_t kItemsCap = 1 << 18;    // signal tiles per call
@@ -107,6 +108,7 @@ struct sgt_ctx {
   uint32_t ag_prod_started = 0;    // AllGather producer workgroups launched so far (cumulative)
   uint32_t ag_prod_done = 0;       // of those, the ones that count themselves finished (cumulative)
   uint32_t ring_prod_done = 0;     // ring AllReduce producer workgroups finished (cumulative)
+  uint32_t rs_prod_done = 0;       // paced ReduceScatter producer workgroups finished (cumulative)
   int ag_claim_parity = 0;         // which of the two AllGather claim-counter sets the next consumer uses
   ProdItem* h_items[kSlots] = {};
   ProdItem* d_items[kSlots] = {};
@@ -1116,7 +1118,7 @@ namespace {
 // producer's workgroups.
 sgt_status launch_paced_peers(sgt_ctx* ctx, const sgt_opts& o, uint32_t* pflags, const float* const* peer_blocks,
                               const float* const* inbox, int W, int rs_tm, int rs_tn, int64_t band_bytes, uint32_t e,
-                              uint32_t* counter, hipStream_t stream, int* pwg_out) {
+                              uint32_t* counter, hipStream_t stream, int* pwg_out, RsArgs* join) {
   int slot;
   sgt_status st;
   const int64_t bands = rs_tm, block_tiles = (int64_t)rs_tm * rs_tn;
@@ -1153,13 +1155,24 @@ sgt_status launch_paced_peers(sgt_ctx* ctx, const sgt_opts& o, uint32_t* pflags,
   HIP_TRY(hipEventRecord(ctx->ev_fork, stream));
   HIP_TRY(hipStreamWaitEvent(ctx->prod, ctx->ev_fork, 0));
   if ((st = stage_items(ctx, items, n, ctx->prod, &slot)) != SGT_OK) return st;
-  HIP_TRY(launch_ag_producer(pflags, ctx->d_items[slot], n, band_bytes, e, o.withhold_peer, nullptr, pwg, ctx->prod));
+  // The consumer kernel joins the producer on the GPU: each producer workgroup
+  // counts itself finished, and the consumer's workgroups wait for the call's
+  // total before they exit (join_paced_peers is then not needed).
+  uint32_t* done = n > 0 ? ctx->d_counters + kRsDoneWord : nullptr;
+  HIP_TRY(launch_ag_producer(pflags, ctx->d_items[slot], n, band_bytes, e, o.withhold_peer, nullptr, pwg, ctx->prod,
+                             nullptr, nullptr, 0, 0, 0, nullptr, 0, nullptr, 0, nullptr, done));
+  if (done) {  // counted once the launch has gone in
+    ctx->rs_prod_done += (uint32_t)pwg;
+    join->prod_done = done;
+    join->prod_done_all = ctx->rs_prod_done;
+  }
   HIP_TRY(hipEventRecord(ctx->slot_ev[slot], ctx->prod));
   ctx->slot_used[slot] = true;
   return SGT_OK;
 }
 
-// The caller's stream waits for the producer forked by launch_paced_peers.
+// The caller's stream waits for the producer forked by launch_paced_peers
+// (when the consumer kernel does not join it on the GPU).
 sgt_status join_paced_peers(sgt_ctx* ctx, hipStream_t stream) {
   HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
   HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
@@ -1180,6 +1193,8 @@ sgt_status rs_plan(const void* A_local, const void* B, const float* const* reduc
   if (st != SGT_OK) return st;
   const sgt_opts& o = *opts;
   const bool paced = peer_blocks != nullptr;
+  a->prod_done = nullptr;  // set by a paced overlapped call once its producer is launched
+  a->prod_done_all = 0;
   if (o.in_dtype != SGT_BF16) return fail(SGT_EUNSUPPORTED, "GEMM+RS takes bf16 inputs");
   if (o.out_dtype != SGT_F32) return fail(SGT_EUNSUPPORTED, "GEMM+RS partials are fp32");
   if (!paced && o.producer == SGT_PROD_CU && o.peer_gbps > 0)
@@ -1280,7 +1295,7 @@ sgt_status gemm_rs_impl(sgt_ctx* ctx, const void* A_local, const void* B, const 
   // serial mode), copies the peers' bands into the inbox and releases their flags.
   int pwg = 0;
   if ((st = launch_paced_peers(ctx, o, pflags, peer_blocks, reduce_from, W, a.rs_tm, a.rs_tn, band_bytes, e,
-                               ctx->d_counters, stream, &pwg)) != SGT_OK)
+                               ctx->d_counters, stream, &pwg, &a)) != SGT_OK)
     return st;
   if (o.producer == SGT_PROD_SERIAL) {
     const int grid = std::min(total, o.consumer_cus > 0 ? std::min(o.consumer_cus, ctx->n_cu) : ctx->n_cu);
@@ -1295,7 +1310,7 @@ sgt_status gemm_rs_impl(sgt_ctx* ctx, const void* A_local, const void* B, const 
   if ((st = mark(o, 0, stream)) != SGT_OK) return st;
   HIP_TRY(launch_gemm_rs(a, grid, stream));
   if ((st = mark(o, 1, stream)) != SGT_OK) return st;
-  if ((st = join_paced_peers(ctx, stream)) != SGT_OK) return st;
+  if (!a.prod_done && (st = join_paced_peers(ctx, stream)) != SGT_OK) return st;
   return finish(ctx, o, stream);
 }
 
@@ -1743,7 +1758,7 @@ sgt_status moe_gemm_rs_impl(sgt_ctx* ctx, const void* Hg, const void* W2, const 
   }
   int pwg = 0;
   if ((st = launch_paced_peers(ctx, o, pflags, peer_blocks, partials, W, rs.rs_tm, rs.rs_tn, band_bytes, e, a.claim,
-                               stream, &pwg)) != SGT_OK)
+                               stream, &pwg, &a.rs)) != SGT_OK)
     return st;
   const bool serial = o.producer == SGT_PROD_SERIAL;
   const int avail = serial ? ctx->n_cu : consumer_beside(ctx, pwg);
@@ -1751,7 +1766,7 @@ sgt_status moe_gemm_rs_impl(sgt_ctx* ctx, const void* Hg, const void* W2, const 
   if ((st = mark(o, 0, stream)) != SGT_OK) return st;
   HIP_TRY(launch_moe_rs(a, grid, stream));
   if ((st = mark(o, 1, stream)) != SGT_OK) return st;
-  if (!serial && (st = join_paced_peers(ctx, stream)) != SGT_OK) return st;
+  if (!serial && !a.rs.prod_done && (st = join_paced_peers(ctx, stream)) != SGT_OK) return st;
   return finish(ctx, o, stream);
 }
 
