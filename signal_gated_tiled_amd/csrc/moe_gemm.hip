@@ -15,6 +15,7 @@
 // rows are gathered straight into LDS
 // (the DMA takes one row offset per load) and the MFMA tile core computes
 // Y[r0 .., n0 ..] = X[row_token[r0 ..]] * W_e[:, n0 ..].
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -237,24 +238,28 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) moe_consumer_bf16(MoeAr
 
 }  // namespace
 
+// `done`, when given, is recorded by the launch itself at the kernel's end
+// (no separate marker on the stream).
 template <int kW, int kR>
-static void launch_moe(const MoeArgs& a, bool nk, bool ob, int grid, hipStream_t stream) {
-  const dim3 blk(Tile<kW>::kThreads);
-  if (nk && ob) hipLaunchKernelGGL((moe_consumer_bf16<kW, kR, true, true>), dim3(grid), blk, 0, stream, a);
-  if (nk && !ob) hipLaunchKernelGGL((moe_consumer_bf16<kW, kR, true, false>), dim3(grid), blk, 0, stream, a);
-  if (!nk && ob) hipLaunchKernelGGL((moe_consumer_bf16<kW, kR, false, true>), dim3(grid), blk, 0, stream, a);
-  if (!nk && !ob) hipLaunchKernelGGL((moe_consumer_bf16<kW, kR, false, false>), dim3(grid), blk, 0, stream, a);
+static void launch_moe(const MoeArgs& a, bool nk, bool ob, int grid, hipStream_t stream, hipEvent_t done) {
+  auto go = [&](auto kernel) {
+    hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(Tile<kW>::kThreads), 0, stream, nullptr, done, 0, a);
+  };
+  if (nk && ob) go(moe_consumer_bf16<kW, kR, true, true>);
+  if (nk && !ob) go(moe_consumer_bf16<kW, kR, true, false>);
+  if (!nk && ob) go(moe_consumer_bf16<kW, kR, false, true>);
+  if (!nk && !ob) go(moe_consumer_bf16<kW, kR, false, false>);
 }
 
 hipError_t launch_moe_consumer(const MoeArgs& a, int b_layout, int out_dtype, int tile_rows, int tile_waves, int grid,
-                               hipStream_t stream) {
+                               hipStream_t stream, hipEvent_t done) {
   const bool nk = b_layout == 1, ob = out_dtype == 1;
   if (tile_rows == 256) {
-    if (tile_waves == 4) launch_moe<4, 256>(a, nk, ob, grid, stream);
-    else launch_moe<8, 256>(a, nk, ob, grid, stream);
+    if (tile_waves == 4) launch_moe<4, 256>(a, nk, ob, grid, stream, done);
+    else launch_moe<8, 256>(a, nk, ob, grid, stream, done);
   } else {
-    if (tile_waves == 4) launch_moe<4, 128>(a, nk, ob, grid, stream);
-    else launch_moe<8, 128>(a, nk, ob, grid, stream);
+    if (tile_waves == 4) launch_moe<4, 128>(a, nk, ob, grid, stream, done);
+    else launch_moe<8, 128>(a, nk, ob, grid, stream, done);
   }
   return hipGetLastError();
 }

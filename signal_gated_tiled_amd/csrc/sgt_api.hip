@@ -51,7 +51,7 @@ hipError_t launch_moe_route(const float* logits, int64_t T, int E, int k, int ti
                             int32_t* expert_off, int32_t* row_token, int32_t* topk_ids, hipStream_t stream);
 hipError_t launch_moe_rs(const MoeRsArgs& a, int grid, hipStream_t stream);
 hipError_t launch_moe_consumer(const MoeArgs& a, int b_layout, int out_dtype, int tile_rows, int tile_waves, int grid,
-                               hipStream_t stream);
+                               hipStream_t stream, hipEvent_t done);
 hipError_t launch_a2a_scan(const A2aArgs& a, hipStream_t stream);
 hipError_t launch_a2a(const A2aArgs& a, int recv_grid, hipStream_t stream);
 inline int kBMrs() { return rs_gemm_tile(); }
@@ -500,9 +500,10 @@ sgt_status sync_locked(sgt_ctx* c) {
 }
 
 // End of a call that launched work on `stream`: remember where the call's work
-// ends (sgt_sync waits for it), and in blocking mode wait and report.
-sgt_status finish(sgt_ctx* ctx, const sgt_opts& o, hipStream_t stream) {
-  HIP_TRY(hipEventRecord(ctx->ev_done, stream));
+// ends (sgt_sync waits for it; done_recorded: the call's last kernel launch
+// already records ev_done at its end), and in blocking mode wait and report.
+sgt_status finish(sgt_ctx* ctx, const sgt_opts& o, hipStream_t stream, bool done_recorded = false) {
+  if (!done_recorded) HIP_TRY(hipEventRecord(ctx->ev_done, stream));
   ctx->ev_done_used = true;
   if (!o.blocking) return SGT_OK;
   HIP_TRY(hipStreamSynchronize(stream));
@@ -1546,6 +1547,7 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   // for the producer; the others (the last launched - keep) yield unless every
   // producer workgroup already runs.  The split is taken on the grid actually
   // launched, so a grid of keep workgroups or fewer never yields.
+  const bool done_bound = I > 0 && !o.consumer_events[1];
   auto route_and_compute = [&](int grid, int keep) -> sgt_status {
     HIP_TRY(launch_moe_route(logits, T, E, topk, rows, tb, expert_off, row_token, topk_ids, stream));
     ctx->moe_parity ^= 1;  // this call's top-k cleared the other counts buffer for the next call
@@ -1554,8 +1556,11 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
       a.late_blocks = keep > 0 ? std::max(0, launched - keep) : 0;
       sgt_status s2;
       if ((s2 = mark(o, 0, stream)) != SGT_OK) return s2;
+      // the launch records ev_done at the consumer's end, the end of the call's
+      // work on this stream (finish records nothing more), unless the caller
+      // times the consumer with events of its own (then its end marker follows)
       HIP_TRY(launch_moe_consumer(a, o.b_layout, o.out_dtype, rows, o.tile_waves ? o.tile_waves : 8, launched,
-                                  stream));
+                                  stream, done_bound ? ctx->ev_done : nullptr));
       if ((s2 = mark(o, 1, stream)) != SGT_OK) return s2;
     }
     return SGT_OK;
@@ -1566,7 +1571,7 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
     HIP_TRY(launch_fill_u32(shard_flags, p.n_flags, e, stream));
     if ((st = route_and_compute(o.consumer_cus > 0 ? std::min(o.consumer_cus, ctx->n_cu) : ctx->n_cu, 0)) != SGT_OK)
       return st;
-    return finish(ctx, o, stream);
+    return finish(ctx, o, stream, done_bound);
   }
 
   int slot;
@@ -1582,7 +1587,7 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
       return st;
     HIP_TRY(hipEventRecord(ctx->slot_ev[slot], stream));
     ctx->slot_used[slot] = true;
-    return finish(ctx, o, stream);
+    return finish(ctx, o, stream, done_bound);
   }
 
   // Overlapped: producer on its own stream and CUs; routing, then the grouped
@@ -1624,7 +1629,7 @@ sgt_status sgt_moe_ag_gemm(sgt_ctx* ctx, const void* const* X_shards, const void
   if ((st = route_and_compute(o.consumer_cus > 0 ? std::min(o.consumer_cus, keep) : ctx->n_cu, keep)) != SGT_OK)
     return st;
   if (!gpu_join) HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
-  return finish(ctx, o, stream);
+  return finish(ctx, o, stream, done_bound);
 }
 
 
