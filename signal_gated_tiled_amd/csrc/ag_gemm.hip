@@ -9,6 +9,7 @@
 //    tiles, one workgroup (4 or 8 wave64s) per CU.
 //  * ag_consumer_f32: fp32 inputs with fp32 FMAs (64 x 64 tiles), for fp32
 //    workloads where a bf16 downcast would lose the required accuracy.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -312,22 +313,26 @@ __global__ void __launch_bounds__(256) ag_consumer_f32(AgArgs a) {
 int ag_panel_rows(int in_dtype) { return in_dtype == 1 ? kBM : kF32BM; }
 int ag_panel_cols(int in_dtype) { return in_dtype == 1 ? kBN : kF32BN; }
 
+// `done`, when given, is recorded by the launch itself at the kernel's end (no
+// separate marker on the stream).
 template <int kW>
-static void launch_bf16(const AgArgs& a, int grid, hipStream_t stream) {
+static void launch_bf16(const AgArgs& a, int grid, hipStream_t stream, hipEvent_t done) {
   const bool nk = a.b_layout == 1, ob = a.out_dtype == 1;
-  const dim3 blk(Tile<kW>::kThreads);
-  if (nk && ob) hipLaunchKernelGGL((ag_consumer_bf16<kW, true, true>), dim3(grid), blk, 0, stream, a);
-  if (nk && !ob) hipLaunchKernelGGL((ag_consumer_bf16<kW, true, false>), dim3(grid), blk, 0, stream, a);
-  if (!nk && ob) hipLaunchKernelGGL((ag_consumer_bf16<kW, false, true>), dim3(grid), blk, 0, stream, a);
-  if (!nk && !ob) hipLaunchKernelGGL((ag_consumer_bf16<kW, false, false>), dim3(grid), blk, 0, stream, a);
+  auto go = [&](auto kernel) {
+    hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(Tile<kW>::kThreads), 0, stream, nullptr, done, 0, a);
+  };
+  if (nk && ob) go(ag_consumer_bf16<kW, true, true>);
+  if (nk && !ob) go(ag_consumer_bf16<kW, true, false>);
+  if (!nk && ob) go(ag_consumer_bf16<kW, false, true>);
+  if (!nk && !ob) go(ag_consumer_bf16<kW, false, false>);
 }
 
-hipError_t launch_ag_consumer(const AgArgs& a, int in_dtype, int grid, hipStream_t stream) {
+hipError_t launch_ag_consumer(const AgArgs& a, int in_dtype, int grid, hipStream_t stream, hipEvent_t done) {
   if (in_dtype == 1) {
-    if (a.tile_waves == 4) launch_bf16<4>(a, grid, stream);
-    else launch_bf16<8>(a, grid, stream);
+    if (a.tile_waves == 4) launch_bf16<4>(a, grid, stream, done);
+    else launch_bf16<8>(a, grid, stream, done);
   } else {
-    hipLaunchKernelGGL(ag_consumer_f32, dim3(grid), dim3(256), 0, stream, a);
+    hipExtLaunchKernelGGL(ag_consumer_f32, dim3(grid), dim3(256), 0, stream, nullptr, done, 0, a);
   }
   return hipGetLastError();
 }

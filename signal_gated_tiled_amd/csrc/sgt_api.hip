@@ -41,7 +41,7 @@ hipError_t launch_ag_allgather(uint32_t* flags, const ProdItem* items, int n_pro
                                uint64_t timeout_ticks, uint32_t* status, uint64_t* trace, hipStream_t stream);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
 hipError_t launch_rs_prepare(uint32_t* pflags, int64_t n, uint32_t v, uint32_t* counter, hipStream_t stream);
-hipError_t launch_ag_consumer(const AgArgs& a, int in_dtype, int grid, hipStream_t stream);
+hipError_t launch_ag_consumer(const AgArgs& a, int in_dtype, int grid, hipStream_t stream, hipEvent_t done);
 int ag_panel_rows(int in_dtype);
 int ag_panel_cols(int in_dtype);
 hipError_t launch_gemm_rs(const RsArgs& a, int grid, hipStream_t stream);
@@ -982,9 +982,14 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
   };
   // the consumer launch; a launch that claims from a counter set hands the
   // other set to the next one
-  auto launch_consumer = [&](int grid) -> sgt_status {
+  // bound: the consumer ends the call's work on this stream, and its launch
+  // records ev_done itself (finish then records nothing more), unless the
+  // caller times the consumer with events of its own
+  bool bound = false;
+  auto launch_consumer = [&](int grid, bool last) -> sgt_status {
     if ((st = mark(o, 0, stream)) != SGT_OK) return st;
-    HIP_TRY(launch_ag_consumer(a, o.in_dtype, grid, stream));
+    bound = last && !o.consumer_events[1];
+    HIP_TRY(launch_ag_consumer(a, o.in_dtype, grid, stream, bound ? ctx->ev_done : nullptr));
     if (a.xcd_claim) ctx->ag_claim_parity ^= 1;
     return mark(o, 1, stream);
   };
@@ -994,8 +999,8 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
     const int grid = std::min(total_tiles, o.consumer_cus > 0 ? o.consumer_cus
                                             : (o.in_dtype == SGT_BF16 ? ctx->n_cu : 4 * ctx->n_cu));
     if ((st = claim_setup(grid, 0)) != SGT_OK) return st;
-    if (N > 0 && (st = launch_consumer(grid)) != SGT_OK) return st;
-    return finish(ctx, o, stream);
+    if (N > 0 && (st = launch_consumer(grid, true)) != SGT_OK) return st;
+    return finish(ctx, o, stream, bound);
   }
 
   int slot;
@@ -1017,8 +1022,8 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
     const int grid = std::min(total_tiles, o.consumer_cus > 0 ? o.consumer_cus
                                             : (o.in_dtype == SGT_BF16 ? ctx->n_cu : 4 * ctx->n_cu));
     if ((st = claim_setup(grid, 0)) != SGT_OK) return st;
-    if (N > 0 && (st = launch_consumer(grid)) != SGT_OK) return st;
-    return finish(ctx, o, stream);
+    if (N > 0 && (st = launch_consumer(grid, true)) != SGT_OK) return st;
+    return finish(ctx, o, stream, bound);
   }
 
   // Overlapped: the producer runs on its own stream.  The consumer keeps one
@@ -1072,12 +1077,12 @@ sgt_status sgt_ag_gemm(sgt_ctx* ctx, const void* const* A_shards, const void* B,
     grid = o.consumer_cus > 0 ? std::min(o.consumer_cus, keep) : keep;
     grid = std::min(grid, total_tiles);
   }
-  if (N > 0 && (st = launch_consumer(grid)) != SGT_OK) return st;
+  if (N > 0 && (st = launch_consumer(grid, gpu_join != nullptr)) != SGT_OK) return st;
   if (!gpu_join) {
     HIP_TRY(hipEventRecord(ctx->ev_join, ctx->prod));
     HIP_TRY(hipStreamWaitEvent(stream, ctx->ev_join, 0));
   }
-  return finish(ctx, o, stream);
+  return finish(ctx, o, stream, bound);
 }
 
 int64_t sgt_rs_trace_words(int W, int64_t M, int64_t N, const sgt_opts* opts) {
