@@ -18,6 +18,7 @@
 // round of GEMM tiles.  Dependencies only point from reduction to GEMM, and a
 // workgroup claims reduction tiles only after all of its own GEMM tiles, so the
 // kernel cannot deadlock; every wait is still bounded.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -148,16 +149,19 @@ __global__ void __launch_bounds__(Tile<kW>::kThreads, 1) gemm_rs_kernel(RsArgs a
 
 int rs_gemm_tile() { return kBM; }
 
-hipError_t launch_gemm_rs(const RsArgs& a, int grid, hipStream_t stream) {
+// `done`, when given, is recorded by the launch itself at the kernel's end (no
+// separate marker on the stream).
+hipError_t launch_gemm_rs(const RsArgs& a, int grid, hipStream_t stream, hipEvent_t done) {
   const bool nk = a.b_layout == 1;
+  auto go = [&](auto kernel, int threads) {
+    hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, stream, nullptr, done, 0, a);
+  };
   if (a.tile_waves == 4) {
-    const dim3 blk(Tile<4>::kThreads);
-    if (nk) hipLaunchKernelGGL((gemm_rs_kernel<4, true>), dim3(grid), blk, 0, stream, a);
-    else hipLaunchKernelGGL((gemm_rs_kernel<4, false>), dim3(grid), blk, 0, stream, a);
+    if (nk) go(gemm_rs_kernel<4, true>, Tile<4>::kThreads);
+    else go(gemm_rs_kernel<4, false>, Tile<4>::kThreads);
   } else {
-    const dim3 blk(Tile<8>::kThreads);
-    if (nk) hipLaunchKernelGGL((gemm_rs_kernel<8, true>), dim3(grid), blk, 0, stream, a);
-    else hipLaunchKernelGGL((gemm_rs_kernel<8, false>), dim3(grid), blk, 0, stream, a);
+    if (nk) go(gemm_rs_kernel<8, true>, Tile<8>::kThreads);
+    else go(gemm_rs_kernel<8, false>, Tile<8>::kThreads);
   }
   return hipGetLastError();
 }

@@ -22,6 +22,7 @@
 // Dependencies point only from later kinds to earlier ones and a workgroup
 // claims only after its own GEMM tiles, with at most one workgroup per CU, so
 // the kernel cannot deadlock; every wait is bounded.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -225,18 +226,22 @@ __global__ void __launch_bounds__(Tile<8>::kThreads, 1) moe_rs_kernel(MoeRsArgs 
 
 }  // namespace
 
-hipError_t launch_moe_rs(const MoeRsArgs& a, int grid, hipStream_t stream) {
+// `done`, when given, is recorded by the main kernel's launch at its end (no
+// separate marker on the stream).
+hipError_t launch_moe_rs(const MoeRsArgs& a, int grid, hipStream_t stream, hipEvent_t done) {
   int64_t pb = (a.rows + 255) / 256;
   if (pb < 1) pb = 1;
   if (pb > 1024) pb = 1024;
   hipLaunchKernelGGL(moe_rs_prep_kernel, dim3((unsigned)pb), dim3(kPrepThreads), 0, stream, a);
-  const dim3 blk(Tile<8>::kThreads);
+  auto go = [&](auto kernel) {
+    hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(Tile<8>::kThreads), 0, stream, nullptr, done, 0, a);
+  };
   if (a.b_layout == 1) {
-    if (a.y_bf16) hipLaunchKernelGGL((moe_rs_kernel<true, true>), dim3(grid), blk, 0, stream, a);
-    else hipLaunchKernelGGL((moe_rs_kernel<true, false>), dim3(grid), blk, 0, stream, a);
+    if (a.y_bf16) go(moe_rs_kernel<true, true>);
+    else go(moe_rs_kernel<true, false>);
   } else {
-    if (a.y_bf16) hipLaunchKernelGGL((moe_rs_kernel<false, true>), dim3(grid), blk, 0, stream, a);
-    else hipLaunchKernelGGL((moe_rs_kernel<false, false>), dim3(grid), blk, 0, stream, a);
+    if (a.y_bf16) go(moe_rs_kernel<false, true>);
+    else go(moe_rs_kernel<false, false>);
   }
   return hipGetLastError();
 }

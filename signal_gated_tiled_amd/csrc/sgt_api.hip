@@ -44,12 +44,12 @@ hipError_t launch_rs_prepare(uint32_t* pflags, int64_t n, uint32_t v, uint32_t* 
 hipError_t launch_ag_consumer(const AgArgs& a, int in_dtype, int grid, hipStream_t stream, hipEvent_t done);
 int ag_panel_rows(int in_dtype);
 int ag_panel_cols(int in_dtype);
-hipError_t launch_gemm_rs(const RsArgs& a, int grid, hipStream_t stream);
+hipError_t launch_gemm_rs(const RsArgs& a, int grid, hipStream_t stream, hipEvent_t done = nullptr);
 int rs_gemm_tile();
 int moe_tokens_per_group(int64_t T, int k);
 hipError_t launch_moe_route(const float* logits, int64_t T, int E, int k, int tile_rows, const MoeTables& tb,
                             int32_t* expert_off, int32_t* row_token, int32_t* topk_ids, hipStream_t stream);
-hipError_t launch_moe_rs(const MoeRsArgs& a, int grid, hipStream_t stream);
+hipError_t launch_moe_rs(const MoeRsArgs& a, int grid, hipStream_t stream, hipEvent_t done = nullptr);
 hipError_t launch_moe_consumer(const MoeArgs& a, int b_layout, int out_dtype, int tile_rows, int tile_waves, int grid,
                                hipStream_t stream, hipEvent_t done);
 hipError_t launch_a2a_scan(const A2aArgs& a, hipStream_t stream);
@@ -502,7 +502,17 @@ sgt_status sync_locked(sgt_ctx* c) {
 // End of a call that launched work on `stream`: remember where the call's work
 // ends (sgt_sync waits for it; done_recorded: the call's last kernel launch
 // already records ev_done at its end), and in blocking mode wait and report.
-sgt_status finish(sgt_ctx* ctx, const sgt_opts& o, hipStream_t stream, bool done_recorded = false) {
+sgt_status finish(sgt_ctx* ctx, const sgt_opts& o, hipStream_t stream, bool done_recorded = false);
+
+// The event a call's last kernel launch records at its end in place of
+// finish()'s marker: ev_done when that kernel ends the call's work on the
+// caller's stream (`last`) and the caller does not time it with events of its
+// own (whose end marker then follows it); else none.
+hipEvent_t end_event(sgt_ctx* ctx, const sgt_opts& o, bool last) {
+  return last && !o.consumer_events[1] ? ctx->ev_done : nullptr;
+}
+
+sgt_status finish(sgt_ctx* ctx, const sgt_opts& o, hipStream_t stream, bool done_recorded) {
   if (!done_recorded) HIP_TRY(hipEventRecord(ctx->ev_done, stream));
   ctx->ev_done_used = true;
   if (!o.blocking) return SGT_OK;
@@ -1292,9 +1302,9 @@ sgt_status gemm_rs_impl(sgt_ctx* ctx, const void* A_local, const void* B, const 
     // item waits on GEMM tiles statically assigned to other workgroups
     const int grid = std::min(total, o.consumer_cus > 0 ? std::min(o.consumer_cus, ctx->n_cu) : ctx->n_cu);
     if ((st = mark(o, 0, stream)) != SGT_OK) return st;
-    HIP_TRY(launch_gemm_rs(a, grid, stream));
+    HIP_TRY(launch_gemm_rs(a, grid, stream, end_event(ctx, o, true)));
     if ((st = mark(o, 1, stream)) != SGT_OK) return st;
-    return finish(ctx, o, stream);
+    return finish(ctx, o, stream, end_event(ctx, o, true) != nullptr);
   }
 
   // Paced peers: the producer, on its own stream (or first on the caller's in
@@ -1306,18 +1316,18 @@ sgt_status gemm_rs_impl(sgt_ctx* ctx, const void* A_local, const void* B, const 
   if (o.producer == SGT_PROD_SERIAL) {
     const int grid = std::min(total, o.consumer_cus > 0 ? std::min(o.consumer_cus, ctx->n_cu) : ctx->n_cu);
     if ((st = mark(o, 0, stream)) != SGT_OK) return st;
-    HIP_TRY(launch_gemm_rs(a, grid, stream));
+    HIP_TRY(launch_gemm_rs(a, grid, stream, end_event(ctx, o, true)));
     if ((st = mark(o, 1, stream)) != SGT_OK) return st;
-    return finish(ctx, o, stream);
+    return finish(ctx, o, stream, end_event(ctx, o, true) != nullptr);
   }
   // Overlapped: the GEMM+RS kernel on the CUs the producer leaves (one
   // workgroup per CU), so the reduction's waits cannot starve it.
   const int grid = std::min(total, std::min(o.consumer_cus > 0 ? o.consumer_cus : ctx->n_cu, consumer_beside(ctx, pwg)));
   if ((st = mark(o, 0, stream)) != SGT_OK) return st;
-  HIP_TRY(launch_gemm_rs(a, grid, stream));
+  HIP_TRY(launch_gemm_rs(a, grid, stream, end_event(ctx, o, a.prod_done != nullptr)));
   if ((st = mark(o, 1, stream)) != SGT_OK) return st;
   if (!a.prod_done && (st = join_paced_peers(ctx, stream)) != SGT_OK) return st;
-  return finish(ctx, o, stream);
+  return finish(ctx, o, stream, end_event(ctx, o, a.prod_done != nullptr) != nullptr);
 }
 
 }  // namespace
@@ -1762,9 +1772,9 @@ sgt_status moe_gemm_rs_impl(sgt_ctx* ctx, const void* Hg, const void* W2, const 
     HIP_TRY(launch_rs_prepare(pflags, np, e, a.claim, stream));
     const int grid = o.consumer_cus > 0 ? std::min(o.consumer_cus, ctx->n_cu) : ctx->n_cu;
     if ((st = mark(o, 0, stream)) != SGT_OK) return st;
-    HIP_TRY(launch_moe_rs(a, grid, stream));
+    HIP_TRY(launch_moe_rs(a, grid, stream, end_event(ctx, o, true)));
     if ((st = mark(o, 1, stream)) != SGT_OK) return st;
-    return finish(ctx, o, stream);
+    return finish(ctx, o, stream, end_event(ctx, o, true) != nullptr);
   }
   int pwg = 0;
   if ((st = launch_paced_peers(ctx, o, pflags, peer_blocks, partials, W, rs.rs_tm, rs.rs_tn, band_bytes, e, a.claim,
@@ -1774,10 +1784,11 @@ sgt_status moe_gemm_rs_impl(sgt_ctx* ctx, const void* Hg, const void* W2, const 
   const int avail = serial ? ctx->n_cu : consumer_beside(ctx, pwg);
   const int grid = o.consumer_cus > 0 ? std::min(o.consumer_cus, avail) : avail;
   if ((st = mark(o, 0, stream)) != SGT_OK) return st;
-  HIP_TRY(launch_moe_rs(a, grid, stream));
+  const bool last = serial || a.rs.prod_done != nullptr;  // the kernel ends the call's work on this stream
+  HIP_TRY(launch_moe_rs(a, grid, stream, end_event(ctx, o, last)));
   if ((st = mark(o, 1, stream)) != SGT_OK) return st;
   if (!serial && !a.rs.prod_done && (st = join_paced_peers(ctx, stream)) != SGT_OK) return st;
-  return finish(ctx, o, stream);
+  return finish(ctx, o, stream, end_event(ctx, o, last) != nullptr);
 }
 
 }  // namespace
