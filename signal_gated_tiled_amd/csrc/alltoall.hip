@@ -20,6 +20,7 @@
 // sender workgroups, one per (block, chunk), each publishing its chunk's flag
 // no earlier than its link (one per peer, all concurrent, the local one
 // unthrottled) would have delivered it.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "alltoall.hpp"
@@ -490,8 +491,10 @@ hipError_t launch_a2a_scan(const A2aArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_a2a(const A2aArgs& a, int recv_grid, hipStream_t stream) {
-  hipLaunchKernelGGL(a2a_kernel, dim3(a.n_send + recv_grid), dim3(kA2aThreads), 0, stream, a);
+// `done`, when given, is recorded by the launch itself at the kernel's end (no
+// separate marker on the stream).
+hipError_t launch_a2a(const A2aArgs& a, int recv_grid, hipStream_t stream, hipEvent_t done) {
+  hipExtLaunchKernelGGL(a2a_kernel, dim3(a.n_send + recv_grid), dim3(kA2aThreads), 0, stream, nullptr, done, 0, a);
   return hipGetLastError();
 }
 

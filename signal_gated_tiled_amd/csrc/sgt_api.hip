@@ -53,7 +53,7 @@ hipError_t launch_moe_rs(const MoeRsArgs& a, int grid, hipStream_t stream, hipEv
 hipError_t launch_moe_consumer(const MoeArgs& a, int b_layout, int out_dtype, int tile_rows, int tile_waves, int grid,
                                hipStream_t stream, hipEvent_t done);
 hipError_t launch_a2a_scan(const A2aArgs& a, hipStream_t stream);
-hipError_t launch_a2a(const A2aArgs& a, int recv_grid, hipStream_t stream);
+hipError_t launch_a2a(const A2aArgs& a, int recv_grid, hipStream_t stream, hipEvent_t done = nullptr);
 inline int kBMrs() { return rs_gemm_tile(); }
 constexpr int kBNmoe() { return 256; }  // column tile of the tile core
 }  // namespace sgt
@@ -2189,9 +2189,10 @@ sgt_status sgt_a2a_dispatch(sgt_ctx* ctx, const void* const* X, const int32_t* c
   a.fused_scan = (a.E_l <= kA2aMaxFusedLocal && a.n_send > 0) ? 1 : 0;
   if ((st = mark(o, 0, stream)) != SGT_OK) return st;
   if (!a.fused_scan) HIP_TRY(launch_a2a_scan(a, stream));
-  if (a.n_send > 0) HIP_TRY(launch_a2a(a, 0, stream));
+  hipEvent_t done = end_event(ctx, o, a.n_send > 0);  // the senders' launch ends the call's work
+  if (a.n_send > 0) HIP_TRY(launch_a2a(a, 0, stream, done));
   if ((st = mark(o, 1, stream)) != SGT_OK) return st;
-  return finish(ctx, o, stream);
+  return finish(ctx, o, stream, done != nullptr);
 }
 
 sgt_status sgt_a2a_combine(sgt_ctx* ctx, const void* const* back, const int32_t* topk, const float* gate, void* cbuf,
@@ -2237,22 +2238,23 @@ sgt_status sgt_a2a_combine(sgt_ctx* ctx, const void* const* back, const int32_t*
                                                                  : std::min<int64_t>((T_r + 3) / 4, ctx->n_cu / 2));
   if ((st = mark(o, 0, stream)) != SGT_OK) return st;
   HIP_TRY(launch_a2a_scan(a, stream));
+  hipEvent_t done = end_event(ctx, o, true);  // the receiver's launch (the last) ends the call's work
   if (preset) {
     // the expert outputs are already in cbuf: every chunk flag set, then the receiver alone
     HIP_TRY(launch_fill_u32(flags, E * nch, e, stream));
     A2aArgs r = a;
     r.n_send = 0;
-    HIP_TRY(launch_a2a(r, rgrid, stream));
+    HIP_TRY(launch_a2a(r, rgrid, stream, done));
   } else if (o.producer == SGT_PROD_SERIAL) {
     HIP_TRY(launch_a2a(a, 0, stream));
     A2aArgs r = a;
     r.n_send = 0;
-    HIP_TRY(launch_a2a(r, rgrid, stream));
+    HIP_TRY(launch_a2a(r, rgrid, stream, done));
   } else {
-    HIP_TRY(launch_a2a(a, rgrid, stream));
+    HIP_TRY(launch_a2a(a, rgrid, stream, done));
   }
   if ((st = mark(o, 1, stream)) != SGT_OK) return st;
-  return finish(ctx, o, stream);
+  return finish(ctx, o, stream, done != nullptr);
 }
 
 }  // extern "C"
